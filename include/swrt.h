@@ -1,0 +1,212 @@
+/*
+ * swrt.h -- C-ABI of libswrt.so: sliding-window / ring KV-cache updates on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Three operations, each one or two kernel launches on the caller's stream:
+ *
+ *   swrt_tensor_scatter    ONNX operator "TensorScatter" (ai.onnx, since
+ *                          version 24): write an update block into a
+ *                          fixed-capacity cache along the sequence axis at a
+ *                          per-batch write index, linear or circular. The
+ *                          circular mode is also the ring-buffer write "slot =
+ *                          position mod W" of the Core AI model zoo page
+ *                          "Stateful decode & KV cache", section
+ *                          "Sliding-window ring buffer".
+ *   swrt_kv_seq_lengths    onnxruntime pull request "GQA support
+ *                          sliding_window_cache", section "Design": the
+ *                          absolute and cache-relative lengths and per-batch
+ *                          eviction counts of one windowed step, derived on the
+ *                          device from seqlens_k.
+ *   swrt_kv_window_append  same page, section "Design": shift the resident
+ *                          window left by E rows and write the S new rows after
+ *                          it, for K and V in one launch; in place when S = 1,
+ *                          through a C+S staging cache with copy-back when S > 1.
+ *
+ * Conventions shared by every entry point
+ *   - Ownership: the caller owns every buffer. The library allocates nothing,
+ *     frees nothing, keeps no pointer after returning and holds no state, so
+ *     calls on disjoint buffers may come from any host thread.
+ *   - Streams: work is enqueued on `stream` (a hipStream_t; NULL is the null
+ *     stream). Nothing synchronises; buffers must stay alive until the stream
+ *     work ends. No call reads device memory on the host, so every call can be
+ *     captured into a HIP graph.
+ *   - Layout: dense row-major buffers only (strided new-token rows excepted).
+ *     Payload is moved as raw bits: any element type of the given width
+ *     round-trips bit-exactly (NaN payloads, -0, fp8 encodings included).
+ *   - Synchronous errors: a non-zero status is returned and nothing is
+ *     launched. SWRT_E_INVALID_ARG for a null required pointer, a bad rank,
+ *     axis, mode, phase or element width, a negative size, S > M (TensorScatter),
+ *     C < 1, a pointer or stride not aligned to the element width, or
+ *     overlapping buffers (other than present == past). SWRT_E_UNSUPPORTED for
+ *     a row that does not end on a byte (4-bit elements, odd row length) and
+ *     for sizes beyond the limits stated below. SWRT_E_LAUNCH when the HIP
+ *     launch itself fails.
+ *   - Data-dependent problems are reported asynchronously: bits are OR-ed into
+ *     the optional device word *d_flags (may be NULL) and the affected batch
+ *     entry is handled as stated per entry point.
+ */
+#ifndef SWRT_H
+#define SWRT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SWRT_ABI_VERSION 1
+
+/* synchronous status codes */
+#define SWRT_OK 0
+#define SWRT_E_INVALID_ARG 1
+#define SWRT_E_UNSUPPORTED 2
+#define SWRT_E_LAUNCH 3
+
+/* asynchronous flags (OR-ed into *d_flags) */
+#define SWRT_FLAG_LINEAR_OOB 1u   /* linear write index < 0 or > M - S        */
+#define SWRT_FLAG_BAD_SEQLEN 2u   /* seqlens_k[b] < 0 or seqlens_k[b] + 1 < S */
+#define SWRT_FLAG_BAD_LENGTHS 4u  /* (Lp, E) not a valid pair for (C, S)      */
+
+/* TensorScatter mode attribute */
+#define SWRT_MODE_LINEAR 0
+#define SWRT_MODE_CIRCULAR 1
+
+/* phases of a multi-token (S > 1) windowed step */
+#define SWRT_PHASE_STAGE 1u   /* seed staging[0..Lp) and write staging[Lp..Lp+S) */
+#define SWRT_PHASE_COMMIT 2u  /* copy the surviving window back into the cache   */
+#define SWRT_PHASE_ALL 3u     /* STAGE, then COMMIT                              */
+
+#define SWRT_MAX_RANK 8
+
+/*
+ * swrt_tensor_scatter -- TensorScatter (ONNX operator page "TensorScatter":
+ * description, pseudocode, Inputs, Outputs, Attributes).
+ *
+ *   present[(*prefix, j(b, s)), :] = update[(*prefix, s), :]
+ *   for every prefix index `prefix` over shape[0..axis) (b = prefix[0]) and
+ *   every s < S, with j = w_b + s (linear) or (w_b + s) mod M (circular,
+ *   floor modulo, so negative w_b wraps too); M = shape[axis]. Every other row
+ *   of present equals past.
+ *
+ * present        device, same shape as past. present == past updates in place
+ *                (only the target rows are written); otherwise present is
+ *                written in full (past rows plus update rows) and must not
+ *                overlap past.
+ * past           device, dense row-major `shape`.
+ * update         device, dense, `shape` with shape[axis] replaced by seq_len.
+ *                Must not overlap present.
+ * write_indices  device int64[shape[0]], or NULL for all zeros.
+ * shape          host int64[rank]; every dim >= 0.
+ * rank           2 .. SWRT_MAX_RANK.
+ * axis           sequence axis; negative counts from the end; after that it
+ *                must lie in [1, rank) (the batch axis 0 is not allowed).
+ * seq_len        S, 0 <= S <= M. S = 0 (or any zero dim) is a no-op apart from
+ *                the out-of-place copy.
+ * mode           SWRT_MODE_LINEAR or SWRT_MODE_CIRCULAR.
+ * elem_bits      4, 8, 16, 32, 64 or 128; 4-bit needs an even row length
+ *                (product of shape[axis+1..rank)).
+ * d_flags        device uint32 or NULL. SWRT_FLAG_LINEAR_OOB when a linear
+ *                w_b < 0 or w_b + S > M: every row of that batch entry keeps
+ *                past's value (no partial write).
+ * Limits: shape[0] * (product of dims) * elem_bits/8 must fit in int64 and
+ * the number of rows written must be below 2^31 * 2^16.
+ */
+int swrt_tensor_scatter(void *present, const void *past, const void *update,
+                        const int64_t *write_indices, const int64_t *shape,
+                        int rank, int axis, int64_t seq_len, int mode,
+                        int elem_bits, uint32_t *d_flags, void *stream);
+
+/*
+ * swrt_kv_seq_lengths -- lengths of one windowed GQA step (pull request "GQA
+ * support sliding_window_cache", section "Design", and the follow-up that
+ * moves the end-pointer arithmetic to 64 bits and clamps the past length).
+ *
+ * For each b < batch, in 64-bit arithmetic:
+ *   T  = seqlens_k[b] + 1          absolute total length after the step
+ *   P  = max(0, T - S)             absolute past length
+ *   Lp = min(P, C)                 rows resident before the step
+ *   E  = max(0, Lp + S - C)        rows evicted by the step
+ *   L  = Lp + S - E  (= min(T, C)) rows resident after the step
+ *
+ * seqlens_k        device int32[batch] (total length minus one).
+ * batch            >= 0 (0 is a no-op).
+ * seq_len          S >= 1, new tokens in this step.
+ * capacity         C >= 1, rows per (b, h) in the cache.
+ * total_lens       device int64[batch] or NULL: T.
+ * past_lens        device int64[batch] or NULL: P.
+ * cache_past_lens  device int32[batch], required: Lp.
+ * cache_total_lens device int32[batch] or NULL: L.
+ * evict_counts     device int32[batch], required: E.
+ * d_flags          device uint32 or NULL. SWRT_FLAG_BAD_SEQLEN when
+ *                  seqlens_k[b] < 0 or T < S; P is then clamped to 0 and the
+ *                  other values follow from it.
+ * Output buffers must not overlap seqlens_k or each other.
+ */
+int swrt_kv_seq_lengths(const int32_t *seqlens_k, int batch, int seq_len,
+                        int capacity, int64_t *total_lens, int64_t *past_lens,
+                        int32_t *cache_past_lens, int32_t *cache_total_lens,
+                        int32_t *evict_counts, uint32_t *d_flags, void *stream);
+
+/*
+ * swrt_kv_window_append -- one windowed cache step for K and V (pull request
+ * "GQA support sliding_window_cache", section "Design": the invariant that
+ * the cache holds the L = min(T, C) most recent tokens at rows [0, L), the
+ * shift cache[E..Lp) -> cache[0..Lp-E), the write of the new tokens to
+ * cache[Lp-E .. Lp-E+S), in-place decode for S = 1 and the C+S staging cache
+ * for S > 1).
+ *
+ * S = 1 (in place, phase ignored): for every (tensor, b, h)
+ *     cache[0 .. Lp-E) <- old cache[E .. Lp)   (E is 0 or 1)
+ *     cache[Lp-E]      <- new[b, h, 0]
+ * S > 1:
+ *   STAGE:  staging[0 .. Lp)    <- cache[0 .. Lp)
+ *           staging[Lp .. Lp+S) <- new[b, h, 0 .. S)
+ *   COMMIT: cache[0 .. L)       <- staging[E .. E+L)
+ *           (when E = 0 only rows [Lp, L) are copied: rows [0, Lp) of staging
+ *           hold what STAGE seeded, and the caller must not change them
+ *           between the phases; attention may read staging in between.)
+ * Cache rows [L, C) and staging rows [Lp+S, C+S) are never written.
+ *
+ * k_cache, v_cache     device [batch, kv_heads, capacity, head_dim], distinct,
+ *                      non-overlapping.
+ * k_new, v_new         device; row (b, h, s) starts at element
+ *                      b*new_strides[0] + h*new_strides[1] + s*new_strides[2]
+ *                      and its head_dim elements are contiguous (BNSH and BSNH
+ *                      both fit). Must not overlap any cache or staging buffer.
+ * new_strides          host int64[3], element strides for b, h, s (>= 0).
+ * k_staging, v_staging device [batch, kv_heads, capacity + seq_len, head_dim];
+ *                      required when S > 1, ignored (may be NULL) when S = 1.
+ * cache_past_lens,
+ * evict_counts         device int32[batch]: Lp and E from swrt_kv_seq_lengths
+ *                      with the same S and C.
+ * batch, kv_heads      >= 0 (0 is a no-op). head_dim >= 0.
+ * capacity             C >= 1. seq_len S >= 1 (S > C is allowed when S > 1).
+ * elem_bits            4, 8, 16, 32, 64 or 128 (4-bit: even head_dim and
+ *                      even strides).
+ * phase                SWRT_PHASE_STAGE, _COMMIT or _ALL when S > 1.
+ * d_flags              device uint32 or NULL. SWRT_FLAG_BAD_LENGTHS when
+ *                      Lp < 0, Lp > C or E != max(0, Lp + S - C): that batch
+ *                      entry is left untouched (cache and staging).
+ * Limits: batch * kv_heads * 2 slices and (capacity + seq_len) * head_dim *
+ * elem_bits / 128 vectors per slice must each stay below 2^31.
+ */
+int swrt_kv_window_append(void *k_cache, void *v_cache, const void *k_new,
+                          const void *v_new, const int64_t *new_strides,
+                          void *k_staging, void *v_staging,
+                          const int32_t *cache_past_lens,
+                          const int32_t *evict_counts, int batch, int kv_heads,
+                          int capacity, int seq_len, int head_dim,
+                          int elem_bits, unsigned phase, uint32_t *d_flags,
+                          void *stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char *swrt_status_string(int status);
+
+/* SWRT_ABI_VERSION of the built library. */
+int swrt_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWRT_H */

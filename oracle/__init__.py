@@ -1,0 +1,185 @@
+"""Plain CPU oracle for the sliding-window KV-cache update path.
+
+TEST INFRASTRUCTURE ONLY. The test suite, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` are the only code allowed to import this
+package. The product package never imports it, and this package imports
+nothing from the product package.
+
+The arithmetic lives in ``swrt_oracle.c`` (plain C, scalar loops, one memcpy per
+row); this module only compiles it with gcc and marshals numpy buffers through
+ctypes. Page citations are in that file's header.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(HERE, "swrt_oracle.c")
+LIBRARY = os.path.join(HERE, "libswrt_oracle.so")
+
+OK = 0
+E_INVALID_ARG = 1
+E_UNSUPPORTED = 2
+FLAG_LINEAR_OOB = 1
+FLAG_BAD_SEQLEN = 2
+FLAG_BAD_LENGTHS = 4
+MODE_LINEAR = 0
+MODE_CIRCULAR = 1
+PHASE_STAGE = 1
+PHASE_COMMIT = 2
+PHASE_ALL = 3
+
+
+def build(source: str = SOURCE, out: str = LIBRARY, extra: tuple = ()) -> str:
+    """Compile the oracle with gcc into a shared library and return its path."""
+    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-Werror", "-shared", "-fPIC",
+           *extra, source, "-o", out]
+    subprocess.run(cmd, check=True, cwd=HERE)
+    return out
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+@dataclass
+class Lengths:
+    total: np.ndarray        # T, int64
+    past: np.ndarray         # P, int64
+    cache_past: np.ndarray   # Lp, int32
+    cache_total: np.ndarray  # L, int32
+    evict: np.ndarray        # E, int32
+    flags: int
+
+
+class Oracle:
+    """ctypes view of one build of the oracle library."""
+
+    def __init__(self, path: str = LIBRARY):
+        if not os.path.exists(path):
+            build(out=path)
+        self.path = path
+        lib = ctypes.CDLL(path)
+        vp, i64, i32, u32p = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.POINTER(ctypes.c_uint32)
+        lib.orc_tensor_scatter.argtypes = [vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, u32p]
+        lib.orc_tensor_scatter.restype = ctypes.c_int
+        lib.orc_kv_seq_lengths.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp, u32p]
+        lib.orc_kv_seq_lengths.restype = ctypes.c_int
+        lib.orc_kv_window_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                             i64, i64, i64, i64, i64, i32, ctypes.c_uint, u32p]
+        lib.orc_kv_window_append.restype = ctypes.c_int
+        self.lib = lib
+
+    # -- TensorScatter ----------------------------------------------------
+    def tensor_scatter_raw(self, present, past, update, write_indices, shape, axis,
+                           seq_len, mode, elem_bits):
+        """Byte-level call. Buffers are C-contiguous numpy arrays (any dtype);
+        ``shape`` is the logical shape of past. Returns (status, flags)."""
+        shp = np.ascontiguousarray(np.asarray(shape, dtype=np.int64))
+        wi = None if write_indices is None else np.ascontiguousarray(write_indices, dtype=np.int64)
+        flags = ctypes.c_uint32(0)
+        st = self.lib.orc_tensor_scatter(_ptr(present), _ptr(past), _ptr(update), _ptr(wi),
+                                         _ptr(shp), len(shape), axis, seq_len, mode, elem_bits,
+                                         ctypes.byref(flags))
+        return st, flags.value
+
+    def tensor_scatter(self, past: np.ndarray, update: np.ndarray, write_indices=None,
+                       axis: int = -2, mode: str = "linear", in_place: bool = False,
+                       elem_bits: int | None = None):
+        """present = TensorScatter(past, update, write_indices). Returns (present, flags).
+        With in_place=True, ``past`` itself is updated and returned."""
+        past = np.ascontiguousarray(past) if not in_place else past
+        assert past.flags.c_contiguous
+        update = np.ascontiguousarray(update)
+        ax = axis + past.ndim if axis < 0 else axis
+        seq_len = update.shape[ax] if update.ndim == past.ndim else 0
+        present = past if in_place else np.empty_like(past)
+        bits = elem_bits or past.dtype.itemsize * 8
+        st, flags = self.tensor_scatter_raw(present, past, update, write_indices, past.shape,
+                                            axis, seq_len,
+                                            MODE_CIRCULAR if mode == "circular" else MODE_LINEAR,
+                                            bits)
+        if st != OK:
+            raise OracleError(f"orc_tensor_scatter status {st}")
+        return present, flags
+
+    # -- lengths ----------------------------------------------------------
+    def kv_seq_lengths(self, seqlens_k, seq_len: int, capacity: int) -> Lengths:
+        sk = np.ascontiguousarray(seqlens_k, dtype=np.int32)
+        B = sk.shape[0]
+        T = np.zeros(B, np.int64)
+        P = np.zeros(B, np.int64)
+        Lp = np.zeros(B, np.int32)
+        L = np.zeros(B, np.int32)
+        E = np.zeros(B, np.int32)
+        flags = ctypes.c_uint32(0)
+        st = self.lib.orc_kv_seq_lengths(_ptr(sk), B, seq_len, capacity, _ptr(T), _ptr(P),
+                                         _ptr(Lp), _ptr(L), _ptr(E), ctypes.byref(flags))
+        if st != OK:
+            raise OracleError(f"orc_kv_seq_lengths status {st}")
+        return Lengths(T, P, Lp, L, E, flags.value)
+
+    def kv_seq_lengths_status(self, seqlens_k, seq_len, capacity) -> int:
+        sk = np.ascontiguousarray(seqlens_k, dtype=np.int32)
+        B = sk.shape[0]
+        out = [np.zeros(B, t) for t in (np.int64, np.int64, np.int32, np.int32, np.int32)]
+        flags = ctypes.c_uint32(0)
+        return self.lib.orc_kv_seq_lengths(_ptr(sk), B, seq_len, capacity,
+                                           *[_ptr(o) for o in out], ctypes.byref(flags))
+
+    # -- windowed step ----------------------------------------------------
+    def kv_window_append(self, k_cache, v_cache, k_new, v_new, cache_past_lens, evict_counts,
+                         k_staging=None, v_staging=None, phase: int = PHASE_ALL,
+                         elem_bits: int | None = None):
+        """In-place windowed step on numpy buffers: caches [B,H,C,D], new rows
+        [B,H,S,D], staging [B,H,C+S,D] (S > 1). Returns the flags."""
+        B, H, C, D = k_cache.shape
+        S = k_new.shape[2]
+        return self.kv_window_append_strided(k_cache, v_cache, np.ascontiguousarray(k_new),
+                                             np.ascontiguousarray(v_new), (H * S * D, S * D, D),
+                                             S, cache_past_lens, evict_counts, k_staging,
+                                             v_staging, phase, elem_bits)
+
+    def kv_window_append_strided(self, k_cache, v_cache, k_new, v_new, new_strides, seq_len,
+                                 cache_past_lens, evict_counts, k_staging=None,
+                                 v_staging=None, phase: int = PHASE_ALL,
+                                 elem_bits: int | None = None, head_dim: int | None = None):
+        B, H, C = k_cache.shape[:3]
+        D = head_dim if head_dim is not None else k_cache.shape[3]
+        bits = elem_bits or k_cache.dtype.itemsize * 8
+        ns = np.ascontiguousarray(np.asarray(new_strides, dtype=np.int64))
+        lp = np.ascontiguousarray(cache_past_lens, dtype=np.int32)
+        ev = np.ascontiguousarray(evict_counts, dtype=np.int32)
+        flags = ctypes.c_uint32(0)
+        st = self.lib.orc_kv_window_append(_ptr(k_cache), _ptr(v_cache), _ptr(k_new),
+                                           _ptr(v_new), _ptr(ns), _ptr(k_staging),
+                                           _ptr(v_staging), _ptr(lp), _ptr(ev), B, H, C,
+                                           seq_len, D, bits, phase, ctypes.byref(flags))
+        if st != OK:
+            raise OracleError(f"orc_kv_window_append status {st}")
+        return flags.value
+
+
+_default: Oracle | None = None
+
+
+def get() -> Oracle:
+    """The oracle built from ``swrt_oracle.c`` in this directory (built on first use)."""
+    global _default
+    if _default is None:
+        if (not os.path.exists(LIBRARY)
+                or os.path.getmtime(LIBRARY) < os.path.getmtime(SOURCE)):
+            build()
+        _default = Oracle(LIBRARY)
+    return _default

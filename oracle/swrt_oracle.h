@@ -1,0 +1,96 @@
+/*
+ * swrt_oracle.h -- plain CPU oracle for the sliding-window KV-cache update path.
+ *
+ * TEST INFRASTRUCTURE ONLY. The test suite, the package smoke check and the
+ * benchmark's CPU-baseline leg are the only users of this library. The GPU
+ * product path never includes this header, links this library or calls it, and
+ * this code includes nothing from the GPU path: the two share no header, helper,
+ * constant or table. The status and flag values below are written out here on
+ * their own; the tests compare them with the product library's values.
+ *
+ * Sources (pages, by title and section):
+ *   [TS]  ONNX operator "TensorScatter" (domain ai.onnx, since version 24):
+ *         description, pseudocode, Inputs, Outputs, Attributes, Type Constraints.
+ *   [RB]  Core AI model zoo, "Stateful decode & KV cache", section
+ *         "Sliding-window ring buffer (long-context memory)".
+ *   [GQA] onnxruntime pull request "GQA support sliding_window_cache" (#29904):
+ *         section "Design" (the invariant and the append formulas, and the two
+ *         details that follow them), and the follow-up commit that widens the
+ *         end-pointer arithmetic to 64 bits and clamps the past length at zero.
+ *
+ * Every function is a plain definition: scalar loops, one memcpy per row, no
+ * blocking, no vector code, no threads.
+ */
+#ifndef SWRT_ORACLE_H
+#define SWRT_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* synchronous status codes */
+#define ORC_OK 0
+#define ORC_E_INVALID_ARG 1
+#define ORC_E_UNSUPPORTED 2
+
+/* per-call data flags (OR-ed into *flags) */
+#define ORC_FLAG_LINEAR_OOB 1u  /* a linear write index left [0, M-S]; batch skipped */
+#define ORC_FLAG_BAD_SEQLEN 2u  /* seqlens_k[b] < 0 or total length < S; clamped   */
+#define ORC_FLAG_BAD_LENGTHS 4u /* (Lp, E) inconsistent with (C, S); batch skipped */
+
+/* TensorScatter "mode" attribute */
+#define ORC_MODE_LINEAR 0
+#define ORC_MODE_CIRCULAR 1
+
+/* phases of a multi-token windowed step */
+#define ORC_PHASE_STAGE 1u
+#define ORC_PHASE_COMMIT 2u
+#define ORC_PHASE_ALL 3u
+
+#define ORC_MAX_RANK 8
+
+/*
+ * [TS] present = TensorScatter(past, update, write_indices; axis, mode).
+ * shape: host array of `rank` dims of past (update has seq_len on `axis`).
+ * write_indices: host int64[shape[0]] or NULL (all zeros).
+ * present may equal past (in place); otherwise present first gets past's bytes.
+ * elem_bits in {4, 8, 16, 32, 64, 128}; 4-bit needs an even row length.
+ */
+int orc_tensor_scatter(void *present, const void *past, const void *update,
+                       const int64_t *write_indices, const int64_t *shape,
+                       int rank, int axis, int64_t seq_len, int mode,
+                       int elem_bits, uint32_t *flags);
+
+/*
+ * [GQA] lengths of one windowed step, for every batch entry.
+ * T = seqlens_k + 1, P = max(0, T - S), Lp = min(P, C),
+ * E = max(0, Lp + S - C), L = Lp + S - E  (all in 64-bit arithmetic).
+ * total_lens, past_lens, cache_total_lens may be NULL.
+ */
+int orc_kv_seq_lengths(const int32_t *seqlens_k, int64_t batch, int64_t seq_len,
+                       int64_t capacity, int64_t *total_lens, int64_t *past_lens,
+                       int32_t *cache_past_lens, int32_t *cache_total_lens,
+                       int32_t *evict_counts, uint32_t *flags);
+
+/*
+ * [GQA] one windowed cache step for K and V.
+ * caches [B, H, C, D]; new rows addressed by new_strides (elements) for b, h, s
+ * with D contiguous; staging [B, H, C+S, D] (needed iff S > 1).
+ * S == 1: in place, shift then append. S > 1: STAGE and/or COMMIT.
+ */
+int orc_kv_window_append(void *k_cache, void *v_cache, const void *k_new,
+                         const void *v_new, const int64_t *new_strides,
+                         void *k_staging, void *v_staging,
+                         const int32_t *cache_past_lens,
+                         const int32_t *evict_counts, int64_t batch,
+                         int64_t kv_heads, int64_t capacity, int64_t seq_len,
+                         int64_t head_dim, int elem_bits, unsigned phase,
+                         uint32_t *flags);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWRT_ORACLE_H */

@@ -1,0 +1,240 @@
+"""Seeded synthetic inputs for the five KV-cache update workloads.
+
+This module only draws inputs: shapes, seeded random payloads, write indices
+and lengths. It holds none of the update arithmetic, so both the GPU path's
+tests and the CPU oracle's checks can take their inputs from it.
+
+Recipe (shared by tests and benchmark):
+  - index and length draws: numpy Generator(PCG64(seed)), seed = workload number;
+  - payloads: U[-1, 1) fp32 rounded to the payload dtype by torch (round to
+    nearest even), or uniform random bytes for the raw-bits variants (every
+    NaN / Inf / fp8 encoding appears). Small payloads are drawn on the host
+    from the same PCG64 stream; large ones on their device with a torch
+    generator seeded from (seed, buffer id), since a 12 GiB host draw would
+    dominate every run.
+
+Workloads (sizes and distributions):
+  1  TensorScatter linear, fp32 past [2,2,16,8], update [2,2,3,8],
+     write_indices ~ U{0..13}, axis -2.
+  2  TensorScatter circular, bf16 cache [8,8,4096,128]; step A update S=1,
+     step B update S=512, each with its own write_indices ~ U{0..4095}.
+  3  windowed decode S=1, K/V bf16 [32,8,128,64], seqlens_k ~ U{1..8192}.
+  4  windowed step S=256 through staging, K/V bf16 [4,8,4096,128], past
+     length P ~ U{0..16384}, seqlens_k = P + 255.
+  5  whole-model decode step: 24 layers, even layers windowed (K/V [64,8,128,64])
+     and odd layers full linear TensorScatter caches (K/V [64,8,8192,64]); new
+     rows [64,8,1,64]; total length T ~ U{1..8192} shared by all layers;
+     windowed seqlens_k = T - 1, full write index T - 1; bf16 or fp8 e4m3fn.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+DTYPES = {
+    "fp32": torch.float32,
+    "bf16": torch.bfloat16,
+    "fp16": torch.float16,
+    "fp8_e4m3fn": torch.float8_e4m3fn,
+    "fp8_e5m2": torch.float8_e5m2,
+    "fp64": torch.float64,
+    "int8": torch.int8,
+    "uint8": torch.uint8,
+    "int16": torch.int16,
+    "int32": torch.int32,
+    "int64": torch.int64,
+    "bool": torch.bool,
+    "complex64": torch.complex64,
+    "complex128": torch.complex128,
+}
+
+_FLOATS = (torch.float32, torch.bfloat16, torch.float16, torch.float8_e4m3fn,
+           torch.float8_e5m2, torch.float64)
+
+
+def rng(seed: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def host_payload(g: np.random.Generator, shape, dtype: torch.dtype,
+                 raw_bits: bool = False) -> torch.Tensor:
+    """Host tensor of `shape`: U[-1,1) rounded to `dtype`, or random bytes."""
+    n = int(np.prod(shape)) if len(shape) else 1
+    if raw_bits or dtype not in _FLOATS:
+        nbytes = n * torch.empty((), dtype=dtype).element_size()
+        raw = torch.from_numpy(g.integers(0, 256, size=nbytes, dtype=np.uint8))
+        if dtype == torch.bool:
+            raw = raw & 1  # a bool byte must hold 0 or 1
+        return raw.view(dtype).reshape(shape).clone()
+    vals = torch.from_numpy(g.uniform(-1.0, 1.0, size=n).astype(np.float32))
+    if dtype == torch.float64:
+        vals = torch.from_numpy(g.uniform(-1.0, 1.0, size=n))
+    return vals.to(dtype).reshape(shape)
+
+
+def device_payload(shape, dtype: torch.dtype, seed: int, buffer_id: int,
+                   device, raw_bits: bool = False) -> torch.Tensor:
+    """Payload drawn on `device` with a torch generator seeded by (seed, buffer_id)."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed * 1_000_003 + buffer_id)
+    elem = torch.empty((), dtype=dtype).element_size()
+    if raw_bits or dtype not in _FLOATS:
+        n = int(np.prod(shape)) * elem
+        raw = torch.randint(0, 256, (n,), dtype=torch.uint8, generator=gen, device=device)
+        if dtype == torch.bool:
+            raw &= 1
+        return raw.view(dtype).reshape(shape)
+    out = torch.empty(shape, dtype=dtype, device=device)
+    flat = out.view(-1)
+    step = 1 << 26
+    for i in range(0, flat.numel(), step):  # bounded fp32 temporaries
+        m = min(step, flat.numel() - i)
+        tmp = torch.rand(m, generator=gen, device=device, dtype=torch.float32)
+        flat[i:i + m] = (tmp * 2.0 - 1.0).to(dtype)
+    return out
+
+
+# --------------------------------------------------------------------------
+# workload descriptions (host draws of everything except large payloads)
+# --------------------------------------------------------------------------
+
+@dataclass
+class ScatterCase:
+    name: str
+    shape: tuple            # past / present shape
+    seq_len: int            # S (update's size on axis)
+    axis: int
+    mode: str               # "linear" | "circular"
+    dtype: torch.dtype
+    write_indices: np.ndarray | None  # int64 [shape[0]] or None
+    seed: int
+    buffer_id: int = 0
+
+    @property
+    def update_shape(self):
+        s = list(self.shape)
+        s[self.axis] = self.seq_len
+        return tuple(s)
+
+
+@dataclass
+class WindowCase:
+    name: str
+    batch: int
+    kv_heads: int
+    capacity: int
+    seq_len: int
+    head_dim: int
+    dtype: torch.dtype
+    seqlens_k: np.ndarray   # int32 [batch]
+    seed: int
+    buffer_id: int = 0
+
+
+@dataclass
+class ModelStep:
+    """Workload 5: windowed layers (even) and full TensorScatter layers (odd)."""
+    layers: int
+    batch: int
+    kv_heads: int
+    head_dim: int
+    window: int
+    max_seq: int
+    dtype: torch.dtype
+    total_lens: np.ndarray          # T, int64 [batch]
+    seqlens_k: np.ndarray           # T - 1, int32 [batch]
+    write_indices: np.ndarray       # T - 1, int64 [batch]
+    seed: int
+    windowed_layers: list = field(default_factory=list)
+    full_layers: list = field(default_factory=list)
+
+
+def workload1() -> ScatterCase:
+    g = rng(1)
+    w = g.integers(0, 13, endpoint=True, size=2).astype(np.int64)
+    return ScatterCase("tensor_scatter_linear_fp32_2x2x16x8_s3", (2, 2, 16, 8), 3, 2,
+                       "linear", torch.float32, w, seed=1)
+
+
+def payload(shape, dtype: torch.dtype, seed: int, buffer_id: int, device="cpu",
+            raw_bits: bool = False) -> torch.Tensor:
+    """Payload for buffer `buffer_id` of workload `seed`: drawn on the host from
+    PCG64(seed * 1000 + buffer_id) when device is the CPU, else on the device."""
+    if torch.device(device).type == "cpu":
+        return host_payload(rng(seed * 1000 + buffer_id), shape, dtype, raw_bits)
+    return device_payload(shape, dtype, seed, buffer_id, device, raw_bits)
+
+
+def scatter_payloads(case: ScatterCase, device="cpu", raw_bits: bool = False):
+    """(past, update) of a TensorScatter case."""
+    past = payload(case.shape, case.dtype, case.seed, 10 * case.buffer_id, device, raw_bits)
+    upd = payload(case.update_shape, case.dtype, case.seed, 10 * case.buffer_id + 1, device,
+                  raw_bits)
+    return past, upd
+
+
+def window_payloads(case: WindowCase, device="cpu", raw_bits: bool = False,
+                    staging: bool = False):
+    """(k_cache, v_cache, k_new, v_new[, k_staging, v_staging]) of a windowed case."""
+    B, H, C, S, D = case.batch, case.kv_heads, case.capacity, case.seq_len, case.head_dim
+    base = 10 * case.buffer_id
+    out = [payload((B, H, C, D), case.dtype, case.seed, base + 0, device, raw_bits),
+           payload((B, H, C, D), case.dtype, case.seed, base + 1, device, raw_bits),
+           payload((B, H, S, D), case.dtype, case.seed, base + 2, device, raw_bits),
+           payload((B, H, S, D), case.dtype, case.seed, base + 3, device, raw_bits)]
+    if staging:
+        out += [payload((B, H, C + S, D), case.dtype, case.seed, base + 4, device, raw_bits),
+                payload((B, H, C + S, D), case.dtype, case.seed, base + 5, device, raw_bits)]
+    return tuple(out)
+
+
+def workload2() -> tuple[ScatterCase, ScatterCase]:
+    g = rng(2)
+    wa = g.integers(0, 4096, size=8).astype(np.int64)
+    wb = g.integers(0, 4096, size=8).astype(np.int64)
+    shape = (8, 8, 4096, 128)
+    a = ScatterCase("tensor_scatter_circular_bf16_8x8x4096x128_s1", shape, 1, 2,
+                    "circular", torch.bfloat16, wa, seed=2, buffer_id=1)
+    b = ScatterCase("tensor_scatter_circular_bf16_8x8x4096x128_s512", shape, 512, 2,
+                    "circular", torch.bfloat16, wb, seed=2, buffer_id=2)
+    return a, b
+
+
+def workload3() -> WindowCase:
+    g = rng(3)
+    sk = g.integers(1, 8192, endpoint=True, size=32).astype(np.int32)
+    return WindowCase("window_decode_bf16_32x8x128x64_s1", 32, 8, 128, 1, 64,
+                      torch.bfloat16, sk, seed=3)
+
+
+def workload4() -> tuple[WindowCase, np.ndarray]:
+    g = rng(4)
+    past = g.integers(0, 16384, endpoint=True, size=4).astype(np.int64)
+    sk = (past + 255).astype(np.int32)
+    return (WindowCase("window_stage_bf16_4x8x4096x128_s256", 4, 8, 4096, 256, 128,
+                       torch.bfloat16, sk, seed=4), past)
+
+
+def workload5(dtype: torch.dtype = torch.bfloat16) -> ModelStep:
+    g = rng(5)
+    T = g.integers(1, 8192, endpoint=True, size=64).astype(np.int64)
+    step = ModelStep(layers=24, batch=64, kv_heads=8, head_dim=64, window=128, max_seq=8192,
+                     dtype=dtype, total_lens=T, seqlens_k=(T - 1).astype(np.int32),
+                     write_indices=(T - 1).astype(np.int64), seed=5)
+    step.windowed_layers = [i for i in range(24) if i % 2 == 0]
+    step.full_layers = [i for i in range(24) if i % 2 == 1]
+    return step
+
+
+def stratified_seqlens(g: np.random.Generator, batch: int, capacity: int, seq_len: int,
+                       hi: int = 8192) -> np.ndarray:
+    """seqlens_k with both regimes forced: half the entries leave the window
+    partly filled (total length <= capacity), half make it full."""
+    lo_part = g.integers(seq_len - 1, max(seq_len - 1, capacity - 1), endpoint=True,
+                         size=batch // 2)
+    hi_part = g.integers(capacity, hi, endpoint=True, size=batch - batch // 2)
+    sk = np.concatenate([lo_part, hi_part])
+    g.shuffle(sk)
+    return sk.astype(np.int32)

@@ -1,0 +1,113 @@
+"""The oracle's pins must catch plausible mistakes.
+
+Each mutant below is a copy of oracle/swrt_oracle.c with one planted mistake
+(an index off by one, a dropped term, a wrong sign, a transposed operand, a
+step done in the wrong order, a check weakened). The mutant is compiled with
+gcc and the whole pin suite (tests/test_oracle_pins.py) runs against it in its
+own process; the suite must fail for every mutant. A mutant that crashes its
+process counts as caught. Everything runs on the CPU.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+MUTANTS = {
+    "linear_index_off_by_one": ("j = w + s;", "j = w + s + 1;"),
+    "circular_wrong_sign": ("j = floor_mod(floor_mod(w, M) + s, M);",
+                            "j = floor_mod(floor_mod(w, M) - s, M);"),
+    "modulo_truncates": ("return r < 0 ? r + m : r;", "return r < 0 ? -r : r;"),
+    "linear_bound_drops_S": ("(w < 0 || w > M - S)", "(w < 0 || w > M - 1)"),
+    "batch_from_last_prefix_dim": ("const int64_t batch_idx = idx[0];",
+                                   "const int64_t batch_idx = idx[axis - 1];"),
+    "out_of_place_copy_dropped": ("if (present != past && total > 0)",
+                                  "if (0 && present != past && total > 0)"),
+    "update_rows_reversed": ("(const char *)update + (o * S + s) * row_bytes",
+                             "(const char *)update + (o * S + (S - 1 - s)) * row_bytes"),
+    "linear_oob_not_flagged": ("set_flag(flags, ORC_FLAG_LINEAR_OOB);", "(void)0;"),
+    "total_without_plus_one": ("(int64_t)seqlens_k[b] + 1;", "(int64_t)seqlens_k[b];"),
+    "total_narrowed_to_32_bits": ("(int64_t)seqlens_k[b] + 1;",
+                                  "(int64_t)(int32_t)((uint32_t)seqlens_k[b] + 1u);"),
+    "past_minus_one_not_S": ("P = T - S; /*", "P = T - 1; /*"),
+    "past_not_clamped": ("if (P < 0)\n            P = 0;", "if (P < -(1LL << 40))\n            P = 0;"),
+    "resident_off_by_one": ("Lp = P < C ? P : C;", "Lp = P < C ? P : C - 1;"),
+    "evict_off_by_one": ("E = Lp + S - C;", "E = Lp + S - C - 1;"),
+    "resident_after_drops_E": ("L = Lp + S - E;      /*", "L = Lp + S;      /*"),
+    "shift_source_not_offset": ("copy_row(tmp + (r - E) * row_bytes, cache + r * row_bytes,",
+                                "copy_row(tmp + (r - E) * row_bytes, cache + (r - E) * row_bytes,"),
+    "k_and_v_swapped": ("news[0] = (const char *)k_new;\n    news[1] = (const char *)v_new;",
+                        "news[0] = (const char *)v_new;\n    news[1] = (const char *)k_new;"),
+    "staged_new_rows_reversed": ("copy_row(stage + (Lp + s) * row_bytes,\n"
+                                 "                                     nw + s * nb_stride[2],",
+                                 "copy_row(stage + (Lp + s) * row_bytes,\n"
+                                 "                                     nw + (S - 1 - s) * nb_stride[2],"),
+    "commit_ignores_evictions": ("stage + (E + r) * row_bytes", "stage + r * row_bytes"),
+    "new_strides_transposed": ("b * nb_stride[0] + h * nb_stride[1]",
+                               "b * nb_stride[1] + h * nb_stride[0]"),
+    "staging_slice_stride_C": ("(b * H + h) * (C + S) * row_bytes", "(b * H + h) * C * row_bytes"),
+    "length_check_weakened": ("E != E_expected", "E < 0"),
+}
+
+# write before shift (the opposite of the order the step formulas list)
+_SHIFT_THEN_WRITE = """                    for (int64_t r = E; r < Lp; ++r)
+                        copy_row(tmp + (r - E) * row_bytes, cache + r * row_bytes,
+                                 row_bytes);
+                    for (int64_t r = 0; r < Lp - E; ++r)
+                        copy_row(cache + r * row_bytes, tmp + r * row_bytes,
+                                 row_bytes);
+                    /* write: new tokens -> cache[Lp-E .. Lp-E+S) */
+                    for (int64_t s = 0; s < S; ++s)
+                        copy_row(cache + (Lp - E + s) * row_bytes,
+                                 nw + s * nb_stride[2], row_bytes);
+"""
+_WRITE_THEN_SHIFT = """                    for (int64_t s = 0; s < S; ++s)
+                        copy_row(cache + (Lp - E + s) * row_bytes,
+                                 nw + s * nb_stride[2], row_bytes);
+                    for (int64_t r = E; r < Lp; ++r)
+                        copy_row(tmp + (r - E) * row_bytes, cache + r * row_bytes,
+                                 row_bytes);
+                    for (int64_t r = 0; r < Lp - E; ++r)
+                        copy_row(cache + r * row_bytes, tmp + r * row_bytes,
+                                 row_bytes);
+"""
+MUTANTS["write_before_shift"] = (_SHIFT_THEN_WRITE, _WRITE_THEN_SHIFT)
+
+
+def _run_pins(lib: str) -> subprocess.CompletedProcess:
+    env = dict(os.environ, SWRT_ORACLE_LIB=lib, PYTHONDONTWRITEBYTECODE="1")
+    return subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                           os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                          cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+
+
+def test_every_mutant_fails_the_pins(tmp_path):
+    src = open(oracle.SOURCE).read()
+    builds = {}
+    for name, (old, new) in MUTANTS.items():
+        assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+        path = tmp_path / f"{name}.c"
+        path.write_text(src.replace(old, new))
+        lib = str(tmp_path / f"lib_{name}.so")
+        subprocess.run(["gcc", "-O1", "-std=c11", "-shared", "-fPIC",
+                        f"-I{os.path.dirname(oracle.SOURCE)}", str(path), "-o", lib],
+                       check=True, capture_output=True)
+        builds[name] = lib
+    with ThreadPoolExecutor(max_workers=4) as ex:
+        results = dict(zip(builds, ex.map(_run_pins, builds.values())))
+    survivors = [n for n, r in results.items() if r.returncode == 0]
+    assert not survivors, f"mutants not caught by the pins: {survivors}"
+
+
+def test_unmutated_oracle_passes_the_pins(tmp_path):
+    lib = str(tmp_path / "lib_clean.so")
+    oracle.build(out=lib)
+    r = _run_pins(lib)
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]

@@ -1,0 +1,459 @@
+"""Pins of the CPU oracle to facts fixed by the pages and by mathematics.
+
+None of these checks re-types the oracle's formulas. They use:
+  - the three worked examples printed on the ONNX operator page "TensorScatter"
+    (Examples section), stored under tests/golden/;
+  - a brute force that follows that page's pseudocode literally (np.ndindex
+    over the prefix, np.mod over the whole index tuple) on tiny inputs;
+  - the ring-buffer rule of the Core AI model zoo page "Stateful decode & KV
+    cache" (section "Sliding-window ring buffer"): the token at position p
+    goes to slot p mod W, checked by searching the write history;
+  - the invariant of the pull request "GQA support sliding_window_cache"
+    (section "Design"): after every step the cache holds the L = min(T, C)
+    most recent tokens at rows [0, L), checked by replaying tagged token
+    histories, and the statement that results match a full-length cache
+    before anything is evicted;
+  - the CPU follow-up's figure of 0.50 MiB moved per decode token at
+    C = W = 128, 8 KV heads of 64, fp32 (section "Thread-pool parallel
+    MoveKvCacheRows");
+  - hand-worked lengths at edge values, including the 32-bit overflow case of
+    the follow-up that widens the end-pointer arithmetic.
+
+SWRT_ORACLE_LIB may name another build of the oracle (the mutation test uses
+this to check that planted mistakes fail here).
+"""
+from __future__ import annotations
+
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from tests import replay
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+@pytest.fixture(scope="module")
+def orc() -> oracle.Oracle:
+    path = os.environ.get("SWRT_ORACLE_LIB")
+    return oracle.Oracle(path) if path else oracle.get()
+
+
+# --------------------------------------------------------------------------
+# TensorScatter: the page's worked examples
+# --------------------------------------------------------------------------
+
+def _examples():
+    with open(os.path.join(HERE, "golden", "tensorscatter_examples.json")) as f:
+        return json.load(f)["examples"]
+
+
+@pytest.mark.parametrize("ex", _examples(), ids=lambda e: e["name"])
+@pytest.mark.parametrize("in_place", [False, True])
+def test_tensorscatter_page_examples(orc, ex, in_place):
+    past = np.array(ex["past_cache"]["values"], dtype=np.float32)
+    upd = np.array(ex["update"]["values"], dtype=np.float32)
+    wi = np.array(ex["write_indices"]["values"], dtype=np.int64)
+    want = np.array(ex["present_cache"]["values"], dtype=np.float32)
+    assert list(past.shape) == ex["past_cache"]["shape"]
+    keep = past.copy()
+    got, flags = orc.tensor_scatter(past, upd, wi, axis=ex["axis"], mode=ex["mode"],
+                                    in_place=in_place)
+    assert flags == 0
+    np.testing.assert_array_equal(got, want)
+    if not in_place:
+        np.testing.assert_array_equal(past, keep)  # past is an input, never written
+
+
+# --------------------------------------------------------------------------
+# TensorScatter: literal pseudocode brute force on tiny inputs
+# --------------------------------------------------------------------------
+
+def _pseudocode(past, update, write_indices, axis, mode):
+    """The page's pseudocode, statement by statement (whole-tuple np.mod)."""
+    present = past.copy()
+    max_sequence_length = past.shape[axis]
+    sequence_length = update.shape[axis]
+    for prefix_idx in np.ndindex(past.shape[:axis]):
+        batch_idx = prefix_idx[0]
+        for sequence_idx in range(sequence_length):
+            cache_idx = (*prefix_idx, write_indices[batch_idx] + sequence_idx)
+            if mode == "circular":
+                cache_idx = tuple(np.mod(np.asarray(cache_idx), max_sequence_length))
+            update_idx = (*prefix_idx, sequence_idx)
+            present[cache_idx] = update[update_idx]
+    return present
+
+
+_TINY_SHAPES = [  # prefix dims stay below M, where the whole-tuple modulo is the
+    (2, 5, 3),    # sequence-index modulo (the oracle's reading)
+    (3, 2, 6, 2),
+    (2, 3, 5, 1),
+    (2, 2, 2, 7, 3),
+    (2, 4, 2),
+]
+
+
+@pytest.mark.parametrize("shape", _TINY_SHAPES, ids=str)
+@pytest.mark.parametrize("dtype", [np.int8, np.int16, np.float32, np.float64, np.complex128])
+def test_tensorscatter_pseudocode_bruteforce(orc, shape, dtype):
+    g = np.random.default_rng(7)
+    rank = len(shape)
+    for axis in range(1, rank):
+        M = shape[axis]
+        if any(d >= M for d in shape[:axis]):
+            continue
+        for S in range(0, M + 1):
+            ushape = list(shape)
+            ushape[axis] = S
+            past = (g.integers(-100, 100, size=shape)).astype(dtype)
+            upd = (g.integers(-100, 100, size=ushape) + 1000).astype(dtype)
+            B = shape[0]
+            ax_arg = axis - rank if axis == rank - 2 and g.integers(2) else axis
+            # circular: every start, including negative ones and several laps
+            for w0 in range(-M - 1, 2 * M + 2):
+                wi = np.array([(w0 + 3 * b) for b in range(B)], dtype=np.int64)
+                want = _pseudocode(past, upd, wi, axis, "circular")
+                got, flags = orc.tensor_scatter(past, upd, wi, axis=ax_arg, mode="circular")
+                assert flags == 0
+                np.testing.assert_array_equal(got, want, err_msg=f"circ {shape} ax{axis} S{S} w{wi}")
+            # linear: every in-range start
+            for w0 in range(0, M - S + 1):
+                wi = np.array([min(w0 + b, M - S) for b in range(B)], dtype=np.int64)
+                want = _pseudocode(past, upd, wi, axis, "linear")
+                got, flags = orc.tensor_scatter(past, upd, wi, axis=ax_arg, mode="linear")
+                assert flags == 0
+                np.testing.assert_array_equal(got, want)
+            # no write_indices: zeros
+            want = _pseudocode(past, upd, np.zeros(B, np.int64), axis, "linear")
+            got, _ = orc.tensor_scatter(past, upd, None, axis=ax_arg, mode="linear")
+            np.testing.assert_array_equal(got, want)
+
+
+def test_tensorscatter_linear_out_of_range_skips_batch(orc):
+    """A linear write index outside [0, M-S] is flagged; that batch entry keeps
+    past's rows, the others are written."""
+    g = np.random.default_rng(3)
+    past = g.integers(0, 50, size=(4, 3, 8, 2)).astype(np.int32)
+    upd = g.integers(100, 150, size=(4, 3, 3, 2)).astype(np.int32)
+    for bad in (-1, 6, 7, 1 << 62, -(1 << 62)):
+        wi = np.array([0, bad, 5, 2], dtype=np.int64)
+        got, flags = orc.tensor_scatter(past, upd, wi, axis=2, mode="linear")
+        assert flags == oracle.FLAG_LINEAR_OOB
+        np.testing.assert_array_equal(got[1], past[1])
+        ok = wi.copy()
+        ok[1] = 0
+        want = _pseudocode(past, upd, ok, 2, "linear")
+        for b in (0, 2, 3):
+            np.testing.assert_array_equal(got[b], want[b])
+
+
+def test_tensorscatter_huge_circular_index(orc):
+    """Circular indices far beyond M (and negative) reduce modulo M."""
+    past = np.arange(2 * 5 * 2, dtype=np.int64).reshape(2, 5, 2)
+    upd = -np.arange(2 * 3 * 2, dtype=np.int64).reshape(2, 3, 2) - 1
+    big = (1 << 62) + 3  # = 3 + 2^62; 2^62 mod 5 = 4 -> 7 mod 5 = 2
+    wi = np.array([big, -(1 << 62)], dtype=np.int64)  # -(2^62) mod 5 = 1
+    got, _ = orc.tensor_scatter(past, upd, wi, axis=1, mode="circular")
+    want = past.copy()
+    for s in range(3):
+        want[0, (2 + s) % 5] = upd[0, s]
+        want[1, (1 + s) % 5] = upd[1, s]
+    np.testing.assert_array_equal(got, want)
+
+
+def test_tensorscatter_rejects_bad_arguments(orc):
+    past = np.zeros((2, 4, 3), np.float32)
+    upd = np.zeros((2, 2, 3), np.float32)
+    pres = np.zeros_like(past)
+    for axis in (0, 3, -3, 5):  # the batch axis and out-of-range axes
+        st, _ = orc.tensor_scatter_raw(pres, past, upd, None, past.shape, axis, 2, 0, 32)
+        assert st == oracle.E_INVALID_ARG
+    st, _ = orc.tensor_scatter_raw(pres, past, upd, None, past.shape, 1, 5, 0, 32)  # S > M
+    assert st == oracle.E_INVALID_ARG
+    st, _ = orc.tensor_scatter_raw(pres, past, upd, None, past.shape, 1, 2, 2, 32)  # mode
+    assert st == oracle.E_INVALID_ARG
+    st, _ = orc.tensor_scatter_raw(pres, past, upd, None, past.shape, 1, 2, 0, 12)  # width
+    assert st == oracle.E_INVALID_ARG
+    st, _ = orc.tensor_scatter_raw(pres, past, upd, None, (2, 4, 3), 1, 2, 0, 4)  # odd 4-bit row
+    assert st == oracle.E_UNSUPPORTED
+
+
+def test_tensorscatter_int4_rows(orc):
+    """4-bit elements: a row of 6 nibbles is 3 bytes; rows move as whole bytes."""
+    g = np.random.default_rng(11)
+    past = g.integers(0, 256, size=(2, 5, 3), dtype=np.uint8)   # logical [2,5,6] int4
+    upd = g.integers(0, 256, size=(2, 2, 3), dtype=np.uint8)    # logical [2,2,6]
+    wi = np.array([4, 1], np.int64)
+    pres = np.empty_like(past)
+    st, flags = orc.tensor_scatter_raw(pres, past, upd, wi, (2, 5, 6), 1, 2, 1, 4)
+    assert st == 0 and flags == 0
+    want = past.copy()
+    want[0, 4], want[0, 0] = upd[0, 0], upd[0, 1]
+    want[1, 1], want[1, 2] = upd[1, 0], upd[1, 1]
+    np.testing.assert_array_equal(pres, want)
+
+
+# --------------------------------------------------------------------------
+# Ring buffer: the token at position p lives in slot p mod W
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("W,chunks", [(8, [1] * 29), (8, [3, 5, 8, 1, 7, 2, 8]),
+                                      (5, [5, 5, 1, 4, 2]), (1, [1] * 4)])
+def test_ring_slot_rule(orc, W, chunks):
+    B, H, D = 3, 2, 4
+    ring = np.concatenate([replay.initial_rows(0, b, h, W, D)[None] for b in range(B)
+                           for h in range(H)]).reshape(B, H, W, D)
+    start = np.array([0, 2, 5])  # each batch entry starts at its own position
+    pos = start.copy()
+    written = [[] for _ in range(B)]
+    for S in chunks:
+        upd = np.empty((B, H, S, D), np.int32)
+        for b in range(B):
+            for h in range(H):
+                upd[b, h] = replay.token_rows(0, b, h, np.arange(pos[b], pos[b] + S), D)
+            written[b] += list(range(pos[b], pos[b] + S))
+        ring, flags = orc.tensor_scatter(ring, upd, pos.astype(np.int64), axis=2,
+                                         mode="circular", in_place=True)
+        assert flags == 0
+        pos += S
+        for b in range(B):
+            for slot in range(W):
+                hits = [p for p in written[b] if p % W == slot]  # search, no formula
+                for h in range(H):
+                    if hits:
+                        want = replay.token_rows(0, b, h, [max(hits)], D)[0]
+                    else:
+                        want = replay.initial_rows(0, b, h, W, D)[slot]
+                    np.testing.assert_array_equal(ring[b, h, slot], want)
+
+
+# --------------------------------------------------------------------------
+# Windowed cache: lengths
+# --------------------------------------------------------------------------
+
+def test_lengths_hand_worked_values(orc):
+    """Values worked out by hand from the definitions (T = seqlens_k + 1)."""
+    C, S = 128, 1
+    cases = {  # seqlens_k: (T, P, Lp, L, E, bad)
+        0: (1, 0, 0, 1, 0, False),
+        126: (127, 126, 126, 127, 0, False),
+        127: (128, 127, 127, 128, 0, False),
+        128: (129, 128, 128, 128, 1, False),
+        5000: (5001, 5000, 128, 128, 1, False),
+        2147483647: (2147483648, 2147483647, 128, 128, 1, False),
+        -1: (0, 0, 0, 1, 0, True),
+        -5: (-4, 0, 0, 1, 0, True),
+        -2147483648: (-2147483647, 0, 0, 1, 0, True),
+    }
+    sk = np.array(list(cases), dtype=np.int32)
+    got = orc.kv_seq_lengths(sk, S, C)
+    for i, k in enumerate(cases):
+        T, P, Lp, L, E, _ = cases[k]
+        assert (got.total[i], got.past[i], got.cache_past[i], got.cache_total[i],
+                got.evict[i]) == (T, P, Lp, L, E), k
+    assert got.flags == oracle.FLAG_BAD_SEQLEN
+    assert orc.kv_seq_lengths(sk[:6], S, C).flags == 0
+
+    # a multi-token step, S = 256, C = 4096
+    cases = {
+        255: (256, 0, 0, 256, 0),        # prompt from zero
+        4095: (4096, 3840, 3840, 4096, 0),  # exactly fills
+        4096: (4097, 3841, 3841, 4096, 1),
+        4351: (4352, 4096, 4096, 4096, 256),
+        20000: (20001, 19745, 4096, 4096, 256),
+    }
+    got = orc.kv_seq_lengths(np.array(list(cases), np.int32), 256, 4096)
+    assert got.flags == 0
+    for i, k in enumerate(cases):
+        assert (got.total[i], got.past[i], got.cache_past[i], got.cache_total[i],
+                got.evict[i]) == cases[k], k
+    # T < S: flagged, past clamped to zero
+    got = orc.kv_seq_lengths(np.array([10], np.int32), 256, 4096)
+    assert got.flags == oracle.FLAG_BAD_SEQLEN
+    assert (got.past[0], got.cache_past[0], got.cache_total[0], got.evict[0]) == (0, 0, 256, 0)
+    # a chunk longer than the capacity: S = 300, C = 100
+    got = orc.kv_seq_lengths(np.array([299, 449], np.int32), 300, 100)
+    assert list(got.cache_past) == [0, 100] and list(got.evict) == [200, 300]
+    assert list(got.cache_total) == [100, 100]
+
+
+def test_lengths_hold_min_T_C_and_conservation(orc):
+    """For every valid total T >= S: L = min(T, C) (the page's invariant) and
+    the step conserves rows: Lp + S = L + E; at most S rows leave."""
+    for C in (1, 2, 7, 128):
+        for S in (1, 2, 5, C, C + 3):
+            T = np.arange(S, S + 3 * C + 10)
+            got = orc.kv_seq_lengths((T - 1).astype(np.int32), S, C)
+            assert got.flags == 0
+            np.testing.assert_array_equal(got.total, T)
+            np.testing.assert_array_equal(got.cache_total, np.minimum(T, C))
+            np.testing.assert_array_equal(got.cache_past + S, got.cache_total + got.evict)
+            assert (got.evict <= S).all() and (got.evict >= 0).all()
+            # the resident rows before the step are those of the previous state
+            np.testing.assert_array_equal(got.cache_past, np.minimum(T - S, C))
+
+
+def test_lengths_rejects_bad_arguments(orc):
+    for S, C in ((0, 8), (1, 0), (-1, 8), (1, -4)):
+        assert orc.kv_seq_lengths_status(np.zeros(2, np.int32), S, C) == oracle.E_INVALID_ARG
+
+
+# --------------------------------------------------------------------------
+# Windowed cache: replay of tagged token histories
+# --------------------------------------------------------------------------
+
+def _step(orc, k, v, T_before, S, C, phase_split=False, bsnh=False):
+    """Append S tokens to every batch entry; returns (k, v, T_after, staging)."""
+    B, H, _, D = k.shape
+    T_after = T_before + S
+    L = orc.kv_seq_lengths((T_after - 1).astype(np.int32), S, C)
+    assert L.flags == 0
+    kn, vn = replay.new_block(B, H, T_before, S, D)
+    ks = vs = None
+    if S > 1:
+        ks, vs = replay.fresh_cache(B, H, C + S, D, tensors=(2, 3))
+    ks0 = None if ks is None else ks.copy()
+    # S = 1 runs in place and ignores the phase: one call per step
+    split = phase_split and S > 1
+    phases = [oracle.PHASE_STAGE, oracle.PHASE_COMMIT] if split else [oracle.PHASE_ALL]
+    if bsnh:  # new rows stored as [B, S, H, D]
+        kb = np.ascontiguousarray(kn.transpose(0, 2, 1, 3))
+        vb = np.ascontiguousarray(vn.transpose(0, 2, 1, 3))
+        strides = (S * H * D, D, H * D)
+        for ph in phases:
+            f = orc.kv_window_append_strided(k, v, kb, vb, strides, S, L.cache_past, L.evict,
+                                             ks, vs, ph)
+            assert f == 0
+    else:
+        for ph in phases:
+            f = orc.kv_window_append(k, v, kn, vn, L.cache_past, L.evict, ks, vs, ph)
+            assert f == 0
+    if ks is not None:  # staging rows at and beyond Lp + S are never written
+        for b in range(B):
+            end = int(L.cache_past[b]) + S
+            np.testing.assert_array_equal(ks[b, :, end:], ks0[b, :, end:])
+    return T_after, L
+
+
+@pytest.mark.parametrize("C", [1, 2, 8, 16])
+@pytest.mark.parametrize("variant", ["plain", "phase_split", "bsnh"])
+def test_window_replay_invariant(orc, C, variant):
+    B, H, D = 3, 2, 6
+    for name, sched in replay.schedules(C).items():
+        sched = [s for s in sched if s >= 1]
+        k, v = replay.fresh_cache(B, H, C, D)
+        T = np.zeros(B, np.int64)
+        for S in sched:
+            kb, vb = k.copy(), v.copy()
+            T, _ = _step(orc, k, v, T, S, C, phase_split=variant == "phase_split",
+                         bsnh=variant == "bsnh")
+            replay.check_window(k, v, T, C, kb, vb)
+
+
+def test_window_replay_mixed_lengths(orc):
+    """Batch entries at different totals (partly filled and full windows side
+    by side), decode and multi-token steps."""
+    B, H, D, C = 6, 3, 5, 12
+    T = np.array([0, 3, 11, 12, 13, 40])
+    k, v = replay.windowed_state(B, H, C, T, D)
+    for S in [1, 1, 4, 1, 12, 1, 15, 2, 1]:
+        kb, vb = k.copy(), v.copy()
+        T, _ = _step(orc, k, v, T, S, C)
+        replay.check_window(k, v, T, C, kb, vb)
+
+
+def test_window_many_decode_steps(orc):
+    """400 decode steps at a small capacity (the CPU follow-up's
+    many-compactions scenario uses 400 steps)."""
+    B, H, D, C = 2, 2, 4, 9
+    T = np.array([0, 5])
+    k, v = replay.windowed_state(B, H, C, T, D)
+    for _ in range(400):
+        T, _ = _step(orc, k, v, T, 1, C)
+    replay.check_window(k, v, T, C)
+
+
+def test_window_bad_lengths_leave_entry_untouched(orc):
+    B, H, D, C = 4, 2, 4, 8
+    k, v = replay.fresh_cache(B, H, C, D)
+    kn, vn = replay.new_block(B, H, np.zeros(B, np.int64), 1, D)
+    k0, v0 = k.copy(), v.copy()
+    lp = np.array([3, 9, 8, -1], np.int32)   # 9 > C, -1 < 0
+    ev = np.array([0, 0, 0, 0], np.int32)    # entry 2: Lp = C needs E = 1
+    f = orc.kv_window_append(k, v, kn, vn, lp, ev)
+    assert f == oracle.FLAG_BAD_LENGTHS
+    for b in (1, 2, 3):
+        np.testing.assert_array_equal(k[b], k0[b])
+        np.testing.assert_array_equal(v[b], v0[b])
+    np.testing.assert_array_equal(k[0, :, 3], kn[0, :, 0])
+
+
+# --------------------------------------------------------------------------
+# Cross-op pins: windowed cache vs a full-length cache and vs a ring
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("C", [4, 10])
+def test_window_matches_full_cache_and_ring(orc, C):
+    """Keep a full-length linear cache (TensorScatter at w = P) and a ring of
+    width C (circular TensorScatter at w = P) next to the window. The window
+    rows [0, L) equal the full cache's rows [T-L, T); while nothing has been
+    evicted the two caches agree row for row; and once T >= C, window row i is
+    ring slot (T - L + i) mod C."""
+    B, H, D = 2, 2, 4
+    Mfull = 80
+    k, v = replay.fresh_cache(B, H, C, D)
+    fk, fv = replay.fresh_cache(B, H, Mfull, D, tensors=(0, 1))
+    rk, rv = replay.fresh_cache(B, H, C, D, tensors=(0, 1))
+    T = np.zeros(B, np.int64)
+    evicted = False
+    for S in [3, 1, 1, min(C, 5), 1, 1, 1, C, 1, 2, 1, 1]:
+        P = T.copy()
+        kn, vn = replay.new_block(B, H, P, S, D)
+        for cache, new in ((fk, kn), (fv, vn)):
+            _, fl = orc.tensor_scatter(cache, new, P, axis=2, mode="linear", in_place=True)
+            assert fl == 0
+        for cache, new in ((rk, kn), (rv, vn)):
+            _, fl = orc.tensor_scatter(cache, new, P, axis=2, mode="circular", in_place=True)
+            assert fl == 0
+        T, lens = _step(orc, k, v, T, S, C)
+        evicted = evicted or bool((lens.evict > 0).any())
+        for b in range(B):
+            L = int(lens.cache_total[b])
+            np.testing.assert_array_equal(k[b, :, :L], fk[b, :, T[b] - L:T[b]])
+            np.testing.assert_array_equal(v[b, :, :L], fv[b, :, T[b] - L:T[b]])
+            if not evicted:
+                np.testing.assert_array_equal(k[b, :, :L], fk[b, :, :L])
+            if T[b] >= C:
+                for i in range(L):
+                    np.testing.assert_array_equal(k[b, :, i], rk[b, :, (T[b] - L + i) % C])
+                    np.testing.assert_array_equal(v[b, :, i], rv[b, :, (T[b] - L + i) % C])
+
+
+# --------------------------------------------------------------------------
+# Byte accounting: "0.50 MiB moved per token" at C = W = 128, 8 heads x 64, fp32
+# --------------------------------------------------------------------------
+
+def test_half_mib_per_token_at_window_128(orc):
+    C, H, D, B = 128, 8, 64, 1
+    k, v = replay.windowed_state(B, H, C, np.array([500]), D)  # full window
+    k0, v0 = k.copy(), v.copy()
+    T, lens = _step(orc, k, v, np.array([500]), 1, C)
+    row_bytes = D * 4  # fp32 rows of head_size 64
+    moved = 0
+    for a, a0 in ((k, k0), (v, v0)):
+        changed = (a != a0).any(axis=-1)            # [B, H, C]
+        changed[:, :, lens.cache_past[0] - lens.evict[0]] = False  # the appended row
+        moved += int(changed.sum()) * row_bytes
+    assert moved == 127 * 256 * 8 * 2
+    assert round(moved / 2**20, 2) == 0.50
+
+
+def test_oracle_source_has_no_gpu_dependency():
+    src = open(oracle.SOURCE).read()
+    for banned in ("hip", "swrt.h", "sliding_window_ring_tensor_amd"):
+        assert banned not in src.lower().replace("thread", ""), banned
