@@ -1,0 +1,236 @@
+"""Benchmark: KV-cache update effective HBM GB/s and us per decode step.
+
+Workload (one "step"): the KV-cache updates of one whole-model decode step of a
+24-layer model whose even layers use a windowed cache (K/V [64, 8, 128, 64],
+capacity 128) and whose odd layers use a full linear cache updated by
+TensorScatter (K/V [64, 8, 8192, 64]); batch 64, 8 KV heads, head_dim 64, total
+lengths T ~ U{1..8192} shared by all layers; bf16 (or --dtype fp8_e4m3fn).
+A step is three launches: kv_seq_lengths, kv_window_append_layers (all 12
+windowed layers, in place) and tensor_scatter_batched (all 24 full caches).
+
+Measurement
+  - value: algorithmic bytes of a step / time of a step, from K steps bracketed
+    by torch.cuda.synchronize(), replayed as one HIP graph per buffer set.
+  - Infinity Cache: every buffer set is independent and --sets sets (default
+    3, over 512 MB of windowed caches touched between two uses of one set)
+    are visited round robin, so no step finds its data in the 256 MB cache.
+  - roofline: the dominant kernel (window shift + append, 12 layers) timed
+    with HIP events on the launch stream around each launch of an eager pass
+    of K steps; achieved = its algorithmic bytes / its mean duration.
+  - cpu_baseline: the CPU oracle (single thread) on the same step, host copies
+    of the same inputs, for a bounded number of steps.
+
+One JSON line on stdout; progress on stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD's published peak
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(step, seconds: float):
+    """The oracle as it stands, one host thread, on host copies of set 0."""
+    import oracle
+
+    orc = oracle.get()
+    spec, b = step.spec, step.buffers
+    D, H = spec.head_dim, spec.kv_heads
+    bits = torch.empty((), dtype=spec.dtype).element_size() * 8
+
+    def host(t):
+        return t.detach().cpu().contiguous().view(torch.uint8).numpy()
+
+    wk = [host(t).copy() for t in b.win_k]
+    wv = [host(t).copy() for t in b.win_v]
+    wkn, wvn = [host(t) for t in b.win_kn], [host(t) for t in b.win_vn]
+    row = D * bits // 8
+    full_shape = (spec.batch, H, spec.max_seq, D)
+    # full caches: only the written rows are ever touched; their prior content
+    # does not change the oracle's work, so they are left uninitialised
+    full = [np.empty((spec.batch, H, spec.max_seq, row), np.uint8)
+            for _ in range(2 * len(spec.full_layers))]
+    fnew = [host(t) for t in b.full_kn + b.full_vn]
+    sk = spec.seqlens_k
+    n, t0 = 0, time.perf_counter()
+    while True:
+        L = orc.kv_seq_lengths(sk, 1, spec.window)
+        for i in range(len(wk)):
+            orc.kv_window_append_strided(wk[i], wv[i], wkn[i], wvn[i], (H * D, D, D), 1,
+                                         L.cache_past, L.evict, elem_bits=bits, head_dim=D)
+        for c, u in zip(full, fnew):
+            orc.tensor_scatter_raw(c, c, u, spec.write_indices, full_shape, 2, 1, 0, bits)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return n, el
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp8_e4m3fn"])
+    ap.add_argument("--sets", type=int, default=3, help="independent buffer sets, round robin")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this path has no cross-GPU step (every (b, h) "
+              "slice is independent); run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import sliding_window_ring_tensor_amd as swrt
+    from sliding_window_ring_tensor_amd import workloads as wl
+    from sliding_window_ring_tensor_amd.decode_step import ModelDecodeStep
+
+    if not os.path.exists(swrt.LIBRARY):
+        from sliding_window_ring_tensor_amd import build as swrt_build
+        swrt_build.build()
+    swrt.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    spec = wl.workload5(wl.DTYPES[args.dtype])
+    log(f"allocating {args.sets} buffer sets ...")
+    steps = [ModelDecodeStep(spec, dev, set_id=i) for i in range(args.sets)]
+    acct = steps[0].algorithmic_bytes()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.Stream()
+    K, W = args.steps, args.warmup
+    with torch.cuda.stream(stream):
+        # ---- graph replay (value) ----
+        graphs = []
+        for st in steps:
+            st.run()  # warm the launch path before capture
+        torch.cuda.synchronize()
+        for st in steps:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                st.run()
+            graphs.append(g)
+        for i in range(W):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+        log(f"timing {K} graph-replayed steps ...")
+        t0 = time.perf_counter()
+        for i in range(K):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+        graph_s = (time.perf_counter() - t0) / K
+
+        # ---- eager pass: events around the dominant kernel ----
+        for i in range(W):
+            steps[i % len(steps)].run()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(K)]
+        log(f"timing {K} eager steps ...")
+        t0 = time.perf_counter()
+        for i in range(K):
+            st = steps[i % len(steps)]
+            st.lengths()
+            ev[i][0].record(stream)
+            st.windowed()
+            ev[i][1].record(stream)
+            st.full()
+        torch.cuda.synchronize()
+        eager_s = (time.perf_counter() - t0) / K
+        win_ms = [a.elapsed_time(b) for a, b in ev]
+
+        # ---- achievable reference: a 1 GiB device-to-device copy ----
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        dst.copy_(src)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(10):
+            dst.copy_(src)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        copy_gbs = 2 * (1 << 30) * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        del src, dst
+
+    flags = [int(st.buffers.flags.item()) for st in steps]
+    if any(flags):
+        raise SystemExit(f"device flags raised during the benchmark: {flags}")
+    win_mean_s = float(np.mean(win_ms)) * 1e-3
+    achieved = acct["windowed"] / win_mean_s / 1e9
+    value = acct["total"] / graph_s / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"timing the CPU oracle for about {args.cpu_seconds:.0f} s ...")
+        n, el = cpu_baseline(steps[0], args.cpu_seconds)
+        cpu = {"value": round(acct["total"] * n / el / 1e9, 4), "unit": "GB/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"{n} whole-model decode steps of the same workload (host copies of "
+                         f"buffer set 0), one thread, {el:.1f} s",
+               "us_per_step": round(el / n * 1e6, 1)}
+
+    out = {
+        "metric": "KV-cache update effective HBM GB/s (% of peak) and us per decode step",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(graph_s * 1e3, 5),
+        "us_per_step": round(graph_s * 1e6, 2),
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": args.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": f"whole-model decode-step KV-cache update, {spec.layers} layers "
+                        f"({len(spec.windowed_layers)} windowed C={spec.window}, "
+                        f"{len(spec.full_layers)} full linear TensorScatter max_seq={spec.max_seq}), "
+                        f"B={spec.batch}, H_kv={spec.kv_heads}, D={spec.head_dim}, "
+                        f"T~U[1,8192] seed {spec.seed}",
+            "bytes_per_step": acct["total"],
+            "timing": "HIP graph replay, one graph per buffer set",
+            "cache_defeat": f"{args.sets} independent buffer sets round robin",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "window_in_place (12 windowed layers, K and V)",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "bytes_per_launch": acct["windowed"],
+            "mean_launch_us": round(win_mean_s * 1e6, 3),
+        },
+        "cpu_baseline": cpu,
+        "eager": {"us_per_step": round(eager_s * 1e6, 2),
+                  "value": round(acct["total"] / eager_s / 1e9, 2)},
+        "copy_reference_gbs": round(copy_gbs, 1),
+        "env": {"gpu": torch.cuda.get_device_name(dev), "torch": torch.__version__,
+                "hip": torch.version.hip, "host": platform.node()},
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

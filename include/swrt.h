@@ -36,9 +36,9 @@
  *   - Synchronous errors: a non-zero status is returned and nothing is
  *     launched. SWRT_E_INVALID_ARG for a null required pointer, a bad rank,
  *     axis, mode, phase or element width, a negative size, S > M (TensorScatter),
- *     C < 1, a pointer or stride not aligned to the element width, or
- *     overlapping buffers (other than present == past). SWRT_E_UNSUPPORTED for
- *     a row that does not end on a byte (4-bit elements, odd row length) and
+ *     C < 1, a pointer not aligned to its element (element size, capped at 8
+ *     bytes), or overlapping buffers (other than present == past).
+ *     SWRT_E_UNSUPPORTED for a row that does not end on a byte (4-bit elements, odd row length) and
  *     for sizes beyond the limits stated below. SWRT_E_LAUNCH when the HIP
  *     launch itself fails.
  *   - Data-dependent problems are reported asynchronously: bits are OR-ed into
@@ -108,13 +108,39 @@ extern "C" {
  * d_flags        device uint32 or NULL. SWRT_FLAG_LINEAR_OOB when a linear
  *                w_b < 0 or w_b + S > M: every row of that batch entry keeps
  *                past's value (no partial write).
- * Limits: shape[0] * (product of dims) * elem_bits/8 must fit in int64 and
- * the number of rows written must be below 2^31 * 2^16.
+ * Limits: sizes must fit int64 bytes, and the words one call moves (update
+ * bytes in place, present bytes otherwise, over a copy word of up to 16
+ * bytes: the widest that divides the row and every address) must stay below
+ * 2^31, i.e. up to 32 GiB per call with 16-byte rows.
  */
 int swrt_tensor_scatter(void *present, const void *past, const void *update,
                         const int64_t *write_indices, const int64_t *shape,
                         int rank, int axis, int64_t seq_len, int mode,
                         int elem_bits, uint32_t *d_flags, void *stream);
+
+/*
+ * swrt_tensor_scatter_batched -- swrt_tensor_scatter on n_tensors caches that
+ * share shape, axis, S, mode, element width and write_indices, in one launch
+ * (e.g. the K and V caches of every full-attention layer of a model at one
+ * decode step).
+ *
+ * n_tensors            0 .. SWRT_MAX_BATCHED.
+ * presents, pasts,
+ * updates              host arrays of n_tensors device pointers, each as in
+ *                      swrt_tensor_scatter. Either every presents[t] equals
+ *                      pasts[t] (in place) or none does. No present may
+ *                      overlap any other buffer of the call; updates and
+ *                      pasts may be shared.
+ * The other arguments and the flag word are shared by all tensors.
+ */
+#define SWRT_MAX_BATCHED 64
+int swrt_tensor_scatter_batched(int n_tensors, void *const *presents,
+                                const void *const *pasts,
+                                const void *const *updates,
+                                const int64_t *write_indices,
+                                const int64_t *shape, int rank, int axis,
+                                int64_t seq_len, int mode, int elem_bits,
+                                uint32_t *d_flags, void *stream);
 
 /*
  * swrt_kv_seq_lengths -- lengths of one windowed GQA step (pull request "GQA
@@ -198,6 +224,38 @@ int swrt_kv_window_append(void *k_cache, void *v_cache, const void *k_new,
                           int capacity, int seq_len, int head_dim,
                           int elem_bits, unsigned phase, uint32_t *d_flags,
                           void *stream);
+
+/*
+ * swrt_kv_window_append_layers -- swrt_kv_window_append for several layers at
+ * once (the pull request's Design section applied to every windowed layer of
+ * a model in one launch per phase, as for a whole-model decode step whose
+ * windowed layers share batch, heads, capacity, head_dim and lengths).
+ *
+ * n_layers             1 .. SWRT_MAX_LAYERS.
+ * k_caches, v_caches,
+ * k_news, v_news       host arrays of n_layers device pointers, each as in
+ *                      swrt_kv_window_append. New rows of all layers share
+ *                      new_strides and may be shared between layers.
+ * k_stagings,
+ * v_stagings           host arrays of n_layers device pointers, required when
+ *                      S > 1 (NULL otherwise).
+ * Every other argument, the lengths and the flag word are shared by all
+ * layers and mean what they mean for swrt_kv_window_append. No cache or
+ * staging buffer may overlap any other buffer of any layer.
+ */
+#define SWRT_MAX_LAYERS 32
+int swrt_kv_window_append_layers(int n_layers, void *const *k_caches,
+                                 void *const *v_caches,
+                                 const void *const *k_news,
+                                 const void *const *v_news,
+                                 const int64_t *new_strides,
+                                 void *const *k_stagings,
+                                 void *const *v_stagings,
+                                 const int32_t *cache_past_lens,
+                                 const int32_t *evict_counts, int batch,
+                                 int kv_heads, int capacity, int seq_len,
+                                 int head_dim, int elem_bits, unsigned phase,
+                                 uint32_t *d_flags, void *stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *swrt_status_string(int status);

@@ -1,0 +1,331 @@
+"""MI355X (gfx950) KV-cache updates for sliding-window / ring caches.
+
+A thin ctypes binding over ``libswrt.so`` (C-ABI in ``include/swrt.h``). The
+functions here only marshal torch tensors (device pointers, shapes, strides,
+the current stream) into the C entry points of the same names; every step of
+the update runs in the library's HIP kernels. If the library has not been
+built, every call raises ``SwrtError``: there is no fallback.
+
+Operations (pages: ONNX operator "TensorScatter"; Core AI model zoo
+"Stateful decode & KV cache"; onnxruntime pull request "GQA support
+sliding_window_cache"):
+
+    tensor_scatter(past, update, write_indices, axis=-2, mode="linear", out=None)
+    tensor_scatter_batched(pasts, updates, write_indices, ...)  # same shape, one launch
+    kv_seq_lengths(seqlens_k, seq_len, capacity)
+    kv_window_append(k_cache, v_cache, k_new, v_new, cache_past_lens, evict_counts,
+                     k_staging=None, v_staging=None, phase="all")
+    kv_window_append_layers(...)   # several layers sharing shapes and lengths
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import NamedTuple, Sequence
+
+import torch
+
+__all__ = [
+    "SwrtError", "tensor_scatter", "tensor_scatter_batched", "kv_seq_lengths", "kv_window_append",
+    "kv_window_append_layers", "WindowLengths", "library_path", "lib",
+    "OK", "E_INVALID_ARG", "E_UNSUPPORTED", "E_LAUNCH",
+    "FLAG_LINEAR_OOB", "FLAG_BAD_SEQLEN", "FLAG_BAD_LENGTHS",
+    "PHASE_STAGE", "PHASE_COMMIT", "PHASE_ALL",
+]
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(PKG, "libswrt.so")
+
+# values of include/swrt.h
+OK, E_INVALID_ARG, E_UNSUPPORTED, E_LAUNCH = 0, 1, 2, 3
+FLAG_LINEAR_OOB, FLAG_BAD_SEQLEN, FLAG_BAD_LENGTHS = 1, 2, 4
+MODE_LINEAR, MODE_CIRCULAR = 0, 1
+PHASE_STAGE, PHASE_COMMIT, PHASE_ALL = 1, 2, 3
+MAX_LAYERS = 32
+MAX_BATCHED = 64
+
+_PHASES = {"stage": PHASE_STAGE, "commit": PHASE_COMMIT, "all": PHASE_ALL}
+_MODES = {"linear": MODE_LINEAR, "circular": MODE_CIRCULAR}
+
+
+class SwrtError(RuntimeError):
+    """A libswrt call failed (or the library is missing)."""
+
+    def __init__(self, msg: str, status: int | None = None):
+        super().__init__(msg)
+        self.status = status
+
+
+_lib: ctypes.CDLL | None = None
+
+
+def library_path() -> str:
+    return LIBRARY
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libswrt.so; raises SwrtError when it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIBRARY):
+        raise SwrtError(f"{LIBRARY} is missing: build it with "
+                        "`python -m sliding_window_ring_tensor_amd.build`")
+    L = ctypes.CDLL(LIBRARY)
+    vp, i32, i64, u32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_uint
+    vpp = ctypes.POINTER(ctypes.c_void_p)
+    L.swrt_tensor_scatter.argtypes = [vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, vp, vp]
+    L.swrt_tensor_scatter_batched.argtypes = [i32, vpp, vpp, vpp, vp, vp, i32, i32, i64, i32,
+                                              i32, vp, vp]
+    L.swrt_kv_seq_lengths.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
+    L.swrt_kv_window_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                        i32, i32, u32, vp, vp]
+    L.swrt_kv_window_append_layers.argtypes = [i32, vpp, vpp, vpp, vpp, vp, vpp, vpp, vp, vp,
+                                               i32, i32, i32, i32, i32, i32, u32, vp, vp]
+    for name in ("swrt_tensor_scatter", "swrt_tensor_scatter_batched", "swrt_kv_seq_lengths", "swrt_kv_window_append",
+                 "swrt_kv_window_append_layers", "swrt_abi_version"):
+        getattr(L, name).restype = ctypes.c_int
+    L.swrt_status_string.argtypes = [ctypes.c_int]
+    L.swrt_status_string.restype = ctypes.c_char_p
+    if L.swrt_abi_version() != 1:
+        raise SwrtError("libswrt ABI version mismatch")
+    _lib = L
+    return L
+
+
+def _check(status: int, what: str) -> None:
+    if status != OK:
+        msg = lib().swrt_status_string(status).decode()
+        raise SwrtError(f"{what}: {msg} (status {status})", status)
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _device_of(*ts: torch.Tensor | None) -> torch.device:
+    devs = {t.device for t in ts if t is not None}
+    if len(devs) != 1:
+        raise SwrtError(f"tensors must share one device, got {sorted(map(str, devs))}")
+    dev = devs.pop()
+    if dev.type != "cuda":
+        raise SwrtError(f"libswrt runs on the GPU only; got a tensor on {dev}")
+    return dev
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _bits(t: torch.Tensor) -> int:
+    return t.element_size() * 8
+
+
+def _contig(name: str, t: torch.Tensor) -> None:
+    if not t.is_contiguous():
+        raise SwrtError(f"{name} must be contiguous (it is never copied)")
+
+
+# ---------------------------------------------------------------------------
+# TensorScatter
+# ---------------------------------------------------------------------------
+
+def tensor_scatter(past: torch.Tensor, update: torch.Tensor,
+                   write_indices: torch.Tensor | None = None, *, axis: int = -2,
+                   mode: str = "linear", out: torch.Tensor | None = None,
+                   flags: torch.Tensor | None = None) -> torch.Tensor:
+    """present = TensorScatter(past, update, write_indices; axis, mode).
+
+    ``out=past`` updates the cache in place (only the target rows are written);
+    otherwise a new (or the given) ``out`` receives past with the update rows.
+    ``write_indices``: int64 [batch] on the device, or None for zeros.
+    ``flags``: optional int32/uint32 device scalar that receives FLAG_* bits.
+    """
+    dev = _device_of(past, update, write_indices, out, flags)
+    _contig("past", past)
+    _contig("update", update)
+    if update.dtype != past.dtype or update.dim() != past.dim():
+        raise SwrtError("update must have past's dtype and rank")
+    if write_indices is not None:
+        _contig("write_indices", write_indices)
+        if write_indices.dtype != torch.int64:
+            raise SwrtError("write_indices must be int64")
+    present = torch.empty_like(past) if out is None else out
+    if present.dtype != past.dtype or present.shape != past.shape:
+        raise SwrtError("out must have past's shape and dtype")
+    _contig("out", present)
+    rank = past.dim()
+    ax = axis + rank if axis < 0 else axis
+    if not 0 <= ax < rank:
+        raise SwrtError(f"axis {axis} out of range for rank {rank}")
+    shape = (ctypes.c_int64 * rank)(*past.shape)
+    with torch.cuda.device(dev):
+        st = lib().swrt_tensor_scatter(_ptr(present), _ptr(past), _ptr(update),
+                                       _ptr(write_indices), shape, rank, axis,
+                                       update.shape[ax], _MODES[mode], _bits(past),
+                                       _ptr(flags), _stream(dev))
+    _check(st, "tensor_scatter")
+    return present
+
+
+def tensor_scatter_batched(pasts: Sequence[torch.Tensor], updates: Sequence[torch.Tensor],
+                           write_indices: torch.Tensor | None = None, *, axis: int = -2,
+                           mode: str = "linear", outs: Sequence[torch.Tensor] | None = None,
+                           flags: torch.Tensor | None = None) -> list:
+    """TensorScatter on several caches of one shape sharing write_indices, in one
+    launch. ``outs=pasts`` updates every cache in place."""
+    n = len(pasts)
+    if len(updates) != n or not 1 <= n <= MAX_BATCHED:
+        raise SwrtError(f"need 1..{MAX_BATCHED} (past, update) pairs")
+    p0, u0 = pasts[0], updates[0]
+    presents = [torch.empty_like(p) for p in pasts] if outs is None else list(outs)
+    dev = _device_of(*pasts, *updates, *presents, write_indices, flags)
+    for p, u, o in zip(pasts, updates, presents):
+        for name, t in (("past", p), ("update", u), ("out", o)):
+            _contig(name, t)
+        if p.shape != p0.shape or o.shape != p0.shape or u.shape != u0.shape or \
+                len({p.dtype, u.dtype, o.dtype, p0.dtype}) != 1:
+            raise SwrtError("every past/out must share one shape, every update another, "
+                            "and all one dtype")
+    if write_indices is not None:
+        _contig("write_indices", write_indices)
+        if write_indices.dtype != torch.int64:
+            raise SwrtError("write_indices must be int64")
+    rank = p0.dim()
+    ax = axis + rank if axis < 0 else axis
+    if not 0 <= ax < rank or u0.dim() != rank:
+        raise SwrtError(f"axis {axis} out of range for rank {rank}")
+    arr = lambda ts: (ctypes.c_void_p * n)(*[t.data_ptr() for t in ts])  # noqa: E731
+    shape = (ctypes.c_int64 * rank)(*p0.shape)
+    with torch.cuda.device(dev):
+        st = lib().swrt_tensor_scatter_batched(n, arr(presents), arr(pasts), arr(updates),
+                                               _ptr(write_indices), shape, rank, axis,
+                                               u0.shape[ax], _MODES[mode], _bits(p0),
+                                               _ptr(flags), _stream(dev))
+    _check(st, "tensor_scatter_batched")
+    return presents
+
+
+# ---------------------------------------------------------------------------
+# windowed step: lengths
+# ---------------------------------------------------------------------------
+
+class WindowLengths(NamedTuple):
+    total: torch.Tensor        # T  = seqlens_k + 1            int64 [B]
+    past: torch.Tensor         # P  = max(0, T - S)            int64 [B]
+    cache_past: torch.Tensor   # Lp = min(P, C)                int32 [B]
+    cache_total: torch.Tensor  # L  = Lp + S - E = min(T, C)   int32 [B]
+    evict: torch.Tensor        # E  = max(0, Lp + S - C)       int32 [B]
+
+
+def kv_seq_lengths(seqlens_k: torch.Tensor, seq_len: int, capacity: int, *,
+                   out: WindowLengths | None = None,
+                   flags: torch.Tensor | None = None) -> WindowLengths:
+    """Lengths of one windowed step for every batch entry, computed on the device."""
+    dev = _device_of(seqlens_k, flags)
+    _contig("seqlens_k", seqlens_k)
+    if seqlens_k.dtype != torch.int32 or seqlens_k.dim() != 1:
+        raise SwrtError("seqlens_k must be a 1-D int32 tensor")
+    B = seqlens_k.shape[0]
+    if out is None:
+        out = WindowLengths(*(torch.empty(B, dtype=dt, device=dev) for dt in
+                              (torch.int64, torch.int64, torch.int32, torch.int32, torch.int32)))
+    with torch.cuda.device(dev):
+        st = lib().swrt_kv_seq_lengths(_ptr(seqlens_k), B, seq_len, capacity, _ptr(out.total),
+                                       _ptr(out.past), _ptr(out.cache_past),
+                                       _ptr(out.cache_total), _ptr(out.evict), _ptr(flags),
+                                       _stream(dev))
+    _check(st, "kv_seq_lengths")
+    return out
+
+
+# ---------------------------------------------------------------------------
+# windowed step: shift + append / stage + commit
+# ---------------------------------------------------------------------------
+
+def _new_strides(k_new: torch.Tensor, v_new: torch.Tensor):
+    if k_new.dim() != 4 or k_new.shape != v_new.shape or k_new.stride() != v_new.stride():
+        raise SwrtError("k_new and v_new must be [B, H, S, D] views with equal strides")
+    if k_new.shape[3] > 1 and k_new.stride(3) != 1:
+        raise SwrtError("head_dim of the new rows must be contiguous")
+    return (ctypes.c_int64 * 3)(*k_new.stride()[:3])
+
+
+def kv_window_append(k_cache: torch.Tensor, v_cache: torch.Tensor, k_new: torch.Tensor,
+                     v_new: torch.Tensor, cache_past_lens: torch.Tensor,
+                     evict_counts: torch.Tensor, *, k_staging: torch.Tensor | None = None,
+                     v_staging: torch.Tensor | None = None, phase: str = "all",
+                     flags: torch.Tensor | None = None) -> None:
+    """One windowed step on caches [B, H, C, D] (in place).
+
+    ``k_new``/``v_new`` are [B, H, S, D] views (BNSH, or BSNH transposed) with
+    head_dim contiguous. ``cache_past_lens``/``evict_counts`` come from
+    ``kv_seq_lengths`` with the same S and C. S > 1 needs staging buffers
+    [B, H, C + S, D]; ``phase`` picks "stage", "commit" or "all".
+    """
+    kv_window_append_layers([k_cache], [v_cache], [k_new], [v_new], cache_past_lens,
+                            evict_counts, k_stagings=None if k_staging is None else [k_staging],
+                            v_stagings=None if v_staging is None else [v_staging],
+                            phase=phase, flags=flags, _single=True)
+
+
+def kv_window_append_layers(k_caches: Sequence[torch.Tensor], v_caches: Sequence[torch.Tensor],
+                            k_news: Sequence[torch.Tensor], v_news: Sequence[torch.Tensor],
+                            cache_past_lens: torch.Tensor, evict_counts: torch.Tensor, *,
+                            k_stagings: Sequence[torch.Tensor] | None = None,
+                            v_stagings: Sequence[torch.Tensor] | None = None,
+                            phase: str = "all", flags: torch.Tensor | None = None,
+                            _single: bool = False) -> None:
+    """The windowed step for several layers that share B, H, C, D, S and the
+    lengths (e.g. every windowed layer of a model), in one launch per phase."""
+    n = len(k_caches)
+    if not (len(v_caches) == len(k_news) == len(v_news) == n) or not 1 <= n <= MAX_LAYERS:
+        raise SwrtError(f"need 1..{MAX_LAYERS} layers with one tensor of each kind")
+    kc = k_caches[0]
+    if kc.dim() != 4:
+        raise SwrtError("caches must be [B, H, C, D]")
+    B, H, C, D = kc.shape
+    S = k_news[0].shape[2]
+    strides = _new_strides(k_news[0], v_news[0])
+    everything = [*k_caches, *v_caches, *k_news, *v_news, cache_past_lens, evict_counts, flags]
+    if k_stagings is not None:
+        everything += [*k_stagings, *v_stagings]
+    dev = _device_of(*everything)
+    for t in (*k_caches, *v_caches):
+        _contig("cache", t)
+        if t.shape != kc.shape or t.dtype != kc.dtype:
+            raise SwrtError("all caches must share shape and dtype")
+    for a, b in zip(k_news, v_news):
+        if a.shape != (B, H, S, D) or b.shape != (B, H, S, D) or a.dtype != kc.dtype \
+                or b.dtype != kc.dtype or a.stride() != k_news[0].stride() \
+                or b.stride() != k_news[0].stride():
+            raise SwrtError("new rows must be [B, H, S, D] with the caches' dtype and "
+                            "one stride pattern")
+    for t in (cache_past_lens, evict_counts):
+        _contig("lengths", t)
+        if t.dtype != torch.int32 or t.shape != (B,):
+            raise SwrtError("cache_past_lens and evict_counts must be int32 [B]")
+    ks = vs = None
+    if S > 1:
+        if k_stagings is None or v_stagings is None:
+            raise SwrtError("S > 1 needs k_staging and v_staging [B, H, C + S, D]")
+        for t in (*k_stagings, *v_stagings):
+            _contig("staging", t)
+            if t.shape != (B, H, C + S, D) or t.dtype != kc.dtype:
+                raise SwrtError("staging must be [B, H, C + S, D] with the caches' dtype")
+    arr = lambda ts: (ctypes.c_void_p * n)(*[t.data_ptr() for t in ts])  # noqa: E731
+    if S > 1:
+        ks, vs = arr(k_stagings), arr(v_stagings)
+    with torch.cuda.device(dev):
+        if _single:
+            st = lib().swrt_kv_window_append(
+                _ptr(k_caches[0]), _ptr(v_caches[0]), _ptr(k_news[0]), _ptr(v_news[0]), strides,
+                None if ks is None else ks[0], None if vs is None else vs[0],
+                _ptr(cache_past_lens), _ptr(evict_counts), B, H, C, S, D, _bits(kc),
+                _PHASES[phase], _ptr(flags), _stream(dev))
+        else:
+            st = lib().swrt_kv_window_append_layers(
+                n, arr(k_caches), arr(v_caches), arr(k_news), arr(v_news), strides, ks, vs,
+                _ptr(cache_past_lens), _ptr(evict_counts), B, H, C, S, D, _bits(kc),
+                _PHASES[phase], _ptr(flags), _stream(dev))
+    _check(st, "kv_window_append")

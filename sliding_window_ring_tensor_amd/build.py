@@ -1,0 +1,45 @@
+"""Compile libswrt.so (HIP, gfx950) in place, next to this file.
+
+    python -m sliding_window_ring_tensor_amd.build
+
+All kernels and the C-ABI live in csrc/*.hip; the public header is
+include/swrt.h at the repository root.
+"""
+from __future__ import annotations
+
+import glob
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+LIBRARY = os.path.join(PKG, "libswrt.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-Wall", "-Wno-unused-function",
+    # packed-fp32 instructions stay off in every kernel of this library
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def sources() -> list[str]:
+    return sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
+
+
+def build(out: str = LIBRARY, extra: tuple = (), verbose: bool = False) -> str:
+    """Compile every csrc/*.hip into one shared library; return its path."""
+    tmp = out + ".tmp"
+    cmd = [HIPCC, *FLAGS, *extra, "-I", os.path.join(ROOT, "include"), *sources(), "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,76 @@
+// kv_seq_lengths.hip -- lengths of one windowed GQA step, on the device.
+//
+// onnxruntime pull request "GQA support sliding_window_cache", section
+// "Design": the step derives, from seqlens_k alone and on the device (so the
+// launches stay graph-capturable), the absolute lengths used for rotary
+// positions, the cache-relative lengths used for cache addressing and the
+// per-batch eviction count. The follow-up commit of the same pull request does
+// this arithmetic in 64 bits (seqlens_k + 1 overflows 32 bits at INT32_MAX)
+// and clamps the derived past length at zero; the cache-relative results are
+// bounded by the capacity and fit 32 bits again.
+//
+// One lane per batch entry; the values are independent per entry.
+#include "swrt_device.hpp"
+
+namespace swrt {
+namespace {
+
+struct LengthArgs {
+  const int32_t *seqlens_k;
+  int64_t *total, *past;  // may be null
+  int32_t *cache_past, *cache_total, *evict;  // cache_total may be null
+  uint32_t *flags;
+  int32_t batch, S, C;
+};
+
+__global__ __launch_bounds__(kBlock) void seq_lengths_kernel(LengthArgs a) {
+  const int32_t b = blockIdx.x * kBlock + threadIdx.x;
+  if (b >= a.batch) return;
+  const int64_t sk = a.seqlens_k[b];
+  const int64_t T = sk + 1;
+  int64_t P = T - a.S;
+  if (P < 0) P = 0;
+  const int64_t Lp = P < a.C ? P : a.C;
+  int64_t E = Lp + a.S - a.C;
+  if (E < 0) E = 0;
+  const int64_t L = Lp + a.S - E;
+  if ((sk < 0 || T < a.S) && a.flags) atomicOr(a.flags, SWRT_FLAG_BAD_SEQLEN);
+  if (a.total) a.total[b] = T;
+  if (a.past) a.past[b] = P;
+  a.cache_past[b] = int32_t(Lp);
+  a.evict[b] = int32_t(E);
+  if (a.cache_total) a.cache_total[b] = int32_t(L);
+}
+
+}  // namespace
+}  // namespace swrt
+
+using namespace swrt;
+
+extern "C" int swrt_kv_seq_lengths(const int32_t *seqlens_k, int batch, int seq_len, int capacity,
+                                   int64_t *total_lens, int64_t *past_lens,
+                                   int32_t *cache_past_lens, int32_t *cache_total_lens,
+                                   int32_t *evict_counts, uint32_t *d_flags, void *stream) {
+  if (batch < 0 || seq_len < 1 || capacity < 1) return SWRT_E_INVALID_ARG;
+  if (batch == 0) return SWRT_OK;
+  if (!seqlens_k || !cache_past_lens || !evict_counts) return SWRT_E_INVALID_ARG;
+  const auto addr = [](const void *p) { return uint64_t(reinterpret_cast<uintptr_t>(p)); };
+  if (addr(seqlens_k) % 4 || addr(cache_past_lens) % 4 || addr(evict_counts) % 4 ||
+      addr(cache_total_lens) % 4 || addr(total_lens) % 8 || addr(past_lens) % 8 ||
+      addr(d_flags) % 4)
+    return SWRT_E_INVALID_ARG;
+  const uint64_t n4 = uint64_t(batch) * 4, n8 = uint64_t(batch) * 8;
+  const void *bufs[6] = {seqlens_k, total_lens, past_lens, cache_past_lens, cache_total_lens,
+                         evict_counts};
+  const uint64_t size[6] = {n4, n8, n8, n4, n4, n4};
+  for (int i = 0; i < 6; ++i)
+    for (int j = i + 1; j < 6; ++j)
+      if (overlaps(bufs[i], size[i], bufs[j], size[j])) return SWRT_E_INVALID_ARG;
+
+  LengthArgs a{seqlens_k, total_lens, past_lens, cache_past_lens, cache_total_lens, evict_counts,
+               d_flags, batch, seq_len, capacity};
+  const uint32_t grid = (uint32_t(batch) + kBlock - 1) / kBlock;
+  hipLaunchKernelGGL(seq_lengths_kernel, dim3(grid), dim3(kBlock), 0,
+                     static_cast<hipStream_t>(stream), a);
+  return launch_status();
+}

@@ -1,0 +1,116 @@
+"""One whole-model decode step of KV-cache updates (three launches).
+
+A model whose layers alternate between windowed attention (a window-sized
+cache, pull request "GQA support sliding_window_cache", section "Design") and
+full attention (a max-length cache updated by TensorScatter in linear mode at
+write index T - 1, ONNX operator page "TensorScatter"). At every decode step
+each layer receives one new K row and one new V row per (batch, kv-head):
+
+  1. kv_seq_lengths           once for all windowed layers (they share the
+                              running lengths): seqlens_k -> Lp, E;
+  2. kv_window_append_layers  every windowed layer's K and V: shift by E and
+                              append at Lp - E, in place (S = 1), one launch;
+  3. tensor_scatter_batched   every full layer's K and V: write row T - 1,
+                              in place, one launch.
+
+The buffers are plain torch tensors on one device; the step only issues the
+three library calls on the current stream, so it can be captured in a graph.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+import sliding_window_ring_tensor_amd as swrt
+from sliding_window_ring_tensor_amd import workloads as wl
+
+
+@dataclass
+class StepBuffers:
+    win_k: list      # windowed K caches [B, H, W, D]
+    win_v: list
+    win_kn: list     # new rows [B, H, 1, D]
+    win_vn: list
+    full_k: list     # full caches [B, H, M, D]
+    full_v: list
+    full_kn: list
+    full_vn: list
+    seqlens_k: torch.Tensor      # int32 [B], T - 1
+    write_indices: torch.Tensor  # int64 [B], T - 1
+    lengths: swrt.WindowLengths  # outputs of kv_seq_lengths
+    flags: torch.Tensor          # int32 [1]
+
+
+class ModelDecodeStep:
+    """The KV-cache updates of one decode step of a windowed/full layer stack."""
+
+    def __init__(self, spec: wl.ModelStep, device, set_id: int = 0, raw_bits: bool = False,
+                 fill: bool = True):
+        self.spec = spec
+        self.device = torch.device(device)
+        B, H, D, W, M = spec.batch, spec.kv_heads, spec.head_dim, spec.window, spec.max_seq
+        dt = spec.dtype
+        seed = spec.seed * 100 + set_id
+
+        def buf(shape, bid):
+            if fill:
+                return wl.payload(shape, dt, seed, bid, self.device, raw_bits)
+            return torch.empty(shape, dtype=dt, device=self.device)
+
+        nw, nf = len(spec.windowed_layers), len(spec.full_layers)
+        self.buffers = StepBuffers(
+            win_k=[buf((B, H, W, D), 10 * i + 0) for i in range(nw)],
+            win_v=[buf((B, H, W, D), 10 * i + 1) for i in range(nw)],
+            win_kn=[buf((B, H, 1, D), 10 * i + 2) for i in range(nw)],
+            win_vn=[buf((B, H, 1, D), 10 * i + 3) for i in range(nw)],
+            full_k=[buf((B, H, M, D), 1000 + 10 * i + 0) for i in range(nf)],
+            full_v=[buf((B, H, M, D), 1000 + 10 * i + 1) for i in range(nf)],
+            full_kn=[buf((B, H, 1, D), 1000 + 10 * i + 2) for i in range(nf)],
+            full_vn=[buf((B, H, 1, D), 1000 + 10 * i + 3) for i in range(nf)],
+            seqlens_k=torch.from_numpy(spec.seqlens_k).to(self.device),
+            write_indices=torch.from_numpy(spec.write_indices).to(self.device),
+            lengths=swrt.WindowLengths(*(torch.zeros(B, dtype=t, device=self.device) for t in (
+                torch.int64, torch.int64, torch.int32, torch.int32, torch.int32))),
+            flags=torch.zeros(1, dtype=torch.int32, device=self.device),
+        )
+
+    # -- the step ---------------------------------------------------------
+    def lengths(self):
+        b = self.buffers
+        swrt.kv_seq_lengths(b.seqlens_k, 1, self.spec.window, out=b.lengths, flags=b.flags)
+
+    def windowed(self):
+        b = self.buffers
+        swrt.kv_window_append_layers(b.win_k, b.win_v, b.win_kn, b.win_vn, b.lengths.cache_past,
+                                     b.lengths.evict, flags=b.flags)
+
+    def full(self):
+        b = self.buffers
+        caches = b.full_k + b.full_v
+        swrt.tensor_scatter_batched(caches, b.full_kn + b.full_vn, b.write_indices, axis=2,
+                                    mode="linear", outs=caches, flags=b.flags)
+
+    def run(self):
+        self.lengths()
+        self.windowed()
+        self.full()
+
+    # -- accounting -------------------------------------------------------
+    def algorithmic_bytes(self) -> dict:
+        """Bytes the method must move in one step: every byte read once and
+        written once. Windowed slice with E = 1: the Lp - 1 shifted rows and the
+        appended row, each read and written; with E = 0: the appended row.
+        Full cache: the written row, read from the update and written."""
+        s = self.spec
+        row = s.head_dim * torch.empty((), dtype=s.dtype).element_size()
+        T = s.total_lens.astype(np.int64)
+        P = T - 1
+        Lp = np.minimum(P, s.window)
+        E = np.maximum(0, Lp + 1 - s.window)
+        per_slice = 2 * row * (E * (Lp - E) + 1)
+        windowed = int(per_slice.sum()) * s.kv_heads * 2 * len(s.windowed_layers)
+        full = 2 * row * s.batch * s.kv_heads * 2 * len(s.full_layers)
+        return {"windowed": windowed, "full": full, "lengths": s.batch * (4 + 8 + 8 + 4 * 3),
+                "total": windowed + full}

@@ -1,0 +1,213 @@
+"""C-ABI checks that need no GPU.
+
+- libswrt.so loads and exports every function include/swrt.h declares;
+- the header's constants agree with the Python binding and (by value) with
+  the oracle's own constants;
+- host validation rejects bad arguments with the documented status before
+  anything is launched;
+- the multiply-shift divider used by the kernels' index math is exact.
+
+The validation calls pass made-up, never dereferenced addresses. They only run
+where no GPU is visible, so a validation bug can never turn into a launch on a
+real device; the GPU suite repeats the interesting rejections with real
+buffers.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+import oracle
+import sliding_window_ring_tensor_amd as swrt
+from sliding_window_ring_tensor_amd import build as swrt_build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "swrt.h")
+
+no_gpu_visible = pytest.mark.skipif(torch.cuda.device_count() > 0,
+                                    reason="made-up addresses are only passed with no GPU visible")
+
+
+@pytest.fixture(scope="session")
+def L():
+    if not os.path.exists(swrt.LIBRARY):
+        swrt_build.build()
+    return swrt.lib()
+
+
+def _header():
+    return open(HEADER).read()
+
+
+def test_exports_every_declared_function(L):
+    declared = set(re.findall(r"^(?:int|const char \*)\s*(swrt_\w+)\s*\(", _header(), re.M))
+    assert {"swrt_tensor_scatter", "swrt_tensor_scatter_batched", "swrt_kv_seq_lengths", "swrt_kv_window_append",
+            "swrt_kv_window_append_layers", "swrt_status_string", "swrt_abi_version"} <= declared
+    out = subprocess.run(["nm", "-D", "--defined-only", swrt.LIBRARY], check=True,
+                         capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (swrt_\w+)", out))
+    assert declared <= exported, declared - exported
+    for name in declared:
+        assert hasattr(L, name)
+
+
+def test_constants_agree():
+    defs = dict(re.findall(r"#define (SWRT_\w+) (\d+)u?", _header()))
+    assert int(defs["SWRT_ABI_VERSION"]) == 1
+    py = {"SWRT_OK": swrt.OK, "SWRT_E_INVALID_ARG": swrt.E_INVALID_ARG,
+          "SWRT_E_UNSUPPORTED": swrt.E_UNSUPPORTED, "SWRT_E_LAUNCH": swrt.E_LAUNCH,
+          "SWRT_FLAG_LINEAR_OOB": swrt.FLAG_LINEAR_OOB, "SWRT_FLAG_BAD_SEQLEN": swrt.FLAG_BAD_SEQLEN,
+          "SWRT_FLAG_BAD_LENGTHS": swrt.FLAG_BAD_LENGTHS, "SWRT_MODE_LINEAR": swrt.MODE_LINEAR,
+          "SWRT_MODE_CIRCULAR": swrt.MODE_CIRCULAR, "SWRT_PHASE_STAGE": swrt.PHASE_STAGE,
+          "SWRT_PHASE_COMMIT": swrt.PHASE_COMMIT, "SWRT_PHASE_ALL": swrt.PHASE_ALL,
+          "SWRT_MAX_LAYERS": swrt.MAX_LAYERS, "SWRT_MAX_BATCHED": swrt.MAX_BATCHED}
+    for k, v in py.items():
+        assert int(defs[k]) == v, k
+    # the oracle defines its own values; they must mean the same bits
+    assert oracle.FLAG_LINEAR_OOB == swrt.FLAG_LINEAR_OOB
+    assert oracle.FLAG_BAD_SEQLEN == swrt.FLAG_BAD_SEQLEN
+    assert oracle.FLAG_BAD_LENGTHS == swrt.FLAG_BAD_LENGTHS
+    assert (oracle.MODE_LINEAR, oracle.MODE_CIRCULAR) == (swrt.MODE_LINEAR, swrt.MODE_CIRCULAR)
+    assert (oracle.PHASE_STAGE, oracle.PHASE_COMMIT, oracle.PHASE_ALL) == \
+        (swrt.PHASE_STAGE, swrt.PHASE_COMMIT, swrt.PHASE_ALL)
+
+
+def test_status_strings(L):
+    for code in (0, 1, 2, 3, 99, -1):
+        assert isinstance(L.swrt_status_string(code), bytes)
+    assert L.swrt_status_string(0) == b"ok"
+    assert L.swrt_abi_version() == 1
+
+
+def test_binding_refuses_cpu_tensors():
+    t = torch.zeros(2, 3, 4)
+    with pytest.raises(swrt.SwrtError):
+        swrt.tensor_scatter(t, t[:, :1].contiguous(), None, axis=1)
+
+
+def test_fastdiv_exact(tmp_path):
+    exe = str(tmp_path / "fastdiv_check")
+    subprocess.run([swrt_build.HIPCC, "-x", "hip", f"--offload-arch={swrt_build.ARCH}", "-O2",
+                    "-I", os.path.join(ROOT, "include"),
+                    os.path.join(ROOT, "tests", "fastdiv_check.cpp"), "-o", exe],
+                   check=True, capture_output=True)
+    r = subprocess.run([exe], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout
+
+
+# ---------------------------------------------------------------------------
+# host validation (made-up addresses, never dereferenced)
+# ---------------------------------------------------------------------------
+
+A, B_, C_, D_ = 0x10_0000_0000, 0x20_0000_0000, 0x30_0000_0000, 0x40_0000_0000
+I64 = ctypes.c_int64
+
+
+def _shape(*d):
+    return (I64 * len(d))(*d)
+
+
+def _ts(L, present=A, past=A, update=B_, wi=None, shape=(2, 3, 16, 8), rank=None, axis=-2,
+        S=2, mode=0, bits=32, flags=None):
+    rank = len(shape) if rank is None else rank
+    return L.swrt_tensor_scatter(present, past, update, wi, _shape(*shape), rank, axis, S, mode,
+                                 bits, flags, None)
+
+
+@no_gpu_visible
+def test_tensor_scatter_rejects(L):
+    INV, UNS, OK = swrt.E_INVALID_ARG, swrt.E_UNSUPPORTED, swrt.OK
+    assert _ts(L, shape=(2, 3, 16, 8), rank=1) == INV
+    assert _ts(L, shape=(2,) * 9) == INV
+    for axis in (0, 4, -5, -4):
+        assert _ts(L, axis=axis) == INV
+    assert _ts(L, mode=2) == INV
+    for bits in (0, 12, 256):
+        assert _ts(L, bits=bits) == INV
+    assert _ts(L, S=17) == INV and _ts(L, S=-1) == INV
+    assert _ts(L, shape=(2, -3, 16, 8)) == INV
+    assert _ts(L, shape=(2, 3, 16, 3), bits=4) == UNS                   # 1.5-byte rows
+    assert _ts(L, present=0, past=0) == INV
+    assert _ts(L, update=0) == INV
+    assert _ts(L, present=A + 2, past=A + 2) == INV                     # fp32 misaligned
+    assert _ts(L, update=A + 64) == INV                                 # update inside present
+    assert _ts(L, present=A, past=A + 256) == INV                       # present overlaps past
+    assert _ts(L, wi=A + 8) == INV                                      # indices inside present
+    assert _ts(L, wi=B_ + 4 * 2 * 3 * 2 * 8 + 4) == INV                 # misaligned int64
+    # no-ops return OK without launching
+    assert _ts(L, shape=(0, 3, 16, 8)) == OK
+    assert _ts(L, shape=(2, 3, 16, 0)) == OK
+    assert _ts(L, S=0) == OK                                            # in place, empty update
+    # batched: mixing in-place and out-of-place tensors, too many tensors, a
+    # present shared by two tensors
+    V = ctypes.c_void_p
+    shp = _shape(2, 3, 16, 8)
+    st = L.swrt_tensor_scatter_batched(2, (V * 2)(A, C_), (V * 2)(A, D_), (V * 2)(B_, B_), None,
+                                       shp, 4, -2, 2, 0, 32, None, None)
+    assert st == INV
+    many = (V * 65)(*([A] * 65))
+    assert L.swrt_tensor_scatter_batched(65, many, many, many, None, shp, 4, -2, 2, 0, 32, None,
+                                         None) == INV
+    st = L.swrt_tensor_scatter_batched(2, (V * 2)(A, A), (V * 2)(A, A), (V * 2)(B_, B_), None,
+                                       shp, 4, -2, 2, 0, 32, None, None)
+    assert st == INV
+
+
+def _lens(L, sk=A, batch=4, S=1, C=8, T=B_, P=B_ + 0x1000, Lp=C_, Lt=C_ + 0x1000, E=D_):
+    return L.swrt_kv_seq_lengths(sk, batch, S, C, T, P, Lp, Lt, E, None, None)
+
+
+@no_gpu_visible
+def test_kv_seq_lengths_rejects(L):
+    INV = swrt.E_INVALID_ARG
+    assert _lens(L, batch=-1) == INV
+    assert _lens(L, S=0) == INV and _lens(L, C=0) == INV
+    assert _lens(L, sk=0) == INV and _lens(L, Lp=0) == INV and _lens(L, E=0) == INV
+    assert _lens(L, sk=A + 2) == INV and _lens(L, T=B_ + 4) == INV
+    assert _lens(L, Lt=C_ + 8) == INV                                   # overlaps Lp
+    assert _lens(L, E=A) == INV                                         # overlaps seqlens_k
+    assert _lens(L, batch=0) == swrt.OK
+
+
+def _win(L, kc=A, vc=A + 0x1000_0000, kn=B_, vn=B_ + 0x1000_0000, strides=None, ks=None, vs=None,
+         lp=D_, ev=D_ + 0x1000, batch=2, H=2, C=8, S=1, D=16, bits=16, phase=3):
+    strides = (I64 * 3)(*(strides or (H * S * D, S * D, D)))
+    return L.swrt_kv_window_append(kc, vc, kn, vn, strides, ks, vs, lp, ev, batch, H, C, S, D,
+                                   bits, phase, None, None)
+
+
+@no_gpu_visible
+def test_kv_window_append_rejects(L):
+    INV, UNS = swrt.E_INVALID_ARG, swrt.E_UNSUPPORTED
+    assert _win(L, C=0) == INV and _win(L, S=0) == INV
+    assert _win(L, batch=-1) == INV and _win(L, H=-1) == INV and _win(L, D=-1) == INV
+    assert _win(L, bits=24) == INV
+    assert _win(L, S=4, phase=0, ks=C_, vs=C_ + 0x1000_0000) == INV
+    assert _win(L, S=4, phase=4, ks=C_, vs=C_ + 0x1000_0000) == INV
+    assert _win(L, S=4) == INV                                          # staging missing
+    assert _win(L, strides=(-1, 16, 16)) == INV
+    assert _win(L, bits=4, D=3) == UNS                                  # odd 4-bit row
+    assert _win(L, kc=0) == INV and _win(L, lp=0) == INV
+    assert _win(L, vc=A + 64) == INV                                    # K and V caches overlap
+    assert _win(L, kn=A + 32) == INV                                    # new rows inside a cache
+    assert _win(L, S=4, ks=A + 512, vs=C_) == INV                       # staging inside a cache
+    assert _win(L, S=4, ks=C_, vs=C_ + 64) == INV                       # staging buffers overlap
+    assert _win(L, kc=A + 1) == INV                                     # bf16 misaligned
+    assert _win(L, lp=A + 16) == INV                                    # lengths inside a cache
+    assert _win(L, batch=0) == swrt.OK and _win(L, H=0) == swrt.OK and _win(L, D=0) == swrt.OK
+    arr = (ctypes.c_void_p * 33)(*([A] * 33))
+    st = L.swrt_kv_window_append_layers(33, arr, arr, arr, arr, (I64 * 3)(32, 16, 16), None, None,
+                                        D_, D_ + 0x1000, 2, 2, 8, 1, 16, 16, 3, None, None)
+    assert st == INV
+    # the same cache in two layers
+    kcs = (ctypes.c_void_p * 2)(A, A)
+    vcs = (ctypes.c_void_p * 2)(A + 0x1000_0000, A + 0x2000_0000)
+    kns = (ctypes.c_void_p * 2)(B_, B_)
+    st = L.swrt_kv_window_append_layers(2, kcs, vcs, kns, kns, (I64 * 3)(32, 16, 16), None, None,
+                                        D_, D_ + 0x1000, 2, 2, 8, 1, 16, 16, 3, None, None)
+    assert st == INV

@@ -1,0 +1,559 @@
+"""GPU parity: libswrt (HIP, gfx950) against the CPU oracle, byte for byte.
+
+The path only moves bits, so every comparison has tolerance 0: whole output
+buffers (caches, staging, length arrays, flag words) are compared as bytes
+after each call. Inputs come from the seeded generators in
+sliding_window_ring_tensor_amd.workloads; the oracle gets host copies of the
+same inputs and computes its own lengths from seqlens_k. Device buffers sit
+inside guard bands of known bytes, which must be unchanged after each call.
+"""
+from __future__ import annotations
+
+import ctypes
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sliding_window_ring_tensor_amd as swrt
+from sliding_window_ring_tensor_amd import workloads as wl
+from sliding_window_ring_tensor_amd.decode_step import ModelDecodeStep
+from tests import replay
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+HERE = os.path.dirname(os.path.abspath(__file__))
+GUARD = 4096
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    swrt.lib()  # fails loudly when the library is missing
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.get()
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def hb(t: torch.Tensor) -> np.ndarray:
+    """Host bytes of a tensor (any dtype), shape [..., last * itemsize]."""
+    t = t.detach().contiguous().cpu()
+    if t.dim() == 0:
+        t = t.reshape(1)
+    return t.view(torch.uint8).numpy()
+
+
+class Guarded:
+    """A device tensor inside a uint8 buffer with guard bands on both sides,
+    optionally starting `offset` bytes past a 256-byte boundary."""
+
+    def __init__(self, host: torch.Tensor | None, shape=None, dtype=None, offset: int = 0,
+                 seed: int = 0):
+        shape = tuple(host.shape) if host is not None else tuple(shape)
+        dtype = host.dtype if host is not None else dtype
+        es = torch.empty((), dtype=dtype).element_size()
+        n = int(np.prod(shape)) * es if len(shape) else es
+        g = np.random.default_rng(seed)
+        self.fill = torch.from_numpy(g.integers(0, 256, size=n + 2 * GUARD + offset,
+                                                dtype=np.uint8))
+        self.buf = self.fill.to(DEV)
+        self.lo, self.hi = GUARD + offset, GUARD + offset + n
+        self.t = self.buf[self.lo:self.hi].view(dtype).view(shape)
+        if host is not None:
+            self.t.copy_(host.to(DEV))
+
+    def check(self, what=""):
+        b = self.buf.cpu()
+        assert torch.equal(b[:self.lo], self.fill[:self.lo]), f"guard before {what} overwritten"
+        assert torch.equal(b[self.hi:], self.fill[self.hi:]), f"guard after {what} overwritten"
+
+
+def flag_word():
+    return torch.zeros(1, dtype=torch.int32, device=DEV)
+
+
+# ---------------------------------------------------------------------------
+# TensorScatter
+# ---------------------------------------------------------------------------
+
+def run_scatter(orc, past_h, upd_h, wi, axis, mode, in_place, offset=0, bits=None,
+                logical_shape=None):
+    """GPU and oracle on the same inputs; assert bytes and flags agree."""
+    bits = bits or past_h.element_size() * 8
+    shape = logical_shape or tuple(past_h.shape)
+    rank = len(shape)
+    ax = axis + rank if axis < 0 else axis
+    S = upd_h.shape[ax]  # packed 4-bit rows keep S on the sequence axis
+    past_g = Guarded(past_h, offset=offset, seed=1)
+    upd_g = Guarded(upd_h, offset=offset, seed=2)
+    out_g = past_g if in_place else Guarded(None, past_h.shape, past_h.dtype, offset, seed=3)
+    wi_d = None if wi is None else torch.from_numpy(np.asarray(wi, np.int64)).to(DEV)
+    flags = flag_word()
+    st = swrt.lib().swrt_tensor_scatter(
+        ctypes.c_void_p(out_g.t.data_ptr()), ctypes.c_void_p(past_g.t.data_ptr()),
+        ctypes.c_void_p(upd_g.t.data_ptr()),
+        None if wi_d is None else ctypes.c_void_p(wi_d.data_ptr()),
+        (ctypes.c_int64 * rank)(*shape), rank, axis, S,
+        swrt.MODE_CIRCULAR if mode == "circular" else swrt.MODE_LINEAR, bits,
+        ctypes.c_void_p(flags.data_ptr()),
+        ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == swrt.OK
+    pb, ub = hb(past_h).copy(), hb(upd_h)
+    present = pb if in_place else np.empty_like(pb)
+    ost, of = orc.tensor_scatter_raw(present, pb, ub, wi, shape, axis, S,
+                                     oracle.MODE_CIRCULAR if mode == "circular" else 0, bits)
+    assert ost == oracle.OK
+    torch.cuda.synchronize()
+    assert flags.item() == of
+    np.testing.assert_array_equal(hb(out_g.t), present)
+    for g, n in ((past_g, "past"), (upd_g, "update"), (out_g, "present")):
+        g.check(n)
+    if not in_place:
+        np.testing.assert_array_equal(hb(past_g.t), hb(past_h))  # past never written
+
+
+def _examples():
+    with open(os.path.join(HERE, "golden", "tensorscatter_examples.json")) as f:
+        return json.load(f)["examples"]
+
+
+@pytest.mark.parametrize("ex", _examples(), ids=lambda e: e["name"])
+@pytest.mark.parametrize("in_place", [False, True])
+def test_page_examples(ex, in_place):
+    past = torch.tensor(ex["past_cache"]["values"], dtype=torch.float32, device=DEV)
+    upd = torch.tensor(ex["update"]["values"], dtype=torch.float32, device=DEV)
+    wi = torch.tensor(ex["write_indices"]["values"], dtype=torch.int64, device=DEV)
+    got = swrt.tensor_scatter(past, upd, wi, axis=ex["axis"], mode=ex["mode"],
+                              out=past if in_place else None)
+    torch.cuda.synchronize()
+    want = np.array(ex["present_cache"]["values"], dtype=np.float32)
+    np.testing.assert_array_equal(got.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("raw_bits", [False, True])
+@pytest.mark.parametrize("in_place", [True, False])
+def test_workload1_linear_fp32(orc, raw_bits, in_place):
+    case = wl.workload1()
+    say("workload1", case.name, raw_bits, in_place)
+    past, upd = wl.scatter_payloads(case, raw_bits=raw_bits)
+    run_scatter(orc, past, upd, case.write_indices, case.axis, case.mode, in_place)
+
+
+@pytest.mark.parametrize("raw_bits", [False, True])
+def test_workload2_circular_two_steps(orc, raw_bits):
+    """Step A (S=1) then step B (S=512) on the same bf16 cache, in place,
+    compared after each step."""
+    a, b = wl.workload2()
+    say("workload2", raw_bits)
+    cache_h, _ = wl.scatter_payloads(a, raw_bits=raw_bits)
+    _, upd_a = wl.scatter_payloads(a, raw_bits=raw_bits)
+    _, upd_b = wl.scatter_payloads(b, raw_bits=raw_bits)
+    cache_d = cache_h.to(DEV)
+    host = hb(cache_h).copy()
+    flags = flag_word()
+    for case, upd in ((a, upd_a), (b, upd_b)):
+        wi_d = torch.from_numpy(case.write_indices).to(DEV)
+        swrt.tensor_scatter(cache_d, upd.to(DEV), wi_d, axis=case.axis, mode=case.mode,
+                            out=cache_d, flags=flags)
+        st, f = orc.tensor_scatter_raw(host, host, hb(upd), case.write_indices, case.shape,
+                                       case.axis, case.seq_len, oracle.MODE_CIRCULAR, 16)
+        assert st == 0 and f == 0
+        torch.cuda.synchronize()
+        assert flags.item() == 0
+        np.testing.assert_array_equal(hb(cache_d), host, err_msg=case.name)
+    # the S=512 writes wrap for the entries whose index is above M - S
+    assert (b.write_indices > 4096 - 512).any()
+
+
+_DTYPES = [torch.uint8, torch.bfloat16, torch.float32, torch.float64, torch.complex128,
+           torch.float8_e4m3fn, torch.int16, torch.bool]
+
+
+def _fuzz_cases(n=70, seed=123):
+    g = np.random.default_rng(seed)
+    for k in range(n):
+        rank = int(g.integers(2, 6))
+        shape = [int(g.integers(1, 5)) for _ in range(rank)]
+        axis = int(g.integers(1, rank))
+        shape[axis] = int(g.integers(1, 40))
+        if g.random() < 0.3:  # a long row or a large cache: several tiles, ragged tail
+            shape[-1 if axis != rank - 1 else 0] = int(g.integers(20, 300))
+        dtype = _DTYPES[k % len(_DTYPES)]
+        es = torch.empty((), dtype=dtype).element_size()
+        M = shape[axis]
+        S = int(g.choice([0, 1, M - 1, M, int(g.integers(0, M + 1))]))
+        mode = "circular" if g.random() < 0.5 else "linear"
+        B = shape[0]
+        if mode == "circular":
+            wi = g.integers(-3 * M, 3 * M, size=B)
+        else:
+            wi = g.integers(0, M - S + 1, size=B)
+            if g.random() < 0.2:
+                wi[int(g.integers(0, B))] = int(g.choice([-1, M - S + 1, 1 << 40]))
+        if g.random() < 0.15:
+            wi = None
+        offset = int(g.choice([0, es, 2 * es, 4 * es, 8 * es])) if es < 16 else 0
+        yield pytest.param(tuple(shape), axis - rank if g.random() < 0.3 else axis, S, mode,
+                           dtype, wi, bool(g.random() < 0.5), offset, int(g.integers(1 << 30)),
+                           id=f"{k}-{tuple(shape)}-ax{axis}-S{S}-{mode}-{str(dtype)[6:]}")
+
+
+@pytest.mark.parametrize("shape,axis,S,mode,dtype,wi,in_place,offset,seed", list(_fuzz_cases()))
+def test_tensor_scatter_fuzz(orc, shape, axis, S, mode, dtype, wi, in_place, offset, seed):
+    say("fuzz", shape, axis, S, mode, dtype, in_place, offset)
+    rank = len(shape)
+    ax = axis + rank if axis < 0 else axis
+    ushape = list(shape)
+    ushape[ax] = S
+    past = wl.host_payload(wl.rng(seed), shape, dtype, raw_bits=True)
+    upd = wl.host_payload(wl.rng(seed + 1), ushape, dtype, raw_bits=True)
+    run_scatter(orc, past, upd, wi, axis, mode, in_place, offset=offset)
+
+
+@pytest.mark.parametrize("in_place", [True, False])
+@pytest.mark.parametrize("mode", ["linear", "circular"])
+def test_tensor_scatter_int4_rows(orc, in_place, mode):
+    """4-bit elements: logical rows of 10 nibbles (5 bytes) and 6 nibbles."""
+    g = np.random.default_rng(5)
+    for logical in ((3, 2, 9, 10), (2, 7, 6)):
+        say("int4", logical, mode, in_place)
+        row_bytes = logical[-1] // 2
+        pshape = (*logical[:-1], row_bytes)
+        S = 4 if len(logical) == 4 else 3
+        ushape = list(pshape)
+        ushape[-2] = S
+        past = torch.from_numpy(g.integers(0, 256, size=pshape, dtype=np.uint8))
+        upd = torch.from_numpy(g.integers(0, 256, size=ushape, dtype=np.uint8))
+        M = logical[-2]
+        wi = g.integers(0, M - S + 1, size=logical[0]) if mode == "linear" else \
+            g.integers(-M, 2 * M, size=logical[0])
+        run_scatter(orc, past, upd, wi, -2, mode, in_place, bits=4, logical_shape=logical)
+
+
+def test_tensor_scatter_batched_matches_single(orc):
+    """The batched entry point gives what one call per tensor gives."""
+    g = np.random.default_rng(9)
+    shape, S = (4, 3, 50, 24), 5
+    pasts = [wl.host_payload(g, shape, torch.bfloat16, True) for _ in range(6)]
+    upds = [wl.host_payload(g, (4, 3, S, 24), torch.bfloat16, True) for _ in range(6)]
+    wi = g.integers(-60, 60, size=4)
+    wi_d = torch.from_numpy(wi).to(DEV)
+    for mode in ("linear", "circular"):
+        w = np.clip(wi, 0, 50 - S) if mode == "linear" else wi
+        w_d = torch.from_numpy(w).to(DEV)
+        dev = [p.to(DEV) for p in pasts]
+        swrt.tensor_scatter_batched(dev, [u.to(DEV) for u in upds], w_d, axis=2, mode=mode,
+                                    outs=dev)
+        outs = swrt.tensor_scatter_batched([p.to(DEV) for p in pasts], [u.to(DEV) for u in upds],
+                                           w_d, axis=2, mode=mode)
+        torch.cuda.synchronize()
+        for p, u, d, o in zip(pasts, upds, dev, outs):
+            want, _ = orc.tensor_scatter(p.view(torch.int16).numpy(), u.view(torch.int16).numpy(),
+                                         w, axis=2, mode=mode)
+            np.testing.assert_array_equal(d.cpu().view(torch.int16).numpy(), want)
+            np.testing.assert_array_equal(o.cpu().view(torch.int16).numpy(), want)
+    del wi_d
+
+
+def test_tensor_scatter_rejects_real_buffers():
+    # update inside present: rejected before anything is launched
+    big = torch.zeros(2 * 4 * 8 * 16 + 2 * 4 * 2 * 16, device=DEV)
+    pres = big[:2 * 4 * 8 * 16].view(2, 4, 8, 16)
+    upd = big[100:100 + 2 * 4 * 2 * 16].view(2, 4, 2, 16)
+    with pytest.raises(swrt.SwrtError) as e:
+        swrt.tensor_scatter(pres, upd, None, out=pres)
+    assert e.value.status == swrt.E_INVALID_ARG
+
+
+# ---------------------------------------------------------------------------
+# windowed step: lengths
+# ---------------------------------------------------------------------------
+
+def run_lengths(orc, sk: np.ndarray, S: int, C: int):
+    flags = flag_word()
+    got = swrt.kv_seq_lengths(torch.from_numpy(sk.astype(np.int32)).to(DEV), S, C, flags=flags)
+    want = orc.kv_seq_lengths(sk, S, C)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(got.total.cpu().numpy(), want.total)
+    np.testing.assert_array_equal(got.past.cpu().numpy(), want.past)
+    np.testing.assert_array_equal(got.cache_past.cpu().numpy(), want.cache_past)
+    np.testing.assert_array_equal(got.cache_total.cpu().numpy(), want.cache_total)
+    np.testing.assert_array_equal(got.evict.cpu().numpy(), want.evict)
+    assert flags.item() == want.flags
+    return got, want
+
+
+def test_lengths_workloads_and_edges(orc):
+    g = np.random.default_rng(17)
+    run_lengths(orc, wl.workload3().seqlens_k, 1, 128)
+    c4, _ = wl.workload4()
+    run_lengths(orc, c4.seqlens_k, 256, 4096)
+    run_lengths(orc, wl.workload5().seqlens_k, 1, 128)
+    edges = np.array([-5, -1, 0, 1, 126, 127, 128, 129, 4095, 4096, 4351, 2**31 - 1, -2**31],
+                     dtype=np.int64)
+    for S, C in ((1, 128), (256, 4096), (300, 100), (1, 1), (7, 3)):
+        run_lengths(orc, edges.astype(np.int32), S, C)
+    for B in (1, 63, 64, 65, 257, 1000):  # several workgroups, ragged tail
+        run_lengths(orc, g.integers(-10, 20000, size=B).astype(np.int32), 3, 64)
+
+
+# ---------------------------------------------------------------------------
+# windowed step: shift + append, stage + commit
+# ---------------------------------------------------------------------------
+
+def run_window(orc, kc, vc, kn, vn, sk, S, C, ks=None, vs=None, phase="all", offset=0,
+               bsnh=False, split=False):
+    """One step on the GPU and in the oracle; assert all buffers agree."""
+    B, H, _, D = kc.shape
+    bits = kc.element_size() * 8
+    gs = [Guarded(t, offset=offset, seed=i) for i, t in enumerate((kc, vc))]
+    if bsnh:  # new rows stored [B, S, H, D], passed as a [B, H, S, D] view
+        kn_s, vn_s = kn.transpose(1, 2).contiguous(), vn.transpose(1, 2).contiguous()
+        gn = [Guarded(t, offset=offset, seed=5 + i) for i, t in enumerate((kn_s, vn_s))]
+        kn_v, vn_v = gn[0].t.transpose(1, 2), gn[1].t.transpose(1, 2)
+        strides = (S * H * D, D, H * D)
+        kn_flat, vn_flat = hb(kn_s), hb(vn_s)
+    else:
+        gn = [Guarded(t, offset=offset, seed=5 + i) for i, t in enumerate((kn, vn))]
+        kn_v, vn_v = gn[0].t, gn[1].t
+        strides = (H * S * D, S * D, D)
+        kn_flat, vn_flat = hb(kn), hb(vn)
+    gst = [Guarded(t, offset=offset, seed=8 + i) for i, t in enumerate((ks, vs))] \
+        if ks is not None else [None, None]
+    f1, f2 = flag_word(), flag_word()
+    lens = swrt.kv_seq_lengths(torch.from_numpy(sk.astype(np.int32)).to(DEV), S, C, flags=f1)
+    phases = ["stage", "commit"] if split else [phase]
+    for ph in phases:
+        swrt.kv_window_append(gs[0].t, gs[1].t, kn_v, vn_v, lens.cache_past, lens.evict,
+                              k_staging=None if gst[0] is None else gst[0].t,
+                              v_staging=None if gst[1] is None else gst[1].t, phase=ph, flags=f2)
+    # oracle on host copies
+    L = orc.kv_seq_lengths(sk, S, C)
+    hk, hv = hb(kc).copy(), hb(vc).copy()
+    hks = None if ks is None else hb(ks).copy()
+    hvs = None if vs is None else hb(vs).copy()
+    for ph in phases:
+        code = {"all": oracle.PHASE_ALL, "stage": oracle.PHASE_STAGE,
+                "commit": oracle.PHASE_COMMIT}[ph]
+        of = orc.kv_window_append_strided(hk, hv, kn_flat, vn_flat, strides, S, L.cache_past,
+                                          L.evict, hks, hvs, code, bits, head_dim=D)
+    torch.cuda.synchronize()
+    assert f1.item() == L.flags
+    assert f2.item() == of
+    np.testing.assert_array_equal(hb(gs[0].t), hk, err_msg="K cache")
+    np.testing.assert_array_equal(hb(gs[1].t), hv, err_msg="V cache")
+    if ks is not None:
+        np.testing.assert_array_equal(hb(gst[0].t), hks, err_msg="K staging")
+        np.testing.assert_array_equal(hb(gst[1].t), hvs, err_msg="V staging")
+    for g in [*gs, *gn, *[x for x in gst if x is not None]]:
+        g.check()
+    return L
+
+
+@pytest.mark.parametrize("draw", ["literal", "stratified", "raw_bits"])
+def test_workload3_decode_in_place(orc, draw):
+    case = wl.workload3()
+    say("workload3", draw)
+    sk = case.seqlens_k if draw != "stratified" else \
+        wl.stratified_seqlens(wl.rng(33), case.batch, case.capacity, 1)
+    kc, vc, kn, vn = wl.window_payloads(case, raw_bits=draw == "raw_bits")
+    L = run_window(orc, kc, vc, kn, vn, sk, 1, case.capacity)
+    if draw == "stratified":
+        assert (L.evict == 0).any() and (L.evict == 1).any()
+
+
+@pytest.mark.parametrize("phase", ["all", "split", "stage"])
+def test_workload4_staged(orc, phase):
+    case, _ = wl.workload4()
+    say("workload4", phase)
+    kc, vc, kn, vn, ks, vs = wl.window_payloads(case, raw_bits=True, staging=True)
+    run_window(orc, kc, vc, kn, vn, case.seqlens_k, case.seq_len, case.capacity, ks, vs,
+               phase="stage" if phase == "stage" else "all", split=phase == "split")
+
+
+def test_workload4_stratified_lengths(orc):
+    case, _ = wl.workload4()
+    sk = wl.stratified_seqlens(wl.rng(44), 8, case.capacity, case.seq_len, hi=16384 + 255)
+    c = wl.WindowCase(case.name, 8, 4, case.capacity, case.seq_len, 64, torch.bfloat16, sk, 4, 7)
+    kc, vc, kn, vn, ks, vs = wl.window_payloads(c, raw_bits=True, staging=True)
+    L = run_window(orc, kc, vc, kn, vn, sk, c.seq_len, c.capacity, ks, vs)
+    assert (L.evict == 0).any() and (L.evict > 0).any()
+
+
+def _window_cases():
+    g = np.random.default_rng(77)
+    dts = [torch.bfloat16, torch.float8_e4m3fn, torch.float32, torch.float64, torch.int16,
+           torch.uint8]
+    for k in range(40):
+        B, H = int(g.integers(1, 6)), int(g.integers(1, 5))
+        C = int(g.choice([1, 2, 5, 16, 128, 300]))
+        D = int(g.choice([1, 3, 5, 8, 24, 64, 80, 128, 300]))
+        S = int(g.choice([1, 1, 2, 3, C, C + 1, 2 * C + 1]))
+        dt = dts[k % len(dts)]
+        es = torch.empty((), dtype=dt).element_size()
+        yield pytest.param(B, H, C, S, D, dt, int(g.choice([0, es, 4 * es])) if es < 8 else 0,
+                           bool(g.random() < 0.3), int(g.integers(1 << 30)),
+                           id=f"{k}-B{B}H{H}C{C}S{S}D{D}-{str(dt)[6:]}")
+
+
+@pytest.mark.parametrize("B,H,C,S,D,dtype,offset,bsnh,seed", list(_window_cases()))
+def test_window_fuzz(orc, B, H, C, S, D, dtype, offset, bsnh, seed):
+    say("window fuzz", B, H, C, S, D, dtype, offset, bsnh)
+    g = wl.rng(seed)
+    sk = g.integers(S - 1, 3 * C + S + 5, size=B).astype(np.int32)
+    kc = wl.host_payload(g, (B, H, C, D), dtype, True)
+    vc = wl.host_payload(g, (B, H, C, D), dtype, True)
+    kn = wl.host_payload(g, (B, H, S, D), dtype, True)
+    vn = wl.host_payload(g, (B, H, S, D), dtype, True)
+    ks = vs = None
+    if S > 1:
+        ks = wl.host_payload(g, (B, H, C + S, D), dtype, True)
+        vs = wl.host_payload(g, (B, H, C + S, D), dtype, True)
+    run_window(orc, kc, vc, kn, vn, sk, S, C, ks, vs, offset=offset, bsnh=bsnh)
+
+
+@pytest.mark.parametrize("C,D", [(4096, 128), (1000, 40), (513, 8)])
+def test_window_in_place_multi_tile_shift(orc, C, D):
+    """S = 1 slices much larger than one tile: the ascending-tile shift must
+    never read a row after another tile has written it. Repeated steps."""
+    g = wl.rng(C)
+    B, H = 3, 4
+    kc = wl.host_payload(g, (B, H, C, D), torch.bfloat16, True)
+    vc = wl.host_payload(g, (B, H, C, D), torch.bfloat16, True)
+    for step in range(4):
+        say("multi-tile shift", C, D, step)
+        kn = wl.host_payload(g, (B, H, 1, D), torch.bfloat16, True)
+        vn = wl.host_payload(g, (B, H, 1, D), torch.bfloat16, True)
+        sk = np.array([C + 5, C - 1, 3 * C], dtype=np.int32)
+        run_window(orc, kc, vc, kn, vn, sk, 1, C)
+
+
+def test_window_replay_histories(orc):
+    """Tagged token histories, step after step on the GPU, against the oracle
+    and against the window invariant itself."""
+    B, H, D = 3, 2, 8
+    for C in (1, 2, 8, 16):
+        for name, sched in replay.schedules(C).items():
+            say("replay", C, name)
+            k, v = replay.fresh_cache(B, H, C, D)
+            kd, vd = torch.from_numpy(k).to(DEV), torch.from_numpy(v).to(DEV)
+            T = np.zeros(B, np.int64)
+            for S in sched:
+                Ta = T + S
+                sk_d = torch.from_numpy((Ta - 1).astype(np.int32)).to(DEV)
+                lens = swrt.kv_seq_lengths(sk_d, S, C)
+                kn, vn = replay.new_block(B, H, T, S, D)
+                kw = vw = None
+                if S > 1:
+                    kw, vw = (torch.from_numpy(x).to(DEV) for x in
+                              replay.fresh_cache(B, H, C + S, D, tensors=(2, 3)))
+                swrt.kv_window_append(kd, vd, torch.from_numpy(kn).to(DEV),
+                                      torch.from_numpy(vn).to(DEV), lens.cache_past, lens.evict,
+                                      k_staging=kw, v_staging=vw)
+                T = Ta
+                torch.cuda.synchronize()
+                replay.check_window(kd.cpu().numpy(), vd.cpu().numpy(), T, C)
+
+
+def test_window_bad_lengths_flag_and_skip(orc):
+    B, H, C, D = 4, 2, 8, 16
+    g = wl.rng(3)
+    kc = wl.host_payload(g, (B, H, C, D), torch.bfloat16, True)
+    vc = wl.host_payload(g, (B, H, C, D), torch.bfloat16, True)
+    kn = wl.host_payload(g, (B, H, 1, D), torch.bfloat16, True)
+    vn = wl.host_payload(g, (B, H, 1, D), torch.bfloat16, True)
+    lp = np.array([3, 9, 8, -1], np.int32)
+    ev = np.array([0, 0, 0, 0], np.int32)
+    kd, vd = kc.to(DEV), vc.to(DEV)
+    flags = flag_word()
+    swrt.kv_window_append(kd, vd, kn.to(DEV), vn.to(DEV), torch.from_numpy(lp).to(DEV),
+                          torch.from_numpy(ev).to(DEV), flags=flags)
+    hk, hv = hb(kc).copy(), hb(vc).copy()
+    of = orc.kv_window_append_strided(hk, hv, hb(kn), hb(vn), (H * D, D, D), 1, lp, ev,
+                                      elem_bits=16, head_dim=D)
+    torch.cuda.synchronize()
+    assert flags.item() == of == swrt.FLAG_BAD_LENGTHS
+    np.testing.assert_array_equal(hb(kd), hk)
+    np.testing.assert_array_equal(hb(vd), hv)
+
+
+def test_window_graph_replays():
+    """The decode step captured in a graph: every replay matches eager."""
+    case = wl.workload3()
+    kc, vc, kn, vn = wl.window_payloads(case)
+    sk_d = torch.from_numpy(case.seqlens_k).to(DEV)
+    eager = [kc.to(DEV), vc.to(DEV)]
+    graphed = [kc.to(DEV), vc.to(DEV)]
+    knd, vnd = kn.to(DEV), vn.to(DEV)
+    lens_e = swrt.kv_seq_lengths(sk_d, 1, 128)
+    lens_g = swrt.WindowLengths(*(torch.zeros_like(t) for t in lens_e))
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            swrt.kv_seq_lengths(sk_d, 1, 128, out=lens_g)
+            swrt.kv_window_append(graphed[0], graphed[1], knd, vnd, lens_g.cache_past,
+                                  lens_g.evict)
+    for rep in range(5):
+        g.replay()
+        swrt.kv_window_append(eager[0], eager[1], knd, vnd, lens_e.cache_past, lens_e.evict)
+        torch.cuda.synchronize()
+        assert torch.equal(hb_t(graphed[0]), hb_t(eager[0])), rep
+        assert torch.equal(hb_t(graphed[1]), hb_t(eager[1])), rep
+
+
+def hb_t(t):
+    return t.view(torch.uint8)
+
+
+# ---------------------------------------------------------------------------
+# the whole-model decode step at full size, in the benchmark's launch shape
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float8_e4m3fn])
+def test_workload5_model_step_full_size(orc, dtype):
+    spec = wl.workload5(dtype)
+    say("workload5", dtype)
+    step = ModelDecodeStep(spec, DEV, set_id=0, raw_bits=True)
+    b = step.buffers
+    win_before = [(hb(k).copy(), hb(v).copy()) for k, v in zip(b.win_k, b.win_v)]
+    sample = [0, len(b.full_k) - 1]  # full layers compared whole; the rest by their new rows
+    full_before = {i: (hb(b.full_k[i]).copy(), hb(b.full_v[i]).copy()) for i in sample}
+    step.run()
+    torch.cuda.synchronize()
+    assert b.flags.item() == 0
+    L = orc.kv_seq_lengths(spec.seqlens_k, 1, spec.window)
+    np.testing.assert_array_equal(b.lengths.cache_past.cpu().numpy(), L.cache_past)
+    np.testing.assert_array_equal(b.lengths.evict.cpu().numpy(), L.evict)
+    D, H = spec.head_dim, spec.kv_heads
+    bits = torch.empty((), dtype=dtype).element_size() * 8
+    for i, (hk, hv) in enumerate(win_before):
+        of = orc.kv_window_append_strided(hk, hv, hb(b.win_kn[i]), hb(b.win_vn[i]),
+                                          (H * D, D, D), 1, L.cache_past, L.evict,
+                                          elem_bits=bits, head_dim=D)
+        assert of == 0
+        np.testing.assert_array_equal(hb(b.win_k[i]), hk, err_msg=f"windowed layer {i} K")
+        np.testing.assert_array_equal(hb(b.win_v[i]), hv, err_msg=f"windowed layer {i} V")
+    for i, (hk, hv) in full_before.items():
+        for cache, new, host in ((b.full_k[i], b.full_kn[i], hk), (b.full_v[i], b.full_vn[i], hv)):
+            st, f = orc.tensor_scatter_raw(host, host, hb(new), spec.write_indices,
+                                           tuple(cache.shape), 2, 1, 0, bits)
+            assert st == 0 and f == 0
+            np.testing.assert_array_equal(hb(cache), host, err_msg=f"full layer {i}")
+    # every other full layer: the row at T - 1 holds the new row
+    wi = torch.from_numpy(spec.write_indices).to(DEV)
+    bi = torch.arange(spec.batch, device=DEV)
+    for cache, new in zip(b.full_k + b.full_v, b.full_kn + b.full_vn):
+        got = cache.view(torch.uint8)[bi, :, wi, :]  # [B, H, row bytes]
+        assert torch.equal(got, new.view(torch.uint8)[:, :, 0, :])
