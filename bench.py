@@ -14,9 +14,10 @@ Measurement
   - Infinity Cache: every buffer set is independent and --sets sets (default
     3, over 512 MB of windowed caches touched between two uses of one set)
     are visited round robin, so no step finds its data in the 256 MB cache.
-  - roofline: the dominant kernel (window shift + append, 12 layers) timed
-    with HIP events on the launch stream around each launch of an eager pass
-    of K steps; achieved = its algorithmic bytes / its mean duration.
+  - roofline: the dominant kernel (window shift + append, 12 layers) launched
+    K times back to back (buffer sets round robin) between one pair of HIP
+    events on the launch stream; achieved = its algorithmic bytes / its mean
+    launch duration.
   - cpu_baseline: the CPU oracle (single thread) on the same step, host copies
     of the same inputs, for a bounded number of steps.
 
@@ -38,6 +39,25 @@ import numpy as np  # noqa: E402
 import torch  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD's published peak
+
+# HBM bytes per launch of the dominant kernel from two rocprofv3 counter passes
+# (FETCH_SIZE, WRITE_SIZE), each scaled by what the counter reads for a 1 GiB
+# copy; valid only for the kernel source they were taken on (its hash).
+MEASURED_TRAFFIC = {
+    ("bf16", "95cd5dbdd486ab6d"): {"read": 195_607_466, "written": 195_531_263},
+}
+TRAFFIC_SOURCES = ("sliding_window_ring_tensor_amd/csrc/kv_window.hip",
+                   "sliding_window_ring_tensor_amd/csrc/swrt_device.hpp")
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def log(*a):
@@ -136,44 +156,65 @@ def main():
         torch.cuda.synchronize()
         graph_s = (time.perf_counter() - t0) / K
 
-        # ---- eager pass: events around the dominant kernel ----
+        # ---- dominant kernel alone and the eager step: HIP events ----
+        # The host needs longer to issue a launch than the GPU to run it. A
+        # sleep kernel issued first keeps the GPU busy while the host queues
+        # a whole timed block, so one pair of events on the launch stream
+        # brackets back-to-back kernel execution, not host gaps.
+        t0 = time.perf_counter()
         for i in range(W):
             steps[i % len(steps)].run()
         torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(K)]
-        log(f"timing {K} eager steps ...")
-        t0 = time.perf_counter()
-        for i in range(K):
-            st = steps[i % len(steps)]
-            st.lengths()
-            ev[i][0].record(stream)
-            st.windowed()
-            ev[i][1].record(stream)
-            st.full()
+        host_step_s = (time.perf_counter() - t0) / max(W, 1)
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
+        torch.cuda._sleep(1_000_000)
+        s1.record(stream)
         torch.cuda.synchronize()
-        eager_s = (time.perf_counter() - t0) / K
-        win_ms = [a.elapsed_time(b) for a, b in ev]
+        cycles_per_s = 1_000_000 / (s0.elapsed_time(s1) * 1e-3)
 
-        # ---- achievable reference: a 1 GiB device-to-device copy ----
+        def events_block(fn):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda._sleep(int(cycles_per_s * min(2.0, 2.0 * K * host_step_s + 0.05)))
+            a.record(stream)
+            for i in range(K):
+                fn(steps[i % len(steps)])
+            b.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) * 1e-3 / K
+
+        log(f"timing {K} launches of the window kernel ...")
+        win_mean_s = events_block(lambda st: st.windowed())
+        log(f"timing {K} eager steps ...")
+        eager_s = events_block(lambda st: st.run())
+
+        # ---- achievable reference: 1 GiB device-to-device copies ----
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         src.fill_(1)
-        dst.copy_(src)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(10):
-            dst.copy_(src)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        copy_gbs = 2 * (1 << 30) * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
-        del src, dst
+
+        def copy_gbs(fn, n=10):
+            fn()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(n):
+                fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            return 2 * (1 << 30) * n / (a.elapsed_time(b) * 1e-3) / 1e9
+
+        torch_copy = copy_gbs(lambda: dst.copy_(src))
+        # the library's own copy engine: TensorScatter out of place, S = 0
+        s3, d3 = src.view(1, 1 << 26, 16), dst.view(1, 1 << 26, 16)
+        swrt_copy = copy_gbs(lambda: swrt.tensor_scatter(s3, s3[:, :0], None, axis=1, out=d3))
+        del src, dst, s3, d3
 
     flags = [int(st.buffers.flags.item()) for st in steps]
     if any(flags):
         raise SystemExit(f"device flags raised during the benchmark: {flags}")
-    win_mean_s = float(np.mean(win_ms)) * 1e-3
     achieved = acct["windowed"] / win_mean_s / 1e9
+    meas = MEASURED_TRAFFIC.get((args.dtype, kernel_source_hash()))
+    traffic = None if meas is None else meas["read"] + meas["written"]
     value = acct["total"] / graph_s / 1e9
 
     cpu = None
@@ -218,14 +259,15 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": traffic,
             "bytes_per_launch": acct["windowed"],
             "mean_launch_us": round(win_mean_s * 1e6, 3),
         },
         "cpu_baseline": cpu,
         "eager": {"us_per_step": round(eager_s * 1e6, 2),
                   "value": round(acct["total"] / eager_s / 1e9, 2)},
-        "copy_reference_gbs": round(copy_gbs, 1),
+        "copy_reference_gbs": {"torch_copy": round(torch_copy, 1),
+                               "swrt_tensor_scatter_copy": round(swrt_copy, 1)},
         "env": {"gpu": torch.cuda.get_device_name(dev), "torch": torch.__version__,
                 "hip": torch.version.hip, "host": platform.node()},
     }

@@ -34,7 +34,10 @@
 namespace swrt {
 namespace {
 
-constexpr int kUnroll = 4;      // words per thread per tile
+#ifndef SWRT_WINDOW_UNROLL
+#define SWRT_WINDOW_UNROLL 4
+#endif
+constexpr int kUnroll = SWRT_WINDOW_UNROLL;  // words per thread per tile
 constexpr int kMaxLayers = SWRT_MAX_LAYERS;  // layers per batched launch
 
 template <int NL>

@@ -8,10 +8,10 @@ Recipe (shared by tests and benchmark):
   - index and length draws: numpy Generator(PCG64(seed)), seed = workload number;
   - payloads: U[-1, 1) fp32 rounded to the payload dtype by torch (round to
     nearest even), or uniform random bytes for the raw-bits variants (every
-    NaN / Inf / fp8 encoding appears). Small payloads are drawn on the host
-    from the same PCG64 stream; large ones on their device with a torch
-    generator seeded from (seed, buffer id), since a 12 GiB host draw would
-    dominate every run.
+    NaN / Inf / fp8 encoding appears). Host payloads come from
+    PCG64(seed * 1000 + buffer id); large ones are drawn on their device with
+    a torch generator seeded from (seed, buffer id), since a 12 GiB host draw
+    would dominate every run.
 
 Workloads (sizes and distributions):
   1  TensorScatter linear, fp32 past [2,2,16,8], update [2,2,3,8],
@@ -62,6 +62,8 @@ def host_payload(g: np.random.Generator, shape, dtype: torch.dtype,
                  raw_bits: bool = False) -> torch.Tensor:
     """Host tensor of `shape`: U[-1,1) rounded to `dtype`, or random bytes."""
     n = int(np.prod(shape)) if len(shape) else 1
+    if n == 0:
+        return torch.empty(shape, dtype=dtype)
     if raw_bits or dtype not in _FLOATS:
         nbytes = n * torch.empty((), dtype=dtype).element_size()
         raw = torch.from_numpy(g.integers(0, 256, size=nbytes, dtype=np.uint8))
@@ -80,6 +82,8 @@ def device_payload(shape, dtype: torch.dtype, seed: int, buffer_id: int,
     gen = torch.Generator(device=device)
     gen.manual_seed(seed * 1_000_003 + buffer_id)
     elem = torch.empty((), dtype=dtype).element_size()
+    if int(np.prod(shape)) == 0:
+        return torch.empty(shape, dtype=dtype, device=device)
     if raw_bits or dtype not in _FLOATS:
         n = int(np.prod(shape)) * elem
         raw = torch.randint(0, 256, (n,), dtype=torch.uint8, generator=gen, device=device)

@@ -50,6 +50,8 @@ def hb(t: torch.Tensor) -> np.ndarray:
     t = t.detach().contiguous().cpu()
     if t.dim() == 0:
         t = t.reshape(1)
+    if t.numel() == 0:
+        return np.zeros((*t.shape[:-1], t.shape[-1] * t.element_size()), np.uint8)
     return t.view(torch.uint8).numpy()
 
 
@@ -68,6 +70,9 @@ class Guarded:
                                                 dtype=np.uint8))
         self.buf = self.fill.to(DEV)
         self.lo, self.hi = GUARD + offset, GUARD + offset + n
+        if n == 0:  # an empty tensor has no bytes to place between the guards
+            self.t = torch.empty(shape, dtype=dtype, device=DEV)
+            return
         self.t = self.buf[self.lo:self.hi].view(dtype).view(shape)
         if host is not None:
             self.t.copy_(host.to(DEV))
@@ -448,7 +453,7 @@ def test_window_replay_histories(orc):
             k, v = replay.fresh_cache(B, H, C, D)
             kd, vd = torch.from_numpy(k).to(DEV), torch.from_numpy(v).to(DEV)
             T = np.zeros(B, np.int64)
-            for S in sched:
+            for S in [s for s in sched if s >= 1]:
                 Ta = T + S
                 sk_d = torch.from_numpy((Ta - 1).astype(np.int32)).to(DEV)
                 lens = swrt.kv_seq_lengths(sk_d, S, C)
