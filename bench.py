@@ -5,8 +5,10 @@ Workload (one "step"): the KV-cache updates of one whole-model decode step of a
 capacity 128) and whose odd layers use a full linear cache updated by
 TensorScatter (K/V [64, 8, 8192, 64]); batch 64, 8 KV heads, head_dim 64, total
 lengths T ~ U{1..8192} shared by all layers; bf16 (or --dtype fp8_e4m3fn).
-A step is three launches: kv_seq_lengths, kv_window_append_layers (all 12
+A step is one launch of kv_decode_step (default), or with --form three the
+three-call composition: kv_seq_lengths, kv_window_append_layers (all 12
 windowed layers, in place) and tensor_scatter_batched (all 24 full caches).
+Both forms are timed in every run; --form picks the one `value` reports.
 
 Measurement
   - value: algorithmic bytes of a step / time of a step, from K steps bracketed
@@ -14,10 +16,10 @@ Measurement
   - Infinity Cache: every buffer set is independent and --sets sets (default
     3, over 512 MB of windowed caches touched between two uses of one set)
     are visited round robin, so no step finds its data in the 256 MB cache.
-  - roofline: the dominant kernel (window shift + append, 12 layers) launched
-    K times back to back (buffer sets round robin) between one pair of HIP
-    events on the launch stream; achieved = its algorithmic bytes / its mean
-    launch duration.
+  - roofline: the dominant kernel (the one-launch step; with --form three the
+    window shift + append of the 12 layers) launched K times back to back
+    (buffer sets round robin) between one pair of HIP events on the launch
+    stream; achieved = its algorithmic bytes / its mean launch duration.
   - cpu_baseline: the CPU oracle (single thread) on the same step, host copies
     of the same inputs, for a bounded number of steps.
 
@@ -43,19 +45,21 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD's published peak
 # HBM bytes per launch of the dominant kernel from two rocprofv3 counter passes
 # (FETCH_SIZE, WRITE_SIZE), each scaled by what the counter reads for a 1 GiB
 # copy; valid only for the kernel source they were taken on (its hash).
-MEASURED_TRAFFIC = {
-    ("bf16", "95cd5dbdd486ab6d"): {"read": 195_607_466, "written": 195_531_263},
+MEASURED_TRAFFIC = {}
+_CSRC = "sliding_window_ring_tensor_amd/csrc/"
+KERNEL_SOURCES = {
+    "window_in_place": ("kv_window.hip", "window_device.hpp", "swrt_device.hpp"),
+    "decode_step_kernel": ("decode_step.hip", "window_device.hpp", "scatter_device.hpp",
+                           "swrt_device.hpp"),
 }
-TRAFFIC_SOURCES = ("sliding_window_ring_tensor_amd/csrc/kv_window.hip",
-                   "sliding_window_ring_tensor_amd/csrc/swrt_device.hpp")
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(kernel: str) -> str:
     import hashlib
 
     h = hashlib.sha256()
-    for rel in TRAFFIC_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
+    for rel in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, _CSRC + rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -111,6 +115,8 @@ def main():
     ap.add_argument("--sets", type=int, default=3, help="independent buffer sets, round robin")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--form", default="fused", choices=["fused", "three"],
+                    help="one launch per step (default) or the three-call composition")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path has no cross-GPU step (every (b, h) "
@@ -135,35 +141,42 @@ def main():
 
     stream = torch.cuda.Stream()
     K, W = args.steps, args.warmup
+    fused = args.form == "fused"
     with torch.cuda.stream(stream):
-        # ---- graph replay (value) ----
-        graphs = []
-        for st in steps:
-            st.run()  # warm the launch path before capture
-        torch.cuda.synchronize()
-        for st in steps:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                st.run()
-            graphs.append(g)
-        for i in range(W):
-            graphs[i % len(graphs)].replay()
-        torch.cuda.synchronize()
-        log(f"timing {K} graph-replayed steps ...")
-        t0 = time.perf_counter()
-        for i in range(K):
-            graphs[i % len(graphs)].replay()
-        torch.cuda.synchronize()
-        graph_s = (time.perf_counter() - t0) / K
+        def graph_time(fn):
+            """K steps replayed as graphs (one per buffer set), wall clock
+            between two synchronizations."""
+            for st in steps:
+                fn(st)  # warm the launch path before capture
+            torch.cuda.synchronize()
+            graphs = []
+            for st in steps:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    fn(st)
+                graphs.append(g)
+            for i in range(W):
+                graphs[i % len(graphs)].replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(K):
+                graphs[i % len(graphs)].replay()
+            torch.cuda.synchronize()
+            return (time.perf_counter() - t0) / K
 
-        # ---- dominant kernel alone and the eager step: HIP events ----
+        log(f"timing {K} graph-replayed steps, one launch per step ...")
+        graph_fused_s = graph_time(lambda st: st.run_fused())
+        log(f"timing {K} graph-replayed steps, three launches per step ...")
+        graph_three_s = graph_time(lambda st: st.run_three())
+
+        # ---- kernels alone: HIP events ----
         # The host needs longer to issue a launch than the GPU to run it. A
         # sleep kernel issued first keeps the GPU busy while the host queues
         # a whole timed block, so one pair of events on the launch stream
         # brackets back-to-back kernel execution, not host gaps.
         t0 = time.perf_counter()
         for i in range(W):
-            steps[i % len(steps)].run()
+            steps[i % len(steps)].run_three()
         torch.cuda.synchronize()
         host_step_s = (time.perf_counter() - t0) / max(W, 1)
         s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -183,10 +196,12 @@ def main():
             torch.cuda.synchronize()
             return a.elapsed_time(b) * 1e-3 / K
 
-        log(f"timing {K} launches of the window kernel ...")
+        log(f"timing {K} launches of the one-launch step ...")
+        fused_mean_s = events_block(lambda st: st.run_fused())
+        log(f"timing {K} launches of the window kernel alone ...")
         win_mean_s = events_block(lambda st: st.windowed())
-        log(f"timing {K} eager steps ...")
-        eager_s = events_block(lambda st: st.run())
+        log(f"timing {K} three-launch steps ...")
+        three_eager_s = events_block(lambda st: st.run_three())
 
         # ---- achievable reference: 1 GiB device-to-device copies ----
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -212,10 +227,17 @@ def main():
     flags = [int(st.buffers.flags.item()) for st in steps]
     if any(flags):
         raise SystemExit(f"device flags raised during the benchmark: {flags}")
-    achieved = acct["windowed"] / win_mean_s / 1e9
-    meas = MEASURED_TRAFFIC.get((args.dtype, kernel_source_hash()))
+    step_s = graph_fused_s if fused else graph_three_s
+    value = acct["total"] / step_s / 1e9
+    if fused:
+        kname, kbytes, kmean = "decode_step_kernel", acct["total"], fused_mean_s
+        kdesc = "decode_step_kernel: the whole step in one launch (lengths, 12 windowed layers, 24 full caches)"
+    else:
+        kname, kbytes, kmean = "window_in_place", acct["windowed"], win_mean_s
+        kdesc = "window_in_place: 12 windowed layers, K and V, one launch"
+    achieved = kbytes / kmean / 1e9
+    meas = MEASURED_TRAFFIC.get((args.dtype, kname, kernel_source_hash(kname)))
     traffic = None if meas is None else meas["read"] + meas["written"]
-    value = acct["total"] / graph_s / 1e9
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -234,8 +256,8 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": W,
-        "ms_per_step": round(graph_s * 1e3, 5),
-        "us_per_step": round(graph_s * 1e6, 2),
+        "ms_per_step": round(step_s * 1e3, 5),
+        "us_per_step": round(step_s * 1e6, 2),
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "higher_is_better": True,
         "scaling": "weak",
@@ -249,23 +271,30 @@ def main():
                         f"B={spec.batch}, H_kv={spec.kv_heads}, D={spec.head_dim}, "
                         f"T~U[1,8192] seed {spec.seed}",
             "bytes_per_step": acct["total"],
+            "form": "one launch per step (kv_decode_step)" if fused else
+                    "three launches per step (kv_seq_lengths, kv_window_append_layers, "
+                    "tensor_scatter_batched)",
             "timing": "HIP graph replay, one graph per buffer set",
             "cache_defeat": f"{args.sets} independent buffer sets round robin",
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "window_in_place (12 windowed layers, K and V)",
+            "kernel": kdesc,
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "bytes_per_launch": acct["windowed"],
-            "mean_launch_us": round(win_mean_s * 1e6, 3),
+            "bytes_per_launch": kbytes,
+            "mean_launch_us": round(kmean * 1e6, 3),
         },
         "cpu_baseline": cpu,
-        "eager": {"us_per_step": round(eager_s * 1e6, 2),
-                  "value": round(acct["total"] / eager_s / 1e9, 2)},
+        "one_launch": {"graph_us_per_step": round(graph_fused_s * 1e6, 2),
+                       "events_us_per_launch": round(fused_mean_s * 1e6, 2)},
+        "three_launches": {"graph_us_per_step": round(graph_three_s * 1e6, 2),
+                           "events_us_per_step": round(three_eager_s * 1e6, 2),
+                           "window_kernel_us": round(win_mean_s * 1e6, 3),
+                           "window_kernel_gbs": round(acct["windowed"] / win_mean_s / 1e9, 1)},
         "copy_reference_gbs": {"torch_copy": round(torch_copy, 1),
                                "swrt_tensor_scatter_copy": round(swrt_copy, 1)},
         "env": {"gpu": torch.cuda.get_device_name(dev), "torch": torch.__version__,

@@ -21,6 +21,8 @@
  *                          window left by E rows and write the S new rows after
  *                          it, for K and V in one launch; in place when S = 1,
  *                          through a C+S staging cache with copy-back when S > 1.
+ * plus batched forms of the last two and of TensorScatter (several layers or
+ * caches per launch) and swrt_kv_decode_step (all of a decode step at once).
  *
  * Conventions shared by every entry point
  *   - Ownership: the caller owns every buffer. The library allocates nothing,
@@ -256,6 +258,53 @@ int swrt_kv_window_append_layers(int n_layers, void *const *k_caches,
                                  int kv_heads, int capacity, int seq_len,
                                  int head_dim, int elem_bits, unsigned phase,
                                  uint32_t *d_flags, void *stream);
+
+/*
+ * swrt_kv_decode_step -- every KV-cache update of one decode step (S = 1) of a
+ * model with windowed layers (pull request "GQA support sliding_window_cache",
+ * section "Design") and full-length layers (ONNX operator page "TensorScatter",
+ * linear mode), in one launch. It writes exactly the bytes of
+ *
+ *   swrt_kv_seq_lengths(seqlens_k, batch, 1, capacity, total_lens, past_lens,
+ *                       cache_past_lens, cache_total_lens, evict_counts)
+ *   swrt_kv_window_append_layers(n_window_layers, win_*, win_new_strides,
+ *                       Lp, E, batch, kv_heads, capacity, 1, head_dim, ...)
+ *   swrt_tensor_scatter_batched(n_full, full_caches, full_caches, full_new,
+ *                       write_indices, {batch, kv_heads, max_seq, head_dim},
+ *                       rank 4, axis 2, S = 1, SWRT_MODE_LINEAR, ...)
+ *
+ * with the windowed part deriving each entry's (Lp, E) from seqlens_k itself.
+ *
+ * n_window_layers      0 .. SWRT_MAX_LAYERS; win_* as for
+ *                      swrt_kv_window_append_layers (caches [B, H, C, D], new
+ *                      rows [B, H, 1, D] by win_new_strides, host int64[3]).
+ * seqlens_k            device int32[batch]; required when there are windowed
+ *                      layers or length outputs.
+ * capacity             C >= 1 of the windowed caches.
+ * total_lens .. evict_counts
+ *                      optional device outputs as for swrt_kv_seq_lengths
+ *                      (any may be NULL).
+ * n_full               0 .. SWRT_MAX_BATCHED full caches [B, H, max_seq, D],
+ *                      updated in place; full_new: their new rows, dense
+ *                      [B, H, 1, D]; write_indices: device int64[batch].
+ * batch, kv_heads, head_dim, elem_bits: shared by every cache.
+ * d_flags              SWRT_FLAG_BAD_SEQLEN (lengths clamped, step proceeds)
+ *                      and SWRT_FLAG_LINEAR_OOB (that batch entry of every full
+ *                      cache keeps its rows), as for the three calls.
+ * No written buffer may overlap any other buffer of the call.
+ */
+int swrt_kv_decode_step(int n_window_layers, void *const *win_k_caches,
+                        void *const *win_v_caches, const void *const *win_k_new,
+                        const void *const *win_v_new,
+                        const int64_t *win_new_strides,
+                        const int32_t *seqlens_k, int capacity,
+                        int64_t *total_lens, int64_t *past_lens,
+                        int32_t *cache_past_lens, int32_t *cache_total_lens,
+                        int32_t *evict_counts, int n_full,
+                        void *const *full_caches, const void *const *full_new,
+                        const int64_t *write_indices, int max_seq, int batch,
+                        int kv_heads, int head_dim, int elem_bits,
+                        uint32_t *d_flags, void *stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *swrt_status_string(int status);

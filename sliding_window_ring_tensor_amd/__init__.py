@@ -11,11 +11,16 @@ Operations (pages: ONNX operator "TensorScatter"; Core AI model zoo
 sliding_window_cache"):
 
     tensor_scatter(past, update, write_indices, axis=-2, mode="linear", out=None)
-    tensor_scatter_batched(pasts, updates, write_indices, ...)  # same shape, one launch
+    tensor_scatter_batched(pasts, updates, write_indices, ...)  # one shape, one launch
     kv_seq_lengths(seqlens_k, seq_len, capacity)
     kv_window_append(k_cache, v_cache, k_new, v_new, cache_past_lens, evict_counts,
                      k_staging=None, v_staging=None, phase="all")
     kv_window_append_layers(...)   # several layers sharing shapes and lengths
+    kv_decode_step(...)            # lengths + windowed layers + full layers, one launch
+
+Every function has a ``prepare_*`` twin returning a ``PreparedCall``: the
+arguments are checked and marshalled once, and each call of the object only
+adds the current stream. Decode loops use it to keep host cost per step small.
 """
 from __future__ import annotations
 
@@ -26,8 +31,11 @@ from typing import NamedTuple, Sequence
 import torch
 
 __all__ = [
-    "SwrtError", "tensor_scatter", "tensor_scatter_batched", "kv_seq_lengths", "kv_window_append",
-    "kv_window_append_layers", "WindowLengths", "library_path", "lib",
+    "SwrtError", "PreparedCall", "WindowLengths", "library_path", "lib",
+    "tensor_scatter", "tensor_scatter_batched", "kv_seq_lengths", "kv_window_append",
+    "kv_window_append_layers", "kv_decode_step",
+    "prepare_tensor_scatter", "prepare_tensor_scatter_batched", "prepare_kv_seq_lengths",
+    "prepare_kv_window_append_layers", "prepare_kv_decode_step",
     "OK", "E_INVALID_ARG", "E_UNSUPPORTED", "E_LAUNCH",
     "FLAG_LINEAR_OOB", "FLAG_BAD_SEQLEN", "FLAG_BAD_LENGTHS",
     "PHASE_STAGE", "PHASE_COMMIT", "PHASE_ALL",
@@ -82,8 +90,11 @@ def lib() -> ctypes.CDLL:
                                         i32, i32, u32, vp, vp]
     L.swrt_kv_window_append_layers.argtypes = [i32, vpp, vpp, vpp, vpp, vp, vpp, vpp, vp, vp,
                                                i32, i32, i32, i32, i32, i32, u32, vp, vp]
-    for name in ("swrt_tensor_scatter", "swrt_tensor_scatter_batched", "swrt_kv_seq_lengths", "swrt_kv_window_append",
-                 "swrt_kv_window_append_layers", "swrt_abi_version"):
+    L.swrt_kv_decode_step.argtypes = [i32, vpp, vpp, vpp, vpp, vp, vp, i32, vp, vp, vp, vp, vp,
+                                      i32, vpp, vpp, vp, i32, i32, i32, i32, i32, vp, vp]
+    for name in ("swrt_tensor_scatter", "swrt_tensor_scatter_batched", "swrt_kv_seq_lengths",
+                 "swrt_kv_window_append", "swrt_kv_window_append_layers", "swrt_kv_decode_step",
+                 "swrt_abi_version"):
         getattr(L, name).restype = ctypes.c_int
     L.swrt_status_string.argtypes = [ctypes.c_int]
     L.swrt_status_string.restype = ctypes.c_char_p
@@ -103,6 +114,12 @@ def _ptr(t: torch.Tensor | None):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _ptrs(ts: Sequence[torch.Tensor] | None):
+    if ts is None:
+        return None
+    return (ctypes.c_void_p * len(ts))(*[t.data_ptr() for t in ts])
+
+
 def _device_of(*ts: torch.Tensor | None) -> torch.device:
     devs = {t.device for t in ts if t is not None}
     if len(devs) != 1:
@@ -111,10 +128,6 @@ def _device_of(*ts: torch.Tensor | None) -> torch.device:
     if dev.type != "cuda":
         raise SwrtError(f"libswrt runs on the GPU only; got a tensor on {dev}")
     return dev
-
-
-def _stream(dev: torch.device):
-    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
 
 def _bits(t: torch.Tensor) -> int:
@@ -126,54 +139,34 @@ def _contig(name: str, t: torch.Tensor) -> None:
         raise SwrtError(f"{name} must be contiguous (it is never copied)")
 
 
+class PreparedCall:
+    """One library call with its arguments marshalled; calling it enqueues the
+    call on the current stream of the tensors' device. It keeps the tensors it
+    points at alive."""
+
+    def __init__(self, fn, args: tuple, device: torch.device, what: str, keep: tuple, result=None):
+        self._fn, self._args, self._dev, self._what = fn, args, device, what
+        self._keep, self.result = keep, result
+
+    def __call__(self):
+        with torch.cuda.device(self._dev):
+            st = self._fn(*self._args, ctypes.c_void_p(
+                torch.cuda.current_stream(self._dev).cuda_stream))
+        _check(st, self._what)
+        return self.result
+
+
 # ---------------------------------------------------------------------------
 # TensorScatter
 # ---------------------------------------------------------------------------
 
-def tensor_scatter(past: torch.Tensor, update: torch.Tensor,
-                   write_indices: torch.Tensor | None = None, *, axis: int = -2,
-                   mode: str = "linear", out: torch.Tensor | None = None,
-                   flags: torch.Tensor | None = None) -> torch.Tensor:
-    """present = TensorScatter(past, update, write_indices; axis, mode).
-
-    ``out=past`` updates the cache in place (only the target rows are written);
-    otherwise a new (or the given) ``out`` receives past with the update rows.
-    ``write_indices``: int64 [batch] on the device, or None for zeros.
-    ``flags``: optional int32/uint32 device scalar that receives FLAG_* bits.
-    """
-    dev = _device_of(past, update, write_indices, out, flags)
-    _contig("past", past)
-    _contig("update", update)
-    if update.dtype != past.dtype or update.dim() != past.dim():
-        raise SwrtError("update must have past's dtype and rank")
-    if write_indices is not None:
-        _contig("write_indices", write_indices)
-        if write_indices.dtype != torch.int64:
-            raise SwrtError("write_indices must be int64")
-    present = torch.empty_like(past) if out is None else out
-    if present.dtype != past.dtype or present.shape != past.shape:
-        raise SwrtError("out must have past's shape and dtype")
-    _contig("out", present)
-    rank = past.dim()
-    ax = axis + rank if axis < 0 else axis
-    if not 0 <= ax < rank:
-        raise SwrtError(f"axis {axis} out of range for rank {rank}")
-    shape = (ctypes.c_int64 * rank)(*past.shape)
-    with torch.cuda.device(dev):
-        st = lib().swrt_tensor_scatter(_ptr(present), _ptr(past), _ptr(update),
-                                       _ptr(write_indices), shape, rank, axis,
-                                       update.shape[ax], _MODES[mode], _bits(past),
-                                       _ptr(flags), _stream(dev))
-    _check(st, "tensor_scatter")
-    return present
-
-
-def tensor_scatter_batched(pasts: Sequence[torch.Tensor], updates: Sequence[torch.Tensor],
-                           write_indices: torch.Tensor | None = None, *, axis: int = -2,
-                           mode: str = "linear", outs: Sequence[torch.Tensor] | None = None,
-                           flags: torch.Tensor | None = None) -> list:
-    """TensorScatter on several caches of one shape sharing write_indices, in one
-    launch. ``outs=pasts`` updates every cache in place."""
+def prepare_tensor_scatter_batched(pasts: Sequence[torch.Tensor],
+                                   updates: Sequence[torch.Tensor],
+                                   write_indices: torch.Tensor | None = None, *, axis: int = -2,
+                                   mode: str = "linear",
+                                   outs: Sequence[torch.Tensor] | None = None,
+                                   flags: torch.Tensor | None = None,
+                                   _single: bool = False) -> PreparedCall:
     n = len(pasts)
     if len(updates) != n or not 1 <= n <= MAX_BATCHED:
         raise SwrtError(f"need 1..{MAX_BATCHED} (past, update) pairs")
@@ -195,15 +188,52 @@ def tensor_scatter_batched(pasts: Sequence[torch.Tensor], updates: Sequence[torc
     ax = axis + rank if axis < 0 else axis
     if not 0 <= ax < rank or u0.dim() != rank:
         raise SwrtError(f"axis {axis} out of range for rank {rank}")
-    arr = lambda ts: (ctypes.c_void_p * n)(*[t.data_ptr() for t in ts])  # noqa: E731
     shape = (ctypes.c_int64 * rank)(*p0.shape)
-    with torch.cuda.device(dev):
-        st = lib().swrt_tensor_scatter_batched(n, arr(presents), arr(pasts), arr(updates),
-                                               _ptr(write_indices), shape, rank, axis,
-                                               u0.shape[ax], _MODES[mode], _bits(p0),
-                                               _ptr(flags), _stream(dev))
-    _check(st, "tensor_scatter_batched")
-    return presents
+    L = lib()
+    keep = (*pasts, *updates, *presents, write_indices, flags)
+    if _single:
+        args = (_ptr(presents[0]), _ptr(p0), _ptr(u0), _ptr(write_indices), shape, rank, axis,
+                u0.shape[ax], _MODES[mode], _bits(p0), _ptr(flags))
+        return PreparedCall(L.swrt_tensor_scatter, args, dev, "tensor_scatter", keep,
+                            presents[0])
+    args = (n, _ptrs(presents), _ptrs(pasts), _ptrs(updates), _ptr(write_indices), shape, rank,
+            axis, u0.shape[ax], _MODES[mode], _bits(p0), _ptr(flags))
+    return PreparedCall(L.swrt_tensor_scatter_batched, args, dev, "tensor_scatter_batched", keep,
+                        presents)
+
+
+def prepare_tensor_scatter(past, update, write_indices=None, *, axis=-2, mode="linear", out=None,
+                           flags=None) -> PreparedCall:
+    if update.dtype != past.dtype or update.dim() != past.dim():
+        raise SwrtError("update must have past's dtype and rank")
+    return prepare_tensor_scatter_batched([past], [update], write_indices, axis=axis, mode=mode,
+                                          outs=None if out is None else [out], flags=flags,
+                                          _single=True)
+
+
+def tensor_scatter(past: torch.Tensor, update: torch.Tensor,
+                   write_indices: torch.Tensor | None = None, *, axis: int = -2,
+                   mode: str = "linear", out: torch.Tensor | None = None,
+                   flags: torch.Tensor | None = None) -> torch.Tensor:
+    """present = TensorScatter(past, update, write_indices; axis, mode).
+
+    ``out=past`` updates the cache in place (only the target rows are written);
+    otherwise a new (or the given) ``out`` receives past with the update rows.
+    ``write_indices``: int64 [batch] on the device, or None for zeros.
+    ``flags``: optional int32 device word that receives FLAG_* bits.
+    """
+    return prepare_tensor_scatter(past, update, write_indices, axis=axis, mode=mode, out=out,
+                                  flags=flags)()
+
+
+def tensor_scatter_batched(pasts: Sequence[torch.Tensor], updates: Sequence[torch.Tensor],
+                           write_indices: torch.Tensor | None = None, *, axis: int = -2,
+                           mode: str = "linear", outs: Sequence[torch.Tensor] | None = None,
+                           flags: torch.Tensor | None = None) -> list:
+    """TensorScatter on several caches of one shape sharing write_indices, in one
+    launch. ``outs=pasts`` updates every cache in place."""
+    return prepare_tensor_scatter_batched(pasts, updates, write_indices, axis=axis, mode=mode,
+                                          outs=outs, flags=flags)()
 
 
 # ---------------------------------------------------------------------------
@@ -218,25 +248,35 @@ class WindowLengths(NamedTuple):
     evict: torch.Tensor        # E  = max(0, Lp + S - C)       int32 [B]
 
 
+def _new_lengths(B: int, dev) -> WindowLengths:
+    return WindowLengths(*(torch.empty(B, dtype=dt, device=dev) for dt in
+                           (torch.int64, torch.int64, torch.int32, torch.int32, torch.int32)))
+
+
+def _check_seqlens(seqlens_k: torch.Tensor) -> None:
+    _contig("seqlens_k", seqlens_k)
+    if seqlens_k.dtype != torch.int32 or seqlens_k.dim() != 1:
+        raise SwrtError("seqlens_k must be a 1-D int32 tensor")
+
+
+def prepare_kv_seq_lengths(seqlens_k: torch.Tensor, seq_len: int, capacity: int, *,
+                           out: WindowLengths | None = None,
+                           flags: torch.Tensor | None = None) -> PreparedCall:
+    dev = _device_of(seqlens_k, flags)
+    _check_seqlens(seqlens_k)
+    B = seqlens_k.shape[0]
+    out = _new_lengths(B, dev) if out is None else out
+    args = (_ptr(seqlens_k), B, seq_len, capacity, _ptr(out.total), _ptr(out.past),
+            _ptr(out.cache_past), _ptr(out.cache_total), _ptr(out.evict), _ptr(flags))
+    return PreparedCall(lib().swrt_kv_seq_lengths, args, dev, "kv_seq_lengths",
+                        (seqlens_k, *out, flags), out)
+
+
 def kv_seq_lengths(seqlens_k: torch.Tensor, seq_len: int, capacity: int, *,
                    out: WindowLengths | None = None,
                    flags: torch.Tensor | None = None) -> WindowLengths:
     """Lengths of one windowed step for every batch entry, computed on the device."""
-    dev = _device_of(seqlens_k, flags)
-    _contig("seqlens_k", seqlens_k)
-    if seqlens_k.dtype != torch.int32 or seqlens_k.dim() != 1:
-        raise SwrtError("seqlens_k must be a 1-D int32 tensor")
-    B = seqlens_k.shape[0]
-    if out is None:
-        out = WindowLengths(*(torch.empty(B, dtype=dt, device=dev) for dt in
-                              (torch.int64, torch.int64, torch.int32, torch.int32, torch.int32)))
-    with torch.cuda.device(dev):
-        st = lib().swrt_kv_seq_lengths(_ptr(seqlens_k), B, seq_len, capacity, _ptr(out.total),
-                                       _ptr(out.past), _ptr(out.cache_past),
-                                       _ptr(out.cache_total), _ptr(out.evict), _ptr(flags),
-                                       _stream(dev))
-    _check(st, "kv_seq_lengths")
-    return out
+    return prepare_kv_seq_lengths(seqlens_k, seq_len, capacity, out=out, flags=flags)()
 
 
 # ---------------------------------------------------------------------------
@@ -251,6 +291,66 @@ def _new_strides(k_new: torch.Tensor, v_new: torch.Tensor):
     return (ctypes.c_int64 * 3)(*k_new.stride()[:3])
 
 
+def _check_layers(k_caches, v_caches, k_news, v_news):
+    n = len(k_caches)
+    if not (len(v_caches) == len(k_news) == len(v_news) == n) or not 1 <= n <= MAX_LAYERS:
+        raise SwrtError(f"need 1..{MAX_LAYERS} layers with one tensor of each kind")
+    kc = k_caches[0]
+    if kc.dim() != 4:
+        raise SwrtError("caches must be [B, H, C, D]")
+    B, H, C, D = kc.shape
+    S = k_news[0].shape[2]
+    for t in (*k_caches, *v_caches):
+        _contig("cache", t)
+        if t.shape != kc.shape or t.dtype != kc.dtype:
+            raise SwrtError("all caches must share shape and dtype")
+    for a, b in zip(k_news, v_news):
+        if a.shape != (B, H, S, D) or b.shape != (B, H, S, D) or a.dtype != kc.dtype \
+                or b.dtype != kc.dtype or a.stride() != k_news[0].stride() \
+                or b.stride() != k_news[0].stride():
+            raise SwrtError("new rows must be [B, H, S, D] with the caches' dtype and "
+                            "one stride pattern")
+    return n, B, H, C, D, S, _new_strides(k_news[0], v_news[0])
+
+
+def prepare_kv_window_append_layers(k_caches, v_caches, k_news, v_news, cache_past_lens,
+                                    evict_counts, *, k_stagings=None, v_stagings=None,
+                                    phase: str = "all", flags: torch.Tensor | None = None,
+                                    _single: bool = False) -> PreparedCall:
+    n, B, H, C, D, S, strides = _check_layers(k_caches, v_caches, k_news, v_news)
+    kc = k_caches[0]
+    everything = [*k_caches, *v_caches, *k_news, *v_news, cache_past_lens, evict_counts, flags]
+    if S > 1:
+        if k_stagings is None or v_stagings is None:
+            raise SwrtError("S > 1 needs k_staging and v_staging [B, H, C + S, D]")
+        for t in (*k_stagings, *v_stagings):
+            _contig("staging", t)
+            if t.shape != (B, H, C + S, D) or t.dtype != kc.dtype:
+                raise SwrtError("staging must be [B, H, C + S, D] with the caches' dtype")
+        everything += [*k_stagings, *v_stagings]
+    else:
+        k_stagings = v_stagings = None
+    dev = _device_of(*everything)
+    for t in (cache_past_lens, evict_counts):
+        _contig("lengths", t)
+        if t.dtype != torch.int32 or t.shape != (B,):
+            raise SwrtError("cache_past_lens and evict_counts must be int32 [B]")
+    L = lib()
+    if _single:
+        args = (_ptr(kc), _ptr(v_caches[0]), _ptr(k_news[0]), _ptr(v_news[0]), strides,
+                None if k_stagings is None else _ptr(k_stagings[0]),
+                None if v_stagings is None else _ptr(v_stagings[0]),
+                _ptr(cache_past_lens), _ptr(evict_counts), B, H, C, S, D, _bits(kc),
+                _PHASES[phase], _ptr(flags))
+        return PreparedCall(L.swrt_kv_window_append, args, dev, "kv_window_append",
+                            tuple(everything))
+    args = (n, _ptrs(k_caches), _ptrs(v_caches), _ptrs(k_news), _ptrs(v_news), strides,
+            _ptrs(k_stagings), _ptrs(v_stagings), _ptr(cache_past_lens), _ptr(evict_counts),
+            B, H, C, S, D, _bits(kc), _PHASES[phase], _ptr(flags))
+    return PreparedCall(L.swrt_kv_window_append_layers, args, dev, "kv_window_append_layers",
+                        tuple(everything))
+
+
 def kv_window_append(k_cache: torch.Tensor, v_cache: torch.Tensor, k_new: torch.Tensor,
                      v_new: torch.Tensor, cache_past_lens: torch.Tensor,
                      evict_counts: torch.Tensor, *, k_staging: torch.Tensor | None = None,
@@ -263,10 +363,11 @@ def kv_window_append(k_cache: torch.Tensor, v_cache: torch.Tensor, k_new: torch.
     ``kv_seq_lengths`` with the same S and C. S > 1 needs staging buffers
     [B, H, C + S, D]; ``phase`` picks "stage", "commit" or "all".
     """
-    kv_window_append_layers([k_cache], [v_cache], [k_new], [v_new], cache_past_lens,
-                            evict_counts, k_stagings=None if k_staging is None else [k_staging],
-                            v_stagings=None if v_staging is None else [v_staging],
-                            phase=phase, flags=flags, _single=True)
+    prepare_kv_window_append_layers(
+        [k_cache], [v_cache], [k_new], [v_new], cache_past_lens, evict_counts,
+        k_stagings=None if k_staging is None else [k_staging],
+        v_stagings=None if v_staging is None else [v_staging], phase=phase, flags=flags,
+        _single=True)()
 
 
 def kv_window_append_layers(k_caches: Sequence[torch.Tensor], v_caches: Sequence[torch.Tensor],
@@ -274,58 +375,64 @@ def kv_window_append_layers(k_caches: Sequence[torch.Tensor], v_caches: Sequence
                             cache_past_lens: torch.Tensor, evict_counts: torch.Tensor, *,
                             k_stagings: Sequence[torch.Tensor] | None = None,
                             v_stagings: Sequence[torch.Tensor] | None = None,
-                            phase: str = "all", flags: torch.Tensor | None = None,
-                            _single: bool = False) -> None:
+                            phase: str = "all", flags: torch.Tensor | None = None) -> None:
     """The windowed step for several layers that share B, H, C, D, S and the
     lengths (e.g. every windowed layer of a model), in one launch per phase."""
-    n = len(k_caches)
-    if not (len(v_caches) == len(k_news) == len(v_news) == n) or not 1 <= n <= MAX_LAYERS:
-        raise SwrtError(f"need 1..{MAX_LAYERS} layers with one tensor of each kind")
-    kc = k_caches[0]
-    if kc.dim() != 4:
-        raise SwrtError("caches must be [B, H, C, D]")
-    B, H, C, D = kc.shape
-    S = k_news[0].shape[2]
-    strides = _new_strides(k_news[0], v_news[0])
-    everything = [*k_caches, *v_caches, *k_news, *v_news, cache_past_lens, evict_counts, flags]
-    if k_stagings is not None:
-        everything += [*k_stagings, *v_stagings]
-    dev = _device_of(*everything)
-    for t in (*k_caches, *v_caches):
-        _contig("cache", t)
-        if t.shape != kc.shape or t.dtype != kc.dtype:
-            raise SwrtError("all caches must share shape and dtype")
-    for a, b in zip(k_news, v_news):
-        if a.shape != (B, H, S, D) or b.shape != (B, H, S, D) or a.dtype != kc.dtype \
-                or b.dtype != kc.dtype or a.stride() != k_news[0].stride() \
-                or b.stride() != k_news[0].stride():
-            raise SwrtError("new rows must be [B, H, S, D] with the caches' dtype and "
-                            "one stride pattern")
-    for t in (cache_past_lens, evict_counts):
-        _contig("lengths", t)
-        if t.dtype != torch.int32 or t.shape != (B,):
-            raise SwrtError("cache_past_lens and evict_counts must be int32 [B]")
-    ks = vs = None
-    if S > 1:
-        if k_stagings is None or v_stagings is None:
-            raise SwrtError("S > 1 needs k_staging and v_staging [B, H, C + S, D]")
-        for t in (*k_stagings, *v_stagings):
-            _contig("staging", t)
-            if t.shape != (B, H, C + S, D) or t.dtype != kc.dtype:
-                raise SwrtError("staging must be [B, H, C + S, D] with the caches' dtype")
-    arr = lambda ts: (ctypes.c_void_p * n)(*[t.data_ptr() for t in ts])  # noqa: E731
-    if S > 1:
-        ks, vs = arr(k_stagings), arr(v_stagings)
-    with torch.cuda.device(dev):
-        if _single:
-            st = lib().swrt_kv_window_append(
-                _ptr(k_caches[0]), _ptr(v_caches[0]), _ptr(k_news[0]), _ptr(v_news[0]), strides,
-                None if ks is None else ks[0], None if vs is None else vs[0],
-                _ptr(cache_past_lens), _ptr(evict_counts), B, H, C, S, D, _bits(kc),
-                _PHASES[phase], _ptr(flags), _stream(dev))
-        else:
-            st = lib().swrt_kv_window_append_layers(
-                n, arr(k_caches), arr(v_caches), arr(k_news), arr(v_news), strides, ks, vs,
-                _ptr(cache_past_lens), _ptr(evict_counts), B, H, C, S, D, _bits(kc),
-                _PHASES[phase], _ptr(flags), _stream(dev))
-    _check(st, "kv_window_append")
+    prepare_kv_window_append_layers(k_caches, v_caches, k_news, v_news, cache_past_lens,
+                                    evict_counts, k_stagings=k_stagings, v_stagings=v_stagings,
+                                    phase=phase, flags=flags)()
+
+
+# ---------------------------------------------------------------------------
+# whole decode step in one launch
+# ---------------------------------------------------------------------------
+
+def prepare_kv_decode_step(win_k: Sequence[torch.Tensor], win_v: Sequence[torch.Tensor],
+                           win_k_new: Sequence[torch.Tensor], win_v_new: Sequence[torch.Tensor],
+                           seqlens_k: torch.Tensor, full_caches: Sequence[torch.Tensor],
+                           full_new: Sequence[torch.Tensor], write_indices: torch.Tensor, *,
+                           out: WindowLengths | None = None,
+                           flags: torch.Tensor | None = None) -> PreparedCall:
+    """See ``kv_decode_step``."""
+    n, B, H, C, D, S, strides = _check_layers(win_k, win_v, win_k_new, win_v_new)
+    if S != 1:
+        raise SwrtError("a decode step appends one row (S = 1)")
+    _check_seqlens(seqlens_k)
+    nf = len(full_caches)
+    if len(full_new) != nf or not 0 <= nf <= MAX_BATCHED:
+        raise SwrtError(f"need 0..{MAX_BATCHED} full caches, each with its new rows")
+    M = full_caches[0].shape[2] if nf else 1
+    for c, u in zip(full_caches, full_new):
+        _contig("full cache", c)
+        _contig("full-cache new rows", u)
+        if c.shape != (B, H, M, D) or u.shape != (B, H, 1, D) or c.dtype != win_k[0].dtype \
+                or u.dtype != win_k[0].dtype:
+            raise SwrtError("full caches must be [B, H, M, D] and their new rows [B, H, 1, D], "
+                            "in the windowed caches' dtype")
+    if nf:
+        _contig("write_indices", write_indices)
+        if write_indices.dtype != torch.int64 or write_indices.shape != (B,):
+            raise SwrtError("write_indices must be int64 [B]")
+    dev = _device_of(*win_k, *win_v, *win_k_new, *win_v_new, seqlens_k, *full_caches,
+                     *full_new, write_indices, flags)
+    out = _new_lengths(B, dev) if out is None else out
+    args = (n, _ptrs(win_k), _ptrs(win_v), _ptrs(win_k_new), _ptrs(win_v_new), strides,
+            _ptr(seqlens_k), C, _ptr(out.total), _ptr(out.past), _ptr(out.cache_past),
+            _ptr(out.cache_total), _ptr(out.evict), nf, _ptrs(full_caches) if nf else None,
+            _ptrs(full_new) if nf else None, _ptr(write_indices) if nf else None, M, B, H, D,
+            _bits(win_k[0]), _ptr(flags))
+    keep = (*win_k, *win_v, *win_k_new, *win_v_new, seqlens_k, *full_caches, *full_new,
+            write_indices, *out, flags)
+    return PreparedCall(lib().swrt_kv_decode_step, args, dev, "kv_decode_step", keep, out)
+
+
+def kv_decode_step(win_k, win_v, win_k_new, win_v_new, seqlens_k, full_caches, full_new,
+                   write_indices, *, out: WindowLengths | None = None,
+                   flags: torch.Tensor | None = None) -> WindowLengths:
+    """Every KV-cache update of one decode step in one launch: the lengths of
+    the windowed layers from ``seqlens_k`` (returned), the in-place shift and
+    append of every windowed layer's K and V, and the linear TensorScatter of
+    one new row at ``write_indices`` into every full cache. Same bytes as
+    kv_seq_lengths + kv_window_append_layers + tensor_scatter_batched."""
+    return prepare_kv_decode_step(win_k, win_v, win_k_new, win_v_new, seqlens_k, full_caches,
+                                  full_new, write_indices, out=out, flags=flags)()

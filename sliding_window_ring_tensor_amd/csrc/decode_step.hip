@@ -1,0 +1,165 @@
+// decode_step.hip -- every KV-cache update of one decode step in one launch.
+//
+// A model whose layers use windowed caches (onnxruntime pull request "GQA
+// support sliding_window_cache", section "Design") and full max-length caches
+// updated by TensorScatter in linear mode (ONNX operator page "TensorScatter")
+// gets one new K and V row per (batch, kv-head) and layer at every decode
+// step. swrt_kv_decode_step does, in one grid, exactly what these three calls
+// do in three launches:
+//
+//   swrt_kv_seq_lengths(seqlens_k, B, 1, C, T, P, Lp, L, E)
+//   swrt_kv_window_append_layers(all windowed layers, Lp, E, S = 1)
+//   swrt_tensor_scatter_batched(all full caches in place, write_indices,
+//                               [B, H, M, D], axis 2, S = 1, linear)
+//
+// Workgroup roles (uniform per workgroup): the first workgroups carry the
+// full-cache row writes, the rest one windowed slice each; every window
+// workgroup derives its own (Lp, E) from seqlens_k with the same arithmetic
+// as kv_seq_lengths, and the first ceil(B / 256) workgroups also write the
+// length arrays for the attention that follows. Two kernel boundaries per
+// step disappear, and with them their dispatch and cache-maintenance cost.
+#include "swrt_host.hpp"
+
+namespace swrt {
+namespace {
+
+struct DecodeArgs {
+  char *wc[kMaxLayers][2];        // windowed caches
+  const char *wn[kMaxLayers][2];  // windowed new rows
+  char *fc[kMaxTensors];          // full caches
+  const char *fu[kMaxTensors];    // full-cache new rows
+  WindowGeom wg;
+  ScatterGeom sg;
+  const int32_t *seqlens_k;
+  int64_t *total, *past;
+  int32_t *cache_past, *cache_total, *evict;
+  uint32_t full_tiles, full_blocks, win_blocks, len_blocks;
+  int32_t batch;
+};
+
+template <int VEC>
+__global__ __launch_bounds__(kBlock) void decode_step_kernel(DecodeArgs a) {
+  __shared__ TileBatches tb;
+  const uint32_t bid = blockIdx.x;
+  if (bid < a.len_blocks) {  // the length arrays (no barrier in this part)
+    const int32_t b = int32_t(bid * kBlock + threadIdx.x);
+    if (b < a.batch) {
+      const StepLengths r = step_lengths(a.seqlens_k[b], 1, a.wg.C);
+      if (r.bad && a.wg.flags) atomicOr(a.wg.flags, SWRT_FLAG_BAD_SEQLEN);
+      if (a.total) a.total[b] = r.T;
+      if (a.past) a.past[b] = r.P;
+      if (a.cache_past) a.cache_past[b] = int32_t(r.Lp);
+      if (a.cache_total) a.cache_total[b] = int32_t(r.L);
+      if (a.evict) a.evict[b] = int32_t(r.E);
+    }
+  }
+  if (bid < a.full_blocks) {  // full caches: TensorScatter rows in place
+    const uint32_t t = bid / a.full_tiles;
+    scatter_in_place_tile<VEC>(a.sg, a.fc[t], a.fu[t], (bid - t * a.full_tiles) * kScatTile, tb);
+    return;
+  }
+  const uint32_t slice = bid - a.full_blocks;
+  if (slice >= a.win_blocks) return;  // a grid sized by the length arrays alone
+  const Slice s = decode_slice(a.wg, slice);
+  const StepLengths r = step_lengths(a.seqlens_k[s.b], 1, a.wg.C);
+  char *base = a.wc[s.layer][s.t] + uint64_t(s.b * a.wg.H + s.h) * uint64_t(a.wg.C) * a.wg.row_bytes;
+  shift_append_slice<VEC>(base, a.wn[s.layer][s.t] + s.b * a.wg.nb_b + s.h * a.wg.nb_h, r.Lp,
+                          r.E, a.wg.row_bytes, a.wg.row_words);
+}
+
+}  // namespace
+}  // namespace swrt
+
+using namespace swrt;
+
+extern "C" int swrt_kv_decode_step(int n_window_layers, void *const *win_k_caches,
+                                   void *const *win_v_caches, const void *const *win_k_new,
+                                   const void *const *win_v_new, const int64_t *win_new_strides,
+                                   const int32_t *seqlens_k, int capacity, int64_t *total_lens,
+                                   int64_t *past_lens, int32_t *cache_past_lens,
+                                   int32_t *cache_total_lens, int32_t *evict_counts, int n_full,
+                                   void *const *full_caches, const void *const *full_new,
+                                   const int64_t *write_indices, int max_seq, int batch,
+                                   int kv_heads, int head_dim, int elem_bits, uint32_t *d_flags,
+                                   void *stream) {
+  if (batch < 0 || capacity < 1 || n_window_layers < 0 || n_full < 0) return SWRT_E_INVALID_ARG;
+  WindowPlan wp{};
+  ScatterPlan sp{};
+  Range ranges[6 * kMaxLayers + 3 * kMaxTensors + 12];
+  int nr = 0;
+  int st = plan_window(n_window_layers, win_k_caches, win_v_caches, win_k_new, win_v_new,
+                       win_new_strides, nullptr, nullptr, nullptr, nullptr, true, batch, kv_heads,
+                       capacity, 1, head_dim, elem_bits, SWRT_PHASE_ALL, d_flags, &wp, ranges,
+                       &nr);
+  if (st != SWRT_OK) return st;
+  const int64_t shape[4] = {batch, kv_heads, max_seq, head_dim};
+  sp.empty = true;
+  if (n_full > 0) {
+    st = plan_scatter(n_full, full_caches, const_cast<const void *const *>(full_caches), full_new,
+                      write_indices, shape, 4, 2, 1, SWRT_MODE_LINEAR, elem_bits, d_flags, &sp,
+                      ranges, &nr);
+    if (st != SWRT_OK) return st;
+  }
+  const bool lengths_out = total_lens || past_lens || cache_past_lens || cache_total_lens ||
+                           evict_counts;
+  if ((lengths_out || !wp.empty) && batch > 0 && !seqlens_k) return SWRT_E_INVALID_ARG;
+  const uint64_t B = uint64_t(batch);
+  if (addr_of(seqlens_k) % 4 || addr_of(total_lens) % 8 || addr_of(past_lens) % 8 ||
+      addr_of(cache_past_lens) % 4 || addr_of(cache_total_lens) % 4 || addr_of(evict_counts) % 4)
+    return SWRT_E_INVALID_ARG;
+  ranges[nr++] = range(seqlens_k, B * 4, false);
+  ranges[nr++] = range(total_lens, B * 8, true);
+  ranges[nr++] = range(past_lens, B * 8, true);
+  ranges[nr++] = range(cache_past_lens, B * 4, true);
+  ranges[nr++] = range(cache_total_lens, B * 4, true);
+  ranges[nr++] = range(evict_counts, B * 4, true);
+  ranges[nr++] = range(d_flags, 4, true);
+  if (written_overlap(ranges, nr)) return SWRT_E_INVALID_ARG;
+
+  const bool do_len = lengths_out && batch > 0;
+  if (wp.empty && sp.empty && !do_len) return SWRT_OK;
+  // one copy word for both parts: the rows have the same size
+  const int vec = word_of((wp.empty ? 0 : wp.align) | (sp.empty ? 0 : sp.align) |
+                          uint64_t(wp.empty && sp.empty ? 16 : 0));
+  if (!wp.empty && (st = finish_window(&wp, vec)) != SWRT_OK) return st;
+  if (!sp.empty && (st = finish_scatter(&sp, vec)) != SWRT_OK) return st;
+
+  static_assert(sizeof(DecodeArgs) <= 4096, "kernel arguments exceed 4 KiB");
+  DecodeArgs a;
+  for (int l = 0; l < n_window_layers && !wp.empty; ++l)
+    for (int t = 0; t < 2; ++t) {
+      a.wc[l][t] = wp.cache[l][t];
+      a.wn[l][t] = wp.nw[l][t];
+    }
+  for (int t = 0; t < n_full && !sp.empty; ++t) {
+    a.fc[t] = sp.present[t];
+    a.fu[t] = sp.update[t];
+  }
+  a.wg = wp.g;
+  a.wg.C = capacity;
+  a.wg.flags = d_flags;
+  a.sg = sp.g;
+  a.seqlens_k = seqlens_k;
+  a.total = total_lens;
+  a.past = past_lens;
+  a.cache_past = cache_past_lens;
+  a.cache_total = cache_total_lens;
+  a.evict = evict_counts;
+  a.batch = batch;
+  a.full_tiles = sp.empty ? 1 : sp.tiles;
+  a.full_blocks = sp.empty ? 0 : sp.tiles * uint32_t(sp.n);
+  a.len_blocks = do_len ? uint32_t((B + kBlock - 1) / kBlock) : 0;
+  a.win_blocks = wp.empty ? 0 : wp.slices;
+  uint64_t grid = uint64_t(a.full_blocks) + a.win_blocks;
+  if (grid < a.len_blocks) grid = a.len_blocks;  // length arrays alone
+  if (grid >= (uint64_t(1) << 31)) return SWRT_E_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (vec) {
+    case 16: hipLaunchKernelGGL(decode_step_kernel<16>, dim3(grid), dim3(kBlock), 0, s, a); break;
+    case 8: hipLaunchKernelGGL(decode_step_kernel<8>, dim3(grid), dim3(kBlock), 0, s, a); break;
+    case 4: hipLaunchKernelGGL(decode_step_kernel<4>, dim3(grid), dim3(kBlock), 0, s, a); break;
+    case 2: hipLaunchKernelGGL(decode_step_kernel<2>, dim3(grid), dim3(kBlock), 0, s, a); break;
+    default: hipLaunchKernelGGL(decode_step_kernel<1>, dim3(grid), dim3(kBlock), 0, s, a); break;
+  }
+  return launch_status();
+}

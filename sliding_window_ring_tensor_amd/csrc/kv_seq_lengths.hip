@@ -10,7 +10,7 @@
 // bounded by the capacity and fit 32 bits again.
 //
 // One lane per batch entry; the values are independent per entry.
-#include "swrt_device.hpp"
+#include "window_device.hpp"
 
 namespace swrt {
 namespace {
@@ -26,20 +26,13 @@ struct LengthArgs {
 __global__ __launch_bounds__(kBlock) void seq_lengths_kernel(LengthArgs a) {
   const int32_t b = blockIdx.x * kBlock + threadIdx.x;
   if (b >= a.batch) return;
-  const int64_t sk = a.seqlens_k[b];
-  const int64_t T = sk + 1;
-  int64_t P = T - a.S;
-  if (P < 0) P = 0;
-  const int64_t Lp = P < a.C ? P : a.C;
-  int64_t E = Lp + a.S - a.C;
-  if (E < 0) E = 0;
-  const int64_t L = Lp + a.S - E;
-  if ((sk < 0 || T < a.S) && a.flags) atomicOr(a.flags, SWRT_FLAG_BAD_SEQLEN);
-  if (a.total) a.total[b] = T;
-  if (a.past) a.past[b] = P;
-  a.cache_past[b] = int32_t(Lp);
-  a.evict[b] = int32_t(E);
-  if (a.cache_total) a.cache_total[b] = int32_t(L);
+  const StepLengths r = step_lengths(a.seqlens_k[b], a.S, a.C);
+  if (r.bad && a.flags) atomicOr(a.flags, SWRT_FLAG_BAD_SEQLEN);
+  if (a.total) a.total[b] = r.T;
+  if (a.past) a.past[b] = r.P;
+  a.cache_past[b] = int32_t(r.Lp);
+  a.evict[b] = int32_t(r.E);
+  if (a.cache_total) a.cache_total[b] = int32_t(r.L);
 }
 
 }  // namespace

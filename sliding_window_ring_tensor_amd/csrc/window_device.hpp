@@ -1,0 +1,190 @@
+// window_device.hpp -- device bodies of the windowed GQA cache step.
+//
+// onnxruntime pull request "GQA support sliding_window_cache", section
+// "Design": a windowed cache of capacity C keeps the L = min(T, C) most recent
+// tokens at rows [0, L) of every (b, h) slice. Appending S tokens onto a past
+// of P tokens, with Lp = min(P, C) resident and E = max(0, Lp + S - C)
+// evicted, shifts cache[E .. Lp) to cache[0 .. Lp-E) and writes the new rows
+// to cache[Lp-E .. Lp-E+S). Decode (S = 1) runs in place; any S > 1 step goes
+// through a C+S staging cache that is copied back.
+//
+// Used by kv_seq_lengths.hip, kv_window.hip and decode_step.hip.
+#pragma once
+
+#include "swrt_device.hpp"
+
+namespace swrt {
+
+#ifndef SWRT_WINDOW_UNROLL
+#define SWRT_WINDOW_UNROLL 4
+#endif
+constexpr int kWinUnroll = SWRT_WINDOW_UNROLL;  // words per thread per tile
+constexpr uint32_t kWinTile = kBlock * kWinUnroll;
+
+// ---------------------------------------------------------------------------
+// lengths of one step (same page, section "Design"; the follow-up commit does
+// the arithmetic in 64 bits because seqlens_k + 1 overflows 32 bits at
+// INT32_MAX, and clamps the past length at zero)
+// ---------------------------------------------------------------------------
+struct StepLengths {
+  int64_t T, P, Lp, E, L;
+  bool bad;  // seqlens_k < 0 or T < S
+};
+
+__device__ __forceinline__ StepLengths step_lengths(int32_t seqlens_k, int64_t S, int64_t C) {
+  StepLengths r;
+  r.T = int64_t(seqlens_k) + 1;  // absolute total length after the step
+  r.P = r.T - S;                  // absolute past length, clamped at zero
+  if (r.P < 0) r.P = 0;
+  r.Lp = r.P < C ? r.P : C;       // tokens resident before the step
+  r.E = r.Lp + S - C;             // tokens evicted by the step
+  if (r.E < 0) r.E = 0;
+  r.L = r.Lp + S - r.E;           // tokens resident after the step
+  r.bad = seqlens_k < 0 || r.T < S;
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// geometry shared by every slice of a launch
+// ---------------------------------------------------------------------------
+struct WindowGeom {
+  const int32_t *lp, *ev;    // Lp, E per batch entry (null when derived in-kernel)
+  uint32_t *flags;
+  int64_t nb_b, nb_h, nb_s;  // new-row strides, bytes
+  uint64_t row_bytes;
+  uint32_t H, BH, tiles, row_words;
+  int32_t C, S;
+  FastDiv by_row;            // words of the new part -> row (staging)
+};
+
+struct Slice {
+  uint32_t layer, t, b, h;
+};
+
+// slice index -> (layer, tensor, b, h); h fastest, so consecutive workgroups
+// walk consecutive slices of one cache
+__device__ __forceinline__ Slice decode_slice(const WindowGeom &g, uint32_t slice) {
+  const uint32_t lt = slice / g.BH, bh = slice - lt * g.BH;
+  Slice s;
+  s.layer = lt >> 1;
+  s.t = lt & 1;
+  s.b = bh / g.H;
+  s.h = bh - s.b * g.H;
+  return s;
+}
+
+// (Lp, E) must be the pair the lengths give for (C, S): 0 <= Lp <= C and
+// E = max(0, Lp + S - C). Otherwise flag once per batch entry and skip it.
+__device__ __forceinline__ bool lengths_ok(const WindowGeom &g, const Slice &s, uint32_t tile,
+                                           int64_t Lp, int64_t E) {
+  int64_t e = Lp + g.S - g.C;
+  if (e < 0) e = 0;
+  if (Lp >= 0 && Lp <= g.C && E == e) return true;
+  if (g.flags && s.layer == 0 && s.t == 0 && s.h == 0 && tile == 0 && threadIdx.x == 0)
+    atomicOr(g.flags, SWRT_FLAG_BAD_LENGTHS);
+  return false;
+}
+
+// ---------------------------------------------------------------------------
+// S = 1, in place: one workgroup shifts one slice by E (0 or 1) rows and
+// appends the new row at Lp - E.
+//
+// The shift is an overlapping move with dst < src. The workgroup walks the
+// slice in ascending tiles and, per tile, loads every word into registers,
+// meets at a barrier, then stores: a later tile only reads rows above
+// everything written so far, and a tile only overwrites rows whose old values
+// its own loads already returned. No other workgroup touches the slice and no
+// scratch memory is needed. Lanes past the end of the last tile clamp to its
+// last word (same value to the same address as the owning lane), so the loop
+// has no per-lane branch and the wait counters stay exact.
+// ---------------------------------------------------------------------------
+template <int VEC>
+__device__ __forceinline__ void shift_append_slice(char *base, const char *new_row, int64_t Lp,
+                                                   int64_t E, uint64_t row_bytes,
+                                                   uint32_t row_words) {
+  using W = typename Word<VEC>::T;
+  W *dst = reinterpret_cast<W *>(base);
+  // The new row lives in its own buffer: fetch it first so its latency
+  // overlaps the shift; it is stored at row Lp - E.
+  const W *nsrc = reinterpret_cast<const W *>(new_row);
+  W *adst = reinterpret_cast<W *>(base + uint64_t(Lp - E) * row_bytes);
+  const bool row_in_one_pass = row_words <= uint32_t(kBlock);
+  const uint32_t ai = min(threadIdx.x, row_words - 1);
+  W nv;
+  if (row_in_one_pass) nv = ld(nsrc + ai);
+  bool appended = false;
+  if (E) {
+    const W *src = reinterpret_cast<const W *>(base + uint64_t(E) * row_bytes);
+    const uint32_t n = uint32_t(Lp - E) * row_words;
+    for (uint32_t c0 = 0; c0 < n; c0 += kWinTile) {
+      W v[kWinUnroll];
+#pragma unroll
+      for (int u = 0; u < kWinUnroll; ++u) v[u] = ld(src + min(c0 + u * kBlock + threadIdx.x, n - 1));
+      __syncthreads();  // every old value of this tile is in registers
+      // Row Lp - E is read by the last tile and is no shift destination: the
+      // new row can go out as soon as that tile's loads are done.
+      if (row_in_one_pass && c0 + kWinTile >= n) {
+        st(adst + ai, nv);
+        appended = true;
+      }
+#pragma unroll
+      for (int u = 0; u < kWinUnroll; ++u) st(dst + min(c0 + u * kBlock + threadIdx.x, n - 1), v[u]);
+    }
+  }
+  if (!appended) {  // no shift, or a row wider than one pass: after every load
+    if (row_in_one_pass) {
+      st(adst + ai, nv);
+    } else {
+      for (uint32_t i = threadIdx.x; i < row_words; i += kBlock) st(adst + i, ld(nsrc + i));
+    }
+  }
+}
+
+// S > 1, STAGE: tile `tile` of staging[0 .. Lp+S): words of rows [0, Lp) from
+// the cache, of rows [Lp, Lp+S) from the (strided) new rows.
+template <int VEC>
+__device__ __forceinline__ void stage_tile(const WindowGeom &g, const char *cache_slice,
+                                           char *stage_slice, const char *new_rows, int64_t Lp,
+                                           uint32_t tile) {
+  using W = typename Word<VEC>::T;
+  const uint32_t n_seed = uint32_t(Lp) * g.row_words;
+  const uint32_t n = uint32_t(Lp + g.S) * g.row_words;
+  const uint32_t i0 = tile * kWinTile;
+  if (i0 >= n) return;
+  const W *cache = reinterpret_cast<const W *>(cache_slice);
+  W *stage = reinterpret_cast<W *>(stage_slice);
+  W v[kWinUnroll];
+#pragma unroll
+  for (int u = 0; u < kWinUnroll; ++u) {
+    const uint32_t i = min(i0 + u * kBlock + threadIdx.x, n - 1);  // tail lanes repeat the last word
+    const uint32_t j = i < n_seed ? 0 : i - n_seed, r = g.by_row.div(j), c = j - r * g.row_words;
+    const W *p = i < n_seed ? cache + i : reinterpret_cast<const W *>(new_rows + int64_t(r) * g.nb_s) + c;
+    v[u] = ld(p);
+  }
+#pragma unroll
+  for (int u = 0; u < kWinUnroll; ++u) st(stage + min(i0 + u * kBlock + threadIdx.x, n - 1), v[u]);
+}
+
+// S > 1, COMMIT: tile `tile` of cache[0 .. L) <- staging[E .. E+L), or of rows
+// [Lp, L) only when nothing was evicted (rows below Lp of staging are the
+// cache's own rows).
+template <int VEC>
+__device__ __forceinline__ void commit_tile(const WindowGeom &g, char *cache_slice,
+                                            const char *stage_slice, int64_t Lp, int64_t E,
+                                            uint32_t tile) {
+  using W = typename Word<VEC>::T;
+  const int64_t L = Lp + g.S - E;
+  const int64_t r0 = E ? 0 : Lp;
+  const uint32_t n = uint32_t(L - r0) * g.row_words;
+  const uint32_t i0 = tile * kWinTile;
+  if (i0 >= n) return;
+  W *dst = reinterpret_cast<W *>(cache_slice + uint64_t(r0) * g.row_bytes);
+  const W *src = reinterpret_cast<const W *>(stage_slice + uint64_t(E + r0) * g.row_bytes);
+  W v[kWinUnroll];
+#pragma unroll
+  for (int u = 0; u < kWinUnroll; ++u) v[u] = ld(src + min(i0 + u * kBlock + threadIdx.x, n - 1));
+#pragma unroll
+  for (int u = 0; u < kWinUnroll; ++u) st(dst + min(i0 + u * kBlock + threadIdx.x, n - 1), v[u]);
+}
+
+}  // namespace swrt

@@ -1,4 +1,4 @@
-"""One whole-model decode step of KV-cache updates (three launches).
+"""One whole-model decode step of KV-cache updates (one launch, or three).
 
 A model whose layers alternate between windowed attention (a window-sized
 cache, pull request "GQA support sliding_window_cache", section "Design") and
@@ -11,10 +11,12 @@ each layer receives one new K row and one new V row per (batch, kv-head):
   2. kv_window_append_layers  every windowed layer's K and V: shift by E and
                               append at Lp - E, in place (S = 1), one launch;
   3. tensor_scatter_batched   every full layer's K and V: write row T - 1,
-                              in place, one launch.
+                              in place, one launch;
 
-The buffers are plain torch tensors on one device; the step only issues the
-three library calls on the current stream, so it can be captured in a graph.
+or all three in one launch (kv_decode_step, the default), which writes the
+same bytes. The buffers are plain torch tensors on one device; the step only
+issues library calls (marshalled once) on the current stream, so it can be
+captured in a graph.
 """
 from __future__ import annotations
 
@@ -77,25 +79,50 @@ class ModelDecodeStep:
         )
 
     # -- the step ---------------------------------------------------------
+    def _prepared(self):
+        if getattr(self, "_calls", None) is None:
+            b, s = self.buffers, self.spec
+            caches = b.full_k + b.full_v
+            self._calls = {
+                "lengths": swrt.prepare_kv_seq_lengths(b.seqlens_k, 1, s.window, out=b.lengths,
+                                                       flags=b.flags),
+                "windowed": swrt.prepare_kv_window_append_layers(
+                    b.win_k, b.win_v, b.win_kn, b.win_vn, b.lengths.cache_past, b.lengths.evict,
+                    flags=b.flags),
+                "full": swrt.prepare_tensor_scatter_batched(
+                    caches, b.full_kn + b.full_vn, b.write_indices, axis=2, mode="linear",
+                    outs=caches, flags=b.flags),
+                "fused": swrt.prepare_kv_decode_step(
+                    b.win_k, b.win_v, b.win_kn, b.win_vn, b.seqlens_k, caches,
+                    b.full_kn + b.full_vn, b.write_indices, out=b.lengths, flags=b.flags),
+            }
+        return self._calls
+
     def lengths(self):
-        b = self.buffers
-        swrt.kv_seq_lengths(b.seqlens_k, 1, self.spec.window, out=b.lengths, flags=b.flags)
+        self._prepared()["lengths"]()
 
     def windowed(self):
-        b = self.buffers
-        swrt.kv_window_append_layers(b.win_k, b.win_v, b.win_kn, b.win_vn, b.lengths.cache_past,
-                                     b.lengths.evict, flags=b.flags)
+        self._prepared()["windowed"]()
 
     def full(self):
-        b = self.buffers
-        caches = b.full_k + b.full_v
-        swrt.tensor_scatter_batched(caches, b.full_kn + b.full_vn, b.write_indices, axis=2,
-                                    mode="linear", outs=caches, flags=b.flags)
+        self._prepared()["full"]()
 
-    def run(self):
-        self.lengths()
-        self.windowed()
-        self.full()
+    def run_three(self):
+        """The step as three launches: lengths, windowed layers, full layers."""
+        c = self._prepared()
+        c["lengths"]()
+        c["windowed"]()
+        c["full"]()
+
+    def run_fused(self):
+        """The step as one launch (swrt_kv_decode_step)."""
+        self._prepared()["fused"]()
+
+    def run(self, fused: bool = True):
+        if fused:
+            self.run_fused()
+        else:
+            self.run_three()
 
     # -- accounting -------------------------------------------------------
     def algorithmic_bytes(self) -> dict:

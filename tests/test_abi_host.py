@@ -47,7 +47,8 @@ def _header():
 def test_exports_every_declared_function(L):
     declared = set(re.findall(r"^(?:int|const char \*)\s*(swrt_\w+)\s*\(", _header(), re.M))
     assert {"swrt_tensor_scatter", "swrt_tensor_scatter_batched", "swrt_kv_seq_lengths", "swrt_kv_window_append",
-            "swrt_kv_window_append_layers", "swrt_status_string", "swrt_abi_version"} <= declared
+            "swrt_kv_window_append_layers", "swrt_kv_decode_step", "swrt_status_string",
+            "swrt_abi_version"} <= declared
     out = subprocess.run(["nm", "-D", "--defined-only", swrt.LIBRARY], check=True,
                          capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT (swrt_\w+)", out))
@@ -211,3 +212,24 @@ def test_kv_window_append_rejects(L):
     st = L.swrt_kv_window_append_layers(2, kcs, vcs, kns, kns, (I64 * 3)(32, 16, 16), None, None,
                                         D_, D_ + 0x1000, 2, 2, 8, 1, 16, 16, 3, None, None)
     assert st == INV
+
+
+@no_gpu_visible
+def test_kv_decode_step_rejects(L):
+    INV = swrt.E_INVALID_ARG
+    V = ctypes.c_void_p
+
+    def call(nw=1, nf=1, wk=A, wv=A + 0x1000_0000, fc=C_, sk=D_, C=8, M=16, batch=2, lens=None):
+        arr = lambda *p: (V * len(p))(*p)  # noqa: E731
+        return L.swrt_kv_decode_step(nw, arr(wk), arr(wv), arr(B_), arr(B_ + 0x1000),
+                                     (I64 * 3)(32, 16, 16), sk, C, None, None, lens, None, None,
+                                     nf, arr(fc), arr(B_ + 0x2000), D_ + 0x1000, M, batch, 2, 16,
+                                     16, None, None)
+    assert call(nw=33) == INV and call(nf=65) == INV and call(nw=-1) == INV
+    assert call(C=0) == INV and call(batch=-1) == INV
+    assert call(sk=0) == INV                                   # windowed layers need seqlens_k
+    assert call(fc=A + 64) == INV                              # full cache inside a windowed one
+    assert call(M=0) == INV                                    # S = 1 > M
+    assert call(lens=D_ + 4) == INV                            # length output inside seqlens_k
+    assert call(sk=D_ + 2) == INV                              # misaligned seqlens_k
+    assert call(nw=0, nf=0) == swrt.OK                         # nothing to do

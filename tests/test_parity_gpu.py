@@ -526,21 +526,22 @@ def hb_t(t):
 # the whole-model decode step at full size, in the benchmark's launch shape
 # ---------------------------------------------------------------------------
 
+@pytest.mark.parametrize("fused", [True, False], ids=["one_launch", "three_launches"])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float8_e4m3fn])
-def test_workload5_model_step_full_size(orc, dtype):
+def test_workload5_model_step_full_size(orc, dtype, fused):
     spec = wl.workload5(dtype)
-    say("workload5", dtype)
+    say("workload5", dtype, "fused" if fused else "three launches")
     step = ModelDecodeStep(spec, DEV, set_id=0, raw_bits=True)
     b = step.buffers
     win_before = [(hb(k).copy(), hb(v).copy()) for k, v in zip(b.win_k, b.win_v)]
     sample = [0, len(b.full_k) - 1]  # full layers compared whole; the rest by their new rows
     full_before = {i: (hb(b.full_k[i]).copy(), hb(b.full_v[i]).copy()) for i in sample}
-    step.run()
+    step.run(fused=fused)
     torch.cuda.synchronize()
     assert b.flags.item() == 0
     L = orc.kv_seq_lengths(spec.seqlens_k, 1, spec.window)
-    np.testing.assert_array_equal(b.lengths.cache_past.cpu().numpy(), L.cache_past)
-    np.testing.assert_array_equal(b.lengths.evict.cpu().numpy(), L.evict)
+    for got, want in zip(b.lengths, (L.total, L.past, L.cache_past, L.cache_total, L.evict)):
+        np.testing.assert_array_equal(got.cpu().numpy(), want)
     D, H = spec.head_dim, spec.kv_heads
     bits = torch.empty((), dtype=dtype).element_size() * 8
     for i, (hk, hv) in enumerate(win_before):
@@ -562,3 +563,94 @@ def test_workload5_model_step_full_size(orc, dtype):
     for cache, new in zip(b.full_k + b.full_v, b.full_kn + b.full_vn):
         got = cache.view(torch.uint8)[bi, :, wi, :]  # [B, H, row bytes]
         assert torch.equal(got, new.view(torch.uint8)[:, :, 0, :])
+
+
+# ---------------------------------------------------------------------------
+# the one-launch decode step against the three-call composition
+# ---------------------------------------------------------------------------
+
+def _decode_buffers(g, B, H, C, M, D, nw, nf, dtype):
+    mk = lambda shape: wl.host_payload(g, shape, dtype, raw_bits=True)  # noqa: E731
+    return ([mk((B, H, C, D)) for _ in range(nw)], [mk((B, H, C, D)) for _ in range(nw)],
+            [mk((B, H, 1, D)) for _ in range(nw)], [mk((B, H, 1, D)) for _ in range(nw)],
+            [mk((B, H, M, D)) for _ in range(nf)], [mk((B, H, 1, D)) for _ in range(nf)])
+
+
+_DECODE_CASES = ["both", "windowed_only", "full_only", "bad_seqlens", "linear_out_of_range",
+                 "odd_rows"]
+
+
+@pytest.mark.parametrize("case", _DECODE_CASES)
+def test_decode_step_one_launch_equals_three(orc, case):
+    g = wl.rng(500 + _DECODE_CASES.index(case))
+    B, H, C, M, D, nw, nf, dtype = 9, 3, 16, 40, 64, 3, 4, torch.bfloat16
+    if case == "windowed_only":
+        nf = 0
+    if case == "full_only":
+        nw = 1  # the windowed part needs one layer; lengths still come out
+    if case == "odd_rows":
+        D, dtype = 5, torch.float32  # 20-byte rows: 4-byte words
+    say("decode step", case)
+    T = g.integers(1, 3 * C, size=B)
+    sk = (T - 1).astype(np.int32)
+    wi = (T - 1).astype(np.int64) % M
+    if case == "bad_seqlens":
+        sk[[0, 3]] = [-7, -1]
+    if case == "linear_out_of_range":
+        wi[[1, 5]] = [M, -2]
+    host = _decode_buffers(g, B, H, C, M, D, nw, nf, dtype)
+    results = []
+    for fused in (True, False):
+        wk, wv, wkn, wvn, fc, fn = [[t.to(DEV) for t in grp] for grp in host]
+        sk_d, wi_d = torch.from_numpy(sk).to(DEV), torch.from_numpy(wi).to(DEV)
+        flags = flag_word()
+        if fused:
+            lens = swrt.kv_decode_step(wk, wv, wkn, wvn, sk_d, fc, fn, wi_d, flags=flags)
+        else:
+            lens = swrt.kv_seq_lengths(sk_d, 1, C, flags=flags)
+            swrt.kv_window_append_layers(wk, wv, wkn, wvn, lens.cache_past, lens.evict,
+                                         flags=flags)
+            if nf:
+                swrt.tensor_scatter_batched(fc, fn, wi_d, axis=2, mode="linear", outs=fc,
+                                            flags=flags)
+        torch.cuda.synchronize()
+        results.append(([hb(t) for t in (*wk, *wv, *fc, *lens)], flags.item()))
+    (a, fa), (b3, fb) = results
+    assert fa == fb
+    for x, y in zip(a, b3):
+        np.testing.assert_array_equal(x, y)
+    # and both against the oracle
+    L = orc.kv_seq_lengths(sk, 1, C)
+    want_flags = L.flags
+    bits = torch.empty((), dtype=dtype).element_size() * 8
+    wk, wv, wkn, wvn, fc, fn = [[hb(t).copy() for t in grp] for grp in host]
+    for i in range(nw):
+        want_flags |= orc.kv_window_append_strided(wk[i], wv[i], wkn[i], wvn[i], (H * D, D, D), 1,
+                                                   L.cache_past, L.evict, elem_bits=bits,
+                                                   head_dim=D)
+    for c, u in zip(fc, fn):
+        st, f = orc.tensor_scatter_raw(c, c, u, wi, (B, H, M, D), 2, 1, 0, bits)
+        assert st == 0
+        want_flags |= f
+    assert fa == want_flags
+    want = [*wk, *wv, *fc]
+    for x, y in zip(a[:len(want)], want):
+        np.testing.assert_array_equal(x, y)
+    if case == "bad_seqlens":
+        assert fa & swrt.FLAG_BAD_SEQLEN
+    if case == "linear_out_of_range":
+        assert fa & swrt.FLAG_LINEAR_OOB
+
+
+def test_decode_step_rejects_overlap():
+    B, H, C, M, D = 2, 2, 8, 16, 16
+    big = torch.zeros(B * H * M * D + B * H * C * D, dtype=torch.bfloat16, device=DEV)
+    full = big[:B * H * M * D].view(B, H, M, D)
+    win = big[100:100 + B * H * C * D].view(B, H, C, D)   # inside the full cache
+    other = torch.zeros(B, H, C, D, dtype=torch.bfloat16, device=DEV)
+    new = torch.zeros(B, H, 1, D, dtype=torch.bfloat16, device=DEV)
+    sk = torch.zeros(B, dtype=torch.int32, device=DEV)
+    wi = torch.zeros(B, dtype=torch.int64, device=DEV)
+    with pytest.raises(swrt.SwrtError) as e:
+        swrt.kv_decode_step([win], [other], [new], [new], sk, [full], [new], wi)
+    assert e.value.status == swrt.E_INVALID_ARG
