@@ -12,7 +12,9 @@ Both forms are timed in every run; --form picks the one `value` reports.
 
 Measurement
   - value: algorithmic bytes of a step / time of a step, from K steps bracketed
-    by torch.cuda.synchronize(), replayed as one HIP graph per buffer set.
+    by torch.cuda.synchronize(), issued eagerly with arguments marshalled once
+    (with --timing graph: replayed as one HIP graph per buffer set; on this
+    ROCm a graph launch costs a few microseconds more than a kernel launch).
   - Infinity Cache: every buffer set is independent and --sets sets (default
     3, over 512 MB of windowed caches touched between two uses of one set)
     are visited round robin, so no step finds its data in the 256 MB cache.
@@ -117,6 +119,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--form", default="fused", choices=["fused", "three"],
                     help="one launch per step (default) or the three-call composition")
+    ap.add_argument("--timing", default="eager", choices=["eager", "graph"],
+                    help="the timed loop `value` reports (both are measured)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path has no cross-GPU step (every (b, h) "
@@ -164,6 +168,22 @@ def main():
             torch.cuda.synchronize()
             return (time.perf_counter() - t0) / K
 
+        def eager_time(fn):
+            """K steps issued from the host (arguments marshalled once), wall
+            clock between two synchronizations."""
+            for i in range(W):
+                fn(steps[i % len(steps)])
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(K):
+                fn(steps[i % len(steps)])
+            torch.cuda.synchronize()
+            return (time.perf_counter() - t0) / K
+
+        log(f"timing {K} eager steps, one launch per step ...")
+        eager_fused_s = eager_time(lambda st: st.run_fused())
+        log(f"timing {K} eager steps, three launches per step ...")
+        eager_three_s = eager_time(lambda st: st.run_three())
         log(f"timing {K} graph-replayed steps, one launch per step ...")
         graph_fused_s = graph_time(lambda st: st.run_fused())
         log(f"timing {K} graph-replayed steps, three launches per step ...")
@@ -227,7 +247,10 @@ def main():
     flags = [int(st.buffers.flags.item()) for st in steps]
     if any(flags):
         raise SystemExit(f"device flags raised during the benchmark: {flags}")
-    step_s = graph_fused_s if fused else graph_three_s
+    if args.timing == "eager":
+        step_s = eager_fused_s if fused else eager_three_s
+    else:
+        step_s = graph_fused_s if fused else graph_three_s
     value = acct["total"] / step_s / 1e9
     if fused:
         kname, kbytes, kmean = "decode_step_kernel", acct["total"], fused_mean_s
@@ -274,7 +297,9 @@ def main():
             "form": "one launch per step (kv_decode_step)" if fused else
                     "three launches per step (kv_seq_lengths, kv_window_append_layers, "
                     "tensor_scatter_batched)",
-            "timing": "HIP graph replay, one graph per buffer set",
+            "timing": "eager: library calls with arguments marshalled once, K steps between "
+                      "two synchronizations" if args.timing == "eager" else
+                      "HIP graph replay, one graph per buffer set",
             "cache_defeat": f"{args.sets} independent buffer sets round robin",
         },
         "roofline": {
@@ -290,8 +315,10 @@ def main():
         },
         "cpu_baseline": cpu,
         "one_launch": {"graph_us_per_step": round(graph_fused_s * 1e6, 2),
+                       "eager_us_per_step": round(eager_fused_s * 1e6, 2),
                        "events_us_per_launch": round(fused_mean_s * 1e6, 2)},
         "three_launches": {"graph_us_per_step": round(graph_three_s * 1e6, 2),
+                           "eager_us_per_step": round(eager_three_s * 1e6, 2),
                            "events_us_per_step": round(three_eager_s * 1e6, 2),
                            "window_kernel_us": round(win_mean_s * 1e6, 3),
                            "window_kernel_gbs": round(acct["windowed"] / win_mean_s / 1e9, 1)},

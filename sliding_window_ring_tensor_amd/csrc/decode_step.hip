@@ -15,7 +15,7 @@
 // Workgroup roles (uniform per workgroup): the first workgroups carry the
 // full-cache row writes, the rest one windowed slice each; every window
 // workgroup derives its own (Lp, E) from seqlens_k with the same arithmetic
-// as kv_seq_lengths, and the first ceil(B / 256) workgroups also write the
+// as kv_seq_lengths, and the first ceil(B / 512) workgroups also write the
 // length arrays for the attention that follows. Two kernel boundaries per
 // step disappear, and with them their dispatch and cache-maintenance cost.
 #include "swrt_host.hpp"
@@ -37,12 +37,14 @@ struct DecodeArgs {
   int32_t batch;
 };
 
+constexpr uint32_t kFullTile = kWinBlock * kScatUnroll;  // full-cache words per workgroup
+
 template <int VEC>
-__global__ __launch_bounds__(kBlock) void decode_step_kernel(DecodeArgs a) {
-  __shared__ TileBatches tb;
+__global__ __launch_bounds__(kWinBlock) void decode_step_kernel(DecodeArgs a) {
+  __shared__ TileBatches<kFullTile> tb;
   const uint32_t bid = blockIdx.x;
   if (bid < a.len_blocks) {  // the length arrays (no barrier in this part)
-    const int32_t b = int32_t(bid * kBlock + threadIdx.x);
+    const int32_t b = int32_t(bid * kWinBlock + threadIdx.x);
     if (b < a.batch) {
       const StepLengths r = step_lengths(a.seqlens_k[b], 1, a.wg.C);
       if (r.bad && a.wg.flags) atomicOr(a.wg.flags, SWRT_FLAG_BAD_SEQLEN);
@@ -55,7 +57,8 @@ __global__ __launch_bounds__(kBlock) void decode_step_kernel(DecodeArgs a) {
   }
   if (bid < a.full_blocks) {  // full caches: TensorScatter rows in place
     const uint32_t t = bid / a.full_tiles;
-    scatter_in_place_tile<VEC>(a.sg, a.fc[t], a.fu[t], (bid - t * a.full_tiles) * kScatTile, tb);
+    scatter_in_place_tile<VEC, kWinBlock>(a.sg, a.fc[t], a.fu[t], (bid - t * a.full_tiles) * kFullTile,
+                                          tb);
     return;
   }
   const uint32_t slice = bid - a.full_blocks;
@@ -122,7 +125,7 @@ extern "C" int swrt_kv_decode_step(int n_window_layers, void *const *win_k_cache
   const int vec = word_of((wp.empty ? 0 : wp.align) | (sp.empty ? 0 : sp.align) |
                           uint64_t(wp.empty && sp.empty ? 16 : 0));
   if (!wp.empty && (st = finish_window(&wp, vec)) != SWRT_OK) return st;
-  if (!sp.empty && (st = finish_scatter(&sp, vec)) != SWRT_OK) return st;
+  if (!sp.empty && (st = finish_scatter(&sp, vec, kFullTile)) != SWRT_OK) return st;
 
   static_assert(sizeof(DecodeArgs) <= 4096, "kernel arguments exceed 4 KiB");
   DecodeArgs a;
@@ -148,18 +151,18 @@ extern "C" int swrt_kv_decode_step(int n_window_layers, void *const *win_k_cache
   a.batch = batch;
   a.full_tiles = sp.empty ? 1 : sp.tiles;
   a.full_blocks = sp.empty ? 0 : sp.tiles * uint32_t(sp.n);
-  a.len_blocks = do_len ? uint32_t((B + kBlock - 1) / kBlock) : 0;
+  a.len_blocks = do_len ? uint32_t((B + kWinBlock - 1) / kWinBlock) : 0;
   a.win_blocks = wp.empty ? 0 : wp.slices;
   uint64_t grid = uint64_t(a.full_blocks) + a.win_blocks;
   if (grid < a.len_blocks) grid = a.len_blocks;  // length arrays alone
   if (grid >= (uint64_t(1) << 31)) return SWRT_E_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (vec) {
-    case 16: hipLaunchKernelGGL(decode_step_kernel<16>, dim3(grid), dim3(kBlock), 0, s, a); break;
-    case 8: hipLaunchKernelGGL(decode_step_kernel<8>, dim3(grid), dim3(kBlock), 0, s, a); break;
-    case 4: hipLaunchKernelGGL(decode_step_kernel<4>, dim3(grid), dim3(kBlock), 0, s, a); break;
-    case 2: hipLaunchKernelGGL(decode_step_kernel<2>, dim3(grid), dim3(kBlock), 0, s, a); break;
-    default: hipLaunchKernelGGL(decode_step_kernel<1>, dim3(grid), dim3(kBlock), 0, s, a); break;
+    case 16: hipLaunchKernelGGL(decode_step_kernel<16>, dim3(grid), dim3(kWinBlock), 0, s, a); break;
+    case 8: hipLaunchKernelGGL(decode_step_kernel<8>, dim3(grid), dim3(kWinBlock), 0, s, a); break;
+    case 4: hipLaunchKernelGGL(decode_step_kernel<4>, dim3(grid), dim3(kWinBlock), 0, s, a); break;
+    case 2: hipLaunchKernelGGL(decode_step_kernel<2>, dim3(grid), dim3(kWinBlock), 0, s, a); break;
+    default: hipLaunchKernelGGL(decode_step_kernel<1>, dim3(grid), dim3(kWinBlock), 0, s, a); break;
   }
   return launch_status();
 }

@@ -23,7 +23,7 @@ struct WinArgs {
 };
 
 template <int VEC, int NL>
-__global__ __launch_bounds__(kBlock) void window_in_place(WinArgs<NL> a) {
+__global__ __launch_bounds__(kWinBlock) void window_in_place(WinArgs<NL> a) {
   const Slice s = decode_slice(a.g, blockIdx.x);
   const int64_t Lp = a.g.lp[s.b], E = a.g.ev[s.b];
   if (!lengths_ok(a.g, s, 0, Lp, E)) return;
@@ -33,7 +33,7 @@ __global__ __launch_bounds__(kBlock) void window_in_place(WinArgs<NL> a) {
 }
 
 template <int VEC, int NL>
-__global__ __launch_bounds__(kBlock) void window_stage(WinArgs<NL> a) {
+__global__ __launch_bounds__(kWinBlock) void window_stage(WinArgs<NL> a) {
   const uint32_t slice = blockIdx.x / a.g.tiles, tile = blockIdx.x - slice * a.g.tiles;
   const Slice s = decode_slice(a.g, slice);
   const int64_t Lp = a.g.lp[s.b], E = a.g.ev[s.b];
@@ -45,7 +45,7 @@ __global__ __launch_bounds__(kBlock) void window_stage(WinArgs<NL> a) {
 }
 
 template <int VEC, int NL>
-__global__ __launch_bounds__(kBlock) void window_commit(WinArgs<NL> a) {
+__global__ __launch_bounds__(kWinBlock) void window_commit(WinArgs<NL> a) {
   const uint32_t slice = blockIdx.x / a.g.tiles, tile = blockIdx.x - slice * a.g.tiles;
   const Slice s = decode_slice(a.g, slice);
   const int64_t Lp = a.g.lp[s.b], E = a.g.ev[s.b];
@@ -67,18 +67,18 @@ int launch(const WindowPlan &p, unsigned phase, hipStream_t stream) {
     }
   a.g = p.g;
   if (p.g.S == 1) {
-    hipLaunchKernelGGL((window_in_place<VEC, NL>), dim3(p.slices), dim3(kBlock), 0, stream, a);
+    hipLaunchKernelGGL((window_in_place<VEC, NL>), dim3(p.slices), dim3(kWinBlock), 0, stream, a);
     return launch_status();
   }
   if (phase & SWRT_PHASE_STAGE) {
     a.g.tiles = uint32_t((uint64_t(p.g.C + p.g.S) * p.g.row_words + kWinTile - 1) / kWinTile);
-    hipLaunchKernelGGL((window_stage<VEC, NL>), dim3(p.slices * a.g.tiles), dim3(kBlock), 0,
+    hipLaunchKernelGGL((window_stage<VEC, NL>), dim3(p.slices * a.g.tiles), dim3(kWinBlock), 0,
                        stream, a);
     if (launch_status() != SWRT_OK) return SWRT_E_LAUNCH;
   }
   if (phase & SWRT_PHASE_COMMIT) {
     a.g.tiles = uint32_t((uint64_t(p.g.C) * p.g.row_words + kWinTile - 1) / kWinTile);
-    hipLaunchKernelGGL((window_commit<VEC, NL>), dim3(p.slices * a.g.tiles), dim3(kBlock), 0,
+    hipLaunchKernelGGL((window_commit<VEC, NL>), dim3(p.slices * a.g.tiles), dim3(kWinBlock), 0,
                        stream, a);
     if (launch_status() != SWRT_OK) return SWRT_E_LAUNCH;
   }

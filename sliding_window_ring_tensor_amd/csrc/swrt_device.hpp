@@ -16,7 +16,7 @@
 
 namespace swrt {
 
-constexpr int kBlock = 256;  // threads per workgroup: 4 wave64s
+constexpr int kBlock = 256;  // threads per workgroup of the small kernels (4 wave64s)
 
 // ---------------------------------------------------------------------------
 // raw-bit words

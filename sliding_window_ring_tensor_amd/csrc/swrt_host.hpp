@@ -71,6 +71,7 @@ int plan_scatter(int n_tensors, void *const *presents, const void *const *pasts,
                  int rank, int axis, int64_t seq_len, int mode, int elem_bits, uint32_t *d_flags,
                  ScatterPlan *p, Range *ranges, int *nr);
 
-int finish_scatter(ScatterPlan *p, int vec);
+// tile_words: words per workgroup tile of the kernel that will run the plan
+int finish_scatter(ScatterPlan *p, int vec, uint32_t tile_words);
 
 }  // namespace swrt

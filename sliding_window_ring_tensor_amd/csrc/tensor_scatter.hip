@@ -21,20 +21,22 @@ struct ScatterArgs {
   ScatterGeom g;
 };
 
+constexpr uint32_t kTile = kScatBlock * kScatUnroll;
+
 template <int VEC, int NT>
-__global__ __launch_bounds__(kBlock) void scatter_in_place(ScatterArgs<NT> a) {
-  __shared__ TileBatches tb;
+__global__ __launch_bounds__(kScatBlock) void scatter_in_place(ScatterArgs<NT> a) {
+  __shared__ TileBatches<kTile> tb;
   const uint32_t t = blockIdx.x / a.tiles;  // which tensor of a batched call
-  const uint32_t tile = (blockIdx.x - t * a.tiles) * kScatTile;
-  scatter_in_place_tile<VEC>(a.g, a.present[t], a.update[t], tile, tb);
+  const uint32_t tile = (blockIdx.x - t * a.tiles) * kTile;
+  scatter_in_place_tile<VEC, kScatBlock>(a.g, a.present[t], a.update[t], tile, tb);
 }
 
 template <int VEC, int NT>
-__global__ __launch_bounds__(kBlock) void scatter_out_of_place(ScatterArgs<NT> a) {
-  __shared__ TileBatches tb;
+__global__ __launch_bounds__(kScatBlock) void scatter_out_of_place(ScatterArgs<NT> a) {
+  __shared__ TileBatches<kTile> tb;
   const uint32_t t = blockIdx.x / a.tiles;
-  const uint32_t tile = (blockIdx.x - t * a.tiles) * kScatTile;
-  scatter_out_of_place_tile<VEC>(a.g, a.present[t], a.past[t], a.update[t], tile, tb);
+  const uint32_t tile = (blockIdx.x - t * a.tiles) * kTile;
+  scatter_out_of_place_tile<VEC, kScatBlock>(a.g, a.present[t], a.past[t], a.update[t], tile, tb);
 }
 
 template <int VEC, int NT>
@@ -49,9 +51,9 @@ int launch(const ScatterPlan &p, hipStream_t stream) {
   a.g = p.g;
   const dim3 grid(p.tiles * uint32_t(p.n));
   if (p.in_place)
-    hipLaunchKernelGGL((scatter_in_place<VEC, NT>), grid, dim3(kBlock), 0, stream, a);
+    hipLaunchKernelGGL((scatter_in_place<VEC, NT>), grid, dim3(kScatBlock), 0, stream, a);
   else
-    hipLaunchKernelGGL((scatter_out_of_place<VEC, NT>), grid, dim3(kBlock), 0, stream, a);
+    hipLaunchKernelGGL((scatter_out_of_place<VEC, NT>), grid, dim3(kScatBlock), 0, stream, a);
   return launch_status();
 }
 
@@ -80,7 +82,7 @@ int scatter(int n_tensors, void *const *presents, const void *const *pasts,
   if (written_overlap(ranges, nr)) return SWRT_E_INVALID_ARG;
   if (p.empty) return SWRT_OK;
   const int vec = word_of(p.align);
-  if ((st = finish_scatter(&p, vec)) != SWRT_OK) return st;
+  if ((st = finish_scatter(&p, vec, kTile)) != SWRT_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return p.n == 1 ? dispatch<1>(p, vec, s) : dispatch<kMaxTensors>(p, vec, s);
 }
@@ -157,12 +159,12 @@ int plan_scatter(int n_tensors, void *const *presents, const void *const *pasts,
   return SWRT_OK;
 }
 
-int finish_scatter(ScatterPlan *p, int vec) {
+int finish_scatter(ScatterPlan *p, int vec, uint32_t tile_words) {
   const int64_t words_per_row = p->row / vec;
   int64_t n_words;
   if (!mul_ok(p->rows, words_per_row, &n_words) || n_words >= (int64_t(1) << 31))
     return SWRT_E_UNSUPPORTED;
-  const int64_t tiles = (n_words + kScatTile - 1) / kScatTile;
+  const int64_t tiles = (n_words + tile_words - 1) / tile_words;
   if (tiles * p->n >= (int64_t(1) << 31)) return SWRT_E_UNSUPPORTED;
   p->tiles = uint32_t(tiles);
   p->g.n_words = uint32_t(n_words);

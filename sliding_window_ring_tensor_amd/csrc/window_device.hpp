@@ -15,11 +15,19 @@
 
 namespace swrt {
 
-#ifndef SWRT_WINDOW_UNROLL
-#define SWRT_WINDOW_UNROLL 4
+// Workgroup shape of the window kernels: 512 threads (8 wave64s) moving two
+// 16-byte words each per tile, i.e. one 16 KiB tile. Measured on MI355X for
+// the decode step (C = 128, D = 64, bf16: one 16 KiB slice per workgroup):
+// 512 x 2 beat 256 x 4, 128 x 8, 1024 x 1 and the 8 KiB tiles.
+#ifndef SWRT_WIN_BLOCK
+#define SWRT_WIN_BLOCK 512
 #endif
+#ifndef SWRT_WINDOW_UNROLL
+#define SWRT_WINDOW_UNROLL 2
+#endif
+constexpr int kWinBlock = SWRT_WIN_BLOCK;
 constexpr int kWinUnroll = SWRT_WINDOW_UNROLL;  // words per thread per tile
-constexpr uint32_t kWinTile = kBlock * kWinUnroll;
+constexpr uint32_t kWinTile = kWinBlock * kWinUnroll;
 
 // ---------------------------------------------------------------------------
 // lengths of one step (same page, section "Design"; the follow-up commit does
@@ -108,7 +116,7 @@ __device__ __forceinline__ void shift_append_slice(char *base, const char *new_r
   // overlaps the shift; it is stored at row Lp - E.
   const W *nsrc = reinterpret_cast<const W *>(new_row);
   W *adst = reinterpret_cast<W *>(base + uint64_t(Lp - E) * row_bytes);
-  const bool row_in_one_pass = row_words <= uint32_t(kBlock);
+  const bool row_in_one_pass = row_words <= uint32_t(kWinBlock);
   const uint32_t ai = min(threadIdx.x, row_words - 1);
   W nv;
   if (row_in_one_pass) nv = ld(nsrc + ai);
@@ -119,7 +127,7 @@ __device__ __forceinline__ void shift_append_slice(char *base, const char *new_r
     for (uint32_t c0 = 0; c0 < n; c0 += kWinTile) {
       W v[kWinUnroll];
 #pragma unroll
-      for (int u = 0; u < kWinUnroll; ++u) v[u] = ld(src + min(c0 + u * kBlock + threadIdx.x, n - 1));
+      for (int u = 0; u < kWinUnroll; ++u) v[u] = ld(src + min(c0 + u * kWinBlock + threadIdx.x, n - 1));
       __syncthreads();  // every old value of this tile is in registers
       // Row Lp - E is read by the last tile and is no shift destination: the
       // new row can go out as soon as that tile's loads are done.
@@ -128,14 +136,14 @@ __device__ __forceinline__ void shift_append_slice(char *base, const char *new_r
         appended = true;
       }
 #pragma unroll
-      for (int u = 0; u < kWinUnroll; ++u) st(dst + min(c0 + u * kBlock + threadIdx.x, n - 1), v[u]);
+      for (int u = 0; u < kWinUnroll; ++u) st(dst + min(c0 + u * kWinBlock + threadIdx.x, n - 1), v[u]);
     }
   }
   if (!appended) {  // no shift, or a row wider than one pass: after every load
     if (row_in_one_pass) {
       st(adst + ai, nv);
     } else {
-      for (uint32_t i = threadIdx.x; i < row_words; i += kBlock) st(adst + i, ld(nsrc + i));
+      for (uint32_t i = threadIdx.x; i < row_words; i += kWinBlock) st(adst + i, ld(nsrc + i));
     }
   }
 }
@@ -156,13 +164,13 @@ __device__ __forceinline__ void stage_tile(const WindowGeom &g, const char *cach
   W v[kWinUnroll];
 #pragma unroll
   for (int u = 0; u < kWinUnroll; ++u) {
-    const uint32_t i = min(i0 + u * kBlock + threadIdx.x, n - 1);  // tail lanes repeat the last word
+    const uint32_t i = min(i0 + u * kWinBlock + threadIdx.x, n - 1);  // tail lanes repeat the last word
     const uint32_t j = i < n_seed ? 0 : i - n_seed, r = g.by_row.div(j), c = j - r * g.row_words;
     const W *p = i < n_seed ? cache + i : reinterpret_cast<const W *>(new_rows + int64_t(r) * g.nb_s) + c;
     v[u] = ld(p);
   }
 #pragma unroll
-  for (int u = 0; u < kWinUnroll; ++u) st(stage + min(i0 + u * kBlock + threadIdx.x, n - 1), v[u]);
+  for (int u = 0; u < kWinUnroll; ++u) st(stage + min(i0 + u * kWinBlock + threadIdx.x, n - 1), v[u]);
 }
 
 // S > 1, COMMIT: tile `tile` of cache[0 .. L) <- staging[E .. E+L), or of rows
@@ -182,9 +190,9 @@ __device__ __forceinline__ void commit_tile(const WindowGeom &g, char *cache_sli
   const W *src = reinterpret_cast<const W *>(stage_slice + uint64_t(E + r0) * g.row_bytes);
   W v[kWinUnroll];
 #pragma unroll
-  for (int u = 0; u < kWinUnroll; ++u) v[u] = ld(src + min(i0 + u * kBlock + threadIdx.x, n - 1));
+  for (int u = 0; u < kWinUnroll; ++u) v[u] = ld(src + min(i0 + u * kWinBlock + threadIdx.x, n - 1));
 #pragma unroll
-  for (int u = 0; u < kWinUnroll; ++u) st(dst + min(i0 + u * kBlock + threadIdx.x, n - 1), v[u]);
+  for (int u = 0; u < kWinUnroll; ++u) st(dst + min(i0 + u * kWinBlock + threadIdx.x, n - 1), v[u]);
 }
 
 }  // namespace swrt
