@@ -47,7 +47,11 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD's published peak
 # HBM bytes per launch of the dominant kernel from two rocprofv3 counter passes
 # (FETCH_SIZE, WRITE_SIZE), each scaled by what the counter reads for a 1 GiB
 # copy; valid only for the kernel source they were taken on (its hash).
-MEASURED_TRAFFIC = {}
+MEASURED_TRAFFIC = {
+    ("bf16", "decode_step_kernel", "880137acf7bb05ad"): {"read": 196_773_137,
+                                                         "written": 196_848_891},
+    ("bf16", "window_in_place", "79910ea0398d8c78"): {"read": 195_179_285, "written": 195_994_201},
+}
 _CSRC = "sliding_window_ring_tensor_amd/csrc/"
 KERNEL_SOURCES = {
     "window_in_place": ("kv_window.hip", "window_device.hpp", "swrt_device.hpp"),
