@@ -112,6 +112,152 @@ def cpu_baseline(step, seconds: float):
     return n, el
 
 
+def _timers(stream, K, W):
+    """eager wall clock, event-timed device time and graph replay of fn(set)."""
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record(stream)
+    torch.cuda._sleep(1_000_000)
+    s1.record(stream)
+    torch.cuda.synchronize()
+    cycles_per_s = 1_000_000 / (s0.elapsed_time(s1) * 1e-3)
+
+    def eager(fn, n_sets):
+        for i in range(W):
+            fn(i % n_sets)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K):
+            fn(i % n_sets)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / K
+
+    def device(fn, n_sets, host_s):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(int(cycles_per_s * min(2.0, 2.0 * K * host_s + 0.05)))
+        a.record(stream)
+        for i in range(K):
+            fn(i % n_sets)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e-3 / K
+
+    def graph(fn, n_sets):
+        graphs = []
+        for i in range(n_sets):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                fn(i)
+            graphs.append(g)
+        for i in range(W):
+            graphs[i % n_sets].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K):
+            graphs[i % n_sets].replay()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / K
+
+    return eager, device, graph
+
+
+def other_workload(args, dev):
+    """Workloads 1-4: same timing method as the decode step, one JSON line."""
+    import sliding_window_ring_tensor_amd as swrt
+    from sliding_window_ring_tensor_amd import workloads as wl
+
+    K, W, n = args.steps, args.warmup, args.workload
+    sets, calls, desc = [], [], ""
+    if n in (1, 2):
+        cases = [wl.workload1()] if n == 1 else list(wl.workload2())
+        c0 = cases[0]
+        es = torch.empty((), dtype=c0.dtype).element_size()
+        row = int(np.prod(c0.shape[c0.axis + 1:])) * es
+        O = int(np.prod(c0.shape[:c0.axis]))
+        step_bytes = sum(2 * O * c.seq_len * row for c in cases)
+        touched = step_bytes
+        n_sets = 64 if n == 1 else int(np.ceil(512e6 / touched)) + 1
+        for k in range(n_sets):
+            cache = wl.payload(c0.shape, c0.dtype, c0.seed, 1000 + 10 * k, dev)
+            seq = []
+            for c in cases:
+                upd = wl.payload(c.update_shape, c.dtype, c.seed, 1000 + 10 * k + 1 + c.buffer_id, dev)
+                wi = torch.from_numpy(c.write_indices).to(dev)
+                seq.append(swrt.prepare_tensor_scatter(cache, upd, wi, axis=c.axis, mode=c.mode,
+                                                       out=cache))
+            calls.append(seq)
+        desc = " then ".join(c.name for c in cases)
+    elif n == 3:
+        c = wl.workload3()
+        es = torch.empty((), dtype=c.dtype).element_size()
+        row = c.head_dim * es
+        T = c.seqlens_k.astype(np.int64) + 1
+        Lp = np.minimum(T - 1, c.capacity)
+        E = np.maximum(0, Lp + 1 - c.capacity)
+        step_bytes = int((2 * row * (E * (Lp - E) + 1)).sum()) * c.kv_heads * 2
+        n_sets = int(np.ceil(512e6 / step_bytes)) + 1
+        for k in range(n_sets):
+            c.buffer_id = 10 + k
+            kc, vc, kn, vn = wl.window_payloads(c, device=dev)
+            sk = torch.from_numpy(c.seqlens_k).to(dev)
+            calls.append([swrt.prepare_kv_decode_step([kc], [vc], [kn], [vn], sk, [], [], None)])
+        desc = c.name + " (lengths + shift/append in one launch)"
+    else:
+        c, _ = wl.workload4()
+        es = torch.empty((), dtype=c.dtype).element_size()
+        row = c.head_dim * es
+        T = c.seqlens_k.astype(np.int64) + 1
+        S, C = c.seq_len, c.capacity
+        Lp = np.minimum(np.maximum(T - S, 0), C)
+        E = np.maximum(0, Lp + S - C)
+        L = Lp + S - E
+        stage = 2 * row * (Lp + S)
+        commit = 2 * row * np.where(E > 0, L, S)
+        step_bytes = int((stage + commit).sum()) * c.kv_heads * 2
+        n_sets = int(np.ceil(512e6 / step_bytes)) + 1
+        for k in range(n_sets):
+            c.buffer_id = 10 + k
+            kc, vc, kn, vn, ks, vs = wl.window_payloads(c, device=dev, staging=True)
+            sk = torch.from_numpy(c.seqlens_k).to(dev)
+            lens = swrt.kv_seq_lengths(sk, S, C)
+            calls.append([swrt.prepare_kv_seq_lengths(sk, S, C, out=lens),
+                          swrt.prepare_kv_window_append_layers(
+                              [kc], [vc], [kn], [vn], lens.cache_past, lens.evict,
+                              k_stagings=[ks], v_stagings=[vs], phase="all")])
+        desc = c.name + " (lengths, stage, commit: three launches)"
+    torch.cuda.synchronize()
+
+    def step(i):
+        for call in calls[i]:
+            call()
+
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        eager, device, graph = _timers(stream, K, W)
+        t0 = time.perf_counter()
+        for i in range(W):
+            step(i % len(calls))
+        torch.cuda.synchronize()
+        host_s = (time.perf_counter() - t0) / max(W, 1)
+        eager_s = eager(step, len(calls))
+        device_s = device(step, len(calls), host_s)
+        graph_s = graph(step, len(calls))
+    out = {
+        "metric": "KV-cache update effective HBM GB/s (% of peak) and us per decode step",
+        "value": round(step_bytes / eager_s / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": K, "warmup": W, "ms_per_step": round(eager_s * 1e3, 5),
+        "us_per_step": round(eager_s * 1e6, 2), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": str(c0.dtype if n in (1, 2) else c.dtype).replace("torch.", ""),
+        "data": "synthetic",
+        "config": {"workload": f"workload {n}: {desc}", "bytes_per_step": step_bytes,
+                   "cache_defeat": f"{len(calls)} independent buffer sets round robin"},
+        "device_us_per_step": round(device_s * 1e6, 3),
+        "device_gbs": round(step_bytes / device_s / 1e9, 1),
+        "device_pct_of_hbm_peak": round(100 * step_bytes / device_s / 1e9 / HBM_PEAK_GBS, 2),
+        "graph_us_per_step": round(graph_s * 1e6, 2),
+    }
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -125,6 +271,9 @@ def main():
                     help="one launch per step (default) or the three-call composition")
     ap.add_argument("--timing", default="eager", choices=["eager", "graph"],
                     help="the timed loop `value` reports (both are measured)")
+    ap.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5],
+                    help="5: the whole-model decode step (default); 1-4: the other workloads, "
+                         "one line each, for the design notes")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path has no cross-GPU step (every (b, h) "
@@ -141,6 +290,8 @@ def main():
     swrt.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.workload != 5:
+        return other_workload(args, dev)
     spec = wl.workload5(wl.DTYPES[args.dtype])
     log(f"allocating {args.sets} buffer sets ...")
     steps = [ModelDecodeStep(spec, dev, set_id=i) for i in range(args.sets)]

@@ -39,7 +39,7 @@ struct DecodeArgs {
 
 constexpr uint32_t kFullTile = kWinBlock * kScatUnroll;  // full-cache words per workgroup
 
-template <int VEC>
+template <int VEC, int SPW>
 __global__ __launch_bounds__(kWinBlock) void decode_step_kernel(DecodeArgs a) {
   __shared__ TileBatches<kFullTile> tb;
   const uint32_t bid = blockIdx.x;
@@ -61,13 +61,36 @@ __global__ __launch_bounds__(kWinBlock) void decode_step_kernel(DecodeArgs a) {
                                           tb);
     return;
   }
-  const uint32_t slice = bid - a.full_blocks;
-  if (slice >= a.win_blocks) return;  // a grid sized by the length arrays alone
-  const Slice s = decode_slice(a.wg, slice);
-  const StepLengths r = step_lengths(a.seqlens_k[s.b], 1, a.wg.C);
-  char *base = a.wc[s.layer][s.t] + uint64_t(s.b * a.wg.H + s.h) * uint64_t(a.wg.C) * a.wg.row_bytes;
-  shift_append_slice<VEC>(base, a.wn[s.layer][s.t] + s.b * a.wg.nb_b + s.h * a.wg.nb_h, r.Lp,
-                          r.E, a.wg.row_bytes, a.wg.row_words);
+  const uint32_t wb = bid - a.full_blocks;
+  if (wb >= a.win_blocks) return;  // a grid sized by the length arrays alone
+  // the window workgroup's slice(s); (Lp, E) from seqlens_k, always a valid pair
+  const auto work = [&](uint32_t slice, int) {
+    const Slice s = decode_slice(a.wg, slice);
+    const StepLengths r = step_lengths(a.seqlens_k[s.b], 1, a.wg.C);
+    SliceWork w;
+    w.Lp = r.Lp;
+    w.E = r.E;
+    w.ok = true;
+    w.base = a.wc[s.layer][s.t] + uint64_t(s.b * a.wg.H + s.h) * uint64_t(a.wg.C) * a.wg.row_bytes;
+    w.new_row = a.wn[s.layer][s.t] + s.b * a.wg.nb_b + s.h * a.wg.nb_h;
+    return w;
+  };
+  if constexpr (SPW == 1) {
+    const SliceWork w = work(wb, 0);
+    shift_append_slice<VEC>(w.base, w.new_row, w.Lp, w.E, a.wg.row_bytes, a.wg.row_words);
+  } else {
+    shift_append_group<VEC, SPW>(wb * SPW, a.wg.slices, a.wg.row_bytes, a.wg.row_words, work);
+  }
+}
+
+template <int VEC>
+void launch_decode(const DecodeArgs &a, int spw, uint64_t grid, hipStream_t s) {
+  if (spw == 4)
+    hipLaunchKernelGGL((decode_step_kernel<VEC, 4>), dim3(grid), dim3(kWinBlock), 0, s, a);
+  else if (spw == 2)
+    hipLaunchKernelGGL((decode_step_kernel<VEC, 2>), dim3(grid), dim3(kWinBlock), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_step_kernel<VEC, 1>), dim3(grid), dim3(kWinBlock), 0, s, a);
 }
 
 }  // namespace
@@ -152,17 +175,18 @@ extern "C" int swrt_kv_decode_step(int n_window_layers, void *const *win_k_cache
   a.full_tiles = sp.empty ? 1 : sp.tiles;
   a.full_blocks = sp.empty ? 0 : sp.tiles * uint32_t(sp.n);
   a.len_blocks = do_len ? uint32_t((B + kWinBlock - 1) / kWinBlock) : 0;
-  a.win_blocks = wp.empty ? 0 : wp.slices;
+  const int spw = wp.empty ? 1 : slices_per_group(capacity, wp.g.row_words);
+  a.win_blocks = wp.empty ? 0 : (wp.slices + spw - 1) / spw;
   uint64_t grid = uint64_t(a.full_blocks) + a.win_blocks;
   if (grid < a.len_blocks) grid = a.len_blocks;  // length arrays alone
   if (grid >= (uint64_t(1) << 31)) return SWRT_E_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (vec) {
-    case 16: hipLaunchKernelGGL(decode_step_kernel<16>, dim3(grid), dim3(kWinBlock), 0, s, a); break;
-    case 8: hipLaunchKernelGGL(decode_step_kernel<8>, dim3(grid), dim3(kWinBlock), 0, s, a); break;
-    case 4: hipLaunchKernelGGL(decode_step_kernel<4>, dim3(grid), dim3(kWinBlock), 0, s, a); break;
-    case 2: hipLaunchKernelGGL(decode_step_kernel<2>, dim3(grid), dim3(kWinBlock), 0, s, a); break;
-    default: hipLaunchKernelGGL(decode_step_kernel<1>, dim3(grid), dim3(kWinBlock), 0, s, a); break;
+    case 16: launch_decode<16>(a, spw, grid, s); break;
+    case 8: launch_decode<8>(a, spw, grid, s); break;
+    case 4: launch_decode<4>(a, spw, grid, s); break;
+    case 2: launch_decode<2>(a, spw, grid, s); break;
+    default: launch_decode<1>(a, spw, grid, s); break;
   }
   return launch_status();
 }

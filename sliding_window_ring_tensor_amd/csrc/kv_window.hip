@@ -22,14 +22,30 @@ struct WinArgs {
   WindowGeom g;
 };
 
-template <int VEC, int NL>
+template <int VEC, int NL, int SPW>
 __global__ __launch_bounds__(kWinBlock) void window_in_place(WinArgs<NL> a) {
-  const Slice s = decode_slice(a.g, blockIdx.x);
-  const int64_t Lp = a.g.lp[s.b], E = a.g.ev[s.b];
-  if (!lengths_ok(a.g, s, 0, Lp, E)) return;
-  char *base = a.cache[s.layer][s.t] + uint64_t(s.b * a.g.H + s.h) * uint64_t(a.g.C) * a.g.row_bytes;
-  shift_append_slice<VEC>(base, a.nw[s.layer][s.t] + s.b * a.g.nb_b + s.h * a.g.nb_h, Lp, E,
-                          a.g.row_bytes, a.g.row_words);
+  if constexpr (SPW == 1) {
+    const Slice s = decode_slice(a.g, blockIdx.x);
+    const int64_t Lp = a.g.lp[s.b], E = a.g.ev[s.b];
+    if (!lengths_ok(a.g, s, threadIdx.x == 0, Lp, E)) return;
+    char *base = a.cache[s.layer][s.t] + uint64_t(s.b * a.g.H + s.h) * uint64_t(a.g.C) * a.g.row_bytes;
+    shift_append_slice<VEC>(base, a.nw[s.layer][s.t] + s.b * a.g.nb_b + s.h * a.g.nb_h, Lp, E,
+                            a.g.row_bytes, a.g.row_words);
+  } else {
+    constexpr uint32_t GB = kWinBlock / SPW;
+    shift_append_group<VEC, SPW>(blockIdx.x * SPW, a.g.slices, a.g.row_bytes, a.g.row_words,
+                                 [&](uint32_t slice, int g) {
+                                   const Slice s = decode_slice(a.g, slice);
+                                   SliceWork w;
+                                   w.Lp = a.g.lp[s.b];
+                                   w.E = a.g.ev[s.b];
+                                   w.ok = lengths_ok(a.g, s, threadIdx.x == g * GB, w.Lp, w.E);
+                                   w.base = a.cache[s.layer][s.t] +
+                                            uint64_t(s.b * a.g.H + s.h) * uint64_t(a.g.C) * a.g.row_bytes;
+                                   w.new_row = a.nw[s.layer][s.t] + s.b * a.g.nb_b + s.h * a.g.nb_h;
+                                   return w;
+                                 });
+  }
 }
 
 template <int VEC, int NL>
@@ -37,7 +53,7 @@ __global__ __launch_bounds__(kWinBlock) void window_stage(WinArgs<NL> a) {
   const uint32_t slice = blockIdx.x / a.g.tiles, tile = blockIdx.x - slice * a.g.tiles;
   const Slice s = decode_slice(a.g, slice);
   const int64_t Lp = a.g.lp[s.b], E = a.g.ev[s.b];
-  if (!lengths_ok(a.g, s, tile, Lp, E)) return;
+  if (!lengths_ok(a.g, s, tile == 0 && threadIdx.x == 0, Lp, E)) return;
   const uint64_t bh = s.b * a.g.H + s.h;
   stage_tile<VEC>(a.g, a.cache[s.layer][s.t] + bh * uint64_t(a.g.C) * a.g.row_bytes,
                   a.stage[s.layer][s.t] + bh * uint64_t(a.g.C + a.g.S) * a.g.row_bytes,
@@ -49,7 +65,7 @@ __global__ __launch_bounds__(kWinBlock) void window_commit(WinArgs<NL> a) {
   const uint32_t slice = blockIdx.x / a.g.tiles, tile = blockIdx.x - slice * a.g.tiles;
   const Slice s = decode_slice(a.g, slice);
   const int64_t Lp = a.g.lp[s.b], E = a.g.ev[s.b];
-  if (!lengths_ok(a.g, s, tile, Lp, E)) return;
+  if (!lengths_ok(a.g, s, tile == 0 && threadIdx.x == 0, Lp, E)) return;
   const uint64_t bh = s.b * a.g.H + s.h;
   commit_tile<VEC>(a.g, a.cache[s.layer][s.t] + bh * uint64_t(a.g.C) * a.g.row_bytes,
                    a.stage[s.layer][s.t] + bh * uint64_t(a.g.C + a.g.S) * a.g.row_bytes, Lp, E,
@@ -67,7 +83,14 @@ int launch(const WindowPlan &p, unsigned phase, hipStream_t stream) {
     }
   a.g = p.g;
   if (p.g.S == 1) {
-    hipLaunchKernelGGL((window_in_place<VEC, NL>), dim3(p.slices), dim3(kWinBlock), 0, stream, a);
+    const int spw = slices_per_group(p.g.C, p.g.row_words);
+    const dim3 grid((p.slices + spw - 1) / spw);
+    if (spw == 4)
+      hipLaunchKernelGGL((window_in_place<VEC, NL, 4>), grid, dim3(kWinBlock), 0, stream, a);
+    else if (spw == 2)
+      hipLaunchKernelGGL((window_in_place<VEC, NL, 2>), grid, dim3(kWinBlock), 0, stream, a);
+    else
+      hipLaunchKernelGGL((window_in_place<VEC, NL, 1>), grid, dim3(kWinBlock), 0, stream, a);
     return launch_status();
   }
   if (phase & SWRT_PHASE_STAGE) {
@@ -188,6 +211,7 @@ int plan_window(int n_layers, void *const *k_caches, void *const *v_caches,
   }
   p->align = acc;
   p->slices = uint32_t(slices);
+  p->g.slices = uint32_t(slices);
   p->g.lp = lengths_in_kernel ? nullptr : cache_past_lens;
   p->g.ev = lengths_in_kernel ? nullptr : evict_counts;
   p->g.flags = d_flags;

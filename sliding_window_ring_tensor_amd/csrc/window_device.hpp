@@ -61,6 +61,7 @@ struct WindowGeom {
   int64_t nb_b, nb_h, nb_s;  // new-row strides, bytes
   uint64_t row_bytes;
   uint32_t H, BH, tiles, row_words;
+  uint32_t slices;           // (layer, tensor, b, h) slices of the launch
   int32_t C, S;
   FastDiv by_row;            // words of the new part -> row (staging)
 };
@@ -82,13 +83,14 @@ __device__ __forceinline__ Slice decode_slice(const WindowGeom &g, uint32_t slic
 }
 
 // (Lp, E) must be the pair the lengths give for (C, S): 0 <= Lp <= C and
-// E = max(0, Lp + S - C). Otherwise flag once per batch entry and skip it.
-__device__ __forceinline__ bool lengths_ok(const WindowGeom &g, const Slice &s, uint32_t tile,
+// E = max(0, Lp + S - C). Otherwise flag once per batch entry (by the leader
+// lane of the (layer 0, K, h 0) slice's first tile) and skip it.
+__device__ __forceinline__ bool lengths_ok(const WindowGeom &g, const Slice &s, bool leader,
                                            int64_t Lp, int64_t E) {
   int64_t e = Lp + g.S - g.C;
   if (e < 0) e = 0;
   if (Lp >= 0 && Lp <= g.C && E == e) return true;
-  if (g.flags && s.layer == 0 && s.t == 0 && s.h == 0 && tile == 0 && threadIdx.x == 0)
+  if (g.flags && s.layer == 0 && s.t == 0 && s.h == 0 && leader)
     atomicOr(g.flags, SWRT_FLAG_BAD_LENGTHS);
   return false;
 }
@@ -146,6 +148,75 @@ __device__ __forceinline__ void shift_append_slice(char *base, const char *new_r
       for (uint32_t i = threadIdx.x; i < row_words; i += kWinBlock) st(adst + i, ld(nsrc + i));
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// S = 1, in place, several small slices per workgroup. When a whole slice is
+// at most one tile of a subgroup (kWinBlock / SPW threads), the workgroup is
+// split into SPW subgroups of whole waves, one slice each, meeting at a single
+// shared barrier: loads of every subgroup, barrier, stores. The same ordering
+// argument as shift_append_slice holds inside each slice; slices never share
+// rows. `info(slice, g)` returns the work of subgroup g's slice (ok = false:
+// leave it alone); it is evaluated for every subgroup in uniform code, so its
+// table lookups stay scalar, and each lane then takes its own subgroup's.
+// ---------------------------------------------------------------------------
+struct SliceWork {
+  char *base;           // row 0 of the slice
+  const char *new_row;  // the appended row
+  int64_t Lp, E;
+  bool ok;
+};
+
+template <int VEC, int SPW, typename Info>
+__device__ __forceinline__ void shift_append_group(uint32_t first_slice, uint32_t n_slices,
+                                                   uint64_t row_bytes, uint32_t row_words,
+                                                   Info info) {
+  using W = typename Word<VEC>::T;
+  constexpr uint32_t GB = kWinBlock / SPW;  // threads per subgroup (a multiple of 64)
+  static_assert(GB % 64 == 0, "subgroups must be whole waves");
+  const uint32_t lid = threadIdx.x % GB, grp = threadIdx.x / GB;
+  SliceWork w;
+  w.ok = false;
+#pragma unroll
+  for (int g = 0; g < SPW; ++g) {
+    SliceWork x;
+    x.ok = false;
+    if (first_slice + g < n_slices) x = info(first_slice + g, g);
+    if (grp == uint32_t(g)) w = x;
+  }
+  // n, the words to shift, and w.ok are uniform inside a subgroup, so the two
+  // predicated blocks below never split a wave. A slice with nothing to shift
+  // (E = 0) points its shift words at the appended row: the same value to the
+  // same address. Loads and stores then each form one straight block, which
+  // keeps the wait counters exact (stores are never held behind other stores).
+  const uint32_t n = (w.ok && w.E) ? uint32_t(w.Lp - w.E) * row_words : 0;
+  const uint32_t ai = min(lid, row_words - 1);
+  const W *nsrc = reinterpret_cast<const W *>(w.new_row) + ai;
+  W *adst = reinterpret_cast<W *>(w.base + uint64_t(w.Lp - w.E) * row_bytes) + ai;
+  const W *src = reinterpret_cast<const W *>(w.base + uint64_t(w.E) * row_bytes);
+  W *dst = reinterpret_cast<W *>(w.base);
+  W v[kWinUnroll], nv;
+  if (w.ok) {
+    nv = ld(nsrc);
+#pragma unroll
+    for (int u = 0; u < kWinUnroll; ++u) v[u] = ld(n ? src + min(u * GB + lid, n - 1) : nsrc);
+  }
+  __syncthreads();  // every old value of every slice of the workgroup is in registers
+  if (w.ok) {
+#pragma unroll
+    for (int u = 0; u < kWinUnroll; ++u) st(n ? dst + min(u * GB + lid, n - 1) : adst, v[u]);
+    st(adst, nv);
+  }
+}
+
+// Slices per workgroup for an in-place launch: the most (1, 2 or 4) whose
+// subgroup tile still holds a whole shift and whose subgroup covers a row.
+inline int slices_per_group(int64_t capacity, uint32_t row_words) {
+  int spw = 1;
+  while (spw < 4 && uint64_t(capacity - 1) * row_words <= uint64_t(kWinTile / (2 * spw)) &&
+         row_words <= uint32_t(kWinBlock / (2 * spw)))
+    spw *= 2;
+  return spw;
 }
 
 // S > 1, STAGE: tile `tile` of staging[0 .. Lp+S): words of rows [0, Lp) from
