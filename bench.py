@@ -48,9 +48,9 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD's published peak
 # (FETCH_SIZE, WRITE_SIZE), each scaled by what the counter reads for a 1 GiB
 # copy; valid only for the kernel source they were taken on (its hash).
 MEASURED_TRAFFIC = {
-    ("bf16", "decode_step_kernel", "880137acf7bb05ad"): {"read": 196_773_137,
-                                                         "written": 196_848_891},
-    ("bf16", "window_in_place", "79910ea0398d8c78"): {"read": 195_179_285, "written": 195_994_201},
+    ("bf16", "decode_step_kernel", "b3c645c1db481e98"): {"read": 196_781_015,
+                                                         "written": 196_831_387},
+    ("bf16", "window_in_place", "4016938b0441144f"): {"read": 195_186_307, "written": 196_004_004},
 }
 _CSRC = "sliding_window_ring_tensor_amd/csrc/"
 KERNEL_SOURCES = {

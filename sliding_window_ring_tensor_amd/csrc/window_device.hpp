@@ -167,6 +167,11 @@ struct SliceWork {
   bool ok;
 };
 
+#ifndef SWRT_GROUP_UNROLL
+#define SWRT_GROUP_UNROLL 2
+#endif
+constexpr int kGroupUnroll = SWRT_GROUP_UNROLL;  // words per lane per slice in group mode
+
 template <int VEC, int SPW, typename Info>
 __device__ __forceinline__ void shift_append_group(uint32_t first_slice, uint32_t n_slices,
                                                    uint64_t row_bytes, uint32_t row_words,
@@ -195,16 +200,16 @@ __device__ __forceinline__ void shift_append_group(uint32_t first_slice, uint32_
   W *adst = reinterpret_cast<W *>(w.base + uint64_t(w.Lp - w.E) * row_bytes) + ai;
   const W *src = reinterpret_cast<const W *>(w.base + uint64_t(w.E) * row_bytes);
   W *dst = reinterpret_cast<W *>(w.base);
-  W v[kWinUnroll], nv;
+  W v[kGroupUnroll], nv;
   if (w.ok) {
     nv = ld(nsrc);
 #pragma unroll
-    for (int u = 0; u < kWinUnroll; ++u) v[u] = ld(n ? src + min(u * GB + lid, n - 1) : nsrc);
+    for (int u = 0; u < kGroupUnroll; ++u) v[u] = ld(n ? src + min(u * GB + lid, n - 1) : nsrc);
   }
   __syncthreads();  // every old value of every slice of the workgroup is in registers
   if (w.ok) {
 #pragma unroll
-    for (int u = 0; u < kWinUnroll; ++u) st(n ? dst + min(u * GB + lid, n - 1) : adst, v[u]);
+    for (int u = 0; u < kGroupUnroll; ++u) st(n ? dst + min(u * GB + lid, n - 1) : adst, v[u]);
     st(adst, nv);
   }
 }
@@ -213,7 +218,8 @@ __device__ __forceinline__ void shift_append_group(uint32_t first_slice, uint32_
 // subgroup tile still holds a whole shift and whose subgroup covers a row.
 inline int slices_per_group(int64_t capacity, uint32_t row_words) {
   int spw = 1;
-  while (spw < 4 && uint64_t(capacity - 1) * row_words <= uint64_t(kWinTile / (2 * spw)) &&
+  while (spw < 4 &&
+         uint64_t(capacity - 1) * row_words <= uint64_t(kWinBlock / (2 * spw)) * kGroupUnroll &&
          row_words <= uint32_t(kWinBlock / (2 * spw)))
     spw *= 2;
   return spw;
