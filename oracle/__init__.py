@@ -76,6 +76,8 @@ class Oracle:
         lib.orc_tensor_scatter.restype = ctypes.c_int
         lib.orc_kv_seq_lengths.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp, u32p]
         lib.orc_kv_seq_lengths.restype = ctypes.c_int
+        lib.orc_kv_seq_lengths_drift.argtypes = [vp, i64, i64, i64, i64, vp, vp, vp, vp, vp, u32p]
+        lib.orc_kv_seq_lengths_drift.restype = ctypes.c_int
         lib.orc_kv_window_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                              i64, i64, i64, i64, i64, i32, ctypes.c_uint, u32p]
         lib.orc_kv_window_append.restype = ctypes.c_int
@@ -128,6 +130,23 @@ class Oracle:
                                          _ptr(Lp), _ptr(L), _ptr(E), ctypes.byref(flags))
         if st != OK:
             raise OracleError(f"orc_kv_seq_lengths status {st}")
+        return Lengths(T, P, Lp, L, E, flags.value)
+
+    def kv_seq_lengths_drift(self, seqlens_k, seq_len: int, capacity: int,
+                             window: int) -> Lengths:
+        sk = np.ascontiguousarray(seqlens_k, dtype=np.int32)
+        B = sk.shape[0]
+        T = np.zeros(B, np.int64)
+        P = np.zeros(B, np.int64)
+        Lp = np.zeros(B, np.int32)
+        L = np.zeros(B, np.int32)
+        E = np.zeros(B, np.int32)
+        flags = ctypes.c_uint32(0)
+        st = self.lib.orc_kv_seq_lengths_drift(_ptr(sk), B, seq_len, capacity, window, _ptr(T),
+                                               _ptr(P), _ptr(Lp), _ptr(L), _ptr(E),
+                                               ctypes.byref(flags))
+        if st != OK:
+            raise OracleError(f"orc_kv_seq_lengths_drift status {st}")
         return Lengths(T, P, Lp, L, E, flags.value)
 
     def kv_seq_lengths_status(self, seqlens_k, seq_len, capacity) -> int:

@@ -22,6 +22,10 @@
  *     as are staging rows at and beyond Lp + S.
  *   - [GQA] an S = 1 step shifts first, then writes: when E = 1 the row the
  *     new token goes to is one of the shift's sources.
+ *   - the append accepts any (Lp, E) that describes a step fitting the cache
+ *     (0 <= Lp <= C, L = Lp + S - E with 1 <= L <= C, E >= 0): the base
+ *     lengths evict only what does not fit, the drifting layout of the CPU
+ *     follow-up evicts a whole gap of rows at once; both are such steps.
  */
 #include "swrt_oracle.h"
 
@@ -175,6 +179,63 @@ int orc_kv_seq_lengths(const int32_t *seqlens_k, int64_t batch, int64_t seq_len,
 }
 
 /* ------------------------------------------------------------------------ */
+/* [GQA-CPU] drifting layout: lengths of a windowed step                     */
+/* ------------------------------------------------------------------------ */
+
+/* The append point of the drifting layout for an absolute length x: with
+ * gap = C - W + 1 it is x while x <= C, afterwards x minus as many whole gaps
+ * as it takes to come back to at most C (so W <= end <= C). */
+static int64_t drift_end(int64_t x, int64_t C, int64_t gap)
+{
+    int64_t gaps;
+    if (x <= C)
+        return x;
+    gaps = (x - C + gap - 1) / gap; /* ceil((x - C) / gap), 64-bit */
+    return x - gap * gaps;
+}
+
+int orc_kv_seq_lengths_drift(const int32_t *seqlens_k, int64_t batch,
+                             int64_t seq_len, int64_t capacity, int64_t window,
+                             int64_t *total_lens, int64_t *past_lens,
+                             int32_t *cache_past_lens, int32_t *cache_total_lens,
+                             int32_t *evict_counts, uint32_t *flags)
+{
+    const int64_t S = seq_len, C = capacity, W = window;
+
+    if (batch < 0 || S < 1 || C < 1 || S > INT32_MAX || C > INT32_MAX)
+        return ORC_E_INVALID_ARG;
+    if (W < 1 || W > C)
+        return ORC_E_INVALID_ARG;
+    if (batch > 0 && (!seqlens_k || !cache_past_lens || !evict_counts))
+        return ORC_E_INVALID_ARG;
+
+    for (int64_t b = 0; b < batch; ++b) {
+        const int64_t gap = C - W + 1;
+        const int64_t T = (int64_t)seqlens_k[b] + 1;
+        int64_t P, Lp, L, E;
+
+        if (seqlens_k[b] < 0 || T < S)
+            set_flag(flags, ORC_FLAG_BAD_SEQLEN);
+        P = T - S;
+        if (P < 0)
+            P = 0;
+        Lp = drift_end(P, C, gap);     /* resident before the step */
+        L = drift_end(P + S, C, gap);  /* resident after the step */
+        E = Lp + S - L;                /* rows reclaimed by the step */
+
+        if (total_lens)
+            total_lens[b] = T;
+        if (past_lens)
+            past_lens[b] = P;
+        cache_past_lens[b] = (int32_t)Lp;
+        evict_counts[b] = (int32_t)E;
+        if (cache_total_lens)
+            cache_total_lens[b] = (int32_t)L;
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* [GQA] windowed step: shift + append (S = 1), stage / commit (S > 1)       */
 /* ------------------------------------------------------------------------ */
 
@@ -234,15 +295,14 @@ int orc_kv_window_append(void *k_cache, void *v_cache, const void *k_new,
     for (int64_t b = 0; b < B; ++b) {
         const int64_t Lp = cache_past_lens[b];
         const int64_t E = evict_counts[b];
-        int64_t E_expected = Lp + S - C, L;
+        const int64_t L = Lp + S - E;
 
-        if (E_expected < 0)
-            E_expected = 0;
-        if (Lp < 0 || Lp > C || E != E_expected) {
+        /* the step must fit: Lp resident rows, at least the rows that do not
+         * fit the capacity evicted, and at least one row left */
+        if (Lp < 0 || Lp > C || E < 0 || L > C || L < 1) {
             set_flag(flags, ORC_FLAG_BAD_LENGTHS);
             continue; /* this batch entry keeps every byte it had */
         }
-        L = Lp + S - E;
 
         for (int t = 0; t < 2; ++t) { /* K, then V */
             for (int64_t h = 0; h < H; ++h) {

@@ -17,6 +17,9 @@
  *         section "Design" (the invariant and the append formulas, and the two
  *         details that follow them), and the follow-up commit that widens the
  *         end-pointer arithmetic to 64 bits and clamps the past length at zero.
+ *   [GQA-CPU] the same pull request's CPU follow-up description, section "Key
+ *         design decisions": the drifting layout (gap, end pointer, one
+ *         compaction per gap decode steps).
  *
  * Every function is a plain definition: scalar loops, one memcpy per row, no
  * blocking, no vector code, no threads.
@@ -75,10 +78,26 @@ int orc_kv_seq_lengths(const int32_t *seqlens_k, int64_t batch, int64_t seq_len,
                        int32_t *evict_counts, uint32_t *flags);
 
 /*
+ * [GQA-CPU] lengths of one windowed step under the drifting layout of the
+ * CPU follow-up ("Key design decisions", "Drifting layout"): with gap =
+ * C - W + 1 the append point is end(x) = x while x <= C, else
+ * x - gap * ceil((x - C) / gap). T = seqlens_k + 1, P = max(0, T - S),
+ * Lp = end(P), L = end(T), E = Lp + S - L. W = C (gap 1) is the base method.
+ * 1 <= window <= capacity.
+ */
+int orc_kv_seq_lengths_drift(const int32_t *seqlens_k, int64_t batch,
+                             int64_t seq_len, int64_t capacity, int64_t window,
+                             int64_t *total_lens, int64_t *past_lens,
+                             int32_t *cache_past_lens, int32_t *cache_total_lens,
+                             int32_t *evict_counts, uint32_t *flags);
+
+/*
  * [GQA] one windowed cache step for K and V.
  * caches [B, H, C, D]; new rows addressed by new_strides (elements) for b, h, s
  * with D contiguous; staging [B, H, C+S, D] (needed iff S > 1).
  * S == 1: in place, shift then append. S > 1: STAGE and/or COMMIT.
+ * A batch entry whose (Lp, E) is not a step that fits (0 <= Lp <= C, E >= 0,
+ * 1 <= Lp + S - E <= C) is flagged and left untouched.
  */
 int orc_kv_window_append(void *k_cache, void *v_cache, const void *k_new,
                          const void *v_new, const int64_t *new_strides,

@@ -37,10 +37,16 @@ template <> struct Word<16> { using T = u32x4; };
 #ifndef SWRT_NONTEMPORAL
 #define SWRT_NONTEMPORAL 1
 #endif
+#ifndef SWRT_NT_LOADS
+#define SWRT_NT_LOADS SWRT_NONTEMPORAL
+#endif
+#ifndef SWRT_NT_STORES
+#define SWRT_NT_STORES SWRT_NONTEMPORAL
+#endif
 
 template <typename T>
 __device__ __forceinline__ T ld(const T *p) {
-#if SWRT_NONTEMPORAL
+#if SWRT_NT_LOADS
   return __builtin_nontemporal_load(p);
 #else
   return *p;
@@ -49,7 +55,7 @@ __device__ __forceinline__ T ld(const T *p) {
 
 template <typename T>
 __device__ __forceinline__ void st(T *p, T v) {
-#if SWRT_NONTEMPORAL
+#if SWRT_NT_STORES
   __builtin_nontemporal_store(v, p);
 #else
   *p = v;

@@ -33,11 +33,17 @@ MUTANTS = {
     "update_rows_reversed": ("(const char *)update + (o * S + s) * row_bytes",
                              "(const char *)update + (o * S + (S - 1 - s)) * row_bytes"),
     "linear_oob_not_flagged": ("set_flag(flags, ORC_FLAG_LINEAR_OOB);", "(void)0;"),
-    "total_without_plus_one": ("(int64_t)seqlens_k[b] + 1;", "(int64_t)seqlens_k[b];"),
-    "total_narrowed_to_32_bits": ("(int64_t)seqlens_k[b] + 1;",
-                                  "(int64_t)(int32_t)((uint32_t)seqlens_k[b] + 1u);"),
+    "total_without_plus_one": ("(int64_t)seqlens_k[b] + 1; /* absolute",
+                               "(int64_t)seqlens_k[b]; /* absolute"),
+    "total_narrowed_to_32_bits": ("(int64_t)seqlens_k[b] + 1; /* absolute",
+                                  "(int64_t)(int32_t)((uint32_t)seqlens_k[b] + 1u); /* absolute"),
+    "drift_total_without_plus_one": ("(int64_t)seqlens_k[b] + 1;\n        int64_t P, Lp, L, E;",
+                                     "(int64_t)seqlens_k[b];\n        int64_t P, Lp, L, E;"),
     "past_minus_one_not_S": ("P = T - S; /*", "P = T - 1; /*"),
-    "past_not_clamped": ("if (P < 0)\n            P = 0;", "if (P < -(1LL << 40))\n            P = 0;"),
+    "past_not_clamped": ("clamped at zero */\n        if (P < 0)\n            P = 0;",
+                         "clamped at zero */\n        if (P < -(1LL << 40))\n            P = 0;"),
+    "drift_past_not_clamped": ("P = T - S;\n        if (P < 0)\n            P = 0;",
+                               "P = T - S;\n        if (P < -(1LL << 40))\n            P = 0;"),
     "resident_off_by_one": ("Lp = P < C ? P : C;", "Lp = P < C ? P : C - 1;"),
     "evict_off_by_one": ("E = Lp + S - C;", "E = Lp + S - C - 1;"),
     "resident_after_drops_E": ("L = Lp + S - E;      /*", "L = Lp + S;      /*"),
@@ -53,7 +59,12 @@ MUTANTS = {
     "new_strides_transposed": ("b * nb_stride[0] + h * nb_stride[1]",
                                "b * nb_stride[1] + h * nb_stride[0]"),
     "staging_slice_stride_C": ("(b * H + h) * (C + S) * row_bytes", "(b * H + h) * C * row_bytes"),
-    "length_check_weakened": ("E != E_expected", "E < 0"),
+    "length_check_weakened": ("if (Lp < 0 || Lp > C || E < 0 || L > C || L < 1)",
+                              "if (Lp < 0 || Lp > C || E < 0)"),
+    "drift_gap_too_small": ("const int64_t gap = C - W + 1;", "const int64_t gap = C - W + 2;"),
+    "drift_floor_not_ceil": ("(x - C + gap - 1) / gap", "(x - C) / gap"),
+    "drift_end_off_by_one": ("L = drift_end(P + S, C, gap);", "L = drift_end(P + S, C, gap) - 1;"),
+    "drift_past_from_total": ("Lp = drift_end(P, C, gap);", "Lp = drift_end(P + S, C, gap);"),
 }
 
 # write before shift (the opposite of the order the step formulas list)

@@ -457,3 +457,106 @@ def test_oracle_source_has_no_gpu_dependency():
     src = open(oracle.SOURCE).read()
     for banned in ("hip", "swrt.h", "sliding_window_ring_tensor_amd"):
         assert banned not in src.lower().replace("thread", ""), banned
+
+
+# --------------------------------------------------------------------------
+# Drifting layout (CPU follow-up of the same pull request, "Key design
+# decisions: Drifting layout", and its Tests section)
+# --------------------------------------------------------------------------
+
+def test_drift_with_window_equal_capacity_is_the_base_method(orc):
+    """gap = C - W + 1 = 1 when W = C: compaction on every step, which is the
+    base method (the follow-up's A/B baseline pins gap = 1 this way)."""
+    g = np.random.default_rng(21)
+    for C in (1, 3, 16, 128):
+        for S in (1, 2, C, C + 5):
+            sk = np.concatenate([g.integers(-3, 4 * C + S, size=200),
+                                 [0, S - 1, C - 1, C, C + S, 2**31 - 1]]).astype(np.int32)
+            a = orc.kv_seq_lengths(sk, S, C)
+            b = orc.kv_seq_lengths_drift(sk, S, C, C)
+            for x, y in zip((a.total, a.past, a.cache_past, a.cache_total, a.evict),
+                            (b.total, b.past, b.cache_past, b.cache_total, b.evict)):
+                np.testing.assert_array_equal(x, y)
+            assert a.flags == b.flags
+
+
+def _drift_step(orc, k, v, T_before, S, C, W):
+    B, H, _, D = k.shape
+    T_after = T_before + S
+    L = orc.kv_seq_lengths_drift((T_after - 1).astype(np.int32), S, C, W)
+    assert L.flags == 0
+    kn, vn = replay.new_block(B, H, T_before, S, D)
+    ks = vs = None
+    if S > 1:
+        ks, vs = replay.fresh_cache(B, H, C + S, D, tensors=(2, 3))
+    assert orc.kv_window_append(k, v, kn, vn, L.cache_past, L.evict, ks, vs) == 0
+    return T_after, L
+
+
+def _check_drift_window(k, v, T, L, C, W):
+    """Rows [0, L) hold the last L tokens; the last min(T, W) tokens are
+    always among them; once T > C the page's bound W <= L <= C holds."""
+    B, H, _, D = k.shape
+    for b in range(B):
+        n = int(L.cache_total[b])
+        assert min(int(T[b]), W) <= n <= C
+        if T[b] > C:
+            assert W <= n <= C
+        toks = np.arange(T[b] - n, T[b])
+        for h in range(H):
+            np.testing.assert_array_equal(k[b, h, :n], replay.token_rows(0, b, h, toks, D))
+            np.testing.assert_array_equal(v[b, h, :n], replay.token_rows(1, b, h, toks, D))
+
+
+@pytest.mark.parametrize("C,W", [(16, 8), (17, 16), (12, 12), (9, 1), (136, 128)])
+def test_drift_replay_invariant(orc, C, W):
+    B, H, D = 3, 2, 4
+    for name, sched in replay.schedules(min(C, 16)).items():
+        sched = [s for s in sched if s >= 1]
+        k, v = replay.fresh_cache(B, H, C, D)
+        T = np.array([0, 0, 0])
+        for S in sched + [1] * (2 * C):
+            T, L = _drift_step(orc, k, v, T, S, C, W)
+            _check_drift_window(k, v, T, L, C, W)
+
+
+def test_drift_compacts_once_per_gap(orc):
+    """Decode steps only: rows are reclaimed a whole gap at a time, exactly
+    every gap steps, and never otherwise. The follow-up's small-slack test
+    (C = W + 8, 400 decode steps) reports about 44 compactions."""
+    W = 128
+    C = W + 8
+    gap = C - W + 1
+    B, H, D = 2, 1, 4
+    k, v = replay.fresh_cache(B, H, C, D)
+    T = np.array([0, 0])
+    T, L = _drift_step(orc, k, v, T, C, C, W)  # a prompt that fills the capacity
+    events = []
+    for step in range(400):
+        T, L = _drift_step(orc, k, v, T, 1, C, W)
+        assert set(L.evict.tolist()) <= {0, gap}
+        if L.evict[0] == gap:
+            events.append(step)
+        _check_drift_window(k, v, T, L, C, W)
+    assert np.all(np.diff(events) == gap)
+    assert len(events) in (44, 45)
+
+
+def test_drift_chunked_prefill_small_slack(orc):
+    """The follow-up's chunked-prefill test: 32-token chunks at C = W + 8,
+    through staging, then decode."""
+    W = 40
+    C = W + 8
+    B, H, D = 2, 2, 4
+    k, v = replay.fresh_cache(B, H, C, D)
+    T = np.array([0, 0])
+    for S in [32] * 6 + [1] * 30 + [32, 1, 1]:
+        T, L = _drift_step(orc, k, v, T, S, C, W)
+        _check_drift_window(k, v, T, L, C, W)
+
+
+def test_drift_rejects_bad_window(orc):
+    sk = np.zeros(2, np.int32)
+    for W in (0, -1, 9):
+        with pytest.raises(oracle.OracleError):
+            orc.kv_seq_lengths_drift(sk, 1, 8, W)
