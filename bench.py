@@ -258,6 +258,88 @@ def other_workload(args, dev):
     print(json.dumps(out))
 
 
+def drift_loop(args, dev):
+    """Workload 6: K consecutive decode steps of workload 5's model, T
+    advancing by one per step, windowed caches of capacity W + slack under the
+    drifting layout, against the same loop at capacity W (compaction every
+    step). Bytes come from the lengths the kernels returned."""
+    import sliding_window_ring_tensor_amd as swrt
+    from sliding_window_ring_tensor_amd import workloads as wl
+
+    spec = wl.workload5(wl.DTYPES[args.dtype])
+    K, W, n_sets = args.steps, args.warmup, 3
+    B, H, D, Wn, M = spec.batch, spec.kv_heads, spec.head_dim, spec.window, spec.max_seq
+    es = torch.empty((), dtype=spec.dtype).element_size()
+    row = D * es
+    nw, nf = len(spec.windowed_layers), len(spec.full_layers)
+    steps_per_set = (K + W) // n_sets + 2
+    res = {}
+    for label, cap in (("drift", Wn + args.slack), ("base", Wn)):
+        log(f"{label}: capacity {cap}, window {Wn}")
+        calls, outs = [], []
+        for i in range(n_sets):
+            seed = spec.seed * 100 + 50 + i
+            buf = lambda shape, bid: wl.payload(shape, spec.dtype, seed, bid, dev)  # noqa: E731
+            wk = [buf((B, H, cap, D), 10 * j) for j in range(nw)]
+            wv = [buf((B, H, cap, D), 10 * j + 1) for j in range(nw)]
+            wkn = [buf((B, H, 1, D), 10 * j + 2) for j in range(nw)]
+            wvn = [buf((B, H, 1, D), 10 * j + 3) for j in range(nw)]
+            fc = [buf((B, H, M, D), 1000 + j) for j in range(2 * nf)]
+            fn = [buf((B, H, 1, D), 2000 + j) for j in range(2 * nf)]
+            # set i's j-th step appends token T0 + j (T0 the drawn lengths, kept below M)
+            T0 = np.minimum(spec.total_lens, M - steps_per_set)
+            Ts = T0[None, :] + np.arange(steps_per_set)[:, None]
+            sk = torch.from_numpy((Ts - 1).astype(np.int32)).to(dev)
+            wi = torch.from_numpy((Ts - 1).astype(np.int64)).to(dev)
+            lens = [swrt.WindowLengths(*(torch.zeros(B, dtype=t, device=dev) for t in (
+                torch.int64, torch.int64, torch.int32, torch.int32, torch.int32)))
+                for _ in range(steps_per_set)]
+            calls.append([swrt.prepare_kv_decode_step(wk, wv, wkn, wvn, sk[j], fc, fn, wi[j],
+                                                      window=Wn, out=lens[j])
+                          for j in range(steps_per_set)])
+            outs.append(lens)
+        torch.cuda.synchronize()
+        order = [(k % n_sets, k // n_sets) for k in range(W + K)]
+        stream = torch.cuda.Stream()
+        with torch.cuda.stream(stream):
+            for s_, j in order[:W]:
+                calls[s_][j]()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for s_, j in order[W:]:
+                calls[s_][j]()
+            torch.cuda.synchronize()
+            wall = (time.perf_counter() - t0) / K
+        byts = 0
+        for s_, j in order[W:]:
+            L = outs[s_][j]
+            Lp = L.cache_past.cpu().numpy().astype(np.int64)
+            E = L.evict.cpu().numpy().astype(np.int64)
+            byts += int((2 * row * (np.where(E > 0, Lp - E, 0) + 1)).sum()) * H * 2 * nw
+            byts += 2 * row * B * H * 2 * nf
+        compactions = sum(int((outs[s_][j].evict > 0).sum().item()) for s_, j in order[W:])
+        res[label] = {"capacity": cap, "us_per_step": wall * 1e6, "bytes_per_step": byts / K,
+                      "compacting_entries_per_step": compactions / K}
+        del calls, outs
+        torch.cuda.empty_cache()
+    d, b = res["drift"], res["base"]
+    out = {
+        "metric": "KV-cache update effective HBM GB/s (% of peak) and us per decode step",
+        "value": round(d["bytes_per_step"] / d["us_per_step"] / 1e3, 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(d["us_per_step"] / 1e3, 5),
+        "us_per_step": round(d["us_per_step"], 2), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": args.dtype, "data": "synthetic",
+        "config": {"workload": f"workload 6: workload 5's decode loop, {K} consecutive steps, "
+                               f"windowed caches C = {d['capacity']} = W + {args.slack} under "
+                               f"the drifting layout (gap {d['capacity'] - Wn + 1})",
+                   "cache_defeat": f"{n_sets} independent buffer sets round robin"},
+        "drift": {k: round(v, 3) for k, v in d.items()},
+        "base_layout_same_loop": {k: round(v, 3) for k, v in b.items()},
+        "speedup_vs_base_layout": round(b["us_per_step"] / d["us_per_step"], 3),
+    }
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -271,9 +353,11 @@ def main():
                     help="one launch per step (default) or the three-call composition")
     ap.add_argument("--timing", default="eager", choices=["eager", "graph"],
                     help="the timed loop `value` reports (both are measured)")
-    ap.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5],
-                    help="5: the whole-model decode step (default); 1-4: the other workloads, "
-                         "one line each, for the design notes")
+    ap.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5, 6],
+                    help="5: the whole-model decode step (default); 1-4: the other workloads; "
+                         "6: workload 5's decode loop with drifting windowed caches "
+                         "(capacity W + --slack), one line each, for the design notes")
+    ap.add_argument("--slack", type=int, default=16, help="workload 6: capacity - window")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path has no cross-GPU step (every (b, h) "
@@ -290,6 +374,8 @@ def main():
     swrt.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.workload == 6:
+        return drift_loop(args, dev)
     if args.workload != 5:
         return other_workload(args, dev)
     spec = wl.workload5(wl.DTYPES[args.dtype])

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define SWRT_ABI_VERSION 1
+#define SWRT_ABI_VERSION 2
 
 /* synchronous status codes */
 #define SWRT_OK 0
@@ -67,7 +67,7 @@ extern "C" {
 /* asynchronous flags (OR-ed into *d_flags) */
 #define SWRT_FLAG_LINEAR_OOB 1u   /* linear write index < 0 or > M - S        */
 #define SWRT_FLAG_BAD_SEQLEN 2u   /* seqlens_k[b] < 0 or seqlens_k[b] + 1 < S */
-#define SWRT_FLAG_BAD_LENGTHS 4u  /* (Lp, E) not a valid pair for (C, S)      */
+#define SWRT_FLAG_BAD_LENGTHS 4u  /* (Lp, E) not a step that fits (C, S)      */
 
 /* TensorScatter mode attribute */
 #define SWRT_MODE_LINEAR 0
@@ -176,6 +176,26 @@ int swrt_kv_seq_lengths(const int32_t *seqlens_k, int batch, int seq_len,
                         int32_t *evict_counts, uint32_t *d_flags, void *stream);
 
 /*
+ * swrt_kv_seq_lengths_drift -- lengths of one windowed step under the
+ * drifting layout of the same pull request's CPU follow-up ("Key design
+ * decisions: Drifting layout"). Resident tokens live at rows [0, end) with
+ * gap = C - W + 1 and end(x) = x while x <= C, else
+ * x - gap * ceil((x - C) / gap), so W <= end <= C: a whole gap of rows is
+ * reclaimed at once, once every gap decode steps, and the other steps only
+ * append. With T and P as in swrt_kv_seq_lengths:
+ *   Lp = end(P), L = end(T), E = Lp + S - L.
+ * The window W (1 <= W <= C, else SWRT_E_INVALID_ARG) is the attention
+ * window the last W tokens of which stay resident; W = C gives exactly the
+ * values of swrt_kv_seq_lengths. Every other argument as there. The (Lp, E)
+ * pairs feed swrt_kv_window_append unchanged.
+ */
+int swrt_kv_seq_lengths_drift(const int32_t *seqlens_k, int batch, int seq_len,
+                              int capacity, int window, int64_t *total_lens,
+                              int64_t *past_lens, int32_t *cache_past_lens,
+                              int32_t *cache_total_lens, int32_t *evict_counts,
+                              uint32_t *d_flags, void *stream);
+
+/*
  * swrt_kv_window_append -- one windowed cache step for K and V (pull request
  * "GQA support sliding_window_cache", section "Design": the invariant that
  * the cache holds the L = min(T, C) most recent tokens at rows [0, L), the
@@ -184,7 +204,8 @@ int swrt_kv_seq_lengths(const int32_t *seqlens_k, int batch, int seq_len,
  * for S > 1).
  *
  * S = 1 (in place, phase ignored): for every (tensor, b, h)
- *     cache[0 .. Lp-E) <- old cache[E .. Lp)   (E is 0 or 1)
+ *     cache[0 .. Lp-E) <- old cache[E .. Lp)   (E is 0 or 1; a whole gap
+ *                                               under the drifting layout)
  *     cache[Lp-E]      <- new[b, h, 0]
  * S > 1:
  *   STAGE:  staging[0 .. Lp)    <- cache[0 .. Lp)
@@ -206,15 +227,16 @@ int swrt_kv_seq_lengths(const int32_t *seqlens_k, int batch, int seq_len,
  *                      required when S > 1, ignored (may be NULL) when S = 1.
  * cache_past_lens,
  * evict_counts         device int32[batch]: Lp and E from swrt_kv_seq_lengths
- *                      with the same S and C.
+ *                      (or swrt_kv_seq_lengths_drift) with the same S and C.
  * batch, kv_heads      >= 0 (0 is a no-op). head_dim >= 0.
  * capacity             C >= 1. seq_len S >= 1 (S > C is allowed when S > 1).
  * elem_bits            4, 8, 16, 32, 64 or 128 (4-bit: even head_dim and
  *                      even strides).
  * phase                SWRT_PHASE_STAGE, _COMMIT or _ALL when S > 1.
- * d_flags              device uint32 or NULL. SWRT_FLAG_BAD_LENGTHS when
- *                      Lp < 0, Lp > C or E != max(0, Lp + S - C): that batch
- *                      entry is left untouched (cache and staging).
+ * d_flags              device uint32 or NULL. SWRT_FLAG_BAD_LENGTHS when the
+ *                      pair is not a step that fits (Lp < 0, Lp > C, E < 0,
+ *                      or L = Lp + S - E outside [1, C]): that batch entry is
+ *                      left untouched (cache and staging).
  * Limits: batch * kv_heads * 2 slices and (capacity + seq_len) * head_dim *
  * elem_bits / 128 vectors per slice must each stay below 2^31.
  */
@@ -265,8 +287,10 @@ int swrt_kv_window_append_layers(int n_layers, void *const *k_caches,
  * section "Design") and full-length layers (ONNX operator page "TensorScatter",
  * linear mode), in one launch. It writes exactly the bytes of
  *
- *   swrt_kv_seq_lengths(seqlens_k, batch, 1, capacity, total_lens, past_lens,
- *                       cache_past_lens, cache_total_lens, evict_counts)
+ *   swrt_kv_seq_lengths_drift(seqlens_k, batch, 1, capacity, window,
+ *                       total_lens, past_lens, cache_past_lens,
+ *                       cache_total_lens, evict_counts)
+ *                       (window == capacity: exactly swrt_kv_seq_lengths)
  *   swrt_kv_window_append_layers(n_window_layers, win_*, win_new_strides,
  *                       Lp, E, batch, kv_heads, capacity, 1, head_dim, ...)
  *   swrt_tensor_scatter_batched(n_full, full_caches, full_caches, full_new,
@@ -281,6 +305,8 @@ int swrt_kv_window_append_layers(int n_layers, void *const *k_caches,
  * seqlens_k            device int32[batch]; required when there are windowed
  *                      layers or length outputs.
  * capacity             C >= 1 of the windowed caches.
+ * window               W, 1 <= W <= C: the drifting layout's window (see
+ *                      swrt_kv_seq_lengths_drift); W = C is the base layout.
  * total_lens .. evict_counts
  *                      optional device outputs as for swrt_kv_seq_lengths
  *                      (any may be NULL).
@@ -297,7 +323,7 @@ int swrt_kv_decode_step(int n_window_layers, void *const *win_k_caches,
                         void *const *win_v_caches, const void *const *win_k_new,
                         const void *const *win_v_new,
                         const int64_t *win_new_strides,
-                        const int32_t *seqlens_k, int capacity,
+                        const int32_t *seqlens_k, int capacity, int window,
                         int64_t *total_lens, int64_t *past_lens,
                         int32_t *cache_past_lens, int32_t *cache_total_lens,
                         int32_t *evict_counts, int n_full,

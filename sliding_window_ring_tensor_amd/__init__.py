@@ -51,6 +51,7 @@ MODE_LINEAR, MODE_CIRCULAR = 0, 1
 PHASE_STAGE, PHASE_COMMIT, PHASE_ALL = 1, 2, 3
 MAX_LAYERS = 32
 MAX_BATCHED = 64
+ABI_VERSION = 2
 
 _PHASES = {"stage": PHASE_STAGE, "commit": PHASE_COMMIT, "all": PHASE_ALL}
 _MODES = {"linear": MODE_LINEAR, "circular": MODE_CIRCULAR}
@@ -86,19 +87,21 @@ def lib() -> ctypes.CDLL:
     L.swrt_tensor_scatter_batched.argtypes = [i32, vpp, vpp, vpp, vp, vp, i32, i32, i64, i32,
                                               i32, vp, vp]
     L.swrt_kv_seq_lengths.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
+    L.swrt_kv_seq_lengths_drift.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
     L.swrt_kv_window_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                         i32, i32, u32, vp, vp]
     L.swrt_kv_window_append_layers.argtypes = [i32, vpp, vpp, vpp, vpp, vp, vpp, vpp, vp, vp,
                                                i32, i32, i32, i32, i32, i32, u32, vp, vp]
-    L.swrt_kv_decode_step.argtypes = [i32, vpp, vpp, vpp, vpp, vp, vp, i32, vp, vp, vp, vp, vp,
-                                      i32, vpp, vpp, vp, i32, i32, i32, i32, i32, vp, vp]
+    L.swrt_kv_decode_step.argtypes = [i32, vpp, vpp, vpp, vpp, vp, vp, i32, i32, vp, vp, vp, vp,
+                                      vp, i32, vpp, vpp, vp, i32, i32, i32, i32, i32, vp, vp]
     for name in ("swrt_tensor_scatter", "swrt_tensor_scatter_batched", "swrt_kv_seq_lengths",
+                 "swrt_kv_seq_lengths_drift",
                  "swrt_kv_window_append", "swrt_kv_window_append_layers", "swrt_kv_decode_step",
                  "swrt_abi_version"):
         getattr(L, name).restype = ctypes.c_int
     L.swrt_status_string.argtypes = [ctypes.c_int]
     L.swrt_status_string.restype = ctypes.c_char_p
-    if L.swrt_abi_version() != 1:
+    if L.swrt_abi_version() != ABI_VERSION:
         raise SwrtError("libswrt ABI version mismatch")
     _lib = L
     return L
@@ -260,23 +263,31 @@ def _check_seqlens(seqlens_k: torch.Tensor) -> None:
 
 
 def prepare_kv_seq_lengths(seqlens_k: torch.Tensor, seq_len: int, capacity: int, *,
-                           out: WindowLengths | None = None,
+                           window: int | None = None, out: WindowLengths | None = None,
                            flags: torch.Tensor | None = None) -> PreparedCall:
     dev = _device_of(seqlens_k, flags)
     _check_seqlens(seqlens_k)
     B = seqlens_k.shape[0]
     out = _new_lengths(B, dev) if out is None else out
-    args = (_ptr(seqlens_k), B, seq_len, capacity, _ptr(out.total), _ptr(out.past),
-            _ptr(out.cache_past), _ptr(out.cache_total), _ptr(out.evict), _ptr(flags))
-    return PreparedCall(lib().swrt_kv_seq_lengths, args, dev, "kv_seq_lengths",
-                        (seqlens_k, *out, flags), out)
+    tail = (_ptr(out.total), _ptr(out.past), _ptr(out.cache_past), _ptr(out.cache_total),
+            _ptr(out.evict), _ptr(flags))
+    if window is None:
+        fn, args, what = lib().swrt_kv_seq_lengths, (_ptr(seqlens_k), B, seq_len, capacity,
+                                                     *tail), "kv_seq_lengths"
+    else:
+        fn, args, what = lib().swrt_kv_seq_lengths_drift, (_ptr(seqlens_k), B, seq_len, capacity,
+                                                           window, *tail), "kv_seq_lengths_drift"
+    return PreparedCall(fn, args, dev, what, (seqlens_k, *out, flags), out)
 
 
 def kv_seq_lengths(seqlens_k: torch.Tensor, seq_len: int, capacity: int, *,
-                   out: WindowLengths | None = None,
+                   window: int | None = None, out: WindowLengths | None = None,
                    flags: torch.Tensor | None = None) -> WindowLengths:
-    """Lengths of one windowed step for every batch entry, computed on the device."""
-    return prepare_kv_seq_lengths(seqlens_k, seq_len, capacity, out=out, flags=flags)()
+    """Lengths of one windowed step for every batch entry, computed on the device.
+    With ``window`` (W <= capacity) the drifting layout's lengths: the append
+    point drifts and a whole gap of C - W + 1 rows is reclaimed at once."""
+    return prepare_kv_seq_lengths(seqlens_k, seq_len, capacity, window=window, out=out,
+                                  flags=flags)()
 
 
 # ---------------------------------------------------------------------------
@@ -391,7 +402,7 @@ def prepare_kv_decode_step(win_k: Sequence[torch.Tensor], win_v: Sequence[torch.
                            win_k_new: Sequence[torch.Tensor], win_v_new: Sequence[torch.Tensor],
                            seqlens_k: torch.Tensor, full_caches: Sequence[torch.Tensor],
                            full_new: Sequence[torch.Tensor], write_indices: torch.Tensor, *,
-                           out: WindowLengths | None = None,
+                           window: int | None = None, out: WindowLengths | None = None,
                            flags: torch.Tensor | None = None) -> PreparedCall:
     """See ``kv_decode_step``."""
     n, B, H, C, D, S, strides = _check_layers(win_k, win_v, win_k_new, win_v_new)
@@ -417,7 +428,8 @@ def prepare_kv_decode_step(win_k: Sequence[torch.Tensor], win_v: Sequence[torch.
                      *full_new, write_indices, flags)
     out = _new_lengths(B, dev) if out is None else out
     args = (n, _ptrs(win_k), _ptrs(win_v), _ptrs(win_k_new), _ptrs(win_v_new), strides,
-            _ptr(seqlens_k), C, _ptr(out.total), _ptr(out.past), _ptr(out.cache_past),
+            _ptr(seqlens_k), C, C if window is None else window, _ptr(out.total), _ptr(out.past),
+            _ptr(out.cache_past),
             _ptr(out.cache_total), _ptr(out.evict), nf, _ptrs(full_caches) if nf else None,
             _ptrs(full_new) if nf else None, _ptr(write_indices) if nf else None, M, B, H, D,
             _bits(win_k[0]), _ptr(flags))
@@ -427,12 +439,14 @@ def prepare_kv_decode_step(win_k: Sequence[torch.Tensor], win_v: Sequence[torch.
 
 
 def kv_decode_step(win_k, win_v, win_k_new, win_v_new, seqlens_k, full_caches, full_new,
-                   write_indices, *, out: WindowLengths | None = None,
+                   write_indices, *, window: int | None = None, out: WindowLengths | None = None,
                    flags: torch.Tensor | None = None) -> WindowLengths:
     """Every KV-cache update of one decode step in one launch: the lengths of
     the windowed layers from ``seqlens_k`` (returned), the in-place shift and
     append of every windowed layer's K and V, and the linear TensorScatter of
     one new row at ``write_indices`` into every full cache. Same bytes as
-    kv_seq_lengths + kv_window_append_layers + tensor_scatter_batched."""
+    kv_seq_lengths + kv_window_append_layers + tensor_scatter_batched; with
+    ``window`` the windowed layers use the drifting layout."""
     return prepare_kv_decode_step(win_k, win_v, win_k_new, win_v_new, seqlens_k, full_caches,
-                                  full_new, write_indices, out=out, flags=flags)()
+                                  full_new, write_indices, window=window, out=out,
+                                  flags=flags)()

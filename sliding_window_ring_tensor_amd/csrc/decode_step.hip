@@ -15,7 +15,8 @@
 // Workgroup roles (uniform per workgroup): the first workgroups carry the
 // full-cache row writes, the rest one windowed slice each; every window
 // workgroup derives its own (Lp, E) from seqlens_k with the same arithmetic
-// as kv_seq_lengths, and the first ceil(B / 512) workgroups also write the
+// as kv_seq_lengths (or kv_seq_lengths_drift when window < capacity), and the
+// first workgroups (one batch entry per lane) also write the
 // length arrays for the attention that follows. Two kernel boundaries per
 // step disappear, and with them their dispatch and cache-maintenance cost.
 #include "swrt_host.hpp"
@@ -35,18 +36,21 @@ struct DecodeArgs {
   int32_t *cache_past, *cache_total, *evict;
   uint32_t full_tiles, full_blocks, win_blocks, len_blocks;
   int32_t batch;
+  FastDiv gap;  // capacity - window + 1
 };
 
-constexpr uint32_t kFullTile = kWinBlock * kScatUnroll;  // full-cache words per workgroup
-
-template <int VEC, int SPW>
-__global__ __launch_bounds__(kWinBlock) void decode_step_kernel(DecodeArgs a) {
+// BLOCK x UNROLL: the window shape (512 x 2 for the base layout; one wave,
+// 64 x 16, for the drifting layout, whose steps are mostly single-row appends).
+// DRIFT: window < capacity (the lengths take the gap).
+template <int VEC, int SPW, int BLOCK, int UNROLL, bool DRIFT>
+__global__ __launch_bounds__(BLOCK) void decode_step_kernel(DecodeArgs a) {
+  constexpr uint32_t kFullTile = BLOCK * kScatUnroll;  // full-cache words per workgroup
   __shared__ TileBatches<kFullTile> tb;
   const uint32_t bid = blockIdx.x;
   if (bid < a.len_blocks) {  // the length arrays (no barrier in this part)
-    const int32_t b = int32_t(bid * kWinBlock + threadIdx.x);
+    const int32_t b = int32_t(bid * BLOCK + threadIdx.x);
     if (b < a.batch) {
-      const StepLengths r = step_lengths(a.seqlens_k[b], 1, a.wg.C);
+      const StepLengths r = step_lengths<DRIFT>(a.seqlens_k[b], 1, a.wg.C, a.gap);
       if (r.bad && a.wg.flags) atomicOr(a.wg.flags, SWRT_FLAG_BAD_SEQLEN);
       if (a.total) a.total[b] = r.T;
       if (a.past) a.past[b] = r.P;
@@ -57,8 +61,8 @@ __global__ __launch_bounds__(kWinBlock) void decode_step_kernel(DecodeArgs a) {
   }
   if (bid < a.full_blocks) {  // full caches: TensorScatter rows in place
     const uint32_t t = bid / a.full_tiles;
-    scatter_in_place_tile<VEC, kWinBlock>(a.sg, a.fc[t], a.fu[t], (bid - t * a.full_tiles) * kFullTile,
-                                          tb);
+    scatter_in_place_tile<VEC, BLOCK>(a.sg, a.fc[t], a.fu[t], (bid - t * a.full_tiles) * kFullTile,
+                                      tb);
     return;
   }
   const uint32_t wb = bid - a.full_blocks;
@@ -66,7 +70,7 @@ __global__ __launch_bounds__(kWinBlock) void decode_step_kernel(DecodeArgs a) {
   // the window workgroup's slice(s); (Lp, E) from seqlens_k, always a valid pair
   const auto work = [&](uint32_t slice, int) {
     const Slice s = decode_slice(a.wg, slice);
-    const StepLengths r = step_lengths(a.seqlens_k[s.b], 1, a.wg.C);
+    const StepLengths r = step_lengths<DRIFT>(a.seqlens_k[s.b], 1, a.wg.C, a.gap);
     SliceWork w;
     w.Lp = r.Lp;
     w.E = r.E;
@@ -77,20 +81,27 @@ __global__ __launch_bounds__(kWinBlock) void decode_step_kernel(DecodeArgs a) {
   };
   if constexpr (SPW == 1) {
     const SliceWork w = work(wb, 0);
-    shift_append_slice<VEC>(w.base, w.new_row, w.Lp, w.E, a.wg.row_bytes, a.wg.row_words);
+    shift_append_slice<VEC, BLOCK, UNROLL>(w.base, w.new_row, w.Lp, w.E, a.wg.row_bytes,
+                                           a.wg.row_words);
   } else {
     shift_append_group<VEC, SPW>(wb * SPW, a.wg.slices, a.wg.row_bytes, a.wg.row_words, work);
   }
 }
 
 template <int VEC>
-void launch_decode(const DecodeArgs &a, int spw, uint64_t grid, hipStream_t s) {
-  if (spw == 4)
-    hipLaunchKernelGGL((decode_step_kernel<VEC, 4>), dim3(grid), dim3(kWinBlock), 0, s, a);
+void launch_decode(const DecodeArgs &a, bool drift, int spw, uint64_t grid, hipStream_t s) {
+  if (drift)
+    hipLaunchKernelGGL((decode_step_kernel<VEC, 1, kWaveBlock, kWaveUnroll, true>), dim3(grid),
+                       dim3(kWaveBlock), 0, s, a);
+  else if (spw == 4)
+    hipLaunchKernelGGL((decode_step_kernel<VEC, 4, kWinBlock, kWinUnroll, false>), dim3(grid),
+                       dim3(kWinBlock), 0, s, a);
   else if (spw == 2)
-    hipLaunchKernelGGL((decode_step_kernel<VEC, 2>), dim3(grid), dim3(kWinBlock), 0, s, a);
+    hipLaunchKernelGGL((decode_step_kernel<VEC, 2, kWinBlock, kWinUnroll, false>), dim3(grid),
+                       dim3(kWinBlock), 0, s, a);
   else
-    hipLaunchKernelGGL((decode_step_kernel<VEC, 1>), dim3(grid), dim3(kWinBlock), 0, s, a);
+    hipLaunchKernelGGL((decode_step_kernel<VEC, 1, kWinBlock, kWinUnroll, false>), dim3(grid),
+                       dim3(kWinBlock), 0, s, a);
 }
 
 }  // namespace
@@ -101,7 +112,8 @@ using namespace swrt;
 extern "C" int swrt_kv_decode_step(int n_window_layers, void *const *win_k_caches,
                                    void *const *win_v_caches, const void *const *win_k_new,
                                    const void *const *win_v_new, const int64_t *win_new_strides,
-                                   const int32_t *seqlens_k, int capacity, int64_t *total_lens,
+                                   const int32_t *seqlens_k, int capacity, int window,
+                                   int64_t *total_lens,
                                    int64_t *past_lens, int32_t *cache_past_lens,
                                    int32_t *cache_total_lens, int32_t *evict_counts, int n_full,
                                    void *const *full_caches, const void *const *full_new,
@@ -109,6 +121,7 @@ extern "C" int swrt_kv_decode_step(int n_window_layers, void *const *win_k_cache
                                    int kv_heads, int head_dim, int elem_bits, uint32_t *d_flags,
                                    void *stream) {
   if (batch < 0 || capacity < 1 || n_window_layers < 0 || n_full < 0) return SWRT_E_INVALID_ARG;
+  if (window < 1 || window > capacity) return SWRT_E_INVALID_ARG;
   WindowPlan wp{};
   ScatterPlan sp{};
   Range ranges[6 * kMaxLayers + 3 * kMaxTensors + 12];
@@ -148,7 +161,11 @@ extern "C" int swrt_kv_decode_step(int n_window_layers, void *const *win_k_cache
   const int vec = word_of((wp.empty ? 0 : wp.align) | (sp.empty ? 0 : sp.align) |
                           uint64_t(wp.empty && sp.empty ? 16 : 0));
   if (!wp.empty && (st = finish_window(&wp, vec)) != SWRT_OK) return st;
-  if (!sp.empty && (st = finish_scatter(&sp, vec, kFullTile)) != SWRT_OK) return st;
+  // the drifting layout runs the one-wave shape (see decode_step_kernel)
+  const bool drift = window < capacity;
+  const int block = drift ? kWaveBlock : kWinBlock;
+  if (!sp.empty && (st = finish_scatter(&sp, vec, uint32_t(block * kScatUnroll))) != SWRT_OK)
+    return st;
 
   static_assert(sizeof(DecodeArgs) <= 4096, "kernel arguments exceed 4 KiB");
   DecodeArgs a;
@@ -172,21 +189,22 @@ extern "C" int swrt_kv_decode_step(int n_window_layers, void *const *win_k_cache
   a.cache_total = cache_total_lens;
   a.evict = evict_counts;
   a.batch = batch;
+  a.gap = FastDiv(uint32_t(capacity - window + 1));
   a.full_tiles = sp.empty ? 1 : sp.tiles;
   a.full_blocks = sp.empty ? 0 : sp.tiles * uint32_t(sp.n);
-  a.len_blocks = do_len ? uint32_t((B + kWinBlock - 1) / kWinBlock) : 0;
-  const int spw = wp.empty ? 1 : slices_per_group(capacity, wp.g.row_words);
+  a.len_blocks = do_len ? uint32_t((B + block - 1) / block) : 0;
+  const int spw = wp.empty || drift ? 1 : slices_per_group(capacity, wp.g.row_words);
   a.win_blocks = wp.empty ? 0 : (wp.slices + spw - 1) / spw;
   uint64_t grid = uint64_t(a.full_blocks) + a.win_blocks;
   if (grid < a.len_blocks) grid = a.len_blocks;  // length arrays alone
   if (grid >= (uint64_t(1) << 31)) return SWRT_E_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (vec) {
-    case 16: launch_decode<16>(a, spw, grid, s); break;
-    case 8: launch_decode<8>(a, spw, grid, s); break;
-    case 4: launch_decode<4>(a, spw, grid, s); break;
-    case 2: launch_decode<2>(a, spw, grid, s); break;
-    default: launch_decode<1>(a, spw, grid, s); break;
+    case 16: launch_decode<16>(a, drift, spw, grid, s); break;
+    case 8: launch_decode<8>(a, drift, spw, grid, s); break;
+    case 4: launch_decode<4>(a, drift, spw, grid, s); break;
+    case 2: launch_decode<2>(a, drift, spw, grid, s); break;
+    default: launch_decode<1>(a, drift, spw, grid, s); break;
   }
   return launch_status();
 }

@@ -12,6 +12,8 @@
 // One lane per batch entry; the values are independent per entry.
 #include "window_device.hpp"
 
+#include "swrt_host.hpp"
+
 namespace swrt {
 namespace {
 
@@ -21,12 +23,13 @@ struct LengthArgs {
   int32_t *cache_past, *cache_total, *evict;  // cache_total may be null
   uint32_t *flags;
   int32_t batch, S, C;
+  FastDiv gap;  // capacity - window + 1
 };
 
 __global__ __launch_bounds__(kBlock) void seq_lengths_kernel(LengthArgs a) {
   const int32_t b = blockIdx.x * kBlock + threadIdx.x;
   if (b >= a.batch) return;
-  const StepLengths r = step_lengths(a.seqlens_k[b], a.S, a.C);
+  const StepLengths r = step_lengths(a.seqlens_k[b], a.S, a.C, a.gap);
   if (r.bad && a.flags) atomicOr(a.flags, SWRT_FLAG_BAD_SEQLEN);
   if (a.total) a.total[b] = r.T;
   if (a.past) a.past[b] = r.P;
@@ -40,11 +43,14 @@ __global__ __launch_bounds__(kBlock) void seq_lengths_kernel(LengthArgs a) {
 
 using namespace swrt;
 
-extern "C" int swrt_kv_seq_lengths(const int32_t *seqlens_k, int batch, int seq_len, int capacity,
-                                   int64_t *total_lens, int64_t *past_lens,
-                                   int32_t *cache_past_lens, int32_t *cache_total_lens,
-                                   int32_t *evict_counts, uint32_t *d_flags, void *stream) {
+namespace {
+
+int seq_lengths(const int32_t *seqlens_k, int batch, int seq_len, int capacity, int window,
+                int64_t *total_lens, int64_t *past_lens, int32_t *cache_past_lens,
+                int32_t *cache_total_lens, int32_t *evict_counts, uint32_t *d_flags,
+                void *stream) {
   if (batch < 0 || seq_len < 1 || capacity < 1) return SWRT_E_INVALID_ARG;
+  if (window < 1 || window > capacity) return SWRT_E_INVALID_ARG;
   if (batch == 0) return SWRT_OK;
   if (!seqlens_k || !cache_past_lens || !evict_counts) return SWRT_E_INVALID_ARG;
   const auto addr = [](const void *p) { return uint64_t(reinterpret_cast<uintptr_t>(p)); };
@@ -53,17 +59,35 @@ extern "C" int swrt_kv_seq_lengths(const int32_t *seqlens_k, int batch, int seq_
       addr(d_flags) % 4)
     return SWRT_E_INVALID_ARG;
   const uint64_t n4 = uint64_t(batch) * 4, n8 = uint64_t(batch) * 8;
-  const void *bufs[6] = {seqlens_k, total_lens, past_lens, cache_past_lens, cache_total_lens,
-                         evict_counts};
-  const uint64_t size[6] = {n4, n8, n8, n4, n4, n4};
-  for (int i = 0; i < 6; ++i)
-    for (int j = i + 1; j < 6; ++j)
-      if (overlaps(bufs[i], size[i], bufs[j], size[j])) return SWRT_E_INVALID_ARG;
+  Range ranges[7] = {range(seqlens_k, n4, false),      range(total_lens, n8, true),
+                     range(past_lens, n8, true),        range(cache_past_lens, n4, true),
+                     range(cache_total_lens, n4, true), range(evict_counts, n4, true),
+                     range(d_flags, 4, true)};
+  if (written_overlap(ranges, 7)) return SWRT_E_INVALID_ARG;
 
   LengthArgs a{seqlens_k, total_lens, past_lens, cache_past_lens, cache_total_lens, evict_counts,
-               d_flags, batch, seq_len, capacity};
+               d_flags, batch, seq_len, capacity, FastDiv(uint32_t(capacity - window + 1))};
   const uint32_t grid = (uint32_t(batch) + kBlock - 1) / kBlock;
   hipLaunchKernelGGL(seq_lengths_kernel, dim3(grid), dim3(kBlock), 0,
                      static_cast<hipStream_t>(stream), a);
   return launch_status();
+}
+
+}  // namespace
+
+extern "C" int swrt_kv_seq_lengths(const int32_t *seqlens_k, int batch, int seq_len, int capacity,
+                                   int64_t *total_lens, int64_t *past_lens,
+                                   int32_t *cache_past_lens, int32_t *cache_total_lens,
+                                   int32_t *evict_counts, uint32_t *d_flags, void *stream) {
+  return seq_lengths(seqlens_k, batch, seq_len, capacity, capacity, total_lens, past_lens,
+                     cache_past_lens, cache_total_lens, evict_counts, d_flags, stream);
+}
+
+extern "C" int swrt_kv_seq_lengths_drift(const int32_t *seqlens_k, int batch, int seq_len,
+                                         int capacity, int window, int64_t *total_lens,
+                                         int64_t *past_lens, int32_t *cache_past_lens,
+                                         int32_t *cache_total_lens, int32_t *evict_counts,
+                                         uint32_t *d_flags, void *stream) {
+  return seq_lengths(seqlens_k, batch, seq_len, capacity, window, total_lens, past_lens,
+                     cache_past_lens, cache_total_lens, evict_counts, d_flags, stream);
 }

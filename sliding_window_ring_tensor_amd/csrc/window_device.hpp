@@ -32,22 +32,45 @@ constexpr uint32_t kWinTile = kWinBlock * kWinUnroll;
 // ---------------------------------------------------------------------------
 // lengths of one step (same page, section "Design"; the follow-up commit does
 // the arithmetic in 64 bits because seqlens_k + 1 overflows 32 bits at
-// INT32_MAX, and clamps the past length at zero)
+// INT32_MAX, and clamps the past length at zero).
+//
+// The resident count after x tokens is end(x). The base layout keeps
+// end(x) = min(x, C). The drifting layout of the CPU follow-up ("Key design
+// decisions") lets the append point drift: with gap = C - W + 1, end(x) = x
+// while x <= C, afterwards x minus as many whole gaps as bring it back to at
+// most C (so W <= end <= C), which reclaims a whole gap at once, once every
+// gap decode steps. gap = 1 is the base layout. A step appending S tokens
+// onto P then has Lp = end(P), L = end(P + S) and E = Lp + S - L.
 // ---------------------------------------------------------------------------
 struct StepLengths {
   int64_t T, P, Lp, E, L;
   bool bad;  // seqlens_k < 0 or T < S
 };
 
-__device__ __forceinline__ StepLengths step_lengths(int32_t seqlens_k, int64_t S, int64_t C) {
+// x <= max(seqlens_k + 1, S) <= 2^31, so the ceiling quotient's numerator
+// x - C + gap - 1 = x - W stays below 2^31 and the launch-wide divider applies.
+__device__ __forceinline__ int64_t resident_end(int64_t x, int64_t C, const FastDiv &gap) {
+  if (x <= C) return x;
+  return x - int64_t(gap.d) * gap.div(uint32_t(x - C + gap.d - 1));
+}
+
+// DRIFT = false is the base layout (gap 1, end(x) = min(x, C)) without the
+// division; DRIFT = true takes the gap from the launch.
+template <bool DRIFT = true>
+__device__ __forceinline__ StepLengths step_lengths(int32_t seqlens_k, int64_t S, int64_t C,
+                                                    const FastDiv &gap) {
   StepLengths r;
   r.T = int64_t(seqlens_k) + 1;  // absolute total length after the step
   r.P = r.T - S;                  // absolute past length, clamped at zero
   if (r.P < 0) r.P = 0;
-  r.Lp = r.P < C ? r.P : C;       // tokens resident before the step
-  r.E = r.Lp + S - C;             // tokens evicted by the step
-  if (r.E < 0) r.E = 0;
-  r.L = r.Lp + S - r.E;           // tokens resident after the step
+  if constexpr (DRIFT) {
+    r.Lp = resident_end(r.P, C, gap);     // tokens resident before the step
+    r.L = resident_end(r.P + S, C, gap);  // tokens resident after the step
+  } else {
+    r.Lp = r.P < C ? r.P : C;
+    r.L = r.P + S < C ? r.P + S : C;
+  }
+  r.E = r.Lp + S - r.L;  // tokens evicted by the step
   r.bad = seqlens_k < 0 || r.T < S;
   return r;
 }
@@ -82,22 +105,22 @@ __device__ __forceinline__ Slice decode_slice(const WindowGeom &g, uint32_t slic
   return s;
 }
 
-// (Lp, E) must be the pair the lengths give for (C, S): 0 <= Lp <= C and
-// E = max(0, Lp + S - C). Otherwise flag once per batch entry (by the leader
-// lane of the (layer 0, K, h 0) slice's first tile) and skip it.
+// (Lp, E) must describe a step that fits the cache: 0 <= Lp <= C, E >= 0 and
+// 1 <= L = Lp + S - E <= C (the base lengths and the drifting layout's both
+// do). Otherwise flag once per batch entry (by the leader lane of the
+// (layer 0, K, h 0) slice's first tile) and skip it.
 __device__ __forceinline__ bool lengths_ok(const WindowGeom &g, const Slice &s, bool leader,
                                            int64_t Lp, int64_t E) {
-  int64_t e = Lp + g.S - g.C;
-  if (e < 0) e = 0;
-  if (Lp >= 0 && Lp <= g.C && E == e) return true;
+  const int64_t L = Lp + g.S - E;
+  if (Lp >= 0 && Lp <= g.C && E >= 0 && L >= 1 && L <= g.C) return true;
   if (g.flags && s.layer == 0 && s.t == 0 && s.h == 0 && leader)
     atomicOr(g.flags, SWRT_FLAG_BAD_LENGTHS);
   return false;
 }
 
 // ---------------------------------------------------------------------------
-// S = 1, in place: one workgroup shifts one slice by E (0 or 1) rows and
-// appends the new row at Lp - E.
+// S = 1, in place: one workgroup (BLOCK threads, UNROLL words each per tile)
+// shifts one slice by E rows and appends the new row at Lp - E.
 //
 // The shift is an overlapping move with dst < src. The workgroup walks the
 // slice in ascending tiles and, per tile, loads every word into registers,
@@ -106,9 +129,12 @@ __device__ __forceinline__ bool lengths_ok(const WindowGeom &g, const Slice &s, 
 // its own loads already returned. No other workgroup touches the slice and no
 // scratch memory is needed. Lanes past the end of the last tile clamp to its
 // last word (same value to the same address as the owning lane), so the loop
-// has no per-lane branch and the wait counters stay exact.
+// has no per-lane branch and the wait counters stay exact. With a one-wave
+// workgroup the barrier compiles to nothing: the wave's vector memory
+// operations take effect in issue order, and every store is issued after the
+// load of its address, which keeps the same guarantee.
 // ---------------------------------------------------------------------------
-template <int VEC>
+template <int VEC, int BLOCK = kWinBlock, int UNROLL = kWinUnroll>
 __device__ __forceinline__ void shift_append_slice(char *base, const char *new_row, int64_t Lp,
                                                    int64_t E, uint64_t row_bytes,
                                                    uint32_t row_words) {
@@ -118,7 +144,7 @@ __device__ __forceinline__ void shift_append_slice(char *base, const char *new_r
   // overlaps the shift; it is stored at row Lp - E.
   const W *nsrc = reinterpret_cast<const W *>(new_row);
   W *adst = reinterpret_cast<W *>(base + uint64_t(Lp - E) * row_bytes);
-  const bool row_in_one_pass = row_words <= uint32_t(kWinBlock);
+  const bool row_in_one_pass = row_words <= uint32_t(BLOCK);
   const uint32_t ai = min(threadIdx.x, row_words - 1);
   W nv;
   if (row_in_one_pass) nv = ld(nsrc + ai);
@@ -126,29 +152,38 @@ __device__ __forceinline__ void shift_append_slice(char *base, const char *new_r
   if (E) {
     const W *src = reinterpret_cast<const W *>(base + uint64_t(E) * row_bytes);
     const uint32_t n = uint32_t(Lp - E) * row_words;
-    for (uint32_t c0 = 0; c0 < n; c0 += kWinTile) {
-      W v[kWinUnroll];
+    for (uint32_t c0 = 0; c0 < n; c0 += uint32_t(BLOCK * UNROLL)) {
+      W v[UNROLL];
 #pragma unroll
-      for (int u = 0; u < kWinUnroll; ++u) v[u] = ld(src + min(c0 + u * kWinBlock + threadIdx.x, n - 1));
+      for (int u = 0; u < UNROLL; ++u) v[u] = ld(src + min(c0 + u * BLOCK + threadIdx.x, n - 1));
       __syncthreads();  // every old value of this tile is in registers
-      // Row Lp - E is read by the last tile and is no shift destination: the
-      // new row can go out as soon as that tile's loads are done.
-      if (row_in_one_pass && c0 + kWinTile >= n) {
+      // Row Lp - E is no shift destination, and from here on every load of
+      // every tile (this last one's included) has returned: the new row can
+      // go out now.
+      if (row_in_one_pass && c0 + uint32_t(BLOCK * UNROLL) >= n) {
         st(adst + ai, nv);
         appended = true;
       }
 #pragma unroll
-      for (int u = 0; u < kWinUnroll; ++u) st(dst + min(c0 + u * kWinBlock + threadIdx.x, n - 1), v[u]);
+      for (int u = 0; u < UNROLL; ++u) st(dst + min(c0 + u * BLOCK + threadIdx.x, n - 1), v[u]);
     }
   }
   if (!appended) {  // no shift, or a row wider than one pass: after every load
     if (row_in_one_pass) {
       st(adst + ai, nv);
     } else {
-      for (uint32_t i = threadIdx.x; i < row_words; i += kWinBlock) st(adst + i, ld(nsrc + i));
+      for (uint32_t i = threadIdx.x; i < row_words; i += BLOCK) st(adst + i, ld(nsrc + i));
     }
   }
 }
+
+// ---------------------------------------------------------------------------
+// Shape of the one-wave variant: under the drifting layout most slices of a
+// decode step only append their new row, so the step is many short
+// workgroups; 64-thread workgroups (one wave, 16 words per lane) let 32 of
+// them share a CU where 512-thread ones allow 4.
+constexpr int kWaveBlock = 64;
+constexpr int kWaveUnroll = 16;
 
 // ---------------------------------------------------------------------------
 // S = 1, in place, several small slices per workgroup. When a whole slice is

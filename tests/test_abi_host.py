@@ -47,7 +47,8 @@ def _header():
 def test_exports_every_declared_function(L):
     declared = set(re.findall(r"^(?:int|const char \*)\s*(swrt_\w+)\s*\(", _header(), re.M))
     assert {"swrt_tensor_scatter", "swrt_tensor_scatter_batched", "swrt_kv_seq_lengths", "swrt_kv_window_append",
-            "swrt_kv_window_append_layers", "swrt_kv_decode_step", "swrt_status_string",
+            "swrt_kv_window_append_layers", "swrt_kv_decode_step", "swrt_kv_seq_lengths_drift",
+            "swrt_status_string",
             "swrt_abi_version"} <= declared
     out = subprocess.run(["nm", "-D", "--defined-only", swrt.LIBRARY], check=True,
                          capture_output=True, text=True).stdout
@@ -59,7 +60,7 @@ def test_exports_every_declared_function(L):
 
 def test_constants_agree():
     defs = dict(re.findall(r"#define (SWRT_\w+) (\d+)u?", _header()))
-    assert int(defs["SWRT_ABI_VERSION"]) == 1
+    assert int(defs["SWRT_ABI_VERSION"]) == swrt.ABI_VERSION
     py = {"SWRT_OK": swrt.OK, "SWRT_E_INVALID_ARG": swrt.E_INVALID_ARG,
           "SWRT_E_UNSUPPORTED": swrt.E_UNSUPPORTED, "SWRT_E_LAUNCH": swrt.E_LAUNCH,
           "SWRT_FLAG_LINEAR_OOB": swrt.FLAG_LINEAR_OOB, "SWRT_FLAG_BAD_SEQLEN": swrt.FLAG_BAD_SEQLEN,
@@ -82,7 +83,7 @@ def test_status_strings(L):
     for code in (0, 1, 2, 3, 99, -1):
         assert isinstance(L.swrt_status_string(code), bytes)
     assert L.swrt_status_string(0) == b"ok"
-    assert L.swrt_abi_version() == 1
+    assert L.swrt_abi_version() == swrt.ABI_VERSION
 
 
 def test_binding_refuses_cpu_tensors():
@@ -173,6 +174,10 @@ def test_kv_seq_lengths_rejects(L):
     assert _lens(L, Lt=C_ + 8) == INV                                   # overlaps Lp
     assert _lens(L, E=A) == INV                                         # overlaps seqlens_k
     assert _lens(L, batch=0) == swrt.OK
+    drift = L.swrt_kv_seq_lengths_drift
+    assert drift(A, 4, 1, 8, 0, B_, B_ + 0x1000, C_, C_ + 0x1000, D_, None, None) == INV
+    assert drift(A, 4, 1, 8, 9, B_, B_ + 0x1000, C_, C_ + 0x1000, D_, None, None) == INV
+    assert drift(A, 0, 1, 8, 5, B_, B_ + 0x1000, C_, C_ + 0x1000, D_, None, None) == swrt.OK
 
 
 def _win(L, kc=A, vc=A + 0x1000_0000, kn=B_, vn=B_ + 0x1000_0000, strides=None, ks=None, vs=None,
@@ -219,10 +224,12 @@ def test_kv_decode_step_rejects(L):
     INV = swrt.E_INVALID_ARG
     V = ctypes.c_void_p
 
-    def call(nw=1, nf=1, wk=A, wv=A + 0x1000_0000, fc=C_, sk=D_, C=8, M=16, batch=2, lens=None):
+    def call(nw=1, nf=1, wk=A, wv=A + 0x1000_0000, fc=C_, sk=D_, C=8, M=16, batch=2, lens=None,
+             W=None):
         arr = lambda *p: (V * len(p))(*p)  # noqa: E731
         return L.swrt_kv_decode_step(nw, arr(wk), arr(wv), arr(B_), arr(B_ + 0x1000),
-                                     (I64 * 3)(32, 16, 16), sk, C, None, None, lens, None, None,
+                                     (I64 * 3)(32, 16, 16), sk, C, C if W is None else W, None,
+                                     None, lens, None, None,
                                      nf, arr(fc), arr(B_ + 0x2000), D_ + 0x1000, M, batch, 2, 16,
                                      16, None, None)
     assert call(nw=33) == INV and call(nf=65) == INV and call(nw=-1) == INV
@@ -232,4 +239,5 @@ def test_kv_decode_step_rejects(L):
     assert call(M=0) == INV                                    # S = 1 > M
     assert call(lens=D_ + 4) == INV                            # length output inside seqlens_k
     assert call(sk=D_ + 2) == INV                              # misaligned seqlens_k
+    assert call(W=0) == INV and call(W=9) == INV               # window outside [1, C]
     assert call(nw=0, nf=0) == swrt.OK                         # nothing to do

@@ -654,3 +654,150 @@ def test_decode_step_rejects_overlap():
     with pytest.raises(swrt.SwrtError) as e:
         swrt.kv_decode_step([win], [other], [new], [new], sk, [full], [new], wi)
     assert e.value.status == swrt.E_INVALID_ARG
+
+
+# ---------------------------------------------------------------------------
+# drifting layout (CPU follow-up of the pull request: Key design decisions)
+# ---------------------------------------------------------------------------
+
+def test_drift_lengths(orc):
+    g = np.random.default_rng(61)
+    edges = np.array([-5, -1, 0, 1, 127, 128, 129, 135, 136, 137, 144, 145, 146, 4095, 2**31 - 1,
+                      -2**31], dtype=np.int64)
+    for S, C, W in ((1, 136, 128), (1, 144, 128), (1, 128, 128), (32, 48, 40), (300, 100, 60),
+                    (1, 9, 1), (7, 16, 9), (1, 2**31 - 1, 1), (1000, 2**31 - 1, 2**31 - 2),
+                    (3, 2**30 + 7, 5)):  # gaps up to 2^31 - 1
+        for sk in (edges.astype(np.int32), g.integers(-3, 6 * C, size=333).astype(np.int32)):
+            flags = flag_word()
+            got = swrt.kv_seq_lengths(torch.from_numpy(sk).to(DEV), S, C, window=W, flags=flags)
+            want = orc.kv_seq_lengths_drift(sk, S, C, W)
+            torch.cuda.synchronize()
+            for x, y in zip(got, (want.total, want.past, want.cache_past, want.cache_total,
+                                  want.evict)):
+                np.testing.assert_array_equal(x.cpu().numpy(), y)
+            assert flags.item() == want.flags
+
+
+@pytest.mark.parametrize("C,W,sched", [
+    (136, 128, [136] + [1] * 60),                 # decode past capacity: compactions every 9 steps
+    (48, 40, [32] * 6 + [1] * 30 + [32, 1, 1]),   # 32-token chunks at C = W + 8 (staging)
+    (16, 8, [5, 1, 1, 20, 1, 1, 1, 9, 1] + [1] * 20),
+    (12, 12, [3] + [1] * 30),                     # gap 1: the base layout
+])
+def test_drift_replay(orc, C, W, sched):
+    """Tagged histories on the GPU with drifting lengths, compared with the
+    oracle after every step and with the window the page guarantees."""
+    B, H, D = 3, 2, 8
+    k, v = replay.fresh_cache(B, H, C, D)
+    kd, vd = torch.from_numpy(k).to(DEV), torch.from_numpy(v).to(DEV)
+    T = np.array([0, 0, 0])
+    for step, S in enumerate(sched):
+        say("drift replay", C, W, step, S)
+        Ta = T + S
+        sk = (Ta - 1).astype(np.int32)
+        lens = swrt.kv_seq_lengths(torch.from_numpy(sk).to(DEV), S, C, window=W)
+        kn, vn = replay.new_block(B, H, T, S, D)
+        kw = vw = None
+        if S > 1:
+            ks, vs = replay.fresh_cache(B, H, C + S, D, tensors=(2, 3))
+            kw, vw = torch.from_numpy(ks).to(DEV), torch.from_numpy(vs).to(DEV)
+        flags = flag_word()
+        swrt.kv_window_append(kd, vd, torch.from_numpy(kn).to(DEV), torch.from_numpy(vn).to(DEV),
+                              lens.cache_past, lens.evict, k_staging=kw, v_staging=vw, flags=flags)
+        L = orc.kv_seq_lengths_drift(sk, S, C, W)
+        f = orc.kv_window_append(k, v, kn, vn, L.cache_past, L.evict,
+                                 None if S == 1 else ks, None if S == 1 else vs)
+        T = Ta
+        torch.cuda.synchronize()
+        assert flags.item() == f == 0
+        np.testing.assert_array_equal(kd.cpu().numpy(), k)
+        np.testing.assert_array_equal(vd.cpu().numpy(), v)
+        for b in range(B):
+            n = int(L.cache_total[b])
+            assert min(int(T[b]), W) <= n <= C
+            toks = np.arange(T[b] - n, T[b])
+            np.testing.assert_array_equal(k[b, 0, :n], replay.token_rows(0, b, 0, toks, D))
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["append", "decode_step"])
+@pytest.mark.parametrize("C,W,D", [(4096 + 16, 4096, 128), (1000, 900, 40)])
+def test_drift_multi_tile_gap_shift(orc, C, W, D, fused):
+    """S = 1 compaction steps that move a whole gap over slices much larger
+    than one tile, through the windowed append and through the one-launch
+    decode step (its one-wave shape)."""
+    g = wl.rng(C)
+    B, H = 3, 2
+    kc = wl.host_payload(g, (B, H, C, D), torch.bfloat16, True)
+    vc = wl.host_payload(g, (B, H, C, D), torch.bfloat16, True)
+    gap = C - W + 1
+    for sk0 in (C, C + gap, 5 * C + 3):  # each batch entry at a compaction step or not
+        kn = wl.host_payload(g, (B, H, 1, D), torch.bfloat16, True)
+        vn = wl.host_payload(g, (B, H, 1, D), torch.bfloat16, True)
+        sk = np.array([sk0, sk0 + 1, sk0 - 1], dtype=np.int32)
+        say("drift gap shift", C, W, D, sk0, fused)
+        kd, vd = kc.to(DEV), vc.to(DEV)
+        sk_d = torch.from_numpy(sk).to(DEV)
+        if fused:
+            empty = torch.empty(0, dtype=torch.int64, device=DEV)
+            swrt.kv_decode_step([kd], [vd], [kn.to(DEV)], [vn.to(DEV)], sk_d, [], [], empty,
+                                window=W)
+        else:
+            lens = swrt.kv_seq_lengths(sk_d, 1, C, window=W)
+            swrt.kv_window_append(kd, vd, kn.to(DEV), vn.to(DEV), lens.cache_past, lens.evict)
+        L = orc.kv_seq_lengths_drift(sk, 1, C, W)
+        hk, hv = hb(kc).copy(), hb(vc).copy()
+        assert orc.kv_window_append_strided(hk, hv, hb(kn), hb(vn), (H * D, D, D), 1,
+                                            L.cache_past, L.evict, elem_bits=16, head_dim=D) == 0
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(hb(kd), hk)
+        np.testing.assert_array_equal(hb(vd), hv)
+        kc, vc = kd.cpu(), vd.cpu()
+
+
+# (dtype, head_dim): 8- and 4-word rows in one pass, 64-word rows whose shifts
+# span several one-wave tiles, 128-word rows wider than one pass, 3-word rows
+@pytest.mark.parametrize("dtype,D", [(torch.bfloat16, 64), (torch.float8_e4m3fn, 64),
+                                     (torch.float32, 256), (torch.float32, 512),
+                                     (torch.bfloat16, 6)])
+def test_decode_step_drift(orc, dtype, D):
+    """The one-launch step with a window below the capacity against the
+    three-call composition with drifting lengths and against the oracle."""
+    g = wl.rng(71 + D)
+    B, H, W, M, nw, nf = 16, 4, 128, 300, 3, 4
+    C = W + 16
+    say("decode step drift", dtype, D)
+    T = g.integers(1, 4 * C, size=B)
+    T[:4] = [C + 1, C + 17, C + 18, 2 * C]  # compaction steps and plain appends side by side
+    sk = (T - 1).astype(np.int32)
+    wi = ((T - 1) % M).astype(np.int64)
+    host = _decode_buffers(g, B, H, C, M, D, nw, nf, dtype)
+    results = []
+    for fused in (True, False):
+        wk, wv, wkn, wvn, fc, fn = [[t.to(DEV) for t in grp] for grp in host]
+        sk_d, wi_d = torch.from_numpy(sk).to(DEV), torch.from_numpy(wi).to(DEV)
+        flags = flag_word()
+        if fused:
+            lens = swrt.kv_decode_step(wk, wv, wkn, wvn, sk_d, fc, fn, wi_d, window=W, flags=flags)
+        else:
+            lens = swrt.kv_seq_lengths(sk_d, 1, C, window=W, flags=flags)
+            swrt.kv_window_append_layers(wk, wv, wkn, wvn, lens.cache_past, lens.evict,
+                                         flags=flags)
+            swrt.tensor_scatter_batched(fc, fn, wi_d, axis=2, mode="linear", outs=fc, flags=flags)
+        torch.cuda.synchronize()
+        results.append(([hb(t) for t in (*wk, *wv, *fc, *lens)], flags.item()))
+    (a, fa), (b3, fb) = results
+    assert fa == fb == 0
+    for x, y in zip(a, b3):
+        np.testing.assert_array_equal(x, y)
+    L = orc.kv_seq_lengths_drift(sk, 1, C, W)
+    assert (L.evict > 0).any() and (L.evict == 0).any()
+    bits = torch.empty((), dtype=dtype).element_size() * 8
+    wk, wv, wkn, wvn, fc, fn = [[hb(t).copy() for t in grp] for grp in host]
+    for i in range(nw):
+        assert orc.kv_window_append_strided(wk[i], wv[i], wkn[i], wvn[i], (H * D, D, D), 1,
+                                            L.cache_past, L.evict, elem_bits=bits,
+                                            head_dim=D) == 0
+    for c, u in zip(fc, fn):
+        assert orc.tensor_scatter_raw(c, c, u, wi, (B, H, M, D), 2, 1, 0, bits) == (0, 0)
+    for x, y in zip(a, [*wk, *wv, *fc]):
+        np.testing.assert_array_equal(x, y)
