@@ -48,9 +48,9 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD's published peak
 # (FETCH_SIZE, WRITE_SIZE), each scaled by what the counter reads for a 1 GiB
 # copy; valid only for the kernel source they were taken on (its hash).
 MEASURED_TRAFFIC = {
-    ("bf16", "decode_step_kernel", "b3c645c1db481e98"): {"read": 196_781_015,
-                                                         "written": 196_831_387},
-    ("bf16", "window_in_place", "4016938b0441144f"): {"read": 195_186_307, "written": 196_004_004},
+    ("bf16", "decode_step_kernel", "897262af264568cb"): {"read": 196_783_552,
+                                                         "written": 196_835_808},
+    ("bf16", "window_in_place", "f2dfcf6af985c7eb"): {"read": 195_176_829, "written": 196_010_155},
 }
 _CSRC = "sliding_window_ring_tensor_amd/csrc/"
 KERNEL_SOURCES = {
