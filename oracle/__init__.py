@@ -33,18 +33,61 @@ MODE_CIRCULAR = 1
 PHASE_STAGE = 1
 PHASE_COMMIT = 2
 PHASE_ALL = 3
+FLAG_ROPE_RANGE = 8
+# element types of the row transform
+XF_F32, XF_F16, XF_BF16, XF_INT8, XF_UINT8 = 1, 2, 3, 4, 5
+XF_BYTES = {XF_F32: 4, XF_F16: 2, XF_BF16: 2, XF_INT8: 1, XF_UINT8: 1}
 
 
 def build(source: str = SOURCE, out: str = LIBRARY, extra: tuple = ()) -> str:
     """Compile the oracle with gcc into a shared library and return its path."""
-    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-Werror", "-shared", "-fPIC",
-           *extra, source, "-o", out]
+    # -ffp-contract=off: every float operation of the row transform is rounded
+    # on its own, as its definition states
+    cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-Wall", "-Wextra", "-Werror",
+           "-shared", "-fPIC", *extra, source, "-o", out, "-lm"]
     subprocess.run(cmd, check=True, cwd=HERE)
     return out
 
 
 class OracleError(RuntimeError):
     pass
+
+
+class RowXf(ctypes.Structure):
+    """The C struct orc_row_xf."""
+    _fields_ = [("in_type", ctypes.c_int), ("out_type", ctypes.c_int),
+                ("cos_table", ctypes.c_void_p), ("sin_table", ctypes.c_void_p),
+                ("max_position", ctypes.c_int64), ("rotary_dim", ctypes.c_int64),
+                ("interleaved", ctypes.c_int), ("scale", ctypes.c_float * 2),
+                ("zero_point", ctypes.c_int32 * 2)]
+
+
+@dataclass
+class Transform:
+    """A row transform: RoPE tables (float32 [max_position, rotary_dim/2], or
+    None), element types and the K / V affine parameters."""
+    in_type: int
+    out_type: int
+    cos: np.ndarray | None = None
+    sin: np.ndarray | None = None
+    rotary_dim: int = 0
+    interleaved: bool = False
+    scale: tuple = (1.0, 1.0)
+    zero_point: tuple = (0, 0)
+
+    def c(self) -> RowXf:
+        x = RowXf()
+        x.in_type, x.out_type = self.in_type, self.out_type
+        if self.cos is not None:
+            self.cos = np.ascontiguousarray(self.cos, dtype=np.float32)
+            self.sin = np.ascontiguousarray(self.sin, dtype=np.float32)
+            x.cos_table, x.sin_table = self.cos.ctypes.data, self.sin.ctypes.data
+            x.max_position = self.cos.shape[0]
+        x.rotary_dim = self.rotary_dim
+        x.interleaved = int(self.interleaved)
+        x.scale[0], x.scale[1] = self.scale
+        x.zero_point[0], x.zero_point[1] = self.zero_point
+        return x
 
 
 def _ptr(a):
@@ -81,6 +124,14 @@ class Oracle:
         lib.orc_kv_window_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                              i64, i64, i64, i64, i64, i32, ctypes.c_uint, u32p]
         lib.orc_kv_window_append.restype = ctypes.c_int
+        xfp = ctypes.POINTER(RowXf)
+        lib.orc_xf_row.argtypes = [xfp, i32, i64, vp, vp, i64]
+        lib.orc_xf_row.restype = ctypes.c_int
+        lib.orc_kv_window_append_xf.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64,
+                                                i64, i64, i64, ctypes.c_uint, xfp, u32p]
+        lib.orc_kv_window_append_xf.restype = ctypes.c_int
+        lib.orc_tensor_scatter_xf.argtypes = [vp, vp, vp, vp, vp, i32, i64, i32, i32, xfp, u32p]
+        lib.orc_tensor_scatter_xf.restype = ctypes.c_int
         self.lib = lib
 
     # -- TensorScatter ----------------------------------------------------
@@ -188,6 +239,56 @@ class Oracle:
         if st != OK:
             raise OracleError(f"orc_kv_window_append status {st}")
         return flags.value
+
+
+    # -- fused append: RoPE + conversion / quantization -------------------
+    def xf_row(self, x: Transform, t: int, pos: int, row: np.ndarray, out: np.ndarray) -> int:
+        """One row through the transform (row: head_dim elements of in_type,
+        out: head_dim elements of out_type, both contiguous). Returns the status."""
+        D = out.size
+        if x.in_type in (XF_F32, XF_F16, XF_BF16) and x.out_type in XF_BYTES:
+            assert row.nbytes == D * XF_BYTES[x.in_type] and out.nbytes == D * XF_BYTES[x.out_type]
+        return self.lib.orc_xf_row(ctypes.byref(x.c()), t, pos, _ptr(row), _ptr(out), D)
+
+    def kv_window_append_xf(self, x: Transform, k_cache, v_cache, k_new, v_new, new_strides,
+                            seq_len, cache_past_lens, evict_counts, past_lens, k_staging=None,
+                            v_staging=None, phase: int = PHASE_ALL) -> int:
+        """Windowed step whose new rows pass through ``x`` first. Caches
+        [B, H, C, row] hold D out_type elements per row (any numpy dtype; D
+        follows from the row bytes), new rows of in_type are addressed by
+        ``new_strides`` (elements). Returns the flags."""
+        B, H, C = k_cache.shape[:3]
+        D = k_cache.shape[3] * k_cache.itemsize // XF_BYTES[x.out_type]  # elements per row
+        ns = np.ascontiguousarray(np.asarray(new_strides, dtype=np.int64))
+        lp = np.ascontiguousarray(cache_past_lens, dtype=np.int32)
+        ev = np.ascontiguousarray(evict_counts, dtype=np.int32)
+        pl = np.ascontiguousarray(past_lens, dtype=np.int64)
+        flags = ctypes.c_uint32(0)
+        st = self.lib.orc_kv_window_append_xf(_ptr(k_cache), _ptr(v_cache), _ptr(k_new),
+                                              _ptr(v_new), _ptr(ns), _ptr(k_staging),
+                                              _ptr(v_staging), _ptr(lp), _ptr(ev), _ptr(pl), B,
+                                              H, C, seq_len, D, phase, ctypes.byref(x.c()),
+                                              ctypes.byref(flags))
+        if st != OK:
+            raise OracleError(f"orc_kv_window_append_xf status {st}")
+        return flags.value
+
+    def tensor_scatter_xf(self, x: Transform, t: int, present, past, update, write_indices,
+                          mode: str = "linear"):
+        """TensorScatter along axis -2 whose update rows pass through ``x``
+        (t = 0: K, rotated; 1: V). present / past [..., M, row] hold D out_type
+        elements per row, update [..., S, row'] D in_type elements (any numpy
+        dtypes). Returns (status, flags)."""
+        shp = np.asarray(past.shape, dtype=np.int64)
+        shp[-1] = past.shape[-1] * past.itemsize // XF_BYTES[x.out_type]  # elements per row
+        assert update.shape[-1] * update.itemsize == shp[-1] * XF_BYTES[x.in_type]
+        wi = None if write_indices is None else np.ascontiguousarray(write_indices, dtype=np.int64)
+        flags = ctypes.c_uint32(0)
+        st = self.lib.orc_tensor_scatter_xf(_ptr(present), _ptr(past), _ptr(update), _ptr(wi),
+                                            _ptr(shp), past.ndim, update.shape[-2],
+                                            MODE_CIRCULAR if mode == "circular" else MODE_LINEAR,
+                                            t, ctypes.byref(x.c()), ctypes.byref(flags))
+        return st, flags.value
 
 
 _default: Oracle | None = None

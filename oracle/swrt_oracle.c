@@ -26,9 +26,22 @@
  *     (0 <= Lp <= C, L = Lp + S - E with 1 <= L <= C, E >= 0): the base
  *     lengths evict only what does not fit, the drifting layout of the CPU
  *     follow-up evicts a whole gap of rows at once; both are such steps.
+ *   - [GQA-ROPE] names RoPE at the absolute position but not its arithmetic:
+ *     the rotation is the usual pairwise one, read from caller-given cosine
+ *     and sine tables (one row per position), half-split or interleaved
+ *     pairs, computed in binary32 one operation at a time (the precision the
+ *     rounded value and the quantized code are decided in); only K turns.
+ *     Row s of a windowed step sits at position P + s (P the absolute past
+ *     length), row s of a TensorScatter at write_indices[b] + s before any
+ *     wrap; an entry with a position outside the tables is flagged and
+ *     skipped whole, K and V alike.
+ *   - [PF] fixes rounding (ties to even) and saturation of affine codes but
+ *     not NaN: NaN takes the zero point; half-precision outputs store NaN as
+ *     the positive canonical quiet NaN.
  */
 #include "swrt_oracle.h"
 
+#include <math.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -347,4 +360,370 @@ int orc_kv_window_append(void *k_cache, void *v_cache, const void *k_new,
     }
     free(tmp);
     return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* [GQA-ROPE] + [PF] the row transform of a fused append                    */
+/* ------------------------------------------------------------------------ */
+
+static int xf_float_type(int type)
+{
+    return type == ORC_XF_F32 || type == ORC_XF_F16 || type == ORC_XF_BF16;
+}
+
+static int64_t xf_elem_bytes(int type)
+{
+    switch (type) {
+    case ORC_XF_F32: return 4;
+    case ORC_XF_F16:
+    case ORC_XF_BF16: return 2;
+    case ORC_XF_INT8:
+    case ORC_XF_UINT8: return 1;
+    default: return 0;
+    }
+}
+
+static int xf_code_range(int type, int32_t *lo, int32_t *hi)
+{
+    if (type == ORC_XF_INT8) {
+        *lo = -128;
+        *hi = 127;
+        return 1;
+    }
+    if (type == ORC_XF_UINT8) {
+        *lo = 0;
+        *hi = 255;
+        return 1;
+    }
+    return 0;
+}
+
+/* a transform the functions below accept, for rows of head_dim elements */
+static int xf_valid(const orc_row_xf *x, int64_t head_dim)
+{
+    int32_t lo, hi;
+    if (!x || !xf_float_type(x->in_type) || xf_elem_bytes(x->out_type) == 0)
+        return 0;
+    if ((x->cos_table == NULL) != (x->sin_table == NULL))
+        return 0;
+    if (x->cos_table) {
+        if (x->max_position < 1 || x->rotary_dim < 2 || x->rotary_dim % 2 != 0 ||
+            x->rotary_dim > head_dim)
+            return 0;
+    }
+    if (xf_code_range(x->out_type, &lo, &hi)) {
+        for (int t = 0; t < 2; ++t) {
+            if (!(x->scale[t] > 0.0f) || isinf(x->scale[t]))
+                return 0;
+            if (x->zero_point[t] < lo || x->zero_point[t] > hi)
+                return 0;
+        }
+    }
+    return 1;
+}
+
+static float bf16_bits_to_float(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16; /* bf16 is the top half of a binary32 */
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+/* binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits */
+static float f16_bits_to_float(uint16_t h)
+{
+    const int sign = h >> 15, e = (h >> 10) & 31, m = h & 1023;
+    double v;
+    if (e == 31)
+        v = m ? NAN : INFINITY;
+    else if (e == 0)
+        v = ldexp((double)m, -24); /* subnormal: m * 2^-24 */
+    else
+        v = ldexp((double)(m + 1024), e - 25); /* (1 + m/1024) * 2^(e-15) */
+    return (float)(sign ? -v : v);
+}
+
+static uint16_t float_to_bf16_bits(float f)
+{
+    uint32_t u;
+    if (isnan(f))
+        return 0x7FC0; /* the positive canonical quiet NaN */
+    memcpy(&u, &f, 4);
+    /* round to nearest, ties to even, on the 16 bits that are dropped */
+    const uint32_t dropped = u & 0xFFFF, kept = u >> 16;
+    if (dropped > 0x8000 || (dropped == 0x8000 && (kept & 1)))
+        return (uint16_t)(kept + 1); /* a carry into the exponent is exact */
+    return (uint16_t)kept;
+}
+
+static uint16_t float_to_f16_bits(float f)
+{
+    uint16_t sign;
+    double a;
+    int e;
+    if (isnan(f))
+        return 0x7E00; /* the positive canonical quiet NaN */
+    sign = signbit(f) ? 0x8000 : 0;
+    a = fabs((double)f);
+    if (a == 0.0)
+        return sign;
+    if (a >= 65520.0) /* half-way between 65504 and 2^16 rounds to the even 2^16 */
+        return sign | 0x7C00;
+    frexp(a, &e); /* a = m * 2^e, 0.5 <= m < 1: the leading bit is 2^(e-1) */
+    if (e - 1 < -14) {
+        /* subnormal range: count units of 2^-24; 1024 units is the smallest
+         * normal, whose encoding is the same integer */
+        const double q = nearbyint(ldexp(a, 24));
+        return sign | (uint16_t)q;
+    }
+    {
+        /* 11 significant bits: q in [1024, 2048] */
+        double q = nearbyint(ldexp(a, 10 - (e - 1)));
+        int ex = e - 1;
+        if (q == 2048.0) {
+            q = 1024.0;
+            ex += 1;
+        }
+        if (ex > 15)
+            return sign | 0x7C00;
+        return sign | (uint16_t)((ex + 15) << 10) | (uint16_t)(q - 1024.0);
+    }
+}
+
+static float xf_load(int type, const char *row, int64_t i)
+{
+    uint16_t h;
+    float f;
+    switch (type) {
+    case ORC_XF_F32:
+        memcpy(&f, row + 4 * i, 4);
+        return f;
+    case ORC_XF_F16:
+        memcpy(&h, row + 2 * i, 2);
+        return f16_bits_to_float(h);
+    default: /* ORC_XF_BF16 */
+        memcpy(&h, row + 2 * i, 2);
+        return bf16_bits_to_float(h);
+    }
+}
+
+/* [PF]: saturate(round_half_even(y / scale) + zero_point); NaN -> zero_point */
+static int32_t xf_quantize(float y, float scale, int32_t zero_point, int32_t lo, int32_t hi)
+{
+    float q;
+    if (isnan(y))
+        return zero_point;
+    q = nearbyintf(y / scale) + (float)zero_point; /* default rounding: ties to even */
+    if (q < (float)lo)
+        return lo;
+    if (q > (float)hi)
+        return hi;
+    return (int32_t)q;
+}
+
+static void xf_store(const orc_row_xf *x, int t, char *row, int64_t i, float y)
+{
+    uint16_t h;
+    int32_t lo, hi, q;
+    switch (x->out_type) {
+    case ORC_XF_F32:
+        memcpy(row + 4 * i, &y, 4);
+        break;
+    case ORC_XF_F16:
+        h = float_to_f16_bits(y);
+        memcpy(row + 2 * i, &h, 2);
+        break;
+    case ORC_XF_BF16:
+        h = float_to_bf16_bits(y);
+        memcpy(row + 2 * i, &h, 2);
+        break;
+    default: /* ORC_XF_INT8, ORC_XF_UINT8 */
+        xf_code_range(x->out_type, &lo, &hi);
+        q = xf_quantize(y, x->scale[t], x->zero_point[t], lo, hi);
+        if (x->out_type == ORC_XF_INT8) {
+            const int8_t c = (int8_t)q;
+            memcpy(row + i, &c, 1);
+        } else {
+            const uint8_t c = (uint8_t)q;
+            memcpy(row + i, &c, 1);
+        }
+        break;
+    }
+}
+
+int orc_xf_row(const orc_row_xf *x, int t, int64_t pos, const void *in, void *out,
+               int64_t head_dim)
+{
+    float *v;
+    if (head_dim < 0 || (t != 0 && t != 1) || !xf_valid(x, head_dim))
+        return ORC_E_INVALID_ARG;
+    if (head_dim == 0)
+        return ORC_OK;
+    if (!in || !out)
+        return ORC_E_INVALID_ARG;
+    if (t == 0 && x->cos_table && (pos < 0 || pos >= x->max_position))
+        return ORC_E_INVALID_ARG;
+    v = (float *)malloc((size_t)head_dim * sizeof(float));
+    if (!v)
+        return ORC_E_INVALID_ARG;
+    for (int64_t i = 0; i < head_dim; ++i)
+        v[i] = xf_load(x->in_type, (const char *)in, i);
+    if (t == 0 && x->cos_table) {
+        /* [GQA-ROPE] RoPE at the absolute position: each pair (x0, x1) turns
+         * by the angle whose cosine and sine are table row pos, column j */
+        const int64_t half = x->rotary_dim / 2;
+        const float *c = x->cos_table + pos * half;
+        const float *s = x->sin_table + pos * half;
+        for (int64_t j = 0; j < half; ++j) {
+            const int64_t i0 = x->interleaved ? 2 * j : j;
+            const int64_t i1 = x->interleaved ? 2 * j + 1 : j + half;
+            const float x0 = v[i0], x1 = v[i1];
+            const float x0c = x0 * c[j], x1s = x1 * s[j];
+            const float x1c = x1 * c[j], x0s = x0 * s[j];
+            v[i0] = x0c - x1s;
+            v[i1] = x1c + x0s;
+        }
+    }
+    for (int64_t i = 0; i < head_dim; ++i)
+        xf_store(x, t, (char *)out, i, v[i]);
+    free(v);
+    return ORC_OK;
+}
+
+/* the positions [p0, p0 + n) all have table rows (or nothing rotates) */
+static int xf_positions_ok(const orc_row_xf *x, int64_t p0, int64_t n)
+{
+    return !x->cos_table || (p0 >= 0 && p0 <= x->max_position - n);
+}
+
+int orc_kv_window_append_xf(void *k_cache, void *v_cache, const void *k_new,
+                            const void *v_new, const int64_t *new_strides,
+                            void *k_staging, void *v_staging,
+                            const int32_t *cache_past_lens,
+                            const int32_t *evict_counts, const int64_t *past_lens,
+                            int64_t batch, int64_t kv_heads, int64_t capacity,
+                            int64_t seq_len, int64_t head_dim, unsigned phase,
+                            const orc_row_xf *x, uint32_t *flags)
+{
+    const int64_t B = batch, H = kv_heads, C = capacity, S = seq_len, D = head_dim;
+    int64_t in_es, out_row, rows_strides[3];
+    const char *news[2] = {(const char *)k_new, (const char *)v_new}; /* K, V */
+    char *tmp[2];
+    int status = ORC_OK;
+
+    if (B < 0 || H < 0 || D < 0 || C < 1 || S < 1 || !xf_valid(x, D))
+        return ORC_E_INVALID_ARG;
+    in_es = xf_elem_bytes(x->in_type);
+    out_row = D * xf_elem_bytes(x->out_type);
+    if (B == 0 || H == 0 || D == 0)
+        return ORC_OK;
+    if (!k_new || !v_new || !new_strides || !past_lens || !cache_past_lens ||
+        !evict_counts || !k_cache || !v_cache)
+        return ORC_E_INVALID_ARG;
+    /* the transformed rows of one batch entry, [1, H, S, D] in out_type */
+    tmp[0] = (char *)malloc((size_t)(H * S * out_row));
+    tmp[1] = (char *)malloc((size_t)(H * S * out_row));
+    rows_strides[0] = H * S * D;
+    rows_strides[1] = S * D;
+    rows_strides[2] = D;
+    if (!tmp[0] || !tmp[1]) {
+        free(tmp[0]);
+        free(tmp[1]);
+        return ORC_E_INVALID_ARG;
+    }
+    for (int64_t b = 0; b < B && status == ORC_OK; ++b) {
+        const int64_t Lp = cache_past_lens[b], E = evict_counts[b], L = Lp + S - E;
+        if (L < 1 || L > C || E < 0 || Lp < 0 || Lp > C) {
+            set_flag(flags, ORC_FLAG_BAD_LENGTHS); /* as orc_kv_window_append */
+            continue;
+        }
+        if (!xf_positions_ok(x, past_lens[b], S)) {
+            set_flag(flags, ORC_FLAG_ROPE_RANGE);
+            continue; /* this batch entry keeps every byte it had */
+        }
+        for (int t = 0; t < 2 && status == ORC_OK; ++t)
+            for (int64_t h = 0; h < H && status == ORC_OK; ++h)
+                for (int64_t s = 0; s < S && status == ORC_OK; ++s)
+                    status = orc_xf_row(x, t, past_lens[b] + s,
+                                        news[t] + (b * new_strides[0] + h * new_strides[1] +
+                                                   s * new_strides[2]) * in_es,
+                                        tmp[t] + (h * S + s) * out_row, D);
+        if (status != ORC_OK)
+            break;
+        /* then the plain step for this one batch entry, on out_type rows */
+        status = orc_kv_window_append(
+            (char *)k_cache + b * H * C * out_row, (char *)v_cache + b * H * C * out_row,
+            tmp[0], tmp[1], rows_strides,
+            S > 1 ? (char *)k_staging + b * H * (C + S) * out_row : NULL,
+            S > 1 ? (char *)v_staging + b * H * (C + S) * out_row : NULL,
+            cache_past_lens + b, evict_counts + b, 1, H, C, S, D,
+            (int)(xf_elem_bytes(x->out_type) * 8), phase, flags);
+    }
+    free(tmp[0]);
+    free(tmp[1]);
+    return status;
+}
+
+int orc_tensor_scatter_xf(void *present, const void *past, const void *update,
+                          const int64_t *write_indices, const int64_t *shape,
+                          int rank, int64_t seq_len, int mode, int t,
+                          const orc_row_xf *x, uint32_t *flags)
+{
+    int64_t D, M, O1 = 1, in_es, out_es, block, ushape[ORC_MAX_RANK];
+    int64_t B;
+    char *tmp;
+    int status = ORC_OK;
+
+    if (rank < 3 || rank > ORC_MAX_RANK || !shape || (t != 0 && t != 1))
+        return ORC_E_INVALID_ARG;
+    D = shape[rank - 1];
+    M = shape[rank - 2];
+    B = shape[0];
+    if (!xf_valid(x, D) || seq_len < 0 || seq_len > M)
+        return ORC_E_INVALID_ARG;
+    for (int i = 0; i < rank; ++i)
+        if (shape[i] < 0)
+            return ORC_E_INVALID_ARG;
+    for (int i = 1; i < rank - 2; ++i)
+        O1 *= shape[i]; /* prefixes per batch entry */
+    in_es = xf_elem_bytes(x->in_type);
+    out_es = xf_elem_bytes(x->out_type);
+    block = O1 * M * D * out_es; /* one batch entry of present / past */
+    if (B == 0 || O1 == 0 || M == 0 || D == 0)
+        return ORC_OK;
+    if (!present || !past || (seq_len > 0 && !update))
+        return ORC_E_INVALID_ARG;
+    for (int i = 0; i < rank; ++i)
+        ushape[i] = shape[i];
+    ushape[0] = 1;
+    tmp = (char *)malloc((size_t)(O1 * (seq_len ? seq_len : 1) * D * out_es));
+    if (!tmp)
+        return ORC_E_INVALID_ARG;
+    for (int64_t b = 0; b < B && status == ORC_OK; ++b) {
+        const int64_t w = write_indices ? write_indices[b] : 0;
+        char *pres = (char *)present + b * block;
+        const char *pst = (const char *)past + b * block;
+        const int linear_ok = mode != ORC_MODE_LINEAR || (w >= 0 && w <= M - seq_len);
+        if (linear_ok && !xf_positions_ok(x, w, seq_len)) {
+            set_flag(flags, ORC_FLAG_ROPE_RANGE);
+            if (pres != pst)
+                memcpy(pres, pst, (size_t)block); /* the entry keeps past's rows */
+            continue;
+        }
+        /* the entry's update rows, transformed at positions w + s */
+        for (int64_t o = 0; o < O1 && linear_ok && status == ORC_OK; ++o)
+            for (int64_t s = 0; s < seq_len && status == ORC_OK; ++s)
+                status = orc_xf_row(x, t, w + s,
+                                    (const char *)update + ((b * O1 + o) * seq_len + s) * D * in_es,
+                                    tmp + (o * seq_len + s) * D * out_es, D);
+        if (status != ORC_OK)
+            break;
+        /* then plain TensorScatter of this one entry on out_type rows */
+        status = orc_tensor_scatter(pres, pst, tmp, write_indices ? write_indices + b : NULL,
+                                    ushape, rank, rank - 2, seq_len, mode,
+                                    (int)(out_es * 8), flags);
+    }
+    free(tmp);
+    return status;
 }

@@ -20,6 +20,14 @@
  *   [GQA-CPU] the same pull request's CPU follow-up description, section "Key
  *         design decisions": the drifting layout (gap, end pointer, one
  *         compaction per gap decode steps).
+ *   [GQA-ROPE] the same pull request's "Summary of Changes": the KV append
+ *         writes at the cache-relative offset while RoPE keeps the absolute
+ *         position, bounded by its own maximum position, not by the capacity.
+ *   [PF]  onnx-light how-to "Persistent input/output feedback", section
+ *         "Optional heterogeneous paged KV" ("Selected-block quantization",
+ *         "Serialized cache values"): affine INT8/UINT8 codes with FLOAT
+ *         scales, scalar parameters on append, rounding ties to even and
+ *         saturating to the code range.
  *
  * Every function is a plain definition: scalar loops, one memcpy per row, no
  * blocking, no vector code, no threads.
@@ -42,6 +50,7 @@ extern "C" {
 #define ORC_FLAG_LINEAR_OOB 1u  /* a linear write index left [0, M-S]; batch skipped */
 #define ORC_FLAG_BAD_SEQLEN 2u  /* seqlens_k[b] < 0 or total length < S; clamped   */
 #define ORC_FLAG_BAD_LENGTHS 4u /* (Lp, E) inconsistent with (C, S); batch skipped */
+#define ORC_FLAG_ROPE_RANGE 8u  /* a rotary position outside [0, max); batch skipped */
 
 /* TensorScatter "mode" attribute */
 #define ORC_MODE_LINEAR 0
@@ -107,6 +116,74 @@ int orc_kv_window_append(void *k_cache, void *v_cache, const void *k_new,
                          int64_t kv_heads, int64_t capacity, int64_t seq_len,
                          int64_t head_dim, int elem_bits, unsigned phase,
                          uint32_t *flags);
+
+/* ------------------------------------------------------------------------ */
+/* the row transform of a fused append: RoPE on K, then conversion or affine   */
+/* quantization into the cache's element type                                  */
+/* ------------------------------------------------------------------------ */
+#define ORC_XF_F32 1
+#define ORC_XF_F16 2
+#define ORC_XF_BF16 3
+#define ORC_XF_INT8 4
+#define ORC_XF_UINT8 5
+
+typedef struct {
+    int in_type;            /* new rows: ORC_XF_F32, ORC_XF_F16 or ORC_XF_BF16 */
+    int out_type;           /* cache rows: any ORC_XF_* type */
+    const float *cos_table; /* [max_position, rotary_dim / 2]; NULL: no rotation */
+    const float *sin_table; /* same shape; NULL exactly when cos_table is */
+    int64_t max_position;   /* rows of the tables */
+    int64_t rotary_dim;     /* even, 2 .. head_dim; later elements pass unrotated */
+    int interleaved;        /* 0: pairs (j, j + rotary_dim/2); 1: pairs (2j, 2j+1) */
+    float scale[2];         /* K, V scales: positive and finite (integer out_type) */
+    int32_t zero_point[2];  /* K, V zero points: inside the code range */
+} orc_row_xf;
+
+/*
+ * One row of head_dim elements: read as float, rotate when t == 0 (K) and
+ * tables are given, using table row `pos`; then write in out_type. Every
+ * float operation is one IEEE binary32 operation, rounded to nearest even:
+ *   x0' = fl(fl(x0 * c) - fl(x1 * s)),  x1' = fl(fl(x1 * c) + fl(x0 * s)).
+ * bf16 / f16 outputs round to nearest even (NaN -> the positive canonical
+ * quiet NaN of the type, overflow -> infinity); integer outputs are
+ * saturate(round_half_even(fl(y / scale)) + zero_point), NaN -> zero_point.
+ * Returns ORC_E_INVALID_ARG on a bad transform or a position outside the
+ * tables.
+ */
+int orc_xf_row(const orc_row_xf *x, int t, int64_t pos, const void *in, void *out,
+               int64_t head_dim);
+
+/*
+ * [GQA] + [GQA-ROPE] + [PF]: orc_kv_window_append whose new rows (in_type,
+ * new_strides in elements) first pass through the transform, row s of batch
+ * entry b at absolute position past_lens[b] + s; caches and staging hold
+ * out_type rows. A batch entry whose lengths do not fit is flagged
+ * BAD_LENGTHS and skipped; then one whose positions leave [0, max_position)
+ * (rotation on) is flagged ROPE_RANGE and skipped.
+ */
+int orc_kv_window_append_xf(void *k_cache, void *v_cache, const void *k_new,
+                            const void *v_new, const int64_t *new_strides,
+                            void *k_staging, void *v_staging,
+                            const int32_t *cache_past_lens,
+                            const int32_t *evict_counts, const int64_t *past_lens,
+                            int64_t batch, int64_t kv_heads, int64_t capacity,
+                            int64_t seq_len, int64_t head_dim, unsigned phase,
+                            const orc_row_xf *x, uint32_t *flags);
+
+/*
+ * [TS] + [GQA-ROPE] + [PF]: TensorScatter with axis = rank - 2 (a row is the
+ * last dimension, head_dim) whose update rows (in_type) pass through the
+ * transform first, update row s of batch entry b at absolute position
+ * write_indices[b] + s (before any circular wrap). present / past hold
+ * out_type rows. `t` selects K (0: rotated) or V (1). A linear entry out of
+ * range is flagged LINEAR_OOB and skipped; then an entry whose positions leave
+ * [0, max_position) (rotation on) is flagged ROPE_RANGE and skipped (keeping
+ * past's rows).
+ */
+int orc_tensor_scatter_xf(void *present, const void *past, const void *update,
+                          const int64_t *write_indices, const int64_t *shape,
+                          int rank, int64_t seq_len, int mode, int t,
+                          const orc_row_xf *x, uint32_t *flags);
 
 #ifdef __cplusplus
 }

@@ -3,7 +3,8 @@
 Each mutant below is a copy of oracle/swrt_oracle.c with one planted mistake
 (an index off by one, a dropped term, a wrong sign, a transposed operand, a
 step done in the wrong order, a check weakened). The mutant is compiled with
-gcc and the whole pin suite (tests/test_oracle_pins.py) runs against it in its
+gcc and the whole pin suite (tests/test_oracle_pins.py and
+tests/test_oracle_xf_pins.py) runs against it in its
 own process; the suite must fail for every mutant. A mutant that crashes its
 process counts as caught. Everything runs on the CPU.
 """
@@ -65,6 +66,56 @@ MUTANTS = {
     "drift_floor_not_ceil": ("(x - C + gap - 1) / gap", "(x - C) / gap"),
     "drift_end_off_by_one": ("L = drift_end(P + S, C, gap);", "L = drift_end(P + S, C, gap) - 1;"),
     "drift_past_from_total": ("Lp = drift_end(P, C, gap);", "Lp = drift_end(P + S, C, gap);"),
+    # the fused append's row transform
+    "xf_k_and_v_swapped": ("{(const char *)k_new, (const char *)v_new}; /* K, V */",
+                           "{(const char *)v_new, (const char *)k_new}; /* K, V */"),
+    "xf_lengths_checked_after_positions": ("if (L < 1 || L > C || E < 0 || Lp < 0 || Lp > C)",
+                                           "if (0)"),
+    "rope_first_sign": ("v[i0] = x0c - x1s;", "v[i0] = x0c + x1s;"),
+    "rope_second_sign": ("v[i1] = x1c + x0s;", "v[i1] = x1c - x0s;"),
+    "rope_wrong_partner": ("x->interleaved ? 2 * j + 1 : j + half;",
+                           "x->interleaved ? 2 * j + 1 : half - 1 - j;"),
+    "rope_interleaved_as_half_split": ("const int64_t i0 = x->interleaved ? 2 * j : j;",
+                                       "const int64_t i0 = j;"),
+    "rope_next_table_row": ("const float *c = x->cos_table + pos * half;",
+                            "const float *c = x->cos_table + (pos + 1) * half;"),
+    "rope_sin_column_swapped": ("const float *s = x->sin_table + pos * half;",
+                                "const float *s = x->cos_table + pos * half;"),
+    "rope_rotates_v": ("if (t == 0 && x->cos_table) {\n        /* [GQA-ROPE]",
+                       "if (x->cos_table) {\n        /* [GQA-ROPE]"),
+    "rope_tail_rotated": ("const int64_t half = x->rotary_dim / 2;",
+                          "const int64_t half = head_dim / 2;"),
+    "rope_position_cache_relative": ("status = orc_xf_row(x, t, past_lens[b] + s,",
+                                     "status = orc_xf_row(x, t, cache_past_lens[b] + s,"),
+    "rope_position_ignores_s": ("status = orc_xf_row(x, t, past_lens[b] + s,",
+                                "status = orc_xf_row(x, t, past_lens[b],"),
+    "scatter_position_wrapped": ("status = orc_xf_row(x, t, w + s,",
+                                 "status = orc_xf_row(x, t, floor_mod(w + s, M),"),
+    "rope_range_off_by_one": ("(p0 >= 0 && p0 <= x->max_position - n)",
+                              "(p0 >= 0 && p0 <= x->max_position - n + 1)"),
+    "rope_range_not_flagged": ("set_flag(flags, ORC_FLAG_ROPE_RANGE);\n            continue;",
+                               "continue;"),
+    "quant_round_half_up": ("q = nearbyintf(y / scale) + (float)zero_point;",
+                            "q = floorf(y / scale + 0.5f) + (float)zero_point;"),
+    "quant_zero_point_subtracted": ("q = nearbyintf(y / scale) + (float)zero_point;",
+                                    "q = nearbyintf(y / scale) - (float)zero_point;"),
+    "quant_truncates": ("q = nearbyintf(y / scale) + (float)zero_point;",
+                        "q = truncf(y / scale) + (float)zero_point;"),
+    "quant_high_code_wraps": ("        *hi = 127;", "        *hi = 128;"),
+    "quant_nan_to_low_code": ("if (isnan(y))\n        return zero_point;",
+                              "if (isnan(y))\n        return lo;"),
+    "quant_v_uses_k_parameters": ("q = xf_quantize(y, x->scale[t], x->zero_point[t], lo, hi);",
+                                  "q = xf_quantize(y, x->scale[0], x->zero_point[0], lo, hi);"),
+    "bf16_ties_away": ("if (dropped > 0x8000 || (dropped == 0x8000 && (kept & 1)))",
+                       "if (dropped >= 0x8000)"),
+    "bf16_truncates": ("if (dropped > 0x8000 || (dropped == 0x8000 && (kept & 1)))", "if (0)"),
+    "f16_rounding_carry_lost": ("if (q == 2048.0) {", "if (q > 2048.0) {"),
+    "f16_subnormal_unit": ("const double q = nearbyint(ldexp(a, 24));",
+                           "const double q = nearbyint(ldexp(a, 23));"),
+    "f16_exponent_bias": ("return sign | (uint16_t)((ex + 15) << 10)",
+                          "return sign | (uint16_t)((ex + 14) << 10)"),
+    "f16_decode_subnormal": ("v = ldexp((double)m, -24);", "v = ldexp((double)m, -25);"),
+    "bf16_decode_shift": ("uint32_t u = (uint32_t)h << 16;", "uint32_t u = (uint32_t)h << 15;"),
 }
 
 # write before shift (the opposite of the order the step formulas list)
@@ -95,7 +146,8 @@ MUTANTS["write_before_shift"] = (_SHIFT_THEN_WRITE, _WRITE_THEN_SHIFT)
 def _run_pins(lib: str) -> subprocess.CompletedProcess:
     env = dict(os.environ, SWRT_ORACLE_LIB=lib, PYTHONDONTWRITEBYTECODE="1")
     return subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                           os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                           os.path.join(ROOT, "tests", "test_oracle_pins.py"),
+                           os.path.join(ROOT, "tests", "test_oracle_xf_pins.py")],
                           cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
 
 
@@ -107,8 +159,8 @@ def test_every_mutant_fails_the_pins(tmp_path):
         path = tmp_path / f"{name}.c"
         path.write_text(src.replace(old, new))
         lib = str(tmp_path / f"lib_{name}.so")
-        subprocess.run(["gcc", "-O1", "-std=c11", "-shared", "-fPIC",
-                        f"-I{os.path.dirname(oracle.SOURCE)}", str(path), "-o", lib],
+        subprocess.run(["gcc", "-O1", "-std=c11", "-ffp-contract=off", "-shared", "-fPIC",
+                        f"-I{os.path.dirname(oracle.SOURCE)}", str(path), "-o", lib, "-lm"],
                        check=True, capture_output=True)
         builds[name] = lib
     with ThreadPoolExecutor(max_workers=4) as ex:
