@@ -36,8 +36,10 @@
  *     wrap; an entry with a position outside the tables is flagged and
  *     skipped whole, K and V alike.
  *   - [PF] fixes rounding (ties to even) and saturation of affine codes but
- *     not NaN: NaN takes the zero point; half-precision outputs store NaN as
- *     the positive canonical quiet NaN.
+ *     not NaN: NaN takes the zero point; float outputs (binary32 and the half
+ *     types) store any NaN as the positive canonical quiet NaN, since the sign
+ *     and payload a NaN carries out of float arithmetic differ between
+ *     processors.
  */
 #include "swrt_oracle.h"
 
@@ -528,7 +530,12 @@ static void xf_store(const orc_row_xf *x, int t, char *row, int64_t i, float y)
     int32_t lo, hi, q;
     switch (x->out_type) {
     case ORC_XF_F32:
-        memcpy(row + 4 * i, &y, 4);
+        if (isnan(y)) {
+            const uint32_t canonical = 0x7FC00000u; /* sign and payload are not fixed */
+            memcpy(row + 4 * i, &canonical, 4);
+        } else {
+            memcpy(row + 4 * i, &y, 4);
+        }
         break;
     case ORC_XF_F16:
         h = float_to_f16_bits(y);

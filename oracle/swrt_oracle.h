@@ -144,8 +144,9 @@ typedef struct {
  * tables are given, using table row `pos`; then write in out_type. Every
  * float operation is one IEEE binary32 operation, rounded to nearest even:
  *   x0' = fl(fl(x0 * c) - fl(x1 * s)),  x1' = fl(fl(x1 * c) + fl(x0 * s)).
- * bf16 / f16 outputs round to nearest even (NaN -> the positive canonical
- * quiet NaN of the type, overflow -> infinity); integer outputs are
+ * bf16 / f16 outputs round to nearest even (overflow -> infinity); every
+ * float output stores NaN as the positive canonical quiet NaN of its type;
+ * integer outputs are
  * saturate(round_half_even(fl(y / scale)) + zero_point), NaN -> zero_point.
  * Returns ORC_E_INVALID_ARG on a bad transform or a position outside the
  * tables.

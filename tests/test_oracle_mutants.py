@@ -106,6 +106,8 @@ MUTANTS = {
                               "if (isnan(y))\n        return lo;"),
     "quant_v_uses_k_parameters": ("q = xf_quantize(y, x->scale[t], x->zero_point[t], lo, hi);",
                                   "q = xf_quantize(y, x->scale[0], x->zero_point[0], lo, hi);"),
+    "f32_nan_payload_kept": ("if (isnan(y)) {\n            const uint32_t canonical",
+                             "if (0) {\n            const uint32_t canonical"),
     "bf16_ties_away": ("if (dropped > 0x8000 || (dropped == 0x8000 && (kept & 1)))",
                        "if (dropped >= 0x8000)"),
     "bf16_truncates": ("if (dropped > 0x8000 || (dropped == 0x8000 && (kept & 1)))", "if (0)"),

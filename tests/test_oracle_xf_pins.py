@@ -109,6 +109,19 @@ def test_f16_output_rounds_like_numpy(orc):
     assert nan.view(np.uint16)[0] == 0x7E00
 
 
+def test_float32_nan_is_canonical(orc):
+    """Any NaN, whatever its sign and payload, is stored as 0x7FC00000."""
+    nans = np.array([0x7FC00000, 0xFFC00000, 0x7F800001, 0xFFFFFFFF, 0x7FA12345], np.uint32)
+    got = row_out(orc, Transform(XF_F32, XF_F32), 1, 0, nans.view(np.float32))
+    np.testing.assert_array_equal(got.view(np.uint32), [0x7FC00000] * 5)
+    h = row_out(orc, Transform(XF_F16, XF_F32), 1, 0, np.uint16([0xFE01, 0x7C01]).view(np.float16))
+    np.testing.assert_array_equal(h.view(np.uint32), [0x7FC00000] * 2)
+    # a NaN made by the rotation itself (inf * 0) as well
+    cos, sin = np.float32([[0.0]]), np.float32([[1.0]])
+    r = row_out(orc, Transform(XF_F32, XF_F32, cos, sin, 2), 0, 0, np.float32([np.inf, 0.0]))
+    assert r.view(np.uint32)[0] == 0x7FC00000
+
+
 def test_inputs_decode_exactly(orc):
     every = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     f16 = row_out(orc, Transform(XF_F16, XF_F32), 1, 0, every.view(np.float16))
