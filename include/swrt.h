@@ -22,7 +22,10 @@
  *                          it, for K and V in one launch; in place when S = 1,
  *                          through a C+S staging cache with copy-back when S > 1.
  * plus batched forms of the last two and of TensorScatter (several layers or
- * caches per launch) and swrt_kv_decode_step (all of a decode step at once).
+ * caches per launch) and swrt_kv_decode_step (all of a decode step at once),
+ * and *_xf forms that fuse the row transform of the append into the write:
+ * RoPE on K at the absolute position and conversion or affine quantization
+ * into the cache's element type (swrt_row_transform below).
  *
  * Conventions shared by every entry point
  *   - Ownership: the caller owns every buffer. The library allocates nothing,
@@ -56,7 +59,7 @@
 extern "C" {
 #endif
 
-#define SWRT_ABI_VERSION 2
+#define SWRT_ABI_VERSION 3
 
 /* synchronous status codes */
 #define SWRT_OK 0
@@ -68,6 +71,7 @@ extern "C" {
 #define SWRT_FLAG_LINEAR_OOB 1u   /* linear write index < 0 or > M - S        */
 #define SWRT_FLAG_BAD_SEQLEN 2u   /* seqlens_k[b] < 0 or seqlens_k[b] + 1 < S */
 #define SWRT_FLAG_BAD_LENGTHS 4u  /* (Lp, E) not a step that fits (C, S)      */
+#define SWRT_FLAG_ROPE_RANGE 8u   /* a rotary position outside the tables     */
 
 /* TensorScatter mode attribute */
 #define SWRT_MODE_LINEAR 0
@@ -331,6 +335,123 @@ int swrt_kv_decode_step(int n_window_layers, void *const *win_k_caches,
                         const int64_t *write_indices, int max_seq, int batch,
                         int kv_heads, int head_dim, int elem_bits,
                         uint32_t *d_flags, void *stream);
+
+/*
+ * ---------------------------------------------------------------------------
+ * Fused append: the row transform (pull request "GQA support
+ * sliding_window_cache", "Summary of Changes": the KV append writes at the
+ * cache-relative offset while RoPE keeps the absolute position, bounded by
+ * its own maximum position rather than the capacity; onnx-light how-to
+ * "Persistent input/output feedback", section "Optional heterogeneous paged
+ * KV": affine INT8 / UINT8 codes with FLOAT scales and scalar parameters on
+ * append, ties rounded to even, codes saturated).
+ *
+ * Every new row (head_dim elements of in_type) is read as binary32. A K row
+ * (never a V row) is rotated when tables are given: each pair (x0, x1) --
+ * elements (j, j + rotary_dim/2), or (2j, 2j+1) when interleaved -- becomes
+ *   x0' = x0*c - x1*s,  x1' = x1*c + x0*s,  c = cos_table[pos][j], s = sin_table[pos][j],
+ * each product and sum one binary32 operation rounded to nearest even (no
+ * fused multiply-add); elements from rotary_dim on pass unrotated. Each
+ * element is then written in out_type: F32 as is; F16 / BF16 rounded to
+ * nearest even (overflow to infinity); any NaN of a float type as its
+ * positive canonical quiet NaN (0x7FC00000 / 0x7E00 / 0x7FC0); INT8 / UINT8 as
+ *   clamp(round_half_even(y / scale) + zero_point, code range),
+ * NaN -> zero_point, with y / scale the correctly rounded binary32 quotient.
+ * The positions are absolute: past length + s on the windowed path,
+ * write_indices[b] + s (before any circular wrap) on TensorScatter.
+ * ---------------------------------------------------------------------------
+ */
+#define SWRT_XF_F32 1
+#define SWRT_XF_F16 2
+#define SWRT_XF_BF16 3
+#define SWRT_XF_INT8 4
+#define SWRT_XF_UINT8 5
+
+typedef struct swrt_row_transform {
+  int in_type;             /* new rows: SWRT_XF_F32, _F16 or _BF16 */
+  int out_type;            /* cache: any SWRT_XF_* type */
+  const float *cos_table;  /* device binary32 [max_position, rotary_dim / 2],
+                              or NULL: no rotation */
+  const float *sin_table;  /* same shape; NULL exactly when cos_table is */
+  int64_t max_position;    /* rows of the tables, >= 1 when rotating */
+  int64_t rotary_dim;      /* even, 2 .. head_dim when rotating */
+  int interleaved;         /* 0: pairs (j, j + rotary_dim/2); 1: (2j, 2j+1) */
+  float scale[2];          /* K, V: positive, finite (integer out_type) */
+  int32_t zero_point[2];   /* K, V: inside the code range (integer out_type) */
+} swrt_row_transform;
+
+/*
+ * swrt_kv_window_append_xf -- swrt_kv_window_append_layers whose new rows
+ * pass through *xf on their way into the caches (and staging): row s of
+ * batch entry b sits at absolute position past_lens[b] + s. Caches and
+ * staging hold out_type elements; new rows are in_type elements addressed by
+ * new_strides (in elements). The shift moves cache rows unchanged.
+ *
+ * past_lens  device int64[batch]: the absolute past length P of
+ *            swrt_kv_seq_lengths (or _drift) with the same S.
+ * xf         host pointer, read during the call only. The tables must not
+ *            overlap any written buffer.
+ * d_flags    as for swrt_kv_window_append, and then SWRT_FLAG_ROPE_RANGE when
+ *            rotating and P < 0 or P + S > max_position: that batch entry is
+ *            left untouched, K and V, cache and staging (every phase checks).
+ * Errors: SWRT_E_INVALID_ARG also for a transform outside the ranges above.
+ */
+int swrt_kv_window_append_xf(int n_layers, void *const *k_caches,
+                             void *const *v_caches, const void *const *k_news,
+                             const void *const *v_news,
+                             const int64_t *new_strides,
+                             void *const *k_stagings, void *const *v_stagings,
+                             const int32_t *cache_past_lens,
+                             const int32_t *evict_counts,
+                             const int64_t *past_lens, int batch, int kv_heads,
+                             int capacity, int seq_len, int head_dim,
+                             unsigned phase, const swrt_row_transform *xf,
+                             uint32_t *d_flags, void *stream);
+
+/*
+ * swrt_tensor_scatter_xf -- swrt_tensor_scatter_batched with axis = rank - 2
+ * (a row is the last dimension, head_dim) whose update rows (in_type) pass
+ * through *xf: update row s of batch entry b at absolute position
+ * write_indices[b] + s, before the circular wrap. present / past hold
+ * out_type elements. tensors[i] is 0 for a K cache (rotated) and 1 for a V
+ * cache; tensors is a host int[n_tensors]. rank 3 .. SWRT_MAX_RANK.
+ * d_flags: SWRT_FLAG_LINEAR_OOB as for TensorScatter, and then
+ * SWRT_FLAG_ROPE_RANGE (rotating, w_b < 0 or w_b + S > max_position): that
+ * batch entry keeps past's rows in every tensor of the call.
+ */
+int swrt_tensor_scatter_xf(int n_tensors, void *const *presents,
+                           const void *const *pasts, const void *const *updates,
+                           const int *tensors, const int64_t *write_indices,
+                           const int64_t *shape, int rank, int64_t seq_len,
+                           int mode, const swrt_row_transform *xf,
+                           uint32_t *d_flags, void *stream);
+
+/*
+ * swrt_kv_decode_step_xf -- swrt_kv_decode_step with the row transform fused
+ * into every write: the same bytes as swrt_kv_seq_lengths(_drift), then
+ * swrt_kv_window_append_xf with past_lens = P, then swrt_tensor_scatter_xf on
+ * the full caches (K caches tensor 0, V caches tensor 1, linear mode), in one
+ * launch. Full caches come as n_full_layers K and V pairs
+ * (full_k_caches[i], full_v_caches[i]) with their new rows. Windowed caches
+ * hold out_type elements; new rows are in_type. d_flags as for those calls.
+ */
+int swrt_kv_decode_step_xf(int n_window_layers, void *const *win_k_caches,
+                           void *const *win_v_caches,
+                           const void *const *win_k_new,
+                           const void *const *win_v_new,
+                           const int64_t *win_new_strides,
+                           const int32_t *seqlens_k, int capacity, int window,
+                           int64_t *total_lens, int64_t *past_lens,
+                           int32_t *cache_past_lens, int32_t *cache_total_lens,
+                           int32_t *evict_counts, int n_full_layers,
+                           void *const *full_k_caches,
+                           void *const *full_v_caches,
+                           const void *const *full_k_new,
+                           const void *const *full_v_new,
+                           const int64_t *write_indices, int max_seq,
+                           int batch, int kv_heads, int head_dim,
+                           const swrt_row_transform *xf, uint32_t *d_flags,
+                           void *stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *swrt_status_string(int status);

@@ -18,6 +18,11 @@ sliding_window_cache"):
     kv_window_append_layers(...)   # several layers sharing shapes and lengths
     kv_decode_step(...)            # lengths + windowed layers + full layers, one launch
 
+Fused appends (``Transform``: RoPE on K at the absolute position, then
+conversion or affine INT8 / UINT8 quantization into the cache's dtype):
+
+    kv_window_append_xf(...), tensor_scatter_xf(...), kv_decode_step_xf(...)
+
 Every function has a ``prepare_*`` twin returning a ``PreparedCall``: the
 arguments are checked and marshalled once, and each call of the object only
 adds the current stream. Decode loops use it to keep host cost per step small.
@@ -26,6 +31,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+from dataclasses import dataclass
 from typing import NamedTuple, Sequence
 
 import torch
@@ -36,8 +42,10 @@ __all__ = [
     "kv_window_append_layers", "kv_decode_step",
     "prepare_tensor_scatter", "prepare_tensor_scatter_batched", "prepare_kv_seq_lengths",
     "prepare_kv_window_append_layers", "prepare_kv_decode_step",
+    "Transform", "kv_window_append_xf", "tensor_scatter_xf", "kv_decode_step_xf",
+    "prepare_kv_window_append_xf", "prepare_tensor_scatter_xf", "prepare_kv_decode_step_xf",
     "OK", "E_INVALID_ARG", "E_UNSUPPORTED", "E_LAUNCH",
-    "FLAG_LINEAR_OOB", "FLAG_BAD_SEQLEN", "FLAG_BAD_LENGTHS",
+    "FLAG_LINEAR_OOB", "FLAG_BAD_SEQLEN", "FLAG_BAD_LENGTHS", "FLAG_ROPE_RANGE",
     "PHASE_STAGE", "PHASE_COMMIT", "PHASE_ALL",
 ]
 
@@ -46,12 +54,12 @@ LIBRARY = os.path.join(PKG, "libswrt.so")
 
 # values of include/swrt.h
 OK, E_INVALID_ARG, E_UNSUPPORTED, E_LAUNCH = 0, 1, 2, 3
-FLAG_LINEAR_OOB, FLAG_BAD_SEQLEN, FLAG_BAD_LENGTHS = 1, 2, 4
+FLAG_LINEAR_OOB, FLAG_BAD_SEQLEN, FLAG_BAD_LENGTHS, FLAG_ROPE_RANGE = 1, 2, 4, 8
 MODE_LINEAR, MODE_CIRCULAR = 0, 1
 PHASE_STAGE, PHASE_COMMIT, PHASE_ALL = 1, 2, 3
 MAX_LAYERS = 32
 MAX_BATCHED = 64
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 _PHASES = {"stage": PHASE_STAGE, "commit": PHASE_COMMIT, "all": PHASE_ALL}
 _MODES = {"linear": MODE_LINEAR, "circular": MODE_CIRCULAR}
@@ -66,6 +74,62 @@ class SwrtError(RuntimeError):
 
 
 _lib: ctypes.CDLL | None = None
+
+# element types of a row transform (include/swrt.h SWRT_XF_*)
+XF_TYPES = {torch.float32: 1, torch.float16: 2, torch.bfloat16: 3, torch.int8: 4,
+            torch.uint8: 5}
+
+
+class RowTransform(ctypes.Structure):
+    """The C struct swrt_row_transform."""
+    _fields_ = [("in_type", ctypes.c_int), ("out_type", ctypes.c_int),
+                ("cos_table", ctypes.c_void_p), ("sin_table", ctypes.c_void_p),
+                ("max_position", ctypes.c_int64), ("rotary_dim", ctypes.c_int64),
+                ("interleaved", ctypes.c_int), ("scale", ctypes.c_float * 2),
+                ("zero_point", ctypes.c_int32 * 2)]
+
+
+@dataclass
+class Transform:
+    """Row transform of a fused append: K rows turn by RoPE at their absolute
+    position (when ``cos``/``sin`` are given: float32 [max_position,
+    rotary_dim / 2] device tables), then every element is written in the
+    cache's dtype: float32 / float16 / bfloat16 rounded to nearest even, or an
+    int8 / uint8 affine code round(y / scale) + zero_point (ties to even,
+    saturated) with the K or V scale and zero point."""
+    cos: torch.Tensor | None = None
+    sin: torch.Tensor | None = None
+    interleaved: bool = False
+    k_scale: float = 1.0
+    v_scale: float = 1.0
+    k_zero_point: int = 0
+    v_zero_point: int = 0
+
+    def c(self, in_dtype: torch.dtype, out_dtype: torch.dtype) -> RowTransform:
+        if in_dtype not in (torch.float32, torch.float16, torch.bfloat16):
+            raise SwrtError("new rows must be float32, float16 or bfloat16")
+        if out_dtype not in XF_TYPES:
+            raise SwrtError("caches of a fused append must be float32, float16, bfloat16, int8 "
+                            "or uint8")
+        x = RowTransform()
+        x.in_type, x.out_type = XF_TYPES[in_dtype], XF_TYPES[out_dtype]
+        if (self.cos is None) != (self.sin is None):
+            raise SwrtError("give both rotary tables or neither")
+        if self.cos is not None:
+            for t in (self.cos, self.sin):
+                _contig("rotary table", t)
+                if t.dtype != torch.float32 or t.dim() != 2 or t.shape != self.cos.shape:
+                    raise SwrtError("rotary tables must be float32 [max_position, rotary_dim/2]")
+            x.cos_table, x.sin_table = self.cos.data_ptr(), self.sin.data_ptr()
+            x.max_position = self.cos.shape[0]
+            x.rotary_dim = 2 * self.cos.shape[1]
+        x.interleaved = int(self.interleaved)
+        x.scale[0], x.scale[1] = self.k_scale, self.v_scale
+        x.zero_point[0], x.zero_point[1] = self.k_zero_point, self.v_zero_point
+        return x
+
+    def tables(self) -> tuple:
+        return (self.cos, self.sin)
 
 
 def library_path() -> str:
@@ -94,9 +158,18 @@ def lib() -> ctypes.CDLL:
                                                i32, i32, i32, i32, i32, i32, u32, vp, vp]
     L.swrt_kv_decode_step.argtypes = [i32, vpp, vpp, vpp, vpp, vp, vp, i32, i32, vp, vp, vp, vp,
                                       vp, i32, vpp, vpp, vp, i32, i32, i32, i32, i32, vp, vp]
+    xfp = ctypes.POINTER(RowTransform)
+    L.swrt_kv_window_append_xf.argtypes = [i32, vpp, vpp, vpp, vpp, vp, vpp, vpp, vp, vp, vp,
+                                           i32, i32, i32, i32, i32, u32, xfp, vp, vp]
+    L.swrt_tensor_scatter_xf.argtypes = [i32, vpp, vpp, vpp, vp, vp, vp, i32, i64, i32, xfp, vp,
+                                         vp]
+    L.swrt_kv_decode_step_xf.argtypes = [i32, vpp, vpp, vpp, vpp, vp, vp, i32, i32, vp, vp, vp,
+                                         vp, vp, i32, vpp, vpp, vpp, vpp, vp, i32, i32, i32, i32,
+                                         xfp, vp, vp]
     for name in ("swrt_tensor_scatter", "swrt_tensor_scatter_batched", "swrt_kv_seq_lengths",
                  "swrt_kv_seq_lengths_drift",
                  "swrt_kv_window_append", "swrt_kv_window_append_layers", "swrt_kv_decode_step",
+                 "swrt_kv_window_append_xf", "swrt_tensor_scatter_xf", "swrt_kv_decode_step_xf",
                  "swrt_abi_version"):
         getattr(L, name).restype = ctypes.c_int
     L.swrt_status_string.argtypes = [ctypes.c_int]
@@ -302,7 +375,8 @@ def _new_strides(k_new: torch.Tensor, v_new: torch.Tensor):
     return (ctypes.c_int64 * 3)(*k_new.stride()[:3])
 
 
-def _check_layers(k_caches, v_caches, k_news, v_news):
+def _check_layers(k_caches, v_caches, k_news, v_news, new_dtype: torch.dtype | None = None):
+    """new_dtype: the new rows' dtype when it differs from the caches' (fused append)."""
     n = len(k_caches)
     if not (len(v_caches) == len(k_news) == len(v_news) == n) or not 1 <= n <= MAX_LAYERS:
         raise SwrtError(f"need 1..{MAX_LAYERS} layers with one tensor of each kind")
@@ -315,12 +389,13 @@ def _check_layers(k_caches, v_caches, k_news, v_news):
         _contig("cache", t)
         if t.shape != kc.shape or t.dtype != kc.dtype:
             raise SwrtError("all caches must share shape and dtype")
+    nd = kc.dtype if new_dtype is None else new_dtype
     for a, b in zip(k_news, v_news):
-        if a.shape != (B, H, S, D) or b.shape != (B, H, S, D) or a.dtype != kc.dtype \
-                or b.dtype != kc.dtype or a.stride() != k_news[0].stride() \
+        if a.shape != (B, H, S, D) or b.shape != (B, H, S, D) or a.dtype != nd \
+                or b.dtype != nd or a.stride() != k_news[0].stride() \
                 or b.stride() != k_news[0].stride():
-            raise SwrtError("new rows must be [B, H, S, D] with the caches' dtype and "
-                            "one stride pattern")
+            raise SwrtError("new rows must be [B, H, S, D] in one dtype (the caches' unless "
+                            "fused) and one stride pattern")
     return n, B, H, C, D, S, _new_strides(k_news[0], v_news[0])
 
 
@@ -450,3 +525,164 @@ def kv_decode_step(win_k, win_v, win_k_new, win_v_new, seqlens_k, full_caches, f
     return prepare_kv_decode_step(win_k, win_v, win_k_new, win_v_new, seqlens_k, full_caches,
                                   full_new, write_indices, window=window, out=out,
                                   flags=flags)()
+
+
+# ---------------------------------------------------------------------------
+# fused appends: RoPE on K at the absolute position + conversion / quantization
+# ---------------------------------------------------------------------------
+
+def _check_staging(k_stagings, v_stagings, B, H, C, S, D, dtype):
+    if k_stagings is None or v_stagings is None:
+        raise SwrtError("S > 1 needs k_staging and v_staging [B, H, C + S, D]")
+    for t in (*k_stagings, *v_stagings):
+        _contig("staging", t)
+        if t.shape != (B, H, C + S, D) or t.dtype != dtype:
+            raise SwrtError("staging must be [B, H, C + S, D] with the caches' dtype")
+
+
+def prepare_kv_window_append_xf(k_caches, v_caches, k_news, v_news, cache_past_lens,
+                                evict_counts, past_lens, xf: Transform, *, k_stagings=None,
+                                v_stagings=None, phase: str = "all",
+                                flags: torch.Tensor | None = None) -> PreparedCall:
+    """See ``kv_window_append_xf``."""
+    n, B, H, C, D, S, strides = _check_layers(k_caches, v_caches, k_news, v_news,
+                                              new_dtype=k_news[0].dtype)
+    kc = k_caches[0]
+    x = xf.c(k_news[0].dtype, kc.dtype)
+    everything = [*k_caches, *v_caches, *k_news, *v_news, cache_past_lens, evict_counts,
+                  past_lens, flags, *xf.tables()]
+    if S > 1:
+        _check_staging(k_stagings, v_stagings, B, H, C, S, D, kc.dtype)
+        everything += [*k_stagings, *v_stagings]
+    else:
+        k_stagings = v_stagings = None
+    dev = _device_of(*everything)
+    for t in (cache_past_lens, evict_counts):
+        _contig("lengths", t)
+        if t.dtype != torch.int32 or t.shape != (B,):
+            raise SwrtError("cache_past_lens and evict_counts must be int32 [B]")
+    _contig("past_lens", past_lens)
+    if past_lens.dtype != torch.int64 or past_lens.shape != (B,):
+        raise SwrtError("past_lens must be int64 [B]")
+    args = (n, _ptrs(k_caches), _ptrs(v_caches), _ptrs(k_news), _ptrs(v_news), strides,
+            _ptrs(k_stagings), _ptrs(v_stagings), _ptr(cache_past_lens), _ptr(evict_counts),
+            _ptr(past_lens), B, H, C, S, D, _PHASES[phase], ctypes.byref(x), _ptr(flags))
+    return PreparedCall(lib().swrt_kv_window_append_xf, args, dev, "kv_window_append_xf",
+                        (*everything, x))
+
+
+def kv_window_append_xf(k_caches, v_caches, k_news, v_news, cache_past_lens, evict_counts,
+                        past_lens, xf: Transform, *, k_stagings=None, v_stagings=None,
+                        phase: str = "all", flags: torch.Tensor | None = None) -> None:
+    """``kv_window_append_layers`` whose new rows (float32 / float16 /
+    bfloat16 [B, H, S, D] views) pass through ``xf`` on their way into caches
+    of any transform dtype: row s of entry b at absolute position
+    past_lens[b] + s (``past_lens`` = the lengths' ``past``). An entry whose
+    positions leave the rotary tables is flagged FLAG_ROPE_RANGE and left
+    untouched."""
+    prepare_kv_window_append_xf(k_caches, v_caches, k_news, v_news, cache_past_lens, evict_counts,
+                                past_lens, xf, k_stagings=k_stagings, v_stagings=v_stagings,
+                                phase=phase, flags=flags)()
+
+
+def prepare_tensor_scatter_xf(pasts: Sequence[torch.Tensor], updates: Sequence[torch.Tensor],
+                              tensors: Sequence[int], write_indices: torch.Tensor | None,
+                              xf: Transform, *, mode: str = "linear",
+                              outs: Sequence[torch.Tensor] | None = None,
+                              flags: torch.Tensor | None = None) -> PreparedCall:
+    """See ``tensor_scatter_xf``."""
+    n = len(pasts)
+    if len(updates) != n or len(tensors) != n or not 1 <= n <= MAX_BATCHED:
+        raise SwrtError(f"need 1..{MAX_BATCHED} (past, update, tensor) triples")
+    p0, u0 = pasts[0], updates[0]
+    presents = [torch.empty_like(p) for p in pasts] if outs is None else list(outs)
+    x = xf.c(u0.dtype, p0.dtype)
+    dev = _device_of(*pasts, *updates, *presents, write_indices, flags, *xf.tables())
+    if p0.dim() < 3:
+        raise SwrtError("a fused TensorScatter needs rank >= 3 ([..., M, head_dim])")
+    for p, u, o in zip(pasts, updates, presents):
+        for name, t in (("past", p), ("update", u), ("out", o)):
+            _contig(name, t)
+        if p.shape != p0.shape or o.shape != p0.shape or u.shape != u0.shape or \
+                p.dtype != p0.dtype or o.dtype != p0.dtype or u.dtype != u0.dtype:
+            raise SwrtError("every past/out must share one shape and dtype, every update too")
+    if u0.dim() != p0.dim() or u0.shape[:-2] != p0.shape[:-2] or u0.shape[-1] != p0.shape[-1]:
+        raise SwrtError("updates must be [..., S, head_dim] with the caches' other dims")
+    if write_indices is not None:
+        _contig("write_indices", write_indices)
+        if write_indices.dtype != torch.int64:
+            raise SwrtError("write_indices must be int64")
+    rank = p0.dim()
+    shape = (ctypes.c_int64 * rank)(*p0.shape)
+    tens = (ctypes.c_int * n)(*[int(t) for t in tensors])
+    args = (n, _ptrs(presents), _ptrs(pasts), _ptrs(updates), tens, _ptr(write_indices), shape,
+            rank, u0.shape[-2], _MODES[mode], ctypes.byref(x), _ptr(flags))
+    keep = (*pasts, *updates, *presents, write_indices, flags, *xf.tables(), x, tens, shape)
+    return PreparedCall(lib().swrt_tensor_scatter_xf, args, dev, "tensor_scatter_xf", keep,
+                        presents)
+
+
+def tensor_scatter_xf(pasts, updates, tensors, write_indices, xf: Transform, *,
+                      mode: str = "linear", outs=None, flags=None) -> list:
+    """TensorScatter along axis -2 (caches [..., M, head_dim]) whose update
+    rows pass through ``xf``: row s of batch entry b at absolute position
+    write_indices[b] + s (before the circular wrap). ``tensors[i]`` is 0 for a
+    K cache (rotated) and 1 for a V cache. ``outs=pasts`` updates in place."""
+    return prepare_tensor_scatter_xf(pasts, updates, tensors, write_indices, xf, mode=mode,
+                                     outs=outs, flags=flags)()
+
+
+def prepare_kv_decode_step_xf(win_k, win_v, win_k_new, win_v_new, seqlens_k, full_k, full_v,
+                              full_k_new, full_v_new, write_indices, xf: Transform, *,
+                              window: int | None = None, out: WindowLengths | None = None,
+                              flags: torch.Tensor | None = None) -> PreparedCall:
+    """See ``kv_decode_step_xf``."""
+    n, B, H, C, D, S, strides = _check_layers(win_k, win_v, win_k_new, win_v_new,
+                                              new_dtype=win_k_new[0].dtype)
+    if S != 1:
+        raise SwrtError("a decode step appends one row (S = 1)")
+    _check_seqlens(seqlens_k)
+    nf = len(full_k)
+    if not (len(full_v) == len(full_k_new) == len(full_v_new) == nf) or \
+            not 0 <= nf <= MAX_BATCHED // 2:
+        raise SwrtError(f"need 0..{MAX_BATCHED // 2} full layers, each with K, V and new rows")
+    cdt, ndt = win_k[0].dtype, win_k_new[0].dtype
+    x = xf.c(ndt, cdt)
+    M = full_k[0].shape[2] if nf else 1
+    for c in (*full_k, *full_v):
+        _contig("full cache", c)
+        if c.shape != (B, H, M, D) or c.dtype != cdt:
+            raise SwrtError("full caches must be [B, H, M, D] in the windowed caches' dtype")
+    for u in (*full_k_new, *full_v_new):
+        _contig("full-cache new rows", u)
+        if u.shape != (B, H, 1, D) or u.dtype != ndt:
+            raise SwrtError("full-cache new rows must be [B, H, 1, D] in the new rows' dtype")
+    if nf:
+        _contig("write_indices", write_indices)
+        if write_indices.dtype != torch.int64 or write_indices.shape != (B,):
+            raise SwrtError("write_indices must be int64 [B]")
+    dev = _device_of(*win_k, *win_v, *win_k_new, *win_v_new, seqlens_k, *full_k, *full_v,
+                     *full_k_new, *full_v_new, write_indices, flags, *xf.tables())
+    out = _new_lengths(B, dev) if out is None else out
+    args = (n, _ptrs(win_k), _ptrs(win_v), _ptrs(win_k_new), _ptrs(win_v_new), strides,
+            _ptr(seqlens_k), C, C if window is None else window, _ptr(out.total), _ptr(out.past),
+            _ptr(out.cache_past), _ptr(out.cache_total), _ptr(out.evict), nf,
+            _ptrs(full_k) if nf else None, _ptrs(full_v) if nf else None,
+            _ptrs(full_k_new) if nf else None, _ptrs(full_v_new) if nf else None,
+            _ptr(write_indices) if nf else None, M, B, H, D, ctypes.byref(x), _ptr(flags))
+    keep = (*win_k, *win_v, *win_k_new, *win_v_new, seqlens_k, *full_k, *full_v, *full_k_new,
+            *full_v_new, write_indices, *out, flags, *xf.tables(), x)
+    return PreparedCall(lib().swrt_kv_decode_step_xf, args, dev, "kv_decode_step_xf", keep, out)
+
+
+def kv_decode_step_xf(win_k, win_v, win_k_new, win_v_new, seqlens_k, full_k, full_v, full_k_new,
+                      full_v_new, write_indices, xf: Transform, *, window: int | None = None,
+                      out: WindowLengths | None = None,
+                      flags: torch.Tensor | None = None) -> WindowLengths:
+    """``kv_decode_step`` with the row transform fused into every write: new
+    rows (float32 / float16 / bfloat16) of the windowed layers at position
+    T - 1, of the full layers (K and V caches given separately) at
+    write_indices[b]; every cache in the transform's output dtype."""
+    return prepare_kv_decode_step_xf(win_k, win_v, win_k_new, win_v_new, seqlens_k, full_k,
+                                     full_v, full_k_new, full_v_new, write_indices, xf,
+                                     window=window, out=out, flags=flags)()

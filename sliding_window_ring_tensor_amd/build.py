@@ -11,6 +11,8 @@ import glob
 import os
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -19,7 +21,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Wall", "-Wno-unused-function",
     # packed-fp32 instructions stay off in every kernel of this library
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -31,12 +33,27 @@ def sources() -> list[str]:
 
 
 def build(out: str = LIBRARY, extra: tuple = (), verbose: bool = False) -> str:
-    """Compile every csrc/*.hip into one shared library; return its path."""
+    """Compile every csrc/*.hip (one compiler process per file, in parallel)
+    and link them into one shared library; return its path."""
     tmp = out + ".tmp"
-    cmd = [HIPCC, *FLAGS, *extra, "-I", os.path.join(ROOT, "include"), *sources(), "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
+    srcs = sources()
+    with tempfile.TemporaryDirectory(prefix="swrt_build_") as objdir:
+        def compile_one(src: str) -> str:
+            obj = os.path.join(objdir, os.path.basename(src) + ".o")
+            cmd = [HIPCC, *FLAGS, *extra, "-I", os.path.join(ROOT, "include"), "-c", src,
+                   "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            subprocess.run(cmd, check=True)
+            return obj
+
+        jobs = max(1, min(len(srcs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))
+        with ThreadPoolExecutor(max_workers=jobs) as pool:
+            objs = list(pool.map(compile_one, srcs))
+        link = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+        if verbose:
+            print(" ".join(link), flush=True)
+        subprocess.run(link, check=True)
     os.replace(tmp, out)
     return out
 

@@ -19,6 +19,9 @@
 // first workgroups (one batch entry per lane) also write the
 // length arrays for the attention that follows. Two kernel boundaries per
 // step disappear, and with them their dispatch and cache-maintenance cost.
+// The XF instances (swrt_kv_decode_step_xf) fuse the row transform of
+// xf_device.hpp into every write: windowed rows at position P = T - 1, full
+// caches at their write index; full caches alternate K and V.
 #include "swrt_host.hpp"
 
 namespace swrt {
@@ -37,15 +40,16 @@ struct DecodeArgs {
   uint32_t full_tiles, full_blocks, win_blocks, len_blocks;
   int32_t batch;
   FastDiv gap;  // capacity - window + 1
+  RowXf xf;     // fused append only
 };
 
 // BLOCK x UNROLL: the window shape (512 x 2 for the base layout; one wave,
 // 64 x 16, for the drifting layout, whose steps are mostly single-row appends).
-// DRIFT: window < capacity (the lengths take the gap).
-template <int VEC, int SPW, int BLOCK, int UNROLL, bool DRIFT>
+// DRIFT: window < capacity (the lengths take the gap). XF: fused append.
+template <int VEC, int SPW, int BLOCK, int UNROLL, bool DRIFT, bool XF>
 __global__ __launch_bounds__(BLOCK) void decode_step_kernel(DecodeArgs a) {
   constexpr uint32_t kFullTile = BLOCK * kScatUnroll;  // full-cache words per workgroup
-  __shared__ TileBatches<kFullTile> tb;
+  __shared__ TileBatches<kFullTile, XF> tb;
   const uint32_t bid = blockIdx.x;
   if (bid < a.len_blocks) {  // the length arrays (no barrier in this part)
     const int32_t b = int32_t(bid * BLOCK + threadIdx.x);
@@ -61,47 +65,64 @@ __global__ __launch_bounds__(BLOCK) void decode_step_kernel(DecodeArgs a) {
   }
   if (bid < a.full_blocks) {  // full caches: TensorScatter rows in place
     const uint32_t t = bid / a.full_tiles;
-    scatter_in_place_tile<VEC, BLOCK>(a.sg, a.fc[t], a.fu[t], (bid - t * a.full_tiles) * kFullTile,
-                                      tb);
+    scatter_in_place_tile<VEC, BLOCK, XF>(a.sg, a.fc[t], a.fu[t],
+                                          (bid - t * a.full_tiles) * kFullTile, tb, &a.xf,
+                                          int(t & 1));
     return;
   }
   const uint32_t wb = bid - a.full_blocks;
   if (wb >= a.win_blocks) return;  // a grid sized by the length arrays alone
   // the window workgroup's slice(s); (Lp, E) from seqlens_k, always a valid pair
-  const auto work = [&](uint32_t slice, int) {
+  const auto work = [&](uint32_t slice, int g) {
     const Slice s = decode_slice(a.wg, slice);
     const StepLengths r = step_lengths<DRIFT>(a.seqlens_k[s.b], 1, a.wg.C, a.gap);
     SliceWork w;
     w.Lp = r.Lp;
     w.E = r.E;
+    w.t = int(s.t);
+    w.pos = r.P;
     w.ok = true;
+    if constexpr (XF) w.ok = positions_ok(a.wg, a.xf, s, threadIdx.x == g * (BLOCK / SPW), r.P);
     w.base = a.wc[s.layer][s.t] + uint64_t(s.b * a.wg.H + s.h) * uint64_t(a.wg.C) * a.wg.row_bytes;
     w.new_row = a.wn[s.layer][s.t] + s.b * a.wg.nb_b + s.h * a.wg.nb_h;
     return w;
   };
   if constexpr (SPW == 1) {
     const SliceWork w = work(wb, 0);
-    shift_append_slice<VEC, BLOCK, UNROLL>(w.base, w.new_row, w.Lp, w.E, a.wg.row_bytes,
-                                           a.wg.row_words);
+    if (!w.ok) return;
+    shift_append_slice<VEC, BLOCK, UNROLL, XF>(w.base, w.new_row, w.Lp, w.E, a.wg.row_bytes,
+                                               a.wg.row_words, &a.xf, w.t, w.pos);
   } else {
-    shift_append_group<VEC, SPW>(wb * SPW, a.wg.slices, a.wg.row_bytes, a.wg.row_words, work);
+    shift_append_group<VEC, SPW, XF>(wb * SPW, a.wg.slices, a.wg.row_bytes, a.wg.row_words, work,
+                                     &a.xf);
   }
 }
 
-template <int VEC>
+template <int VEC, bool XF>
 void launch_decode(const DecodeArgs &a, bool drift, int spw, uint64_t grid, hipStream_t s) {
   if (drift)
-    hipLaunchKernelGGL((decode_step_kernel<VEC, 1, kWaveBlock, kWaveUnroll, true>), dim3(grid),
-                       dim3(kWaveBlock), 0, s, a);
+    hipLaunchKernelGGL((decode_step_kernel<VEC, 1, kWaveBlock, kWaveUnroll, true, XF>),
+                       dim3(grid), dim3(kWaveBlock), 0, s, a);
   else if (spw == 4)
-    hipLaunchKernelGGL((decode_step_kernel<VEC, 4, kWinBlock, kWinUnroll, false>), dim3(grid),
-                       dim3(kWinBlock), 0, s, a);
+    hipLaunchKernelGGL((decode_step_kernel<VEC, 4, kWinBlock, kWinUnroll, false, XF>),
+                       dim3(grid), dim3(kWinBlock), 0, s, a);
   else if (spw == 2)
-    hipLaunchKernelGGL((decode_step_kernel<VEC, 2, kWinBlock, kWinUnroll, false>), dim3(grid),
-                       dim3(kWinBlock), 0, s, a);
+    hipLaunchKernelGGL((decode_step_kernel<VEC, 2, kWinBlock, kWinUnroll, false, XF>),
+                       dim3(grid), dim3(kWinBlock), 0, s, a);
   else
-    hipLaunchKernelGGL((decode_step_kernel<VEC, 1, kWinBlock, kWinUnroll, false>), dim3(grid),
-                       dim3(kWinBlock), 0, s, a);
+    hipLaunchKernelGGL((decode_step_kernel<VEC, 1, kWinBlock, kWinUnroll, false, XF>),
+                       dim3(grid), dim3(kWinBlock), 0, s, a);
+}
+
+template <bool XF>
+void launch_vec(int vec, const DecodeArgs &a, bool drift, int spw, uint64_t grid, hipStream_t s) {
+  switch (vec) {
+    case 16: launch_decode<16, XF>(a, drift, spw, grid, s); break;
+    case 8: launch_decode<8, XF>(a, drift, spw, grid, s); break;
+    case 4: launch_decode<4, XF>(a, drift, spw, grid, s); break;
+    case 2: launch_decode<2, XF>(a, drift, spw, grid, s); break;
+    default: launch_decode<1, XF>(a, drift, spw, grid, s); break;
+  }
 }
 
 }  // namespace
@@ -109,34 +130,40 @@ void launch_decode(const DecodeArgs &a, bool drift, int spw, uint64_t grid, hipS
 
 using namespace swrt;
 
-extern "C" int swrt_kv_decode_step(int n_window_layers, void *const *win_k_caches,
-                                   void *const *win_v_caches, const void *const *win_k_new,
-                                   const void *const *win_v_new, const int64_t *win_new_strides,
-                                   const int32_t *seqlens_k, int capacity, int window,
-                                   int64_t *total_lens,
-                                   int64_t *past_lens, int32_t *cache_past_lens,
-                                   int32_t *cache_total_lens, int32_t *evict_counts, int n_full,
-                                   void *const *full_caches, const void *const *full_new,
-                                   const int64_t *write_indices, int max_seq, int batch,
-                                   int kv_heads, int head_dim, int elem_bits, uint32_t *d_flags,
-                                   void *stream) {
+namespace {
+
+// xf: the fused append (null: plain copies); full caches then alternate K, V
+int decode_step(int n_window_layers, void *const *win_k_caches, void *const *win_v_caches,
+                const void *const *win_k_new, const void *const *win_v_new,
+                const int64_t *win_new_strides, const int32_t *seqlens_k, int capacity, int window,
+                int64_t *total_lens, int64_t *past_lens, int32_t *cache_past_lens,
+                int32_t *cache_total_lens, int32_t *evict_counts, int n_full,
+                void *const *full_caches, const void *const *full_new,
+                const int64_t *write_indices, int max_seq, int batch, int kv_heads, int head_dim,
+                int elem_bits, const swrt_row_transform *xf, uint32_t *d_flags, void *stream) {
   if (batch < 0 || capacity < 1 || n_window_layers < 0 || n_full < 0) return SWRT_E_INVALID_ARG;
   if (window < 1 || window > capacity) return SWRT_E_INVALID_ARG;
   WindowPlan wp{};
   ScatterPlan sp{};
-  Range ranges[6 * kMaxLayers + 3 * kMaxTensors + 12];
+  Range ranges[6 * kMaxLayers + 3 * kMaxTensors + 14];
   int nr = 0;
-  int st = plan_window(n_window_layers, win_k_caches, win_v_caches, win_k_new, win_v_new,
-                       win_new_strides, nullptr, nullptr, nullptr, nullptr, true, batch, kv_heads,
-                       capacity, 1, head_dim, elem_bits, SWRT_PHASE_ALL, d_flags, &wp, ranges,
-                       &nr);
+  RowXf x{};
+  int st;
+  if (xf) {
+    if ((st = plan_xf(xf, head_dim, &x, ranges, &nr)) != SWRT_OK) return st;
+    elem_bits = x.out_bytes * 8;
+  }
+  st = plan_window(n_window_layers, win_k_caches, win_v_caches, win_k_new, win_v_new,
+                   win_new_strides, nullptr, nullptr, nullptr, nullptr, true, batch, kv_heads,
+                   capacity, 1, head_dim, elem_bits, SWRT_PHASE_ALL, d_flags, xf ? &x : nullptr,
+                   &wp, ranges, &nr);
   if (st != SWRT_OK) return st;
   const int64_t shape[4] = {batch, kv_heads, max_seq, head_dim};
   sp.empty = true;
   if (n_full > 0) {
     st = plan_scatter(n_full, full_caches, const_cast<const void *const *>(full_caches), full_new,
-                      write_indices, shape, 4, 2, 1, SWRT_MODE_LINEAR, elem_bits, d_flags, &sp,
-                      ranges, &nr);
+                      write_indices, shape, 4, 2, 1, SWRT_MODE_LINEAR, elem_bits, d_flags,
+                      xf ? &x : nullptr, &sp, ranges, &nr);
     if (st != SWRT_OK) return st;
   }
   const bool lengths_out = total_lens || past_lens || cache_past_lens || cache_total_lens ||
@@ -190,6 +217,7 @@ extern "C" int swrt_kv_decode_step(int n_window_layers, void *const *win_k_cache
   a.evict = evict_counts;
   a.batch = batch;
   a.gap = FastDiv(uint32_t(capacity - window + 1));
+  a.xf = x;
   a.full_tiles = sp.empty ? 1 : sp.tiles;
   a.full_blocks = sp.empty ? 0 : sp.tiles * uint32_t(sp.n);
   a.len_blocks = do_len ? uint32_t((B + block - 1) / block) : 0;
@@ -199,12 +227,55 @@ extern "C" int swrt_kv_decode_step(int n_window_layers, void *const *win_k_cache
   if (grid < a.len_blocks) grid = a.len_blocks;  // length arrays alone
   if (grid >= (uint64_t(1) << 31)) return SWRT_E_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  switch (vec) {
-    case 16: launch_decode<16>(a, drift, spw, grid, s); break;
-    case 8: launch_decode<8>(a, drift, spw, grid, s); break;
-    case 4: launch_decode<4>(a, drift, spw, grid, s); break;
-    case 2: launch_decode<2>(a, drift, spw, grid, s); break;
-    default: launch_decode<1>(a, drift, spw, grid, s); break;
-  }
+  if (xf)
+    launch_vec<true>(vec, a, drift, spw, grid, s);
+  else
+    launch_vec<false>(vec, a, drift, spw, grid, s);
   return launch_status();
+}
+
+}  // namespace
+
+extern "C" int swrt_kv_decode_step(int n_window_layers, void *const *win_k_caches,
+                                   void *const *win_v_caches, const void *const *win_k_new,
+                                   const void *const *win_v_new, const int64_t *win_new_strides,
+                                   const int32_t *seqlens_k, int capacity, int window,
+                                   int64_t *total_lens, int64_t *past_lens,
+                                   int32_t *cache_past_lens, int32_t *cache_total_lens,
+                                   int32_t *evict_counts, int n_full, void *const *full_caches,
+                                   const void *const *full_new, const int64_t *write_indices,
+                                   int max_seq, int batch, int kv_heads, int head_dim,
+                                   int elem_bits, uint32_t *d_flags, void *stream) {
+  return decode_step(n_window_layers, win_k_caches, win_v_caches, win_k_new, win_v_new,
+                     win_new_strides, seqlens_k, capacity, window, total_lens, past_lens,
+                     cache_past_lens, cache_total_lens, evict_counts, n_full, full_caches,
+                     full_new, write_indices, max_seq, batch, kv_heads, head_dim, elem_bits,
+                     nullptr, d_flags, stream);
+}
+
+extern "C" int swrt_kv_decode_step_xf(
+    int n_window_layers, void *const *win_k_caches, void *const *win_v_caches,
+    const void *const *win_k_new, const void *const *win_v_new, const int64_t *win_new_strides,
+    const int32_t *seqlens_k, int capacity, int window, int64_t *total_lens, int64_t *past_lens,
+    int32_t *cache_past_lens, int32_t *cache_total_lens, int32_t *evict_counts,
+    int n_full_layers, void *const *full_k_caches, void *const *full_v_caches,
+    const void *const *full_k_new, const void *const *full_v_new, const int64_t *write_indices,
+    int max_seq, int batch, int kv_heads, int head_dim, const swrt_row_transform *xf,
+    uint32_t *d_flags, void *stream) {
+  if (!xf || n_full_layers < 0 || 2 * n_full_layers > kMaxTensors) return SWRT_E_INVALID_ARG;
+  if (n_full_layers > 0 && (!full_k_caches || !full_v_caches || !full_k_new || !full_v_new))
+    return SWRT_E_INVALID_ARG;
+  void *caches[kMaxTensors];
+  const void *news[kMaxTensors];
+  for (int l = 0; l < n_full_layers; ++l) {  // K, V, K, V, ...: tensor = index & 1
+    caches[2 * l] = full_k_caches[l];
+    caches[2 * l + 1] = full_v_caches[l];
+    news[2 * l] = full_k_new[l];
+    news[2 * l + 1] = full_v_new[l];
+  }
+  return decode_step(n_window_layers, win_k_caches, win_v_caches, win_k_new, win_v_new,
+                     win_new_strides, seqlens_k, capacity, window, total_lens, past_lens,
+                     cache_past_lens, cache_total_lens, evict_counts, 2 * n_full_layers, caches,
+                     news, write_indices, max_seq, batch, kv_heads, head_dim, 8, xf, d_flags,
+                     stream);
 }

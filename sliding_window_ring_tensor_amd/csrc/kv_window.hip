@@ -7,8 +7,10 @@
 //   window_in_place  S = 1: one workgroup per slice, shift by E then append.
 //   window_stage     S > 1, phase STAGE: 16 KiB tiles of each staging slice.
 //   window_commit    S > 1, phase COMMIT: 16 KiB tiles of each cache slice.
-// Batch entries whose (Lp, E) pair is not the one the lengths define for
-// (C, S) are flagged and left untouched.
+// Batch entries whose (Lp, E) pair is not a step that fits (C, S) are flagged
+// and left untouched. The XF instances are the fused append (xf_device.hpp):
+// new rows pass through the row transform at positions past_lens[b] + s, and
+// entries whose positions leave the rotary tables are flagged and skipped.
 #include "swrt_host.hpp"
 
 namespace swrt {
@@ -20,59 +22,82 @@ struct WinArgs {
   const char *nw[NL][2];
   char *stage[NL][2];
   WindowGeom g;
+  RowXf xf;  // fused append only
 };
 
-template <int VEC, int NL, int SPW>
+template <int VEC, int NL, int SPW, bool XF>
 __global__ __launch_bounds__(kWinBlock) void window_in_place(WinArgs<NL> a) {
   if constexpr (SPW == 1) {
     const Slice s = decode_slice(a.g, blockIdx.x);
     const int64_t Lp = a.g.lp[s.b], E = a.g.ev[s.b];
     if (!lengths_ok(a.g, s, threadIdx.x == 0, Lp, E)) return;
+    int64_t P = 0;
+    if constexpr (XF) {
+      P = a.g.past[s.b];
+      if (!positions_ok(a.g, a.xf, s, threadIdx.x == 0, P)) return;
+    }
     char *base = a.cache[s.layer][s.t] + uint64_t(s.b * a.g.H + s.h) * uint64_t(a.g.C) * a.g.row_bytes;
-    shift_append_slice<VEC>(base, a.nw[s.layer][s.t] + s.b * a.g.nb_b + s.h * a.g.nb_h, Lp, E,
-                            a.g.row_bytes, a.g.row_words);
+    shift_append_slice<VEC, kWinBlock, kWinUnroll, XF>(
+        base, a.nw[s.layer][s.t] + s.b * a.g.nb_b + s.h * a.g.nb_h, Lp, E, a.g.row_bytes,
+        a.g.row_words, &a.xf, int(s.t), P);
   } else {
     constexpr uint32_t GB = kWinBlock / SPW;
-    shift_append_group<VEC, SPW>(blockIdx.x * SPW, a.g.slices, a.g.row_bytes, a.g.row_words,
-                                 [&](uint32_t slice, int g) {
-                                   const Slice s = decode_slice(a.g, slice);
-                                   SliceWork w;
-                                   w.Lp = a.g.lp[s.b];
-                                   w.E = a.g.ev[s.b];
-                                   w.ok = lengths_ok(a.g, s, threadIdx.x == g * GB, w.Lp, w.E);
-                                   w.base = a.cache[s.layer][s.t] +
-                                            uint64_t(s.b * a.g.H + s.h) * uint64_t(a.g.C) * a.g.row_bytes;
-                                   w.new_row = a.nw[s.layer][s.t] + s.b * a.g.nb_b + s.h * a.g.nb_h;
-                                   return w;
-                                 });
+    shift_append_group<VEC, SPW, XF>(
+        blockIdx.x * SPW, a.g.slices, a.g.row_bytes, a.g.row_words,
+        [&](uint32_t slice, int g) {
+          const Slice s = decode_slice(a.g, slice);
+          SliceWork w;
+          w.Lp = a.g.lp[s.b];
+          w.E = a.g.ev[s.b];
+          w.ok = lengths_ok(a.g, s, threadIdx.x == g * GB, w.Lp, w.E);
+          w.t = int(s.t);
+          w.pos = 0;
+          if constexpr (XF) {
+            w.pos = a.g.past[s.b];
+            w.ok = w.ok && positions_ok(a.g, a.xf, s, threadIdx.x == g * GB, w.pos);
+          }
+          w.base = a.cache[s.layer][s.t] + uint64_t(s.b * a.g.H + s.h) * uint64_t(a.g.C) * a.g.row_bytes;
+          w.new_row = a.nw[s.layer][s.t] + s.b * a.g.nb_b + s.h * a.g.nb_h;
+          return w;
+        },
+        &a.xf);
   }
 }
 
-template <int VEC, int NL>
+template <int VEC, int NL, bool XF>
 __global__ __launch_bounds__(kWinBlock) void window_stage(WinArgs<NL> a) {
   const uint32_t slice = blockIdx.x / a.g.tiles, tile = blockIdx.x - slice * a.g.tiles;
   const Slice s = decode_slice(a.g, slice);
   const int64_t Lp = a.g.lp[s.b], E = a.g.ev[s.b];
   if (!lengths_ok(a.g, s, tile == 0 && threadIdx.x == 0, Lp, E)) return;
+  int64_t P = 0;
+  if constexpr (XF) {
+    P = a.g.past[s.b];
+    if (!positions_ok(a.g, a.xf, s, tile == 0 && threadIdx.x == 0, P)) return;
+  }
   const uint64_t bh = s.b * a.g.H + s.h;
-  stage_tile<VEC>(a.g, a.cache[s.layer][s.t] + bh * uint64_t(a.g.C) * a.g.row_bytes,
-                  a.stage[s.layer][s.t] + bh * uint64_t(a.g.C + a.g.S) * a.g.row_bytes,
-                  a.nw[s.layer][s.t] + s.b * a.g.nb_b + s.h * a.g.nb_h, Lp, tile);
+  stage_tile<VEC, XF>(a.g, a.cache[s.layer][s.t] + bh * uint64_t(a.g.C) * a.g.row_bytes,
+                      a.stage[s.layer][s.t] + bh * uint64_t(a.g.C + a.g.S) * a.g.row_bytes,
+                      a.nw[s.layer][s.t] + s.b * a.g.nb_b + s.h * a.g.nb_h, Lp, tile, &a.xf,
+                      int(s.t), P);
 }
 
-template <int VEC, int NL>
+template <int VEC, int NL, bool XF>
 __global__ __launch_bounds__(kWinBlock) void window_commit(WinArgs<NL> a) {
   const uint32_t slice = blockIdx.x / a.g.tiles, tile = blockIdx.x - slice * a.g.tiles;
   const Slice s = decode_slice(a.g, slice);
   const int64_t Lp = a.g.lp[s.b], E = a.g.ev[s.b];
   if (!lengths_ok(a.g, s, tile == 0 && threadIdx.x == 0, Lp, E)) return;
+  if constexpr (XF) {  // an entry the stage phase skipped stays untouched
+    if (!positions_ok(a.g, a.xf, s, tile == 0 && threadIdx.x == 0, a.g.past[s.b])) return;
+  }
   const uint64_t bh = s.b * a.g.H + s.h;
   commit_tile<VEC>(a.g, a.cache[s.layer][s.t] + bh * uint64_t(a.g.C) * a.g.row_bytes,
                    a.stage[s.layer][s.t] + bh * uint64_t(a.g.C + a.g.S) * a.g.row_bytes, Lp, E,
                    tile);
 }
 
-template <int VEC, int NL>
+template <int VEC, int NL, bool XF>
 int launch(const WindowPlan &p, unsigned phase, hipStream_t stream) {
   WinArgs<NL> a;
   for (int l = 0; l < NL && l < p.n_layers; ++l)
@@ -82,62 +107,81 @@ int launch(const WindowPlan &p, unsigned phase, hipStream_t stream) {
       a.stage[l][t] = p.stage[l][t];
     }
   a.g = p.g;
+  a.xf = p.xf;
   if (p.g.S == 1) {
     const int spw = slices_per_group(p.g.C, p.g.row_words);
     const dim3 grid((p.slices + spw - 1) / spw);
     if (spw == 4)
-      hipLaunchKernelGGL((window_in_place<VEC, NL, 4>), grid, dim3(kWinBlock), 0, stream, a);
+      hipLaunchKernelGGL((window_in_place<VEC, NL, 4, XF>), grid, dim3(kWinBlock), 0, stream, a);
     else if (spw == 2)
-      hipLaunchKernelGGL((window_in_place<VEC, NL, 2>), grid, dim3(kWinBlock), 0, stream, a);
+      hipLaunchKernelGGL((window_in_place<VEC, NL, 2, XF>), grid, dim3(kWinBlock), 0, stream, a);
     else
-      hipLaunchKernelGGL((window_in_place<VEC, NL, 1>), grid, dim3(kWinBlock), 0, stream, a);
+      hipLaunchKernelGGL((window_in_place<VEC, NL, 1, XF>), grid, dim3(kWinBlock), 0, stream, a);
     return launch_status();
   }
   if (phase & SWRT_PHASE_STAGE) {
     a.g.tiles = uint32_t((uint64_t(p.g.C + p.g.S) * p.g.row_words + kWinTile - 1) / kWinTile);
-    hipLaunchKernelGGL((window_stage<VEC, NL>), dim3(p.slices * a.g.tiles), dim3(kWinBlock), 0,
+    hipLaunchKernelGGL((window_stage<VEC, NL, XF>), dim3(p.slices * a.g.tiles), dim3(kWinBlock), 0,
                        stream, a);
     if (launch_status() != SWRT_OK) return SWRT_E_LAUNCH;
   }
   if (phase & SWRT_PHASE_COMMIT) {
     a.g.tiles = uint32_t((uint64_t(p.g.C) * p.g.row_words + kWinTile - 1) / kWinTile);
-    hipLaunchKernelGGL((window_commit<VEC, NL>), dim3(p.slices * a.g.tiles), dim3(kWinBlock), 0,
+    hipLaunchKernelGGL((window_commit<VEC, NL, XF>), dim3(p.slices * a.g.tiles), dim3(kWinBlock), 0,
                        stream, a);
     if (launch_status() != SWRT_OK) return SWRT_E_LAUNCH;
   }
   return SWRT_OK;
 }
 
-template <int NL>
+template <int NL, bool XF>
 int dispatch(const WindowPlan &p, int vec, unsigned phase, hipStream_t s) {
   switch (vec) {
-    case 16: return launch<16, NL>(p, phase, s);
-    case 8: return launch<8, NL>(p, phase, s);
-    case 4: return launch<4, NL>(p, phase, s);
-    case 2: return launch<2, NL>(p, phase, s);
-    default: return launch<1, NL>(p, phase, s);
+    case 16: return launch<16, NL, XF>(p, phase, s);
+    case 8: return launch<8, NL, XF>(p, phase, s);
+    case 4: return launch<4, NL, XF>(p, phase, s);
+    case 2: return launch<2, NL, XF>(p, phase, s);
+    default: return launch<1, NL, XF>(p, phase, s);
   }
 }
 
+// xf: the fused append's transform (null: a plain copy), with past_lens
 int window_append(int n_layers, void *const *k_caches, void *const *v_caches,
                   const void *const *k_news, const void *const *v_news,
                   const int64_t *new_strides, void *const *k_stagings, void *const *v_stagings,
                   const int32_t *cache_past_lens, const int32_t *evict_counts, int batch,
                   int kv_heads, int capacity, int seq_len, int head_dim, int elem_bits,
-                  unsigned phase, uint32_t *d_flags, void *stream) {
+                  unsigned phase, const swrt_row_transform *xf, const int64_t *past_lens,
+                  uint32_t *d_flags, void *stream) {
   WindowPlan p;
-  Range ranges[6 * kMaxLayers + 4];
+  Range ranges[6 * kMaxLayers + 8];
   int nr = 0;
-  int st = plan_window(n_layers, k_caches, v_caches, k_news, v_news, new_strides, k_stagings,
-                       v_stagings, cache_past_lens, evict_counts, false, batch, kv_heads,
-                       capacity, seq_len, head_dim, elem_bits, phase, d_flags, &p, ranges, &nr);
+  RowXf x{};
+  int st;
+  if (xf) {
+    if ((st = plan_xf(xf, head_dim, &x, ranges, &nr)) != SWRT_OK) return st;
+    elem_bits = x.out_bytes * 8;
+  }
+  st = plan_window(n_layers, k_caches, v_caches, k_news, v_news, new_strides, k_stagings,
+                   v_stagings, cache_past_lens, evict_counts, false, batch, kv_heads, capacity,
+                   seq_len, head_dim, elem_bits, phase, d_flags, xf ? &x : nullptr, &p, ranges,
+                   &nr);
   if (st != SWRT_OK || p.empty) return st;
+  if (xf) {
+    if (!past_lens || addr_of(past_lens) % 8) return SWRT_E_INVALID_ARG;
+    ranges[nr++] = range(past_lens, uint64_t(batch) * 8, false);
+    p.g.past = past_lens;
+  }
   ranges[nr++] = range(d_flags, 4, true);
   if (written_overlap(ranges, nr)) return SWRT_E_INVALID_ARG;
   const int vec = word_of(p.align);
   if ((st = finish_window(&p, vec)) != SWRT_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return n_layers == 1 ? dispatch<1>(p, vec, phase, s) : dispatch<kMaxLayers>(p, vec, phase, s);
+  if (xf)
+    return n_layers == 1 ? dispatch<1, true>(p, vec, phase, s)
+                         : dispatch<kMaxLayers, true>(p, vec, phase, s);
+  return n_layers == 1 ? dispatch<1, false>(p, vec, phase, s)
+                       : dispatch<kMaxLayers, false>(p, vec, phase, s);
 }
 
 }  // namespace
@@ -150,8 +194,10 @@ int plan_window(int n_layers, void *const *k_caches, void *const *v_caches,
                 void *const *k_stagings, void *const *v_stagings, const int32_t *cache_past_lens,
                 const int32_t *evict_counts, bool lengths_in_kernel, int batch, int kv_heads,
                 int capacity, int seq_len, int head_dim, int elem_bits, unsigned phase,
-                uint32_t *d_flags, WindowPlan *p, Range *ranges, int *nr) {
+                uint32_t *d_flags, const RowXf *xf, WindowPlan *p, Range *ranges, int *nr) {
   p->empty = true;
+  p->xf = xf ? *xf : RowXf{};
+  p->g.past = nullptr;
   p->n_layers = n_layers;
   if (n_layers < 0 || n_layers > kMaxLayers) return SWRT_E_INVALID_ARG;
   if (batch < 0 || kv_heads < 0 || head_dim < 0 || capacity < 1 || seq_len < 1)
@@ -162,13 +208,16 @@ int plan_window(int n_layers, void *const *k_caches, void *const *v_caches,
     return SWRT_E_INVALID_ARG;
   if (!new_strides) return SWRT_E_INVALID_ARG;
   if ((D * elem_bits) % 8) return SWRT_E_UNSUPPORTED;
+  // new rows: the cache's elements, or the fused append's input elements
+  const int new_bits = xf ? xf->in_bytes * 8 : elem_bits;
   int64_t nb[3];
   for (int i = 0; i < 3; ++i) {
     if (new_strides[i] < 0) return SWRT_E_INVALID_ARG;
-    if (!mul_ok(new_strides[i], elem_bits, &nb[i]) || nb[i] % 8) return SWRT_E_UNSUPPORTED;
+    if (!mul_ok(new_strides[i], new_bits, &nb[i]) || nb[i] % 8) return SWRT_E_UNSUPPORTED;
     nb[i] /= 8;
   }
   const int64_t row = D * elem_bits / 8;
+  const int64_t new_row = D * new_bits / 8;
   p->row = row;
   if (n_layers == 0 || B == 0 || H == 0 || row == 0) return SWRT_OK;
   if (!k_caches || !v_caches || !k_news || !v_news) return SWRT_E_INVALID_ARG;
@@ -180,12 +229,14 @@ int plan_window(int n_layers, void *const *k_caches, void *const *v_caches,
     return SWRT_E_UNSUPPORTED;
   if (!mul_ok(B * H * C, row, &cache_bytes) || !mul_ok(B * H * (C + S), row, &stage_bytes))
     return SWRT_E_UNSUPPORTED;
-  const int64_t new_span = (B - 1) * nb[0] + (H - 1) * nb[1] + (S - 1) * nb[2] + row;
-  const uint64_t align = elem_align(elem_bits);
+  const int64_t new_span = (B - 1) * nb[0] + (H - 1) * nb[1] + (S - 1) * nb[2] + new_row;
+  const uint64_t align = elem_align(elem_bits), new_align = elem_align(new_bits);
   if (addr_of(cache_past_lens) % 4 || addr_of(evict_counts) % 4 || addr_of(d_flags) % 4)
     return SWRT_E_INVALID_ARG;
 
-  uint64_t acc = uint64_t(row) | uint64_t(nb[0]) | uint64_t(nb[1]) | uint64_t(nb[2]);
+  // the copy word must divide every copied address and stride; fused-append
+  // new rows are read element by element, so they do not count
+  uint64_t acc = uint64_t(row) | (xf ? 0 : uint64_t(nb[0]) | uint64_t(nb[1]) | uint64_t(nb[2]));
   // caches and staging buffers are written: nothing may overlap them (across
   // layers too); new rows and lengths are only read and may be shared
   for (int l = 0; l < n_layers; ++l) {
@@ -194,9 +245,10 @@ int plan_window(int n_layers, void *const *k_caches, void *const *v_caches,
     const uint64_t n[6] = {uint64_t(cache_bytes), uint64_t(cache_bytes), uint64_t(new_span),
                            uint64_t(new_span), uint64_t(stage_bytes), uint64_t(stage_bytes)};
     for (int i = 0; i < (S > 1 ? 6 : 4); ++i) {
-      if (!q[i] || addr_of(q[i]) % align) return SWRT_E_INVALID_ARG;
-      acc |= addr_of(q[i]);
-      ranges[(*nr)++] = range(q[i], n[i], i != 2 && i != 3);
+      const bool is_new = i == 2 || i == 3;
+      if (!q[i] || addr_of(q[i]) % (is_new ? new_align : align)) return SWRT_E_INVALID_ARG;
+      if (!(xf && is_new)) acc |= addr_of(q[i]);
+      ranges[(*nr)++] = range(q[i], n[i], !is_new);
     }
     p->cache[l][0] = static_cast<char *>(k_caches[l]);
     p->cache[l][1] = static_cast<char *>(v_caches[l]);
@@ -251,7 +303,8 @@ extern "C" int swrt_kv_window_append(void *k_cache, void *v_cache, const void *k
                                      uint32_t *d_flags, void *stream) {
   return swrt::window_append(1, &k_cache, &v_cache, &k_new, &v_new, new_strides, &k_staging,
                              &v_staging, cache_past_lens, evict_counts, batch, kv_heads, capacity,
-                             seq_len, head_dim, elem_bits, phase, d_flags, stream);
+                             seq_len, head_dim, elem_bits, phase, nullptr, nullptr, d_flags,
+                             stream);
 }
 
 extern "C" int swrt_kv_window_append_layers(int n_layers, void *const *k_caches,
@@ -264,5 +317,22 @@ extern "C" int swrt_kv_window_append_layers(int n_layers, void *const *k_caches,
                                             unsigned phase, uint32_t *d_flags, void *stream) {
   return swrt::window_append(n_layers, k_caches, v_caches, k_news, v_news, new_strides, k_stagings,
                              v_stagings, cache_past_lens, evict_counts, batch, kv_heads, capacity,
-                             seq_len, head_dim, elem_bits, phase, d_flags, stream);
+                             seq_len, head_dim, elem_bits, phase, nullptr, nullptr, d_flags,
+                             stream);
+}
+
+extern "C" int swrt_kv_window_append_xf(int n_layers, void *const *k_caches,
+                                        void *const *v_caches, const void *const *k_news,
+                                        const void *const *v_news, const int64_t *new_strides,
+                                        void *const *k_stagings, void *const *v_stagings,
+                                        const int32_t *cache_past_lens,
+                                        const int32_t *evict_counts, const int64_t *past_lens,
+                                        int batch, int kv_heads, int capacity, int seq_len,
+                                        int head_dim, unsigned phase,
+                                        const swrt_row_transform *xf, uint32_t *d_flags,
+                                        void *stream) {
+  if (!xf) return SWRT_E_INVALID_ARG;
+  return swrt::window_append(n_layers, k_caches, v_caches, k_news, v_news, new_strides, k_stagings,
+                             v_stagings, cache_past_lens, evict_counts, batch, kv_heads, capacity,
+                             seq_len, head_dim, 8, phase, xf, past_lens, d_flags, stream);
 }

@@ -10,10 +10,14 @@
 // only). A linear entry with w_b < 0 or w_b > M - S is flagged and its rows
 // keep past's values.
 //
-// Used by tensor_scatter.hip and decode_step.hip.
+// Used by tensor_scatter.hip and decode_step.hip. The XF instances are the
+// fused append (xf_device.hpp): update rows pass through the row transform at
+// absolute positions w_b + s (before the circular wrap), and entries whose
+// positions leave the rotary tables are flagged and skipped like linear
+// out-of-range ones.
 #pragma once
 
-#include "swrt_device.hpp"
+#include "xf_device.hpp"
 
 namespace swrt {
 
@@ -38,6 +42,7 @@ struct ScatterGeom {
   FastDiv by_seq;          // row -> (o, s) in place; row -> (o, j) out of place
   FastDiv by_batch;        // o -> b
   int circular;
+  uint32_t in_row_bytes;   // fused append: bytes of an update row (in_type)
 };
 
 // floor modulo of a 64-bit index into [0, M); the division is skipped for the
@@ -53,10 +58,11 @@ __device__ __forceinline__ int64_t wrap_index(int64_t w, int64_t M) {
 // w mod M; linear entries hold w, or -1 when the entry is out of range (then
 // flagged). Lane lookups are LDS reads, so the only global loads of a lane are
 // its payload words.
-template <uint32_t TILE>
+template <uint32_t TILE, bool RAW = false>
 struct TileBatches {
   uint32_t first;
   int64_t w[TILE + 1];
+  int64_t raw[RAW ? TILE + 1 : 1];  // fused append: w before the wrap (the position)
 };
 
 __device__ __forceinline__ int64_t reduce_write_index(const ScatterGeom &g, int64_t w) {
@@ -89,31 +95,54 @@ __device__ __forceinline__ WPrefetch prefetch_write_indices(const ScatterGeom &g
   return p;
 }
 
-template <int BLOCK, uint32_t TILE>
+// fused append: a valid entry must also have its positions in the tables
+__device__ __forceinline__ int64_t reduce_write_index_xf(const ScatterGeom &g, const RowXf &x,
+                                                         int64_t w) {
+  const int64_t r = reduce_write_index(g, w);
+  if (r < 0 || xf_positions_ok(x, w, g.S)) return r;
+  if (g.flags) atomicOr(g.flags, SWRT_FLAG_ROPE_RANGE);
+  return -1;
+}
+
+template <int BLOCK, uint32_t TILE, bool XF = false>
 __device__ __forceinline__ void finish_write_indices(const ScatterGeom &g, const WPrefetch &p,
-                                                     TileBatches<TILE> &tb) {
+                                                     TileBatches<TILE, XF> &tb,
+                                                     const RowXf *xf = nullptr) {
+  const auto stage = [&](uint32_t k, int64_t w) {
+    if constexpr (XF) {
+      tb.w[k] = reduce_write_index_xf(g, *xf, w);
+      tb.raw[k] = w;
+    } else {
+      tb.w[k] = reduce_write_index(g, w);
+    }
+  };
   if (threadIdx.x == 0) tb.first = p.first;
-  if (threadIdx.x < p.count) tb.w[threadIdx.x] = reduce_write_index(g, p.w);
+  if (threadIdx.x < p.count) stage(threadIdx.x, p.w);
   for (uint32_t k = threadIdx.x + BLOCK; k < p.count; k += BLOCK)  // many tiny rows
-    tb.w[k] = reduce_write_index(g, g.write_indices ? g.write_indices[p.first + k] : 0);
+    stage(k, g.write_indices ? g.write_indices[p.first + k] : 0);
   __syncthreads();
 }
 
 // In place: tile `tile` (a word offset) of the update moves to its cache rows.
 // Lanes past the last word clamp to it (repeating that lane's load and store),
-// so only the linear out-of-range skip guards stores.
-template <int VEC, int BLOCK>
+// so only the linear out-of-range skip guards stores. XF: each word is the
+// transform of update row (o, s) at position w + s (tensor t), computed once
+// the write indices are staged.
+template <int VEC, int BLOCK, bool XF = false>
 __device__ __forceinline__ void scatter_in_place_tile(const ScatterGeom &g, char *present_,
                                                       const char *update_, uint32_t tile,
-                                                      TileBatches<BLOCK * kScatUnroll> &tb) {
+                                                      TileBatches<BLOCK * kScatUnroll, XF> &tb,
+                                                      const RowXf *xf = nullptr, int t = 0) {
   using W = typename Word<VEC>::T;
   const WPrefetch wp = prefetch_write_indices<BLOCK>(g, tile);
   const W *update = reinterpret_cast<const W *>(update_);
   W *present = reinterpret_cast<W *>(present_);
   W v[kScatUnroll];
+  if constexpr (!XF) {
 #pragma unroll
-  for (int u = 0; u < kScatUnroll; ++u) v[u] = ld(update + min(tile + u * BLOCK + threadIdx.x, g.n_words - 1));
-  finish_write_indices<BLOCK>(g, wp, tb);
+    for (int u = 0; u < kScatUnroll; ++u) v[u] = ld(update + min(tile + u * BLOCK + threadIdx.x, g.n_words - 1));
+  }
+  finish_write_indices<BLOCK>(g, wp, tb, xf);
 #pragma unroll
   for (int u = 0; u < kScatUnroll; ++u) {
     const uint32_t i = min(tile + u * BLOCK + threadIdx.x, g.n_words - 1);
@@ -121,21 +150,27 @@ __device__ __forceinline__ void scatter_in_place_tile(const ScatterGeom &g, char
     const uint32_t col = i - row * g.words_per_row;
     const uint32_t o = g.by_seq.div(row);
     const uint32_t s = row - o * uint32_t(g.S);
-    const int64_t w = tb.w[g.by_batch.div(o) - tb.first];
+    const uint32_t k = g.by_batch.div(o) - tb.first;
+    const int64_t w = tb.w[k];
     int64_t j = w + s;
     if (g.circular && j >= g.M) j -= g.M;
-    if (w >= 0) st(present + (int64_t(o) * g.M + j) * g.words_per_row + col, v[u]);
+    if (w >= 0) {
+      if constexpr (XF)
+        v[u] = xf_word<VEC>(*xf, t, update_ + uint64_t(row) * g.in_row_bytes, tb.raw[k] + s, col);
+      st(present + (int64_t(o) * g.M + j) * g.words_per_row + col, v[u]);
+    }
   }
 }
 
 // Out of place: tile `tile` of present, every word from past or the update.
-template <int VEC, int BLOCK>
+template <int VEC, int BLOCK, bool XF = false>
 __device__ __forceinline__ void scatter_out_of_place_tile(const ScatterGeom &g, char *present_,
                                                           const char *past_, const char *update_,
                                                           uint32_t tile,
-                                                          TileBatches<BLOCK * kScatUnroll> &tb) {
+                                                          TileBatches<BLOCK * kScatUnroll, XF> &tb,
+                                                          const RowXf *xf = nullptr, int t = 0) {
   using W = typename Word<VEC>::T;
-  finish_write_indices<BLOCK>(g, prefetch_write_indices<BLOCK>(g, tile), tb);
+  finish_write_indices<BLOCK>(g, prefetch_write_indices<BLOCK>(g, tile), tb, xf);
   const W *update = reinterpret_cast<const W *>(update_);
   const W *past = reinterpret_cast<const W *>(past_);
   W *present = reinterpret_cast<W *>(present_);
@@ -147,14 +182,21 @@ __device__ __forceinline__ void scatter_out_of_place_tile(const ScatterGeom &g, 
     const uint32_t col = i - row * g.words_per_row;
     const uint32_t o = g.by_seq.div(row);
     const int64_t j = row - o * uint32_t(g.M);
-    const int64_t w = tb.w[g.by_batch.div(o) - tb.first];
+    const uint32_t k = g.by_batch.div(o) - tb.first;
+    const int64_t w = tb.w[k];
     int64_t s = -1;  // the update row landing on (o, j), if any
     if (w >= 0) {
       s = j - w;
       if (g.circular && s < 0) s += g.M;
       if (s >= g.S) s = -1;
     }
-    v[u] = ld(s >= 0 ? update + (int64_t(o) * g.S + s) * g.words_per_row + col : past + i);
+    if constexpr (XF) {
+      v[u] = s >= 0 ? xf_word<VEC>(*xf, t, update_ + (uint64_t(o) * g.S + s) * g.in_row_bytes,
+                                   tb.raw[k] + s, col)
+                    : ld(past + i);
+    } else {
+      v[u] = ld(s >= 0 ? update + (int64_t(o) * g.S + s) * g.words_per_row + col : past + i);
+    }
   }
 #pragma unroll
   for (int u = 0; u < kScatUnroll; ++u) st(present + min(tile + u * BLOCK + threadIdx.x, g.n_words - 1), v[u]);

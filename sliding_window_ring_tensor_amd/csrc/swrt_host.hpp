@@ -29,6 +29,7 @@ inline uint64_t elem_align(int elem_bits) {
 
 struct WindowPlan {
   WindowGeom g;
+  RowXf xf;  // the fused append's transform (zero for a plain copy)
   char *cache[kMaxLayers][2];
   const char *nw[kMaxLayers][2];
   char *stage[kMaxLayers][2];
@@ -40,19 +41,22 @@ struct WindowPlan {
 };
 
 // Validate a windowed step. With lengths_in_kernel, cache_past_lens and
-// evict_counts are not used (the kernel derives them from seqlens_k).
+// evict_counts are not used (the kernel derives them from seqlens_k). With
+// xf (a checked transform, see plan_xf), new rows hold xf->in_type elements
+// and caches elem_bits = 8 * xf->out_bytes.
 int plan_window(int n_layers, void *const *k_caches, void *const *v_caches,
                 const void *const *k_news, const void *const *v_news, const int64_t *new_strides,
                 void *const *k_stagings, void *const *v_stagings, const int32_t *cache_past_lens,
                 const int32_t *evict_counts, bool lengths_in_kernel, int batch, int kv_heads,
                 int capacity, int seq_len, int head_dim, int elem_bits, unsigned phase,
-                uint32_t *d_flags, WindowPlan *p, Range *ranges, int *nr);
+                uint32_t *d_flags, const RowXf *xf, WindowPlan *p, Range *ranges, int *nr);
 
 // Fill the word-dependent geometry; SWRT_E_UNSUPPORTED past the size limits.
 int finish_window(WindowPlan *p, int vec);
 
 struct ScatterPlan {
   ScatterGeom g;
+  RowXf xf;  // the fused append's transform (zero for a plain copy)
   char *present[kMaxTensors];
   const char *past[kMaxTensors];
   const char *update[kMaxTensors];
@@ -66,12 +70,61 @@ struct ScatterPlan {
   uint32_t tiles;  // tiles per tensor
 };
 
+// With xf, update rows hold xf->in_type elements (axis must be rank - 2) and
+// caches elem_bits = 8 * xf->out_bytes.
 int plan_scatter(int n_tensors, void *const *presents, const void *const *pasts,
                  const void *const *updates, const int64_t *write_indices, const int64_t *shape,
                  int rank, int axis, int64_t seq_len, int mode, int elem_bits, uint32_t *d_flags,
-                 ScatterPlan *p, Range *ranges, int *nr);
+                 const RowXf *xf, ScatterPlan *p, Range *ranges, int *nr);
 
 // tile_words: words per workgroup tile of the kernel that will run the plan
 int finish_scatter(ScatterPlan *p, int vec, uint32_t tile_words);
+
+// Check a row transform for rows of head_dim elements and fill the device
+// form; the tables join the read-only ranges of the call.
+inline int plan_xf(const swrt_row_transform *t, int64_t head_dim, RowXf *x, Range *ranges,
+                   int *nr) {
+  const auto bytes = [](int type) {
+    return type == SWRT_XF_F32 ? 4 : type == SWRT_XF_F16 || type == SWRT_XF_BF16 ? 2
+                                 : type == SWRT_XF_INT8 || type == SWRT_XF_UINT8 ? 1 : 0;
+  };
+  if (!t || head_dim < 0) return SWRT_E_INVALID_ARG;
+  if (t->in_type != SWRT_XF_F32 && t->in_type != SWRT_XF_F16 && t->in_type != SWRT_XF_BF16)
+    return SWRT_E_INVALID_ARG;
+  if (bytes(t->out_type) == 0) return SWRT_E_INVALID_ARG;
+  if ((t->cos_table == nullptr) != (t->sin_table == nullptr)) return SWRT_E_INVALID_ARG;
+  *x = RowXf{};
+  x->in_type = t->in_type;
+  x->out_type = t->out_type;
+  x->in_bytes = bytes(t->in_type);
+  x->out_bytes = bytes(t->out_type);
+  if (t->cos_table) {
+    int64_t n;
+    if (t->max_position < 1 || t->rotary_dim < 2 || t->rotary_dim % 2 ||
+        t->rotary_dim > head_dim)
+      return SWRT_E_INVALID_ARG;
+    if (addr_of(t->cos_table) % 4 || addr_of(t->sin_table) % 4) return SWRT_E_INVALID_ARG;
+    if (!mul_ok(t->max_position, t->rotary_dim / 2 * 4, &n)) return SWRT_E_UNSUPPORTED;
+    ranges[(*nr)++] = range(t->cos_table, uint64_t(n), false);
+    ranges[(*nr)++] = range(t->sin_table, uint64_t(n), false);
+    x->cos = t->cos_table;
+    x->sin = t->sin_table;
+    x->max_pos = t->max_position;
+    x->half = int32_t(t->rotary_dim / 2);
+    x->interleaved = t->interleaved ? 1 : 0;
+  }
+  if (x->out_bytes == 1) {
+    x->lo = t->out_type == SWRT_XF_INT8 ? -128 : 0;
+    x->hi = t->out_type == SWRT_XF_INT8 ? 127 : 255;
+    for (int k = 0; k < 2; ++k) {
+      const float sc = t->scale[k];
+      if (!(sc > 0.0f) || sc > 3.4028235e38f) return SWRT_E_INVALID_ARG;  // positive, finite
+      if (t->zero_point[k] < x->lo || t->zero_point[k] > x->hi) return SWRT_E_INVALID_ARG;
+      x->scale[k] = sc;
+      x->zero[k] = t->zero_point[k];
+    }
+  }
+  return SWRT_OK;
+}
 
 }  // namespace swrt

@@ -6,7 +6,8 @@
 // raw-bit word of the update, consecutive threads on consecutive words, so the
 // update is read and the target rows are written fully coalesced. Out of place
 // every present row is produced in one pass from either past or the update.
-// A batched call runs every tensor of one shape in a single grid.
+// A batched call runs every tensor of one shape in a single grid. The XF
+// instances are the fused append (row transform on the update rows).
 #include "swrt_host.hpp"
 
 namespace swrt {
@@ -19,28 +20,32 @@ struct ScatterArgs {
   const char *update[NT];
   uint32_t tiles;  // tiles per tensor
   ScatterGeom g;
+  RowXf xf;        // fused append only
+  uint64_t vmask;  // fused append: bit t set when tensor t is a V cache
 };
 
 constexpr uint32_t kTile = kScatBlock * kScatUnroll;
 
-template <int VEC, int NT>
+template <int VEC, int NT, bool XF>
 __global__ __launch_bounds__(kScatBlock) void scatter_in_place(ScatterArgs<NT> a) {
-  __shared__ TileBatches<kTile> tb;
+  __shared__ TileBatches<kTile, XF> tb;
   const uint32_t t = blockIdx.x / a.tiles;  // which tensor of a batched call
   const uint32_t tile = (blockIdx.x - t * a.tiles) * kTile;
-  scatter_in_place_tile<VEC, kScatBlock>(a.g, a.present[t], a.update[t], tile, tb);
+  scatter_in_place_tile<VEC, kScatBlock, XF>(a.g, a.present[t], a.update[t], tile, tb, &a.xf,
+                                             int((a.vmask >> t) & 1));
 }
 
-template <int VEC, int NT>
+template <int VEC, int NT, bool XF>
 __global__ __launch_bounds__(kScatBlock) void scatter_out_of_place(ScatterArgs<NT> a) {
-  __shared__ TileBatches<kTile> tb;
+  __shared__ TileBatches<kTile, XF> tb;
   const uint32_t t = blockIdx.x / a.tiles;
   const uint32_t tile = (blockIdx.x - t * a.tiles) * kTile;
-  scatter_out_of_place_tile<VEC, kScatBlock>(a.g, a.present[t], a.past[t], a.update[t], tile, tb);
+  scatter_out_of_place_tile<VEC, kScatBlock, XF>(a.g, a.present[t], a.past[t], a.update[t], tile,
+                                                 tb, &a.xf, int((a.vmask >> t) & 1));
 }
 
-template <int VEC, int NT>
-int launch(const ScatterPlan &p, hipStream_t stream) {
+template <int VEC, int NT, bool XF>
+int launch(const ScatterPlan &p, uint64_t vmask, hipStream_t stream) {
   ScatterArgs<NT> a;
   for (int t = 0; t < NT && t < p.n; ++t) {
     a.present[t] = p.present[t];
@@ -49,34 +54,51 @@ int launch(const ScatterPlan &p, hipStream_t stream) {
   }
   a.tiles = p.tiles;
   a.g = p.g;
+  a.xf = p.xf;
+  a.vmask = vmask;
   const dim3 grid(p.tiles * uint32_t(p.n));
   if (p.in_place)
-    hipLaunchKernelGGL((scatter_in_place<VEC, NT>), grid, dim3(kScatBlock), 0, stream, a);
+    hipLaunchKernelGGL((scatter_in_place<VEC, NT, XF>), grid, dim3(kScatBlock), 0, stream, a);
   else
-    hipLaunchKernelGGL((scatter_out_of_place<VEC, NT>), grid, dim3(kScatBlock), 0, stream, a);
+    hipLaunchKernelGGL((scatter_out_of_place<VEC, NT, XF>), grid, dim3(kScatBlock), 0, stream, a);
   return launch_status();
 }
 
-template <int NT>
-int dispatch(const ScatterPlan &p, int vec, hipStream_t s) {
+template <int NT, bool XF>
+int dispatch(const ScatterPlan &p, int vec, uint64_t vmask, hipStream_t s) {
   switch (vec) {
-    case 16: return launch<16, NT>(p, s);
-    case 8: return launch<8, NT>(p, s);
-    case 4: return launch<4, NT>(p, s);
-    case 2: return launch<2, NT>(p, s);
-    default: return launch<1, NT>(p, s);
+    case 16: return launch<16, NT, XF>(p, vmask, s);
+    case 8: return launch<8, NT, XF>(p, vmask, s);
+    case 4: return launch<4, NT, XF>(p, vmask, s);
+    case 2: return launch<2, NT, XF>(p, vmask, s);
+    default: return launch<1, NT, XF>(p, vmask, s);
   }
 }
 
+// xf: the fused append's transform (null: a plain copy); tensors: K (0) or V
+// (1) per tensor, with xf
 int scatter(int n_tensors, void *const *presents, const void *const *pasts,
             const void *const *updates, const int64_t *write_indices, const int64_t *shape,
-            int rank, int axis, int64_t seq_len, int mode, int elem_bits, uint32_t *d_flags,
-            void *stream) {
+            int rank, int axis, int64_t seq_len, int mode, int elem_bits,
+            const swrt_row_transform *xf, const int *tensors, uint32_t *d_flags, void *stream) {
   ScatterPlan p;
-  Range ranges[3 * kMaxTensors + 3];
+  Range ranges[3 * kMaxTensors + 5];
   int nr = 0;
-  int st = plan_scatter(n_tensors, presents, pasts, updates, write_indices, shape, rank, axis,
-                        seq_len, mode, elem_bits, d_flags, &p, ranges, &nr);
+  RowXf x{};
+  uint64_t vmask = 0;
+  int st;
+  if (xf) {
+    if (!shape || rank < 3 || rank > SWRT_MAX_RANK) return SWRT_E_INVALID_ARG;
+    if ((st = plan_xf(xf, shape[rank - 1], &x, ranges, &nr)) != SWRT_OK) return st;
+    if (n_tensors > 0 && !tensors) return SWRT_E_INVALID_ARG;
+    for (int t = 0; t < n_tensors && t < kMaxTensors; ++t) {
+      if (tensors[t] != 0 && tensors[t] != 1) return SWRT_E_INVALID_ARG;
+      vmask |= uint64_t(tensors[t]) << t;
+    }
+    elem_bits = x.out_bytes * 8;
+  }
+  st = plan_scatter(n_tensors, presents, pasts, updates, write_indices, shape, rank, axis,
+                    seq_len, mode, elem_bits, d_flags, xf ? &x : nullptr, &p, ranges, &nr);
   if (st != SWRT_OK) return st;
   ranges[nr++] = range(d_flags, 4, true);
   if (written_overlap(ranges, nr)) return SWRT_E_INVALID_ARG;
@@ -84,7 +106,10 @@ int scatter(int n_tensors, void *const *presents, const void *const *pasts,
   const int vec = word_of(p.align);
   if ((st = finish_scatter(&p, vec, kTile)) != SWRT_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return p.n == 1 ? dispatch<1>(p, vec, s) : dispatch<kMaxTensors>(p, vec, s);
+  if (xf)
+    return p.n == 1 ? dispatch<1, true>(p, vec, vmask, s)
+                    : dispatch<kMaxTensors, true>(p, vec, vmask, s);
+  return p.n == 1 ? dispatch<1, false>(p, vec, 0, s) : dispatch<kMaxTensors, false>(p, vec, 0, s);
 }
 
 }  // namespace
@@ -95,15 +120,17 @@ int scatter(int n_tensors, void *const *presents, const void *const *pasts,
 int plan_scatter(int n_tensors, void *const *presents, const void *const *pasts,
                  const void *const *updates, const int64_t *write_indices, const int64_t *shape,
                  int rank, int axis, int64_t seq_len, int mode, int elem_bits, uint32_t *d_flags,
-                 ScatterPlan *p, Range *ranges, int *nr) {
+                 const RowXf *xf, ScatterPlan *p, Range *ranges, int *nr) {
   p->empty = true;
   p->n = n_tensors;
+  p->xf = xf ? *xf : RowXf{};
   if (n_tensors < 0 || n_tensors > kMaxTensors) return SWRT_E_INVALID_ARG;
   if (!shape || rank < 2 || rank > SWRT_MAX_RANK) return SWRT_E_INVALID_ARG;
   for (int d = 0; d < rank; ++d)
     if (shape[d] < 0) return SWRT_E_INVALID_ARG;
   if (axis < 0) axis += rank;
   if (axis < 1 || axis >= rank) return SWRT_E_INVALID_ARG;  // never the batch axis
+  if (xf && axis != rank - 2) return SWRT_E_INVALID_ARG;     // a row is one head_dim
   if (mode != SWRT_MODE_LINEAR && mode != SWRT_MODE_CIRCULAR) return SWRT_E_INVALID_ARG;
   if (!valid_elem_bits(elem_bits)) return SWRT_E_INVALID_ARG;
   const int64_t M = shape[axis], S = seq_len, B = shape[0];
@@ -119,20 +146,26 @@ int plan_scatter(int n_tensors, void *const *presents, const void *const *pasts,
   const int64_t row = row_bits / 8;
   int64_t cache_bytes, upd_bytes;
   if (!mul_ok(O, M, &n_rows) || !mul_ok(n_rows, row, &cache_bytes)) return SWRT_E_UNSUPPORTED;
-  if (!mul_ok(O, S, &upd_rows) || !mul_ok(upd_rows, row, &upd_bytes)) return SWRT_E_UNSUPPORTED;
+  // update rows: the cache's elements, or the fused append's input elements
+  const int64_t upd_row = xf ? I * xf->in_bytes : row;
+  if (upd_row >= (int64_t(1) << 32)) return SWRT_E_UNSUPPORTED;
+  if (!mul_ok(O, S, &upd_rows) || !mul_ok(upd_rows, upd_row, &upd_bytes)) return SWRT_E_UNSUPPORTED;
   if (n_tensors == 0 || cache_bytes == 0) return SWRT_OK;
   if (!presents || !pasts || (upd_bytes > 0 && !updates)) return SWRT_E_INVALID_ARG;
 
   // every tensor is in place, or every tensor is out of place
   const bool in_place = presents[0] == pasts[0];
   const uint64_t align = elem_align(elem_bits);
+  const uint64_t upd_align = xf ? uint64_t(xf->in_bytes) : align;
   uint64_t acc = uint64_t(row);
   for (int t = 0; t < n_tensors; ++t) {
     const void *pr = presents[t], *pa = pasts[t], *up = upd_bytes > 0 ? updates[t] : nullptr;
     if (!pr || !pa || (upd_bytes > 0 && !up)) return SWRT_E_INVALID_ARG;
     if ((pr == pa) != in_place) return SWRT_E_INVALID_ARG;
-    if (addr_of(pr) % align || addr_of(pa) % align || addr_of(up) % align) return SWRT_E_INVALID_ARG;
-    acc |= addr_of(pr) | addr_of(pa) | addr_of(up);
+    if (addr_of(pr) % align || addr_of(pa) % align || addr_of(up) % upd_align)
+      return SWRT_E_INVALID_ARG;
+    // fused-append updates are read element by element: not part of the word
+    acc |= addr_of(pr) | addr_of(pa) | (xf ? 0 : addr_of(up));
     ranges[(*nr)++] = range(pr, uint64_t(cache_bytes), true);
     if (!in_place) ranges[(*nr)++] = range(pa, uint64_t(cache_bytes), false);
     ranges[(*nr)++] = range(up, uint64_t(upd_bytes), false);
@@ -155,6 +188,7 @@ int plan_scatter(int n_tensors, void *const *presents, const void *const *pasts,
   p->g.M = M;
   p->g.S = S;
   p->g.circular = mode == SWRT_MODE_CIRCULAR;
+  p->g.in_row_bytes = uint32_t(upd_row);
   p->empty = in_place && upd_bytes == 0;
   return SWRT_OK;
 }
@@ -182,7 +216,7 @@ extern "C" int swrt_tensor_scatter(void *present, const void *past, const void *
                                    int axis, int64_t seq_len, int mode, int elem_bits,
                                    uint32_t *d_flags, void *stream) {
   return swrt::scatter(1, &present, &past, &update, write_indices, shape, rank, axis, seq_len,
-                       mode, elem_bits, d_flags, stream);
+                       mode, elem_bits, nullptr, nullptr, d_flags, stream);
 }
 
 extern "C" int swrt_tensor_scatter_batched(int n_tensors, void *const *presents,
@@ -191,5 +225,16 @@ extern "C" int swrt_tensor_scatter_batched(int n_tensors, void *const *presents,
                                            int rank, int axis, int64_t seq_len, int mode,
                                            int elem_bits, uint32_t *d_flags, void *stream) {
   return swrt::scatter(n_tensors, presents, pasts, updates, write_indices, shape, rank, axis,
-                       seq_len, mode, elem_bits, d_flags, stream);
+                       seq_len, mode, elem_bits, nullptr, nullptr, d_flags, stream);
+}
+
+extern "C" int swrt_tensor_scatter_xf(int n_tensors, void *const *presents,
+                                      const void *const *pasts, const void *const *updates,
+                                      const int *tensors, const int64_t *write_indices,
+                                      const int64_t *shape, int rank, int64_t seq_len, int mode,
+                                      const swrt_row_transform *xf, uint32_t *d_flags,
+                                      void *stream) {
+  if (!xf) return SWRT_E_INVALID_ARG;
+  return swrt::scatter(n_tensors, presents, pasts, updates, write_indices, shape, rank, rank - 2,
+                       seq_len, mode, 8, xf, tensors, d_flags, stream);
 }

@@ -11,7 +11,7 @@
 // Used by kv_seq_lengths.hip, kv_window.hip and decode_step.hip.
 #pragma once
 
-#include "swrt_device.hpp"
+#include "xf_device.hpp"
 
 namespace swrt {
 
@@ -80,6 +80,7 @@ __device__ __forceinline__ StepLengths step_lengths(int32_t seqlens_k, int64_t S
 // ---------------------------------------------------------------------------
 struct WindowGeom {
   const int32_t *lp, *ev;    // Lp, E per batch entry (null when derived in-kernel)
+  const int64_t *past;       // absolute past lengths, the fused append's positions
   uint32_t *flags;
   int64_t nb_b, nb_h, nb_s;  // new-row strides, bytes
   uint64_t row_bytes;
@@ -118,6 +119,17 @@ __device__ __forceinline__ bool lengths_ok(const WindowGeom &g, const Slice &s, 
   return false;
 }
 
+// Fused append: the entry's positions [P, P + S) must have table rows.
+// Otherwise flag once per batch entry and skip it (the lengths were checked
+// first).
+__device__ __forceinline__ bool positions_ok(const WindowGeom &g, const RowXf &x, const Slice &s,
+                                             bool leader, int64_t P) {
+  if (xf_positions_ok(x, P, g.S)) return true;
+  if (g.flags && s.layer == 0 && s.t == 0 && s.h == 0 && leader)
+    atomicOr(g.flags, SWRT_FLAG_ROPE_RANGE);
+  return false;
+}
+
 // ---------------------------------------------------------------------------
 // S = 1, in place: one workgroup (BLOCK threads, UNROLL words each per tile)
 // shifts one slice by E rows and appends the new row at Lp - E.
@@ -134,20 +146,30 @@ __device__ __forceinline__ bool lengths_ok(const WindowGeom &g, const Slice &s, 
 // operations take effect in issue order, and every store is issued after the
 // load of its address, which keeps the same guarantee.
 // ---------------------------------------------------------------------------
-template <int VEC, int BLOCK = kWinBlock, int UNROLL = kWinUnroll>
+//
+// XF: the appended row is the transform *xf of new_row (tensor t, absolute
+// position pos) instead of a copy.
+template <int VEC, int BLOCK = kWinBlock, int UNROLL = kWinUnroll, bool XF = false>
 __device__ __forceinline__ void shift_append_slice(char *base, const char *new_row, int64_t Lp,
                                                    int64_t E, uint64_t row_bytes,
-                                                   uint32_t row_words) {
+                                                   uint32_t row_words, const RowXf *xf = nullptr,
+                                                   int t = 0, int64_t pos = 0) {
   using W = typename Word<VEC>::T;
   W *dst = reinterpret_cast<W *>(base);
   // The new row lives in its own buffer: fetch it first so its latency
   // overlaps the shift; it is stored at row Lp - E.
   const W *nsrc = reinterpret_cast<const W *>(new_row);
+  const auto new_word = [&](uint32_t i) -> W {
+    if constexpr (XF)
+      return xf_word<VEC>(*xf, t, new_row, pos, i);
+    else
+      return ld(nsrc + i);
+  };
   W *adst = reinterpret_cast<W *>(base + uint64_t(Lp - E) * row_bytes);
   const bool row_in_one_pass = row_words <= uint32_t(BLOCK);
   const uint32_t ai = min(threadIdx.x, row_words - 1);
   W nv;
-  if (row_in_one_pass) nv = ld(nsrc + ai);
+  if (row_in_one_pass) nv = new_word(ai);
   bool appended = false;
   if (E) {
     const W *src = reinterpret_cast<const W *>(base + uint64_t(E) * row_bytes);
@@ -172,7 +194,7 @@ __device__ __forceinline__ void shift_append_slice(char *base, const char *new_r
     if (row_in_one_pass) {
       st(adst + ai, nv);
     } else {
-      for (uint32_t i = threadIdx.x; i < row_words; i += BLOCK) st(adst + i, ld(nsrc + i));
+      for (uint32_t i = threadIdx.x; i < row_words; i += BLOCK) st(adst + i, new_word(i));
     }
   }
 }
@@ -199,6 +221,8 @@ struct SliceWork {
   char *base;           // row 0 of the slice
   const char *new_row;  // the appended row
   int64_t Lp, E;
+  int64_t pos;          // its absolute position (fused append)
+  int t;                // 0 = K, 1 = V
   bool ok;
 };
 
@@ -207,10 +231,10 @@ struct SliceWork {
 #endif
 constexpr int kGroupUnroll = SWRT_GROUP_UNROLL;  // words per lane per slice in group mode
 
-template <int VEC, int SPW, typename Info>
+template <int VEC, int SPW, bool XF = false, typename Info>
 __device__ __forceinline__ void shift_append_group(uint32_t first_slice, uint32_t n_slices,
                                                    uint64_t row_bytes, uint32_t row_words,
-                                                   Info info) {
+                                                   Info info, const RowXf *xf = nullptr) {
   using W = typename Word<VEC>::T;
   constexpr uint32_t GB = kWinBlock / SPW;  // threads per subgroup (a multiple of 64)
   static_assert(GB % 64 == 0, "subgroups must be whole waves");
@@ -237,7 +261,10 @@ __device__ __forceinline__ void shift_append_group(uint32_t first_slice, uint32_
   W *dst = reinterpret_cast<W *>(w.base);
   W v[kGroupUnroll], nv;
   if (w.ok) {
-    nv = ld(nsrc);
+    if constexpr (XF)
+      nv = xf_word<VEC>(*xf, w.t, w.new_row, w.pos, ai);
+    else
+      nv = ld(nsrc);
 #pragma unroll
     for (int u = 0; u < kGroupUnroll; ++u) v[u] = ld(n ? src + min(u * GB + lid, n - 1) : nsrc);
   }
@@ -262,10 +289,14 @@ inline int slices_per_group(int64_t capacity, uint32_t row_words) {
 
 // S > 1, STAGE: tile `tile` of staging[0 .. Lp+S): words of rows [0, Lp) from
 // the cache, of rows [Lp, Lp+S) from the (strided) new rows.
-template <int VEC>
+//
+// XF: new row r is the transform *xf of the given row (tensor t, absolute
+// position P + r).
+template <int VEC, bool XF = false>
 __device__ __forceinline__ void stage_tile(const WindowGeom &g, const char *cache_slice,
                                            char *stage_slice, const char *new_rows, int64_t Lp,
-                                           uint32_t tile) {
+                                           uint32_t tile, const RowXf *xf = nullptr, int t = 0,
+                                           int64_t P = 0) {
   using W = typename Word<VEC>::T;
   const uint32_t n_seed = uint32_t(Lp) * g.row_words;
   const uint32_t n = uint32_t(Lp + g.S) * g.row_words;
@@ -278,8 +309,12 @@ __device__ __forceinline__ void stage_tile(const WindowGeom &g, const char *cach
   for (int u = 0; u < kWinUnroll; ++u) {
     const uint32_t i = min(i0 + u * kWinBlock + threadIdx.x, n - 1);  // tail lanes repeat the last word
     const uint32_t j = i < n_seed ? 0 : i - n_seed, r = g.by_row.div(j), c = j - r * g.row_words;
-    const W *p = i < n_seed ? cache + i : reinterpret_cast<const W *>(new_rows + int64_t(r) * g.nb_s) + c;
-    v[u] = ld(p);
+    if constexpr (XF) {
+      v[u] = i < n_seed ? ld(cache + i) : xf_word<VEC>(*xf, t, new_rows + int64_t(r) * g.nb_s, P + r, c);
+    } else {
+      const W *p = i < n_seed ? cache + i : reinterpret_cast<const W *>(new_rows + int64_t(r) * g.nb_s) + c;
+      v[u] = ld(p);
+    }
   }
 #pragma unroll
   for (int u = 0; u < kWinUnroll; ++u) st(stage + min(i0 + u * kWinBlock + threadIdx.x, n - 1), v[u]);

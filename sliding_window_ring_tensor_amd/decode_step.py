@@ -14,7 +14,10 @@ each layer receives one new K row and one new V row per (batch, kv-head):
                               in place, one launch;
 
 or all three in one launch (kv_decode_step, the default), which writes the
-same bytes. The buffers are plain torch tensors on one device; the step only
+same bytes. With a fused-append workload (spec.new_dtype set) the new rows
+pass through the row transform on their way in (kv_window_append_xf,
+tensor_scatter_xf, kv_decode_step_xf): K rotated at position T - 1, every
+row converted or quantized into the caches' dtype. The buffers are plain torch tensors on one device; the step only
 issues library calls (marshalled once) on the current stream, so it can be
 captured in a graph.
 """
@@ -43,6 +46,7 @@ class StepBuffers:
     write_indices: torch.Tensor  # int64 [B], T - 1
     lengths: swrt.WindowLengths  # outputs of kv_seq_lengths
     flags: torch.Tensor          # int32 [1]
+    xf: swrt.Transform | None = None  # fused append
 
 
 class ModelDecodeStep:
@@ -54,12 +58,14 @@ class ModelDecodeStep:
         self.device = torch.device(device)
         B, H, D, W, M = spec.batch, spec.kv_heads, spec.head_dim, spec.window, spec.max_seq
         dt = spec.dtype
+        ndt = spec.new_dtype or dt  # new rows
         seed = spec.seed * 100 + set_id
 
         def buf(shape, bid):
+            t = ndt if shape[2] == 1 else dt
             if fill:
-                return wl.payload(shape, dt, seed, bid, self.device, raw_bits)
-            return torch.empty(shape, dtype=dt, device=self.device)
+                return wl.payload(shape, t, seed, bid, self.device, raw_bits and t == dt)
+            return torch.empty(shape, dtype=t, device=self.device)
 
         nw, nf = len(spec.windowed_layers), len(spec.full_layers)
         self.buffers = StepBuffers(
@@ -77,9 +83,31 @@ class ModelDecodeStep:
                 torch.int64, torch.int64, torch.int32, torch.int32, torch.int32))),
             flags=torch.zeros(1, dtype=torch.int32, device=self.device),
         )
+        if spec.new_dtype is not None:
+            cos = sin = None
+            if spec.rotary_dim:
+                cos, sin = wl.rope_tables(spec.rope_positions, spec.rotary_dim,
+                                          device=self.device)
+            self.buffers.xf = swrt.Transform(cos, sin, False, spec.k_scale, spec.v_scale)
 
     # -- the step ---------------------------------------------------------
     def _prepared(self):
+        if getattr(self, "_calls", None) is None and self.buffers.xf is not None:
+            b, s = self.buffers, self.spec
+            nf = len(b.full_k)
+            self._calls = {
+                "lengths": swrt.prepare_kv_seq_lengths(b.seqlens_k, 1, s.window, out=b.lengths,
+                                                       flags=b.flags),
+                "windowed": swrt.prepare_kv_window_append_xf(
+                    b.win_k, b.win_v, b.win_kn, b.win_vn, b.lengths.cache_past, b.lengths.evict,
+                    b.lengths.past, b.xf, flags=b.flags),
+                "full": swrt.prepare_tensor_scatter_xf(
+                    b.full_k + b.full_v, b.full_kn + b.full_vn, [0] * nf + [1] * nf,
+                    b.write_indices, b.xf, outs=b.full_k + b.full_v, flags=b.flags),
+                "fused": swrt.prepare_kv_decode_step_xf(
+                    b.win_k, b.win_v, b.win_kn, b.win_vn, b.seqlens_k, b.full_k, b.full_v,
+                    b.full_kn, b.full_vn, b.write_indices, b.xf, out=b.lengths, flags=b.flags),
+            }
         if getattr(self, "_calls", None) is None:
             b, s = self.buffers, self.spec
             caches = b.full_k + b.full_v
@@ -127,17 +155,21 @@ class ModelDecodeStep:
     # -- accounting -------------------------------------------------------
     def algorithmic_bytes(self) -> dict:
         """Bytes the method must move in one step: every byte read once and
-        written once. Windowed slice with E = 1: the Lp - 1 shifted rows and the
-        appended row, each read and written; with E = 0: the appended row.
-        Full cache: the written row, read from the update and written."""
+        written once. Windowed slice with E = 1: the Lp - 1 shifted rows, each
+        read and written, and the appended row (read as a new row, written as
+        a cache row); with E = 0: the appended row. Full cache: the written
+        row. A fused append also reads each batch entry's table row once (cos
+        and sin)."""
         s = self.spec
         row = s.head_dim * torch.empty((), dtype=s.dtype).element_size()
+        new_row = s.head_dim * torch.empty((), dtype=s.new_dtype or s.dtype).element_size()
         T = s.total_lens.astype(np.int64)
         P = T - 1
         Lp = np.minimum(P, s.window)
         E = np.maximum(0, Lp + 1 - s.window)
-        per_slice = 2 * row * (E * (Lp - E) + 1)
+        per_slice = 2 * row * E * (Lp - E) + row + new_row
         windowed = int(per_slice.sum()) * s.kv_heads * 2 * len(s.windowed_layers)
-        full = 2 * row * s.batch * s.kv_heads * 2 * len(s.full_layers)
-        return {"windowed": windowed, "full": full, "lengths": s.batch * (4 + 8 + 8 + 4 * 3),
-                "total": windowed + full}
+        full = (row + new_row) * s.batch * s.kv_heads * 2 * len(s.full_layers)
+        tables = s.batch * s.rotary_dim * 4 if s.new_dtype is not None else 0
+        return {"windowed": windowed, "full": full, "tables": tables,
+                "lengths": s.batch * (4 + 8 + 8 + 4 * 3), "total": windowed + full + tables}

@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the five KV-cache update workloads.
+"""Seeded synthetic inputs for the KV-cache update workloads.
 
 This module only draws inputs: shapes, seeded random payloads, write indices
 and lengths. It holds none of the update arithmetic, so both the GPU path's
@@ -25,6 +25,12 @@ Workloads (sizes and distributions):
      and odd layers full linear TensorScatter caches (K/V [64,8,8192,64]); new
      rows [64,8,1,64]; total length T ~ U{1..8192} shared by all layers;
      windowed seqlens_k = T - 1, full write index T - 1; bf16 or fp8 e4m3fn.
+  6  workload 5 as a loop of 200 consecutive decode steps (the benchmark
+     builds it from workload 5's draws).
+  7  workload 5 with the fused append: new rows bf16 [64,8,1,64] (U[-1,1)),
+     caches int8 (random bytes); K rows rotated at position T - 1 with
+     rotary_dim 64 (half-split pairs, tables cos/sin of p * 10000^(-2j/64),
+     8192 positions); K scale 0.02, V scale 0.01, zero points 0.
 """
 from __future__ import annotations
 
@@ -153,6 +159,12 @@ class ModelStep:
     seed: int
     windowed_layers: list = field(default_factory=list)
     full_layers: list = field(default_factory=list)
+    # fused append (new rows in new_dtype; caches in dtype), else None
+    new_dtype: torch.dtype | None = None
+    rotary_dim: int = 0
+    rope_positions: int = 0
+    k_scale: float = 1.0
+    v_scale: float = 1.0
 
 
 def workload1() -> ScatterCase:
@@ -230,6 +242,26 @@ def workload5(dtype: torch.dtype = torch.bfloat16) -> ModelStep:
     step.windowed_layers = [i for i in range(24) if i % 2 == 0]
     step.full_layers = [i for i in range(24) if i % 2 == 1]
     return step
+
+
+def workload7() -> ModelStep:
+    step = workload5(torch.int8)
+    step.seed = 7
+    step.new_dtype = torch.bfloat16
+    step.rotary_dim = 64
+    step.rope_positions = 8192
+    step.k_scale, step.v_scale = 0.02, 0.01
+    return step
+
+
+def rope_tables(positions: int, rotary_dim: int, base: float = 10000.0, device="cpu"):
+    """Rotary tables (inputs of the fused append): cos and sin of
+    p * base^(-2j / rotary_dim) for p < positions, j < rotary_dim / 2,
+    evaluated in float64 and stored as float32 [positions, rotary_dim / 2]."""
+    j = np.arange(rotary_dim // 2)
+    ang = np.arange(positions)[:, None] * base ** (-2.0 * j / rotary_dim)[None, :]
+    return (torch.from_numpy(np.cos(ang).astype(np.float32)).to(device),
+            torch.from_numpy(np.sin(ang).astype(np.float32)).to(device))
 
 
 def stratified_seqlens(g: np.random.Generator, batch: int, capacity: int, seq_len: int,

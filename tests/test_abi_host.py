@@ -48,6 +48,7 @@ def test_exports_every_declared_function(L):
     declared = set(re.findall(r"^(?:int|const char \*)\s*(swrt_\w+)\s*\(", _header(), re.M))
     assert {"swrt_tensor_scatter", "swrt_tensor_scatter_batched", "swrt_kv_seq_lengths", "swrt_kv_window_append",
             "swrt_kv_window_append_layers", "swrt_kv_decode_step", "swrt_kv_seq_lengths_drift",
+            "swrt_kv_window_append_xf", "swrt_tensor_scatter_xf", "swrt_kv_decode_step_xf",
             "swrt_status_string",
             "swrt_abi_version"} <= declared
     out = subprocess.run(["nm", "-D", "--defined-only", swrt.LIBRARY], check=True,
@@ -67,13 +68,24 @@ def test_constants_agree():
           "SWRT_FLAG_BAD_LENGTHS": swrt.FLAG_BAD_LENGTHS, "SWRT_MODE_LINEAR": swrt.MODE_LINEAR,
           "SWRT_MODE_CIRCULAR": swrt.MODE_CIRCULAR, "SWRT_PHASE_STAGE": swrt.PHASE_STAGE,
           "SWRT_PHASE_COMMIT": swrt.PHASE_COMMIT, "SWRT_PHASE_ALL": swrt.PHASE_ALL,
-          "SWRT_MAX_LAYERS": swrt.MAX_LAYERS, "SWRT_MAX_BATCHED": swrt.MAX_BATCHED}
+          "SWRT_MAX_LAYERS": swrt.MAX_LAYERS, "SWRT_MAX_BATCHED": swrt.MAX_BATCHED,
+          "SWRT_FLAG_ROPE_RANGE": swrt.FLAG_ROPE_RANGE,
+          "SWRT_XF_F32": swrt.XF_TYPES[torch.float32], "SWRT_XF_F16": swrt.XF_TYPES[torch.float16],
+          "SWRT_XF_BF16": swrt.XF_TYPES[torch.bfloat16], "SWRT_XF_INT8": swrt.XF_TYPES[torch.int8],
+          "SWRT_XF_UINT8": swrt.XF_TYPES[torch.uint8]}
     for k, v in py.items():
         assert int(defs[k]) == v, k
     # the oracle defines its own values; they must mean the same bits
     assert oracle.FLAG_LINEAR_OOB == swrt.FLAG_LINEAR_OOB
     assert oracle.FLAG_BAD_SEQLEN == swrt.FLAG_BAD_SEQLEN
     assert oracle.FLAG_BAD_LENGTHS == swrt.FLAG_BAD_LENGTHS
+    assert oracle.FLAG_ROPE_RANGE == swrt.FLAG_ROPE_RANGE
+    assert (oracle.XF_F32, oracle.XF_F16, oracle.XF_BF16, oracle.XF_INT8, oracle.XF_UINT8) == \
+        tuple(swrt.XF_TYPES[t] for t in (torch.float32, torch.float16, torch.bfloat16, torch.int8,
+                                          torch.uint8))
+    # the two transform structs have the same field layout
+    assert [f[0] for f in oracle.RowXf._fields_] == [f[0] for f in swrt.RowTransform._fields_]
+    assert ctypes.sizeof(oracle.RowXf) == ctypes.sizeof(swrt.RowTransform)
     assert (oracle.MODE_LINEAR, oracle.MODE_CIRCULAR) == (swrt.MODE_LINEAR, swrt.MODE_CIRCULAR)
     assert (oracle.PHASE_STAGE, oracle.PHASE_COMMIT, oracle.PHASE_ALL) == \
         (swrt.PHASE_STAGE, swrt.PHASE_COMMIT, swrt.PHASE_ALL)
@@ -241,3 +253,68 @@ def test_kv_decode_step_rejects(L):
     assert call(sk=D_ + 2) == INV                              # misaligned seqlens_k
     assert call(W=0) == INV and call(W=9) == INV               # window outside [1, C]
     assert call(nw=0, nf=0) == swrt.OK                         # nothing to do
+
+
+def _xf(in_type=1, out_type=4, cos=None, sin=None, max_pos=0, rot=0, scale=(0.5, 0.5), zp=(0, 0)):
+    x = swrt.RowTransform()
+    x.in_type, x.out_type = in_type, out_type
+    x.cos_table, x.sin_table = cos, sin
+    x.max_position, x.rotary_dim = max_pos, rot
+    x.scale[0], x.scale[1] = scale
+    x.zero_point[0], x.zero_point[1] = zp
+    return x
+
+
+@no_gpu_visible
+def test_fused_append_rejects(L):
+    """Bad transforms and buffers are refused before any launch; good ones get
+    as far as the launch (which fails here: no GPU is visible, and these
+    made-up addresses are never dereferenced)."""
+    INV, V = swrt.E_INVALID_ARG, ctypes.c_void_p
+    launched = (swrt.OK, swrt.E_LAUNCH)
+    arr = lambda *p: (V * len(p))(*p)  # noqa: E731
+
+    def win(x, kc=A, kn=B_, S=1, D=16, strides=None, past=D_ + 0x2000):
+        st = (I64 * 3)(*(strides or (2 * S * D, S * D, D)))
+        return L.swrt_kv_window_append_xf(1, arr(kc), arr(kc + 0x1000_0000), arr(kn),
+                                          arr(kn + 0x1000_0000), st, None, None, D_, D_ + 0x1000,
+                                          past, 2, 2, 8, S, D, 3,
+                                          None if x is None else ctypes.byref(x), None, None)
+    tab = C_
+    ok = _xf(cos=tab, sin=tab + 0x1000, max_pos=64, rot=16)
+    assert win(None) == INV                                              # no transform
+    assert win(_xf(in_type=4)) == INV                                    # int8 new rows
+    assert win(_xf(out_type=9)) == INV
+    assert win(_xf(scale=(0.0, 1.0))) == INV and win(_xf(scale=(1.0, float("inf")))) == INV
+    assert win(_xf(scale=(float("nan"), 1.0))) == INV
+    assert win(_xf(zp=(128, 0))) == INV and win(_xf(out_type=5, zp=(0, -1))) == INV
+    assert win(_xf(cos=tab, sin=None, max_pos=64, rot=16)) == INV      # one table only
+    assert win(_xf(cos=tab, sin=tab + 0x1000, max_pos=0, rot=16)) == INV
+    assert win(_xf(cos=tab, sin=tab + 0x1000, max_pos=64, rot=15)) == INV
+    assert win(_xf(cos=tab, sin=tab + 0x1000, max_pos=64, rot=18)) == INV  # > head_dim
+    assert win(_xf(cos=tab + 2, sin=tab + 0x1000, max_pos=64, rot=16)) == INV  # misaligned
+    assert win(_xf(cos=A + 64, sin=tab + 0x1000, max_pos=64, rot=16)) == INV   # table in a cache
+    assert win(ok, past=0) == INV and win(ok, past=D_ + 0x2004) == INV   # past_lens
+    assert win(ok, kn=B_ + 2) == INV                                     # f32 rows misaligned
+    assert win(ok) in launched and win(ok, kn=B_ + 4) in launched       # element alignment
+    assert win(_xf(in_type=3, out_type=3)) in launched
+
+    def ts(x, rank=4, tensors=(0, 1), n=2, mode=0):
+        shape = _shape(*((2, 3, 16, 8) if rank == 4 else (2, 16)))
+        t = (ctypes.c_int * 2)(*tensors)
+        return L.swrt_tensor_scatter_xf(n, arr(A, A + 0x1000_0000), arr(A, A + 0x1000_0000),
+                                        arr(B_, B_ + 0x1000_0000), t, None, shape, rank, 2, mode,
+                                        None if x is None else ctypes.byref(x), None, None)
+    assert ts(None) == INV and ts(ok, rank=2) == INV and ts(ok, tensors=(0, 2)) == INV
+    assert ts(_xf(cos=tab, sin=tab + 0x1000, max_pos=64, rot=10)) == INV  # > head_dim 8
+    assert ts(_xf()) in launched and ts(_xf(), mode=1) in launched
+
+    def dec(x, nfl=1):
+        return L.swrt_kv_decode_step_xf(1, arr(A), arr(A + 0x1000_0000), arr(B_),
+                                        arr(B_ + 0x1000), (I64 * 3)(32, 16, 16), D_, 8, 8, None,
+                                        None, None, None, None, nfl, arr(C_ + 0x10_0000),
+                                        arr(C_ + 0x20_0000), arr(B_ + 0x2000), arr(B_ + 0x3000),
+                                        D_ + 0x1000, 16, 2, 2, 16,
+                                        None if x is None else ctypes.byref(x), None, None)
+    assert dec(None) == INV and dec(_xf(), nfl=33) == INV and dec(_xf(), nfl=-1) == INV
+    assert dec(_xf()) in launched
