@@ -9,6 +9,9 @@ A step is one launch of kv_decode_step (default), or with --form three the
 three-call composition: kv_seq_lengths, kv_window_append_layers (all 12
 windowed layers, in place) and tensor_scatter_batched (all 24 full caches).
 Both forms are timed in every run; --form picks the one `value` reports.
+--workload 7 is the same step with the fused append: bf16 new rows, K rotated
+at its absolute position, int8 caches (kv_decode_step_xf, or the three xf
+calls).
 
 Measurement
   - value: algorithmic bytes of a step / time of a step, from K steps bracketed
@@ -80,6 +83,8 @@ def cpu_baseline(step, seconds: float):
 
     orc = oracle.get()
     spec, b = step.spec, step.buffers
+    if b.xf is not None:
+        return cpu_baseline_xf(orc, step, seconds)
     D, H = spec.head_dim, spec.kv_heads
     bits = torch.empty((), dtype=spec.dtype).element_size() * 8
 
@@ -97,19 +102,67 @@ def cpu_baseline(step, seconds: float):
             for _ in range(2 * len(spec.full_layers))]
     fnew = [host(t) for t in b.full_kn + b.full_vn]
     sk = spec.seqlens_k
-    n, t0 = 0, time.perf_counter()
-    while True:
+
+    def one_step():
         L = orc.kv_seq_lengths(sk, 1, spec.window)
         for i in range(len(wk)):
             orc.kv_window_append_strided(wk[i], wv[i], wkn[i], wvn[i], (H * D, D, D), 1,
                                          L.cache_past, L.evict, elem_bits=bits, head_dim=D)
         for c, u in zip(full, fnew):
             orc.tensor_scatter_raw(c, c, u, spec.write_indices, full_shape, 2, 1, 0, bits)
+
+    return _time_steps(one_step, seconds)
+
+
+def _time_steps(one_step, seconds: float):
+    """One untimed step (the host pages of the written rows are mapped on
+    first touch), then steps until `seconds` have passed."""
+    one_step()
+    n, t0 = 0, time.perf_counter()
+    while True:
+        one_step()
         n += 1
         el = time.perf_counter() - t0
         if el >= seconds:
             break
     return n, el
+
+
+def cpu_baseline_xf(orc, step, seconds: float):
+    """cpu_baseline for the fused-append step (workload 7)."""
+    import oracle
+
+    spec, b = step.spec, step.buffers
+    D, H = spec.head_dim, spec.kv_heads
+
+    def host(t):
+        return t.detach().cpu().contiguous().view(torch.uint8).numpy()
+
+    types = {torch.bfloat16: oracle.XF_BF16, torch.float16: oracle.XF_F16,
+             torch.float32: oracle.XF_F32, torch.int8: oracle.XF_INT8, torch.uint8: oracle.XF_UINT8}
+    x = b.xf
+    xo = oracle.Transform(types[spec.new_dtype], types[spec.dtype],
+                          None if x.cos is None else x.cos.cpu().numpy(),
+                          None if x.sin is None else x.sin.cpu().numpy(),
+                          0 if x.cos is None else 2 * x.cos.shape[1], x.interleaved,
+                          (x.k_scale, x.v_scale), (x.k_zero_point, x.v_zero_point))
+    wk = [host(t).copy() for t in b.win_k]
+    wv = [host(t).copy() for t in b.win_v]
+    wkn, wvn = [host(t) for t in b.win_kn], [host(t) for t in b.win_vn]
+    row = D * torch.empty((), dtype=spec.dtype).element_size()
+    # full caches: only the written rows are touched (see cpu_baseline)
+    nf = len(spec.full_layers)
+    full = [np.empty((spec.batch, H, spec.max_seq, row), np.uint8) for _ in range(2 * nf)]
+    fnew = [host(t) for t in b.full_kn + b.full_vn]
+    def one_step():
+        L = orc.kv_seq_lengths(spec.seqlens_k, 1, spec.window)
+        for i in range(len(wk)):
+            orc.kv_window_append_xf(xo, wk[i], wv[i], wkn[i], wvn[i], (H * D, D, D), 1,
+                                    L.cache_past, L.evict, L.past)
+        for i, (c, u) in enumerate(zip(full, fnew)):
+            orc.tensor_scatter_xf(xo, i // nf, c, c, u, spec.write_indices)
+
+    return _time_steps(one_step, seconds)
 
 
 def _timers(stream, K, W):
@@ -353,10 +406,11 @@ def main():
                     help="one launch per step (default) or the three-call composition")
     ap.add_argument("--timing", default="eager", choices=["eager", "graph"],
                     help="the timed loop `value` reports (both are measured)")
-    ap.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5, 6],
+    ap.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5, 6, 7],
                     help="5: the whole-model decode step (default); 1-4: the other workloads; "
                          "6: workload 5's decode loop with drifting windowed caches "
-                         "(capacity W + --slack), one line each, for the design notes")
+                         "(capacity W + --slack); 7: workload 5 with the fused append (bf16 "
+                         "rows, RoPE on K, int8 caches); one line each, for the design notes")
     ap.add_argument("--slack", type=int, default=16, help="workload 6: capacity - window")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -376,9 +430,11 @@ def main():
     torch.cuda.set_device(dev)
     if args.workload == 6:
         return drift_loop(args, dev)
-    if args.workload != 5:
+    if args.workload not in (5, 7):
         return other_workload(args, dev)
-    spec = wl.workload5(wl.DTYPES[args.dtype])
+    xf = args.workload == 7
+    spec = wl.workload7() if xf else wl.workload5(wl.DTYPES[args.dtype])
+    dtype_label = "bf16->int8" if xf else args.dtype
     log(f"allocating {args.sets} buffer sets ...")
     steps = [ModelDecodeStep(spec, dev, set_id=i) for i in range(args.sets)]
     acct = steps[0].algorithmic_bytes()
@@ -493,14 +549,16 @@ def main():
     else:
         step_s = graph_fused_s if fused else graph_three_s
     value = acct["total"] / step_s / 1e9
+    fx = " with the fused append (RoPE on K, int8 quantization)" if xf else ""
     if fused:
         kname, kbytes, kmean = "decode_step_kernel", acct["total"], fused_mean_s
-        kdesc = "decode_step_kernel: the whole step in one launch (lengths, 12 windowed layers, 24 full caches)"
+        kdesc = ("decode_step_kernel: the whole step in one launch (lengths, 12 windowed layers, "
+                 f"24 full caches){fx}")
     else:
         kname, kbytes, kmean = "window_in_place", acct["windowed"], win_mean_s
-        kdesc = "window_in_place: 12 windowed layers, K and V, one launch"
+        kdesc = f"window_in_place: 12 windowed layers, K and V, one launch{fx}"
     achieved = kbytes / kmean / 1e9
-    meas = MEASURED_TRAFFIC.get((args.dtype, kname, kernel_source_hash(kname)))
+    meas = MEASURED_TRAFFIC.get((dtype_label, kname, kernel_source_hash(kname)))
     traffic = None if meas is None else meas["read"] + meas["written"]
 
     cpu = None
@@ -526,18 +584,24 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": args.dtype,
+        "dtype": dtype_label,
         "data": "synthetic",
         "config": {
             "workload": f"whole-model decode-step KV-cache update, {spec.layers} layers "
                         f"({len(spec.windowed_layers)} windowed C={spec.window}, "
                         f"{len(spec.full_layers)} full linear TensorScatter max_seq={spec.max_seq}), "
                         f"B={spec.batch}, H_kv={spec.kv_heads}, D={spec.head_dim}, "
-                        f"T~U[1,8192] seed {spec.seed}",
+                        f"T~U[1,8192] seed {spec.seed}" + (
+                            f"; fused append: bf16 new rows, K rotated at position T-1 "
+                            f"(rotary_dim {spec.rotary_dim}), int8 caches, K scale "
+                            f"{spec.k_scale}, V scale {spec.v_scale}" if xf else ""),
             "bytes_per_step": acct["total"],
-            "form": "one launch per step (kv_decode_step)" if fused else
-                    "three launches per step (kv_seq_lengths, kv_window_append_layers, "
-                    "tensor_scatter_batched)",
+            "form": ("one launch per step (kv_decode_step_xf)" if xf else
+                     "one launch per step (kv_decode_step)") if fused else
+                    ("three launches per step (kv_seq_lengths, kv_window_append_xf, "
+                     "tensor_scatter_xf)" if xf else
+                     "three launches per step (kv_seq_lengths, kv_window_append_layers, "
+                     "tensor_scatter_batched)"),
             "timing": "eager: library calls with arguments marshalled once, K steps between "
                       "two synchronizations" if args.timing == "eager" else
                       "HIP graph replay, one graph per buffer set",

@@ -394,7 +394,8 @@ typedef struct swrt_row_transform {
  * d_flags    as for swrt_kv_window_append, and then SWRT_FLAG_ROPE_RANGE when
  *            rotating and P < 0 or P + S > max_position: that batch entry is
  *            left untouched, K and V, cache and staging (every phase checks).
- * Errors: SWRT_E_INVALID_ARG also for a transform outside the ranges above.
+ * Errors: SWRT_E_INVALID_ARG also for a transform outside the ranges above;
+ * SWRT_E_UNSUPPORTED for S = 1 with head_dim > 4096.
  */
 int swrt_kv_window_append_xf(int n_layers, void *const *k_caches,
                              void *const *v_caches, const void *const *k_news,
@@ -434,6 +435,8 @@ int swrt_tensor_scatter_xf(int n_tensors, void *const *presents,
  * launch. Full caches come as n_full_layers K and V pairs
  * (full_k_caches[i], full_v_caches[i]) with their new rows. Windowed caches
  * hold out_type elements; new rows are in_type. d_flags as for those calls.
+ * n_full_layers: 0 .. SWRT_MAX_BATCHED / 2. SWRT_E_UNSUPPORTED for head_dim
+ * above 4096 (above 512 when window < capacity).
  */
 int swrt_kv_decode_step_xf(int n_window_layers, void *const *win_k_caches,
                            void *const *win_v_caches,

@@ -65,9 +65,11 @@ __global__ __launch_bounds__(BLOCK) void decode_step_kernel(DecodeArgs a) {
   }
   if (bid < a.full_blocks) {  // full caches: TensorScatter rows in place
     const uint32_t t = bid / a.full_tiles;
-    scatter_in_place_tile<VEC, BLOCK, XF>(a.sg, a.fc[t], a.fu[t],
-                                          (bid - t * a.full_tiles) * kFullTile, tb, &a.xf,
-                                          int(t & 1));
+    // fused append: 4-byte words at most, so each lane transforms few elements
+    constexpr int VS = XF && VEC > 4 ? 4 : VEC;
+    scatter_in_place_tile<VS, BLOCK, XF>(a.sg, a.fc[t], a.fu[t],
+                                         (bid - t * a.full_tiles) * kFullTile, tb, &a.xf,
+                                         int(t & 1));
     return;
   }
   const uint32_t wb = bid - a.full_blocks;
@@ -191,7 +193,9 @@ int decode_step(int n_window_layers, void *const *win_k_caches, void *const *win
   // the drifting layout runs the one-wave shape (see decode_step_kernel)
   const bool drift = window < capacity;
   const int block = drift ? kWaveBlock : kWinBlock;
-  if (!sp.empty && (st = finish_scatter(&sp, vec, uint32_t(block * kScatUnroll))) != SWRT_OK)
+  if (xf && head_dim > kXfLaneElems * block) return SWRT_E_UNSUPPORTED;  // XfLanes per lane
+  const int vec_s = xf && vec > 4 ? 4 : vec;  // the full caches' word (see decode_step_kernel)
+  if (!sp.empty && (st = finish_scatter(&sp, vec_s, uint32_t(block * kScatUnroll))) != SWRT_OK)
     return st;
 
   static_assert(sizeof(DecodeArgs) <= 4096, "kernel arguments exceed 4 KiB");

@@ -161,6 +161,8 @@ int window_append(int n_layers, void *const *k_caches, void *const *v_caches,
   if (xf) {
     if ((st = plan_xf(xf, head_dim, &x, ranges, &nr)) != SWRT_OK) return st;
     elem_bits = x.out_bytes * 8;
+    // in place, the appended row is spread over one workgroup's lanes
+    if (seq_len == 1 && head_dim > kXfLaneElems * kWinBlock) return SWRT_E_UNSUPPORTED;
   }
   st = plan_window(n_layers, k_caches, v_caches, k_news, v_news, new_strides, k_stagings,
                    v_stagings, cache_past_lens, evict_counts, false, batch, kv_heads, capacity,

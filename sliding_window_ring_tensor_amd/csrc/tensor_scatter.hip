@@ -103,7 +103,8 @@ int scatter(int n_tensors, void *const *presents, const void *const *pasts,
   ranges[nr++] = range(d_flags, 4, true);
   if (written_overlap(ranges, nr)) return SWRT_E_INVALID_ARG;
   if (p.empty) return SWRT_OK;
-  const int vec = word_of(p.align);
+  int vec = word_of(p.align);
+  if (xf && vec > 4) vec = 4;  // fused append: few elements to transform per lane
   if ((st = finish_scatter(&p, vec, kTile)) != SWRT_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (xf)

@@ -157,19 +157,27 @@ __device__ __forceinline__ void shift_append_slice(char *base, const char *new_r
   using W = typename Word<VEC>::T;
   W *dst = reinterpret_cast<W *>(base);
   // The new row lives in its own buffer: fetch it first so its latency
-  // overlaps the shift; it is stored at row Lp - E.
+  // overlaps the shift; it is stored at row Lp - E. (XF: its elements, one
+  // or a few per lane, as XfLanes.)
   const W *nsrc = reinterpret_cast<const W *>(new_row);
-  const auto new_word = [&](uint32_t i) -> W {
-    if constexpr (XF)
-      return xf_word<VEC>(*xf, t, new_row, pos, i);
-    else
-      return ld(nsrc + i);
-  };
   W *adst = reinterpret_cast<W *>(base + uint64_t(Lp - E) * row_bytes);
-  const bool row_in_one_pass = row_words <= uint32_t(BLOCK);
+  const bool row_in_one_pass = XF || row_words <= uint32_t(BLOCK);
   const uint32_t ai = min(threadIdx.x, row_words - 1);
   W nv;
-  if (row_in_one_pass) nv = new_word(ai);
+  XfLanes xl;
+  uint32_t D = 0;
+  // XF: the row's loads go out right after the first tile's (or alone when
+  // nothing shifts), never ahead of a wait the shift's addresses need
+  if constexpr (XF)
+    D = uint32_t(row_bytes) / uint32_t(xf->out_bytes);
+  else if (row_in_one_pass)
+    nv = ld(nsrc + ai);
+  const auto append = [&]() {
+    if constexpr (XF)
+      xf_lanes_store(xl, *xf, t, reinterpret_cast<char *>(adst), threadIdx.x, BLOCK, D);
+    else
+      st(adst + ai, nv);
+  };
   bool appended = false;
   if (E) {
     const W *src = reinterpret_cast<const W *>(base + uint64_t(E) * row_bytes);
@@ -178,23 +186,34 @@ __device__ __forceinline__ void shift_append_slice(char *base, const char *new_r
       W v[UNROLL];
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u) v[u] = ld(src + min(c0 + u * BLOCK + threadIdx.x, n - 1));
+      if constexpr (XF) {
+        if (c0 == 0) xf_lanes_load(xl, *xf, t, new_row, pos, threadIdx.x, BLOCK, D);
+        xf_lanes_hold(xl);
+      }
       __syncthreads();  // every old value of this tile is in registers
       // Row Lp - E is no shift destination, and from here on every load of
       // every tile (this last one's included) has returned: the new row can
-      // go out now.
-      if (row_in_one_pass && c0 + uint32_t(BLOCK * UNROLL) >= n) {
-        st(adst + ai, nv);
+      // go out now (a copy before the tile's stores; a transformed row after
+      // them, so its arithmetic overlaps their draining).
+      const bool last = row_in_one_pass && c0 + uint32_t(BLOCK * UNROLL) >= n;
+      if (!XF && last) {
+        append();
         appended = true;
       }
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u) st(dst + min(c0 + u * BLOCK + threadIdx.x, n - 1), v[u]);
+      if (XF && last) {
+        append();
+        appended = true;
+      }
     }
   }
   if (!appended) {  // no shift, or a row wider than one pass: after every load
     if (row_in_one_pass) {
-      st(adst + ai, nv);
+      if constexpr (XF) xf_lanes_load(xl, *xf, t, new_row, pos, threadIdx.x, BLOCK, D);
+      append();
     } else {
-      for (uint32_t i = threadIdx.x; i < row_words; i += BLOCK) st(adst + i, new_word(i));
+      for (uint32_t i = threadIdx.x; i < row_words; i += BLOCK) st(adst + i, ld(nsrc + i));
     }
   }
 }
@@ -260,19 +279,38 @@ __device__ __forceinline__ void shift_append_group(uint32_t first_slice, uint32_
   const W *src = reinterpret_cast<const W *>(w.base + uint64_t(w.E) * row_bytes);
   W *dst = reinterpret_cast<W *>(w.base);
   W v[kGroupUnroll], nv;
+  XfLanes xl;
+  const uint32_t D = XF ? uint32_t(row_bytes) / uint32_t(xf->out_bytes) : 0;
   if (w.ok) {
-    if constexpr (XF)
-      nv = xf_word<VEC>(*xf, w.t, w.new_row, w.pos, ai);
-    else
+    if constexpr (XF) {
+      // the appended row is transformed, not copied: a slice with nothing to
+      // shift (n = 0, uniform in the subgroup) moves no words at all; the
+      // row's loads follow the shift's (no wait for them precedes a shift load)
+      if (n) {
+#pragma unroll
+        for (int u = 0; u < kGroupUnroll; ++u) v[u] = ld(src + min(u * GB + lid, n - 1));
+      }
+      xf_lanes_load(xl, *xf, w.t, w.new_row, w.pos, lid, GB, D);
+      xf_lanes_hold(xl);
+    } else {
       nv = ld(nsrc);
 #pragma unroll
-    for (int u = 0; u < kGroupUnroll; ++u) v[u] = ld(n ? src + min(u * GB + lid, n - 1) : nsrc);
+      for (int u = 0; u < kGroupUnroll; ++u) v[u] = ld(n ? src + min(u * GB + lid, n - 1) : nsrc);
+    }
   }
   __syncthreads();  // every old value of every slice of the workgroup is in registers
   if (w.ok) {
+    if constexpr (XF) {  // the shift's stores first: the transform overlaps them
+      if (n) {
 #pragma unroll
-    for (int u = 0; u < kGroupUnroll; ++u) st(n ? dst + min(u * GB + lid, n - 1) : adst, v[u]);
-    st(adst, nv);
+        for (int u = 0; u < kGroupUnroll; ++u) st(dst + min(u * GB + lid, n - 1), v[u]);
+      }
+      xf_lanes_store(xl, *xf, w.t, w.base + uint64_t(w.Lp - w.E) * row_bytes, lid, GB, D);
+    } else {
+#pragma unroll
+      for (int u = 0; u < kGroupUnroll; ++u) st(n ? dst + min(u * GB + lid, n - 1) : adst, v[u]);
+      st(adst, nv);
+    }
   }
 }
 

@@ -46,13 +46,6 @@ __device__ __forceinline__ bool xf_positions_ok(const RowXf &x, int64_t p0, int6
   return !x.cos || (p0 >= 0 && p0 <= x.max_pos - n);
 }
 
-__device__ __forceinline__ float xf_in(const RowXf &x, const char *row, uint32_t e) {
-  if (x.in_type == SWRT_XF_F32) return reinterpret_cast<const float *>(row)[e];
-  const uint16_t h = reinterpret_cast<const uint16_t *>(row)[e];
-  if (x.in_type == SWRT_XF_BF16) return __uint_as_float(uint32_t(h) << 16);
-  return float(__builtin_bit_cast(_Float16, h));
-}
-
 // binary32 -> bf16 bits, round to nearest even (a carry into the exponent is
 // the correct next value, infinity included)
 __device__ __forceinline__ uint16_t xf_bf16(float f) {
@@ -66,32 +59,63 @@ __device__ __forceinline__ uint16_t xf_f16(float f) {
   return __builtin_bit_cast(uint16_t, _Float16(f));  // hardware conversion, nearest even
 }
 
-__device__ __forceinline__ int32_t xf_code(const RowXf &x, int t, float y) {
-  if (y != y) return x.zero[t];
-  float q = __builtin_rintf(y / x.scale[t]) + float(x.zero[t]);
+__device__ __forceinline__ int32_t xf_code_of(const RowXf &x, float scale, int32_t zero, float y) {
+  if (y != y) return zero;
+  float q = __builtin_rintf(y / scale) + float(zero);
   q = fminf(fmaxf(q, float(x.lo)), float(x.hi));
   return int32_t(q);
 }
 
-// element e of the row after the rotation (K with tables) or as it is
-template <bool ROT>
-__device__ __forceinline__ float xf_element(const RowXf &x, const char *row, const float *cr,
-                                            const float *sr, uint32_t e) {
+__device__ __forceinline__ int32_t xf_code(const RowXf &x, int t, float y) {
+  return xf_code_of(x, t ? x.scale[1] : x.scale[0], t ? x.zero[1] : x.zero[0], y);
+}
+
+// the input element e of a row as float, the input type fixed at compile time
+template <int IN>
+__device__ __forceinline__ uint32_t xf_raw_t(const char *row, uint32_t e) {
+  if constexpr (IN == SWRT_XF_F32)
+    return reinterpret_cast<const uint32_t *>(row)[e];
+  else
+    return uint32_t(reinterpret_cast<const uint16_t *>(row)[e]);
+}
+
+template <int IN>
+__device__ __forceinline__ float xf_decode_t(uint32_t r) {
+  if constexpr (IN == SWRT_XF_F32)
+    return __uint_as_float(r);
+  else if constexpr (IN == SWRT_XF_BF16)
+    return __uint_as_float(r << 16);
+  else
+    return float(__builtin_bit_cast(_Float16, uint16_t(r)));
+}
+
+// element e < rotary_dim: is it the first of its pair, its table column j and
+// its partner pe
+__device__ __forceinline__ void xf_pair(const RowXf &x, uint32_t e, bool &first, uint32_t &j,
+                                        uint32_t &pe) {
+  const uint32_t h = uint32_t(x.half);
+  first = x.interleaved ? (e & 1u) == 0 : e < h;
+  j = x.interleaved ? e >> 1 : (first ? e : e - h);
+  pe = x.interleaved ? (e ^ 1u) : (first ? e + h : e - h);
+}
+
+// one output element from its raw input, its partner's and its table entries
+template <int IN>
+__device__ __forceinline__ float xf_rotate(const RowXf &x, bool rot, uint32_t e, uint32_t xr,
+                                           uint32_t pr, float c, float s) {
 #pragma clang fp contract(off)
-  float v = xf_in(x, row, e);
-  if (ROT && e < uint32_t(2 * x.half)) {
-    const uint32_t h = uint32_t(x.half);
-    const bool first = x.interleaved ? (e & 1u) == 0 : e < h;
-    const uint32_t j = x.interleaved ? e >> 1 : (first ? e : e - h);
-    const uint32_t pe = x.interleaved ? (e ^ 1u) : (first ? e + h : e - h);
-    const float p = xf_in(x, row, pe);
-    const float vc = v * cr[j], ps = p * sr[j];
+  float v = xf_decode_t<IN>(xr);
+  if (rot && e < uint32_t(2 * x.half)) {
+    bool first;
+    uint32_t j, pe;
+    xf_pair(x, e, first, j, pe);
+    const float vc = v * c, ps = xf_decode_t<IN>(pr) * s;
     v = first ? vc - ps : vc + ps;
   }
   return v;
 }
 
-template <int VEC, int OB, bool ROT>
+template <int VEC, int IN, int OB, bool ROT>
 __device__ __forceinline__ typename Word<VEC>::T xf_word_of(const RowXf &x, int t, const char *row,
                                                             const float *cr, const float *sr,
                                                             uint32_t i) {
@@ -99,9 +123,27 @@ __device__ __forceinline__ typename Word<VEC>::T xf_word_of(const RowXf &x, int 
   constexpr int N = VEC / OB;  // elements in the word
   uint8_t b[VEC] = {};
   if constexpr (N >= 1) {
+    // every load first (straight-line), then the arithmetic
+    uint32_t xr[N], pr[N];
+    float c[N], s[N];
 #pragma unroll
     for (int k = 0; k < N; ++k) {
-      const float v = xf_element<ROT>(x, row, cr, sr, i * N + k);
+      const uint32_t e = i * N + k;
+      xr[k] = xf_raw_t<IN>(row, e);
+      pr[k] = 0;
+      c[k] = s[k] = 0.0f;
+      if constexpr (ROT) {
+        bool first;
+        uint32_t j, pe;
+        xf_pair(x, min(e, uint32_t(2 * x.half) - 1), first, j, pe);
+        pr[k] = xf_raw_t<IN>(row, pe);
+        c[k] = cr[j];
+        s[k] = sr[j];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+      const float v = xf_rotate<IN>(x, ROT, i * N + k, xr[k], pr[k], c[k], s[k]);
       if constexpr (OB == 4) {
         const uint32_t u = v != v ? 0x7FC00000u : __float_as_uint(v);
         __builtin_memcpy(b + 4 * k, &u, 4);
@@ -118,21 +160,154 @@ __device__ __forceinline__ typename Word<VEC>::T xf_word_of(const RowXf &x, int 
   return w;
 }
 
+template <int VEC, int IN>
+__device__ __forceinline__ typename Word<VEC>::T xf_word_in(const RowXf &x, int t, const char *row,
+                                                            int64_t pos, uint32_t i) {
+  if (t == 0 && x.cos) {
+    const float *cr = x.cos + pos * x.half, *sr = x.sin + pos * x.half;
+    if (x.out_bytes == 1) return xf_word_of<VEC, IN, 1, true>(x, t, row, cr, sr, i);
+    if (x.out_bytes == 2) return xf_word_of<VEC, IN, 2, true>(x, t, row, cr, sr, i);
+    return xf_word_of<VEC, IN, 4, true>(x, t, row, cr, sr, i);
+  }
+  if (x.out_bytes == 1) return xf_word_of<VEC, IN, 1, false>(x, t, row, nullptr, nullptr, i);
+  if (x.out_bytes == 2) return xf_word_of<VEC, IN, 2, false>(x, t, row, nullptr, nullptr, i);
+  return xf_word_of<VEC, IN, 4, false>(x, t, row, nullptr, nullptr, i);
+}
+
 // Word i (VEC bytes of out_type elements) of the transform of `row`, tensor t
 // (0 = K, rotated when tables are given; 1 = V) at absolute position pos.
 // The cache's element alignment makes VEC a multiple of out_bytes.
 template <int VEC>
 __device__ __forceinline__ typename Word<VEC>::T xf_word(const RowXf &x, int t, const char *row,
                                                          int64_t pos, uint32_t i) {
-  if (t == 0 && x.cos) {
-    const float *cr = x.cos + pos * x.half, *sr = x.sin + pos * x.half;
-    if (x.out_bytes == 1) return xf_word_of<VEC, 1, true>(x, t, row, cr, sr, i);
-    if (x.out_bytes == 2) return xf_word_of<VEC, 2, true>(x, t, row, cr, sr, i);
-    return xf_word_of<VEC, 4, true>(x, t, row, cr, sr, i);
+  if (x.in_type == SWRT_XF_F32) return xf_word_in<VEC, SWRT_XF_F32>(x, t, row, pos, i);
+  if (x.in_type == SWRT_XF_BF16) return xf_word_in<VEC, SWRT_XF_BF16>(x, t, row, pos, i);
+  return xf_word_in<VEC, SWRT_XF_F16>(x, t, row, pos, i);
+}
+
+// ---------------------------------------------------------------------------
+// The appended row of an in-place windowed step, spread over the slice's
+// lanes: element e belongs to lane e mod n (n lanes, at most kXfLaneElems
+// elements each). Its raw input bits, its partner's and its table entries are
+// loaded before the shift's loads and turned into cache elements after the
+// shift's barrier, so their latency overlaps the shift and each lane's
+// arithmetic stays a few elements long. Lanes past the row load its last
+// element and store nothing.
+// ---------------------------------------------------------------------------
+constexpr int kXfLaneElems = 8;
+
+struct XfLanes {
+  uint32_t x[kXfLaneElems], p[kXfLaneElems];  // raw bits of the element and its partner
+  float c[kXfLaneElems], s[kXfLaneElems];     // its table entries (rotated K only)
+  float scale;                                // the tensor's affine parameters
+  int32_t zero;
+};
+
+template <int IN>
+__device__ __forceinline__ void xf_lane_load_one(XfLanes &l, int k, const RowXf &x, bool rot,
+                                                 const char *row, const float *cr,
+                                                 const float *sr, uint32_t e) {
+  l.x[k] = xf_raw_t<IN>(row, e);
+  l.p[k] = 0;
+  l.c[k] = l.s[k] = 0.0f;
+  if (rot) {  // an unrotated element loads a pair it will not use
+    bool first;
+    uint32_t j, pe;
+    xf_pair(x, min(e, uint32_t(2 * x.half) - 1), first, j, pe);
+    l.p[k] = xf_raw_t<IN>(row, pe);
+    l.c[k] = cr[j];
+    l.s[k] = sr[j];
   }
-  if (x.out_bytes == 1) return xf_word_of<VEC, 1, false>(x, t, row, nullptr, nullptr, i);
-  if (x.out_bytes == 2) return xf_word_of<VEC, 2, false>(x, t, row, nullptr, nullptr, i);
-  return xf_word_of<VEC, 4, false>(x, t, row, nullptr, nullptr, i);
+}
+
+template <int IN>
+__device__ __forceinline__ void xf_lanes_load_t(XfLanes &l, const RowXf &x, bool rot,
+                                                const char *row, const float *cr,
+                                                const float *sr, uint32_t lane, uint32_t n,
+                                                uint32_t D, uint32_t m) {
+#pragma unroll
+  for (int k = 0; k < kXfLaneElems; ++k) l.x[k] = l.p[k] = 0, l.c[k] = l.s[k] = 0.0f;
+  if (m == 1) {  // the usual row: one element per lane, straight-line
+    xf_lane_load_one<IN>(l, 0, x, rot, row, cr, sr, min(lane, D - 1));
+    return;
+  }
+#pragma unroll
+  for (int k = 0; k < kXfLaneElems; ++k)
+    if (uint32_t(k) < m)  // uniform
+      xf_lane_load_one<IN>(l, k, x, rot, row, cr, sr, min(lane + k * n, D - 1));
+}
+
+__device__ __forceinline__ void xf_lanes_load(XfLanes &l, const RowXf &x, int t, const char *row,
+                                              int64_t pos, uint32_t lane, uint32_t n,
+                                              uint32_t D) {
+  const uint32_t m = (D + n - 1) / n;  // elements per lane (uniform)
+  const bool rot = t == 0 && x.cos;
+  const float *cr = rot ? x.cos + pos * x.half : nullptr;
+  const float *sr = rot ? x.sin + pos * x.half : nullptr;
+  // (t may differ between the waves of a workgroup; picking the parameter
+  // may then become a load, issued here with the others)
+  l.scale = t ? x.scale[1] : x.scale[0];
+  l.zero = t ? x.zero[1] : x.zero[0];
+  if (x.in_type == SWRT_XF_F32)
+    xf_lanes_load_t<SWRT_XF_F32>(l, x, rot, row, cr, sr, lane, n, D, m);
+  else if (x.in_type == SWRT_XF_BF16)
+    xf_lanes_load_t<SWRT_XF_BF16>(l, x, rot, row, cr, sr, lane, n, D, m);
+  else
+    xf_lanes_load_t<SWRT_XF_F16>(l, x, rot, row, cr, sr, lane, n, D, m);
+}
+
+// Make the loaded values live here: called after the shift's loads are
+// issued and before its barrier, it keeps the compiler from sinking the
+// loads past the barrier to their uses (which would wait for each of them in
+// turn); the wait it implies covers the older loads only.
+__device__ __forceinline__ void xf_lanes_hold(XfLanes &l) {
+#pragma unroll
+  for (int k = 0; k < kXfLaneElems; ++k)
+    asm volatile("" : "+v"(l.x[k]), "+v"(l.p[k]), "+v"(l.c[k]), "+v"(l.s[k]));
+  asm volatile("" : "+v"(l.scale), "+v"(l.zero));
+}
+
+template <int IN>
+__device__ __forceinline__ void xf_lane_store_one(const XfLanes &l, int k, const RowXf &x,
+                                                  bool rot, char *dst, uint32_t e) {
+  const float v = xf_rotate<IN>(x, rot, e, l.x[k], l.p[k], l.c[k], l.s[k]);
+  if (x.out_bytes == 4) {
+    __builtin_nontemporal_store(v != v ? 0x7FC00000u : __float_as_uint(v),
+                                reinterpret_cast<uint32_t *>(dst) + e);
+  } else if (x.out_bytes == 2) {
+    __builtin_nontemporal_store(x.out_type == SWRT_XF_BF16 ? xf_bf16(v) : xf_f16(v),
+                                reinterpret_cast<uint16_t *>(dst) + e);
+  } else {
+    __builtin_nontemporal_store(uint8_t(xf_code_of(x, l.scale, l.zero, v)),
+                                reinterpret_cast<uint8_t *>(dst) + e);
+  }
+}
+
+template <int IN>
+__device__ __forceinline__ void xf_lanes_store_t(const XfLanes &l, const RowXf &x, int t,
+                                                 char *dst, uint32_t lane, uint32_t n,
+                                                 uint32_t D) {
+  const uint32_t m = (D + n - 1) / n;
+  const bool rot = t == 0 && x.cos;
+  if (m == 1) {
+    if (lane < D) xf_lane_store_one<IN>(l, 0, x, rot, dst, lane);
+    return;
+  }
+#pragma unroll
+  for (int k = 0; k < kXfLaneElems; ++k) {
+    const uint32_t e = lane + k * n;
+    if (uint32_t(k) < m && e < D) xf_lane_store_one<IN>(l, k, x, rot, dst, e);
+  }
+}
+
+__device__ __forceinline__ void xf_lanes_store(const XfLanes &l, const RowXf &x, int t, char *dst,
+                                               uint32_t lane, uint32_t n, uint32_t D) {
+  if (x.in_type == SWRT_XF_F32)
+    xf_lanes_store_t<SWRT_XF_F32>(l, x, t, dst, lane, n, D);
+  else if (x.in_type == SWRT_XF_BF16)
+    xf_lanes_store_t<SWRT_XF_BF16>(l, x, t, dst, lane, n, D);
+  else
+    xf_lanes_store_t<SWRT_XF_F16>(l, x, t, dst, lane, n, D);
 }
 
 }  // namespace swrt
