@@ -51,15 +51,17 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD's published peak
 # (FETCH_SIZE, WRITE_SIZE), each scaled by what the counter reads for a 1 GiB
 # copy; valid only for the kernel source they were taken on (its hash).
 MEASURED_TRAFFIC = {
-    ("bf16", "decode_step_kernel", "897262af264568cb"): {"read": 196_783_552,
-                                                         "written": 196_835_808},
-    ("bf16", "window_in_place", "f2dfcf6af985c7eb"): {"read": 195_176_829, "written": 196_010_155},
+    ("bf16", "decode_step_kernel", "5a17d20369dcd20b"): {"read": 196_784_295,
+                                                         "written": 196_844_560},
+    ("bf16->int8", "decode_step_kernel", "5a17d20369dcd20b"): {"read": 101_380_857,
+                                                               "written": 98_911_877},
+    ("bf16", "window_in_place", "f3fee1005c69ec6b"): {"read": 195_175_201, "written": 196_001_407},
 }
 _CSRC = "sliding_window_ring_tensor_amd/csrc/"
 KERNEL_SOURCES = {
-    "window_in_place": ("kv_window.hip", "window_device.hpp", "swrt_device.hpp"),
+    "window_in_place": ("kv_window.hip", "window_device.hpp", "xf_device.hpp", "swrt_device.hpp"),
     "decode_step_kernel": ("decode_step.hip", "window_device.hpp", "scatter_device.hpp",
-                           "swrt_device.hpp"),
+                           "xf_device.hpp", "swrt_device.hpp"),
 }
 
 
