@@ -132,6 +132,9 @@ class Oracle:
         lib.orc_kv_window_append_xf.restype = ctypes.c_int
         lib.orc_tensor_scatter_xf.argtypes = [vp, vp, vp, vp, vp, i32, i64, i32, i32, xfp, u32p]
         lib.orc_tensor_scatter_xf.restype = ctypes.c_int
+        lib.orc_window_attention.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                                             ctypes.c_double, i32, u32p]
+        lib.orc_window_attention.restype = ctypes.c_int
         self.lib = lib
 
     # -- TensorScatter ----------------------------------------------------
@@ -289,6 +292,28 @@ class Oracle:
                                             MODE_CIRCULAR if mode == "circular" else MODE_LINEAR,
                                             t, ctypes.byref(x.c()), ctypes.byref(flags))
         return st, flags.value
+
+
+    # -- windowed decode attention -----------------------------------------
+    def window_attention(self, q, k_cache, v_cache, cache_total_lens, window: int,
+                         scale: float, elem_type: int, out: np.ndarray | None = None):
+        """float64 attention of q [B, Hq, D] over caches [B, Hkv, C, D] (any numpy
+        arrays holding elem_type elements; D follows from the row bytes).
+        Returns (out [B, Hq, D] float64, flags)."""
+        es = XF_BYTES[elem_type]
+        B, Hkv, C = k_cache.shape[:3]
+        D = k_cache.shape[3] * k_cache.itemsize // es
+        Hq = q.shape[1]
+        if out is None:
+            out = np.zeros((B, Hq, D), np.float64)
+        L = np.ascontiguousarray(cache_total_lens, dtype=np.int32)
+        qc, kc, vc = (np.ascontiguousarray(a) for a in (q, k_cache, v_cache))  # alive for the call
+        flags = ctypes.c_uint32(0)
+        st = self.lib.orc_window_attention(_ptr(qc), _ptr(kc), _ptr(vc), _ptr(out), _ptr(L), window,
+                                           B, Hq, Hkv, C, D, scale, elem_type, ctypes.byref(flags))
+        if st != OK:
+            raise OracleError(f"orc_window_attention status {st}")
+        return out, flags.value
 
 
 _default: Oracle | None = None

@@ -35,6 +35,12 @@
  *     length), row s of a TensorScatter at write_indices[b] + s before any
  *     wrap; an entry with a position outside the tables is flagged and
  *     skipped whole, K and V alike.
+ *   - [ATT] the local window: the query at absolute position T - 1 sees the
+ *     last W resident tokens, rows [max(0, L - W), L) (the drifting layout's
+ *     "rows older than the window are masked"; C >= W is the minimum
+ *     capacity). The ring-buffer cache is the case W = C with L = min(T, C).
+ *     Scores are scaled dot products (the caller's scale, usually
+ *     1/sqrt(head_dim)); an empty window gives zeros.
  *   - [PF] fixes rounding (ties to even) and saturation of affine codes but
  *     not NaN: NaN takes the zero point; float outputs (binary32 and the half
  *     types) store any NaN as the positive canonical quiet NaN, since the sign
@@ -733,4 +739,78 @@ int orc_tensor_scatter_xf(void *present, const void *past, const void *update,
     }
     free(tmp);
     return status;
+}
+
+/* ------------------------------------------------------------------------ */
+/* [ATT] windowed decode attention                                          */
+/* ------------------------------------------------------------------------ */
+
+static double att_load(int type, const char *base, int64_t i)
+{
+    return (double)xf_load(type, base, i); /* every f32/f16/bf16 value is exact in float64 */
+}
+
+int orc_window_attention(const void *q, const void *k_cache, const void *v_cache,
+                         double *out, const int32_t *cache_total_lens, int64_t window,
+                         int64_t batch, int64_t q_heads, int64_t kv_heads,
+                         int64_t capacity, int64_t head_dim, double scale, int elem_type,
+                         uint32_t *flags)
+{
+    const int64_t B = batch, Hq = q_heads, Hkv = kv_heads, C = capacity, D = head_dim;
+    int64_t es, group;
+    double *s, *acc;
+
+    if (B < 0 || Hq < 0 || Hkv < 1 || C < 1 || D < 0 || window < 1)
+        return ORC_E_INVALID_ARG;
+    if (!xf_float_type(elem_type) || Hq % Hkv != 0)
+        return ORC_E_INVALID_ARG;
+    if (B == 0 || Hq == 0 || D == 0)
+        return ORC_OK;
+    if (!q || !k_cache || !v_cache || !out || !cache_total_lens)
+        return ORC_E_INVALID_ARG;
+    es = xf_elem_bytes(elem_type);
+    group = Hq / Hkv;
+    s = (double *)malloc((size_t)C * sizeof(double));
+    acc = (double *)malloc((size_t)D * sizeof(double));
+    if (!s || !acc) {
+        free(s);
+        free(acc);
+        return ORC_E_INVALID_ARG;
+    }
+    for (int64_t b = 0; b < B; ++b) {
+        const int64_t L = cache_total_lens[b];
+        const int64_t r0 = L > window ? L - window : 0; /* the last W resident rows */
+        if (L < 0 || L > C) {
+            set_flag(flags, ORC_FLAG_BAD_LENGTHS);
+            continue;
+        }
+        for (int64_t h = 0; h < Hq; ++h) {
+            const int64_t g = h / group; /* the KV head this query head reads */
+            const char *qrow = (const char *)q + (b * Hq + h) * D * es;
+            const char *kbase = (const char *)k_cache + (b * Hkv + g) * C * D * es;
+            const char *vbase = (const char *)v_cache + (b * Hkv + g) * C * D * es;
+            double m = -INFINITY, denom = 0.0;
+            for (int64_t d = 0; d < D; ++d)
+                acc[d] = 0.0;
+            for (int64_t r = r0; r < L; ++r) { /* scores */
+                double dot = 0.0;
+                for (int64_t d = 0; d < D; ++d)
+                    dot += att_load(elem_type, qrow, d) * att_load(elem_type, kbase, r * D + d);
+                s[r] = scale * dot;
+                if (s[r] > m)
+                    m = s[r];
+            }
+            for (int64_t r = r0; r < L; ++r) { /* softmax weights and the weighted V */
+                const double p = exp(s[r] - m);
+                denom += p;
+                for (int64_t d = 0; d < D; ++d)
+                    acc[d] += p * att_load(elem_type, vbase, r * D + d);
+            }
+            for (int64_t d = 0; d < D; ++d)
+                out[(b * Hq + h) * D + d] = L > r0 ? acc[d] / denom : 0.0;
+        }
+    }
+    free(s);
+    free(acc);
+    return ORC_OK;
 }

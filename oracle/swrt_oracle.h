@@ -23,6 +23,11 @@
  *   [GQA-ROPE] the same pull request's "Summary of Changes": the KV append
  *         writes at the cache-relative offset while RoPE keeps the absolute
  *         position, bounded by its own maximum position, not by the capacity.
+ *   [ATT] onnx-light-cpu "Persistent KV Cache and Decode Performance
+ *         Roadmap", section "Phase 1: decode with contiguous KV cache"
+ *         (streaming decode attention, GQA head grouping), with [GQA] "Design"
+ *         (the invariant and the local window) and [RB] (attention over the
+ *         ring under a position mask; slot order does not change scores).
  *   [PF]  onnx-light how-to "Persistent input/output feedback", section
  *         "Optional heterogeneous paged KV" ("Selected-block quantization",
  *         "Serialized cache values"): affine INT8/UINT8 codes with FLOAT
@@ -185,6 +190,31 @@ int orc_tensor_scatter_xf(void *present, const void *past, const void *update,
                           const int64_t *write_indices, const int64_t *shape,
                           int rank, int64_t seq_len, int mode, int t,
                           const orc_row_xf *x, uint32_t *flags);
+
+/* ------------------------------------------------------------------------ */
+/* windowed decode attention                                                 */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * [ATT] one-token decode attention over each batch entry's visible window of
+ * a windowed cache, for every query head (the onnx-light-cpu roadmap, "Phase
+ * 1: decode with contiguous KV cache": q.K dot products, softmax, weighted
+ * V; GQA query heads share their KV head). In float64 from the decoded
+ * elements:
+ *   rows  r in [max(0, L_b - W), L_b)      (the last W resident tokens)
+ *   kv    g = h / (Hq / Hkv)
+ *   s_r   = scale * sum_d q[b,h,d] * k[b,g,r,d]
+ *   o     = sum_r exp(s_r - max s) v[b,g,r,:] / sum_r exp(s_r - max s)
+ * q [B, Hq, D], caches [B, Hkv, C, D] of elem_type (ORC_XF_F32 / F16 /
+ * BF16), out [B, Hq, D] float64. An empty window (L_b = 0) gives zeros; an
+ * entry with L_b < 0 or L_b > C is flagged BAD_LENGTHS and its outputs are
+ * left as they were. Hq must be a multiple of Hkv; W >= 1.
+ */
+int orc_window_attention(const void *q, const void *k_cache, const void *v_cache,
+                         double *out, const int32_t *cache_total_lens, int64_t window,
+                         int64_t batch, int64_t q_heads, int64_t kv_heads,
+                         int64_t capacity, int64_t head_dim, double scale, int elem_type,
+                         uint32_t *flags);
 
 #ifdef __cplusplus
 }

@@ -3,8 +3,8 @@
 Each mutant below is a copy of oracle/swrt_oracle.c with one planted mistake
 (an index off by one, a dropped term, a wrong sign, a transposed operand, a
 step done in the wrong order, a check weakened). The mutant is compiled with
-gcc and the whole pin suite (tests/test_oracle_pins.py and
-tests/test_oracle_xf_pins.py) runs against it in its
+gcc and the whole pin suite (tests/test_oracle_pins.py, test_oracle_xf_pins.py
+and test_oracle_att_pins.py) runs against it in its
 own process; the suite must fail for every mutant. A mutant that crashes its
 process counts as caught. Everything runs on the CPU.
 """
@@ -117,6 +117,18 @@ MUTANTS = {
     "f16_exponent_bias": ("return sign | (uint16_t)((ex + 15) << 10)",
                           "return sign | (uint16_t)((ex + 14) << 10)"),
     "f16_decode_subnormal": ("v = ldexp((double)m, -24);", "v = ldexp((double)m, -25);"),
+    # windowed decode attention
+    "att_gqa_modulo": ("const int64_t g = h / group; /* the KV head", "const int64_t g = h % Hkv; /* the KV head"),
+    "att_window_one_short": ("const int64_t r0 = L > window ? L - window : 0;",
+                             "const int64_t r0 = L > window ? L - window + 1 : 0;"),
+    "att_window_one_long": ("const int64_t r0 = L > window ? L - window : 0;",
+                            "const int64_t r0 = L > window ? L - window - 1 : 0;"),
+    "att_scale_dropped": ("s[r] = scale * dot;", "s[r] = dot;"),
+    "att_no_max_shift": ("const double p = exp(s[r] - m);", "const double p = exp(s[r]);"),
+    "att_last_row_dropped": ("for (int64_t r = r0; r < L; ++r) { /* softmax", "for (int64_t r = r0; r < L - 1; ++r) { /* softmax"),
+    "att_v_from_k": ("const char *vbase = (const char *)v_cache", "const char *vbase = (const char *)k_cache"),
+    "att_query_of_kv_head": ("(const char *)q + (b * Hq + h) * D * es", "(const char *)q + (b * Hq + g) * D * es"),
+    "att_not_normalised": ("L > r0 ? acc[d] / denom : 0.0", "L > r0 ? acc[d] : 0.0"),
     "bf16_decode_shift": ("uint32_t u = (uint32_t)h << 16;", "uint32_t u = (uint32_t)h << 15;"),
 }
 
@@ -149,7 +161,8 @@ def _run_pins(lib: str) -> subprocess.CompletedProcess:
     env = dict(os.environ, SWRT_ORACLE_LIB=lib, PYTHONDONTWRITEBYTECODE="1")
     return subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                            os.path.join(ROOT, "tests", "test_oracle_pins.py"),
-                           os.path.join(ROOT, "tests", "test_oracle_xf_pins.py")],
+                           os.path.join(ROOT, "tests", "test_oracle_xf_pins.py"),
+                           os.path.join(ROOT, "tests", "test_oracle_att_pins.py")],
                           cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
 
 
