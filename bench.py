@@ -62,6 +62,7 @@ KERNEL_SOURCES = {
     "window_in_place": ("kv_window.hip", "window_device.hpp", "xf_device.hpp", "swrt_device.hpp"),
     "decode_step_kernel": ("decode_step.hip", "window_device.hpp", "scatter_device.hpp",
                            "xf_device.hpp", "swrt_device.hpp"),
+    "window_attention_kernel": ("window_attention.hip", "xf_device.hpp", "swrt_device.hpp"),
 }
 
 
@@ -395,6 +396,86 @@ def drift_loop(args, dev):
     print(json.dumps(out))
 
 
+def attention_bench(args, dev):
+    """Workload 8: decode attention over the 12 windowed layers of the model
+    step (window_attention, one launch), after the step's append; K launches
+    round robin over the buffer sets."""
+    import oracle
+    import sliding_window_ring_tensor_amd as swrt  # noqa: F401
+    from sliding_window_ring_tensor_amd import workloads as wl
+    from sliding_window_ring_tensor_amd.decode_step import ModelDecodeStep
+
+    spec = wl.workload8()
+    K, W = args.steps, args.warmup
+    log(f"allocating {args.sets} buffer sets ...")
+    steps = [ModelDecodeStep(spec, dev, set_id=i) for i in range(args.sets)]
+    for st in steps:  # the step's append writes the windows and their lengths
+        st.run_fused()
+    torch.cuda.synchronize()
+    byts = steps[0].attention_bytes()
+    stream = torch.cuda.Stream()
+    eager, device, _ = _timers(stream, K, W)
+    with torch.cuda.stream(stream):
+        log(f"timing {K} attention launches ...")
+        att_s = eager(lambda i: steps[i].attention(), len(steps))
+        att_dev = device(lambda i: steps[i].attention(), len(steps), att_s)
+        log(f"timing {K} steps of append + attention ...")
+        both_s = eager(lambda i: (steps[i].run_fused(), steps[i].attention()), len(steps))
+    flags = [int(st.buffers.flags.item()) for st in steps]
+    if any(flags):
+        raise SystemExit(f"device flags raised during the benchmark: {flags}")
+    value = byts / att_s / 1e9
+    achieved = byts / att_dev / 1e9
+    meas = MEASURED_TRAFFIC.get(("bf16", "window_attention_kernel",
+                                 kernel_source_hash("window_attention_kernel")))
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"timing the CPU oracle for about {args.cpu_seconds:.0f} s ...")
+        orc = oracle.get()
+        b = steps[0].buffers
+
+        def host(t):
+            return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+        qs, ks, vs = ([host(t) for t in ts] for ts in (b.win_q, b.win_k, b.win_v))
+        L = b.lengths.cache_total.cpu().numpy()
+
+        def one_step():
+            for q, k, v in zip(qs, ks, vs):
+                orc.window_attention(q, k, v, L, spec.window, spec.head_dim ** -0.5,
+                                     oracle.XF_BF16)
+
+        n, el = _time_steps(one_step, args.cpu_seconds)
+        cpu = {"value": round(byts * n / el / 1e9, 4), "unit": "GB/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"{n} attention steps (12 layers) on host copies of buffer set 0, "
+                         f"one thread, float64, {el:.1f} s",
+               "us_per_step": round(el / n * 1e6, 1)}
+    out = {
+        "metric": "KV-cache update effective HBM GB/s (% of peak) and us per decode step",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(att_s * 1e3, 5), "us_per_step": round(att_s * 1e6, 2),
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"workload 8: decode attention over the {len(spec.windowed_layers)} "
+                               f"windowed layers of the model step, B={spec.batch}, "
+                               f"Hq={spec.q_heads}, Hkv={spec.kv_heads}, D={spec.head_dim}, "
+                               f"C=W={spec.window}, lengths min(T, C) of T~U[1,8192] seed 8, "
+                               f"bf16 in and out, fp32 softmax",
+                   "bytes_per_step": byts,
+                   "form": "one launch per step (window_attention, all windowed layers)",
+                   "cache_defeat": f"{args.sets} independent buffer sets round robin"},
+        "roofline": {"bound": "hbm", "kernel": "window_attention_kernel: 12 layers, one launch",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None if meas is None else meas["read"] + meas["written"],
+                     "bytes_per_launch": byts, "mean_launch_us": round(att_dev * 1e6, 3)},
+        "cpu_baseline": cpu,
+        "append_plus_attention_us_per_step": round(both_s * 1e6, 2),
+    }
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -408,11 +489,12 @@ def main():
                     help="one launch per step (default) or the three-call composition")
     ap.add_argument("--timing", default="eager", choices=["eager", "graph"],
                     help="the timed loop `value` reports (both are measured)")
-    ap.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5, 6, 7],
+    ap.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5, 6, 7, 8],
                     help="5: the whole-model decode step (default); 1-4: the other workloads; "
                          "6: workload 5's decode loop with drifting windowed caches "
                          "(capacity W + --slack); 7: workload 5 with the fused append (bf16 "
-                         "rows, RoPE on K, int8 caches); one line each, for the design notes")
+                         "rows, RoPE on K, int8 caches); 8: decode attention over workload 5's "
+                         "windowed layers; one line each, for the design notes")
     ap.add_argument("--slack", type=int, default=16, help="workload 6: capacity - window")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -432,6 +514,8 @@ def main():
     torch.cuda.set_device(dev)
     if args.workload == 6:
         return drift_loop(args, dev)
+    if args.workload == 8:
+        return attention_bench(args, dev)
     if args.workload not in (5, 7):
         return other_workload(args, dev)
     xf = args.workload == 7

@@ -25,7 +25,8 @@
  * caches per launch) and swrt_kv_decode_step (all of a decode step at once),
  * and *_xf forms that fuse the row transform of the append into the write:
  * RoPE on K at the absolute position and conversion or affine quantization
- * into the cache's element type (swrt_row_transform below).
+ * into the cache's element type (swrt_row_transform below), and
+ * swrt_window_attention, the decode attention that reads the windowed caches.
  *
  * Conventions shared by every entry point
  *   - Ownership: the caller owns every buffer. The library allocates nothing,
@@ -59,7 +60,7 @@
 extern "C" {
 #endif
 
-#define SWRT_ABI_VERSION 3
+#define SWRT_ABI_VERSION 4
 
 /* synchronous status codes */
 #define SWRT_OK 0
@@ -455,6 +456,45 @@ int swrt_kv_decode_step_xf(int n_window_layers, void *const *win_k_caches,
                            int batch, int kv_heads, int head_dim,
                            const swrt_row_transform *xf, uint32_t *d_flags,
                            void *stream);
+
+/*
+ * swrt_window_attention -- one-token decode attention over windowed caches
+ * (onnx-light-cpu "Persistent KV Cache and Decode Performance Roadmap",
+ * section "Phase 1: decode with contiguous KV cache": per KV block the
+ * query/K dot products, the online-softmax update and the V accumulation,
+ * without storing the score vector; query heads sharing a KV head read it
+ * once; fp32 scores, softmax and accumulation. The window is that of the pull
+ * request "GQA support sliding_window_cache": the query at absolute position
+ * T - 1 sees the last W resident rows.) For every layer, batch entry b and
+ * query head h, with L = cache_total_lens[b] and g = h / (q_heads / kv_heads):
+ *   rows  r in [max(0, L - W), L)
+ *   out[b, h, :] = sum_r softmax_r(scale * q[b, h, :] . k[b, g, r, :]) v[b, g, r, :]
+ * An empty window (L = 0) writes zeros.
+ *
+ * n_layers          1 .. SWRT_MAX_LAYERS; q, k_caches, v_caches, out are host
+ *                   arrays of n_layers device pointers (one launch for all).
+ * q                 [batch, q_heads, head_dim] elem_type, 8-byte aligned.
+ * k_caches, v_caches [batch, kv_heads, capacity, head_dim] elem_type, 8-byte
+ *                   aligned (the windowed caches of swrt_kv_window_append).
+ * out               [batch, q_heads, head_dim] out_type; must not overlap any
+ *                   other buffer.
+ * cache_total_lens  device int32[batch]: L of swrt_kv_seq_lengths (or _drift).
+ * window            W >= 1 (W = capacity: every resident row; the ring-buffer
+ *                   cache is this case).
+ * scale             finite (usually 1 / sqrt(head_dim)).
+ * elem_type         SWRT_XF_F32, _F16 or _BF16; out_type the same set.
+ * d_flags           SWRT_FLAG_BAD_LENGTHS when L < 0 or L > capacity: that
+ *                   entry's outputs are left as they were.
+ * Supported shapes (else SWRT_E_UNSUPPORTED): q_heads / kv_heads in
+ * {1, 2, 4, 8, 16}; head_dim * element size in {64, 128, 256, 512} bytes;
+ * (q_heads / kv_heads) * head_dim * element size <= 2048 bytes.
+ */
+int swrt_window_attention(int n_layers, const void *const *q,
+                          const void *const *k_caches, const void *const *v_caches,
+                          void *const *out, const int32_t *cache_total_lens,
+                          int window, int batch, int q_heads, int kv_heads,
+                          int capacity, int head_dim, float scale, int elem_type,
+                          int out_type, uint32_t *d_flags, void *stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *swrt_status_string(int status);

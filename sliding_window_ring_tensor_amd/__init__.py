@@ -23,6 +23,11 @@ conversion or affine INT8 / UINT8 quantization into the cache's dtype):
 
     kv_window_append_xf(...), tensor_scatter_xf(...), kv_decode_step_xf(...)
 
+Decode attention over the windowed caches (every query head over the last W
+resident rows of its KV head):
+
+    window_attention(qs, k_caches, v_caches, cache_total_lens, window, ...)
+
 Every function has a ``prepare_*`` twin returning a ``PreparedCall``: the
 arguments are checked and marshalled once, and each call of the object only
 adds the current stream. Decode loops use it to keep host cost per step small.
@@ -44,6 +49,7 @@ __all__ = [
     "prepare_kv_window_append_layers", "prepare_kv_decode_step",
     "Transform", "kv_window_append_xf", "tensor_scatter_xf", "kv_decode_step_xf",
     "prepare_kv_window_append_xf", "prepare_tensor_scatter_xf", "prepare_kv_decode_step_xf",
+    "window_attention", "prepare_window_attention",
     "OK", "E_INVALID_ARG", "E_UNSUPPORTED", "E_LAUNCH",
     "FLAG_LINEAR_OOB", "FLAG_BAD_SEQLEN", "FLAG_BAD_LENGTHS", "FLAG_ROPE_RANGE",
     "PHASE_STAGE", "PHASE_COMMIT", "PHASE_ALL",
@@ -59,7 +65,7 @@ MODE_LINEAR, MODE_CIRCULAR = 0, 1
 PHASE_STAGE, PHASE_COMMIT, PHASE_ALL = 1, 2, 3
 MAX_LAYERS = 32
 MAX_BATCHED = 64
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 _PHASES = {"stage": PHASE_STAGE, "commit": PHASE_COMMIT, "all": PHASE_ALL}
 _MODES = {"linear": MODE_LINEAR, "circular": MODE_CIRCULAR}
@@ -166,11 +172,13 @@ def lib() -> ctypes.CDLL:
     L.swrt_kv_decode_step_xf.argtypes = [i32, vpp, vpp, vpp, vpp, vp, vp, i32, i32, vp, vp, vp,
                                          vp, vp, i32, vpp, vpp, vpp, vpp, vp, i32, i32, i32, i32,
                                          xfp, vp, vp]
+    L.swrt_window_attention.argtypes = [i32, vpp, vpp, vpp, vpp, vp, i32, i32, i32, i32, i32,
+                                        i32, ctypes.c_float, i32, i32, vp, vp]
     for name in ("swrt_tensor_scatter", "swrt_tensor_scatter_batched", "swrt_kv_seq_lengths",
                  "swrt_kv_seq_lengths_drift",
                  "swrt_kv_window_append", "swrt_kv_window_append_layers", "swrt_kv_decode_step",
                  "swrt_kv_window_append_xf", "swrt_tensor_scatter_xf", "swrt_kv_decode_step_xf",
-                 "swrt_abi_version"):
+                 "swrt_window_attention", "swrt_abi_version"):
         getattr(L, name).restype = ctypes.c_int
     L.swrt_status_string.argtypes = [ctypes.c_int]
     L.swrt_status_string.restype = ctypes.c_char_p
@@ -686,3 +694,64 @@ def kv_decode_step_xf(win_k, win_v, win_k_new, win_v_new, seqlens_k, full_k, ful
     return prepare_kv_decode_step_xf(win_k, win_v, win_k_new, win_v_new, seqlens_k, full_k,
                                      full_v, full_k_new, full_v_new, write_indices, xf,
                                      window=window, out=out, flags=flags)()
+
+
+# ---------------------------------------------------------------------------
+# decode attention over the windowed caches
+# ---------------------------------------------------------------------------
+
+def prepare_window_attention(qs: Sequence[torch.Tensor], k_caches: Sequence[torch.Tensor],
+                             v_caches: Sequence[torch.Tensor], cache_total_lens: torch.Tensor,
+                             window: int, *, scale: float | None = None,
+                             out_dtype: torch.dtype | None = None,
+                             outs: Sequence[torch.Tensor] | None = None,
+                             flags: torch.Tensor | None = None) -> PreparedCall:
+    """See ``window_attention``."""
+    n = len(qs)
+    if not (len(k_caches) == len(v_caches) == n) or not 1 <= n <= MAX_LAYERS:
+        raise SwrtError(f"need 1..{MAX_LAYERS} layers with q, K and V each")
+    kc = k_caches[0]
+    if kc.dim() != 4 or qs[0].dim() != 3:
+        raise SwrtError("caches must be [B, Hkv, C, D] and queries [B, Hq, D]")
+    B, Hkv, C, D = kc.shape
+    Hq = qs[0].shape[1]
+    dt = kc.dtype
+    if dt not in (torch.float32, torch.float16, torch.bfloat16):
+        raise SwrtError("attention takes float32, float16 or bfloat16 caches")
+    odt = out_dtype if out_dtype is not None else (outs[0].dtype if outs else dt)
+    outs = [torch.empty((B, Hq, D), dtype=odt, device=kc.device) for _ in range(n)] \
+        if outs is None else list(outs)
+    for t in (*k_caches, *v_caches):
+        _contig("cache", t)
+        if t.shape != kc.shape or t.dtype != dt:
+            raise SwrtError("all caches must share shape and dtype")
+    for t in qs:
+        _contig("q", t)
+        if t.shape != (B, Hq, D) or t.dtype != dt:
+            raise SwrtError("queries must be [B, Hq, D] in the caches' dtype")
+    for t in outs:
+        _contig("out", t)
+        if t.shape != (B, Hq, D) or t.dtype != odt or odt not in XF_TYPES or \
+                odt in (torch.int8, torch.uint8):
+            raise SwrtError("outputs must be [B, Hq, D] float32, float16 or bfloat16")
+    _contig("cache_total_lens", cache_total_lens)
+    if cache_total_lens.dtype != torch.int32 or cache_total_lens.shape != (B,):
+        raise SwrtError("cache_total_lens must be int32 [B]")
+    dev = _device_of(*qs, *k_caches, *v_caches, *outs, cache_total_lens, flags)
+    sc = D ** -0.5 if scale is None else float(scale)
+    args = (n, _ptrs(qs), _ptrs(k_caches), _ptrs(v_caches), _ptrs(outs), _ptr(cache_total_lens),
+            window, B, Hq, Hkv, C, D, sc, XF_TYPES[dt], XF_TYPES[odt], _ptr(flags))
+    keep = (*qs, *k_caches, *v_caches, *outs, cache_total_lens, flags)
+    return PreparedCall(lib().swrt_window_attention, args, dev, "window_attention", keep, outs)
+
+
+def window_attention(qs, k_caches, v_caches, cache_total_lens, window: int, *,
+                     scale: float | None = None, out_dtype: torch.dtype | None = None,
+                     outs=None, flags=None) -> list:
+    """One-token decode attention of every layer's queries [B, Hq, D] over
+    its windowed caches [B, Hkv, C, D]: each query head h attends the last
+    ``window`` resident rows [max(0, L - W), L) of KV head h // (Hq // Hkv),
+    L = ``cache_total_lens`` (the lengths' ``cache_total``). fp32 softmax and
+    accumulation; ``scale`` defaults to 1 / sqrt(D). Returns the outputs."""
+    return prepare_window_attention(qs, k_caches, v_caches, cache_total_lens, window,
+                                    scale=scale, out_dtype=out_dtype, outs=outs, flags=flags)()

@@ -1,0 +1,392 @@
+// window_attention.hip -- one-token decode attention over windowed caches on
+// gfx950 (onnx-light-cpu "Persistent KV Cache and Decode Performance
+// Roadmap", section "Phase 1: decode with contiguous KV cache": a streaming
+// kernel that, per KV block, takes the query/K dot products, updates the
+// online-softmax state and accumulates V without storing the score vector;
+// query heads that share a KV head read each KV block once; scores, softmax
+// and accumulation in fp32. The window is that of the pull request "GQA
+// support sliding_window_cache": the query at position T - 1 sees the last W
+// resident rows, [max(0, L - W), L).)
+//
+// One workgroup (4 waves) per (layer, b, kv head). Its G = Hq / Hkv query
+// heads are held by every lane; a K or V row is split over LPR lanes of 8
+// bytes each, so one wave covers 64 / LPR consecutive rows per step and the
+// four waves interleave their steps (each load instruction of a wave reads
+// 512 contiguous bytes). Each lane keeps an online-softmax state (m, l, o)
+// per head for the rows it has seen; states merge exactly across the rows of
+// a wave (lane shuffles) and across waves (LDS). Scores use exp2 with log2(e)
+// folded into the scale.
+#include "swrt_host.hpp"
+
+namespace swrt {
+namespace {
+
+constexpr int kAttBlock = 256;  // 4 waves
+constexpr int kAttWaves = kAttBlock / 64;
+// steps (of 64 / LPR rows) a wave loads at once, a block of the stream;
+// fewer for large groups, whose per-head state fills the registers
+constexpr int att_steps(int G) { return G <= 4 ? 8 : G == 8 ? 4 : 2; }
+// per-wave states published through LDS: G * LPR lanes' worth at most 256
+constexpr bool att_supported(int LPR, int G) { return G * LPR <= 256; }
+
+struct AttArgs {
+  const char *q[kMaxLayers];
+  const char *k[kMaxLayers];
+  const char *v[kMaxLayers];
+  char *out[kMaxLayers];
+  const int32_t *L;
+  uint32_t *flags;
+  float scale_log2;  // scale * log2(e)
+  int32_t W, B, Hq, Hkv, C, D, out_type;
+};
+
+template <int ELEM>
+__device__ __forceinline__ float att_decode(uint32_t r) {
+  if constexpr (ELEM == SWRT_XF_F32)
+    return __uint_as_float(r);
+  else if constexpr (ELEM == SWRT_XF_BF16)
+    return __uint_as_float(r << 16);
+  else
+    return float(__builtin_bit_cast(_Float16, uint16_t(r)));
+}
+
+// the EPL elements of an 8-byte chunk
+template <int ELEM, int EPL>
+__device__ __forceinline__ void att_unpack(u32x2 w, float (&x)[EPL]) {
+  if constexpr (ELEM == SWRT_XF_F32) {
+    x[0] = __uint_as_float(w.x);
+    x[1] = __uint_as_float(w.y);
+  } else {
+    x[0] = att_decode<ELEM>(w.x & 0xFFFFu);
+    x[1] = att_decode<ELEM>(w.x >> 16);
+    x[2] = att_decode<ELEM>(w.y & 0xFFFFu);
+    x[3] = att_decode<ELEM>(w.y >> 16);
+  }
+}
+
+// sums over aligned groups of N lanes (N a power of two, 1 .. 64) of K values
+// at once, level by level, so the lane exchanges of different values
+// interleave; every lane of a group gets the group's sums
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float x) {
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF,
+                                                        false));
+}
+
+template <int N, int K>
+__device__ __forceinline__ void group_sums(float (&x)[K]) {
+#pragma unroll
+  for (int k = 0; k < K; ++k)
+    if constexpr (N >= 2) x[k] = dpp_add<0xB1>(x[k]);  // lanes i ^ 1
+#pragma unroll
+  for (int k = 0; k < K; ++k)
+    if constexpr (N >= 4) x[k] = dpp_add<0x4E>(x[k]);  // lanes i ^ 2
+#pragma unroll
+  for (int k = 0; k < K; ++k)
+    if constexpr (N >= 8) x[k] = dpp_add<0x141>(x[k]);  // the other quad of the half row
+#pragma unroll
+  for (int k = 0; k < K; ++k)
+    if constexpr (N >= 16) x[k] = dpp_add<0x140>(x[k]);  // the other half of the row
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    if constexpr (N >= 32) x[k] += __shfl_xor(x[k], 16);
+    if constexpr (N >= 64) x[k] += __shfl_xor(x[k], 32);
+  }
+}
+
+// A block of S scores (masked rows: -inf) joins a head's online-softmax
+// state: the new maximum, the factor f that rescales the old state and the
+// weights p of the rows. Each score is rounded once and compared with
+// itself: a fused multiply-add of dot * scale - max would leave that
+// rounding as a residual and give the row at the maximum a weight other
+// than 1. Selects, not branches, handle a state that has seen nothing.
+template <int S>
+__device__ __forceinline__ void att_block(const float (&dot)[S], const bool (&ok)[S],
+                                          float scale_log2, float &m, float &f, float (&p)[S]) {
+#pragma clang fp contract(off)
+  float sc[S];
+  float mn = m;
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    sc[s] = ok[s] ? dot[s] * scale_log2 : -INFINITY;
+    mn = fmaxf(mn, sc[s]);
+  }
+  const bool none = mn == -INFINITY;  // nothing seen yet
+  f = none ? 1.0f : __builtin_amdgcn_exp2f(m - mn);
+#pragma unroll
+  for (int s = 0; s < S; ++s) p[s] = none ? 0.0f : __builtin_amdgcn_exp2f(sc[s] - mn);
+  m = mn;
+}
+
+// merge online-softmax state b into a (same rows never counted twice)
+template <int EPL>
+__device__ __forceinline__ void att_merge(float &m, float &l, float (&o)[EPL], float mb, float lb,
+                                          const float (&ob)[EPL]) {
+  const float mn = fmaxf(m, mb);
+  if (mn == -INFINITY) return;  // both empty
+  const float fa = __builtin_amdgcn_exp2f(m - mn), fb = __builtin_amdgcn_exp2f(mb - mn);
+  l = l * fa + lb * fb;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) o[e] = o[e] * fa + ob[e] * fb;
+  m = mn;
+}
+
+template <int ELEM, int LPR, int G>
+__global__ __launch_bounds__(kAttBlock) void window_attention_kernel(AttArgs a) {
+  constexpr int EPL = ELEM == SWRT_XF_F32 ? 2 : 4;  // elements per 8-byte chunk
+  constexpr int RW = 64 / LPR;                      // rows per wave step
+  constexpr int kAttStep = att_steps(G);
+  const uint32_t bid = blockIdx.x;
+  const uint32_t g = bid % uint32_t(a.Hkv), b = (bid / uint32_t(a.Hkv)) % uint32_t(a.B);
+  const uint32_t layer = bid / uint32_t(a.Hkv * a.B);
+  const int64_t L = a.L[b];
+  if (L < 0 || L > a.C) {  // no partial output for this entry
+    if (a.flags && g == 0 && layer == 0 && threadIdx.x == 0) atomicOr(a.flags, SWRT_FLAG_BAD_LENGTHS);
+    return;
+  }
+  const int64_t r0 = L > a.W ? L - a.W : 0;
+  const uint32_t lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  const uint32_t c = lane % LPR, rr = lane / LPR;  // chunk of the row, row of the step
+  const uint32_t es = ELEM == SWRT_XF_F32 ? 4 : 2;
+  const uint64_t row_bytes = uint64_t(a.D) * es;
+  const uint64_t kv_off = (uint64_t(b) * a.Hkv + g) * uint64_t(a.C) * row_bytes;
+  const char *kb = a.k[layer] + kv_off + c * 8;
+  const char *vb = a.v[layer] + kv_off + c * 8;
+
+  // this lane's chunk of every query head of the group
+  float q[G][EPL];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    const u32x2 w = *reinterpret_cast<const u32x2 *>(
+        a.q[layer] + ((uint64_t(b) * a.Hq + g * G + j) * row_bytes) + c * 8);
+    att_unpack<ELEM, EPL>(w, q[j]);
+  }
+
+  float m[G], l[G], o[G][EPL];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    m[j] = -INFINITY;
+    l[j] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[j][e] = 0.0f;
+  }
+
+  // rows of this wave: r0 + (s * waves + wave) * RW + rr, s = 0, 1, ...
+  const int64_t stride = int64_t(kAttWaves) * RW;
+  for (int64_t base = r0 + int64_t(wave) * RW; base < L; base += kAttStep * stride) {
+    // every load of the block first (steps past the window, uniform in the
+    // wave, load nothing), then the rows one step at a time
+    u32x2 kw[kAttStep], vw[kAttStep];
+#pragma unroll
+    for (int s = 0; s < kAttStep; ++s) {
+      if (base + s * stride < L) {
+        const int64_t r = base + s * stride + rr;
+        const int64_t rc = r < L ? r : L - 1;  // lanes past the window repeat a valid row
+        kw[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(kb + rc * row_bytes));
+        vw[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(vb + rc * row_bytes));
+      } else {  // zeros: a masked row's weight 0 times its V must stay 0
+        kw[s] = u32x2{0u, 0u};
+        vw[s] = u32x2{0u, 0u};
+      }
+    }
+    // scores of the block: per step, every head's partial dot, then their
+    // lane sums together (rows past the window compute on a repeated row
+    // and are masked)
+    bool ok[kAttStep];
+    float dots[G][kAttStep];
+#pragma unroll
+    for (int s = 0; s < kAttStep; ++s) {
+      ok[s] = base + s * stride + rr < L;
+      float kx[EPL];
+      att_unpack<ELEM, EPL>(kw[s], kx);
+      float d[G];
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        d[j] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) d[j] += q[j][e] * kx[e];
+      }
+      group_sums<LPR, G>(d);
+#pragma unroll
+      for (int j = 0; j < G; ++j) dots[j][s] = d[j];
+    }
+    // one rescale per head, then the block's weighted rows
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      float f, p[kAttStep];
+      att_block<kAttStep>(dots[j], ok, a.scale_log2, m[j], f, p);
+      l[j] *= f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[j][e] *= f;
+#pragma unroll
+      for (int s = 0; s < kAttStep; ++s) {
+        float vx[EPL];
+        att_unpack<ELEM, EPL>(vw[s], vx);
+        l[j] += p[s];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[j][e] += p[s] * vx[e];
+      }
+    }
+  }
+
+  // merge the RW row groups of the wave (lanes c, c + LPR, c + 2 LPR, ...)
+#pragma unroll
+  for (int off = LPR; off < 64; off *= 2) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      float ob[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) ob[e] = __shfl_xor(o[j][e], off);
+      att_merge<EPL>(m[j], l[j], o[j], __shfl_xor(m[j], off), __shfl_xor(l[j], off), ob);
+    }
+  }
+  // then the waves, through LDS: lanes rr == 0 of each wave publish
+  __shared__ float st[kAttWaves][G][LPR][EPL + 2];
+  if (rr == 0) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      st[wave][j][c][0] = m[j];
+      st[wave][j][c][1] = l[j];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) st[wave][j][c][2 + e] = o[j][e];
+    }
+  }
+  __syncthreads();
+  if (wave != 0 || rr != 0) return;
+#pragma unroll
+  for (int w = 1; w < kAttWaves; ++w) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      float ob[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) ob[e] = st[w][j][c][2 + e];
+      att_merge<EPL>(m[j], l[j], o[j], st[w][j][c][0], st[w][j][c][1], ob);
+    }
+  }
+  // normalise and write head g * G + j's chunk c
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    const float inv = l[j] > 0.0f ? 1.0f / l[j] : 0.0f;  // an empty window gives zeros
+    char *dst = a.out[layer] + (uint64_t(b) * a.Hq + g * G + j) * uint64_t(a.D) *
+                                   (a.out_type == SWRT_XF_F32 ? 4 : 2);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const float y = o[j][e] * inv;
+      const uint32_t idx = c * EPL + e;
+      if (a.out_type == SWRT_XF_F32)
+        reinterpret_cast<float *>(dst)[idx] = y;
+      else if (a.out_type == SWRT_XF_BF16)
+        reinterpret_cast<uint16_t *>(dst)[idx] = xf_bf16(y);
+      else
+        reinterpret_cast<uint16_t *>(dst)[idx] = xf_f16(y);
+    }
+  }
+}
+
+template <int ELEM, int LPR, int G>
+int launch_one(const AttArgs &a, uint32_t grid, hipStream_t s) {
+  if constexpr (att_supported(LPR, G)) {
+    hipLaunchKernelGGL((window_attention_kernel<ELEM, LPR, G>), dim3(grid), dim3(kAttBlock), 0, s,
+                       a);
+    return launch_status();
+  } else {
+    return SWRT_E_UNSUPPORTED;  // refused on the host before this point
+  }
+}
+
+template <int ELEM, int LPR>
+int launch_g(const AttArgs &a, int G, uint32_t grid, hipStream_t s) {
+  switch (G) {
+    case 1: return launch_one<ELEM, LPR, 1>(a, grid, s);
+    case 2: return launch_one<ELEM, LPR, 2>(a, grid, s);
+    case 4: return launch_one<ELEM, LPR, 4>(a, grid, s);
+    case 8: return launch_one<ELEM, LPR, 8>(a, grid, s);
+    default: return launch_one<ELEM, LPR, 16>(a, grid, s);
+  }
+}
+
+template <int ELEM>
+int launch_lpr(const AttArgs &a, int lpr, int G, uint32_t grid, hipStream_t s) {
+  switch (lpr) {
+    case 8: return launch_g<ELEM, 8>(a, G, grid, s);
+    case 16: return launch_g<ELEM, 16>(a, G, grid, s);
+    case 32: return launch_g<ELEM, 32>(a, G, grid, s);
+    default: return launch_g<ELEM, 64>(a, G, grid, s);
+  }
+}
+
+}  // namespace
+}  // namespace swrt
+
+using namespace swrt;
+
+extern "C" int swrt_window_attention(int n_layers, const void *const *q,
+                                     const void *const *k_caches, const void *const *v_caches,
+                                     void *const *out, const int32_t *cache_total_lens,
+                                     int window, int batch, int q_heads, int kv_heads,
+                                     int capacity, int head_dim, float scale, int elem_type,
+                                     int out_type, uint32_t *d_flags, void *stream) {
+  if (n_layers < 0 || n_layers > kMaxLayers || batch < 0 || q_heads < 0 || kv_heads < 1 ||
+      capacity < 1 || head_dim < 0 || window < 1)
+    return SWRT_E_INVALID_ARG;
+  if (elem_type != SWRT_XF_F32 && elem_type != SWRT_XF_F16 && elem_type != SWRT_XF_BF16)
+    return SWRT_E_INVALID_ARG;
+  if (out_type != SWRT_XF_F32 && out_type != SWRT_XF_F16 && out_type != SWRT_XF_BF16)
+    return SWRT_E_INVALID_ARG;
+  if (q_heads % kv_heads) return SWRT_E_INVALID_ARG;
+  if (!(scale == scale) || scale > 3.4028235e38f || scale < -3.4028235e38f) return SWRT_E_INVALID_ARG;
+  if (n_layers == 0 || batch == 0 || q_heads == 0 || head_dim == 0) return SWRT_OK;
+  const int G = q_heads / kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return SWRT_E_UNSUPPORTED;
+  const int64_t es = elem_type == SWRT_XF_F32 ? 4 : 2, oes = out_type == SWRT_XF_F32 ? 4 : 2;
+  const int64_t row = int64_t(head_dim) * es;
+  const int64_t lpr = row / 8;
+  if (row % 8 || (lpr != 8 && lpr != 16 && lpr != 32 && lpr != 64)) return SWRT_E_UNSUPPORTED;
+  if (G * lpr > 256) return SWRT_E_UNSUPPORTED;  // see att_supported
+  if (!q || !k_caches || !v_caches || !out || !cache_total_lens) return SWRT_E_INVALID_ARG;
+  int64_t cache_bytes, q_bytes, o_bytes;
+  if (!mul_ok(int64_t(batch) * kv_heads * capacity, row, &cache_bytes) ||
+      !mul_ok(int64_t(batch) * q_heads, row, &q_bytes) ||
+      !mul_ok(int64_t(batch) * q_heads * head_dim, oes, &o_bytes))
+    return SWRT_E_UNSUPPORTED;
+  if (uint64_t(n_layers) * batch * kv_heads >= (uint64_t(1) << 31)) return SWRT_E_UNSUPPORTED;
+  Range ranges[4 * kMaxLayers + 2];
+  int nr = 0;
+  AttArgs a;
+  for (int l = 0; l < n_layers; ++l) {
+    if (!q[l] || !k_caches[l] || !v_caches[l] || !out[l]) return SWRT_E_INVALID_ARG;
+    if (addr_of(q[l]) % 8 || addr_of(k_caches[l]) % 8 || addr_of(v_caches[l]) % 8 ||
+        addr_of(out[l]) % uint64_t(oes))
+      return SWRT_E_INVALID_ARG;
+    ranges[nr++] = range(q[l], uint64_t(q_bytes), false);
+    ranges[nr++] = range(k_caches[l], uint64_t(cache_bytes), false);
+    ranges[nr++] = range(v_caches[l], uint64_t(cache_bytes), false);
+    ranges[nr++] = range(out[l], uint64_t(o_bytes), true);
+    a.q[l] = static_cast<const char *>(q[l]);
+    a.k[l] = static_cast<const char *>(k_caches[l]);
+    a.v[l] = static_cast<const char *>(v_caches[l]);
+    a.out[l] = static_cast<char *>(out[l]);
+  }
+  if (addr_of(cache_total_lens) % 4 || addr_of(d_flags) % 4) return SWRT_E_INVALID_ARG;
+  ranges[nr++] = range(cache_total_lens, uint64_t(batch) * 4, false);
+  ranges[nr++] = range(d_flags, 4, true);
+  if (written_overlap(ranges, nr)) return SWRT_E_INVALID_ARG;
+  a.L = cache_total_lens;
+  a.flags = d_flags;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.W = window;
+  a.B = batch;
+  a.Hq = q_heads;
+  a.Hkv = kv_heads;
+  a.C = capacity;
+  a.D = head_dim;
+  a.out_type = out_type;
+  static_assert(sizeof(AttArgs) <= 4096, "kernel arguments exceed 4 KiB");
+  const uint32_t grid = uint32_t(n_layers) * uint32_t(batch) * uint32_t(kv_heads);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (elem_type) {
+    case SWRT_XF_F32: return launch_lpr<SWRT_XF_F32>(a, int(lpr), G, grid, s);
+    case SWRT_XF_F16: return launch_lpr<SWRT_XF_F16>(a, int(lpr), G, grid, s);
+    default: return launch_lpr<SWRT_XF_BF16>(a, int(lpr), G, grid, s);
+  }
+}

@@ -47,6 +47,8 @@ class StepBuffers:
     lengths: swrt.WindowLengths  # outputs of kv_seq_lengths
     flags: torch.Tensor          # int32 [1]
     xf: swrt.Transform | None = None  # fused append
+    win_q: list | None = None         # decode attention: queries [B, Hq, D] per windowed layer
+    win_out: list | None = None       # and its outputs
 
 
 class ModelDecodeStep:
@@ -83,6 +85,11 @@ class ModelDecodeStep:
                 torch.int64, torch.int64, torch.int32, torch.int32, torch.int32))),
             flags=torch.zeros(1, dtype=torch.int32, device=self.device),
         )
+        if spec.q_heads:
+            self.buffers.win_q = [buf((B, spec.q_heads, 1, D), 500 + i).view(B, spec.q_heads, D)
+                                  for i in range(nw)]
+            self.buffers.win_out = [torch.empty((B, spec.q_heads, D), dtype=dt, device=self.device)
+                                    for _ in range(nw)]
         if spec.new_dtype is not None:
             cos = sin = None
             if spec.rotary_dim:
@@ -125,6 +132,26 @@ class ModelDecodeStep:
                     b.full_kn + b.full_vn, b.write_indices, out=b.lengths, flags=b.flags),
             }
         return self._calls
+
+    def attention(self):
+        """Decode attention of every windowed layer over its window (after
+        the step has appended and written the lengths); returns the outputs."""
+        if getattr(self, "_att", None) is None:
+            b, s = self.buffers, self.spec
+            self._att = swrt.prepare_window_attention(b.win_q, b.win_k, b.win_v,
+                                                      b.lengths.cache_total, s.window,
+                                                      outs=b.win_out, flags=b.flags)
+        return self._att()
+
+    def attention_bytes(self) -> int:
+        """Bytes the attention must move: the visible K and V rows of every
+        windowed layer read once, the queries read and the outputs written."""
+        s = self.spec
+        es = torch.empty((), dtype=s.dtype).element_size()
+        L = np.minimum(s.total_lens.astype(np.int64), s.window)  # W = C: every resident row
+        rows = int(L.sum()) * s.kv_heads
+        nw = len(s.windowed_layers)
+        return nw * (2 * rows * s.head_dim * es + 2 * s.batch * s.q_heads * s.head_dim * es)
 
     def lengths(self):
         self._prepared()["lengths"]()

@@ -31,6 +31,9 @@ Workloads (sizes and distributions):
      caches int8 (random bytes); K rows rotated at position T - 1 with
      rotary_dim 64 (half-split pairs, tables cos/sin of p * 10000^(-2j/64),
      8192 positions); K scale 0.02, V scale 0.01, zero points 0.
+  8  workload 5 followed by decode attention over its 12 windowed layers:
+     queries bf16 [64, 64, 64] per layer (64 query heads on 8 KV heads, the
+     CPU follow-up's head layout), window W = 128 = C, scale 1/8.
 """
 from __future__ import annotations
 
@@ -165,6 +168,8 @@ class ModelStep:
     rope_positions: int = 0
     k_scale: float = 1.0
     v_scale: float = 1.0
+    # decode attention over the windowed layers (0: none)
+    q_heads: int = 0
 
 
 def workload1() -> ScatterCase:
@@ -251,6 +256,13 @@ def workload7() -> ModelStep:
     step.rotary_dim = 64
     step.rope_positions = 8192
     step.k_scale, step.v_scale = 0.02, 0.01
+    return step
+
+
+def workload8() -> ModelStep:
+    step = workload5(torch.bfloat16)
+    step.seed = 8
+    step.q_heads = 64
     return step
 
 

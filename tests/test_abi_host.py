@@ -49,7 +49,7 @@ def test_exports_every_declared_function(L):
     assert {"swrt_tensor_scatter", "swrt_tensor_scatter_batched", "swrt_kv_seq_lengths", "swrt_kv_window_append",
             "swrt_kv_window_append_layers", "swrt_kv_decode_step", "swrt_kv_seq_lengths_drift",
             "swrt_kv_window_append_xf", "swrt_tensor_scatter_xf", "swrt_kv_decode_step_xf",
-            "swrt_status_string",
+            "swrt_window_attention", "swrt_status_string",
             "swrt_abi_version"} <= declared
     out = subprocess.run(["nm", "-D", "--defined-only", swrt.LIBRARY], check=True,
                          capture_output=True, text=True).stdout
@@ -318,3 +318,27 @@ def test_fused_append_rejects(L):
                                         None if x is None else ctypes.byref(x), None, None)
     assert dec(None) == INV and dec(_xf(), nfl=33) == INV and dec(_xf(), nfl=-1) == INV
     assert dec(_xf()) in launched
+
+
+@no_gpu_visible
+def test_window_attention_rejects(L):
+    INV, UNS, V = swrt.E_INVALID_ARG, swrt.E_UNSUPPORTED, ctypes.c_void_p
+    launched = (swrt.OK, swrt.E_LAUNCH)
+    arr = lambda *p: (V * len(p))(*p)  # noqa: E731
+
+    def att(q=A, k=B_, v=C_, out=D_, lens=D_ + 0x10_0000, W=8, B=2, Hq=8, Hkv=2, Cap=16, D=64,
+            scale=0.125, et=3, ot=3, n=1):
+        return L.swrt_window_attention(n, arr(q), arr(k), arr(v), arr(out), lens, W, B, Hq, Hkv,
+                                       Cap, D, scale, et, ot, None, None)
+    assert att() in launched
+    assert att(W=0) == INV and att(Cap=0) == INV and att(Hkv=0) == INV and att(B=-1) == INV
+    assert att(Hq=6, Hkv=4) == INV                           # not a multiple
+    assert att(Hq=6, Hkv=2) == UNS                           # group of 3
+    assert att(D=24) == UNS and att(D=40) == UNS             # 48-, 80-byte rows
+    assert att(Hq=32, Hkv=2, D=128) == UNS                   # group 16 x 256-byte rows
+    assert att(et=4) == INV and att(ot=5) == INV             # no integer attention
+    assert att(scale=float("nan")) == INV and att(scale=float("inf")) == INV
+    assert att(q=A + 4) == INV and att(k=B_ + 2) == INV      # 8-byte alignment
+    assert att(out=B_ + 64) == INV                           # output inside a cache
+    assert att(lens=0) == INV and att(n=33) == INV
+    assert att(n=0) == swrt.OK and att(B=0) == swrt.OK
