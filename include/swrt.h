@@ -476,8 +476,8 @@ int swrt_kv_decode_step_xf(int n_window_layers, void *const *win_k_caches,
  * q                 [batch, q_heads, head_dim] elem_type, 8-byte aligned.
  * k_caches, v_caches [batch, kv_heads, capacity, head_dim] elem_type, 8-byte
  *                   aligned (the windowed caches of swrt_kv_window_append).
- * out               [batch, q_heads, head_dim] out_type; must not overlap any
- *                   other buffer.
+ * out               [batch, q_heads, head_dim] out_type, aligned to its
+ *                   element size; must not overlap any other buffer.
  * cache_total_lens  device int32[batch]: L of swrt_kv_seq_lengths (or _drift).
  * window            W >= 1 (W = capacity: every resident row; the ring-buffer
  *                   cache is this case).
@@ -486,7 +486,10 @@ int swrt_kv_decode_step_xf(int n_window_layers, void *const *win_k_caches,
  * d_flags           SWRT_FLAG_BAD_LENGTHS when L < 0 or L > capacity: that
  *                   entry's outputs are left as they were.
  * Supported shapes (else SWRT_E_UNSUPPORTED): q_heads / kv_heads in
- * {1, 2, 4, 8, 16}; head_dim * element size in {64, 128, 256, 512} bytes;
+ * {1, 2, 4, 8, 16}; head_dim * element size in {64, 128, 256, 512} bytes.
+ * 16-bit caches with q, k, v and out all 16-byte aligned run on the matrix
+ * cores and take every such shape; fp32 caches, or 16-bit ones with an
+ * operand only 8-byte aligned, run on the VALU and also need
  * (q_heads / kv_heads) * head_dim * element size <= 2048 bytes.
  */
 int swrt_window_attention(int n_layers, const void *const *q,

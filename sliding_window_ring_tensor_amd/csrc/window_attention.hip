@@ -38,6 +38,7 @@ struct AttArgs {
   uint32_t *flags;
   float scale_log2;  // scale * log2(e)
   int32_t W, B, Hq, Hkv, C, D, out_type;
+  int32_t items;  // n_layers * B * Hkv
 };
 
 template <int ELEM>
@@ -283,6 +284,291 @@ __global__ __launch_bounds__(kAttBlock) void window_attention_kernel(AttArgs a) 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Matrix-core path (16-bit caches). Both contractions of a KV head's window
+// run on MFMA, so the VALU keeps only the softmax of each (row, head) score
+// once, instead of per lane of a row as above.
+//   scores  S^T = K Q^T with v_mfma_f32_16x16x32_{bf16,f16}: 16 window rows
+//           (M) by 16 head slots (N; heads >= G are zero), head_dim reduced
+//           32 per instruction. Products of two 16-bit values are exact in
+//           fp32; the sum of head_dim of them is rounded in fp32.
+//   values  O^T = V^T P^T with v_mfma_f32_16x16x4_f32: 16 output dimensions
+//           by 16 head slots, 4 rows per instruction, the weights P in fp32
+//           (not rounded to 16 bits), V widened exactly to fp32.
+// Lane l holds head slot j = l % 16 of every accumulator and rows
+// q + 4 r (q = l / 16, r = 0..3) of each 16-row tile of scores; the key
+// operand carries tile row pk(i) = i / 4 + 4 (i % 4) at matrix row i, so the
+// scores' row 4 q + r is tile row q + 4 r and the value product's k-th
+// instruction (rows 4 k .. 4 k + 3 of the tile, one per lane group q) takes
+// its weights straight from each lane's r = k score. Dimension
+// MT * i + m (MT = head_dim / 16) sits at matrix row i of output tile m, so a
+// lane reads MT consecutive elements of a V row and ends holding 4 MT
+// consecutive output dimensions, 4 MT q .. 4 MT q + 4 MT - 1, of its head.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int ELEM>
+__device__ __forceinline__ f32x4 score_mfma(u32x4 k, u32x4 q, f32x4 acc) {
+  if constexpr (ELEM == SWRT_XF_BF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k),
+                                                   __builtin_bit_cast(bf16x8, q), acc, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, k),
+                                                  __builtin_bit_cast(f16x8, q), acc, 0, 0, 0);
+}
+
+// NB bytes (4, 8, 16 or 32) of a row as 32-bit words, streamed
+template <int NB>
+__device__ __forceinline__ void att_load_words(const char *p, uint32_t (&w)[NB / 4]) {
+  if constexpr (NB == 4) {
+    w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p));
+  } else if constexpr (NB == 8) {
+    const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+    w[0] = x.x;
+    w[1] = x.y;
+  } else {
+#pragma unroll
+    for (int i = 0; i < NB / 16; ++i) {
+      const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p) + i);
+      w[4 * i] = x.x;
+      w[4 * i + 1] = x.y;
+      w[4 * i + 2] = x.z;
+      w[4 * i + 3] = x.w;
+    }
+  }
+}
+
+// element e of a lane's packed 16-bit V elements, widened exactly
+template <int ELEM, int NW32>
+__device__ __forceinline__ float att_elem(const uint32_t (&w)[NW32], int e) {
+  const uint32_t x = w[e / 2];
+  if constexpr (ELEM == SWRT_XF_BF16)
+    return __uint_as_float(e % 2 ? x & 0xFFFF0000u : x << 16);
+  else
+    return float(__builtin_bit_cast(_Float16, uint16_t(e % 2 ? x >> 16 : x & 0xFFFFu)));
+}
+
+// merge state b into a, branch-free (an empty state has m = -inf, l = 0, o = 0)
+template <int N>
+__device__ __forceinline__ void att_merge_flat(float &m, float &l, f32x4 (&o)[N], float mb,
+                                               float lb, const f32x4 (&ob)[N]) {
+  const float mn = fmaxf(m, mb);
+  const bool none = mn == -INFINITY;
+  const float fa = none ? 0.0f : __builtin_amdgcn_exp2f(m - mn);
+  const float fb = none ? 0.0f : __builtin_amdgcn_exp2f(mb - mn);
+  l = l * fa + lb * fb;
+#pragma unroll
+  for (int i = 0; i < N; ++i) o[i] = o[i] * fa + ob[i] * fb;
+  m = mn;
+}
+
+constexpr int att_tiles(int D) { return D <= 32 ? 4 : D == 64 ? 2 : 1; }
+
+// One (layer, b, kv head) per NW waves: NW = 1 puts four of them in a
+// workgroup, NW = 4 splits one window's 16-row tiles over the four waves and
+// merges their states through LDS.
+template <int ELEM, int D, int NW>
+__global__ __launch_bounds__(kAttBlock) void window_attention_mfma(AttArgs a) {
+  constexpr int KS = D / 32;  // score instructions per tile
+  constexpr int MT = D / 16;  // output tiles
+  constexpr int VB = D / 8;   // bytes of a V row per lane (MT elements)
+  constexpr int T = att_tiles(D);  // tiles per block of the stream
+  constexpr uint32_t row_bytes = D * 2;
+  const uint32_t lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  const uint32_t j = lane % 16, qg = lane / 16;
+  const uint32_t item = blockIdx.x * (kAttWaves / NW) + wave / NW, ws = wave % NW;
+  if (item >= uint32_t(a.items)) return;  // NW = 4: the whole workgroup
+  const uint32_t g = item % uint32_t(a.Hkv), b = (item / uint32_t(a.Hkv)) % uint32_t(a.B);
+  const uint32_t layer = item / uint32_t(a.Hkv * a.B);
+  const int64_t L = a.L[b];
+  if (L < 0 || L > a.C) {  // no partial output for this entry (uniform in the workgroup for NW = 4)
+    if (a.flags && g == 0 && layer == 0 && ws == 0 && lane == 0) atomicOr(a.flags, SWRT_FLAG_BAD_LENGTHS);
+    return;
+  }
+  const int64_t r0 = L > a.W ? L - a.W : 0;
+  const int G = a.Hq / a.Hkv;
+  const bool head = int(j) < G;
+  const uint64_t kv_off = (uint64_t(b) * a.Hkv + g) * uint64_t(a.C) * row_bytes;
+  const char *kb = a.k[layer] + kv_off + 16 * qg;
+  const char *vb = a.v[layer] + kv_off + VB * j;
+
+  // query operand: head slot j's 8 elements of each 32-element step (zeros
+  // for slots past the group; they read head 0's row to stay in bounds)
+  u32x4 qo[KS];
+  {
+    const char *qp = a.q[layer] + (uint64_t(b) * a.Hq + g * G + (head ? j : 0)) * row_bytes +
+                     16 * qg;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const u32x4 x = *reinterpret_cast<const u32x4 *>(qp + 64 * s);
+      qo[s] = head ? x : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  float m = -INFINITY, l = 0.0f;
+  f32x4 acc[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int64_t n_tiles = (L - r0 + 15) / 16;
+  const uint32_t pk = (j >> 2) + 4 * (j & 3);  // tile row of this lane's key operand
+  for (int64_t t0 = int64_t(ws) * T; t0 < n_tiles; t0 += int64_t(NW) * T) {
+    // every load of the block first; tiles past the window (uniform in the
+    // wave) load nothing, and rows past L repeat row L - 1 and are masked
+    u32x4 kw[T][KS];
+    uint32_t vw[T][4][VB / 4];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      if (t0 + t < n_tiles) {
+        const int64_t tb = r0 + 16 * (t0 + t);
+        const int64_t rk = tb + pk < L ? tb + pk : L - 1;
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          kw[t][s] = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x4 *>(kb + rk * row_bytes + 64 * s));
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int64_t rv = tb + 4 * c + qg < L ? tb + 4 * c + qg : L - 1;
+          att_load_words<VB>(vb + rv * row_bytes, vw[t][c]);
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < KS; ++s) kw[t][s] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int i = 0; i < VB / 4; ++i) vw[t][c][i] = 0u;
+      }
+    }
+    // scores, then the block's softmax update: one maximum per head over the
+    // wave (the value product sums every lane group's rows), weights in
+    // fp32. Masked after the scale, so a negative scale cannot flip a -inf.
+    float x[T][4];
+    float bm = -INFINITY;
+    {
+#pragma clang fp contract(off)
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) sc = score_mfma<ELEM>(kw[t][s], qo[s], sc);
+        const int64_t tb = r0 + 16 * (t0 + t) + qg;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          x[t][r] = tb + 4 * r < L ? sc[r] * a.scale_log2 : -INFINITY;
+          bm = fmaxf(bm, x[t][r]);
+        }
+      }
+    }
+    bm = fmaxf(bm, __shfl_xor(bm, 16));
+    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    float p[T][4];
+    {
+#pragma clang fp contract(off)
+      const float mn = fmaxf(m, bm);
+      const bool none = mn == -INFINITY;  // nothing seen yet
+      const float f = none ? 1.0f : __builtin_amdgcn_exp2f(m - mn);
+      l *= f;
+#pragma unroll
+      for (int i = 0; i < MT; ++i) acc[i] *= f;
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          p[t][r] = none ? 0.0f : __builtin_amdgcn_exp2f(x[t][r] - mn);
+          l += p[t][r];
+        }
+      m = mn;
+    }
+    // the block's weighted rows
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(att_elem<ELEM, VB / 4>(vw[t][c], i),
+                                                        p[t][c], acc[i], 0, 0, 0);
+  }
+
+  if constexpr (NW > 1) {  // the waves' states, merged by wave 0 through LDS
+    __shared__ float st[NW - 1][2 + 4 * MT][64];
+    if (ws > 0) {
+      st[ws - 1][0][lane] = m;
+      st[ws - 1][1][lane] = l;
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st[ws - 1][2 + 4 * i + r][lane] = acc[i][r];
+    }
+    __syncthreads();
+    if (ws > 0) return;
+#pragma unroll
+    for (int w = 0; w < NW - 1; ++w) {
+      f32x4 ob[MT];
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ob[i][r] = st[w][2 + 4 * i + r][lane];
+      att_merge_flat<MT>(m, l, acc, st[w][0][lane], st[w][1][lane], ob);
+    }
+  }
+  // the head's weight sum over the four lane groups
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  if (!head) return;
+  const float inv = l > 0.0f ? 1.0f / l : 0.0f;  // an empty window gives zeros
+  // dimensions 4 MT qg + e, e = MT r + i, of head g * G + j
+  float y[4 * MT];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int i = 0; i < MT; ++i) y[MT * r + i] = acc[i][r] * inv;
+  const uint64_t orow = uint64_t(b) * a.Hq + g * G + j;
+  if (a.out_type == SWRT_XF_F32) {
+    u32x4 *dst = reinterpret_cast<u32x4 *>(a.out[layer] + (orow * D + 4 * MT * qg) * 4);
+#pragma unroll
+    for (int c = 0; c < MT; ++c)
+      dst[c] = u32x4{__float_as_uint(y[4 * c]), __float_as_uint(y[4 * c + 1]),
+                     __float_as_uint(y[4 * c + 2]), __float_as_uint(y[4 * c + 3])};
+  } else {
+    uint32_t h[2 * MT];
+#pragma unroll
+    for (int e = 0; e < 2 * MT; ++e) {
+      const uint32_t lo = a.out_type == SWRT_XF_BF16 ? xf_bf16(y[2 * e]) : xf_f16(y[2 * e]);
+      const uint32_t hi = a.out_type == SWRT_XF_BF16 ? xf_bf16(y[2 * e + 1]) : xf_f16(y[2 * e + 1]);
+      h[e] = lo | (hi << 16);
+    }
+    u32x4 *dst = reinterpret_cast<u32x4 *>(a.out[layer] + (orow * D + 4 * MT * qg) * 2);
+#pragma unroll
+    for (int c = 0; c < MT / 2; ++c) dst[c] = u32x4{h[4 * c], h[4 * c + 1], h[4 * c + 2], h[4 * c + 3]};
+  }
+}
+
+template <int ELEM, int D>
+int launch_mfma(const AttArgs &a, int nw, hipStream_t s) {
+  if (nw == 1) {
+    const uint32_t grid = (uint32_t(a.items) + kAttWaves - 1) / kAttWaves;
+    hipLaunchKernelGGL((window_attention_mfma<ELEM, D, 1>), dim3(grid), dim3(kAttBlock), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((window_attention_mfma<ELEM, D, kAttWaves>), dim3(uint32_t(a.items)),
+                       dim3(kAttBlock), 0, s, a);
+  }
+  return launch_status();
+}
+
+template <int ELEM>
+int launch_mfma_d(const AttArgs &a, int nw, hipStream_t s) {
+  switch (a.D) {
+    case 32: return launch_mfma<ELEM, 32>(a, nw, s);
+    case 64: return launch_mfma<ELEM, 64>(a, nw, s);
+    case 128: return launch_mfma<ELEM, 128>(a, nw, s);
+    default: return launch_mfma<ELEM, 256>(a, nw, s);
+  }
+}
+
 template <int ELEM, int LPR, int G>
 int launch_one(const AttArgs &a, uint32_t grid, hipStream_t s) {
   if constexpr (att_supported(LPR, G)) {
@@ -342,7 +628,10 @@ extern "C" int swrt_window_attention(int n_layers, const void *const *q,
   const int64_t row = int64_t(head_dim) * es;
   const int64_t lpr = row / 8;
   if (row % 8 || (lpr != 8 && lpr != 16 && lpr != 32 && lpr != 64)) return SWRT_E_UNSUPPORTED;
-  if (G * lpr > 256) return SWRT_E_UNSUPPORTED;  // see att_supported
+  // 16-bit caches take the matrix-core kernel, 16-byte aligned operands
+  // needed; fp32 caches (or 8-byte aligned operands) the VALU one
+  bool mfma = elem_type != SWRT_XF_F32;
+  if (!mfma && G * lpr > 256) return SWRT_E_UNSUPPORTED;  // see att_supported
   if (!q || !k_caches || !v_caches || !out || !cache_total_lens) return SWRT_E_INVALID_ARG;
   int64_t cache_bytes, q_bytes, o_bytes;
   if (!mul_ok(int64_t(batch) * kv_heads * capacity, row, &cache_bytes) ||
@@ -358,6 +647,9 @@ extern "C" int swrt_window_attention(int n_layers, const void *const *q,
     if (addr_of(q[l]) % 8 || addr_of(k_caches[l]) % 8 || addr_of(v_caches[l]) % 8 ||
         addr_of(out[l]) % uint64_t(oes))
       return SWRT_E_INVALID_ARG;
+    if (addr_of(q[l]) % 16 || addr_of(k_caches[l]) % 16 || addr_of(v_caches[l]) % 16 ||
+        addr_of(out[l]) % 16)
+      mfma = false;
     ranges[nr++] = range(q[l], uint64_t(q_bytes), false);
     ranges[nr++] = range(k_caches[l], uint64_t(cache_bytes), false);
     ranges[nr++] = range(v_caches[l], uint64_t(cache_bytes), false);
@@ -383,7 +675,16 @@ extern "C" int swrt_window_attention(int n_layers, const void *const *q,
   a.out_type = out_type;
   static_assert(sizeof(AttArgs) <= 4096, "kernel arguments exceed 4 KiB");
   const uint32_t grid = uint32_t(n_layers) * uint32_t(batch) * uint32_t(kv_heads);
+  a.items = int32_t(grid);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (mfma) {
+    // one wave per (layer, b, kv head) once there are enough of them to fill
+    // the chip, else four waves share each window
+    const int nw = grid >= 2048 ? 1 : kAttWaves;
+    return elem_type == SWRT_XF_BF16 ? launch_mfma_d<SWRT_XF_BF16>(a, nw, s)
+                                     : launch_mfma_d<SWRT_XF_F16>(a, nw, s);
+  }
+  if (G * lpr > 256) return SWRT_E_UNSUPPORTED;  // misaligned 16-bit operands
   switch (elem_type) {
     case SWRT_XF_F32: return launch_lpr<SWRT_XF_F32>(a, int(lpr), G, grid, s);
     case SWRT_XF_F16: return launch_lpr<SWRT_XF_F16>(a, int(lpr), G, grid, s);

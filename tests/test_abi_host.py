@@ -335,7 +335,9 @@ def test_window_attention_rejects(L):
     assert att(Hq=6, Hkv=4) == INV                           # not a multiple
     assert att(Hq=6, Hkv=2) == UNS                           # group of 3
     assert att(D=24) == UNS and att(D=40) == UNS             # 48-, 80-byte rows
-    assert att(Hq=32, Hkv=2, D=128) == UNS                   # group 16 x 256-byte rows
+    assert att(Hq=32, Hkv=2, D=128) in launched              # 16-bit: the matrix-core kernel
+    assert att(Hq=32, Hkv=2, D=128, q=A + 8) == UNS          # 8-byte aligned: the VALU kernel,
+    assert att(Hq=32, Hkv=2, D=64, et=1, ot=1) == UNS        # as for fp32: group 16 x 256 B
     assert att(et=4) == INV and att(ot=5) == INV             # no integer attention
     assert att(scale=float("nan")) == INV and att(scale=float("inf")) == INV
     assert att(q=A + 4) == INV and att(k=B_ + 2) == INV      # 8-byte alignment

@@ -1,19 +1,22 @@
 """GPU parity of the windowed decode attention against the float64 oracle.
 
-The kernel computes in binary32 (dot products reduced across lanes, exp2 with
-log2(e) folded into the scale, online-softmax merges) and the oracle in
-float64, so outputs agree within a bound derived from that arithmetic, per
-batch entry and head (u = 2^-24, S1 = |scale| * max over visible rows of
-sum_d |q_d k_rd|, Vmax = max |v| over visible rows, n = visible rows):
+The kernels compute in binary32 (dot products of exact 16-bit or fp32
+products, exp2 with log2(e) folded into the scale, online-softmax merges) and
+the oracle in float64, so outputs agree within a bound derived from that
+arithmetic, per batch entry and head (u = 2^-24, D = head_dim, S1 = |scale| *
+max over visible rows of sum_d |q_d k_rd|, Vmax = max |v| over visible rows,
+n = visible rows):
 
-  |gpu - oracle| <= 4 * (2 * (12 u S1 + 2^-21) + (n + 64) u) * Vmax
+  |gpu - oracle| <= 4 * (2 * ((D + 4) u S1 + 2^-21) + (2 n + 64) u) * Vmax
                     (+ one output ulp, 2^-8 |oracle| for bf16, 2^-10 for f16)
 
-the first term bounding the relative error of every softmax weight (a fp32
-score carries at most ~12 roundings of terms bounded by S1; exp2 is within
-2^-22), the second the accumulation of n weighted rows. Dropping or adding a
-row, a wrong window edge, a wrong KV head or a missing scale moves the output
-by about Vmax / n, orders of magnitude above the bound.
+the first term bounding the relative error of every softmax weight (a score
+is a sum of D products rounded in fp32 in an order the matrix cores fix, at
+most D - 1 roundings of terms bounded by S1, then the scale and the shift by
+the maximum; exp2 is within 2^-22), the second the accumulation of n weighted
+rows and one rescale per block of rows. Dropping or adding a row, a wrong
+window edge, a wrong KV head or a missing scale moves the output by about
+Vmax / n, orders of magnitude above the bound.
 """
 from __future__ import annotations
 
@@ -71,7 +74,7 @@ def bound(q, k, v, L, W, scale, out_dtype, ref):
             kr, vr = kd[b, h // G, r0:r1], vd[b, h // G, r0:r1]
             s1 = abs(scale) * np.abs(qd[b, h][None, :] * kr).sum(axis=1).max()
             vmax = np.abs(vr).max()
-            tol[b, h] = 4 * (2 * (12 * U * s1 + 2.0 ** -21) + (r1 - r0 + 64) * U) * vmax
+            tol[b, h] = 4 * (2 * ((D + 4) * U * s1 + 2.0 ** -21) + (2 * (r1 - r0) + 64) * U) * vmax
     return tol * (1 + ULP[out_dtype]) + ULP[out_dtype] * 1.01 * np.abs(ref) + 1e-30
 
 
@@ -101,7 +104,9 @@ SHAPES = [  # (dtype, D, Hq, Hkv): every lanes-per-row width and group size
     (torch.bfloat16, 64, 8, 8), (torch.bfloat16, 64, 16, 8), (torch.bfloat16, 64, 16, 4),
     (torch.bfloat16, 64, 64, 8), (torch.bfloat16, 64, 32, 2),
     (torch.bfloat16, 128, 64, 8), (torch.bfloat16, 256, 16, 4),
-    (torch.float16, 64, 64, 8), (torch.float16, 128, 8, 4),
+    (torch.bfloat16, 128, 32, 2), (torch.bfloat16, 256, 16, 1),  # group 16, matrix cores only
+    (torch.float16, 32, 8, 1), (torch.float16, 64, 64, 8), (torch.float16, 128, 8, 4),
+    (torch.float16, 256, 32, 2),
     (torch.float32, 16, 4, 2), (torch.float32, 64, 64, 8), (torch.float32, 128, 8, 8),
 ]
 
@@ -126,6 +131,47 @@ def test_window_attention_shapes(orc, dtype, D, Hq, Hkv, out_same):
         say("  W", W, "worst err/tol", round(worst, 4))
         for o in outs:  # the empty window gives zeros
             assert (o[0] == 0).all()
+
+
+@pytest.mark.parametrize("dtype,D,Hq,Hkv", [(torch.bfloat16, 64, 32, 4), (torch.float16, 128, 8, 8),
+                                           (torch.bfloat16, 32, 16, 16)], ids=str)
+def test_many_windows_one_wave_each(orc, dtype, D, Hq, Hkv):
+    """Enough (layer, b, kv head) windows that each takes one wave (the
+    matrix-core kernel's other launch shape), ragged lengths and windows."""
+    say("window attention, many windows", dtype, D, Hq, Hkv)
+    g = wl.rng(D + Hq + Hkv)
+    n_layers, B, C = 2, 2048 // Hkv, 48
+    qs, ks, vs = make(g, B, Hq, Hkv, C, D, dtype, n_layers=n_layers)
+    L = g.integers(0, C + 1, size=B).astype(np.int32)
+    L[:4] = [0, 1, 17, C]
+    for W in (C, 21):
+        outs = swrt.window_attention([t.to(DEV) for t in qs], [t.to(DEV) for t in ks],
+                                     [t.to(DEV) for t in vs], torch.from_numpy(L).to(DEV), W,
+                                     out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        worst = check(orc, qs, ks, vs, L, W, D ** -0.5, outs, torch.float32)
+        say("  W", W, "worst err/tol", round(worst, 4))
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_eight_byte_aligned_operands(orc, dtype):
+    """16-bit operands that are 8- but not 16-byte aligned take the VALU
+    kernel; same results within the bound."""
+    g = wl.rng(11)
+    B, Hq, Hkv, C, D = 5, 16, 4, 40, 64
+    qs, ks, vs = make(g, B, Hq, Hkv, C, D, dtype, n_layers=1)
+
+    def shifted(t):  # the same values at an address 8 bytes past a 16-byte boundary
+        buf = torch.empty(t.numel() + 4, dtype=dtype, device=DEV)
+        v = buf[4:].view(t.shape)
+        v.copy_(t.to(DEV))
+        assert v.data_ptr() % 16 == 8
+        return v
+    L = np.array([40, 3, 0, 39, 16], np.int32)
+    outs = swrt.window_attention([shifted(qs[0])], [shifted(ks[0])], [shifted(vs[0])],
+                                 torch.from_numpy(L).to(DEV), 24, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    check(orc, qs, ks, vs, L, 24, D ** -0.5, outs, torch.float32)
 
 
 def test_large_scores_stay_finite(orc):
