@@ -25,6 +25,9 @@ FLAGS = [
     "-Wall", "-Wno-unused-function",
     # packed-fp32 instructions stay off in every kernel of this library
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core accumulators in ordinary VGPRs: the attention kernel
+    # rescales them on the VALU between products
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

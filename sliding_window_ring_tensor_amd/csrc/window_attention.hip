@@ -365,6 +365,7 @@ __device__ __forceinline__ void att_merge_flat(float &m, float &l, f32x4 (&o)[N]
 }
 
 constexpr int att_tiles(int D) { return D <= 32 ? 4 : D == 64 ? 2 : 1; }
+constexpr bool kAttPrefetch = false;
 
 // One (layer, b, kv head) per NW waves: NW = 1 puts four of them in a
 // workgroup, NW = 4 splits one window's 16-row tiles over the four waves and
@@ -387,7 +388,8 @@ __global__ __launch_bounds__(kAttBlock) void window_attention_mfma(AttArgs a) {
     if (a.flags && g == 0 && layer == 0 && ws == 0 && lane == 0) atomicOr(a.flags, SWRT_FLAG_BAD_LENGTHS);
     return;
   }
-  const int64_t r0 = L > a.W ? L - a.W : 0;
+  // row numbers stay below capacity + 16 < 2^31 (checked on the host)
+  const int32_t Li = int32_t(L), r0 = Li > a.W ? Li - a.W : 0, last = Li - 1;
   const int G = a.Hq / a.Hkv;
   const bool head = int(j) < G;
   const uint64_t kv_off = (uint64_t(b) * a.Hkv + g) * uint64_t(a.C) * row_bytes;
@@ -412,36 +414,66 @@ __global__ __launch_bounds__(kAttBlock) void window_attention_mfma(AttArgs a) {
 #pragma unroll
   for (int i = 0; i < MT; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  const int64_t n_tiles = (L - r0 + 15) / 16;
-  const uint32_t pk = (j >> 2) + 4 * (j & 3);  // tile row of this lane's key operand
-  for (int64_t t0 = int64_t(ws) * T; t0 < n_tiles; t0 += int64_t(NW) * T) {
-    // every load of the block first; tiles past the window (uniform in the
-    // wave) load nothing, and rows past L repeat row L - 1 and are masked
+  const int32_t n_tiles = (Li - r0 + 15) / 16;
+  const int32_t pk = (j >> 2) + 4 * (j & 3);  // tile row of this lane's key operand
+  // Blocks of T tiles. A block wholly inside the window loads from two
+  // pointers with constant offsets and needs no mask; the last one clamps
+  // rows past L to row L - 1 (masked), and tiles past the window (uniform in
+  // the wave) load nothing.
+  struct Tiles {
     u32x4 kw[T][KS];
     uint32_t vw[T][4][VB / 4];
+  };
+  auto load = [&](Tiles &d, int32_t t0) {
+    if (r0 + 16 * (t0 + T) <= Li) {
+      const char *kr = kb + uint64_t(uint32_t(r0 + 16 * t0 + pk)) * row_bytes;
+      const char *vr = vb + uint64_t(uint32_t(r0 + 16 * t0 + int32_t(qg))) * row_bytes;
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          d.kw[t][s] = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x4 *>(kr + 16 * t * row_bytes + 64 * s));
+#pragma unroll
+        for (int c = 0; c < 4; ++c) att_load_words<VB>(vr + (16 * t + 4 * c) * row_bytes, d.vw[t][c]);
+      }
+      return;
+    }
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       if (t0 + t < n_tiles) {
-        const int64_t tb = r0 + 16 * (t0 + t);
-        const int64_t rk = tb + pk < L ? tb + pk : L - 1;
+        const int32_t tb = r0 + 16 * (t0 + t);
+        const char *kr = kb + uint64_t(uint32_t(min(tb + pk, last))) * row_bytes;
 #pragma unroll
         for (int s = 0; s < KS; ++s)
-          kw[t][s] = __builtin_nontemporal_load(
-              reinterpret_cast<const u32x4 *>(kb + rk * row_bytes + 64 * s));
+          d.kw[t][s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kr + 64 * s));
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int64_t rv = tb + 4 * c + qg < L ? tb + 4 * c + qg : L - 1;
-          att_load_words<VB>(vb + rv * row_bytes, vw[t][c]);
-        }
+        for (int c = 0; c < 4; ++c)
+          att_load_words<VB>(
+              vb + uint64_t(uint32_t(min(tb + 4 * c + int32_t(qg), last))) * row_bytes,
+              d.vw[t][c]);
       } else {
 #pragma unroll
-        for (int s = 0; s < KS; ++s) kw[t][s] = u32x4{0u, 0u, 0u, 0u};
+        for (int s = 0; s < KS; ++s) d.kw[t][s] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int c = 0; c < 4; ++c)
 #pragma unroll
-          for (int i = 0; i < VB / 4; ++i) vw[t][c][i] = 0u;
+          for (int i = 0; i < VB / 4; ++i) d.vw[t][c][i] = 0u;
       }
     }
+  };
+  Tiles cur;
+  if constexpr (kAttPrefetch) load(cur, int32_t(ws) * T);
+  for (int32_t t0 = int32_t(ws) * T; t0 < n_tiles; t0 += NW * T) {
+    // with prefetch, the next block's loads are issued before this block's
+    // arithmetic, so a wave keeps two blocks of reads in flight
+    Tiles nxt;
+    if constexpr (kAttPrefetch)
+      load(nxt, t0 + NW * T);
+    else
+      load(cur, t0);
+    const auto &kw = cur.kw;
+    const auto &vw = cur.vw;
     // scores, then the block's softmax update: one maximum per head over the
     // wave (the value product sums every lane group's rows), weights in
     // fp32. Masked after the scale, so a negative scale cannot flip a -inf.
@@ -449,30 +481,51 @@ __global__ __launch_bounds__(kAttBlock) void window_attention_mfma(AttArgs a) {
     float bm = -INFINITY;
     {
 #pragma clang fp contract(off)
+      f32x4 sc[T];
 #pragma unroll
       for (int t = 0; t < T; ++t) {
-        f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
+        sc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int s = 0; s < KS; ++s) sc = score_mfma<ELEM>(kw[t][s], qo[s], sc);
-        const int64_t tb = r0 + 16 * (t0 + t) + qg;
+        for (int s = 0; s < KS; ++s) sc[t] = score_mfma<ELEM>(kw[t][s], qo[s], sc[t]);
+      }
+      if (r0 + 16 * (t0 + T) <= Li) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          x[t][r] = tb + 4 * r < L ? sc[r] * a.scale_log2 : -INFINITY;
-          bm = fmaxf(bm, x[t][r]);
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            x[t][r] = sc[t][r] * a.scale_log2;
+            bm = fmaxf(bm, x[t][r]);
+          }
+      } else {
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          const int32_t tb = r0 + 16 * (t0 + t) + int32_t(qg);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            x[t][r] = tb + 4 * r < Li ? sc[t][r] * a.scale_log2 : -INFINITY;
+            bm = fmaxf(bm, x[t][r]);
+          }
         }
       }
     }
     bm = fmaxf(bm, __shfl_xor(bm, 16));
     bm = fmaxf(bm, __shfl_xor(bm, 32));
+    // The reference maximum m moves only when the block's exceeds it by more
+    // than 2^8 (log2 units): weights exp2(x - m) stay below 2^8, which costs
+    // no precision in fp32, and most blocks skip the rescale of the state.
+    // A single visible row still gets weight exp2(0) = 1 exactly.
     float p[T][4];
     {
 #pragma clang fp contract(off)
-      const float mn = fmaxf(m, bm);
-      const bool none = mn == -INFINITY;  // nothing seen yet
-      const float f = none ? 1.0f : __builtin_amdgcn_exp2f(m - mn);
-      l *= f;
+      const bool move = bm > m + 8.0f;  // m = -inf: the first block with a visible row
+      const float mn = move ? bm : m;
+      if (__builtin_amdgcn_ballot_w64(move && m != -INFINITY)) {
+        const float f = move ? __builtin_amdgcn_exp2f(m - mn) : 1.0f;
+        l *= f;
 #pragma unroll
-      for (int i = 0; i < MT; ++i) acc[i] *= f;
+        for (int i = 0; i < MT; ++i) acc[i] *= f;
+      }
+      const bool none = mn == -INFINITY;  // nothing seen yet
 #pragma unroll
       for (int t = 0; t < T; ++t)
 #pragma unroll
@@ -491,6 +544,7 @@ __global__ __launch_bounds__(kAttBlock) void window_attention_mfma(AttArgs a) {
         for (int i = 0; i < MT; ++i)
           acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(att_elem<ELEM, VB / 4>(vw[t][c], i),
                                                         p[t][c], acc[i], 0, 0, 0);
+    if constexpr (kAttPrefetch) cur = nxt;
   }
 
   if constexpr (NW > 1) {  // the waves' states, merged by wave 0 through LDS
@@ -620,6 +674,7 @@ extern "C" int swrt_window_attention(int n_layers, const void *const *q,
   if (out_type != SWRT_XF_F32 && out_type != SWRT_XF_F16 && out_type != SWRT_XF_BF16)
     return SWRT_E_INVALID_ARG;
   if (q_heads % kv_heads) return SWRT_E_INVALID_ARG;
+  if (capacity > INT32_MAX - 32) return SWRT_E_UNSUPPORTED;  // row numbers in int32
   if (!(scale == scale) || scale > 3.4028235e38f || scale < -3.4028235e38f) return SWRT_E_INVALID_ARG;
   if (n_layers == 0 || batch == 0 || q_heads == 0 || head_dim == 0) return SWRT_OK;
   const int G = q_heads / kv_heads;
