@@ -56,13 +56,17 @@ MEASURED_TRAFFIC = {
     ("bf16->int8", "decode_step_kernel", "5a17d20369dcd20b"): {"read": 101_380_857,
                                                                "written": 98_911_877},
     ("bf16", "window_in_place", "f3fee1005c69ec6b"): {"read": 195_175_201, "written": 196_001_407},
+    ("bf16", "window_attention_mfma", "a37d64d0de573e74"): {"read": 202_241_968,
+                                                           "written": 6_291_474},
 }
 _CSRC = "sliding_window_ring_tensor_amd/csrc/"
 KERNEL_SOURCES = {
     "window_in_place": ("kv_window.hip", "window_device.hpp", "xf_device.hpp", "swrt_device.hpp"),
     "decode_step_kernel": ("decode_step.hip", "window_device.hpp", "scatter_device.hpp",
                            "xf_device.hpp", "swrt_device.hpp"),
-    "window_attention_kernel": ("window_attention.hip", "xf_device.hpp", "swrt_device.hpp"),
+    # the attention kernel's code also depends on a code-generation flag of the build
+    "window_attention_mfma": ("window_attention.hip", "xf_device.hpp", "swrt_device.hpp",
+                              "../build.py"),
 }
 
 
@@ -396,6 +400,33 @@ def drift_loop(args, dev):
     print(json.dumps(out))
 
 
+def copy_reference(dev, stream):
+    """Achievable reference: 1 GiB device-to-device copies (GB/s moved), by
+    torch and by the library's own copy engine (TensorScatter out of place,
+    S = 0, which is also the counters' calibration kernel)."""
+    import sliding_window_ring_tensor_amd as swrt
+
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+
+    def copy_gbs(fn, n=10):
+        fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return 2 * (1 << 30) * n / (a.elapsed_time(b) * 1e-3) / 1e9
+
+    torch_copy = copy_gbs(lambda: dst.copy_(src))
+    s3, d3 = src.view(1, 1 << 26, 16), dst.view(1, 1 << 26, 16)
+    swrt_copy = copy_gbs(lambda: swrt.tensor_scatter(s3, s3[:, :0], None, axis=1, out=d3))
+    del src, dst, s3, d3
+    return torch_copy, swrt_copy
+
+
 def attention_bench(args, dev):
     """Workload 8: decode attention over the 12 windowed layers of the model
     step (window_attention, one launch), after the step's append; K launches
@@ -421,13 +452,14 @@ def attention_bench(args, dev):
         att_dev = device(lambda i: steps[i].attention(), len(steps), att_s)
         log(f"timing {K} steps of append + attention ...")
         both_s = eager(lambda i: (steps[i].run_fused(), steps[i].attention()), len(steps))
+        torch_copy, swrt_copy = copy_reference(dev, stream)
     flags = [int(st.buffers.flags.item()) for st in steps]
     if any(flags):
         raise SystemExit(f"device flags raised during the benchmark: {flags}")
     value = byts / att_s / 1e9
     achieved = byts / att_dev / 1e9
-    meas = MEASURED_TRAFFIC.get(("bf16", "window_attention_kernel",
-                                 kernel_source_hash("window_attention_kernel")))
+    meas = MEASURED_TRAFFIC.get(("bf16", "window_attention_mfma",
+                                 kernel_source_hash("window_attention_mfma")))
     cpu = None
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle for about {args.cpu_seconds:.0f} s ...")
@@ -465,13 +497,15 @@ def attention_bench(args, dev):
                    "bytes_per_step": byts,
                    "form": "one launch per step (window_attention, all windowed layers)",
                    "cache_defeat": f"{args.sets} independent buffer sets round robin"},
-        "roofline": {"bound": "hbm", "kernel": "window_attention_kernel: 12 layers, one launch",
+        "roofline": {"bound": "hbm", "kernel": "window_attention_mfma: 12 layers, one launch",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if meas is None else meas["read"] + meas["written"],
                      "bytes_per_launch": byts, "mean_launch_us": round(att_dev * 1e6, 3)},
         "cpu_baseline": cpu,
         "append_plus_attention_us_per_step": round(both_s * 1e6, 2),
+        "copy_reference_gbs": {"torch_copy": round(torch_copy, 1),
+                               "swrt_tensor_scatter_copy": round(swrt_copy, 1)},
     }
     print(json.dumps(out))
 
@@ -606,26 +640,7 @@ def main():
         log(f"timing {K} three-launch steps ...")
         three_eager_s = events_block(lambda st: st.run_three())
 
-        # ---- achievable reference: 1 GiB device-to-device copies ----
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        src.fill_(1)
-
-        def copy_gbs(fn, n=10):
-            fn()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            for _ in range(n):
-                fn()
-            b.record(stream)
-            torch.cuda.synchronize()
-            return 2 * (1 << 30) * n / (a.elapsed_time(b) * 1e-3) / 1e9
-
-        torch_copy = copy_gbs(lambda: dst.copy_(src))
-        # the library's own copy engine: TensorScatter out of place, S = 0
-        s3, d3 = src.view(1, 1 << 26, 16), dst.view(1, 1 << 26, 16)
-        swrt_copy = copy_gbs(lambda: swrt.tensor_scatter(s3, s3[:, :0], None, axis=1, out=d3))
-        del src, dst, s3, d3
+        torch_copy, swrt_copy = copy_reference(dev, stream)
 
     flags = [int(st.buffers.flags.item()) for st in steps]
     if any(flags):
