@@ -37,6 +37,18 @@ FLAG_ROPE_RANGE = 8
 # element types of the row transform
 XF_F32, XF_F16, XF_BF16, XF_INT8, XF_UINT8 = 1, 2, 3, 4, 5
 XF_BYTES = {XF_F32: 4, XF_F16: 2, XF_BF16: 2, XF_INT8: 1, XF_UINT8: 1}
+# page formats beyond those: sub-byte affine codes; bits per element of every format
+XF_INT4, XF_UINT4, XF_INT2, XF_UINT2 = 6, 7, 8, 9
+PAGE_BITS = {XF_F32: 32, XF_F16: 16, XF_BF16: 16, XF_INT8: 8, XF_UINT8: 8, XF_INT4: 4,
+             XF_UINT4: 4, XF_INT2: 2, XF_UINT2: 2}
+FLAG_BAD_PAGES = 16
+FLAG_PAGE_FULL = 32
+# the C struct orc_page, 64 bytes
+PAGE_DTYPE = np.dtype([("start", "<i8"), ("length", "<i4"), ("capacity", "<i4"),
+                       ("k_offset", "<i8"), ("v_offset", "<i8"), ("k_format", "<i4"),
+                       ("v_format", "<i4"), ("k_scale", "<f4"), ("v_scale", "<f4"),
+                       ("k_zero_point", "<i4"), ("v_zero_point", "<i4"), ("reserved", "<i4", (2,))])
+assert PAGE_DTYPE.itemsize == 64
 
 
 def build(source: str = SOURCE, out: str = LIBRARY, extra: tuple = ()) -> str:
@@ -135,6 +147,15 @@ class Oracle:
         lib.orc_window_attention.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
                                              ctypes.c_double, i32, u32p]
         lib.orc_window_attention.restype = ctypes.c_int
+        f32 = ctypes.c_float
+        lib.orc_paged_attention.argtypes = [vp, i32, vp, i64, vp, i64, vp, vp, i64, vp, i64, i64,
+                                            i64, i64, i64, ctypes.c_double, u32p]
+        lib.orc_paged_attention.restype = ctypes.c_int
+        lib.orc_paged_quantize.argtypes = [vp, i64, vp, i64, vp, i64, vp, vp, i64, vp, i32, f32,
+                                           ctypes.c_int32, i32, f32, ctypes.c_int32, i64]
+        lib.orc_paged_quantize.restype = ctypes.c_int
+        lib.orc_paged_append.argtypes = [vp, i64, vp, i64, vp, vp, i64, vp, vp, i32, i64, i64, u32p]
+        lib.orc_paged_append.restype = ctypes.c_int
         self.lib = lib
 
     # -- TensorScatter ----------------------------------------------------
@@ -314,6 +335,63 @@ class Oracle:
         if st != OK:
             raise OracleError(f"orc_window_attention status {st}")
         return out, flags.value
+
+
+    # -- paged caches -----------------------------------------------------------
+    def paged_attention(self, q, q_type: int, arena, pages, page_ptr, page_ids, left_window: int,
+                        kv_heads: int, scale: float, out: np.ndarray | None = None):
+        """float64 attention of q [B, Hq, D] (q_type elements) over the paged
+        caches; returns (out [B, Hq, D] float64, flags)."""
+        B, Hq = q.shape[:2]
+        D = q.shape[2] * q.itemsize // XF_BYTES[q_type]
+        if out is None:
+            out = np.zeros((B, Hq, D), np.float64)
+        qc = np.ascontiguousarray(q)
+        ar = np.ascontiguousarray(arena, dtype=np.uint8)
+        pg = np.ascontiguousarray(pages, dtype=PAGE_DTYPE)
+        ptr = np.ascontiguousarray(page_ptr, dtype=np.int32)
+        ids = np.ascontiguousarray(page_ids, dtype=np.int32)
+        flags = ctypes.c_uint32(0)
+        st = self.lib.orc_paged_attention(_ptr(qc), q_type, _ptr(ar), ar.nbytes, _ptr(pg), len(pg),
+                                          _ptr(ptr), _ptr(ids), len(ids), _ptr(out), left_window,
+                                          B, Hq, kv_heads, D, scale, ctypes.byref(flags))
+        if st != OK:
+            raise OracleError(f"orc_paged_attention status {st}")
+        return out, flags.value
+
+    def paged_quantize(self, arena, pages, blocks, dst_offsets, k_format: int, k_scale: float,
+                       k_zero_point: int, v_format: int, v_scale: float, v_zero_point: int,
+                       head_dim: int, arena_out=None):
+        """QuantizePagedCache on copies: returns (status, arena_out, pages_out).
+        Without ``arena_out`` the destinations lie in (a copy of) the same arena."""
+        ar = np.array(arena, dtype=np.uint8, copy=True)
+        same = arena_out is None
+        out_ar = ar if same else np.array(arena_out, dtype=np.uint8, copy=True)
+        pg = np.ascontiguousarray(pages, dtype=PAGE_DTYPE)
+        pout = pg.copy()
+        bl = np.ascontiguousarray(blocks, dtype=np.int32)
+        dst = np.ascontiguousarray(dst_offsets, dtype=np.int64)
+        st = self.lib.orc_paged_quantize(_ptr(ar), ar.nbytes, _ptr(pg), len(pg), _ptr(bl), len(bl),
+                                         _ptr(dst), _ptr(out_ar), out_ar.nbytes, _ptr(pout),
+                                         k_format, k_scale, k_zero_point, v_format, v_scale,
+                                         v_zero_point, head_dim)
+        return st, out_ar, pout
+
+    def paged_append(self, arena, pages, page_ptr, page_ids, k_new, v_new, new_type: int,
+                     head_dim: int):
+        """Decode append on copies: returns (arena, pages, flags)."""
+        ar = np.array(arena, dtype=np.uint8, copy=True)
+        pg = np.array(pages, dtype=PAGE_DTYPE, copy=True)
+        ptr = np.ascontiguousarray(page_ptr, dtype=np.int32)
+        ids = np.ascontiguousarray(page_ids, dtype=np.int32)
+        kn, vn = np.ascontiguousarray(k_new), np.ascontiguousarray(v_new)
+        flags = ctypes.c_uint32(0)
+        st = self.lib.orc_paged_append(_ptr(ar), ar.nbytes, _ptr(pg), len(pg), _ptr(ptr), _ptr(ids),
+                                       len(ids), _ptr(kn), _ptr(vn), new_type, len(ptr) - 1,
+                                       head_dim, ctypes.byref(flags))
+        if st != OK:
+            raise OracleError(f"orc_paged_append status {st}")
+        return ar, pg, flags.value
 
 
 _default: Oracle | None = None

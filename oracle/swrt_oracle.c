@@ -530,11 +530,11 @@ static int32_t xf_quantize(float y, float scale, int32_t zero_point, int32_t lo,
     return (int32_t)q;
 }
 
-static void xf_store(const orc_row_xf *x, int t, char *row, int64_t i, float y)
+/* element i of a dense f32 / f16 / bf16 row */
+static void store_dense(int type, char *row, int64_t i, float y)
 {
     uint16_t h;
-    int32_t lo, hi, q;
-    switch (x->out_type) {
+    switch (type) {
     case ORC_XF_F32:
         if (isnan(y)) {
             const uint32_t canonical = 0x7FC00000u; /* sign and payload are not fixed */
@@ -547,9 +547,21 @@ static void xf_store(const orc_row_xf *x, int t, char *row, int64_t i, float y)
         h = float_to_f16_bits(y);
         memcpy(row + 2 * i, &h, 2);
         break;
-    case ORC_XF_BF16:
+    default: /* ORC_XF_BF16 */
         h = float_to_bf16_bits(y);
         memcpy(row + 2 * i, &h, 2);
+        break;
+    }
+}
+
+static void xf_store(const orc_row_xf *x, int t, char *row, int64_t i, float y)
+{
+    int32_t lo, hi, q;
+    switch (x->out_type) {
+    case ORC_XF_F32:
+    case ORC_XF_F16:
+    case ORC_XF_BF16:
+        store_dense(x->out_type, row, i, y);
         break;
     default: /* ORC_XF_INT8, ORC_XF_UINT8 */
         xf_code_range(x->out_type, &lo, &hi);
@@ -812,5 +824,400 @@ int orc_window_attention(const void *q, const void *k_cache, const void *v_cache
     }
     free(s);
     free(acc);
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* [PF-PAGED] paged caches with per-page formats                              */
+/* ------------------------------------------------------------------------ */
+
+static int pg_bits(int fmt)
+{
+    switch (fmt) {
+    case ORC_XF_F32: return 32;
+    case ORC_XF_F16:
+    case ORC_XF_BF16: return 16;
+    case ORC_XF_INT8:
+    case ORC_XF_UINT8: return 8;
+    case ORC_XF_INT4:
+    case ORC_XF_UINT4: return 4;
+    case ORC_XF_INT2:
+    case ORC_XF_UINT2: return 2;
+    default: return 0;
+    }
+}
+
+/* the code range of an affine format; 0 for a dense one */
+static int pg_code_range(int fmt, int32_t *lo, int32_t *hi)
+{
+    switch (fmt) {
+    case ORC_XF_INT8: *lo = -128; *hi = 127; return 1;
+    case ORC_XF_UINT8: *lo = 0; *hi = 255; return 1;
+    case ORC_XF_INT4: *lo = -8; *hi = 7; return 1;
+    case ORC_XF_UINT4: *lo = 0; *hi = 15; return 1;
+    case ORC_XF_INT2: *lo = -2; *hi = 1; return 1;
+    case ORC_XF_UINT2: *lo = 0; *hi = 3; return 1;
+    default: return 0;
+    }
+}
+
+/* bytes of one row, or -1 when the format is unknown or the row is not whole bytes */
+static int64_t pg_row_bytes(int fmt, int64_t head_dim)
+{
+    const int bits = pg_bits(fmt);
+    if (bits == 0 || (head_dim * bits) % 8 != 0)
+        return -1;
+    return head_dim * bits / 8;
+}
+
+/* a format with its parameters: an affine one needs a positive finite scale and
+ * a zero point inside its code range */
+static int pg_format_ok(int fmt, float scale, int32_t zero_point, int64_t head_dim)
+{
+    int32_t lo, hi;
+    if (pg_row_bytes(fmt, head_dim) < 0)
+        return 0;
+    if (pg_code_range(fmt, &lo, &hi))
+        return scale > 0.0f && !isinf(scale) && zero_point >= lo && zero_point <= hi;
+    return 1;
+}
+
+/* [offset, offset + bytes) inside [0, arena_bytes) */
+static int pg_inside(int64_t offset, int64_t bytes, int64_t arena_bytes)
+{
+    return offset >= 0 && bytes >= 0 && offset <= arena_bytes && bytes <= arena_bytes - offset;
+}
+
+static int pg_page_ok(const orc_page *p, int64_t head_dim, int64_t arena_bytes)
+{
+    if (p->start < 0 || p->capacity < 1 || p->length < 1 || p->length > p->capacity)
+        return 0;
+    if (!pg_format_ok(p->k_format, p->k_scale, p->k_zero_point, head_dim) ||
+        !pg_format_ok(p->v_format, p->v_scale, p->v_zero_point, head_dim))
+        return 0;
+    if (p->start > INT64_MAX - p->length)
+        return 0;
+    return pg_inside(p->k_offset, p->capacity * pg_row_bytes(p->k_format, head_dim), arena_bytes) &&
+           pg_inside(p->v_offset, p->capacity * pg_row_bytes(p->v_format, head_dim), arena_bytes);
+}
+
+/* code e of an affine row: bits e*b .. e*b + b - 1 counted from the least
+ * significant bit of byte 0; signed formats in two's complement */
+static int32_t pg_get_code(int fmt, const char *row, int64_t e)
+{
+    const int bits = pg_bits(fmt);
+    const int64_t bit = e * bits;
+    const unsigned byte = (unsigned char)row[bit / 8];
+    const unsigned raw = (byte >> (bit % 8)) & ((1u << bits) - 1u);
+    const int is_signed = fmt == ORC_XF_INT8 || fmt == ORC_XF_INT4 || fmt == ORC_XF_INT2;
+    if (is_signed && (raw >> (bits - 1)))
+        return (int32_t)raw - (int32_t)(1u << bits);
+    return (int32_t)raw;
+}
+
+static void pg_put_code(int fmt, char *row, int64_t e, int32_t code)
+{
+    const int bits = pg_bits(fmt);
+    const int64_t bit = e * bits;
+    const unsigned mask = ((1u << bits) - 1u) << (bit % 8);
+    unsigned byte = (unsigned char)row[bit / 8];
+    byte = (byte & ~mask) | (((unsigned)code << (bit % 8)) & mask);
+    row[bit / 8] = (char)byte;
+}
+
+/* element e as a float64 value (exact: a dense element, or (c - zp) * scale
+ * with a small integer and a binary32 scale) */
+static double pg_value64(int fmt, float scale, int32_t zero_point, const char *row, int64_t e)
+{
+    int32_t lo, hi;
+    if (pg_code_range(fmt, &lo, &hi))
+        return (double)(pg_get_code(fmt, row, e) - zero_point) * (double)scale;
+    return (double)xf_load(fmt, row, e);
+}
+
+/* element e decoded in binary32: a dense element as is, an affine one as
+ * fl((c - zp) * scale), one rounding */
+static float pg_value32(int fmt, float scale, int32_t zero_point, const char *row, int64_t e)
+{
+    int32_t lo, hi;
+    if (pg_code_range(fmt, &lo, &hi))
+        return (float)(pg_get_code(fmt, row, e) - zero_point) * scale;
+    return xf_load(fmt, row, e);
+}
+
+/* element e written in a target format */
+static void pg_store(int fmt, float scale, int32_t zero_point, char *row, int64_t e, float y)
+{
+    int32_t lo, hi;
+    if (pg_code_range(fmt, &lo, &hi))
+        pg_put_code(fmt, row, e, xf_quantize(y, scale, zero_point, lo, hi));
+    else
+        store_dense(fmt, row, e, y);
+}
+
+int orc_paged_attention(const void *q, int q_type, const char *arena, int64_t arena_bytes,
+                        const orc_page *pages, int64_t n_pages, const int32_t *page_ptr,
+                        const int32_t *page_ids, int64_t n_ids, double *out,
+                        int64_t left_window, int64_t batch, int64_t q_heads,
+                        int64_t kv_heads, int64_t head_dim, double scale, uint32_t *flags)
+{
+    const int64_t B = batch, Hq = q_heads, Hkv = kv_heads, D = head_dim;
+    int64_t group, qes;
+    double *acc;
+    int64_t *visit;
+
+    if (B < 0 || Hq < 0 || Hkv < 1 || D < 0 || n_pages < 0 || n_ids < 0 || arena_bytes < 0)
+        return ORC_E_INVALID_ARG;
+    if (!xf_float_type(q_type) || Hq % Hkv != 0)
+        return ORC_E_INVALID_ARG;
+    if (B == 0 || Hq == 0 || D == 0)
+        return ORC_OK;
+    if (!q || !out || !page_ptr || (n_pages > 0 && !pages) || (n_ids > 0 && !page_ids) ||
+        (arena_bytes > 0 && !arena))
+        return ORC_E_INVALID_ARG;
+    qes = xf_elem_bytes(q_type);
+    group = Hq / Hkv;
+    acc = (double *)malloc((size_t)D * sizeof(double));
+    visit = (int64_t *)malloc((size_t)(n_ids > 0 ? n_ids : 1) * sizeof(int64_t));
+    if (!acc || !visit) {
+        free(acc);
+        free(visit);
+        return ORC_E_INVALID_ARG;
+    }
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t g = 0; g < Hkv; ++g) {
+            const int64_t st = b * Hkv + g;
+            const int64_t p0 = page_ptr[st], p1 = page_ptr[st + 1];
+            int64_t T = 0, r0 = 0, nv = 0, ok = 1;
+            /* the stream's pages the window reaches, walked back from the last:
+             * each must be valid and end where the next one starts */
+            if (p0 < 0 || p1 < p0 || p1 > n_ids)
+                ok = 0;
+            if (ok && p1 > p0) {
+                int64_t end = -1;
+                for (int64_t k = p1 - 1; k >= p0 && ok; --k) {
+                    const int64_t id = page_ids[k];
+                    const orc_page *p;
+                    if (id < 0 || id >= n_pages || !pg_page_ok(&pages[id], D, arena_bytes)) {
+                        ok = 0;
+                        break;
+                    }
+                    p = &pages[id];
+                    if (end < 0) { /* the last page fixes T and the window */
+                        T = p->start + p->length;
+                        r0 = left_window < 0 ? 0 : (T - 1 - left_window > 0 ? T - 1 - left_window : 0);
+                    } else if (p->start + p->length != end) {
+                        ok = 0;
+                        break;
+                    }
+                    if (k == p0 && p->start != 0) { /* starts run from zero */
+                        ok = 0;
+                        break;
+                    }
+                    visit[nv++] = id;
+                    end = p->start;
+                    if (p->start <= r0)
+                        break; /* earlier pages end before the window */
+                }
+            }
+            if (!ok) {
+                set_flag(flags, ORC_FLAG_BAD_PAGES);
+                continue;
+            }
+            for (int64_t j = 0; j < group; ++j) {
+                const int64_t h = g * group + j;
+                const char *qrow = (const char *)q + (b * Hq + h) * D * qes;
+                double m = -INFINITY, denom = 0.0;
+                for (int64_t d = 0; d < D; ++d)
+                    acc[d] = 0.0;
+                /* two passes over the visible tokens in order: the maximum score,
+                 * then weights and the weighted values */
+                for (int pass = 0; pass < 2; ++pass) {
+                    for (int64_t v = nv - 1; v >= 0; --v) {
+                        const orc_page *p = &pages[visit[v]];
+                        const int64_t kr = pg_row_bytes(p->k_format, D);
+                        const int64_t vr = pg_row_bytes(p->v_format, D);
+                        for (int64_t i = 0; i < p->length; ++i) {
+                            const char *krow, *vrow;
+                            double dot = 0.0, sc;
+                            if (p->start + i < r0)
+                                continue;
+                            krow = arena + p->k_offset + i * kr;
+                            vrow = arena + p->v_offset + i * vr;
+                            for (int64_t d = 0; d < D; ++d)
+                                dot += (double)xf_load(q_type, qrow, d) *
+                                       pg_value64(p->k_format, p->k_scale, p->k_zero_point, krow, d);
+                            sc = scale * dot;
+                            if (pass == 0) {
+                                if (sc > m)
+                                    m = sc;
+                            } else {
+                                const double w = exp(sc - m);
+                                denom += w;
+                                for (int64_t d = 0; d < D; ++d)
+                                    acc[d] += w * pg_value64(p->v_format, p->v_scale,
+                                                             p->v_zero_point, vrow, d);
+                            }
+                        }
+                    }
+                }
+                for (int64_t d = 0; d < D; ++d)
+                    out[(b * Hq + h) * D + d] = denom > 0.0 ? acc[d] / denom : 0.0;
+            }
+        }
+    }
+    free(acc);
+    free(visit);
+    return ORC_OK;
+}
+
+/* [a0, a0 + n0) and [a1, a1 + n1) share a byte */
+static int pg_overlap(int64_t a0, int64_t n0, int64_t a1, int64_t n1)
+{
+    return n0 > 0 && n1 > 0 && a0 < a1 + n1 && a1 < a0 + n0;
+}
+
+int orc_paged_quantize(const char *arena_in, int64_t arena_in_bytes, const orc_page *pages_in,
+                       int64_t n_pages, const int32_t *blocks, int64_t n_blocks,
+                       const int64_t *dst_offsets, char *arena_out, int64_t arena_out_bytes,
+                       orc_page *pages_out, int k_format, float k_scale, int32_t k_zero_point,
+                       int v_format, float v_scale, int32_t v_zero_point, int64_t head_dim)
+{
+    const int64_t D = head_dim;
+    const int fmt[2] = {k_format, v_format};
+    int32_t lo, hi;
+    float sc[2] = {k_scale, v_scale};
+    int32_t zp[2] = {k_zero_point, v_zero_point};
+
+    /* every check before anything is written */
+    if (n_pages < 0 || n_blocks < 0 || D < 1 || arena_in_bytes < 0 || arena_out_bytes < 0)
+        return ORC_E_INVALID_ARG;
+    if ((n_pages > 0 && (!pages_in || !pages_out)) ||
+        (n_blocks > 0 && (!blocks || !dst_offsets || !arena_out)) ||
+        (arena_in_bytes > 0 && !arena_in))
+        return ORC_E_INVALID_ARG;
+    for (int t = 0; t < 2; ++t) {
+        if (!pg_format_ok(fmt[t], sc[t], zp[t], D))
+            return ORC_E_INVALID_ARG;
+        if (!pg_code_range(fmt[t], &lo, &hi)) { /* a dense target has no parameters */
+            sc[t] = 1.0f;
+            zp[t] = 0;
+        }
+    }
+    for (int64_t i = 0; i < n_pages; ++i)
+        if (!pg_page_ok(&pages_in[i], D, arena_in_bytes))
+            return ORC_E_INVALID_ARG;
+    for (int64_t i = 0; i < n_blocks; ++i) {
+        const int64_t id = blocks[i];
+        if (id < 0 || id >= n_pages)
+            return ORC_E_INVALID_ARG;
+        for (int64_t j = 0; j < i; ++j)
+            if (blocks[j] == blocks[i])
+                return ORC_E_INVALID_ARG;
+        for (int t = 0; t < 2; ++t) {
+            const int64_t bytes = pages_in[id].capacity * pg_row_bytes(fmt[t], D);
+            const int64_t dst = dst_offsets[2 * i + t];
+            if (!pg_inside(dst, bytes, arena_out_bytes))
+                return ORC_E_INVALID_ARG;
+            /* destinations are fresh: no other destination and, in the same
+             * arena, no page's payload */
+            for (int64_t j = 0; j <= i; ++j)
+                for (int u = 0; u < 2; ++u) {
+                    if (j == i && u >= t)
+                        continue;
+                    if (pg_overlap(dst, bytes, dst_offsets[2 * j + u],
+                                   pages_in[blocks[j]].capacity * pg_row_bytes(fmt[u], D)))
+                        return ORC_E_INVALID_ARG;
+                }
+            if (arena_out == arena_in)
+                for (int64_t k = 0; k < n_pages; ++k) {
+                    const orc_page *p = &pages_in[k];
+                    if (pg_overlap(dst, bytes, p->k_offset, p->capacity * pg_row_bytes(p->k_format, D)) ||
+                        pg_overlap(dst, bytes, p->v_offset, p->capacity * pg_row_bytes(p->v_format, D)))
+                        return ORC_E_INVALID_ARG;
+                }
+        }
+    }
+    /* convert the selected pages */
+    for (int64_t i = 0; i < n_blocks; ++i) {
+        const orc_page *p = &pages_in[blocks[i]];
+        for (int t = 0; t < 2; ++t) {
+            const int sfmt = t ? p->v_format : p->k_format;
+            const float ss = t ? p->v_scale : p->k_scale;
+            const int32_t sz = t ? p->v_zero_point : p->k_zero_point;
+            const int64_t srb = pg_row_bytes(sfmt, D), drb = pg_row_bytes(fmt[t], D);
+            const char *src = arena_in + (t ? p->v_offset : p->k_offset);
+            char *dst = arena_out + dst_offsets[2 * i + t];
+            for (int64_t r = 0; r < p->capacity; ++r)
+                for (int64_t e = 0; e < D; ++e) {
+                    /* rows past the valid prefix are logical zeros, never read */
+                    const float y = r < p->length ? pg_value32(sfmt, ss, sz, src + r * srb, e) : 0.0f;
+                    pg_store(fmt[t], sc[t], zp[t], dst + r * drb, e, y);
+                }
+        }
+    }
+    /* publish: every descriptor, the selected ones with their new storage */
+    for (int64_t i = 0; i < n_pages; ++i)
+        if (pages_out != pages_in)
+            pages_out[i] = pages_in[i];
+    for (int64_t i = 0; i < n_blocks; ++i) {
+        orc_page *p = &pages_out[blocks[i]];
+        p->k_format = fmt[0];
+        p->v_format = fmt[1];
+        p->k_scale = sc[0];
+        p->v_scale = sc[1];
+        p->k_zero_point = zp[0];
+        p->v_zero_point = zp[1];
+        p->k_offset = dst_offsets[2 * i];
+        p->v_offset = dst_offsets[2 * i + 1];
+    }
+    return ORC_OK;
+}
+
+int orc_paged_append(char *arena, int64_t arena_bytes, orc_page *pages, int64_t n_pages,
+                     const int32_t *page_ptr, const int32_t *page_ids, int64_t n_ids,
+                     const void *k_new, const void *v_new, int new_type, int64_t n_streams,
+                     int64_t head_dim, uint32_t *flags)
+{
+    const int64_t D = head_dim;
+    int64_t nes;
+    if (n_streams < 0 || D < 1 || n_pages < 0 || n_ids < 0 || arena_bytes < 0 ||
+        !xf_float_type(new_type))
+        return ORC_E_INVALID_ARG;
+    if (n_streams == 0)
+        return ORC_OK;
+    if (!page_ptr || !k_new || !v_new || (n_pages > 0 && !pages) || (n_ids > 0 && !page_ids) ||
+        (arena_bytes > 0 && !arena))
+        return ORC_E_INVALID_ARG;
+    nes = xf_elem_bytes(new_type);
+    for (int64_t s = 0; s < n_streams; ++s) {
+        const int64_t p0 = page_ptr[s], p1 = page_ptr[s + 1];
+        int64_t id;
+        orc_page *p;
+        if (p0 < 0 || p1 <= p0 || p1 > n_ids) {
+            set_flag(flags, ORC_FLAG_BAD_PAGES);
+            continue;
+        }
+        id = page_ids[p1 - 1]; /* the stream's last page takes the token */
+        if (id < 0 || id >= n_pages || !pg_page_ok(&pages[id], D, arena_bytes)) {
+            set_flag(flags, ORC_FLAG_BAD_PAGES);
+            continue;
+        }
+        p = &pages[id];
+        if (p->length == p->capacity) {
+            set_flag(flags, ORC_FLAG_PAGE_FULL);
+            continue;
+        }
+        for (int t = 0; t < 2; ++t) {
+            const int fmt = t ? p->v_format : p->k_format;
+            const float sc = t ? p->v_scale : p->k_scale;
+            const int32_t zp = t ? p->v_zero_point : p->k_zero_point;
+            const char *in = (const char *)(t ? v_new : k_new) + s * D * nes;
+            char *row = arena + (t ? p->v_offset : p->k_offset) + p->length * pg_row_bytes(fmt, D);
+            for (int64_t e = 0; e < D; ++e)
+                pg_store(fmt, sc, zp, row, e, xf_load(new_type, in, e));
+        }
+        p->length += 1;
+    }
     return ORC_OK;
 }

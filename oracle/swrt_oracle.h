@@ -33,6 +33,13 @@
  *         "Serialized cache values"): affine INT8/UINT8 codes with FLOAT
  *         scales, scalar parameters on append, rounding ties to even and
  *         saturating to the code range.
+ *   [PF-PAGED] the same section as a whole: pages with start, length and
+ *         capacity, contiguous from zero; dense FLOAT/FLOAT16/BFLOAT16 or
+ *         affine INT8/UINT8/INT4/UINT4/INT2/UINT2 payloads, independently for
+ *         K and V and per page; QuantizePagedCache on selected blocks (valid
+ *         prefix converted, unused rows logical zeros, all checks before
+ *         anything is published); attention reading only visible tokens with
+ *         a left window bounding the preceding tokens.
  *
  * Every function is a plain definition: scalar loops, one memcpy per row, no
  * blocking, no vector code, no threads.
@@ -215,6 +222,104 @@ int orc_window_attention(const void *q, const void *k_cache, const void *v_cache
                          int64_t batch, int64_t q_heads, int64_t kv_heads,
                          int64_t capacity, int64_t head_dim, double scale, int elem_type,
                          uint32_t *flags);
+
+/* ------------------------------------------------------------------------ */
+/* paged caches with per-page formats                                         */
+/* ------------------------------------------------------------------------ */
+
+/* page formats beyond the row transform's: sub-byte affine codes */
+#define ORC_XF_INT4 6
+#define ORC_XF_UINT4 7
+#define ORC_XF_INT2 8
+#define ORC_XF_UINT2 9
+
+#define ORC_FLAG_BAD_PAGES 16u /* a page table or page descriptor failed its checks */
+#define ORC_FLAG_PAGE_FULL 32u /* an append found its page full; stream skipped      */
+
+/*
+ * [PF-PAGED] one page (block) of a paged cache: tokens [start, start + length)
+ * of one stream (batch entry, KV head), capacity physical rows of head_dim
+ * elements for K and for V at byte offsets of an arena. Dense formats
+ * (ORC_XF_F32 / F16 / BF16) hold values; affine formats (INT8, UINT8, INT4,
+ * UINT4, INT2, UINT2) hold codes c with value (c - zero_point) * scale. A row
+ * of a b-bit format is head_dim * b / 8 bytes; sub-byte codes pack from the
+ * least significant bits of each byte (element 0 in the low bits), signed
+ * codes in two's complement. The layout is the GPU library's page descriptor
+ * (64 bytes), defined here on its own.
+ */
+typedef struct {
+    int64_t start;
+    int32_t length;
+    int32_t capacity;
+    int64_t k_offset;
+    int64_t v_offset;
+    int32_t k_format;
+    int32_t v_format;
+    float k_scale;
+    float v_scale;
+    int32_t k_zero_point;
+    int32_t v_zero_point;
+    int32_t reserved[2];
+} orc_page;
+
+/*
+ * [PF-PAGED] + [ATT]: one-token decode attention over paged caches. Stream
+ * s = b * kv_heads + g owns pages page_ids[page_ptr[s] .. page_ptr[s+1]) in
+ * token order; its length T is the last page's start + length (0 without
+ * pages). Query head h of entry b reads stream b * kv_heads + h / (Hq / Hkv)
+ * over tokens [max(0, T - 1 - left_window), T) (left_window < 0: all T; the
+ * query is token T - 1 and left_window bounds the tokens before it), in
+ * float64 from the exactly decoded values:
+ *   o = sum_r exp(s_r - max s) v_r / sum_r exp(s_r - max s),  s_r = scale q.k_r
+ * q [B, Hq, D] of q_type (F32 / F16 / BF16); out [B, Hq, D] float64.
+ * The pages the window reaches must be contiguous (each start the previous
+ * start + length), 1 <= length <= capacity, of valid formats and parameters
+ * (scale > 0 and finite, zero point in the code range) and inside the arena;
+ * page ids must be in [0, n_pages) and the stream's range of page_ids inside
+ * [0, n_ids). A stream that fails is flagged BAD_PAGES and the outputs of its
+ * query heads are left as they were; pages before the window are not read.
+ * An empty window gives zeros.
+ */
+int orc_paged_attention(const void *q, int q_type, const char *arena, int64_t arena_bytes,
+                        const orc_page *pages, int64_t n_pages, const int32_t *page_ptr,
+                        const int32_t *page_ids, int64_t n_ids, double *out,
+                        int64_t left_window, int64_t batch, int64_t q_heads,
+                        int64_t kv_heads, int64_t head_dim, double scale, uint32_t *flags);
+
+/*
+ * [PF-PAGED] selected-block conversion: each page pages_in[blocks[i]] is
+ * decoded (dense: its value; affine: fl((c - zero_point) * scale) in binary32)
+ * and its valid rows written in the target formats to arena_out at
+ * dst_offsets[2 i] (K) and dst_offsets[2 i + 1] (V): F32 as is (NaN
+ * canonical), F16 / BF16 rounded to nearest even (NaN canonical), affine
+ * formats as saturate(round_half_even(fl(y / scale)) + zero_point) (NaN ->
+ * zero point), packed. Rows [length, capacity) are written as logical zeros
+ * of the target (0.0, or the zero point's code) without reading the source.
+ * pages_out is pages_in with the selected descriptors' formats, parameters
+ * and offsets replaced; a dense target's scale is 1 and zero point 0.
+ * Everything is checked first (every page of pages_in, the indices: unique,
+ * in [0, n_pages); the targets; the destinations inside arena_out and not
+ * overlapping each other): on any failure nothing is written and the call
+ * returns ORC_E_INVALID_ARG.
+ */
+int orc_paged_quantize(const char *arena_in, int64_t arena_in_bytes, const orc_page *pages_in,
+                       int64_t n_pages, const int32_t *blocks, int64_t n_blocks,
+                       const int64_t *dst_offsets, char *arena_out, int64_t arena_out_bytes,
+                       orc_page *pages_out, int k_format, float k_scale, int32_t k_zero_point,
+                       int v_format, float v_scale, int32_t v_zero_point, int64_t head_dim);
+
+/*
+ * [PF-PAGED] decode append: stream s writes its new K and V rows (new_type
+ * F32 / F16 / BF16, [n_streams, head_dim]) as row `length` of its last page,
+ * encoded in that page's formats as orc_paged_quantize encodes, and the
+ * page's length grows by one. A stream without pages, or whose last page is
+ * invalid, is flagged BAD_PAGES; one whose last page is full, PAGE_FULL;
+ * either is skipped.
+ */
+int orc_paged_append(char *arena, int64_t arena_bytes, orc_page *pages, int64_t n_pages,
+                     const int32_t *page_ptr, const int32_t *page_ids, int64_t n_ids,
+                     const void *k_new, const void *v_new, int new_type, int64_t n_streams,
+                     int64_t head_dim, uint32_t *flags);
 
 #ifdef __cplusplus
 }

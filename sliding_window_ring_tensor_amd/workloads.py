@@ -286,3 +286,107 @@ def stratified_seqlens(g: np.random.Generator, batch: int, capacity: int, seq_le
     sk = np.concatenate([lo_part, hi_part])
     g.shuffle(sk)
     return sk.astype(np.int32)
+
+
+# ---------------------------------------------------------------------------
+# paged caches
+# ---------------------------------------------------------------------------
+# bits per element of each page format, by its C-ABI value (layout only: what a
+# page occupies; the formats' arithmetic lives in the kernels and the oracle)
+FORMAT_BITS = {1: 32, 2: 16, 3: 16, 4: 8, 5: 8, 6: 4, 7: 4, 8: 2, 9: 2}
+_DENSE = {1: torch.float32, 2: torch.float16, 3: torch.bfloat16}
+PAGE_FIELDS = ("start", "length", "capacity", "k_offset", "v_offset", "k_format", "v_format",
+               "k_scale", "v_scale", "k_zero_point", "v_zero_point")
+
+
+@dataclass
+class PagedCase:
+    """Streams of pages in one arena: descriptor fields as arrays (one entry per
+    page, in arena order), each stream's page ids in token order (CSR), and the
+    arena bytes."""
+    head_dim: int
+    fields: dict
+    page_ptr: np.ndarray
+    page_ids: np.ndarray
+    arena: np.ndarray
+    free_offset: int  # first byte past every page payload (spare room follows)
+
+    @property
+    def n_pages(self) -> int:
+        return len(self.fields["start"])
+
+    def totals(self) -> np.ndarray:
+        """Tokens per stream (the sum of its pages' lengths)."""
+        out = np.zeros(len(self.page_ptr) - 1, np.int64)
+        for s in range(len(out)):
+            ids = self.page_ids[self.page_ptr[s]:self.page_ptr[s + 1]]
+            out[s] = int(self.fields["length"][ids].sum())
+        return out
+
+
+def paged_case(g: np.random.Generator, head_dim: int, streams, page_format, *,
+               spare_bytes: int = 0, align: int = 16) -> PagedCase:
+    """A paged cache: ``streams`` lists, per stream, its pages as (length,
+    capacity) in token order; ``page_format(stream, page, n_pages)`` gives a
+    page's (k_format, v_format, k_scale, v_scale, k_zero_point, v_zero_point).
+    Pages sit in the arena in a shuffled order at ``align``-byte offsets; dense
+    payloads hold U[-1, 1) values rounded to their type, affine payloads
+    uniform random bytes (every row of the capacity is filled, valid or not)."""
+    recs = []
+    for s, pages in enumerate(streams):
+        start = 0
+        for i, (length, cap) in enumerate(pages):
+            kf, vf, ks, vs, kz, vz = page_format(s, i, len(pages))
+            recs.append(dict(stream=s, index=i, start=start, length=length, capacity=cap,
+                             k_format=kf, v_format=vf, k_scale=ks, v_scale=vs,
+                             k_zero_point=kz, v_zero_point=vz))
+            start += length
+    order = g.permutation(len(recs))
+    off = 0
+    chunks = []
+
+    def place(fmt, cap):
+        nonlocal off
+        nbytes = cap * head_dim * FORMAT_BITS[fmt] // 8
+        o = off
+        if fmt in _DENSE:
+            vals = torch.from_numpy(g.uniform(-1, 1, size=cap * head_dim).astype(np.float32))
+            raw = vals.to(_DENSE[fmt]).view(torch.uint8).numpy()
+        else:
+            raw = g.integers(0, 256, size=nbytes, dtype=np.uint8)
+        chunks.append((o, raw))
+        off += -(-nbytes // align) * align
+        return o
+
+    for j in order:
+        r = recs[j]
+        r["k_offset"] = place(r["k_format"], r["capacity"])
+        r["v_offset"] = place(r["v_format"], r["capacity"])
+    arena = np.zeros(off + spare_bytes, np.uint8)
+    for o, raw in chunks:
+        arena[o:o + len(raw)] = raw
+    placed = [recs[j] for j in order]  # descriptor i is the i-th page in the arena
+    fields = {f: np.array([r[f] for r in placed],
+                          dtype=np.float32 if f.endswith("scale") else np.int64)
+              for f in PAGE_FIELDS}
+    ptr = np.zeros(len(streams) + 1, np.int32)
+    ids = []
+    for s, pages in enumerate(streams):
+        mine = sorted((r["index"], i) for i, r in enumerate(placed) if r["stream"] == s)
+        ids.extend(i for _, i in mine)
+        ptr[s + 1] = len(ids)
+    return PagedCase(head_dim, fields, ptr, np.array(ids, np.int32), arena, off)
+
+
+def page_split(g: np.random.Generator, tokens: int, capacity: int, sealed: float = 0.0):
+    """Pages of ``capacity`` rows holding ``tokens`` tokens in order: full pages,
+    except that with probability ``sealed`` a page is closed early (a sealed
+    partial page) and the last page holds the remainder."""
+    pages, left = [], tokens
+    while left > 0:
+        n = min(left, capacity)
+        if sealed and n > 1 and g.random() < sealed:
+            n = int(g.integers(1, n))
+        pages.append((n, capacity))
+        left -= n
+    return pages

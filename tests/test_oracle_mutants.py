@@ -3,8 +3,8 @@
 Each mutant below is a copy of oracle/swrt_oracle.c with one planted mistake
 (an index off by one, a dropped term, a wrong sign, a transposed operand, a
 step done in the wrong order, a check weakened). The mutant is compiled with
-gcc and the whole pin suite (tests/test_oracle_pins.py, test_oracle_xf_pins.py
-and test_oracle_att_pins.py) runs against it in its
+gcc and the whole pin suite (tests/test_oracle_pins.py, test_oracle_xf_pins.py,
+test_oracle_att_pins.py and test_oracle_paged_pins.py) runs against it in its
 own process; the suite must fail for every mutant. A mutant that crashes its
 process counts as caught. Everything runs on the CPU.
 """
@@ -130,6 +130,27 @@ MUTANTS = {
     "att_query_of_kv_head": ("(const char *)q + (b * Hq + h) * D * es", "(const char *)q + (b * Hq + g) * D * es"),
     "att_not_normalised": ("L > r0 ? acc[d] / denom : 0.0", "L > r0 ? acc[d] : 0.0"),
     "bf16_decode_shift": ("uint32_t u = (uint32_t)h << 16;", "uint32_t u = (uint32_t)h << 15;"),
+    # paged caches
+    "paged_window_one_short": ("T - 1 - left_window > 0 ? T - 1 - left_window : 0",
+                               "T - left_window > 0 ? T - left_window : 0"),
+    "paged_zero_point_kept": ("return (double)(pg_get_code(fmt, row, e) - zero_point) * (double)scale;",
+                              "return (double)pg_get_code(fmt, row, e) * (double)scale;"),
+    "paged_codes_high_bits_first": ("const unsigned raw = (byte >> (bit % 8))",
+                                    "const unsigned raw = (byte >> ((8 - bits - bit % 8) & 7))"),
+    "paged_codes_unsigned": ("if (is_signed && (raw >> (bits - 1)))", "if (0 && is_signed)"),
+    "paged_unused_rows_read": ("const float y = r < p->length ? pg_value32(sfmt, ss, sz, src + r * srb, e) : 0.0f;",
+                               "const float y = pg_value32(sfmt, ss, sz, src + r * srb, e);"),
+    "paged_contiguity_unchecked": ("} else if (p->start + p->length != end) {", "} else if (0) {"),
+    "paged_reads_before_window": ("if (p->start <= r0)\n                        break;",
+                                  "if (p->start <= r0)\n                        (void)0;"),
+    "paged_append_overwrites": ("(t ? p->v_offset : p->k_offset) + p->length * pg_row_bytes(fmt, D);",
+                                "(t ? p->v_offset : p->k_offset) + (p->length - 1) * pg_row_bytes(fmt, D);"),
+    "paged_append_length_kept": ("        p->length += 1;\n", "        (void)0;\n"),
+    "paged_dense_target_keeps_parameters": ("            sc[t] = 1.0f;\n            zp[t] = 0;\n", ""),
+    "paged_live_payload_overwritable": ("if (arena_out == arena_in)\n", "if (0)\n"),
+    "paged_duplicates_accepted": ("if (blocks[j] == blocks[i])", "if (0)"),
+    "paged_heads_interleaved": ("const int64_t h = g * group + j;", "const int64_t h = j * Hkv + g;"),
+    "paged_scale_dropped": ("sc = scale * dot;", "sc = dot;"),
 }
 
 # write before shift (the opposite of the order the step formulas list)
@@ -162,7 +183,8 @@ def _run_pins(lib: str) -> subprocess.CompletedProcess:
     return subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                            os.path.join(ROOT, "tests", "test_oracle_pins.py"),
                            os.path.join(ROOT, "tests", "test_oracle_xf_pins.py"),
-                           os.path.join(ROOT, "tests", "test_oracle_att_pins.py")],
+                           os.path.join(ROOT, "tests", "test_oracle_att_pins.py"),
+                           os.path.join(ROOT, "tests", "test_oracle_paged_pins.py")],
                           cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
 
 
@@ -178,7 +200,7 @@ def test_every_mutant_fails_the_pins(tmp_path):
                         f"-I{os.path.dirname(oracle.SOURCE)}", str(path), "-o", lib, "-lm"],
                        check=True, capture_output=True)
         builds[name] = lib
-    with ThreadPoolExecutor(max_workers=4) as ex:
+    with ThreadPoolExecutor(max_workers=max(2, min(8, os.cpu_count() or 2))) as ex:
         results = dict(zip(builds, ex.map(_run_pins, builds.values())))
     survivors = [n for n, r in results.items() if r.returncode == 0]
     assert not survivors, f"mutants not caught by the pins: {survivors}"
