@@ -151,7 +151,7 @@ class Oracle:
         lib.orc_paged_attention.argtypes = [vp, i32, vp, i64, vp, i64, vp, vp, i64, vp, i64, i64,
                                             i64, i64, i64, ctypes.c_double, u32p]
         lib.orc_paged_attention.restype = ctypes.c_int
-        lib.orc_paged_quantize.argtypes = [vp, i64, vp, i64, vp, i64, vp, vp, i64, vp, i32, f32,
+        lib.orc_paged_quantize.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, i64, vp, i32, f32,
                                            ctypes.c_int32, i32, f32, ctypes.c_int32, i64]
         lib.orc_paged_quantize.restype = ctypes.c_int
         lib.orc_paged_append.argtypes = [vp, i64, vp, i64, vp, vp, i64, vp, vp, i32, i64, i64, u32p]
@@ -359,23 +359,20 @@ class Oracle:
             raise OracleError(f"orc_paged_attention status {st}")
         return out, flags.value
 
-    def paged_quantize(self, arena, pages, blocks, dst_offsets, k_format: int, k_scale: float,
-                       k_zero_point: int, v_format: int, v_scale: float, v_zero_point: int,
-                       head_dim: int, arena_out=None):
-        """QuantizePagedCache on copies: returns (status, arena_out, pages_out).
-        Without ``arena_out`` the destinations lie in (a copy of) the same arena."""
+    def paged_quantize(self, arena, pages, blocks, dst_offsets, free_begin: int, free_end: int,
+                       k_format: int, k_scale: float, k_zero_point: int, v_format: int,
+                       v_scale: float, v_zero_point: int, head_dim: int):
+        """QuantizePagedCache on copies: returns (status, arena, pages_out)."""
         ar = np.array(arena, dtype=np.uint8, copy=True)
-        same = arena_out is None
-        out_ar = ar if same else np.array(arena_out, dtype=np.uint8, copy=True)
         pg = np.ascontiguousarray(pages, dtype=PAGE_DTYPE)
         pout = pg.copy()
         bl = np.ascontiguousarray(blocks, dtype=np.int32)
         dst = np.ascontiguousarray(dst_offsets, dtype=np.int64)
         st = self.lib.orc_paged_quantize(_ptr(ar), ar.nbytes, _ptr(pg), len(pg), _ptr(bl), len(bl),
-                                         _ptr(dst), _ptr(out_ar), out_ar.nbytes, _ptr(pout),
-                                         k_format, k_scale, k_zero_point, v_format, v_scale,
-                                         v_zero_point, head_dim)
-        return st, out_ar, pout
+                                         _ptr(dst), free_begin, free_end, _ptr(pout), k_format,
+                                         k_scale, k_zero_point, v_format, v_scale, v_zero_point,
+                                         head_dim)
+        return st, ar, pout
 
     def paged_append(self, arena, pages, page_ptr, page_ids, k_new, v_new, new_type: int,
                      head_dim: int):

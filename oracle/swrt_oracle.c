@@ -1077,9 +1077,9 @@ static int pg_overlap(int64_t a0, int64_t n0, int64_t a1, int64_t n1)
     return n0 > 0 && n1 > 0 && a0 < a1 + n1 && a1 < a0 + n0;
 }
 
-int orc_paged_quantize(const char *arena_in, int64_t arena_in_bytes, const orc_page *pages_in,
+int orc_paged_quantize(char *arena, int64_t arena_bytes, const orc_page *pages_in,
                        int64_t n_pages, const int32_t *blocks, int64_t n_blocks,
-                       const int64_t *dst_offsets, char *arena_out, int64_t arena_out_bytes,
+                       const int64_t *dst_offsets, int64_t free_begin, int64_t free_end,
                        orc_page *pages_out, int k_format, float k_scale, int32_t k_zero_point,
                        int v_format, float v_scale, int32_t v_zero_point, int64_t head_dim)
 {
@@ -1088,13 +1088,15 @@ int orc_paged_quantize(const char *arena_in, int64_t arena_in_bytes, const orc_p
     int32_t lo, hi;
     float sc[2] = {k_scale, v_scale};
     int32_t zp[2] = {k_zero_point, v_zero_point};
+    int64_t next = free_begin; /* where the next destination may start */
 
     /* every check before anything is written */
-    if (n_pages < 0 || n_blocks < 0 || D < 1 || arena_in_bytes < 0 || arena_out_bytes < 0)
+    if (n_pages < 0 || n_blocks < 0 || D < 1 || arena_bytes < 0)
         return ORC_E_INVALID_ARG;
-    if ((n_pages > 0 && (!pages_in || !pages_out)) ||
-        (n_blocks > 0 && (!blocks || !dst_offsets || !arena_out)) ||
-        (arena_in_bytes > 0 && !arena_in))
+    if ((n_pages > 0 && (!pages_in || !pages_out)) || (n_blocks > 0 && (!blocks || !dst_offsets)) ||
+        (arena_bytes > 0 && !arena))
+        return ORC_E_INVALID_ARG;
+    if (free_begin < 0 || free_end < free_begin || free_end > arena_bytes)
         return ORC_E_INVALID_ARG;
     for (int t = 0; t < 2; ++t) {
         if (!pg_format_ok(fmt[t], sc[t], zp[t], D))
@@ -1104,38 +1106,26 @@ int orc_paged_quantize(const char *arena_in, int64_t arena_in_bytes, const orc_p
             zp[t] = 0;
         }
     }
-    for (int64_t i = 0; i < n_pages; ++i)
-        if (!pg_page_ok(&pages_in[i], D, arena_in_bytes))
+    for (int64_t i = 0; i < n_pages; ++i) {
+        const orc_page *p = &pages_in[i];
+        if (!pg_page_ok(p, D, arena_bytes))
             return ORC_E_INVALID_ARG;
+        if (pg_overlap(free_begin, free_end - free_begin, p->k_offset,
+                       p->capacity * pg_row_bytes(p->k_format, D)) ||
+            pg_overlap(free_begin, free_end - free_begin, p->v_offset,
+                       p->capacity * pg_row_bytes(p->v_format, D)))
+            return ORC_E_INVALID_ARG; /* the free region holds no live payload */
+    }
     for (int64_t i = 0; i < n_blocks; ++i) {
         const int64_t id = blocks[i];
-        if (id < 0 || id >= n_pages)
+        if (id < 0 || id >= n_pages || (i > 0 && id <= blocks[i - 1]))
             return ORC_E_INVALID_ARG;
-        for (int64_t j = 0; j < i; ++j)
-            if (blocks[j] == blocks[i])
-                return ORC_E_INVALID_ARG;
         for (int t = 0; t < 2; ++t) {
             const int64_t bytes = pages_in[id].capacity * pg_row_bytes(fmt[t], D);
             const int64_t dst = dst_offsets[2 * i + t];
-            if (!pg_inside(dst, bytes, arena_out_bytes))
+            if (dst < next || bytes > free_end - dst)
                 return ORC_E_INVALID_ARG;
-            /* destinations are fresh: no other destination and, in the same
-             * arena, no page's payload */
-            for (int64_t j = 0; j <= i; ++j)
-                for (int u = 0; u < 2; ++u) {
-                    if (j == i && u >= t)
-                        continue;
-                    if (pg_overlap(dst, bytes, dst_offsets[2 * j + u],
-                                   pages_in[blocks[j]].capacity * pg_row_bytes(fmt[u], D)))
-                        return ORC_E_INVALID_ARG;
-                }
-            if (arena_out == arena_in)
-                for (int64_t k = 0; k < n_pages; ++k) {
-                    const orc_page *p = &pages_in[k];
-                    if (pg_overlap(dst, bytes, p->k_offset, p->capacity * pg_row_bytes(p->k_format, D)) ||
-                        pg_overlap(dst, bytes, p->v_offset, p->capacity * pg_row_bytes(p->v_format, D)))
-                        return ORC_E_INVALID_ARG;
-                }
+            next = dst + bytes;
         }
     }
     /* convert the selected pages */
@@ -1146,8 +1136,8 @@ int orc_paged_quantize(const char *arena_in, int64_t arena_in_bytes, const orc_p
             const float ss = t ? p->v_scale : p->k_scale;
             const int32_t sz = t ? p->v_zero_point : p->k_zero_point;
             const int64_t srb = pg_row_bytes(sfmt, D), drb = pg_row_bytes(fmt[t], D);
-            const char *src = arena_in + (t ? p->v_offset : p->k_offset);
-            char *dst = arena_out + dst_offsets[2 * i + t];
+            const char *src = arena + (t ? p->v_offset : p->k_offset);
+            char *dst = arena + dst_offsets[2 * i + t];
             for (int64_t r = 0; r < p->capacity; ++r)
                 for (int64_t e = 0; e < D; ++e) {
                     /* rows past the valid prefix are logical zeros, never read */

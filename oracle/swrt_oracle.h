@@ -287,24 +287,26 @@ int orc_paged_attention(const void *q, int q_type, const char *arena, int64_t ar
                         int64_t kv_heads, int64_t head_dim, double scale, uint32_t *flags);
 
 /*
- * [PF-PAGED] selected-block conversion: each page pages_in[blocks[i]] is
- * decoded (dense: its value; affine: fl((c - zero_point) * scale) in binary32)
- * and its valid rows written in the target formats to arena_out at
- * dst_offsets[2 i] (K) and dst_offsets[2 i + 1] (V): F32 as is (NaN
- * canonical), F16 / BF16 rounded to nearest even (NaN canonical), affine
+ * [PF-PAGED] selected-block conversion inside one arena: each page
+ * pages_in[blocks[i]] is decoded (dense: its value; affine: fl((c -
+ * zero_point) * scale) in binary32) and its rows written in the target
+ * formats at dst_offsets[2 i] (K) and dst_offsets[2 i + 1] (V): F32 as is
+ * (NaN canonical), F16 / BF16 rounded to nearest even (NaN canonical), affine
  * formats as saturate(round_half_even(fl(y / scale)) + zero_point) (NaN ->
  * zero point), packed. Rows [length, capacity) are written as logical zeros
  * of the target (0.0, or the zero point's code) without reading the source.
- * pages_out is pages_in with the selected descriptors' formats, parameters
- * and offsets replaced; a dense target's scale is 1 and zero point 0.
- * Everything is checked first (every page of pages_in, the indices: unique,
- * in [0, n_pages); the targets; the destinations inside arena_out and not
- * overlapping each other): on any failure nothing is written and the call
+ * pages_out (may be pages_in) is pages_in with the selected descriptors'
+ * formats, parameters and offsets replaced; a dense target's scale is 1 and
+ * zero point 0. Everything is checked first: every page of pages_in (valid,
+ * its payloads outside the free region [free_begin, free_end)); the indices
+ * strictly ascending in [0, n_pages); the targets; the destinations in the
+ * order K0, V0, K1, V1, ... each at or after the end of the one before,
+ * inside the free region. On any failure nothing is written and the call
  * returns ORC_E_INVALID_ARG.
  */
-int orc_paged_quantize(const char *arena_in, int64_t arena_in_bytes, const orc_page *pages_in,
+int orc_paged_quantize(char *arena, int64_t arena_bytes, const orc_page *pages_in,
                        int64_t n_pages, const int32_t *blocks, int64_t n_blocks,
-                       const int64_t *dst_offsets, char *arena_out, int64_t arena_out_bytes,
+                       const int64_t *dst_offsets, int64_t free_begin, int64_t free_end,
                        orc_page *pages_out, int k_format, float k_scale, int32_t k_zero_point,
                        int v_format, float v_scale, int32_t v_zero_point, int64_t head_dim);
 

@@ -147,8 +147,11 @@ MUTANTS = {
                                 "(t ? p->v_offset : p->k_offset) + (p->length - 1) * pg_row_bytes(fmt, D);"),
     "paged_append_length_kept": ("        p->length += 1;\n", "        (void)0;\n"),
     "paged_dense_target_keeps_parameters": ("            sc[t] = 1.0f;\n            zp[t] = 0;\n", ""),
-    "paged_live_payload_overwritable": ("if (arena_out == arena_in)\n", "if (0)\n"),
-    "paged_duplicates_accepted": ("if (blocks[j] == blocks[i])", "if (0)"),
+    "paged_live_payload_overwritable": ("return ORC_E_INVALID_ARG; /* the free region holds no live payload */",
+                                        "(void)0;"),
+    "paged_duplicates_accepted": ("(i > 0 && id <= blocks[i - 1])", "(i > 0 && id < blocks[i - 1])"),
+    "paged_destinations_overlap": ("if (dst < next || bytes > free_end - dst)",
+                                   "if (bytes > free_end - dst)"),
     "paged_heads_interleaved": ("const int64_t h = g * group + j;", "const int64_t h = j * Hkv + g;"),
     "paged_scale_dropped": ("sc = scale * dot;", "sc = dot;"),
 }

@@ -257,8 +257,9 @@ def test_pages_example_int2_keys_uint4_values_then_back(orc):
     v = np.array([[0.3, -1.0, 1.0, 0.0625, -0.0625, 2.0, 0.125, -0.2]], np.float32)
     case, tb = one_page_case(k, v, capacity=3)
     base = case.free_offset
-    st, ar, out = orc.paged_quantize(case.arena, tb, [0], [base, base + 64], I2, 0.25, 0, U4,
-                                     0.125, 8, 8)
+    end = len(case.arena)
+    st, ar, out = orc.paged_quantize(case.arena, tb, [0], [base, base + 64], base, end, I2, 0.25,
+                                     0, U4, 0.125, 8, 8)
     assert st == oracle.OK
     # k / 0.25 = 1.2, 2, -1.6, 0.5, 1.5, -2.4, 0, -0.5 -> 1, 1 (sat), -2, 0, 1 (2 sat), -2, 0, 0
     kc = [1, 1, -2, 0, 1, -2, 0, 0]
@@ -276,8 +277,9 @@ def test_pages_example_int2_keys_uint4_values_then_back(orc):
     assert out[0]["k_scale"] == 0.25 and out[0]["v_zero_point"] == 8
     # back to dense: FLOAT16 keys, BFLOAT16 values (the scales are ignored)
     base2 = base + 256
-    st, ar2, out2 = orc.paged_quantize(ar, out, [0], [base2, base2 + 64], F16, 1.0, 0, BF16,
-                                       1.0, 0, 8)
+    # the first conversion's payloads (at base, base + 64) now sit before the free region
+    st, ar2, out2 = orc.paged_quantize(ar, out, [0], [base2, base2 + 64], base2, end, F16, 1.0,
+                                       0, BF16, 1.0, 0, 8)
     assert st == oracle.OK
     kd = ar2[base2:base2 + 16].view(np.float16).astype(np.float64)
     np.testing.assert_array_equal(kd, np.array(kc) * 0.25)
@@ -285,8 +287,8 @@ def test_pages_example_int2_keys_uint4_values_then_back(orc):
     np.testing.assert_array_equal(vd, (np.array(vc) - 8) * 0.125)
     assert out2[0]["k_scale"] == 1.0 and out2[0]["k_zero_point"] == 0
     # a dense target ignores the scale and the zero point's value (a type marker)
-    st, ar3, out3 = orc.paged_quantize(ar, out, [0], [base2, base2 + 64], F16, 0.5, 3, BF16,
-                                       2.0, -7, 8)
+    st, ar3, out3 = orc.paged_quantize(ar, out, [0], [base2, base2 + 64], base2, end, F16, 0.5,
+                                       3, BF16, 2.0, -7, 8)
     assert st == oracle.OK
     np.testing.assert_array_equal(ar3, ar2)
     assert (out3[0]["k_scale"], out3[0]["k_zero_point"]) == (1.0, 0)
@@ -304,8 +306,8 @@ def test_codes_round_to_even_saturate_and_reconstruct(orc, fmt, lo, hi):
     x[0, :8] = np.array([0.5, 1.5, 2.5, -0.5, -1.5, 1e6, -1e6, np.nan], np.float32) * scale
     case, tb = one_page_case(x, x, capacity=n)
     base = case.free_offset
-    st, ar, out = orc.paged_quantize(case.arena, tb, [0], [base, base + 1024], fmt, scale, zp,
-                                     fmt, scale, zp, D)
+    st, ar, out = orc.paged_quantize(case.arena, tb, [0], [base, base + 1024], base,
+                                     len(case.arena), fmt, scale, zp, fmt, scale, zp, D)
     assert st == oracle.OK
     bits = oracle.PAGE_BITS[fmt]
     raw = ar[base:base + n * D * bits // 8]
@@ -335,10 +337,11 @@ def test_requantize_from_affine_and_untouched_rest(orc):
     case = wl.paged_case(g, D, streams, lambda s, i, n: (I8, BF16, 0.05, 1.0, -4, 0),
                          spare_bytes=2048)
     tb = table(case)
-    sel = [int(case.page_ids[0]), int(case.page_ids[4])]
+    sel = sorted([int(case.page_ids[0]), int(case.page_ids[4])])
     base = case.free_offset
     dst = [base, base + 256, base + 512, base + 768]
-    st, ar, out = orc.paged_quantize(case.arena, tb, sel, dst, U4, 0.2, 8, I8, 0.01, 0, D)
+    st, ar, out = orc.paged_quantize(case.arena, tb, sel, dst, base, len(case.arena), U4, 0.2, 8,
+                                     I8, 0.01, 0, D)
     assert st == oracle.OK
     keep = np.ones(len(ar), bool)
     for d, nb in zip(dst, [64, 128, 64, 128]):
@@ -348,7 +351,7 @@ def test_requantize_from_affine_and_untouched_rest(orc):
         if i not in sel:
             assert out[i].tobytes() == tb[i].tobytes()
     # one K code by hand: int8 code c -> fl((c + 4) * 0.05) -> rne(y / 0.2) + 8
-    p = tb[sel[0]]
+    p = tb[sel[0]]  # its K went to base
     c = case.arena[p["k_offset"]:p["k_offset"] + D].view(np.int8).astype(np.int64)
     y = ((c + 4).astype(np.float32) * np.float32(0.05)).astype(np.float32)
     q = np.clip(np.rint((y / np.float32(0.2)).astype(np.float32)) + 8, 0, 15).astype(np.int64)
@@ -362,22 +365,26 @@ def test_invalid_requests_write_nothing(orc):
     D = 16
     case = wl.paged_case(g, D, [wl.page_split(g, 20, 8)], dense_bf16, spare_bytes=1024)
     tb = table(case)
-    base = case.free_offset
-    good = dict(blocks=[0], dst=[base, base + 256], kf=I8, ks=0.1, kz=0, vf=I8, vs=0.1, vz=0)
+    base, end = case.free_offset, len(case.arena)
+    good = dict(blocks=[0, 1], dst=[base, base + 128, base + 256, base + 384], fb=base, fe=end,
+                kf=I8, ks=0.1, kz=0, vf=I8, vs=0.1, vz=0)
 
     def run(**kw):
         a = {**good, **kw}
-        return orc.paged_quantize(case.arena, tb, a["blocks"], a["dst"], a["kf"], a["ks"], a["kz"],
-                                  a["vf"], a["vs"], a["vz"], D)
+        return orc.paged_quantize(case.arena, tb, a["blocks"], a["dst"], a["fb"], a["fe"],
+                                  a["kf"], a["ks"], a["kz"], a["vf"], a["vs"], a["vz"], D)
     st, ar, out = run()
     assert st == oracle.OK
-    for kw in (dict(blocks=[0, 0], dst=[base, base + 256, base + 512, base + 768]),  # duplicate
-               dict(blocks=[3]),                                   # out of range
-               dict(ks=0.0), dict(vs=float("inf")), dict(kz=128),  # parameters
+    for kw in (dict(blocks=[0, 0]), dict(blocks=[1, 0]),          # duplicate, not ascending
+               dict(blocks=[0, 3]),                                 # out of range
+               dict(ks=0.0), dict(vs=float("inf")), dict(kz=128),   # parameters
                dict(vf=U2, vz=4), dict(kf=10),
-               dict(dst=[base, base + 100]),                       # destinations overlap
-               dict(dst=[int(tb[1]["v_offset"]), base + 256]),     # onto a live payload
-               dict(dst=[base, len(case.arena) - 64])):            # past the arena
+               dict(dst=[base, base + 100, base + 256, base + 384]),  # destinations overlap
+               dict(dst=[base, base + 128, base + 100, base + 384]),  # not in order
+               dict(dst=[base - 16, base + 128, base + 256, base + 384]),  # before the region
+               dict(fe=base + 300),                                 # past the region
+               dict(fb=base - 16, dst=[base - 16, base + 128, base + 256, base + 384]),
+               dict(fb=end + 16)):                                  # region past the arena
         st, ar, out = run(**kw)
         assert st == oracle.E_INVALID_ARG, kw
         np.testing.assert_array_equal(ar, case.arena)
