@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define SWRT_ABI_VERSION 4
+#define SWRT_ABI_VERSION 5
 
 /* synchronous status codes */
 #define SWRT_OK 0
@@ -73,6 +73,8 @@ extern "C" {
 #define SWRT_FLAG_BAD_SEQLEN 2u   /* seqlens_k[b] < 0 or seqlens_k[b] + 1 < S */
 #define SWRT_FLAG_BAD_LENGTHS 4u  /* (Lp, E) not a step that fits (C, S)      */
 #define SWRT_FLAG_ROPE_RANGE 8u   /* a rotary position outside the tables     */
+#define SWRT_FLAG_BAD_PAGES 16u   /* a page table or page descriptor failed   */
+#define SWRT_FLAG_PAGE_FULL 32u   /* a paged append found its page full       */
 
 /* TensorScatter mode attribute */
 #define SWRT_MODE_LINEAR 0
@@ -498,6 +500,147 @@ int swrt_window_attention(int n_layers, const void *const *q,
                           int window, int batch, int q_heads, int kv_heads,
                           int capacity, int head_dim, float scale, int elem_type,
                           int out_type, uint32_t *d_flags, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Paged caches (onnx-light how-to "Persistent input/output feedback",        */
+/* section "Optional heterogeneous paged KV": "Cache value declaration",      */
+/* "Selected-block quantization", "Serialized cache values" and the kernel    */
+/* description that follows them).                                            */
+/* ------------------------------------------------------------------------ */
+
+/* page formats beyond the row transform's: affine sub-byte codes */
+#define SWRT_XF_INT4 6
+#define SWRT_XF_UINT4 7
+#define SWRT_XF_INT2 8
+#define SWRT_XF_UINT2 9
+
+/*
+ * One page (block) of one stream (batch entry b, KV head g; stream
+ * b * kv_heads + g): tokens [start, start + length) of the stream, capacity
+ * physical rows of head_dim elements for K and for V at byte offsets of the
+ * layer's arena (16-byte aligned). A row of a b-bit format is
+ * head_dim * b / 8 bytes. Dense formats (SWRT_XF_F32 / _F16 / _BF16) hold
+ * values; affine formats (SWRT_XF_INT8, _UINT8, _INT4, _UINT4, _INT2,
+ * _UINT2) hold codes c meaning (c - zero_point) * scale, scale > 0 and
+ * finite, zero_point inside the code range; sub-byte codes are packed from
+ * the least significant bits of each byte (element 0 lowest), signed codes in
+ * two's complement. A stream's pages, in token order, are contiguous from
+ * zero (each start is the previous start + length) with
+ * 1 <= length <= capacity. 64 bytes, device memory.
+ */
+typedef struct swrt_page {
+  int64_t start;
+  int32_t length;
+  int32_t capacity;
+  int64_t k_offset;
+  int64_t v_offset;
+  int32_t k_format;
+  int32_t v_format;
+  float k_scale;
+  float v_scale;
+  int32_t k_zero_point;
+  int32_t v_zero_point;
+  int32_t reserved[2];
+} swrt_page;
+
+/*
+ * One layer's paged cache plus its query and output, as the attention takes
+ * them (host struct of device pointers):
+ *   q          [batch, q_heads, head_dim] q_type, 16-byte aligned.
+ *   out        [batch, q_heads, head_dim] out_type, 16-byte aligned; must not
+ *              overlap any input.
+ *   arena      device bytes holding every page payload, 16-byte aligned,
+ *              arena_bytes long.
+ *   pages      device swrt_page[n_pages].
+ *   page_ptr   device int32[batch * kv_heads + 1]: stream s owns
+ *              page_ids[page_ptr[s] .. page_ptr[s + 1]) in token order.
+ *   page_ids   device int32[n_ids]: indices into pages.
+ * Layers may share pages, page_ptr and page_ids (one block table for every
+ * layer, each with its own arena).
+ */
+typedef struct swrt_paged_layer {
+  const void *q;
+  void *out;
+  const void *arena;
+  int64_t arena_bytes;
+  const swrt_page *pages;
+  int64_t n_pages;
+  const int32_t *page_ptr;
+  const int32_t *page_ids;
+  int64_t n_ids;
+} swrt_paged_layer;
+
+/*
+ * swrt_paged_attention -- one-token decode attention over paged caches
+ * (section "Optional heterogeneous paged KV": attention reads only valid,
+ * visible tokens with online softmax, a left window bounds the preceding
+ * tokens, grouped-query heads; onnx-light-cpu "Persistent KV Cache and Decode
+ * Performance Roadmap", "Phase 1": fp32 scores, softmax and accumulation).
+ * For every layer, batch entry b and query head h, with stream
+ * s = b * kv_heads + h / (q_heads / kv_heads) holding T tokens (its last
+ * page's start + length; 0 without pages):
+ *   tokens  r in [max(0, T - 1 - left_window), T)   (left_window < 0: all T)
+ *   out[b, h, :] = sum_r softmax_r(scale * q[b, h, :] . k_r) v_r
+ * with k_r, v_r the decoded values of token r in its page's formats. Only the
+ * pages the window reaches are read, and they are checked first (ids inside
+ * [0, n_pages), contiguous, lengths, formats and parameters, payloads inside
+ * the arena); a stream that fails raises SWRT_FLAG_BAD_PAGES and its query
+ * heads' outputs are left as they were. An empty stream writes zeros.
+ * n_layers 1 .. SWRT_MAX_LAYERS; q_heads / kv_heads in 1 .. 16; head_dim in
+ * {32, 64, 128, 256}; q_type, out_type SWRT_XF_F32 / _F16 / _BF16; scale
+ * finite. Status codes for bad arguments; d_flags device uint32 or NULL.
+ */
+int swrt_paged_attention(int n_layers, const swrt_paged_layer *layers, int64_t left_window,
+                         int batch, int q_heads, int kv_heads, int head_dim, float scale,
+                         int q_type, int out_type, uint32_t *d_flags, void *stream);
+
+/*
+ * swrt_paged_quantize -- selected-block conversion ("Selected-block
+ * quantization": QuantizePagedCache) inside one arena. Each page
+ * pages_in[blocks[i]] is decoded (dense: its value; affine: (c - zero_point)
+ * * scale rounded once to binary32) and its rows written in the target
+ * formats at dst_offsets[2 i] (K) and dst_offsets[2 i + 1] (V): SWRT_XF_F32
+ * as is, F16 / BF16 rounded to nearest even, NaN as the positive canonical
+ * quiet NaN; affine targets saturate(round_half_even(y / scale) +
+ * zero_point), NaN -> zero_point, packed. Rows [length, capacity) become
+ * logical zeros of the target (0.0 or the zero point's code) without reading
+ * the source. Then pages_out (may equal pages_in) receives every descriptor
+ * of pages_in, the selected ones with the new formats, parameters (a dense
+ * target: scale 1, zero point 0) and offsets.
+ * Everything is checked on the device before anything is written: every
+ * page of pages_in (valid, payloads inside the arena and outside the free
+ * region [free_begin, free_end)); blocks strictly ascending inside
+ * [0, n_pages); destinations in the order K0, V0, K1, V1, ... each at or
+ * after the end of the one before, 16-byte aligned, inside the free region.
+ * A failure raises SWRT_FLAG_BAD_PAGES and nothing is written. d_flags is
+ * required and its SWRT_FLAG_BAD_PAGES bit must be clear on entry (a set bit
+ * also stops the conversion). blocks, dst_offsets (int32[n_blocks],
+ * int64[2 n_blocks]), pages_in and pages_out are device memory. Targets are
+ * checked on the host (formats, scale > 0 and finite, zero points in range).
+ */
+int swrt_paged_quantize(void *arena, int64_t arena_bytes, const swrt_page *pages_in,
+                        int64_t n_pages, const int32_t *blocks, int64_t n_blocks,
+                        const int64_t *dst_offsets, int64_t free_begin, int64_t free_end,
+                        swrt_page *pages_out, int k_format, float k_scale,
+                        int32_t k_zero_point, int v_format, float v_scale,
+                        int32_t v_zero_point, int head_dim, uint32_t *d_flags, void *stream);
+
+/*
+ * swrt_paged_append -- the decode step's new token into each stream's last
+ * page: stream s writes k_new[s, :] and v_new[s, :] (new_type F32 / F16 /
+ * BF16, [n_streams, head_dim], 16-byte aligned) as row `length` of page
+ * page_ids[page_ptr[s + 1] - 1], encoded in that page's formats as
+ * swrt_paged_quantize encodes, and that page's length grows by one (on the
+ * device). A stream without pages or whose last page fails its checks raises
+ * SWRT_FLAG_BAD_PAGES, one whose last page is full SWRT_FLAG_PAGE_FULL;
+ * either is skipped. n_layers 1 .. SWRT_MAX_LAYERS, each with its own arena,
+ * pages and block table (arena, pages, page_ptr, page_ids of each
+ * swrt_paged_layer; q and out unused); pages must not be shared between the
+ * layers of one call (each layer's append grows its own pages).
+ */
+int swrt_paged_append(int n_layers, const swrt_paged_layer *layers, const void *const *k_new,
+                      const void *const *v_new, int new_type, int n_streams, int head_dim,
+                      uint32_t *d_flags, void *stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *swrt_status_string(int status);

@@ -882,10 +882,12 @@ static int pg_format_ok(int fmt, float scale, int32_t zero_point, int64_t head_d
     return 1;
 }
 
-/* [offset, offset + bytes) inside [0, arena_bytes) */
+/* [offset, offset + bytes) inside [0, arena_bytes), offset 16-byte aligned (the
+ * library's layout rule for payloads) */
 static int pg_inside(int64_t offset, int64_t bytes, int64_t arena_bytes)
 {
-    return offset >= 0 && bytes >= 0 && offset <= arena_bytes && bytes <= arena_bytes - offset;
+    return offset >= 0 && offset % 16 == 0 && bytes >= 0 && offset <= arena_bytes &&
+           bytes <= arena_bytes - offset;
 }
 
 static int pg_page_ok(const orc_page *p, int64_t head_dim, int64_t arena_bytes)
@@ -1123,7 +1125,7 @@ int orc_paged_quantize(char *arena, int64_t arena_bytes, const orc_page *pages_i
         for (int t = 0; t < 2; ++t) {
             const int64_t bytes = pages_in[id].capacity * pg_row_bytes(fmt[t], D);
             const int64_t dst = dst_offsets[2 * i + t];
-            if (dst < next || bytes > free_end - dst)
+            if (dst < next || dst % 16 != 0 || bytes > free_end - dst)
                 return ORC_E_INVALID_ARG;
             next = dst + bytes;
         }

@@ -241,8 +241,9 @@ int orc_window_attention(const void *q, const void *k_cache, const void *v_cache
  * of one stream (batch entry, KV head), capacity physical rows of head_dim
  * elements for K and for V at byte offsets of an arena. Dense formats
  * (ORC_XF_F32 / F16 / BF16) hold values; affine formats (INT8, UINT8, INT4,
- * UINT4, INT2, UINT2) hold codes c with value (c - zero_point) * scale. A row
- * of a b-bit format is head_dim * b / 8 bytes; sub-byte codes pack from the
+ * UINT4, INT2, UINT2) hold codes c with value (c - zero_point) * scale.
+ * Payload offsets are 16-byte aligned. A row of a b-bit format is
+ * head_dim * b / 8 bytes; sub-byte codes pack from the
  * least significant bits of each byte (element 0 in the low bits), signed
  * codes in two's complement. The layout is the GPU library's page descriptor
  * (64 bytes), defined here on its own.
@@ -300,8 +301,8 @@ int orc_paged_attention(const void *q, int q_type, const char *arena, int64_t ar
  * zero point 0. Everything is checked first: every page of pages_in (valid,
  * its payloads outside the free region [free_begin, free_end)); the indices
  * strictly ascending in [0, n_pages); the targets; the destinations in the
- * order K0, V0, K1, V1, ... each at or after the end of the one before,
- * inside the free region. On any failure nothing is written and the call
+ * order K0, V0, K1, V1, ... each 16-byte aligned and at or after the end of
+ * the one before, inside the free region. On any failure nothing is written and the call
  * returns ORC_E_INVALID_ARG.
  */
 int orc_paged_quantize(char *arena, int64_t arena_bytes, const orc_page *pages_in,

@@ -28,6 +28,14 @@ resident rows of its KV head):
 
     window_attention(qs, k_caches, v_caches, cache_total_lens, window, ...)
 
+Paged caches (onnx-light how-to "Persistent input/output feedback", section
+"Optional heterogeneous paged KV"; ``PagedCache``: one layer's arena, page
+descriptors and block table on the device):
+
+    paged_attention(qs, caches, left_window, kv_heads, ...)
+    paged_quantize(cache, blocks, dst_offsets, free_begin, free_end, ...)
+    paged_append(caches, k_news, v_news, ...)
+
 Every function has a ``prepare_*`` twin returning a ``PreparedCall``: the
 arguments are checked and marshalled once, and each call of the object only
 adds the current stream. Decode loops use it to keep host cost per step small.
@@ -39,6 +47,7 @@ import os
 from dataclasses import dataclass
 from typing import NamedTuple, Sequence
 
+import numpy as np
 import torch
 
 __all__ = [
@@ -50,6 +59,9 @@ __all__ = [
     "Transform", "kv_window_append_xf", "tensor_scatter_xf", "kv_decode_step_xf",
     "prepare_kv_window_append_xf", "prepare_tensor_scatter_xf", "prepare_kv_decode_step_xf",
     "window_attention", "prepare_window_attention",
+    "PagedCache", "PAGE_DTYPE", "PAGE_FORMATS", "page_table", "paged_attention",
+    "prepare_paged_attention", "paged_quantize", "paged_append", "prepare_paged_append",
+    "FLAG_BAD_PAGES", "FLAG_PAGE_FULL",
     "OK", "E_INVALID_ARG", "E_UNSUPPORTED", "E_LAUNCH",
     "FLAG_LINEAR_OOB", "FLAG_BAD_SEQLEN", "FLAG_BAD_LENGTHS", "FLAG_ROPE_RANGE",
     "PHASE_STAGE", "PHASE_COMMIT", "PHASE_ALL",
@@ -61,11 +73,12 @@ LIBRARY = os.path.join(PKG, "libswrt.so")
 # values of include/swrt.h
 OK, E_INVALID_ARG, E_UNSUPPORTED, E_LAUNCH = 0, 1, 2, 3
 FLAG_LINEAR_OOB, FLAG_BAD_SEQLEN, FLAG_BAD_LENGTHS, FLAG_ROPE_RANGE = 1, 2, 4, 8
+FLAG_BAD_PAGES, FLAG_PAGE_FULL = 16, 32
 MODE_LINEAR, MODE_CIRCULAR = 0, 1
 PHASE_STAGE, PHASE_COMMIT, PHASE_ALL = 1, 2, 3
 MAX_LAYERS = 32
 MAX_BATCHED = 64
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 _PHASES = {"stage": PHASE_STAGE, "commit": PHASE_COMMIT, "all": PHASE_ALL}
 _MODES = {"linear": MODE_LINEAR, "circular": MODE_CIRCULAR}
@@ -174,11 +187,17 @@ def lib() -> ctypes.CDLL:
                                          xfp, vp, vp]
     L.swrt_window_attention.argtypes = [i32, vpp, vpp, vpp, vpp, vp, i32, i32, i32, i32, i32,
                                         i32, ctypes.c_float, i32, i32, vp, vp]
+    f32 = ctypes.c_float
+    L.swrt_paged_attention.argtypes = [i32, vp, i64, i32, i32, i32, i32, f32, i32, i32, vp, vp]
+    L.swrt_paged_quantize.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, i64, vp, i32, f32,
+                                      ctypes.c_int32, i32, f32, ctypes.c_int32, i32, vp, vp]
+    L.swrt_paged_append.argtypes = [i32, vp, vpp, vpp, i32, i32, i32, vp, vp]
     for name in ("swrt_tensor_scatter", "swrt_tensor_scatter_batched", "swrt_kv_seq_lengths",
                  "swrt_kv_seq_lengths_drift",
                  "swrt_kv_window_append", "swrt_kv_window_append_layers", "swrt_kv_decode_step",
                  "swrt_kv_window_append_xf", "swrt_tensor_scatter_xf", "swrt_kv_decode_step_xf",
-                 "swrt_window_attention", "swrt_abi_version"):
+                 "swrt_window_attention", "swrt_paged_attention", "swrt_paged_quantize",
+                 "swrt_paged_append", "swrt_abi_version"):
         getattr(L, name).restype = ctypes.c_int
     L.swrt_status_string.argtypes = [ctypes.c_int]
     L.swrt_status_string.restype = ctypes.c_char_p
@@ -755,3 +774,193 @@ def window_attention(qs, k_caches, v_caches, cache_total_lens, window: int, *,
     accumulation; ``scale`` defaults to 1 / sqrt(D). Returns the outputs."""
     return prepare_window_attention(qs, k_caches, v_caches, cache_total_lens, window,
                                     scale=scale, out_dtype=out_dtype, outs=outs, flags=flags)()
+
+
+# ---------------------------------------------------------------------------
+# paged caches
+# ---------------------------------------------------------------------------
+# page formats (include/swrt.h SWRT_XF_*)
+PAGE_FORMATS = {"f32": 1, "f16": 2, "bf16": 3, "int8": 4, "uint8": 5, "int4": 6, "uint4": 7,
+                "int2": 8, "uint2": 9}
+# the C struct swrt_page, 64 bytes
+PAGE_DTYPE = np.dtype([("start", "<i8"), ("length", "<i4"), ("capacity", "<i4"),
+                       ("k_offset", "<i8"), ("v_offset", "<i8"), ("k_format", "<i4"),
+                       ("v_format", "<i4"), ("k_scale", "<f4"), ("v_scale", "<f4"),
+                       ("k_zero_point", "<i4"), ("v_zero_point", "<i4"), ("reserved", "<i4", (2,))])
+_Q_TYPES = {torch.float32: 1, torch.float16: 2, torch.bfloat16: 3}
+
+
+class PagedLayer(ctypes.Structure):
+    """The C struct swrt_paged_layer."""
+    _fields_ = [("q", ctypes.c_void_p), ("out", ctypes.c_void_p), ("arena", ctypes.c_void_p),
+                ("arena_bytes", ctypes.c_int64), ("pages", ctypes.c_void_p),
+                ("n_pages", ctypes.c_int64), ("page_ptr", ctypes.c_void_p),
+                ("page_ids", ctypes.c_void_p), ("n_ids", ctypes.c_int64)]
+
+
+def page_table(fields: dict) -> np.ndarray:
+    """swrt_page descriptors (host, PAGE_DTYPE) from per-field arrays."""
+    n = len(fields["start"])
+    t = np.zeros(n, PAGE_DTYPE)
+    for name in PAGE_DTYPE.names:
+        if name in fields:
+            t[name] = fields[name]
+    return t
+
+
+@dataclass
+class PagedCache:
+    """One layer's paged cache on the device: ``arena`` (uint8, every page
+    payload), ``pages`` (uint8 [n_pages * 64]: the swrt_page descriptors),
+    ``page_ptr`` (int32 [streams + 1]) and ``page_ids`` (int32): stream s owns
+    page_ids[page_ptr[s]:page_ptr[s + 1]] in token order. Several layers may
+    share pages, page_ptr and page_ids (one block table, one arena each)."""
+    arena: torch.Tensor
+    pages: torch.Tensor
+    page_ptr: torch.Tensor
+    page_ids: torch.Tensor
+
+    @staticmethod
+    def upload(table: np.ndarray, page_ptr, page_ids, arena, device) -> "PagedCache":
+        def dev(a, dt):
+            return torch.from_numpy(np.ascontiguousarray(a, dtype=dt)).to(device)
+        pages = torch.from_numpy(np.ascontiguousarray(table, PAGE_DTYPE).view(np.uint8)).to(device)
+        ar = arena if isinstance(arena, torch.Tensor) else dev(arena, np.uint8)
+        return PagedCache(ar, pages, dev(page_ptr, np.int32), dev(page_ids, np.int32))
+
+    @property
+    def n_pages(self) -> int:
+        return self.pages.numel() // PAGE_DTYPE.itemsize
+
+    def table(self) -> np.ndarray:
+        """The descriptors, copied to the host."""
+        return self.pages.cpu().numpy().view(PAGE_DTYPE).copy()
+
+    def _check(self):
+        for name, t, dt in (("arena", self.arena, torch.uint8), ("pages", self.pages, torch.uint8),
+                            ("page_ptr", self.page_ptr, torch.int32),
+                            ("page_ids", self.page_ids, torch.int32)):
+            _contig(name, t)
+            if t.dtype != dt or t.dim() != 1:
+                raise SwrtError(f"{name} must be a 1-D {dt} tensor")
+        if self.pages.numel() % PAGE_DTYPE.itemsize:
+            raise SwrtError("pages must hold whole 64-byte descriptors")
+
+    def layer(self, q=None, out=None) -> PagedLayer:
+        return PagedLayer(_ptr(q), _ptr(out), _ptr(self.arena), self.arena.numel(),
+                          _ptr(self.pages), self.n_pages, _ptr(self.page_ptr),
+                          _ptr(self.page_ids), self.page_ids.numel())
+
+
+def prepare_paged_attention(qs: Sequence[torch.Tensor], caches: Sequence[PagedCache],
+                            left_window: int, kv_heads: int, *, scale: float | None = None,
+                            out_dtype: torch.dtype | None = None,
+                            outs: Sequence[torch.Tensor] | None = None,
+                            flags: torch.Tensor | None = None) -> PreparedCall:
+    """See ``paged_attention``."""
+    n = len(qs)
+    if len(caches) != n or not 1 <= n <= MAX_LAYERS:
+        raise SwrtError(f"need 1..{MAX_LAYERS} layers with a query and a cache each")
+    q0 = qs[0]
+    if q0.dim() != 3 or q0.dtype not in _Q_TYPES:
+        raise SwrtError("queries must be [B, Hq, D] float32, float16 or bfloat16")
+    B, Hq, D = q0.shape
+    odt = out_dtype if out_dtype is not None else (outs[0].dtype if outs else q0.dtype)
+    if odt not in _Q_TYPES:
+        raise SwrtError("outputs are float32, float16 or bfloat16")
+    outs = [torch.empty((B, Hq, D), dtype=odt, device=q0.device) for _ in range(n)] \
+        if outs is None else list(outs)
+    for q, o, c in zip(qs, outs, caches):
+        _contig("q", q)
+        _contig("out", o)
+        if q.shape != q0.shape or q.dtype != q0.dtype or o.shape != q0.shape or o.dtype != odt:
+            raise SwrtError("every query [B, Hq, D] of one dtype, every output of another")
+        c._check()
+        if c.page_ptr.numel() != B * kv_heads + 1:
+            raise SwrtError("page_ptr must hold batch * kv_heads + 1 entries")
+    dev = _device_of(*qs, *outs, *(t for c in caches for t in (c.arena, c.pages, c.page_ptr,
+                                                                c.page_ids)), flags)
+    layers = (PagedLayer * n)(*[c.layer(q, o) for c, q, o in zip(caches, qs, outs)])
+    sc = D ** -0.5 if scale is None else float(scale)
+    args = (n, ctypes.cast(layers, ctypes.c_void_p), int(left_window), B, Hq, kv_heads, D, sc,
+            _Q_TYPES[q0.dtype], _Q_TYPES[odt], _ptr(flags))
+    keep = (layers, *qs, *outs, *caches, flags)
+    return PreparedCall(lib().swrt_paged_attention, args, dev, "paged_attention", keep, outs)
+
+
+def paged_attention(qs, caches, left_window: int, kv_heads: int, *, scale: float | None = None,
+                    out_dtype: torch.dtype | None = None, outs=None, flags=None) -> list:
+    """One-token decode attention of every layer's queries [B, Hq, D] over its
+    paged cache: query head h of entry b reads stream b * kv_heads + h //
+    (Hq // kv_heads) over its last ``left_window`` + 1 tokens (all for a
+    negative value), decoding each page's format. Returns the outputs."""
+    return prepare_paged_attention(qs, caches, left_window, kv_heads, scale=scale,
+                                   out_dtype=out_dtype, outs=outs, flags=flags)()
+
+
+def paged_quantize(cache: PagedCache, blocks: torch.Tensor, dst_offsets: torch.Tensor,
+                   free_begin: int, free_end: int, k_format: int, k_scale: float,
+                   k_zero_point: int, v_format: int, v_scale: float, v_zero_point: int,
+                   head_dim: int, *, pages_out: torch.Tensor | None = None,
+                   flags: torch.Tensor) -> torch.Tensor:
+    """QuantizePagedCache: convert the selected pages (``blocks`` int32,
+    strictly ascending) into the target formats at ``dst_offsets`` (int64
+    [2 n]: K0, V0, K1, ...) inside the arena's free region [free_begin,
+    free_end); returns the new descriptor table (``pages_out``, which may be
+    ``cache.pages``). ``flags`` (int32 device word, BAD_PAGES clear) receives
+    FLAG_BAD_PAGES when a check fails; then nothing is written."""
+    cache._check()
+    out = torch.empty_like(cache.pages) if pages_out is None else pages_out
+    for name, t, dt in (("blocks", blocks, torch.int32), ("dst_offsets", dst_offsets, torch.int64)):
+        _contig(name, t)
+        if t.dtype != dt or t.dim() != 1:
+            raise SwrtError(f"{name} must be a 1-D {dt} tensor")
+    if dst_offsets.numel() != 2 * blocks.numel() or out.shape != cache.pages.shape:
+        raise SwrtError("dst_offsets needs two entries per block; pages_out the table's size")
+    if flags is None:
+        raise SwrtError("paged_quantize needs a flag word")
+    dev = _device_of(cache.arena, cache.pages, blocks, dst_offsets, out, flags)
+    with torch.cuda.device(dev):
+        st = lib().swrt_paged_quantize(
+            _ptr(cache.arena), cache.arena.numel(), _ptr(cache.pages), cache.n_pages,
+            _ptr(blocks), blocks.numel(), _ptr(dst_offsets), int(free_begin), int(free_end),
+            _ptr(out), int(k_format), float(k_scale), int(k_zero_point), int(v_format),
+            float(v_scale), int(v_zero_point), int(head_dim), _ptr(flags),
+            ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
+    _check(st, "paged_quantize")
+    return out
+
+
+def prepare_paged_append(caches: Sequence[PagedCache], k_news: Sequence[torch.Tensor],
+                         v_news: Sequence[torch.Tensor], *,
+                         flags: torch.Tensor | None = None) -> PreparedCall:
+    """See ``paged_append``."""
+    n = len(caches)
+    if len(k_news) != n or len(v_news) != n or not 1 <= n <= MAX_LAYERS:
+        raise SwrtError(f"need 1..{MAX_LAYERS} layers with a cache and new K and V rows each")
+    k0 = k_news[0]
+    if k0.dim() != 2 or k0.dtype not in _Q_TYPES:
+        raise SwrtError("new rows must be [streams, D] float32, float16 or bfloat16")
+    S, D = k0.shape
+    for c, k, v in zip(caches, k_news, v_news):
+        c._check()
+        _contig("k_new", k)
+        _contig("v_new", v)
+        if k.shape != k0.shape or v.shape != k0.shape or k.dtype != k0.dtype or v.dtype != k0.dtype:
+            raise SwrtError("every new row tensor [streams, D] of one dtype")
+        if c.page_ptr.numel() != S + 1:
+            raise SwrtError("page_ptr must hold streams + 1 entries")
+    dev = _device_of(*k_news, *v_news, *(t for c in caches for t in (c.arena, c.pages, c.page_ptr,
+                                                                     c.page_ids)), flags)
+    layers = (PagedLayer * n)(*[c.layer() for c in caches])
+    args = (n, ctypes.cast(layers, ctypes.c_void_p), _ptrs(k_news), _ptrs(v_news),
+            _Q_TYPES[k0.dtype], S, D, _ptr(flags))
+    keep = (layers, *caches, *k_news, *v_news, flags)
+    return PreparedCall(lib().swrt_paged_append, args, dev, "paged_append", keep)
+
+
+def paged_append(caches, k_news, v_news, *, flags=None) -> None:
+    """Each stream's new K and V rows ([streams, D]) into its last page,
+    encoded in the page's formats; the page grows by one row (once per
+    distinct block table)."""
+    prepare_paged_append(caches, k_news, v_news, flags=flags)()

@@ -1,0 +1,851 @@
+// paged.hip -- paged caches with per-page formats on gfx950 (onnx-light how-to
+// "Persistent input/output feedback", section "Optional heterogeneous paged
+// KV": pages with start, length and capacity, contiguous from zero; dense
+// FLOAT / FLOAT16 / BFLOAT16 or affine INT8 / UINT8 / INT4 / UINT4 / INT2 /
+// UINT2 payloads per page, independently for K and V; QuantizePagedCache on
+// selected blocks; attention over the visible tokens only, with online
+// softmax and a left window bounding the preceding tokens).
+//
+// Three kernel families:
+//   paged_attention_kernel  one wave per (layer, batch entry, KV head) stream:
+//                           finds the pages its window reaches, checks each,
+//                           decodes each 16-row tile of a page in the page's
+//                           formats and runs both contractions on the matrix
+//                           cores in fp32 (the formats differ page to page, so
+//                           every operand is widened to binary32 first;
+//                           affine codes enter as the exact integers c - zp,
+//                           their scales applied to the score and the weight).
+//   paged_validate / paged_convert / paged_publish
+//                           the conversion of selected pages: every check on
+//                           the device first, then the payloads, then the
+//                           descriptors, each later kernel stopping when the
+//                           first raised the flag.
+//   paged_append_rows / paged_append_commit
+//                           one wave per (layer, stream): the new token's rows
+//                           into its last page, encoded; then, once per
+//                           distinct block table, the page's length + 1.
+#include "swrt_host.hpp"
+
+namespace swrt {
+namespace {
+
+constexpr int kPgBlock = 256;  // 4 waves, one stream each
+constexpr int kPgWaves = kPgBlock / 64;
+
+struct PgLayer {
+  const char *q;
+  char *out;
+  const char *arena;
+  int64_t arena_bytes;
+  const swrt_page *pages;
+  int64_t n_pages;
+  const int32_t *page_ptr;
+  const int32_t *page_ids;
+  int64_t n_ids;
+};
+
+// ---------------------------------------------------------------------------
+// formats
+// ---------------------------------------------------------------------------
+__host__ __device__ constexpr int pg_bits(int f) {
+  return f == SWRT_XF_F32 ? 32
+         : (f == SWRT_XF_F16 || f == SWRT_XF_BF16) ? 16
+         : (f == SWRT_XF_INT8 || f == SWRT_XF_UINT8) ? 8
+         : (f == SWRT_XF_INT4 || f == SWRT_XF_UINT4) ? 4
+         : (f == SWRT_XF_INT2 || f == SWRT_XF_UINT2) ? 2
+                                                     : 0;
+}
+__host__ __device__ constexpr bool pg_affine(int f) { return f >= SWRT_XF_INT8 && f <= SWRT_XF_UINT2; }
+__host__ __device__ constexpr bool pg_signed(int f) {
+  return f == SWRT_XF_INT8 || f == SWRT_XF_INT4 || f == SWRT_XF_INT2;
+}
+__host__ __device__ constexpr int32_t pg_lo(int f) { return pg_signed(f) ? -(1 << (pg_bits(f) - 1)) : 0; }
+__host__ __device__ constexpr int32_t pg_hi(int f) {
+  return pg_signed(f) ? (1 << (pg_bits(f) - 1)) - 1 : (1 << pg_bits(f)) - 1;
+}
+
+// a format with its parameters (an affine one: positive finite scale, zero
+// point inside the code range)
+__host__ __device__ inline bool pg_format_ok(int f, float scale, int32_t zp) {
+  if (pg_bits(f) == 0) return false;
+  if (!pg_affine(f)) return true;
+  return scale > 0.0f && scale <= 3.4028235e38f && zp >= pg_lo(f) && zp <= pg_hi(f);
+}
+
+__host__ __device__ inline int64_t pg_row_bytes(int f, int D) { return int64_t(D) * pg_bits(f) / 8; }
+
+// [off, off + bytes) inside [0, arena), off 16-byte aligned
+__device__ __forceinline__ bool pg_inside(int64_t off, int64_t bytes, int64_t arena) {
+  return off >= 0 && (off & 15) == 0 && off <= arena && bytes <= arena - off;
+}
+
+__device__ __forceinline__ bool pg_page_ok(const swrt_page &p, int D, int64_t arena) {
+  if (p.start < 0 || p.capacity < 1 || p.length < 1 || p.length > p.capacity) return false;
+  if (!pg_format_ok(p.k_format, p.k_scale, p.k_zero_point) ||
+      !pg_format_ok(p.v_format, p.v_scale, p.v_zero_point))
+    return false;
+  if (p.start > INT64_MAX - p.length) return false;
+  return pg_inside(p.k_offset, p.capacity * pg_row_bytes(p.k_format, D), arena) &&
+         pg_inside(p.v_offset, p.capacity * pg_row_bytes(p.v_format, D), arena);
+}
+
+// a descriptor read whole with uniform (scalar) loads
+__device__ __forceinline__ swrt_page pg_read(const swrt_page *pages, int32_t id) {
+  return pages[__builtin_amdgcn_readfirstlane(id)];
+}
+
+// NB bytes (1, 2, 4, 8 or a multiple of 16) of a payload as 32-bit words
+template <int NB>
+__device__ __forceinline__ void pg_load_raw(const char *p, uint32_t (&w)[(NB + 3) / 4]) {
+  if constexpr (NB == 1) {
+    w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint8_t *>(p));
+  } else if constexpr (NB == 2) {
+    w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(p));
+  } else if constexpr (NB == 4) {
+    w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p));
+  } else if constexpr (NB == 8) {
+    const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+    w[0] = x.x;
+    w[1] = x.y;
+  } else {
+    static_assert(NB % 16 == 0, "payload chunk");
+#pragma unroll
+    for (int i = 0; i < NB / 16; ++i) {
+      const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p) + i);
+      w[4 * i] = x.x;
+      w[4 * i + 1] = x.y;
+      w[4 * i + 2] = x.z;
+      w[4 * i + 3] = x.w;
+    }
+  }
+}
+
+// element e of packed words as binary32: a dense value, or the exact integer
+// c - zp of an affine code (its scale applied by the caller)
+template <int FMT, int NW>
+__device__ __forceinline__ float pg_elem(const uint32_t (&w)[NW], int e, int32_t zp) {
+  if constexpr (FMT == SWRT_XF_F32) {
+    return __uint_as_float(w[e]);
+  } else if constexpr (FMT == SWRT_XF_BF16) {
+    return __uint_as_float(e & 1 ? w[e / 2] & 0xFFFF0000u : w[e / 2] << 16);
+  } else if constexpr (FMT == SWRT_XF_F16) {
+    return float(__builtin_bit_cast(_Float16, uint16_t(w[e / 2] >> (16 * (e & 1)))));
+  } else {
+    constexpr int B = pg_bits(FMT);
+    const uint32_t raw = (w[e * B / 32] >> (e * B % 32)) & ((1u << B) - 1u);
+    int32_t c = int32_t(raw);
+    if constexpr (pg_signed(FMT)) c = int32_t(raw << (32 - B)) >> (32 - B);
+    return float(c - zp);
+  }
+}
+
+// N elements starting at element `first` of a row, decoded (see pg_elem)
+template <int N, int FMT>
+__device__ __forceinline__ void pg_load_decode_t(const char *row, uint32_t first, int32_t zp,
+                                                 float (&out)[N]) {
+  constexpr int B = pg_bits(FMT);
+  constexpr int NB = N * B / 8 > 0 ? N * B / 8 : 1;
+  uint32_t w[(NB + 3) / 4];
+  const uint32_t bit = first * B;
+  pg_load_raw<NB>(row + bit / 8, w);
+  if constexpr (N * B < 8) w[0] >>= bit % 8;  // a sub-byte chunk: its place in the byte
+#pragma unroll
+  for (int e = 0; e < N; ++e) out[e] = pg_elem<FMT>(w, e, zp);
+}
+
+template <int N>
+__device__ __forceinline__ void pg_load_decode(int fmt, const char *row, uint32_t first, int32_t zp,
+                                               float (&out)[N]) {
+  switch (fmt) {  // uniform in the wave
+    case SWRT_XF_F32: pg_load_decode_t<N, SWRT_XF_F32>(row, first, zp, out); break;
+    case SWRT_XF_F16: pg_load_decode_t<N, SWRT_XF_F16>(row, first, zp, out); break;
+    case SWRT_XF_BF16: pg_load_decode_t<N, SWRT_XF_BF16>(row, first, zp, out); break;
+    case SWRT_XF_INT8: pg_load_decode_t<N, SWRT_XF_INT8>(row, first, zp, out); break;
+    case SWRT_XF_UINT8: pg_load_decode_t<N, SWRT_XF_UINT8>(row, first, zp, out); break;
+    case SWRT_XF_INT4: pg_load_decode_t<N, SWRT_XF_INT4>(row, first, zp, out); break;
+    case SWRT_XF_UINT4: pg_load_decode_t<N, SWRT_XF_UINT4>(row, first, zp, out); break;
+    case SWRT_XF_INT2: pg_load_decode_t<N, SWRT_XF_INT2>(row, first, zp, out); break;
+    default: pg_load_decode_t<N, SWRT_XF_UINT2>(row, first, zp, out); break;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// attention
+// ---------------------------------------------------------------------------
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct PgAttArgs {
+  PgLayer L[kMaxLayers];
+  uint32_t *flags;
+  float scale_log2;  // scale * log2(e)
+  int64_t left_window;
+  int32_t B, Hq, Hkv, items, q_type, out_type;
+};
+
+// Lane l holds head slot j = l % 16 of every accumulator. The score product
+// (v_mfma_f32_16x16x4_f32, one dimension per lane and instruction) gives lane
+// l the scores of tile rows q + 4 r (q = l / 16) when the key operand carries
+// tile row i / 4 + 4 (i % 4) at matrix row i; lane group q covers dimensions
+// [q D/4, (q + 1) D/4). The value product's k-th instruction takes rows
+// 4 k .. 4 k + 3 of the tile, weights straight from each lane's r = k score,
+// and output dimension MT i + m at matrix row i of output tile m
+// (MT = D / 16): a lane reads MT consecutive elements of a V row and ends
+// holding 4 MT consecutive output dimensions of its head.
+template <int D>
+__global__ __launch_bounds__(kPgBlock) void paged_attention_kernel(PgAttArgs a) {
+  constexpr int KQ = D / 4;   // dimensions per lane of the score product
+  constexpr int MT = D / 16;  // output tiles; V elements per lane and row
+  const uint32_t lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  const uint32_t j = lane % 16, qg = lane / 16;
+  const uint32_t item = blockIdx.x * kPgWaves + wave;
+  if (item >= uint32_t(a.items)) return;
+  const uint32_t g = item % uint32_t(a.Hkv), b = (item / uint32_t(a.Hkv)) % uint32_t(a.B);
+  const uint32_t layer = item / uint32_t(a.Hkv * a.B);
+  const PgLayer &P = a.L[layer];
+  const int G = a.Hq / a.Hkv;
+  const bool head = int(j) < G;
+  const int64_t s = int64_t(b) * a.Hkv + g;
+
+  // query operand: head slot j's dimensions of lane group qg, in binary32
+  float qf[KQ];
+  {
+    const uint64_t qrow = uint64_t(b) * a.Hq + g * G + (head ? j : 0);
+    const int qes = a.q_type == SWRT_XF_F32 ? 4 : 2;
+    const char *qp = P.q + qrow * uint64_t(D) * qes;
+    pg_load_decode<KQ>(a.q_type, qp, qg * KQ, 0, qf);
+#pragma unroll
+    for (int k = 0; k < KQ; ++k) qf[k] = head ? qf[k] : 0.0f;
+  }
+
+  float m = -INFINITY, l = 0.0f;
+  f32x4 acc[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int64_t ptr0 = __builtin_amdgcn_readfirstlane(P.page_ptr[s]);
+  const int64_t ptr1 = __builtin_amdgcn_readfirstlane(P.page_ptr[s + 1]);
+  bool ok = ptr0 >= 0 && ptr0 <= ptr1 && ptr1 <= P.n_ids;
+  if (ok && ptr1 > ptr0) {
+    // the last page fixes T and the window's first token r0
+    const int32_t last = __builtin_amdgcn_readfirstlane(P.page_ids[ptr1 - 1]);
+    ok = last >= 0 && last < P.n_pages;
+    int64_t T = 0, r0 = 0;
+    if (ok) {
+      const swrt_page lp = pg_read(P.pages, last);
+      ok = pg_page_ok(lp, D, P.arena_bytes);
+      T = lp.start + lp.length;
+      r0 = a.left_window < 0 ? 0 : (T - 1 - a.left_window > 0 ? T - 1 - a.left_window : 0);
+    }
+    // the first page the window reaches: walking back from the last page 64
+    // at a time, the nearest one starting at or before r0
+    int64_t kfirst = -1;
+    for (int64_t top = ptr1 - 1; ok && kfirst < 0; top -= 64) {
+      const int64_t k = top - lane;
+      const bool in = k >= ptr0;
+      const int32_t id = in ? P.page_ids[k] : 0;
+      const bool idok = !in || (id >= 0 && id < P.n_pages);
+      bool hit = false;
+      if (in && idok) hit = P.pages[id].start <= r0;
+      const uint64_t hits = __builtin_amdgcn_ballot_w64(hit);
+      const uint64_t bads = __builtin_amdgcn_ballot_w64(!idok);
+      if (hits) {
+        const int h = __builtin_ctzll(hits);
+        if (bads & ((2ull << h) - 1)) ok = false;  // a bad id among the pages to visit
+        kfirst = top - h;
+      } else if (bads || top - 63 <= ptr0) {
+        ok = false;  // a bad id, or no page starts at or before r0 (the first starts at 0)
+      }
+    }
+    // the visible pages in token order, 16-row tiles of each
+    const int32_t pk = (j >> 2) + 4 * (j & 3);  // tile row of this lane's key operand
+    int64_t expect = 0;
+    for (int64_t k = kfirst; ok && k < ptr1; ++k) {
+      const swrt_page p = pg_read(P.pages, P.page_ids[k]);
+      if (!pg_page_ok(p, D, P.arena_bytes) || (k > kfirst && p.start != expect) ||
+          (k == ptr0 && p.start != 0)) {
+        ok = false;
+        break;
+      }
+      expect = p.start + p.length;
+      const int64_t krow = pg_row_bytes(p.k_format, D), vrow = pg_row_bytes(p.v_format, D);
+      const char *kb = P.arena + p.k_offset;
+      const char *vb = P.arena + p.v_offset;
+      const bool ka = pg_affine(p.k_format), va = pg_affine(p.v_format);
+      const float ks = ka ? p.k_scale * a.scale_log2 : a.scale_log2;
+      const float vs = va ? p.v_scale : 1.0f;
+      const int32_t kz = ka ? p.k_zero_point : 0, vz = va ? p.v_zero_point : 0;
+      const int32_t len = p.length;
+      for (int32_t i = int32_t(r0 > p.start ? r0 - p.start : 0); i < len; i += 16) {
+        // this tile's K and V elements, decoded (rows past the page repeat
+        // its last row and are masked)
+        float kv[KQ];
+        pg_load_decode<KQ>(p.k_format, kb + int64_t(min(i + pk, len - 1)) * krow, qg * KQ, kz, kv);
+        float vv[4][MT];
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          pg_load_decode<MT>(p.v_format, vb + int64_t(min(i + 4 * c + int32_t(qg), len - 1)) * vrow,
+                             j * MT, vz, vv[c]);
+        float x[4];
+        float bm = -INFINITY;
+        {
+#pragma clang fp contract(off)
+          f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int k2 = 0; k2 < KQ; ++k2)
+            sc = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[k2], qf[k2], sc, 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            x[r] = i + int32_t(qg) + 4 * r < len ? sc[r] * ks : -INFINITY;
+            bm = fmaxf(bm, x[r]);
+          }
+        }
+        bm = fmaxf(bm, __shfl_xor(bm, 16));
+        bm = fmaxf(bm, __shfl_xor(bm, 32));
+        float pw[4];
+        {
+#pragma clang fp contract(off)
+          // the reference maximum moves only when a tile's exceeds it by more
+          // than 2^8 (log2 units); a single visible token still weighs 1
+          const bool move = bm > m + 8.0f;
+          const float mn = move ? bm : m;
+          if (__builtin_amdgcn_ballot_w64(move && m != -INFINITY)) {
+            const float f = move ? __builtin_amdgcn_exp2f(m - mn) : 1.0f;
+            l *= f;
+#pragma unroll
+            for (int t = 0; t < MT; ++t) acc[t] *= f;
+          }
+          const bool none = mn == -INFINITY;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float w = none ? 0.0f : __builtin_amdgcn_exp2f(x[r] - mn);
+            l += w;
+            pw[r] = w * vs;  // an affine page's V scale rides on the weight
+          }
+          m = mn;
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int t = 0; t < MT; ++t)
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv[c][t], pw[c], acc[t], 0, 0, 0);
+      }
+    }
+  }
+  if (!ok) {  // no output for this stream's heads
+    if (a.flags && lane == 0) atomicOr(a.flags, SWRT_FLAG_BAD_PAGES);
+    return;
+  }
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  if (!head) return;
+  const float inv = l > 0.0f ? 1.0f / l : 0.0f;  // no visible token: zeros
+  float y[4 * MT];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) y[MT * r + t] = acc[t][r] * inv;
+  const uint64_t orow = uint64_t(b) * a.Hq + g * G + j;
+  if (a.out_type == SWRT_XF_F32) {
+    u32x4 *dst = reinterpret_cast<u32x4 *>(P.out + (orow * D + 4 * MT * qg) * 4);
+#pragma unroll
+    for (int c = 0; c < MT; ++c)
+      dst[c] = u32x4{__float_as_uint(y[4 * c]), __float_as_uint(y[4 * c + 1]),
+                     __float_as_uint(y[4 * c + 2]), __float_as_uint(y[4 * c + 3])};
+  } else {
+    uint32_t h[2 * MT];
+#pragma unroll
+    for (int e = 0; e < 2 * MT; ++e) {
+      const uint32_t lo = a.out_type == SWRT_XF_BF16 ? xf_bf16(y[2 * e]) : xf_f16(y[2 * e]);
+      const uint32_t hi = a.out_type == SWRT_XF_BF16 ? xf_bf16(y[2 * e + 1]) : xf_f16(y[2 * e + 1]);
+      h[e] = lo | (hi << 16);
+    }
+    u32x4 *dst = reinterpret_cast<u32x4 *>(P.out + (orow * D + 4 * MT * qg) * 2);
+#pragma unroll
+    for (int c = 0; c < MT / 2; ++c) dst[c] = u32x4{h[4 * c], h[4 * c + 1], h[4 * c + 2], h[4 * c + 3]};
+  }
+}
+
+// ---------------------------------------------------------------------------
+// encoding eight consecutive elements (conversion and append)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int32_t pg_code(float y, float scale, int32_t zp, int32_t lo, int32_t hi) {
+  if (y != y) return zp;
+  float q = __builtin_rintf(y / scale) + float(zp);  // ties to even
+  q = fminf(fmaxf(q, float(lo)), float(hi));
+  return int32_t(q);
+}
+
+template <int FMT>
+__device__ __forceinline__ void pg_store8_t(char *dst, const float (&y)[8], float scale, int32_t zp) {
+  if constexpr (FMT == SWRT_XF_F32) {
+    uint32_t w[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w[e] = y[e] != y[e] ? 0x7FC00000u : __float_as_uint(y[e]);
+    __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]}, reinterpret_cast<u32x4 *>(dst));
+    __builtin_nontemporal_store(u32x4{w[4], w[5], w[6], w[7]}, reinterpret_cast<u32x4 *>(dst) + 1);
+  } else if constexpr (FMT == SWRT_XF_F16 || FMT == SWRT_XF_BF16) {
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t lo = FMT == SWRT_XF_BF16 ? xf_bf16(y[2 * e]) : xf_f16(y[2 * e]);
+      const uint32_t hi = FMT == SWRT_XF_BF16 ? xf_bf16(y[2 * e + 1]) : xf_f16(y[2 * e + 1]);
+      w[e] = lo | (hi << 16);
+    }
+    __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]}, reinterpret_cast<u32x4 *>(dst));
+  } else {
+    constexpr int B = pg_bits(FMT);
+    uint64_t packed = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t c = uint32_t(pg_code(y[e], scale, zp, pg_lo(FMT), pg_hi(FMT))) & ((1u << B) - 1u);
+      packed |= uint64_t(c) << (e * B);
+    }
+    if constexpr (B == 8) {
+      __builtin_nontemporal_store(u32x2{uint32_t(packed), uint32_t(packed >> 32)},
+                                  reinterpret_cast<u32x2 *>(dst));
+    } else if constexpr (B == 4) {
+      __builtin_nontemporal_store(uint32_t(packed), reinterpret_cast<uint32_t *>(dst));
+    } else {
+      __builtin_nontemporal_store(uint16_t(packed), reinterpret_cast<uint16_t *>(dst));
+    }
+  }
+}
+
+__device__ __forceinline__ void pg_store8(int fmt, char *dst, const float (&y)[8], float scale,
+                                          int32_t zp) {
+  switch (fmt) {
+    case SWRT_XF_F32: pg_store8_t<SWRT_XF_F32>(dst, y, scale, zp); break;
+    case SWRT_XF_F16: pg_store8_t<SWRT_XF_F16>(dst, y, scale, zp); break;
+    case SWRT_XF_BF16: pg_store8_t<SWRT_XF_BF16>(dst, y, scale, zp); break;
+    case SWRT_XF_INT8: pg_store8_t<SWRT_XF_INT8>(dst, y, scale, zp); break;
+    case SWRT_XF_UINT8: pg_store8_t<SWRT_XF_UINT8>(dst, y, scale, zp); break;
+    case SWRT_XF_INT4: pg_store8_t<SWRT_XF_INT4>(dst, y, scale, zp); break;
+    case SWRT_XF_UINT4: pg_store8_t<SWRT_XF_UINT4>(dst, y, scale, zp); break;
+    case SWRT_XF_INT2: pg_store8_t<SWRT_XF_INT2>(dst, y, scale, zp); break;
+    default: pg_store8_t<SWRT_XF_UINT2>(dst, y, scale, zp); break;
+  }
+}
+
+// eight elements of a page row decoded in binary32: dense as is, affine as
+// fl((c - zp) * scale), one rounding
+__device__ __forceinline__ void pg_value8(int fmt, const char *row, uint32_t first, float scale,
+                                          int32_t zp, float (&y)[8]) {
+  pg_load_decode<8>(fmt, row, first, pg_affine(fmt) ? zp : 0, y);
+  if (pg_affine(fmt)) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = y[e] * scale;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// conversion of selected pages
+// ---------------------------------------------------------------------------
+struct PgConvArgs {
+  char *arena;
+  int64_t arena_bytes;
+  const swrt_page *pages_in;
+  swrt_page *pages_out;
+  int64_t n_pages;
+  const int32_t *blocks;
+  int64_t n_blocks;
+  const int64_t *dst;
+  int64_t free_begin, free_end;
+  uint32_t *flags;
+  int32_t fmt[2];
+  float scale[2];  // 1 for a dense target
+  int32_t zp[2];   // 0 for a dense target
+  int32_t D;
+};
+
+__device__ __forceinline__ bool pg_overlap(int64_t a0, int64_t n0, int64_t a1, int64_t n1) {
+  return n0 > 0 && n1 > 0 && a0 < a1 + n1 && a1 < a0 + n0;
+}
+
+// every page, and every selected block with its destinations
+__global__ __launch_bounds__(kPgBlock) void paged_validate_kernel(PgConvArgs a) {
+  const int64_t n = a.n_pages + a.n_blocks;
+  bool bad = false;
+  for (int64_t x = int64_t(blockIdx.x) * kPgBlock + threadIdx.x; x < n;
+       x += int64_t(gridDim.x) * kPgBlock) {
+    if (x < a.n_pages) {
+      const swrt_page p = a.pages_in[x];
+      const int64_t fr = a.free_end - a.free_begin;
+      bad |= !pg_page_ok(p, a.D, a.arena_bytes) ||
+             pg_overlap(a.free_begin, fr, p.k_offset, p.capacity * pg_row_bytes(p.k_format, a.D)) ||
+             pg_overlap(a.free_begin, fr, p.v_offset, p.capacity * pg_row_bytes(p.v_format, a.D));
+    } else {
+      const int64_t i = x - a.n_pages;
+      const int32_t id = a.blocks[i];
+      if (id < 0 || id >= a.n_pages || (i > 0 && id <= a.blocks[i - 1])) {
+        bad = true;
+        continue;
+      }
+      const int64_t cap = a.pages_in[id].capacity;
+      int64_t prev_end = a.free_begin;  // where this block's K may start
+      if (i > 0) {
+        const int32_t pid = a.blocks[i - 1];
+        if (pid < 0 || pid >= a.n_pages) {
+          bad = true;
+          continue;
+        }
+        prev_end = a.dst[2 * i - 1] + a.pages_in[pid].capacity * pg_row_bytes(a.fmt[1], a.D);
+      }
+      const int64_t kb = cap * pg_row_bytes(a.fmt[0], a.D), vb = cap * pg_row_bytes(a.fmt[1], a.D);
+      const int64_t dk = a.dst[2 * i], dv = a.dst[2 * i + 1];
+      bad |= cap < 1 || dk < prev_end || (dk & 15) != 0 || kb > a.free_end - dk ||
+             dv < dk + kb || (dv & 15) != 0 || vb > a.free_end - dv;
+    }
+  }
+  if (bad) atomicOr(a.flags, SWRT_FLAG_BAD_PAGES);
+}
+
+// one wave per (selected block, K or V): every row of the capacity, eight
+// elements per lane step; rows past the page's length are logical zeros
+__global__ __launch_bounds__(64) void paged_convert_kernel(PgConvArgs a) {
+  if (__atomic_load_n(a.flags, __ATOMIC_RELAXED) & SWRT_FLAG_BAD_PAGES) return;
+  const int64_t i = blockIdx.x / 2;
+  const int t = blockIdx.x % 2;
+  const swrt_page p = pg_read(a.pages_in, a.blocks[i]);
+  const int sf = t ? p.v_format : p.k_format;
+  const float ss = t ? p.v_scale : p.k_scale;
+  const int32_t sz = t ? p.v_zero_point : p.k_zero_point;
+  const int df = a.fmt[t];
+  const int64_t srow = pg_row_bytes(sf, a.D), drow = pg_row_bytes(df, a.D);
+  const char *src = a.arena + (t ? p.v_offset : p.k_offset);
+  char *dst = a.arena + a.dst[2 * i + t];
+  const int32_t per_row = a.D / 8;
+  const int64_t n = int64_t(p.capacity) * per_row;
+  for (int64_t o = threadIdx.x; o < n; o += 64) {
+    const int64_t r = o / per_row;
+    const uint32_t e0 = uint32_t(o % per_row) * 8;
+    float y[8];
+    if (r < p.length) {
+      pg_value8(sf, src + r * srow, e0, ss, sz, y);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = 0.0f;
+    }
+    pg_store8(df, dst + r * drow + int64_t(e0) * pg_bits(df) / 8, y, a.scale[t], a.zp[t]);
+  }
+}
+
+// every descriptor to pages_out, the selected ones with their new storage
+__global__ __launch_bounds__(kPgBlock) void paged_publish_kernel(PgConvArgs a) {
+  if (__atomic_load_n(a.flags, __ATOMIC_RELAXED) & SWRT_FLAG_BAD_PAGES) return;
+  for (int64_t x = int64_t(blockIdx.x) * kPgBlock + threadIdx.x; x < a.n_pages;
+       x += int64_t(gridDim.x) * kPgBlock) {
+    swrt_page p = a.pages_in[x];
+    // blocks are ascending: binary search for x
+    int64_t lo = 0, hi = a.n_blocks;
+    while (lo < hi) {
+      const int64_t mid = (lo + hi) / 2;
+      if (a.blocks[mid] < x)
+        lo = mid + 1;
+      else
+        hi = mid;
+    }
+    if (lo < a.n_blocks && a.blocks[lo] == x) {
+      p.k_format = a.fmt[0];
+      p.v_format = a.fmt[1];
+      p.k_scale = a.scale[0];
+      p.v_scale = a.scale[1];
+      p.k_zero_point = a.zp[0];
+      p.v_zero_point = a.zp[1];
+      p.k_offset = a.dst[2 * lo];
+      p.v_offset = a.dst[2 * lo + 1];
+    }
+    a.pages_out[x] = p;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// append
+// ---------------------------------------------------------------------------
+struct PgAppArgs {
+  PgLayer L[kMaxLayers];
+  const char *k_new[kMaxLayers];
+  const char *v_new[kMaxLayers];
+  int32_t table[kMaxLayers];  // layers whose block tables are distinct
+  uint32_t *flags;
+  int32_t n_streams, n_tables, D, new_type, items;
+};
+
+// the page stream s's token goes to, and whether it can take it
+__device__ __forceinline__ uint32_t pg_append_target(const PgLayer &P, int64_t s, int D, int32_t &id,
+                                                     swrt_page &p) {
+  const int64_t ptr0 = __builtin_amdgcn_readfirstlane(P.page_ptr[s]);
+  const int64_t ptr1 = __builtin_amdgcn_readfirstlane(P.page_ptr[s + 1]);
+  if (ptr0 < 0 || ptr1 <= ptr0 || ptr1 > P.n_ids) return SWRT_FLAG_BAD_PAGES;
+  id = __builtin_amdgcn_readfirstlane(P.page_ids[ptr1 - 1]);
+  if (id < 0 || id >= P.n_pages) return SWRT_FLAG_BAD_PAGES;
+  p = pg_read(P.pages, id);
+  if (!pg_page_ok(p, D, P.arena_bytes)) return SWRT_FLAG_BAD_PAGES;
+  return p.length == p.capacity ? SWRT_FLAG_PAGE_FULL : 0u;
+}
+
+// one wave per (layer, stream): the new K and V rows, encoded, as row
+// `length` of the stream's last page
+__global__ __launch_bounds__(kPgBlock) void paged_append_rows_kernel(PgAppArgs a) {
+  const uint32_t lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  const uint32_t item = blockIdx.x * kPgWaves + wave;
+  if (item >= uint32_t(a.items)) return;
+  const int64_t s = item % uint32_t(a.n_streams);
+  const uint32_t layer = item / uint32_t(a.n_streams);
+  const PgLayer &P = a.L[layer];
+  int32_t id;
+  swrt_page p;
+  const uint32_t bad = pg_append_target(P, s, a.D, id, p);
+  if (bad) {
+    if (a.flags && lane == 0) atomicOr(a.flags, bad);
+    return;
+  }
+  const int nes = a.new_type == SWRT_XF_F32 ? 4 : 2;
+  for (int t = 0; t < 2; ++t) {
+    const int fmt = t ? p.v_format : p.k_format;
+    const float sc = t ? p.v_scale : p.k_scale;
+    const int32_t zp = t ? p.v_zero_point : p.k_zero_point;
+    const char *in = (t ? a.v_new[layer] : a.k_new[layer]) + s * a.D * nes;
+    char *row = const_cast<char *>(P.arena) + (t ? p.v_offset : p.k_offset) +
+                int64_t(p.length) * pg_row_bytes(fmt, a.D);
+    for (int e0 = int(lane) * 8; e0 < a.D; e0 += 64 * 8) {
+      float y[8];
+      pg_load_decode<8>(a.new_type, in, uint32_t(e0), 0, y);
+      pg_store8(fmt, row + int64_t(e0) * pg_bits(fmt) / 8, y, sc, zp);
+    }
+  }
+}
+
+// after every layer's rows: each distinct block table's appended pages grow
+// by one row (the same checks decide, on the same descriptors)
+__global__ __launch_bounds__(kPgBlock) void paged_append_commit_kernel(PgAppArgs a) {
+  const int64_t x = int64_t(blockIdx.x) * kPgBlock + threadIdx.x;
+  if (x >= int64_t(a.n_tables) * a.n_streams) return;
+  const PgLayer &P = a.L[a.table[x / a.n_streams]];
+  const int64_t s = x % a.n_streams;
+  const int64_t ptr0 = P.page_ptr[s], ptr1 = P.page_ptr[s + 1];
+  if (ptr0 < 0 || ptr1 <= ptr0 || ptr1 > P.n_ids) return;
+  const int32_t id = P.page_ids[ptr1 - 1];
+  if (id < 0 || id >= P.n_pages) return;
+  swrt_page *pg = const_cast<swrt_page *>(P.pages) + id;
+  if (pg_page_ok(*pg, a.D, P.arena_bytes) && pg->length < pg->capacity) pg->length += 1;
+}
+
+// ---------------------------------------------------------------------------
+// host
+// ---------------------------------------------------------------------------
+bool pg_q_type_ok(int t) { return t == SWRT_XF_F32 || t == SWRT_XF_F16 || t == SWRT_XF_BF16; }
+
+// the per-layer fields the kernels read, checked for what the host can see
+int pg_layers(int n_layers, const swrt_paged_layer *layers, PgLayer *out, bool attention,
+              int64_t n_streams) {
+  for (int l = 0; l < n_layers; ++l) {
+    const swrt_paged_layer &x = layers[l];
+    if (!x.arena || !x.pages || !x.page_ptr || (x.n_ids > 0 && !x.page_ids)) return SWRT_E_INVALID_ARG;
+    if (x.arena_bytes < 0 || x.n_pages < 0 || x.n_ids < 0 || x.n_pages > INT32_MAX)
+      return SWRT_E_INVALID_ARG;
+    if (addr_of(x.arena) % 16 || addr_of(x.pages) % 8 || addr_of(x.page_ptr) % 4 ||
+        addr_of(x.page_ids) % 4)
+      return SWRT_E_INVALID_ARG;
+    if (attention && (!x.q || !x.out || addr_of(x.q) % 16 || addr_of(x.out) % 16))
+      return SWRT_E_INVALID_ARG;
+    out[l] = PgLayer{static_cast<const char *>(x.q), static_cast<char *>(x.out),
+                     static_cast<const char *>(x.arena), x.arena_bytes, x.pages, x.n_pages,
+                     x.page_ptr, x.page_ids, x.n_ids};
+    (void)n_streams;
+  }
+  return SWRT_OK;
+}
+
+}  // namespace
+}  // namespace swrt
+
+using namespace swrt;
+
+extern "C" int swrt_paged_attention(int n_layers, const swrt_paged_layer *layers,
+                                    int64_t left_window, int batch, int q_heads, int kv_heads,
+                                    int head_dim, float scale, int q_type, int out_type,
+                                    uint32_t *d_flags, void *stream) {
+  if (n_layers < 0 || n_layers > kMaxLayers || batch < 0 || q_heads < 0 || kv_heads < 1)
+    return SWRT_E_INVALID_ARG;
+  if (!pg_q_type_ok(q_type) || !pg_q_type_ok(out_type) || q_heads % kv_heads)
+    return SWRT_E_INVALID_ARG;
+  if (!(scale == scale) || scale > 3.4028235e38f || scale < -3.4028235e38f) return SWRT_E_INVALID_ARG;
+  if (head_dim != 32 && head_dim != 64 && head_dim != 128 && head_dim != 256)
+    return SWRT_E_UNSUPPORTED;
+  if (q_heads / kv_heads > 16) return SWRT_E_UNSUPPORTED;
+  if (n_layers == 0 || batch == 0 || q_heads == 0) return SWRT_OK;
+  if (!layers || addr_of(d_flags) % 4) return SWRT_E_INVALID_ARG;
+  if (uint64_t(n_layers) * batch * kv_heads >= (uint64_t(1) << 31)) return SWRT_E_UNSUPPORTED;
+  PgAttArgs a;
+  const int st = pg_layers(n_layers, layers, a.L, true, int64_t(batch) * kv_heads);
+  if (st != SWRT_OK) return st;
+  // outputs must not overlap any input of the call
+  Range ranges[6 * kMaxLayers + 1];
+  int nr = 0;
+  const int64_t qes = q_type == SWRT_XF_F32 ? 4 : 2, oes = out_type == SWRT_XF_F32 ? 4 : 2;
+  const int64_t rows = int64_t(batch) * q_heads * head_dim;
+  for (int l = 0; l < n_layers; ++l) {
+    const swrt_paged_layer &x = layers[l];
+    ranges[nr++] = range(x.q, uint64_t(rows * qes), false);
+    ranges[nr++] = range(x.out, uint64_t(rows * oes), true);
+    ranges[nr++] = range(x.arena, uint64_t(x.arena_bytes), false);
+    ranges[nr++] = range(x.pages, uint64_t(x.n_pages) * sizeof(swrt_page), false);
+    ranges[nr++] = range(x.page_ptr, uint64_t(int64_t(batch) * kv_heads + 1) * 4, false);
+    ranges[nr++] = range(x.page_ids, uint64_t(x.n_ids) * 4, false);
+  }
+  ranges[nr++] = range(d_flags, 4, true);
+  if (written_overlap(ranges, nr)) return SWRT_E_INVALID_ARG;
+  a.flags = d_flags;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.left_window = left_window;
+  a.B = batch;
+  a.Hq = q_heads;
+  a.Hkv = kv_heads;
+  a.items = n_layers * batch * kv_heads;
+  a.q_type = q_type;
+  a.out_type = out_type;
+  static_assert(sizeof(PgAttArgs) <= 4096, "kernel arguments exceed 4 KiB");
+  const dim3 grid((uint32_t(a.items) + kPgWaves - 1) / kPgWaves);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (head_dim) {
+    case 32: hipLaunchKernelGGL(paged_attention_kernel<32>, grid, dim3(kPgBlock), 0, s, a); break;
+    case 64: hipLaunchKernelGGL(paged_attention_kernel<64>, grid, dim3(kPgBlock), 0, s, a); break;
+    case 128: hipLaunchKernelGGL(paged_attention_kernel<128>, grid, dim3(kPgBlock), 0, s, a); break;
+    default: hipLaunchKernelGGL(paged_attention_kernel<256>, grid, dim3(kPgBlock), 0, s, a); break;
+  }
+  return launch_status();
+}
+
+extern "C" int swrt_paged_quantize(void *arena, int64_t arena_bytes, const swrt_page *pages_in,
+                                   int64_t n_pages, const int32_t *blocks, int64_t n_blocks,
+                                   const int64_t *dst_offsets, int64_t free_begin,
+                                   int64_t free_end, swrt_page *pages_out, int k_format,
+                                   float k_scale, int32_t k_zero_point, int v_format,
+                                   float v_scale, int32_t v_zero_point, int head_dim,
+                                   uint32_t *d_flags, void *stream) {
+  if (n_pages < 0 || n_blocks < 0 || arena_bytes < 0 || head_dim < 16 || head_dim % 16 ||
+      head_dim > 4096)
+    return SWRT_E_INVALID_ARG;
+  if (!pg_format_ok(k_format, k_scale, k_zero_point) || !pg_format_ok(v_format, v_scale, v_zero_point))
+    return SWRT_E_INVALID_ARG;
+  if (free_begin < 0 || free_end < free_begin || free_end > arena_bytes) return SWRT_E_INVALID_ARG;
+  if (!d_flags || addr_of(d_flags) % 4) return SWRT_E_INVALID_ARG;
+  if (n_pages > INT32_MAX || n_blocks > n_pages) return SWRT_E_INVALID_ARG;
+  if (n_pages == 0) return SWRT_OK;
+  if (!arena || !pages_in || !pages_out || (n_blocks > 0 && (!blocks || !dst_offsets)))
+    return SWRT_E_INVALID_ARG;
+  if (addr_of(arena) % 16 || addr_of(pages_in) % 8 || addr_of(pages_out) % 8 ||
+      addr_of(blocks) % 4 || addr_of(dst_offsets) % 8)
+    return SWRT_E_INVALID_ARG;
+  // descriptors and the flag word are written: they overlap no input other
+  // than pages_out == pages_in
+  Range ranges[6];
+  int nr = 0;
+  ranges[nr++] = range(arena, uint64_t(arena_bytes), true);
+  if (pages_out != pages_in) ranges[nr++] = range(pages_in, uint64_t(n_pages) * sizeof(swrt_page), false);
+  ranges[nr++] = range(pages_out, uint64_t(n_pages) * sizeof(swrt_page), true);
+  ranges[nr++] = range(blocks, uint64_t(n_blocks) * 4, false);
+  ranges[nr++] = range(dst_offsets, uint64_t(n_blocks) * 16, false);
+  ranges[nr++] = range(d_flags, 4, true);
+  if (written_overlap(ranges, nr)) return SWRT_E_INVALID_ARG;
+  PgConvArgs a;
+  a.arena = static_cast<char *>(arena);
+  a.arena_bytes = arena_bytes;
+  a.pages_in = pages_in;
+  a.pages_out = pages_out;
+  a.n_pages = n_pages;
+  a.blocks = blocks;
+  a.n_blocks = n_blocks;
+  a.dst = dst_offsets;
+  a.free_begin = free_begin;
+  a.free_end = free_end;
+  a.flags = d_flags;
+  a.fmt[0] = k_format;
+  a.fmt[1] = v_format;
+  a.scale[0] = pg_affine(k_format) ? k_scale : 1.0f;
+  a.scale[1] = pg_affine(v_format) ? v_scale : 1.0f;
+  a.zp[0] = pg_affine(k_format) ? k_zero_point : 0;
+  a.zp[1] = pg_affine(v_format) ? v_zero_point : 0;
+  a.D = head_dim;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t nv = n_pages + n_blocks;
+  const uint32_t gv = uint32_t(std::min<int64_t>((nv + kPgBlock - 1) / kPgBlock, 4096));
+  hipLaunchKernelGGL(paged_validate_kernel, dim3(gv), dim3(kPgBlock), 0, s, a);
+  int st = launch_status();
+  if (st != SWRT_OK) return st;
+  if (n_blocks > 0) {
+    if (n_blocks > (int64_t(1) << 30)) return SWRT_E_UNSUPPORTED;
+    hipLaunchKernelGGL(paged_convert_kernel, dim3(uint32_t(2 * n_blocks)), dim3(64), 0, s, a);
+    st = launch_status();
+    if (st != SWRT_OK) return st;
+  }
+  const uint32_t gp = uint32_t(std::min<int64_t>((n_pages + kPgBlock - 1) / kPgBlock, 4096));
+  hipLaunchKernelGGL(paged_publish_kernel, dim3(gp), dim3(kPgBlock), 0, s, a);
+  return launch_status();
+}
+
+extern "C" int swrt_paged_append(int n_layers, const swrt_paged_layer *layers,
+                                 const void *const *k_new, const void *const *v_new, int new_type,
+                                 int n_streams, int head_dim, uint32_t *d_flags, void *stream) {
+  if (n_layers < 0 || n_layers > kMaxLayers || n_streams < 0 || !pg_q_type_ok(new_type))
+    return SWRT_E_INVALID_ARG;
+  if (head_dim < 16 || head_dim % 16 || head_dim > 4096) return SWRT_E_INVALID_ARG;
+  if (n_layers == 0 || n_streams == 0) return SWRT_OK;
+  if (!layers || !k_new || !v_new || addr_of(d_flags) % 4) return SWRT_E_INVALID_ARG;
+  if (uint64_t(n_layers) * n_streams >= (uint64_t(1) << 31)) return SWRT_E_UNSUPPORTED;
+  PgAppArgs a;
+  const int st = pg_layers(n_layers, layers, a.L, false, n_streams);
+  if (st != SWRT_OK) return st;
+  // block tables: a layer either has its own (descriptors, page_ptr and
+  // page_ids apart from every other layer's) or shares all three with an
+  // earlier layer; the lengths of each distinct table grow once
+  a.n_tables = 0;
+  for (int l = 0; l < n_layers; ++l) {
+    int same = -1;
+    for (int e = 0; e < l; ++e) {
+      const swrt_paged_layer &x = layers[e], &y = layers[l];
+      if (x.pages == y.pages && x.page_ptr == y.page_ptr && x.page_ids == y.page_ids &&
+          x.n_pages == y.n_pages && x.n_ids == y.n_ids) {
+        same = e;
+        break;
+      }
+    }
+    if (same < 0) a.table[a.n_tables++] = l;
+  }
+  const int64_t nes = new_type == SWRT_XF_F32 ? 4 : 2;
+  Range ranges[7 * kMaxLayers + 1];
+  int nr = 0;
+  for (int l = 0; l < n_layers; ++l) {
+    const swrt_paged_layer &x = layers[l];
+    if (!k_new[l] || !v_new[l] || addr_of(k_new[l]) % 16 || addr_of(v_new[l]) % 16)
+      return SWRT_E_INVALID_ARG;
+    a.k_new[l] = static_cast<const char *>(k_new[l]);
+    a.v_new[l] = static_cast<const char *>(v_new[l]);
+    ranges[nr++] = range(x.arena, uint64_t(x.arena_bytes), true);
+    ranges[nr++] = range(k_new[l], uint64_t(n_streams) * head_dim * nes, false);
+    ranges[nr++] = range(v_new[l], uint64_t(n_streams) * head_dim * nes, false);
+  }
+  for (int t = 0; t < a.n_tables; ++t) {  // each distinct table once
+    const swrt_paged_layer &x = layers[a.table[t]];
+    ranges[nr++] = range(x.pages, uint64_t(x.n_pages) * sizeof(swrt_page), true);
+    ranges[nr++] = range(x.page_ptr, uint64_t(n_streams + 1) * 4, false);
+    ranges[nr++] = range(x.page_ids, uint64_t(x.n_ids) * 4, false);
+  }
+  ranges[nr++] = range(d_flags, 4, true);
+  if (written_overlap(ranges, nr)) return SWRT_E_INVALID_ARG;
+  a.flags = d_flags;
+  a.n_streams = n_streams;
+  a.D = head_dim;
+  a.new_type = new_type;
+  a.items = n_layers * n_streams;
+  static_assert(sizeof(PgAppArgs) <= 4096, "kernel arguments exceed 4 KiB");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(paged_append_rows_kernel, dim3((uint32_t(a.items) + kPgWaves - 1) / kPgWaves),
+                     dim3(kPgBlock), 0, s, a);
+  const int st2 = launch_status();
+  if (st2 != SWRT_OK) return st2;
+  const int64_t nc = int64_t(a.n_tables) * n_streams;
+  hipLaunchKernelGGL(paged_append_commit_kernel, dim3(uint32_t((nc + kPgBlock - 1) / kPgBlock)),
+                     dim3(kPgBlock), 0, s, a);
+  return launch_status();
+}

@@ -325,13 +325,15 @@ class PagedCase:
 
 
 def paged_case(g: np.random.Generator, head_dim: int, streams, page_format, *,
-               spare_bytes: int = 0, align: int = 16) -> PagedCase:
+               spare_bytes: int = 0, align: int = 16,
+               payload_rng: np.random.Generator | None = None) -> PagedCase:
     """A paged cache: ``streams`` lists, per stream, its pages as (length,
     capacity) in token order; ``page_format(stream, page, n_pages)`` gives a
     page's (k_format, v_format, k_scale, v_scale, k_zero_point, v_zero_point).
     Pages sit in the arena in a shuffled order at ``align``-byte offsets; dense
     payloads hold U[-1, 1) values rounded to their type, affine payloads
-    uniform random bytes (every row of the capacity is filled, valid or not)."""
+    uniform random bytes (every row of the capacity is filled, valid or not),
+    drawn from ``payload_rng`` when given (the same layout with other bytes)."""
     recs = []
     for s, pages in enumerate(streams):
         start = 0
@@ -344,16 +346,17 @@ def paged_case(g: np.random.Generator, head_dim: int, streams, page_format, *,
     order = g.permutation(len(recs))
     off = 0
     chunks = []
+    pg = g if payload_rng is None else payload_rng
 
     def place(fmt, cap):
         nonlocal off
         nbytes = cap * head_dim * FORMAT_BITS[fmt] // 8
         o = off
         if fmt in _DENSE:
-            vals = torch.from_numpy(g.uniform(-1, 1, size=cap * head_dim).astype(np.float32))
+            vals = torch.from_numpy(pg.uniform(-1, 1, size=cap * head_dim).astype(np.float32))
             raw = vals.to(_DENSE[fmt]).view(torch.uint8).numpy()
         else:
-            raw = g.integers(0, 256, size=nbytes, dtype=np.uint8)
+            raw = pg.integers(0, 256, size=nbytes, dtype=np.uint8)
         chunks.append((o, raw))
         off += -(-nbytes // align) * align
         return o

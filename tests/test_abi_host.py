@@ -49,7 +49,8 @@ def test_exports_every_declared_function(L):
     assert {"swrt_tensor_scatter", "swrt_tensor_scatter_batched", "swrt_kv_seq_lengths", "swrt_kv_window_append",
             "swrt_kv_window_append_layers", "swrt_kv_decode_step", "swrt_kv_seq_lengths_drift",
             "swrt_kv_window_append_xf", "swrt_tensor_scatter_xf", "swrt_kv_decode_step_xf",
-            "swrt_window_attention", "swrt_status_string",
+            "swrt_window_attention", "swrt_paged_attention", "swrt_paged_quantize",
+            "swrt_paged_append", "swrt_status_string",
             "swrt_abi_version"} <= declared
     out = subprocess.run(["nm", "-D", "--defined-only", swrt.LIBRARY], check=True,
                          capture_output=True, text=True).stdout
@@ -72,7 +73,10 @@ def test_constants_agree():
           "SWRT_FLAG_ROPE_RANGE": swrt.FLAG_ROPE_RANGE,
           "SWRT_XF_F32": swrt.XF_TYPES[torch.float32], "SWRT_XF_F16": swrt.XF_TYPES[torch.float16],
           "SWRT_XF_BF16": swrt.XF_TYPES[torch.bfloat16], "SWRT_XF_INT8": swrt.XF_TYPES[torch.int8],
-          "SWRT_XF_UINT8": swrt.XF_TYPES[torch.uint8]}
+          "SWRT_XF_UINT8": swrt.XF_TYPES[torch.uint8],
+          "SWRT_XF_INT4": swrt.PAGE_FORMATS["int4"], "SWRT_XF_UINT4": swrt.PAGE_FORMATS["uint4"],
+          "SWRT_XF_INT2": swrt.PAGE_FORMATS["int2"], "SWRT_XF_UINT2": swrt.PAGE_FORMATS["uint2"],
+          "SWRT_FLAG_BAD_PAGES": swrt.FLAG_BAD_PAGES, "SWRT_FLAG_PAGE_FULL": swrt.FLAG_PAGE_FULL}
     for k, v in py.items():
         assert int(defs[k]) == v, k
     # the oracle defines its own values; they must mean the same bits
@@ -86,6 +90,13 @@ def test_constants_agree():
     # the two transform structs have the same field layout
     assert [f[0] for f in oracle.RowXf._fields_] == [f[0] for f in swrt.RowTransform._fields_]
     assert ctypes.sizeof(oracle.RowXf) == ctypes.sizeof(swrt.RowTransform)
+    # page formats, flags and the descriptor layout
+    assert {k: oracle_v for k, oracle_v in (("int4", oracle.XF_INT4), ("uint4", oracle.XF_UINT4),
+                                            ("int2", oracle.XF_INT2), ("uint2", oracle.XF_UINT2))} \
+        == {k: swrt.PAGE_FORMATS[k] for k in ("int4", "uint4", "int2", "uint2")}
+    assert (oracle.FLAG_BAD_PAGES, oracle.FLAG_PAGE_FULL) == (swrt.FLAG_BAD_PAGES, swrt.FLAG_PAGE_FULL)
+    assert oracle.PAGE_DTYPE == swrt.PAGE_DTYPE and swrt.PAGE_DTYPE.itemsize == 64
+    assert ctypes.sizeof(swrt.PagedLayer) == 72
     assert (oracle.MODE_LINEAR, oracle.MODE_CIRCULAR) == (swrt.MODE_LINEAR, swrt.MODE_CIRCULAR)
     assert (oracle.PHASE_STAGE, oracle.PHASE_COMMIT, oracle.PHASE_ALL) == \
         (swrt.PHASE_STAGE, swrt.PHASE_COMMIT, swrt.PHASE_ALL)

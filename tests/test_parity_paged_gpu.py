@@ -1,0 +1,413 @@
+"""GPU parity of the paged caches against the oracle.
+
+Conversion (swrt_paged_quantize) and append (swrt_paged_append) decide every
+byte in binary32 on both sides: whole arenas and descriptor tables are
+compared byte for byte. Attention (swrt_paged_attention) reduces in fp32
+against the oracle's float64 and is held, per batch entry and head, to the
+bound of the windowed attention's tests with the paged kernel's extra
+roundings (u = 2^-24; S1 = |scale| * max over visible tokens of
+sum_d |q_d k_d|, Vmax = max |v| over them, decoded; n = visible tokens):
+
+  |gpu - oracle| <= 4 * (2 * ((D + 4) u S1 + 2^-21) + (3 n + 64) u) * Vmax
+                    (+ one output ulp)
+
+The score adds the rounding of the page's K scale folded into the softmax
+scale, each weight the rounding of the page's V scale (3 n instead of 2 n).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sliding_window_ring_tensor_amd as swrt
+from sliding_window_ring_tensor_amd import workloads as wl
+from tests.test_parity_gpu import DEV, flag_word, say
+
+pytestmark = pytest.mark.gpu
+U = 2.0 ** -24
+F32, F16, BF16, I8, U8, I4, U4, I2, U2 = 1, 2, 3, 4, 5, 6, 7, 8, 9
+ALL_FORMATS = [F32, F16, BF16, I8, U8, I4, U4, I2, U2]
+QT = {torch.float32: oracle.XF_F32, torch.float16: oracle.XF_F16, torch.bfloat16: oracle.XF_BF16}
+ULP = {torch.float32: 0.0, torch.float16: 2.0 ** -10, torch.bfloat16: 2.0 ** -8}
+RANGES = {I8: (-128, 127), U8: (0, 255), I4: (-8, 7), U4: (0, 15), I2: (-2, 1), U2: (0, 3)}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    swrt.lib()
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.get()
+
+
+def otable(case) -> np.ndarray:
+    t = np.zeros(case.n_pages, oracle.PAGE_DTYPE)
+    for f in wl.PAGE_FIELDS:
+        t[f] = case.fields[f]
+    return t
+
+
+def upload(case, table=None) -> swrt.PagedCache:
+    tb = swrt.page_table(case.fields) if table is None else table.view(swrt.PAGE_DTYPE)
+    return swrt.PagedCache.upload(tb, case.page_ptr, case.page_ids, case.arena, DEV)
+
+
+def random_format(g, formats=ALL_FORMATS):
+    def pick(s, i, n):
+        kf, vf = (int(f) for f in g.choice(formats, 2))
+        ks, vs = (float(np.float32(x)) for x in g.uniform(0.01, 0.3, 2))
+        kz = int(g.integers(*RANGES[kf], endpoint=True)) if kf in RANGES else 0
+        vz = int(g.integers(*RANGES[vf], endpoint=True)) if vf in RANGES else 0
+        return (kf, vf, ks if kf in RANGES else 1.0, vs if vf in RANGES else 1.0, kz, vz)
+    return pick
+
+
+def decode_rows(arena, page, D, kv):
+    """float64 values of a page's valid rows (numpy bit unpacking, for the bound)."""
+    fmt = int(page[kv + "_format"])
+    bits = oracle.PAGE_BITS[fmt]
+    n, off = int(page["length"]), int(page[kv + "_offset"])
+    raw = arena[off:off + n * D * bits // 8]
+    if fmt == F32:
+        return raw.view(np.float32).astype(np.float64).reshape(n, D)
+    if fmt == F16:
+        return raw.view(np.float16).astype(np.float64).reshape(n, D)
+    if fmt == BF16:
+        return (raw.view(np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64) \
+            .reshape(n, D)
+    codes = (np.unpackbits(raw, bitorder="little").reshape(-1, bits) *
+             (1 << np.arange(bits))).sum(axis=1).astype(np.int64)
+    if fmt in (I8, I4, I2):
+        codes = np.where(codes >= 1 << (bits - 1), codes - (1 << bits), codes)
+    return ((codes - int(page[kv + "_zero_point"])) * float(page[kv + "_scale"])).reshape(n, D)
+
+
+def bound(case, tb, q, Hkv, left_window, scale, out_dtype, ref):
+    qd = q.detach().cpu().to(torch.float64).numpy()
+    B, Hq, D = qd.shape
+    G = Hq // Hkv
+    tol = np.zeros((B, Hq, 1))
+    for b in range(B):
+        for g in range(Hkv):
+            s = b * Hkv + g
+            ids = case.page_ids[case.page_ptr[s]:case.page_ptr[s + 1]]
+            if len(ids) == 0:
+                continue
+            k = np.concatenate([decode_rows(case.arena, tb[i], D, "k") for i in ids])
+            v = np.concatenate([decode_rows(case.arena, tb[i], D, "v") for i in ids])
+            T = len(k)
+            r0 = 0 if left_window < 0 else max(0, T - 1 - left_window)
+            k, v = k[r0:], v[r0:]
+            for h in range(g * G, (g + 1) * G):
+                s1 = abs(scale) * np.abs(qd[b, h][None, :] * k).sum(axis=1).max()
+                tol[b, h] = 4 * (2 * ((D + 4) * U * s1 + 2.0 ** -21) + (3 * len(k) + 64) * U) * \
+                    np.abs(v).max()
+    return tol * (1 + ULP[out_dtype]) + ULP[out_dtype] * 1.01 * np.abs(ref) + 1e-30
+
+
+def q_host(q: torch.Tensor) -> np.ndarray:
+    t = q.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16).copy()
+    return t.numpy().copy()
+
+
+def run_attention(orc, case, q, Hkv, left_window, out_dtype, scale=None, tb=None):
+    D = q.shape[2]
+    sc = D ** -0.5 if scale is None else scale
+    cache = upload(case) if tb is None else swrt.PagedCache.upload(tb, case.page_ptr,
+                                                                   case.page_ids, case.arena, DEV)
+    flags = flag_word()
+    out = swrt.paged_attention([q.to(DEV)], [cache], left_window, Hkv, scale=sc,
+                               out_dtype=out_dtype, flags=flags)[0]
+    torch.cuda.synchronize()
+    tbo = otable(case) if tb is None else tb
+    ref, f = orc.paged_attention(q_host(q), QT[q.dtype], case.arena, tbo, case.page_ptr,
+                                 case.page_ids, left_window, Hkv, sc)
+    return out, ref, int(flags.item()), f, tbo
+
+
+SHAPES = [  # (q dtype, D, Hq, Hkv)
+    (torch.bfloat16, 64, 16, 2), (torch.bfloat16, 32, 8, 8), (torch.bfloat16, 128, 16, 1),
+    (torch.bfloat16, 256, 4, 4), (torch.float16, 64, 32, 2), (torch.float32, 64, 8, 4),
+    (torch.float32, 32, 3, 1), (torch.bfloat16, 64, 12, 4),
+]
+
+
+@pytest.mark.parametrize("left_window", [-1, 0, 7, 40])
+@pytest.mark.parametrize("qdt,D,Hq,Hkv", SHAPES, ids=str)
+def test_paged_attention_mixed_formats(orc, qdt, D, Hq, Hkv, left_window):
+    """Pages of every format (random per page, K and V apart), sealed partial
+    pages, shuffled arena, ragged streams (empty, one token, many pages)."""
+    say("paged attention", qdt, D, Hq, Hkv, left_window)
+    g = wl.rng(D * 100 + Hq * 10 + Hkv + left_window)
+    B = 3
+    T = g.integers(1, 90, size=B * Hkv)
+    T[0] = 0
+    T[-1] = 1
+    streams = [wl.page_split(g, int(t), int(g.choice([4, 16, 32])), sealed=0.3) for t in T]
+    case = wl.paged_case(g, D, streams, random_format(g))
+    q = torch.from_numpy(g.uniform(-1, 1, (B, Hq, D)).astype(np.float32)).to(qdt)
+    for odt in (torch.float32, qdt):
+        out, ref, fg, fo, tb = run_attention(orc, case, q, Hkv, left_window, odt)
+        assert fg == fo == 0
+        got = out.detach().cpu().to(torch.float64).numpy()
+        tol = bound(case, tb, q, Hkv, left_window, D ** -0.5, odt, ref)
+        err = np.abs(got - ref)
+        assert (err <= tol).all(), f"max err/tol {np.max(err / tol):.3g}"
+        say("  out", odt, "worst err/tol", round(float(np.max(err / tol)), 4))
+        G = Hq // Hkv
+        assert (out[0, :G] == 0).all()  # the empty stream
+
+
+def test_paged_attention_bad_pages_flag_and_skip(orc):
+    g = wl.rng(60)
+    D, B, Hq, Hkv = 64, 2, 4, 2
+    streams = [wl.page_split(g, 40, 16) for _ in range(B * Hkv)]
+    case = wl.paged_case(g, D, streams, lambda s, i, n: (BF16, I8, 1.0, 0.05, 0, 0))
+    q = torch.from_numpy(g.uniform(-1, 1, (B, Hq, D)).astype(np.float32)).to(torch.bfloat16)
+    good, ref, fg, fo, tb = run_attention(orc, case, q, Hkv, 9, torch.float32)
+    assert fg == fo == 0
+    cases = []
+    # stream 0: its first page is outside a 10-token window; wreck it: not read
+    t1 = tb.copy()
+    t1[case.page_ids[0]]["length"] = 0
+    t1[case.page_ids[0]]["k_offset"] = 1 << 40
+    cases.append((t1, 0))
+    # stream 1: last page starts one token late (contiguity)
+    t2 = tb.copy()
+    t2[case.page_ids[case.page_ptr[2] - 1]]["start"] += 1
+    cases.append((t2, oracle.FLAG_BAD_PAGES))
+    # stream 2: a visible page's payload runs past the arena
+    t3 = tb.copy()
+    t3[case.page_ids[case.page_ptr[3] - 1]]["v_offset"] = len(case.arena) - 16
+    cases.append((t3, oracle.FLAG_BAD_PAGES))
+    # stream 3: a visible page with a zero scale; and a misaligned offset
+    t4 = tb.copy()
+    t4[case.page_ids[case.page_ptr[4] - 1]]["v_scale"] = 0.0
+    cases.append((t4, oracle.FLAG_BAD_PAGES))
+    t5 = tb.copy()
+    t5[case.page_ids[case.page_ptr[4] - 1]]["k_offset"] += 8
+    cases.append((t5, oracle.FLAG_BAD_PAGES))
+    for t, want in cases:
+        cache = swrt.PagedCache.upload(t, case.page_ptr, case.page_ids, case.arena, DEV)
+        out = torch.full((B, Hq, D), 7.0, device=DEV)
+        flags = flag_word()
+        swrt.paged_attention([q.to(DEV)], [cache], 9, Hkv, outs=[out], flags=flags)
+        torch.cuda.synchronize()
+        refo, fo = orc.paged_attention(q_host(q), oracle.XF_BF16, case.arena, t, case.page_ptr,
+                                       case.page_ids, 9, Hkv, D ** -0.5,
+                                       out=np.full((B, Hq, D), 7.0))
+        assert int(flags.item()) == fo == want
+        got = out.cpu().numpy()
+        same = refo == 7.0
+        assert (got[same] == 7.0).all()
+        np.testing.assert_allclose(got[~same], refo[~same], atol=1e-4)
+    # an id out of range among the visible pages, and page_ptr past page_ids
+    for mut in ("id", "ptr"):
+        ids, ptr = case.page_ids.copy(), case.page_ptr.copy()
+        if mut == "id":
+            ids[case.page_ptr[1] - 1] = case.n_pages
+        else:
+            ptr[-1] = len(ids) + 1
+        cache = swrt.PagedCache.upload(tb, ptr, ids, case.arena, DEV)
+        flags = flag_word()
+        swrt.paged_attention([q.to(DEV)], [cache], 9, Hkv, flags=flags)
+        torch.cuda.synchronize()
+        assert int(flags.item()) == swrt.FLAG_BAD_PAGES
+
+
+def test_paged_attention_several_layers_sharing_a_block_table(orc):
+    g = wl.rng(61)
+    D, B, Hq, Hkv, n = 64, 4, 16, 2, 3
+    streams = [wl.page_split(g, int(t), 16, 0.2) for t in g.integers(1, 200, B * Hkv)]
+    # one block table (the same layout and formats), each layer its own payload bytes
+    cases = [wl.paged_case(wl.rng(70), D, streams, random_format(wl.rng(71)),
+                           payload_rng=wl.rng(72 + i)) for i in range(n)]
+    for c in cases[1:]:
+        assert all((c.fields[f] == cases[0].fields[f]).all() for f in wl.PAGE_FIELDS)
+    table = swrt.PagedCache.upload(swrt.page_table(cases[0].fields), cases[0].page_ptr,
+                                   cases[0].page_ids, cases[0].arena, DEV)
+    caches = [swrt.PagedCache(torch.from_numpy(c.arena).to(DEV), table.pages, table.page_ptr,
+                              table.page_ids) for c in cases]
+    qs = [torch.from_numpy(g.uniform(-1, 1, (B, Hq, D)).astype(np.float32)).to(torch.bfloat16)
+          for _ in range(n)]
+    flags = flag_word()
+    outs = swrt.paged_attention([q.to(DEV) for q in qs], caches, 30, Hkv, out_dtype=torch.float32,
+                                flags=flags)
+    torch.cuda.synchronize()
+    assert int(flags.item()) == 0
+    tb = otable(cases[0])
+    for i in range(n):
+        ref, f = orc.paged_attention(q_host(qs[i]), oracle.XF_BF16, cases[i].arena, tb,
+                                     cases[0].page_ptr, cases[0].page_ids, 30, Hkv, D ** -0.5)
+        err = np.abs(outs[i].cpu().numpy() - ref)
+        tol = bound(wl.PagedCase(D, cases[0].fields, cases[0].page_ptr, cases[0].page_ids,
+                                 cases[i].arena, 0), tb, qs[i], Hkv, 30, D ** -0.5,
+                    torch.float32, ref)
+        assert (err <= tol).all()
+
+
+# -- conversion -----------------------------------------------------------------------
+
+@pytest.mark.parametrize("kf,vf", [(I8, U4), (I2, U2), (F16, BF16), (F32, I4), (U8, F32),
+                                   (BF16, I8), (I4, I4)])
+def test_paged_quantize_bytes_equal_the_oracle(orc, kf, vf):
+    say("paged quantize", kf, vf)
+    g = wl.rng(62 + kf * 10 + vf)
+    D = 64
+    streams = [wl.page_split(g, int(t), 16, 0.3) for t in g.integers(1, 100, 12)]
+    case = wl.paged_case(g, D, streams, random_format(g), spare_bytes=1 << 20)
+    tb = otable(case)
+    sel = np.sort(g.choice(case.n_pages, size=max(1, case.n_pages // 3), replace=False)).astype(np.int32)
+    base = case.free_offset
+    dst, off = [], base
+    for pid in sel:
+        for f in (kf, vf):
+            dst.append(off)
+            nb = int(tb[pid]["capacity"]) * D * oracle.PAGE_BITS[f] // 8
+            off += -(-nb // 16) * 16 + int(g.integers(0, 3)) * 16
+    ks, vs = 0.0375, 0.011
+    kz = (RANGES[kf][0] + RANGES[kf][1] + 1) // 2 if kf in RANGES else 0
+    vz = RANGES[vf][0] if vf in RANGES else 0
+    st, ar, pout = orc.paged_quantize(case.arena, tb, sel, dst, base, len(case.arena), kf, ks, kz,
+                                      vf, vs, vz, D)
+    assert st == oracle.OK
+    cache = upload(case)
+    flags = flag_word()
+    blocks = torch.from_numpy(sel).to(DEV)
+    dsts = torch.from_numpy(np.array(dst, np.int64)).to(DEV)
+    for in_place in (False, True):
+        c = upload(case)
+        out = swrt.paged_quantize(c, blocks, dsts, base, len(case.arena), kf, ks, kz, vf, vs, vz, D,
+                                  pages_out=c.pages if in_place else None, flags=flags)
+        torch.cuda.synchronize()
+        assert int(flags.item()) == 0
+        np.testing.assert_array_equal(c.arena.cpu().numpy(), ar)
+        assert out.cpu().numpy().tobytes() == pout.tobytes()
+    # attention over the converted cache equals the oracle's within the bound
+    q = torch.from_numpy(g.uniform(-1, 1, (3, 8, D)).astype(np.float32)).to(torch.bfloat16)
+    newcase = wl.PagedCase(D, {f: pout[f] for f in wl.PAGE_FIELDS}, case.page_ptr, case.page_ids,
+                           ar, 0)
+    o, ref, fg, fo, _ = run_attention(orc, newcase, q, 4, -1, torch.float32, tb=pout)
+    assert fg == fo == 0
+    tol = bound(newcase, pout, q, 4, -1, D ** -0.5, torch.float32, ref)
+    assert (np.abs(o.cpu().numpy() - ref) <= tol).all()
+
+
+def test_paged_quantize_rejects_and_writes_nothing(orc):
+    g = wl.rng(63)
+    D = 32
+    case = wl.paged_case(g, D, [wl.page_split(g, 40, 8) for _ in range(2)],
+                         lambda s, i, n: (BF16, BF16, 1.0, 1.0, 0, 0), spare_bytes=4096)
+    base, end = case.free_offset, len(case.arena)
+    tb = otable(case)
+    good = dict(blocks=[0, 1], dst=[base, base + 128, base + 256, base + 384], fb=base, fe=end)
+    bads = [dict(blocks=[1, 1]), dict(blocks=[1, 0]), dict(blocks=[0, case.n_pages]),
+            dict(dst=[base, base + 100, base + 256, base + 384]),
+            dict(dst=[base, base + 136, base + 256, base + 384]),   # misaligned
+            dict(dst=[base + 16, base, base + 256, base + 384]),    # out of order
+            dict(fb=base - 16, dst=[base - 16, base + 128, base + 256, base + 384]),
+            dict(fe=base + 400)]
+    for kw in bads:
+        a = {**good, **kw}
+        st, _, _ = orc.paged_quantize(case.arena, tb, a["blocks"], a["dst"], a["fb"], a["fe"],
+                                      I8, 0.1, 0, I8, 0.1, 0, D)
+        assert st == oracle.E_INVALID_ARG, kw
+        c = upload(case)
+        flags = flag_word()
+        out = swrt.paged_quantize(c, torch.tensor(a["blocks"], dtype=torch.int32, device=DEV),
+                                  torch.tensor(a["dst"], dtype=torch.int64, device=DEV), a["fb"],
+                                  a["fe"], I8, 0.1, 0, I8, 0.1, 0, D, pages_out=c.pages,
+                                  flags=flags)
+        torch.cuda.synchronize()
+        assert int(flags.item()) == swrt.FLAG_BAD_PAGES, kw
+        np.testing.assert_array_equal(c.arena.cpu().numpy(), case.arena)
+        assert out.cpu().numpy().tobytes() == tb.tobytes()
+    # a bad page anywhere in the table stops everything, selected or not
+    t = tb.copy()
+    t[case.n_pages - 1]["capacity"] = 0
+    c = swrt.PagedCache.upload(t, case.page_ptr, case.page_ids, case.arena, DEV)
+    flags = flag_word()
+    swrt.paged_quantize(c, torch.tensor([0], dtype=torch.int32, device=DEV),
+                        torch.tensor([base, base + 128], dtype=torch.int64, device=DEV), base, end,
+                        I8, 0.1, 0, I8, 0.1, 0, D, pages_out=c.pages, flags=flags)
+    torch.cuda.synchronize()
+    assert int(flags.item()) == swrt.FLAG_BAD_PAGES
+    np.testing.assert_array_equal(c.arena.cpu().numpy(), case.arena)
+
+
+# -- append ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("new_dtype", [torch.bfloat16, torch.float32, torch.float16])
+def test_paged_append_equals_the_oracle(orc, new_dtype):
+    g = wl.rng(64)
+    D, S = 64, 24
+    T = g.integers(0, 50, S)
+    T[0], T[1] = 0, 16  # a stream without pages; one whose only page is full
+    streams = [wl.page_split(g, int(t), 16 if i == 1 else int(g.choice([4, 8, 16])), 0.3)
+               for i, t in enumerate(T)]
+    streams[1] = [(16, 16)]
+    case = wl.paged_case(g, D, streams, random_format(g))
+    tb = otable(case)
+    kn = torch.from_numpy(g.uniform(-2, 2, (S, D)).astype(np.float32)).to(new_dtype)
+    vn = torch.from_numpy(g.uniform(-2, 2, (S, D)).astype(np.float32)).to(new_dtype)
+    ar, pout, fo = orc.paged_append(case.arena, tb, case.page_ptr, case.page_ids, q_host(kn),
+                                    q_host(vn), QT[new_dtype], D)
+    c = upload(case)
+    flags = flag_word()
+    swrt.paged_append([c], [kn.to(DEV)], [vn.to(DEV)], flags=flags)
+    torch.cuda.synchronize()
+    assert int(flags.item()) == fo
+    assert fo == swrt.FLAG_BAD_PAGES | swrt.FLAG_PAGE_FULL
+    np.testing.assert_array_equal(c.arena.cpu().numpy(), ar)
+    assert c.table().tobytes() == pout.tobytes()
+
+
+def test_paged_append_shared_table_grows_once_then_attention_sees_it(orc):
+    g = wl.rng(65)
+    D, B, Hkv, n = 64, 2, 4, 3
+    S = B * Hkv
+    streams = [wl.page_split(g, int(t), 16) for t in g.integers(1, 60, S)]
+    cases = [wl.paged_case(wl.rng(80), D, streams, lambda s, i, m: (BF16, BF16, 1.0, 1.0, 0, 0),
+                           payload_rng=wl.rng(90 + i)) for i in range(n)]
+    table = swrt.PagedCache.upload(swrt.page_table(cases[0].fields), cases[0].page_ptr,
+                                   cases[0].page_ids, cases[0].arena, DEV)
+    caches = [swrt.PagedCache(torch.from_numpy(c.arena).to(DEV), table.pages, table.page_ptr,
+                              table.page_ids) for c in cases]
+    kn = [torch.from_numpy(g.uniform(-1, 1, (S, D)).astype(np.float32)).to(torch.bfloat16)
+          for _ in range(n)]
+    vn = [torch.from_numpy(g.uniform(-1, 1, (S, D)).astype(np.float32)).to(torch.bfloat16)
+          for _ in range(n)]
+    full = int((cases[0].fields["length"] == cases[0].fields["capacity"])[
+        cases[0].page_ids[cases[0].page_ptr[1:] - 1]].sum())
+    flags = flag_word()
+    swrt.paged_append(caches, [k.to(DEV) for k in kn], [v.to(DEV) for v in vn], flags=flags)
+    torch.cuda.synchronize()
+    assert int(flags.item()) == (swrt.FLAG_PAGE_FULL if full else 0)
+    tb0 = otable(cases[0])
+    for i in range(n):
+        ar, pout, _ = orc.paged_append(cases[i].arena, tb0, cases[0].page_ptr, cases[0].page_ids,
+                                       q_host(kn[i]), q_host(vn[i]), oracle.XF_BF16, D)
+        np.testing.assert_array_equal(caches[i].arena.cpu().numpy(), ar)
+        assert table.table().tobytes() == pout.tobytes()  # grew once, not n times
+    # attention with a zero left window returns each appended V exactly
+    q = torch.from_numpy(g.uniform(-1, 1, (B, 8, D)).astype(np.float32)).to(torch.bfloat16)
+    outs = swrt.paged_attention([q.to(DEV)] * n, caches, 0, Hkv, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    last = cases[0].page_ids[cases[0].page_ptr[1:] - 1]
+    lengths0 = cases[0].fields["length"][last]
+    caps = cases[0].fields["capacity"][last]
+    for i in range(n):
+        for s in range(S):
+            if lengths0[s] == caps[s]:
+                continue
+            got = outs[i][s // Hkv, (s % Hkv) * 2:(s % Hkv) * 2 + 2].cpu().numpy()
+            want = vn[i][s].float().cpu().numpy()
+            np.testing.assert_array_equal(got, np.stack([want, want]))
