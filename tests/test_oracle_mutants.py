@@ -150,8 +150,8 @@ MUTANTS = {
     "paged_live_payload_overwritable": ("return ORC_E_INVALID_ARG; /* the free region holds no live payload */",
                                         "(void)0;"),
     "paged_duplicates_accepted": ("(i > 0 && id <= blocks[i - 1])", "(i > 0 && id < blocks[i - 1])"),
-    "paged_destinations_overlap": ("if (dst < next || bytes > free_end - dst)",
-                                   "if (bytes > free_end - dst)"),
+    "paged_destinations_overlap": ("if (dst < next || dst % 16 != 0 || bytes > free_end - dst)",
+                                   "if (dst % 16 != 0 || bytes > free_end - dst)"),
     "paged_heads_interleaved": ("const int64_t h = g * group + j;", "const int64_t h = j * Hkv + g;"),
     "paged_scale_dropped": ("sc = scale * dot;", "sc = dot;"),
 }
