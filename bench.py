@@ -64,6 +64,7 @@ KERNEL_SOURCES = {
     "window_in_place": ("kv_window.hip", "window_device.hpp", "xf_device.hpp", "swrt_device.hpp"),
     "decode_step_kernel": ("decode_step.hip", "window_device.hpp", "scatter_device.hpp",
                            "xf_device.hpp", "swrt_device.hpp"),
+    "paged_attention_kernel": ("paged.hip", "xf_device.hpp", "swrt_device.hpp", "../build.py"),
     # the attention kernel's code also depends on a code-generation flag of the build
     "window_attention_mfma": ("window_attention.hip", "xf_device.hpp", "swrt_device.hpp",
                               "../build.py"),
@@ -510,6 +511,110 @@ def attention_bench(args, dev):
     print(json.dumps(out))
 
 
+def paged_bench(args, dev):
+    """Workload 9: paged decode attention over 12 layers sharing one block
+    table (int8 cold pages, bf16 hot pages, left window 127), one launch per
+    step, K launches round robin over the buffer sets; then the cooling
+    conversion of every stream's oldest hot page in one layer (in place)."""
+    import oracle
+    import sliding_window_ring_tensor_amd as swrt
+    from sliding_window_ring_tensor_amd import workloads as wl
+    from sliding_window_ring_tensor_amd.paged_step import PagedDecodeStep
+
+    spec = wl.workload9()
+    K, W = args.steps, args.warmup
+    log(f"allocating {args.sets} buffer sets ...")
+    steps = [PagedDecodeStep(spec, dev, set_id=i, spare_bytes=1 << 20) for i in range(args.sets)]
+    torch.cuda.synchronize()
+    byts = steps[0].attention_bytes()
+    stream = torch.cuda.Stream()
+    eager, device, _ = _timers(stream, K, W)
+    with torch.cuda.stream(stream):
+        log(f"timing {K} paged attention launches ...")
+        att_s = eager(lambda i: steps[i].attention(), len(steps))
+        att_dev = device(lambda i: steps[i].attention(), len(steps), att_s)
+        torch_copy, swrt_copy = copy_reference(dev, stream)
+        # the cooling conversion, in place on copies of each set's table
+        blocks, dst, conv_written = steps[0].cooling_selection()
+        bl = torch.from_numpy(blocks).to(dev)
+        ds = torch.from_numpy(dst).to(dev)
+        tables = [st.caches[0].pages.clone() for st in steps]
+        conv = [swrt.PagedCache(st.arenas[0], t, st.caches[0].page_ptr, st.caches[0].page_ids)
+                for st, t in zip(steps, tables)]
+        cflags = [torch.zeros(1, dtype=torch.int32, device=dev) for _ in steps]
+
+        def convert(i):
+            tables[i].copy_(steps[i].caches[0].pages)  # the unconverted table again
+            swrt.paged_quantize(conv[i], bl, ds, steps[i].layout_bytes,
+                                steps[i].arenas[0].numel(), spec.cold_format, spec.k_scale, 0,
+                                spec.cold_format, spec.v_scale, 0, spec.head_dim,
+                                pages_out=tables[i], flags=cflags[i])
+        log(f"timing {K} conversions ...")
+        conv_s = eager(convert, len(steps))
+    flags = [int(st.flags.item()) for st in steps] + [int(f.item()) for f in cflags]
+    if any(flags):
+        raise SystemExit(f"device flags raised during the benchmark: {flags}")
+    value = byts / att_s / 1e9
+    achieved = byts / att_dev / 1e9
+    meas = MEASURED_TRAFFIC.get(("bf16+int8", "paged_attention_kernel",
+                                 kernel_source_hash("paged_attention_kernel")))
+    rows_bf16 = spec.block * spec.head_dim * 2
+    conv_read = 2 * len(blocks) * rows_bf16 + steps[0].table_host.nbytes + 16 * len(blocks) + \
+        4 * len(blocks)
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"timing the CPU oracle for about {args.cpu_seconds:.0f} s ...")
+        orc = oracle.get()
+        st = steps[0]
+        arenas = [a.cpu().numpy() for a in st.arenas]
+        qs = [q.cpu().view(torch.int16).numpy().view(np.uint16) for q in st.qs]
+        tb = st.table_host.view(oracle.PAGE_DTYPE)
+
+        def one_step():
+            for a, q in zip(arenas, qs):
+                orc.paged_attention(q, oracle.XF_BF16, a, tb, st.page_ptr_host, st.page_ids_host,
+                                    spec.left_window, spec.kv_heads, spec.head_dim ** -0.5)
+
+        n, el = _time_steps(one_step, args.cpu_seconds)
+        cpu = {"value": round(byts * n / el / 1e9, 4), "unit": "GB/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"{n} paged attention steps (12 layers) on host copies of buffer set 0, "
+                         f"one thread, float64, {el:.1f} s",
+               "us_per_step": round(el / n * 1e6, 1)}
+    out = {
+        "metric": "KV-cache update effective HBM GB/s (% of peak) and us per decode step",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(att_s * 1e3, 5), "us_per_step": round(att_s * 1e6, 2),
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16+int8", "data": "synthetic",
+        "config": {"workload": f"workload 9: paged decode attention over {spec.layers} layers "
+                               f"sharing one block table, B={spec.batch}, Hq={spec.q_heads}, "
+                               f"Hkv={spec.kv_heads}, D={spec.head_dim}, pages of {spec.block} "
+                               f"tokens ({steps[0].visible_pages} visible of "
+                               f"{len(steps[0].page_ids_host)}), left window "
+                               f"{spec.left_window}, T~U[1,8192] seed 9, cold pages int8 "
+                               f"(scales {spec.k_scale}/{spec.v_scale}), last {spec.hot_pages} "
+                               f"pages bf16, bf16 queries and outputs",
+                   "bytes_per_step": byts,
+                   "form": "one launch per step (paged_attention, all layers)",
+                   "cache_defeat": f"{args.sets} independent buffer sets round robin"},
+        "roofline": {"bound": "hbm", "kernel": "paged_attention_kernel: 12 layers, one launch",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None if meas is None else meas["read"] + meas["written"],
+                     "bytes_per_launch": byts, "mean_launch_us": round(att_dev * 1e6, 3)},
+        "cpu_baseline": cpu,
+        "cooling_conversion": {"pages": int(len(blocks)), "us_per_call": round(conv_s * 1e6, 2),
+                               "bytes_read": int(conv_read), "bytes_written": int(conv_written),
+                               "form": "one layer, in place: validate the whole table, convert "
+                                       "bf16 -> int8, publish the selected descriptors "
+                                       "(plus a 10 MB table restore per call)"},
+        "copy_reference_gbs": {"torch_copy": round(torch_copy, 1),
+                               "swrt_tensor_scatter_copy": round(swrt_copy, 1)},
+    }
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -523,12 +628,13 @@ def main():
                     help="one launch per step (default) or the three-call composition")
     ap.add_argument("--timing", default="eager", choices=["eager", "graph"],
                     help="the timed loop `value` reports (both are measured)")
-    ap.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5, 6, 7, 8],
+    ap.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5, 6, 7, 8, 9],
                     help="5: the whole-model decode step (default); 1-4: the other workloads; "
                          "6: workload 5's decode loop with drifting windowed caches "
                          "(capacity W + --slack); 7: workload 5 with the fused append (bf16 "
                          "rows, RoPE on K, int8 caches); 8: decode attention over workload 5's "
-                         "windowed layers; one line each, for the design notes")
+                         "windowed layers; 9: paged decode attention (int8 cold pages, bf16 hot "
+                         "pages) and the cooling conversion; one line each, for the design notes")
     ap.add_argument("--slack", type=int, default=16, help="workload 6: capacity - window")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -550,6 +656,8 @@ def main():
         return drift_loop(args, dev)
     if args.workload == 8:
         return attention_bench(args, dev)
+    if args.workload == 9:
+        return paged_bench(args, dev)
     if args.workload not in (5, 7):
         return other_workload(args, dev)
     xf = args.workload == 7

@@ -122,8 +122,8 @@ __device__ __forceinline__ void pg_load_raw(const char *p, uint32_t (&w)[(NB + 3
 
 // element e of packed words as binary32: a dense value, or the exact integer
 // c - zp of an affine code (its scale applied by the caller)
-template <int FMT, int NW>
-__device__ __forceinline__ float pg_elem(const uint32_t (&w)[NW], int e, int32_t zp) {
+template <int FMT>
+__device__ __forceinline__ float pg_elem(const uint32_t *w, int e, int32_t zp) {
   if constexpr (FMT == SWRT_XF_F32) {
     return __uint_as_float(w[e]);
   } else if constexpr (FMT == SWRT_XF_BF16) {
@@ -136,6 +136,63 @@ __device__ __forceinline__ float pg_elem(const uint32_t (&w)[NW], int e, int32_t
     int32_t c = int32_t(raw);
     if constexpr (pg_signed(FMT)) c = int32_t(raw << (32 - B)) >> (32 - B);
     return float(c - zp);
+  }
+}
+
+// the first n bytes (1, 2, 4, 8 or a multiple of 16, at most 4 * NW; uniform
+// in the wave) of a payload chunk as 32-bit words
+template <int NW>
+__device__ __forceinline__ void pg_load_bytes(const char *p, int n, uint32_t (&w)[NW]) {
+  switch (n) {
+    case 1: w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint8_t *>(p)); break;
+    case 2: w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(p)); break;
+    case 4: w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p)); break;
+    case 8: {
+      const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+      w[0] = x.x;
+      w[1] = x.y;
+      break;
+    }
+    default:
+#pragma unroll
+      for (int i = 0; i < (NW + 3) / 4; ++i)
+        if (16 * i < n) {
+          const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p) + i);
+          if (4 * i < NW) w[4 * i] = x.x;
+          if (4 * i + 1 < NW) w[4 * i + 1] = x.y;
+          if (4 * i + 2 < NW) w[4 * i + 2] = x.z;
+          if (4 * i + 3 < NW) w[4 * i + 3] = x.w;
+        }
+      break;
+  }
+}
+
+// N elements of packed words decoded (see pg_elem); a chunk of fewer than 8
+// bits sits `shift` bits up its byte
+template <int N, int NW>
+__device__ __forceinline__ void pg_decode(int fmt, const uint32_t (&w)[NW], int shift, int32_t zp,
+                                          float (&out)[N]) {
+  uint32_t v[NW];
+#pragma unroll
+  for (int i = 0; i < NW; ++i) v[i] = w[i];
+  v[0] >>= shift;
+  switch (fmt) {  // uniform in the wave
+#define SWRT_PG_CASE(F)                                              \
+  case F:                                                            \
+    _Pragma("unroll") for (int e = 0; e < N; ++e) out[e] = pg_elem<F>(v, e, zp); \
+    break;
+    SWRT_PG_CASE(SWRT_XF_F32)
+    SWRT_PG_CASE(SWRT_XF_F16)
+    SWRT_PG_CASE(SWRT_XF_BF16)
+    SWRT_PG_CASE(SWRT_XF_INT8)
+    SWRT_PG_CASE(SWRT_XF_UINT8)
+    SWRT_PG_CASE(SWRT_XF_INT4)
+    SWRT_PG_CASE(SWRT_XF_UINT4)
+    SWRT_PG_CASE(SWRT_XF_INT2)
+    default:
+      _Pragma("unroll") for (int e = 0; e < N; ++e) out[e] = pg_elem<SWRT_XF_UINT2>(v, e, zp);
+      break;
+#undef SWRT_PG_CASE
   }
 }
 
@@ -173,6 +230,11 @@ __device__ __forceinline__ void pg_load_decode(int fmt, const char *row, uint32_
 // attention
 // ---------------------------------------------------------------------------
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// the next tile's payload is loaded before this tile's arithmetic up to
+// head_dim 128 (two sets of raw chunks fit the registers)
+template <int D>
+constexpr bool kPgPrefetch = D <= 128;
 
 struct PgAttArgs {
   PgLayer L[kMaxLayers];
@@ -217,7 +279,7 @@ __global__ __launch_bounds__(kPgBlock) void paged_attention_kernel(PgAttArgs a) 
     for (int k = 0; k < KQ; ++k) qf[k] = head ? qf[k] : 0.0f;
   }
 
-  float m = -INFINITY, l = 0.0f;
+  float m = -INFINITY, l_sum = 0.0f;
   f32x4 acc[MT];
 #pragma unroll
   for (int i = 0; i < MT; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -226,65 +288,168 @@ __global__ __launch_bounds__(kPgBlock) void paged_attention_kernel(PgAttArgs a) 
   const int64_t ptr1 = __builtin_amdgcn_readfirstlane(P.page_ptr[s + 1]);
   bool ok = ptr0 >= 0 && ptr0 <= ptr1 && ptr1 <= P.n_ids;
   if (ok && ptr1 > ptr0) {
-    // the last page fixes T and the window's first token r0
-    const int32_t last = __builtin_amdgcn_readfirstlane(P.page_ids[ptr1 - 1]);
-    ok = last >= 0 && last < P.n_pages;
-    int64_t T = 0, r0 = 0;
-    if (ok) {
-      const swrt_page lp = pg_read(P.pages, last);
-      ok = pg_page_ok(lp, D, P.arena_bytes);
-      T = lp.start + lp.length;
-      r0 = a.left_window < 0 ? 0 : (T - 1 - a.left_window > 0 ? T - 1 - a.left_window : 0);
-    }
-    // the first page the window reaches: walking back from the last page 64
-    // at a time, the nearest one starting at or before r0
-    int64_t kfirst = -1;
-    for (int64_t top = ptr1 - 1; ok && kfirst < 0; top -= 64) {
+    // Pages are taken 64 at a time from the last one back: lane l reads the
+    // whole descriptor of page top - l (ids, then descriptors, one load each
+    // for the group) and checks it, joined to its successor by
+    // start + length == the successor's start. The last page fixes T and the
+    // window's first token r0; a group's pages from its lane 0 down to the
+    // first starting at or before r0 are visible. Pages the window does not
+    // reach are neither decoded nor checked beyond their id and start.
+    const int32_t pk = (j >> 2) + 4 * (j & 3);  // tile row of this lane's key operand
+    int64_t T = -1, r0 = 0, next_start = 0;
+    bool done = false;
+    for (int64_t top = ptr1 - 1; ok && !done; top -= 64) {
       const int64_t k = top - lane;
       const bool in = k >= ptr0;
-      const int32_t id = in ? P.page_ids[k] : 0;
-      const bool idok = !in || (id >= 0 && id < P.n_pages);
-      bool hit = false;
-      if (in && idok) hit = P.pages[id].start <= r0;
-      const uint64_t hits = __builtin_amdgcn_ballot_w64(hit);
-      const uint64_t bads = __builtin_amdgcn_ballot_w64(!idok);
-      if (hits) {
-        const int h = __builtin_ctzll(hits);
-        if (bads & ((2ull << h) - 1)) ok = false;  // a bad id among the pages to visit
-        kfirst = top - h;
-      } else if (bads || top - 63 <= ptr0) {
-        ok = false;  // a bad id, or no page starts at or before r0 (the first starts at 0)
+      int32_t id = 0;
+      if (in) id = P.page_ids[k];
+      bool good = !in || (id >= 0 && id < P.n_pages);
+      swrt_page d = {};
+      if (in && good) {
+        d = P.pages[id];
+        good = pg_page_ok(d, D, P.arena_bytes) && (k != ptr0 || d.start == 0);
       }
-    }
-    // the visible pages in token order, 16-row tiles of each
-    const int32_t pk = (j >> 2) + 4 * (j & 3);  // tile row of this lane's key operand
-    int64_t expect = 0;
-    for (int64_t k = kfirst; ok && k < ptr1; ++k) {
-      const swrt_page p = pg_read(P.pages, P.page_ids[k]);
-      if (!pg_page_ok(p, D, P.arena_bytes) || (k > kfirst && p.start != expect) ||
-          (k == ptr0 && p.start != 0)) {
+      const int64_t end = d.start + d.length;
+      const uint32_t elo = uint32_t(end), ehi = uint32_t(uint64_t(end) >> 32);
+      const uint32_t slo = uint32_t(d.start), shi = uint32_t(uint64_t(d.start) >> 32);
+      if (T < 0) {  // the first group: its lane 0 holds the last page
+        T = int64_t((uint64_t(uint32_t(__builtin_amdgcn_readlane(int(ehi), 0))) << 32) |
+                    uint32_t(__builtin_amdgcn_readlane(int(elo), 0)));
+        r0 = a.left_window < 0 ? 0 : (T - 1 - a.left_window > 0 ? T - 1 - a.left_window : 0);
+        next_start = T;
+      }
+      const int64_t succ = int64_t((uint64_t(uint32_t(__shfl_up(int(shi), 1))) << 32) |
+                                   uint32_t(__shfl_up(int(slo), 1)));
+      if (in && good) good = end == (lane == 0 ? next_start : succ);
+      const uint64_t hits = __builtin_amdgcn_ballot_w64(in && good && d.start <= r0);
+      const uint64_t ins = __builtin_amdgcn_ballot_w64(in);
+      const int h = hits ? __builtin_ctzll(hits) : 63;  // the last lane to take
+      const uint64_t mine = h == 63 ? ~0ull : (2ull << h) - 1;
+      if (__builtin_amdgcn_ballot_w64(in && !good) & mine) {
         ok = false;
         break;
       }
-      expect = p.start + p.length;
-      const int64_t krow = pg_row_bytes(p.k_format, D), vrow = pg_row_bytes(p.v_format, D);
-      const char *kb = P.arena + p.k_offset;
-      const char *vb = P.arena + p.v_offset;
-      const bool ka = pg_affine(p.k_format), va = pg_affine(p.v_format);
-      const float ks = ka ? p.k_scale * a.scale_log2 : a.scale_log2;
-      const float vs = va ? p.v_scale : 1.0f;
-      const int32_t kz = ka ? p.k_zero_point : 0, vz = va ? p.v_zero_point : 0;
-      const int32_t len = p.length;
-      for (int32_t i = int32_t(r0 > p.start ? r0 - p.start : 0); i < len; i += 16) {
-        // this tile's K and V elements, decoded (rows past the page repeat
-        // its last row and are masked)
+      if (!hits && (ins >> 63) == 0) {  // out of pages with none starting at or before r0
+        ok = false;
+        break;
+      }
+      done = hits != 0;
+      const int n_in = hits ? h + 1 : 64;
+      next_start = int64_t((uint64_t(uint32_t(__builtin_amdgcn_readlane(int(shi), n_in - 1))) << 32) |
+                           uint32_t(__builtin_amdgcn_readlane(int(slo), n_in - 1)));
+      // page l's fields, uniform
+      auto field = [&](int32_t x, int l) { return __builtin_amdgcn_readlane(x, l); };
+      auto field64 = [&](int64_t x, int l) {
+        return int64_t((uint64_t(uint32_t(field(int32_t(uint64_t(x) >> 32), l))) << 32) |
+                       uint32_t(field(int32_t(x), l)));
+      };
+      // A tile's raw payload: the 16-byte aligned blocks holding this lane's
+      // K chunk and its four V chunks, loaded without branches (blocks past a
+      // chunk repeat its first; every block lies inside the arena, whose size
+      // is a multiple of 16), with each chunk's first bit inside its block.
+      constexpr int KB = KQ * 4 / 16 > 0 ? KQ * 4 / 16 : 1;  // blocks of an fp32 K chunk
+      constexpr int VB = MT * 4 / 16 > 0 ? MT * 4 / 16 : 1;  // blocks of an fp32 V chunk
+      struct Tile {
+        u32x4 kb[KB];
+        u32x4 vb[4][VB];
+        uint32_t kbit;
+        uint32_t vbit[4];
+      };
+      auto load_tile = [&](Tile &t, int l, int32_t i) {
+        const int kf = field(d.k_format, l), vf = field(d.v_format, l);
+        const int32_t len = field(d.length, l);
+        const int64_t krow = pg_row_bytes(kf, D), vrow = pg_row_bytes(vf, D);
+        const int kchunk = KQ * pg_bits(kf) / 8;  // bytes, at least 2
+        const int nkb = kchunk >= 16 ? kchunk / 16 : 1;
+        const uintptr_t ka = reinterpret_cast<uintptr_t>(
+            P.arena + field64(d.k_offset, l) + int64_t(min(i + pk, len - 1)) * krow +
+            int64_t(qg) * kchunk);
+        t.kbit = uint32_t(ka & 15) * 8;
+#pragma unroll
+        for (int b = 0; b < KB; ++b)
+          t.kb[b] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+              (ka & ~uintptr_t(15)) + 16 * uintptr_t(b < nkb ? b : 0)));
+        const int vbits = MT * pg_bits(vf);  // chunk bits, at least 4
+        const int nvb = vbits >= 128 ? vbits / 128 : 1;
+        const int64_t vbit = int64_t(j) * vbits;
+        const char *vp = P.arena + field64(d.v_offset, l) + vbit / 8;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uintptr_t va = reinterpret_cast<uintptr_t>(
+              vp + int64_t(min(i + 4 * c + int32_t(qg), len - 1)) * vrow);
+          t.vbit[c] = uint32_t(va & 15) * 8 + uint32_t(vbit % 8);
+#pragma unroll
+          for (int b = 0; b < VB; ++b)
+            t.vb[c][b] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+                (va & ~uintptr_t(15)) + 16 * uintptr_t(b < nvb ? b : 0)));
+        }
+      };
+      // word k of a block, k chosen per lane
+      auto sel4 = [](u32x4 v, uint32_t k) {
+        return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
+      };
+      // a chunk as words from its first bit (the decoder's input): a chunk of
+      // 16 bytes or more starts a block, a shorter one lies inside one
+      // (aligned to its size, or a part of a byte). Every word is written, by
+      // selects, so the arrays stay in registers.
+      auto unpack_k = [&](const Tile &t, int kf, uint32_t (&w)[KQ]) {
+        const bool wide = KQ * pg_bits(kf) / 8 >= 16;
+        const uint32_t s0 = sel4(t.kb[0], t.kbit / 32) >> (t.kbit % 32);
+        const uint32_t s1 = sel4(t.kb[0], (t.kbit / 32 + 1) & 3);
+#pragma unroll
+        for (int e = 0; e < KQ; ++e)
+          w[e] = wide ? t.kb[(e / 4) % KB][e % 4] : e == 0 ? s0 : e == 1 ? s1 : 0u;
+      };
+      auto unpack_v = [&](const Tile &t, int c, int vf, uint32_t (&w)[MT]) {
+        const bool wide = MT * pg_bits(vf) >= 128;
+        const uint32_t s0 = sel4(t.vb[c][0], t.vbit[c] / 32) >> (t.vbit[c] % 32);
+        const uint32_t s1 = sel4(t.vb[c][0], (t.vbit[c] / 32 + 1) & 3);
+#pragma unroll
+        for (int e = 0; e < MT; ++e)
+          w[e] = wide ? t.vb[c][(e / 4) % VB][e % 4] : e == 0 ? s0 : e == 1 ? s1 : 0u;
+      };
+      auto first_row = [&](int l) {
+        const int64_t st = field64(d.start, l);
+        return int32_t(r0 > st ? r0 - st : 0);
+      };
+      // the group's visible pages in token order: lanes n_in - 1 .. 0
+      int l = n_in - 1;
+      int32_t i = first_row(l);
+      Tile cur, nxt;
+      load_tile(cur, l, i);
+      while (l >= 0) {
+        // the tile after this one
+        int ln = l;
+        int32_t in_ = i + 16;
+        if (in_ >= field(d.length, l)) {
+          ln = l - 1;
+          in_ = ln >= 0 ? first_row(ln) : 0;
+        }
+        if constexpr (kPgPrefetch<D>) {
+          if (ln >= 0) load_tile(nxt, ln, in_);
+        }
+        // this tile: page l's formats and scales
+        const int kf = field(d.k_format, l), vf = field(d.v_format, l);
+        const int32_t len = field(d.length, l);
+        const bool ka = pg_affine(kf), va = pg_affine(vf);
+        const float ks = ka ? __int_as_float(field(__float_as_int(d.k_scale), l)) * a.scale_log2
+                            : a.scale_log2;
+        const float vs = va ? __int_as_float(field(__float_as_int(d.v_scale), l)) : 1.0f;
+        const int32_t kz = ka ? field(d.k_zero_point, l) : 0;
+        const int32_t vz = va ? field(d.v_zero_point, l) : 0;
         float kv[KQ];
-        pg_load_decode<KQ>(p.k_format, kb + int64_t(min(i + pk, len - 1)) * krow, qg * KQ, kz, kv);
+        {
+          uint32_t w[KQ];
+          unpack_k(cur, kf, w);
+          pg_decode(kf, w, 0, kz, kv);
+        }
         float vv[4][MT];
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-          pg_load_decode<MT>(p.v_format, vb + int64_t(min(i + 4 * c + int32_t(qg), len - 1)) * vrow,
-                             j * MT, vz, vv[c]);
+        for (int c = 0; c < 4; ++c) {
+          uint32_t w[MT];
+          unpack_v(cur, c, vf, w);
+          pg_decode(vf, w, 0, vz, vv[c]);
+        }
         float x[4];
         float bm = -INFINITY;
         {
@@ -310,7 +475,7 @@ __global__ __launch_bounds__(kPgBlock) void paged_attention_kernel(PgAttArgs a) 
           const float mn = move ? bm : m;
           if (__builtin_amdgcn_ballot_w64(move && m != -INFINITY)) {
             const float f = move ? __builtin_amdgcn_exp2f(m - mn) : 1.0f;
-            l *= f;
+            l_sum *= f;
 #pragma unroll
             for (int t = 0; t < MT; ++t) acc[t] *= f;
           }
@@ -318,7 +483,7 @@ __global__ __launch_bounds__(kPgBlock) void paged_attention_kernel(PgAttArgs a) 
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float w = none ? 0.0f : __builtin_amdgcn_exp2f(x[r] - mn);
-            l += w;
+            l_sum += w;
             pw[r] = w * vs;  // an affine page's V scale rides on the weight
           }
           m = mn;
@@ -328,6 +493,13 @@ __global__ __launch_bounds__(kPgBlock) void paged_attention_kernel(PgAttArgs a) 
 #pragma unroll
           for (int t = 0; t < MT; ++t)
             acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv[c][t], pw[c], acc[t], 0, 0, 0);
+        l = ln;
+        i = in_;
+        if constexpr (kPgPrefetch<D>) {
+          cur = nxt;
+        } else {
+          if (l >= 0) load_tile(cur, l, i);
+        }
       }
     }
   }
@@ -335,10 +507,10 @@ __global__ __launch_bounds__(kPgBlock) void paged_attention_kernel(PgAttArgs a) 
     if (a.flags && lane == 0) atomicOr(a.flags, SWRT_FLAG_BAD_PAGES);
     return;
   }
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
+  l_sum += __shfl_xor(l_sum, 16);
+  l_sum += __shfl_xor(l_sum, 32);
   if (!head) return;
-  const float inv = l > 0.0f ? 1.0f / l : 0.0f;  // no visible token: zeros
+  const float inv = l_sum > 0.0f ? 1.0f / l_sum : 0.0f;  // no visible token: zeros
   float y[4 * MT];
 #pragma unroll
   for (int r = 0; r < 4; ++r)
@@ -529,7 +701,30 @@ __global__ __launch_bounds__(64) void paged_convert_kernel(PgConvArgs a) {
   }
 }
 
-// every descriptor to pages_out, the selected ones with their new storage
+// the selected descriptors with their new storage, written in place
+__device__ __forceinline__ void pg_retarget(const PgConvArgs &a, swrt_page &p, int64_t i) {
+  p.k_format = a.fmt[0];
+  p.v_format = a.fmt[1];
+  p.k_scale = a.scale[0];
+  p.v_scale = a.scale[1];
+  p.k_zero_point = a.zp[0];
+  p.v_zero_point = a.zp[1];
+  p.k_offset = a.dst[2 * i];
+  p.v_offset = a.dst[2 * i + 1];
+}
+
+__global__ __launch_bounds__(kPgBlock) void paged_publish_selected_kernel(PgConvArgs a) {
+  if (__atomic_load_n(a.flags, __ATOMIC_RELAXED) & SWRT_FLAG_BAD_PAGES) return;
+  for (int64_t i = int64_t(blockIdx.x) * kPgBlock + threadIdx.x; i < a.n_blocks;
+       i += int64_t(gridDim.x) * kPgBlock) {
+    swrt_page p = a.pages_in[a.blocks[i]];
+    pg_retarget(a, p, i);
+    a.pages_out[a.blocks[i]] = p;
+  }
+}
+
+// every descriptor to a separate pages_out, the selected ones with their new
+// storage
 __global__ __launch_bounds__(kPgBlock) void paged_publish_kernel(PgConvArgs a) {
   if (__atomic_load_n(a.flags, __ATOMIC_RELAXED) & SWRT_FLAG_BAD_PAGES) return;
   for (int64_t x = int64_t(blockIdx.x) * kPgBlock + threadIdx.x; x < a.n_pages;
@@ -544,16 +739,7 @@ __global__ __launch_bounds__(kPgBlock) void paged_publish_kernel(PgConvArgs a) {
       else
         hi = mid;
     }
-    if (lo < a.n_blocks && a.blocks[lo] == x) {
-      p.k_format = a.fmt[0];
-      p.v_format = a.fmt[1];
-      p.k_scale = a.scale[0];
-      p.v_scale = a.scale[1];
-      p.k_zero_point = a.zp[0];
-      p.v_zero_point = a.zp[1];
-      p.k_offset = a.dst[2 * lo];
-      p.v_offset = a.dst[2 * lo + 1];
-    }
+    if (lo < a.n_blocks && a.blocks[lo] == x) pg_retarget(a, p, lo);
     a.pages_out[x] = p;
   }
 }
@@ -641,7 +827,8 @@ int pg_layers(int n_layers, const swrt_paged_layer *layers, PgLayer *out, bool a
   for (int l = 0; l < n_layers; ++l) {
     const swrt_paged_layer &x = layers[l];
     if (!x.arena || !x.pages || !x.page_ptr || (x.n_ids > 0 && !x.page_ids)) return SWRT_E_INVALID_ARG;
-    if (x.arena_bytes < 0 || x.n_pages < 0 || x.n_ids < 0 || x.n_pages > INT32_MAX)
+    if (x.arena_bytes < 0 || x.arena_bytes % 16 || x.n_pages < 0 || x.n_ids < 0 ||
+        x.n_pages > INT32_MAX)
       return SWRT_E_INVALID_ARG;
     if (addr_of(x.arena) % 16 || addr_of(x.pages) % 8 || addr_of(x.page_ptr) % 4 ||
         addr_of(x.page_ids) % 4)
@@ -778,6 +965,12 @@ extern "C" int swrt_paged_quantize(void *arena, int64_t arena_bytes, const swrt_
     hipLaunchKernelGGL(paged_convert_kernel, dim3(uint32_t(2 * n_blocks)), dim3(64), 0, s, a);
     st = launch_status();
     if (st != SWRT_OK) return st;
+  }
+  if (pages_out == pages_in) {  // in place: only the selected descriptors change
+    if (n_blocks == 0) return SWRT_OK;
+    const uint32_t gb = uint32_t(std::min<int64_t>((n_blocks + kPgBlock - 1) / kPgBlock, 4096));
+    hipLaunchKernelGGL(paged_publish_selected_kernel, dim3(gb), dim3(kPgBlock), 0, s, a);
+    return launch_status();
   }
   const uint32_t gp = uint32_t(std::min<int64_t>((n_pages + kPgBlock - 1) / kPgBlock, 4096));
   hipLaunchKernelGGL(paged_publish_kernel, dim3(gp), dim3(kPgBlock), 0, s, a);

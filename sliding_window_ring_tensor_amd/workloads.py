@@ -393,3 +393,78 @@ def page_split(g: np.random.Generator, tokens: int, capacity: int, sealed: float
         pages.append((n, capacity))
         left -= n
     return pages
+
+
+@dataclass
+class PagedStep:
+    """A decode step over paged caches: every layer's streams (batch entry,
+    KV head) hold T tokens of their batch entry in pages of ``block`` tokens,
+    contiguous from zero; one block table serves every layer (each layer its
+    own arena). The last ``hot_pages`` pages of a stream are ``hot_format``,
+    older ones ``cold_format`` with scales ``k_scale`` / ``v_scale`` and zero
+    points 0. Pages the window never reaches keep descriptors but share one
+    placeholder payload (nothing reads it), so the arena holds only what the
+    window can see."""
+    layers: int
+    batch: int
+    kv_heads: int
+    q_heads: int
+    head_dim: int
+    block: int
+    left_window: int
+    total_lens: np.ndarray
+    hot_pages: int = 2
+    hot_format: int = 3      # bf16
+    cold_format: int = 4     # int8
+    k_scale: float = 0.02
+    v_scale: float = 0.01
+    seed: int = 9
+
+
+def workload9() -> PagedStep:
+    g = rng(9)
+    T = g.integers(1, 8192, endpoint=True, size=64).astype(np.int64)
+    return PagedStep(layers=12, batch=64, kv_heads=8, q_heads=64, head_dim=64, block=16,
+                     left_window=127, total_lens=T)
+
+
+def paged_step_layout(step: PagedStep, align: int = 16):
+    """Descriptor fields, page_ptr, page_ids and the arena size of a PagedStep
+    (stream-major page order). Returns (fields, page_ptr, page_ids,
+    arena_bytes, visible_pages)."""
+    D, blk = step.head_dim, step.block
+    rows = {f: blk * D * FORMAT_BITS[f] // 8 for f in (step.hot_format, step.cold_format)}
+    placeholder = -(-max(rows.values()) // align) * align
+    off = placeholder  # [0, placeholder): the shared payload of unreachable pages
+    cols = {f: [] for f in PAGE_FIELDS}
+    ptr = [0]
+    visible = 0
+    for b in range(step.batch):
+        T = int(step.total_lens[b])
+        n = -(-T // blk)
+        r0 = max(0, T - 1 - step.left_window) if step.left_window >= 0 else 0
+        first_visible = r0 // blk
+        for _g in range(step.kv_heads):
+            for i in range(n):
+                start, length = i * blk, min(blk, T - i * blk)
+                fmt = step.hot_format if i >= n - step.hot_pages else step.cold_format
+                affine = fmt not in _DENSE
+                if i >= first_visible:
+                    ko = off
+                    off += -(-rows[fmt] // align) * align
+                    vo = off
+                    off += -(-rows[fmt] // align) * align
+                    visible += 1
+                else:
+                    ko = vo = 0
+                for f, v in (("start", start), ("length", length), ("capacity", blk),
+                             ("k_offset", ko), ("v_offset", vo), ("k_format", fmt),
+                             ("v_format", fmt), ("k_scale", step.k_scale if affine else 1.0),
+                             ("v_scale", step.v_scale if affine else 1.0), ("k_zero_point", 0),
+                             ("v_zero_point", 0)):
+                    cols[f].append(v)
+            ptr.append(len(cols["start"]))
+    fields = {f: np.array(v, dtype=np.float32 if f.endswith("scale") else np.int64)
+              for f, v in cols.items()}
+    n_pages = len(fields["start"])
+    return fields, np.array(ptr, np.int32), np.arange(n_pages, dtype=np.int32), off, visible

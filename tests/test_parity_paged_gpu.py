@@ -411,3 +411,66 @@ def test_paged_append_shared_table_grows_once_then_attention_sees_it(orc):
             got = outs[i][s // Hkv, (s % Hkv) * 2:(s % Hkv) * 2 + 2].cpu().numpy()
             want = vn[i][s].float().cpu().numpy()
             np.testing.assert_array_equal(got, np.stack([want, want]))
+
+
+def test_workload9_full_size(orc):
+    """The paged decode step at full size in the launch configuration the
+    benchmark times: attention over all 12 layers (every output compared),
+    then the cooling conversion of every stream's oldest hot page in one layer
+    and one append into every stream of every layer (bytes compared)."""
+    from sliding_window_ring_tensor_amd.paged_step import PagedDecodeStep
+    spec = wl.workload9()
+    say("workload 9 full size")
+    st = PagedDecodeStep(spec, DEV, set_id=0, spare_bytes=1 << 20)
+    st.attention()
+    torch.cuda.synchronize()
+    assert int(st.flags.item()) == 0
+    tb = st.table_host.view(oracle.PAGE_DTYPE)
+    case = wl.PagedCase(spec.head_dim, st.fields, st.page_ptr_host, st.page_ids_host, None, 0)
+    worst = 0.0
+    for i in range(spec.layers):
+        arena = st.arenas[i].cpu().numpy()
+        ref, f = orc.paged_attention(q_host(st.qs[i]), oracle.XF_BF16, arena, tb,
+                                     st.page_ptr_host, st.page_ids_host, spec.left_window,
+                                     spec.kv_heads, spec.head_dim ** -0.5)
+        assert f == 0
+        case.arena = arena
+        tol = bound(case, tb, st.qs[i], spec.kv_heads, spec.left_window, spec.head_dim ** -0.5,
+                    torch.bfloat16, ref)
+        err = np.abs(st.outs[i].float().cpu().numpy() - ref)
+        assert (err <= tol).all(), f"layer {i}: max err/tol {np.max(err / tol):.3g}"
+        worst = max(worst, float(np.max(err / tol)))
+    say("  attention worst err/tol", round(worst, 4))
+    # cooling: the oldest hot page of every stream, bf16 -> int8, in layer 3
+    blocks, dst, _ = st.cooling_selection()
+    arena = st.arenas[3].cpu().numpy()
+    code, ar, pout = orc.paged_quantize(arena, tb, blocks, dst, st.layout_bytes, len(arena),
+                                        spec.cold_format, spec.k_scale, 0, spec.cold_format,
+                                        spec.v_scale, 0, spec.head_dim)
+    assert code == oracle.OK
+    flags = flag_word()
+    out = swrt.paged_quantize(st.caches[3], torch.from_numpy(blocks).to(DEV),
+                              torch.from_numpy(dst).to(DEV), st.layout_bytes, len(arena),
+                              spec.cold_format, spec.k_scale, 0, spec.cold_format, spec.v_scale, 0,
+                              spec.head_dim, flags=flags)
+    torch.cuda.synchronize()
+    assert int(flags.item()) == 0
+    np.testing.assert_array_equal(st.arenas[3].cpu().numpy(), ar)
+    assert out.cpu().numpy().tobytes() == pout.tobytes()
+    # append: one token into every stream's last page, every layer, one table
+    S = spec.batch * spec.kv_heads
+    kn = [wl.device_payload((S, spec.head_dim), torch.bfloat16, 9, 300 + i, DEV)
+          for i in range(spec.layers)]
+    vn = [wl.device_payload((S, spec.head_dim), torch.bfloat16, 9, 400 + i, DEV)
+          for i in range(spec.layers)]
+    before = [a.cpu().numpy() for a in st.arenas]
+    flags = flag_word()
+    swrt.paged_append(st.caches, kn, vn, flags=flags)
+    torch.cuda.synchronize()
+    full = int((st.fields["length"] == st.fields["capacity"])[st.page_ptr_host[1:] - 1].any())
+    assert int(flags.item()) == (swrt.FLAG_PAGE_FULL if full else 0)
+    for i in (0, 7, 11):
+        ar, pout, f = orc.paged_append(before[i], tb, st.page_ptr_host, st.page_ids_host,
+                                       q_host(kn[i]), q_host(vn[i]), oracle.XF_BF16, spec.head_dim)
+        np.testing.assert_array_equal(st.arenas[i].cpu().numpy(), ar)
+        assert st.caches[i].table().tobytes() == pout.tobytes()
