@@ -550,7 +550,8 @@ typedef struct swrt_page {
  *   out        [batch, q_heads, head_dim] out_type, 16-byte aligned; must not
  *              overlap any input.
  *   arena      device bytes holding every page payload, 16-byte aligned,
- *              arena_bytes long.
+ *              arena_bytes long (a multiple of 16: the kernels read payload
+ *              in aligned 16-byte blocks).
  *   pages      device swrt_page[n_pages].
  *   page_ptr   device int32[batch * kv_heads + 1]: stream s owns
  *              page_ids[page_ptr[s] .. page_ptr[s + 1]) in token order.

@@ -244,6 +244,128 @@ struct PgAttArgs {
   int32_t B, Hq, Hkv, items, q_type, out_type;
 };
 
+// A tile's raw payload for one lane: the 16-byte aligned blocks holding its
+// K chunk (D/4 elements of row pk) and its four V chunks (D/16 elements of
+// rows 4 c + q), with each chunk's first bit inside its first block.
+template <int D>
+struct PgTile {
+  static constexpr int KQ = D / 4, MT = D / 16;
+  static constexpr int KB = KQ * 4 / 16 > 0 ? KQ * 4 / 16 : 1;  // blocks of an fp32 K chunk
+  static constexpr int VB = MT * 4 / 16 > 0 ? MT * 4 / 16 : 1;  // blocks of an fp32 V chunk
+  u32x4 kb[KB];
+  u32x4 vb[4][VB];
+  uint32_t kbit;
+  uint32_t vbit[4];
+};
+
+// word k of a block, k chosen per lane: selects on k's two bits (a chain of
+// equality tests would become a branch per lane)
+__device__ __forceinline__ uint32_t pg_sel4(u32x4 v, uint32_t k) {
+  const bool odd = (k & 1u) != 0, high = (k & 2u) != 0;
+  const uint32_t lo = odd ? v.y : v.x;
+  const uint32_t hi = odd ? v.w : v.z;
+  return high ? hi : lo;
+}
+
+// a chunk of `bits` bits as words from its first bit: 16 bytes or more start a
+// block; a shorter chunk lies inside one (aligned to its size, or a part of
+// a byte). Every word is written so the array stays in registers.
+template <int NW, int BITS, int NB>
+__device__ __forceinline__ void pg_chunk_words(const u32x4 (&blk)[NB], uint32_t bit,
+                                               uint32_t (&w)[NW]) {
+  if constexpr (BITS >= 128) {
+#pragma unroll
+    for (int e = 0; e < NW; ++e) w[e] = e < BITS / 32 ? blk[(e / 4) % NB][e % 4] : 0u;
+  } else {
+    const uint32_t s0 = pg_sel4(blk[0], bit / 32) >> (bit % 32);
+    const uint32_t s1 = BITS > 32 ? pg_sel4(blk[0], (bit / 32 + 1) & 3) : 0u;
+#pragma unroll
+    for (int e = 0; e < NW; ++e) w[e] = e == 0 ? s0 : e == 1 ? s1 : 0u;
+  }
+}
+
+typedef __bf16 pg_bf16x8 __attribute__((ext_vector_type(8)));
+
+// the tile's scores before scaling, K in format KF: on the bf16 matrix
+// instruction when the query is bf16 and K is bf16 or affine (codes enter
+// as the exact bf16 integers c - zp; every product is exact), else on the
+// fp32 one with K widened to binary32
+template <int D, int KF, bool QBF>
+__device__ __forceinline__ f32x4 pg_tile_scores_t(const PgTile<D> &t, const float (&qf)[D / 4],
+                                                  const uint32_t (&qb)[D / 8], int32_t kz) {
+  constexpr int KQ = D / 4;
+  uint32_t w[KQ];
+  pg_chunk_words<KQ, KQ * pg_bits(KF)>(t.kb, t.kbit, w);
+  f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
+  if constexpr (QBF && KF != SWRT_XF_F32 && KF != SWRT_XF_F16) {
+    uint32_t kw[KQ / 2];
+#pragma unroll
+    for (int i = 0; i < KQ / 2; ++i) {
+      if constexpr (KF == SWRT_XF_BF16) {
+        kw[i] = w[i];
+      } else {
+        const uint32_t lo = __float_as_uint(pg_elem<KF>(w, 2 * i, kz));
+        const uint32_t hi = __float_as_uint(pg_elem<KF>(w, 2 * i + 1, kz));
+        kw[i] = (lo >> 16) | (hi & 0xFFFF0000u);  // |c - zp| <= 255: exact in bf16
+      }
+    }
+#pragma unroll
+    for (int st = 0; st < KQ / 8; ++st)
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          __builtin_bit_cast(pg_bf16x8, u32x4{kw[4 * st], kw[4 * st + 1], kw[4 * st + 2], kw[4 * st + 3]}),
+          __builtin_bit_cast(pg_bf16x8, u32x4{qb[4 * st], qb[4 * st + 1], qb[4 * st + 2], qb[4 * st + 3]}),
+          sc, 0, 0, 0);
+  } else {
+#pragma unroll
+    for (int e = 0; e < KQ; ++e)
+      sc = __builtin_amdgcn_mfma_f32_16x16x4f32(pg_elem<KF>(w, e, kz), qf[e], sc, 0, 0, 0);
+  }
+  return sc;
+}
+
+// the tile's weighted values, V in format VF, into the accumulators
+template <int D, int VF>
+__device__ __forceinline__ void pg_tile_values_t(const PgTile<D> &t, const float (&pw)[4], int32_t vz,
+                                                 f32x4 (&acc)[D / 16]) {
+  constexpr int MT = D / 16;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    uint32_t w[MT];
+    pg_chunk_words<MT, MT * pg_bits(VF)>(t.vb[c], t.vbit[c], w);
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+      acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(pg_elem<VF>(w, m, vz), pw[c], acc[m], 0, 0, 0);
+  }
+}
+
+#define SWRT_PG_FORMATS(X) \
+  X(SWRT_XF_F32) X(SWRT_XF_F16) X(SWRT_XF_BF16) X(SWRT_XF_INT8) X(SWRT_XF_UINT8) \
+  X(SWRT_XF_INT4) X(SWRT_XF_UINT4) X(SWRT_XF_INT2)
+
+template <int D, bool QBF>
+__device__ __forceinline__ f32x4 pg_tile_scores(int kf, const PgTile<D> &t, const float (&qf)[D / 4],
+                                                const uint32_t (&qb)[D / 8], int32_t kz) {
+  switch (kf) {  // uniform in the wave
+#define SWRT_PG_K(F) \
+  case F: return pg_tile_scores_t<D, F, QBF>(t, qf, qb, kz);
+    SWRT_PG_FORMATS(SWRT_PG_K)
+#undef SWRT_PG_K
+    default: return pg_tile_scores_t<D, SWRT_XF_UINT2, QBF>(t, qf, qb, kz);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void pg_tile_values(int vf, const PgTile<D> &t, const float (&pw)[4],
+                                               int32_t vz, f32x4 (&acc)[D / 16]) {
+  switch (vf) {  // uniform in the wave
+#define SWRT_PG_V(F) \
+  case F: pg_tile_values_t<D, F>(t, pw, vz, acc); break;
+    SWRT_PG_FORMATS(SWRT_PG_V)
+#undef SWRT_PG_V
+    default: pg_tile_values_t<D, SWRT_XF_UINT2>(t, pw, vz, acc); break;
+  }
+}
+
 // Lane l holds head slot j = l % 16 of every accumulator. The score product
 // (v_mfma_f32_16x16x4_f32, one dimension per lane and instruction) gives lane
 // l the scores of tile rows q + 4 r (q = l / 16) when the key operand carries
@@ -253,7 +375,7 @@ struct PgAttArgs {
 // and output dimension MT i + m at matrix row i of output tile m
 // (MT = D / 16): a lane reads MT consecutive elements of a V row and ends
 // holding 4 MT consecutive output dimensions of its head.
-template <int D>
+template <int D, bool QBF>
 __global__ __launch_bounds__(kPgBlock) void paged_attention_kernel(PgAttArgs a) {
   constexpr int KQ = D / 4;   // dimensions per lane of the score product
   constexpr int MT = D / 16;  // output tiles; V elements per lane and row
@@ -278,6 +400,12 @@ __global__ __launch_bounds__(kPgBlock) void paged_attention_kernel(PgAttArgs a) 
 #pragma unroll
     for (int k = 0; k < KQ; ++k) qf[k] = head ? qf[k] : 0.0f;
   }
+  // the same dimensions as bf16 pairs (a bf16 query only)
+  uint32_t qb[KQ / 2];
+#pragma unroll
+  for (int i = 0; i < KQ / 2; ++i)
+    qb[i] = QBF ? (__float_as_uint(qf[2 * i]) >> 16) | (__float_as_uint(qf[2 * i + 1]) & 0xFFFF0000u)
+                : 0u;
 
   float m = -INFINITY, l_sum = 0.0f;
   f32x4 acc[MT];
@@ -343,18 +471,11 @@ __global__ __launch_bounds__(kPgBlock) void paged_attention_kernel(PgAttArgs a) 
         return int64_t((uint64_t(uint32_t(field(int32_t(uint64_t(x) >> 32), l))) << 32) |
                        uint32_t(field(int32_t(x), l)));
       };
-      // A tile's raw payload: the 16-byte aligned blocks holding this lane's
-      // K chunk and its four V chunks, loaded without branches (blocks past a
-      // chunk repeat its first; every block lies inside the arena, whose size
-      // is a multiple of 16), with each chunk's first bit inside its block.
-      constexpr int KB = KQ * 4 / 16 > 0 ? KQ * 4 / 16 : 1;  // blocks of an fp32 K chunk
-      constexpr int VB = MT * 4 / 16 > 0 ? MT * 4 / 16 : 1;  // blocks of an fp32 V chunk
-      struct Tile {
-        u32x4 kb[KB];
-        u32x4 vb[4][VB];
-        uint32_t kbit;
-        uint32_t vbit[4];
-      };
+      using Tile = PgTile<D>;
+      constexpr int KB = Tile::KB, VB = Tile::VB;
+      // a tile's blocks, loaded without branches (blocks past a chunk repeat
+      // its first; every block lies inside the arena, whose size is a
+      // multiple of 16)
       auto load_tile = [&](Tile &t, int l, int32_t i) {
         const int kf = field(d.k_format, l), vf = field(d.v_format, l);
         const int32_t len = field(d.length, l);
@@ -383,30 +504,6 @@ __global__ __launch_bounds__(kPgBlock) void paged_attention_kernel(PgAttArgs a) 
             t.vb[c][b] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
                 (va & ~uintptr_t(15)) + 16 * uintptr_t(b < nvb ? b : 0)));
         }
-      };
-      // word k of a block, k chosen per lane
-      auto sel4 = [](u32x4 v, uint32_t k) {
-        return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
-      };
-      // a chunk as words from its first bit (the decoder's input): a chunk of
-      // 16 bytes or more starts a block, a shorter one lies inside one
-      // (aligned to its size, or a part of a byte). Every word is written, by
-      // selects, so the arrays stay in registers.
-      auto unpack_k = [&](const Tile &t, int kf, uint32_t (&w)[KQ]) {
-        const bool wide = KQ * pg_bits(kf) / 8 >= 16;
-        const uint32_t s0 = sel4(t.kb[0], t.kbit / 32) >> (t.kbit % 32);
-        const uint32_t s1 = sel4(t.kb[0], (t.kbit / 32 + 1) & 3);
-#pragma unroll
-        for (int e = 0; e < KQ; ++e)
-          w[e] = wide ? t.kb[(e / 4) % KB][e % 4] : e == 0 ? s0 : e == 1 ? s1 : 0u;
-      };
-      auto unpack_v = [&](const Tile &t, int c, int vf, uint32_t (&w)[MT]) {
-        const bool wide = MT * pg_bits(vf) >= 128;
-        const uint32_t s0 = sel4(t.vb[c][0], t.vbit[c] / 32) >> (t.vbit[c] % 32);
-        const uint32_t s1 = sel4(t.vb[c][0], (t.vbit[c] / 32 + 1) & 3);
-#pragma unroll
-        for (int e = 0; e < MT; ++e)
-          w[e] = wide ? t.vb[c][(e / 4) % VB][e % 4] : e == 0 ? s0 : e == 1 ? s1 : 0u;
       };
       auto first_row = [&](int l) {
         const int64_t st = field64(d.start, l);
@@ -437,27 +534,11 @@ __global__ __launch_bounds__(kPgBlock) void paged_attention_kernel(PgAttArgs a) 
         const float vs = va ? __int_as_float(field(__float_as_int(d.v_scale), l)) : 1.0f;
         const int32_t kz = ka ? field(d.k_zero_point, l) : 0;
         const int32_t vz = va ? field(d.v_zero_point, l) : 0;
-        float kv[KQ];
-        {
-          uint32_t w[KQ];
-          unpack_k(cur, kf, w);
-          pg_decode(kf, w, 0, kz, kv);
-        }
-        float vv[4][MT];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          uint32_t w[MT];
-          unpack_v(cur, c, vf, w);
-          pg_decode(vf, w, 0, vz, vv[c]);
-        }
         float x[4];
         float bm = -INFINITY;
         {
 #pragma clang fp contract(off)
-          f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-          for (int k2 = 0; k2 < KQ; ++k2)
-            sc = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[k2], qf[k2], sc, 0, 0, 0);
+          const f32x4 sc = pg_tile_scores<D, QBF>(kf, cur, qf, qb, kz);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             x[r] = i + int32_t(qg) + 4 * r < len ? sc[r] * ks : -INFINITY;
@@ -488,11 +569,7 @@ __global__ __launch_bounds__(kPgBlock) void paged_attention_kernel(PgAttArgs a) 
           }
           m = mn;
         }
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-#pragma unroll
-          for (int t = 0; t < MT; ++t)
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv[c][t], pw[c], acc[t], 0, 0, 0);
+        pg_tile_values<D>(vf, cur, pw, vz, acc);
         l = ln;
         i = in_;
         if constexpr (kPgPrefetch<D>) {
@@ -894,12 +971,19 @@ extern "C" int swrt_paged_attention(int n_layers, const swrt_paged_layer *layers
   static_assert(sizeof(PgAttArgs) <= 4096, "kernel arguments exceed 4 KiB");
   const dim3 grid((uint32_t(a.items) + kPgWaves - 1) / kPgWaves);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool qbf = q_type == SWRT_XF_BF16;
+#define SWRT_PG_LAUNCH(DD)                                                                      \
+  if (qbf)                                                                                      \
+    hipLaunchKernelGGL((paged_attention_kernel<DD, true>), grid, dim3(kPgBlock), 0, s, a);      \
+  else                                                                                          \
+    hipLaunchKernelGGL((paged_attention_kernel<DD, false>), grid, dim3(kPgBlock), 0, s, a);
   switch (head_dim) {
-    case 32: hipLaunchKernelGGL(paged_attention_kernel<32>, grid, dim3(kPgBlock), 0, s, a); break;
-    case 64: hipLaunchKernelGGL(paged_attention_kernel<64>, grid, dim3(kPgBlock), 0, s, a); break;
-    case 128: hipLaunchKernelGGL(paged_attention_kernel<128>, grid, dim3(kPgBlock), 0, s, a); break;
-    default: hipLaunchKernelGGL(paged_attention_kernel<256>, grid, dim3(kPgBlock), 0, s, a); break;
+    case 32: SWRT_PG_LAUNCH(32) break;
+    case 64: SWRT_PG_LAUNCH(64) break;
+    case 128: SWRT_PG_LAUNCH(128) break;
+    default: SWRT_PG_LAUNCH(256) break;
   }
+#undef SWRT_PG_LAUNCH
   return launch_status();
 }
 

@@ -355,3 +355,58 @@ def test_window_attention_rejects(L):
     assert att(out=B_ + 64) == INV                           # output inside a cache
     assert att(lens=0) == INV and att(n=33) == INV
     assert att(n=0) == swrt.OK and att(B=0) == swrt.OK
+
+
+@no_gpu_visible
+def test_paged_rejects(L):
+    """Host-side checks of the paged entry points (nothing is launched)."""
+    INV, UNS = swrt.E_INVALID_ARG, swrt.E_UNSUPPORTED
+    launched = (swrt.OK, swrt.E_LAUNCH)
+
+    def layer(**kw):
+        f = dict(q=A, out=D_, arena=B_, arena_bytes=4096, pages=C_, n_pages=4,
+                 page_ptr=C_ + 0x1000, page_ids=C_ + 0x2000, n_ids=4)
+        f.update(kw)
+        return swrt.PagedLayer(*[f[n] for n, _ in swrt.PagedLayer._fields_])
+
+    def att(layers=None, lw=-1, B=2, Hq=8, Hkv=2, D=64, scale=0.125, qt=3, ot=3, n=1):
+        arr = (swrt.PagedLayer * n)(*([layer()] * n if layers is None else layers))
+        return L.swrt_paged_attention(n, ctypes.cast(arr, ctypes.c_void_p), lw, B, Hq, Hkv, D,
+                                      scale, qt, ot, None, None)
+    assert att() in launched
+    assert att(D=48) == UNS and att(D=512) == UNS           # head_dim
+    assert att(Hq=64, Hkv=2) == UNS                         # a group of 32 heads
+    assert att(Hq=6, Hkv=4) == INV and att(qt=4) == INV and att(ot=9) == INV
+    assert att(scale=float("nan")) == INV and att(n=33) == INV
+    assert att(layers=[layer(arena_bytes=4100)]) == INV     # not a multiple of 16
+    assert att(layers=[layer(arena=B_ + 8)]) == INV         # arena alignment
+    assert att(layers=[layer(q=A + 8)]) == INV              # query alignment
+    assert att(layers=[layer(out=B_ + 64)]) == INV          # output inside the arena
+    assert att(layers=[layer(page_ptr=None)]) == INV
+    assert att(n=0) == swrt.OK and att(B=0) == swrt.OK
+
+    def quant(arena=B_, ab=4096, pin=C_, n=4, bl=C_ + 0x2000, nb=1, dst=C_ + 0x3000, fb=2048,
+              fe=4096, pout=C_, kf=4, ks=0.1, kz=0, vf=4, vs=0.1, vz=0, D=64, flags=D_ + 0x100000):
+        return L.swrt_paged_quantize(arena, ab, pin, n, bl, nb, dst, fb, fe, pout, kf, ks, kz, vf,
+                                     vs, vz, D, flags, None)
+    assert quant() in launched
+    assert quant(kf=10) == INV and quant(ks=0.0) == INV and quant(kz=200) == INV
+    assert quant(vf=9, vz=4) == INV                         # uint2 zero point past 3
+    assert quant(fb=5000) == INV and quant(fe=8192) == INV and quant(fb=3000, fe=2000) == INV
+    assert quant(flags=None) == INV                         # the flag word is required
+    assert quant(D=40) == INV and quant(nb=5) == INV
+    assert quant(pout=B_ + 16) == INV                       # descriptors inside the arena
+
+    def app(layers=None, n=1, S=8, D=64, nt=3):
+        arr = (swrt.PagedLayer * n)(*([layer()] * n if layers is None else layers))
+        kn = (ctypes.c_void_p * n)(*[D_ + 0x200000 * (i + 1) for i in range(n)])
+        vn = (ctypes.c_void_p * n)(*[D_ + 0x200000 * (i + 1) + 0x100000 for i in range(n)])
+        return L.swrt_paged_append(n, ctypes.cast(arr, ctypes.c_void_p), kn, vn, nt, S, D,
+                                   None, None)
+    assert app() in launched
+    three = [layer(arena=B_ + 0x10000 * i) for i in range(3)]
+    assert app(layers=three, n=3) in launched               # three arenas, one block table
+    assert app(n=3) == INV                                  # one arena written by three layers
+    assert app(layers=[three[0], layer(arena=B_ + 0x20000, page_ids=C_ + 0x5000)], n=2) == INV
+    assert app(D=40) == INV and app(nt=4) == INV and app(n=33) == INV
+    assert app(layers=[layer(arena_bytes=4104)]) == INV
