@@ -130,6 +130,11 @@ __device__ __forceinline__ float pg_elem(const uint32_t *w, int e, int32_t zp) {
     return __uint_as_float(e & 1 ? w[e / 2] & 0xFFFF0000u : w[e / 2] << 16);
   } else if constexpr (FMT == SWRT_XF_F16) {
     return float(__builtin_bit_cast(_Float16, uint16_t(w[e / 2] >> (16 * (e & 1)))));
+  } else if constexpr (FMT == SWRT_XF_UINT8) {
+    return float((w[e / 4] >> (8 * (e % 4))) & 0xFFu) - float(zp);  // a byte conversion, exact
+  } else if constexpr (FMT == SWRT_XF_INT8) {
+    // c - zp = (c + 128) - (zp + 128), and c + 128 is the byte with its top bit flipped
+    return float(((w[e / 4] ^ 0x80808080u) >> (8 * (e % 4))) & 0xFFu) - float(zp + 128);
   } else {
     constexpr int B = pg_bits(FMT);
     const uint32_t raw = (w[e * B / 32] >> (e * B % 32)) & ((1u << B) - 1u);
@@ -137,6 +142,11 @@ __device__ __forceinline__ float pg_elem(const uint32_t *w, int e, int32_t zp) {
     if constexpr (pg_signed(FMT)) c = int32_t(raw << (32 - B)) >> (32 - B);
     return float(c - zp);
   }
+}
+
+// the bf16 halves (top 16 bits) of two binary32 values, a in the low half
+__device__ __forceinline__ uint32_t pg_pack_hi(float a, float b) {
+  return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
 }
 
 // the first n bytes (1, 2, 4, 8 or a multiple of 16, at most 4 * NW; uniform
@@ -303,10 +313,8 @@ __device__ __forceinline__ f32x4 pg_tile_scores_t(const PgTile<D> &t, const floa
     for (int i = 0; i < KQ / 2; ++i) {
       if constexpr (KF == SWRT_XF_BF16) {
         kw[i] = w[i];
-      } else {
-        const uint32_t lo = __float_as_uint(pg_elem<KF>(w, 2 * i, kz));
-        const uint32_t hi = __float_as_uint(pg_elem<KF>(w, 2 * i + 1, kz));
-        kw[i] = (lo >> 16) | (hi & 0xFFFF0000u);  // |c - zp| <= 255: exact in bf16
+      } else {  // |c - zp| <= 255: exact in bf16
+        kw[i] = pg_pack_hi(pg_elem<KF>(w, 2 * i, kz), pg_elem<KF>(w, 2 * i + 1, kz));
       }
     }
 #pragma unroll
@@ -323,18 +331,68 @@ __device__ __forceinline__ f32x4 pg_tile_scores_t(const PgTile<D> &t, const floa
   return sc;
 }
 
-// the tile's weighted values, V in format VF, into the accumulators
+typedef short pg_s16x4 __attribute__((ext_vector_type(4)));
+
+// binary32 weights as three bf16 parts each, packed in pairs: truncating to
+// the top 8 significant bits leaves an exact remainder, so the three parts
+// add up to the weight exactly (24 significant bits)
+__device__ __forceinline__ void pg_split3(const float (&pw)[4], uint32_t (&pb)[3][2]) {
+  float part[3][4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float x = pw[r];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      part[k][r] = __uint_as_float(__float_as_uint(x) & 0xFFFF0000u);
+      x = x - part[k][r];  // exact
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    pb[k][0] = pg_pack_hi(part[k][0], part[k][1]);
+    pb[k][1] = pg_pack_hi(part[k][2], part[k][3]);
+  }
+}
+
+// the tile's weighted values, V in format VF, into the accumulators. Lane
+// (j, q) holds rows q + 4 c (c = 0..3) of V, elements MT j .. MT j + MT - 1,
+// and the weights of the same rows. bf16 and affine V go through
+// v_mfma_f32_16x16x16_bf16 (its four k-slots per lane are those four rows;
+// V exact in bf16, the weights as three exact bf16 parts), fp32 and f16 V
+// through v_mfma_f32_16x16x4_f32 (one row per instruction).
 template <int D, int VF>
 __device__ __forceinline__ void pg_tile_values_t(const PgTile<D> &t, const float (&pw)[4], int32_t vz,
                                                  f32x4 (&acc)[D / 16]) {
   constexpr int MT = D / 16;
+  uint32_t w[4][MT];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    uint32_t w[MT];
-    pg_chunk_words<MT, MT * pg_bits(VF)>(t.vb[c], t.vbit[c], w);
+  for (int c = 0; c < 4; ++c) pg_chunk_words<MT, MT * pg_bits(VF)>(t.vb[c], t.vbit[c], w[c]);
+  if constexpr (VF == SWRT_XF_BF16 || pg_affine(VF)) {
+    uint32_t pb[3][2];
+    pg_split3(pw, pb);
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
-      acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(pg_elem<VF>(w, m, vz), pw[c], acc[m], 0, 0, 0);
+    for (int m = 0; m < MT; ++m) {
+      uint32_t lo, hi;  // element m of rows 0, 1 and of rows 2, 3, as bf16 pairs
+      if constexpr (VF == SWRT_XF_BF16) {
+        const uint32_t sel = m % 2 ? 0x07060302u : 0x05040100u;
+        lo = __builtin_amdgcn_perm(w[1][m / 2], w[0][m / 2], sel);
+        hi = __builtin_amdgcn_perm(w[3][m / 2], w[2][m / 2], sel);
+      } else {  // |c - zp| <= 255: exact in bf16
+        lo = pg_pack_hi(pg_elem<VF>(w[0], m, vz), pg_elem<VF>(w[1], m, vz));
+        hi = pg_pack_hi(pg_elem<VF>(w[2], m, vz), pg_elem<VF>(w[3], m, vz));
+      }
+      const pg_s16x4 a = __builtin_bit_cast(pg_s16x4, u32x2{lo, hi});
+#pragma unroll
+      for (int k = 2; k >= 0; --k)  // the small parts first
+        acc[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+            a, __builtin_bit_cast(pg_s16x4, u32x2{pb[k][0], pb[k][1]}), acc[m], 0, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+        acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(pg_elem<VF>(w[c], m, vz), pw[c], acc[m], 0, 0, 0);
   }
 }
 
