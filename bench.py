@@ -58,6 +58,8 @@ MEASURED_TRAFFIC = {
     ("bf16", "window_in_place", "f3fee1005c69ec6b"): {"read": 195_175_201, "written": 196_001_407},
     ("bf16", "window_attention_mfma", "a37d64d0de573e74"): {"read": 202_241_968,
                                                            "written": 6_291_474},
+    ("bf16+int8", "paged_attention_kernel", "4247f5b9ce345eee"): {"read": 128_010_351,
+                                                                 "written": 6_291_418},
 }
 _CSRC = "sliding_window_ring_tensor_amd/csrc/"
 KERNEL_SOURCES = {
