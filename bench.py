@@ -66,10 +66,11 @@ KERNEL_SOURCES = {
     "window_in_place": ("kv_window.hip", "window_device.hpp", "xf_device.hpp", "swrt_device.hpp"),
     "decode_step_kernel": ("decode_step.hip", "window_device.hpp", "scatter_device.hpp",
                            "xf_device.hpp", "swrt_device.hpp"),
-    "paged_attention_kernel": ("paged.hip", "xf_device.hpp", "swrt_device.hpp", "../build.py"),
+    "paged_attention_kernel": ("paged.hip", "att_device.hpp", "xf_device.hpp", "swrt_device.hpp",
+                               "../build.py"),
     # the attention kernel's code also depends on a code-generation flag of the build
-    "window_attention_mfma": ("window_attention.hip", "xf_device.hpp", "swrt_device.hpp",
-                              "../build.py"),
+    "window_attention_mfma": ("window_attention.hip", "att_device.hpp", "xf_device.hpp",
+                              "swrt_device.hpp", "../build.py"),
 }
 
 

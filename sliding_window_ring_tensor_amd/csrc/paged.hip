@@ -25,6 +25,7 @@
 //                           into its last page, encoded; then, once per
 //                           distinct block table, the page's length + 1.
 #include "swrt_host.hpp"
+#include "att_device.hpp"
 
 namespace swrt {
 namespace {
@@ -144,10 +145,6 @@ __device__ __forceinline__ float pg_elem(const uint32_t *w, int e, int32_t zp) {
   }
 }
 
-// the bf16 halves (top 16 bits) of two binary32 values, a in the low half
-__device__ __forceinline__ uint32_t pg_pack_hi(float a, float b) {
-  return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
-}
 
 // the first n bytes (1, 2, 4, 8 or a multiple of 16, at most 4 * NW; uniform
 // in the wave) of a payload chunk as 32-bit words
@@ -314,7 +311,7 @@ __device__ __forceinline__ f32x4 pg_tile_scores_t(const PgTile<D> &t, const floa
       if constexpr (KF == SWRT_XF_BF16) {
         kw[i] = w[i];
       } else {  // |c - zp| <= 255: exact in bf16
-        kw[i] = pg_pack_hi(pg_elem<KF>(w, 2 * i, kz), pg_elem<KF>(w, 2 * i + 1, kz));
+        kw[i] = bf16_pack_hi(pg_elem<KF>(w, 2 * i, kz), pg_elem<KF>(w, 2 * i + 1, kz));
       }
     }
 #pragma unroll
@@ -333,27 +330,6 @@ __device__ __forceinline__ f32x4 pg_tile_scores_t(const PgTile<D> &t, const floa
 
 typedef short pg_s16x4 __attribute__((ext_vector_type(4)));
 
-// binary32 weights as three bf16 parts each, packed in pairs: truncating to
-// the top 8 significant bits leaves an exact remainder, so the three parts
-// add up to the weight exactly (24 significant bits)
-__device__ __forceinline__ void pg_split3(const float (&pw)[4], uint32_t (&pb)[3][2]) {
-  float part[3][4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    float x = pw[r];
-#pragma unroll
-    for (int k = 0; k < 3; ++k) {
-      part[k][r] = __uint_as_float(__float_as_uint(x) & 0xFFFF0000u);
-      x = x - part[k][r];  // exact
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < 3; ++k) {
-    pb[k][0] = pg_pack_hi(part[k][0], part[k][1]);
-    pb[k][1] = pg_pack_hi(part[k][2], part[k][3]);
-  }
-}
-
 // the tile's weighted values, V in format VF, into the accumulators. Lane
 // (j, q) holds rows q + 4 c (c = 0..3) of V, elements MT j .. MT j + MT - 1,
 // and the weights of the same rows. bf16 and affine V go through
@@ -369,7 +345,7 @@ __device__ __forceinline__ void pg_tile_values_t(const PgTile<D> &t, const float
   for (int c = 0; c < 4; ++c) pg_chunk_words<MT, MT * pg_bits(VF)>(t.vb[c], t.vbit[c], w[c]);
   if constexpr (VF == SWRT_XF_BF16 || pg_affine(VF)) {
     uint32_t pb[3][2];
-    pg_split3(pw, pb);
+    bf16_split3(pw, pb);
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       uint32_t lo, hi;  // element m of rows 0, 1 and of rows 2, 3, as bf16 pairs
@@ -378,8 +354,8 @@ __device__ __forceinline__ void pg_tile_values_t(const PgTile<D> &t, const float
         lo = __builtin_amdgcn_perm(w[1][m / 2], w[0][m / 2], sel);
         hi = __builtin_amdgcn_perm(w[3][m / 2], w[2][m / 2], sel);
       } else {  // |c - zp| <= 255: exact in bf16
-        lo = pg_pack_hi(pg_elem<VF>(w[0], m, vz), pg_elem<VF>(w[1], m, vz));
-        hi = pg_pack_hi(pg_elem<VF>(w[2], m, vz), pg_elem<VF>(w[3], m, vz));
+        lo = bf16_pack_hi(pg_elem<VF>(w[0], m, vz), pg_elem<VF>(w[1], m, vz));
+        hi = bf16_pack_hi(pg_elem<VF>(w[2], m, vz), pg_elem<VF>(w[3], m, vz));
       }
       const pg_s16x4 a = __builtin_bit_cast(pg_s16x4, u32x2{lo, hi});
 #pragma unroll

@@ -17,6 +17,7 @@
 // a wave (lane shuffles) and across waves (LDS). Scores use exp2 with log2(e)
 // folded into the scale.
 #include "swrt_host.hpp"
+#include "att_device.hpp"
 
 namespace swrt {
 namespace {
@@ -308,6 +309,7 @@ __global__ __launch_bounds__(kAttBlock) void window_attention_kernel(AttArgs a) 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short att_s16x4 __attribute__((ext_vector_type(4)));
 
 template <int ELEM>
 __device__ __forceinline__ f32x4 score_mfma(u32x4 k, u32x4 q, f32x4 acc) {
@@ -535,15 +537,35 @@ __global__ __launch_bounds__(kAttBlock) void window_attention_mfma(AttArgs a) {
         }
       m = mn;
     }
-    // the block's weighted rows
+    // the block's weighted rows. bf16 V: v_mfma_f32_16x16x16_bf16, whose four
+    // k-slots per lane are the four rows 4 c + q a lane holds (and whose
+    // weights it holds too), each binary32 weight as three exact bf16 parts;
+    // f16 V: v_mfma_f32_16x16x4_f32, one row per instruction
 #pragma unroll
-    for (int t = 0; t < T; ++t)
+    for (int t = 0; t < T; ++t) {
+      if constexpr (ELEM == SWRT_XF_BF16) {
+        uint32_t pb[3][2];
+        bf16_split3(p[t], pb);
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
+        for (int i = 0; i < MT; ++i) {
+          const uint32_t sel = i % 2 ? 0x07060302u : 0x05040100u;
+          const u32x2 va{__builtin_amdgcn_perm(vw[t][1][i / 2], vw[t][0][i / 2], sel),
+                         __builtin_amdgcn_perm(vw[t][3][i / 2], vw[t][2][i / 2], sel)};
 #pragma unroll
-        for (int i = 0; i < MT; ++i)
-          acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(att_elem<ELEM, VB / 4>(vw[t][c], i),
-                                                        p[t][c], acc[i], 0, 0, 0);
+          for (int k = 2; k >= 0; --k)  // the small parts first
+            acc[i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                __builtin_bit_cast(att_s16x4, va),
+                __builtin_bit_cast(att_s16x4, u32x2{pb[k][0], pb[k][1]}), acc[i], 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int i = 0; i < MT; ++i)
+            acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(att_elem<ELEM, VB / 4>(vw[t][c], i),
+                                                          p[t][c], acc[i], 0, 0, 0);
+      }
+    }
     if constexpr (kAttPrefetch) cur = nxt;
   }
 

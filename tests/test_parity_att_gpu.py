@@ -7,14 +7,15 @@ arithmetic, per batch entry and head (u = 2^-24, D = head_dim, S1 = |scale| *
 max over visible rows of sum_d |q_d k_rd|, Vmax = max |v| over visible rows,
 n = visible rows):
 
-  |gpu - oracle| <= 4 * (2 * ((D + 4) u S1 + 2^-21) + (2 n + 64) u) * Vmax
+  |gpu - oracle| <= 4 * (2 * ((D + 4) u S1 + 2^-21) + (4 n + 64) u) * Vmax
                     (+ one output ulp, 2^-8 |oracle| for bf16, 2^-10 for f16)
 
 the first term bounding the relative error of every softmax weight (a score
 is a sum of D products rounded in fp32 in an order the matrix cores fix, at
 most D - 1 roundings of terms bounded by S1, then the scale and the shift by
 the maximum; exp2 is within 2^-22), the second the accumulation of n weighted
-rows and one rescale per block of rows. Dropping or adding a row, a wrong
+rows (with bf16 V each weight enters the value product as three exact bf16
+parts: three additions per row) and one rescale per block of rows. Dropping or adding a row, a wrong
 window edge, a wrong KV head or a missing scale moves the output by about
 Vmax / n, orders of magnitude above the bound.
 """
@@ -74,7 +75,7 @@ def bound(q, k, v, L, W, scale, out_dtype, ref):
             kr, vr = kd[b, h // G, r0:r1], vd[b, h // G, r0:r1]
             s1 = abs(scale) * np.abs(qd[b, h][None, :] * kr).sum(axis=1).max()
             vmax = np.abs(vr).max()
-            tol[b, h] = 4 * (2 * ((D + 4) * U * s1 + 2.0 ** -21) + (2 * (r1 - r0) + 64) * U) * vmax
+            tol[b, h] = 4 * (2 * ((D + 4) * U * s1 + 2.0 ** -21) + (4 * (r1 - r0) + 64) * U) * vmax
     return tol * (1 + ULP[out_dtype]) + ULP[out_dtype] * 1.01 * np.abs(ref) + 1e-30
 
 
