@@ -95,24 +95,41 @@ __device__ __forceinline__ swrt_page pg_read(const swrt_page *pages, int32_t id)
   return pages[__builtin_amdgcn_readfirstlane(id)];
 }
 
+// Payload addresses computed as integers are turned back into pointers to
+// global memory, never generic ones: a generic load also counts on the
+// counter that cross-lane shuffles and scalar loads wait on, so every such
+// wait would stall until all payload loads in flight had landed.
+template <class T>
+__device__ __forceinline__ const __attribute__((address_space(1))) T *pg_g(uintptr_t a) {
+  return (const __attribute__((address_space(1))) T *)a;
+}
+template <class T>
+__device__ __forceinline__ const __attribute__((address_space(1))) T *pg_g(const T *p) {
+  return (const __attribute__((address_space(1))) T *)p;
+}
+template <class T>
+__device__ __forceinline__ __attribute__((address_space(1))) T *pg_gw(T *p) {
+  return (__attribute__((address_space(1))) T *)p;
+}
+
 // NB bytes (1, 2, 4, 8 or a multiple of 16) of a payload as 32-bit words
 template <int NB>
 __device__ __forceinline__ void pg_load_raw(const char *p, uint32_t (&w)[(NB + 3) / 4]) {
   if constexpr (NB == 1) {
-    w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint8_t *>(p));
+    w[0] = __builtin_nontemporal_load(pg_g(reinterpret_cast<const uint8_t *>(p)));
   } else if constexpr (NB == 2) {
-    w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(p));
+    w[0] = __builtin_nontemporal_load(pg_g(reinterpret_cast<const uint16_t *>(p)));
   } else if constexpr (NB == 4) {
-    w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p));
+    w[0] = __builtin_nontemporal_load(pg_g(reinterpret_cast<const uint32_t *>(p)));
   } else if constexpr (NB == 8) {
-    const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+    const u32x2 x = __builtin_nontemporal_load(pg_g(reinterpret_cast<const u32x2 *>(p)));
     w[0] = x.x;
     w[1] = x.y;
   } else {
     static_assert(NB % 16 == 0, "payload chunk");
 #pragma unroll
     for (int i = 0; i < NB / 16; ++i) {
-      const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p) + i);
+      const u32x4 x = __builtin_nontemporal_load(pg_g(reinterpret_cast<const u32x4 *>(p) + i));
       w[4 * i] = x.x;
       w[4 * i + 1] = x.y;
       w[4 * i + 2] = x.z;
@@ -151,11 +168,11 @@ __device__ __forceinline__ float pg_elem(const uint32_t *w, int e, int32_t zp) {
 template <int NW>
 __device__ __forceinline__ void pg_load_bytes(const char *p, int n, uint32_t (&w)[NW]) {
   switch (n) {
-    case 1: w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint8_t *>(p)); break;
-    case 2: w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(p)); break;
-    case 4: w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p)); break;
+    case 1: w[0] = __builtin_nontemporal_load(pg_g(reinterpret_cast<const uint8_t *>(p))); break;
+    case 2: w[0] = __builtin_nontemporal_load(pg_g(reinterpret_cast<const uint16_t *>(p))); break;
+    case 4: w[0] = __builtin_nontemporal_load(pg_g(reinterpret_cast<const uint32_t *>(p))); break;
     case 8: {
-      const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+      const u32x2 x = __builtin_nontemporal_load(pg_g(reinterpret_cast<const u32x2 *>(p)));
       w[0] = x.x;
       w[1] = x.y;
       break;
@@ -164,7 +181,7 @@ __device__ __forceinline__ void pg_load_bytes(const char *p, int n, uint32_t (&w
 #pragma unroll
       for (int i = 0; i < (NW + 3) / 4; ++i)
         if (16 * i < n) {
-          const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p) + i);
+          const u32x4 x = __builtin_nontemporal_load(pg_g(reinterpret_cast<const u32x4 *>(p) + i));
           if (4 * i < NW) w[4 * i] = x.x;
           if (4 * i + 1 < NW) w[4 * i + 1] = x.y;
           if (4 * i + 2 < NW) w[4 * i + 2] = x.z;
@@ -253,16 +270,45 @@ struct PgAttArgs {
 
 // A tile's raw payload for one lane: the 16-byte aligned blocks holding its
 // K chunk (D/4 elements of row pk) and its four V chunks (D/16 elements of
-// rows 4 c + q), with each chunk's first bit inside its first block.
+// rows 4 c + q), with each chunk's first bit inside its first block. The
+// blocks hold a chunk of up to 16 bits per element; a larger fp32 chunk
+// (kF32K, kF32V) is loaded by its own tile code instead.
 template <int D>
 struct PgTile {
   static constexpr int KQ = D / 4, MT = D / 16;
-  static constexpr int KB = KQ * 4 / 16 > 0 ? KQ * 4 / 16 : 1;  // blocks of an fp32 K chunk
-  static constexpr int VB = MT * 4 / 16 > 0 ? MT * 4 / 16 : 1;  // blocks of an fp32 V chunk
+  static constexpr int KB = KQ * 2 / 16 > 0 ? KQ * 2 / 16 : 1;  // blocks of a 16-bit K chunk
+  static constexpr int VB = MT * 2 / 16 > 0 ? MT * 2 / 16 : 1;  // blocks of a 16-bit V chunk
+  static constexpr bool kF32K = KQ * 4 > 16 * KB, kF32V = MT * 4 > 16 * VB;
   u32x4 kb[KB];
   u32x4 vb[4][VB];
   uint32_t kbit;
   uint32_t vbit[4];
+};
+
+// One lane's query operand: head slot j's D/4 dimensions of lane group q, as
+// bf16 pairs for a bf16 query (the values are exactly bf16), else in binary32.
+template <int D, bool QBF>
+struct PgQuery;
+template <int D>
+struct PgQuery<D, true> {
+  uint32_t b[D / 8];
+  __device__ __forceinline__ void set(const float (&v)[D / 4]) {
+#pragma unroll
+    for (int i = 0; i < D / 8; ++i)
+      b[i] = (__float_as_uint(v[2 * i]) >> 16) | (__float_as_uint(v[2 * i + 1]) & 0xFFFF0000u);
+  }
+  __device__ __forceinline__ float f(int e) const {
+    return __uint_as_float(e & 1 ? b[e / 2] & 0xFFFF0000u : b[e / 2] << 16);
+  }
+};
+template <int D>
+struct PgQuery<D, false> {
+  float v[D / 4];
+  __device__ __forceinline__ void set(const float (&x)[D / 4]) {
+#pragma unroll
+    for (int i = 0; i < D / 4; ++i) v[i] = x[i];
+  }
+  __device__ __forceinline__ float f(int e) const { return v[e]; }
 };
 
 // word k of a block, k chosen per lane: selects on k's two bits (a chain of
@@ -291,6 +337,23 @@ __device__ __forceinline__ void pg_chunk_words(const u32x4 (&blk)[NB], uint32_t 
   }
 }
 
+// reductions over the four lanes of a head slot (l, l ^ 16, l ^ 32, l ^ 48)
+// with the row and half-wave swaps: plain VALU work, no LDS round trip.
+// Each step combines a lane's value with its partner's in either order,
+// and max and + are commutative, so all four lanes end with the same value.
+__device__ __forceinline__ float pg_max4(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float pg_sum4(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 typedef __bf16 pg_bf16x8 __attribute__((ext_vector_type(8)));
 
 // the tile's scores before scaling, K in format KF: on the bf16 matrix
@@ -298,11 +361,9 @@ typedef __bf16 pg_bf16x8 __attribute__((ext_vector_type(8)));
 // as the exact bf16 integers c - zp; every product is exact), else on the
 // fp32 one with K widened to binary32
 template <int D, int KF, bool QBF>
-__device__ __forceinline__ f32x4 pg_tile_scores_t(const PgTile<D> &t, const float (&qf)[D / 4],
-                                                  const uint32_t (&qb)[D / 8], int32_t kz) {
+__device__ __forceinline__ f32x4 pg_scores_words(const uint32_t (&w)[D / 4], const PgQuery<D, QBF> &q,
+                                                 int32_t kz) {
   constexpr int KQ = D / 4;
-  uint32_t w[KQ];
-  pg_chunk_words<KQ, KQ * pg_bits(KF)>(t.kb, t.kbit, w);
   f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
   if constexpr (QBF && KF != SWRT_XF_F32 && KF != SWRT_XF_F16) {
     uint32_t kw[KQ / 2];
@@ -318,14 +379,22 @@ __device__ __forceinline__ f32x4 pg_tile_scores_t(const PgTile<D> &t, const floa
     for (int st = 0; st < KQ / 8; ++st)
       sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
           __builtin_bit_cast(pg_bf16x8, u32x4{kw[4 * st], kw[4 * st + 1], kw[4 * st + 2], kw[4 * st + 3]}),
-          __builtin_bit_cast(pg_bf16x8, u32x4{qb[4 * st], qb[4 * st + 1], qb[4 * st + 2], qb[4 * st + 3]}),
+          __builtin_bit_cast(pg_bf16x8, u32x4{q.b[4 * st], q.b[4 * st + 1], q.b[4 * st + 2], q.b[4 * st + 3]}),
           sc, 0, 0, 0);
   } else {
 #pragma unroll
     for (int e = 0; e < KQ; ++e)
-      sc = __builtin_amdgcn_mfma_f32_16x16x4f32(pg_elem<KF>(w, e, kz), qf[e], sc, 0, 0, 0);
+      sc = __builtin_amdgcn_mfma_f32_16x16x4f32(pg_elem<KF>(w, e, kz), q.f(e), sc, 0, 0, 0);
   }
   return sc;
+}
+
+template <int D, int KF, bool QBF>
+__device__ __forceinline__ f32x4 pg_tile_scores_t(const PgTile<D> &t, const PgQuery<D, QBF> &q, int32_t kz) {
+  constexpr int KQ = D / 4;
+  uint32_t w[KQ];
+  pg_chunk_words<KQ, KQ * pg_bits(KF)>(t.kb, t.kbit, w);
+  return pg_scores_words<D, KF, QBF>(w, q, kz);
 }
 
 typedef short pg_s16x4 __attribute__((ext_vector_type(4)));
@@ -337,12 +406,9 @@ typedef short pg_s16x4 __attribute__((ext_vector_type(4)));
 // V exact in bf16, the weights as three exact bf16 parts), fp32 and f16 V
 // through v_mfma_f32_16x16x4_f32 (one row per instruction).
 template <int D, int VF>
-__device__ __forceinline__ void pg_tile_values_t(const PgTile<D> &t, const float (&pw)[4], int32_t vz,
-                                                 f32x4 (&acc)[D / 16]) {
+__device__ __forceinline__ void pg_values_words(const uint32_t (&w)[4][D / 16], const float (&pw)[4],
+                                                int32_t vz, f32x4 (&acc)[D / 16]) {
   constexpr int MT = D / 16;
-  uint32_t w[4][MT];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) pg_chunk_words<MT, MT * pg_bits(VF)>(t.vb[c], t.vbit[c], w[c]);
   if constexpr (VF == SWRT_XF_BF16 || pg_affine(VF)) {
     uint32_t pb[3][2];
     bf16_split3(pw, pb);
@@ -372,19 +438,34 @@ __device__ __forceinline__ void pg_tile_values_t(const PgTile<D> &t, const float
   }
 }
 
-#define SWRT_PG_FORMATS(X) \
-  X(SWRT_XF_F32) X(SWRT_XF_F16) X(SWRT_XF_BF16) X(SWRT_XF_INT8) X(SWRT_XF_UINT8) \
-  X(SWRT_XF_INT4) X(SWRT_XF_UINT4) X(SWRT_XF_INT2)
+template <int D, int VF>
+__device__ __forceinline__ void pg_tile_values_t(const PgTile<D> &t, const float (&pw)[4], int32_t vz,
+                                                 f32x4 (&acc)[D / 16]) {
+  constexpr int MT = D / 16;
+  uint32_t w[4][MT];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) pg_chunk_words<MT, MT * pg_bits(VF)>(t.vb[c], t.vbit[c], w[c]);
+  pg_values_words<D, VF>(w, pw, vz, acc);
+}
 
+// every format but fp32 and the last one (the switch's default)
+#define SWRT_PG_FORMATS(X) \
+  X(SWRT_XF_F16) X(SWRT_XF_BF16) X(SWRT_XF_INT8) X(SWRT_XF_UINT8) X(SWRT_XF_INT4) \
+  X(SWRT_XF_UINT4) X(SWRT_XF_INT2)
+
+// an fp32 page reaches these only when its chunk fits the tile's blocks
 template <int D, bool QBF>
-__device__ __forceinline__ f32x4 pg_tile_scores(int kf, const PgTile<D> &t, const float (&qf)[D / 4],
-                                                const uint32_t (&qb)[D / 8], int32_t kz) {
+__device__ __forceinline__ f32x4 pg_tile_scores(int kf, const PgTile<D> &t, const PgQuery<D, QBF> &q,
+                                                int32_t kz) {
   switch (kf) {  // uniform in the wave
+    case SWRT_XF_F32:
+      if constexpr (!PgTile<D>::kF32K) return pg_tile_scores_t<D, SWRT_XF_F32, QBF>(t, q, kz);
+      return f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #define SWRT_PG_K(F) \
-  case F: return pg_tile_scores_t<D, F, QBF>(t, qf, qb, kz);
+  case F: return pg_tile_scores_t<D, F, QBF>(t, q, kz);
     SWRT_PG_FORMATS(SWRT_PG_K)
 #undef SWRT_PG_K
-    default: return pg_tile_scores_t<D, SWRT_XF_UINT2, QBF>(t, qf, qb, kz);
+    default: return pg_tile_scores_t<D, SWRT_XF_UINT2, QBF>(t, q, kz);
   }
 }
 
@@ -392,6 +473,9 @@ template <int D>
 __device__ __forceinline__ void pg_tile_values(int vf, const PgTile<D> &t, const float (&pw)[4],
                                                int32_t vz, f32x4 (&acc)[D / 16]) {
   switch (vf) {  // uniform in the wave
+    case SWRT_XF_F32:
+      if constexpr (!PgTile<D>::kF32V) pg_tile_values_t<D, SWRT_XF_F32>(t, pw, vz, acc);
+      break;
 #define SWRT_PG_V(F) \
   case F: pg_tile_values_t<D, F>(t, pw, vz, acc); break;
     SWRT_PG_FORMATS(SWRT_PG_V)
@@ -424,22 +508,18 @@ __global__ __launch_bounds__(kPgBlock) void paged_attention_kernel(PgAttArgs a) 
   const bool head = int(j) < G;
   const int64_t s = int64_t(b) * a.Hkv + g;
 
-  // query operand: head slot j's dimensions of lane group qg, in binary32
-  float qf[KQ];
+  // query operand: head slot j's dimensions of lane group qg
+  PgQuery<D, QBF> q;
   {
+    float qf[KQ];
     const uint64_t qrow = uint64_t(b) * a.Hq + g * G + (head ? j : 0);
     const int qes = a.q_type == SWRT_XF_F32 ? 4 : 2;
     const char *qp = P.q + qrow * uint64_t(D) * qes;
     pg_load_decode<KQ>(a.q_type, qp, qg * KQ, 0, qf);
 #pragma unroll
     for (int k = 0; k < KQ; ++k) qf[k] = head ? qf[k] : 0.0f;
+    q.set(qf);
   }
-  // the same dimensions as bf16 pairs (a bf16 query only)
-  uint32_t qb[KQ / 2];
-#pragma unroll
-  for (int i = 0; i < KQ / 2; ++i)
-    qb[i] = QBF ? (__float_as_uint(qf[2 * i]) >> 16) | (__float_as_uint(qf[2 * i + 1]) & 0xFFFF0000u)
-                : 0u;
 
   float m = -INFINITY, l_sum = 0.0f;
   f32x4 acc[MT];
@@ -522,8 +602,8 @@ __global__ __launch_bounds__(kPgBlock) void paged_attention_kernel(PgAttArgs a) 
         t.kbit = uint32_t(ka & 15) * 8;
 #pragma unroll
         for (int b = 0; b < KB; ++b)
-          t.kb[b] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
-              (ka & ~uintptr_t(15)) + 16 * uintptr_t(b < nkb ? b : 0)));
+          t.kb[b] = __builtin_nontemporal_load(
+              pg_g<u32x4>((ka & ~uintptr_t(15)) + 16 * uintptr_t(b < nkb ? b : 0)));
         const int vbits = MT * pg_bits(vf);  // chunk bits, at least 4
         const int nvb = vbits >= 128 ? vbits / 128 : 1;
         const int64_t vbit = int64_t(j) * vbits;
@@ -535,8 +615,8 @@ __global__ __launch_bounds__(kPgBlock) void paged_attention_kernel(PgAttArgs a) 
           t.vbit[c] = uint32_t(va & 15) * 8 + uint32_t(vbit % 8);
 #pragma unroll
           for (int b = 0; b < VB; ++b)
-            t.vb[c][b] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
-                (va & ~uintptr_t(15)) + 16 * uintptr_t(b < nvb ? b : 0)));
+            t.vb[c][b] = __builtin_nontemporal_load(
+                pg_g<u32x4>((va & ~uintptr_t(15)) + 16 * uintptr_t(b < nvb ? b : 0)));
         }
       };
       auto first_row = [&](int l) {
@@ -572,15 +652,23 @@ __global__ __launch_bounds__(kPgBlock) void paged_attention_kernel(PgAttArgs a) 
         float bm = -INFINITY;
         {
 #pragma clang fp contract(off)
-          const f32x4 sc = pg_tile_scores<D, QBF>(kf, cur, qf, qb, kz);
+          f32x4 sc;
+          if (Tile::kF32K && kf == SWRT_XF_F32) {  // a chunk larger than the tile's blocks
+            uint32_t w[KQ];
+            pg_load_raw<KQ * 4>(P.arena + field64(d.k_offset, l) +
+                                    int64_t(min(i + pk, len - 1)) * (4 * D) + int64_t(qg) * (4 * KQ),
+                                w);
+            sc = pg_scores_words<D, SWRT_XF_F32, QBF>(w, q, 0);
+          } else {
+            sc = pg_tile_scores<D, QBF>(kf, cur, q, kz);
+          }
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             x[r] = i + int32_t(qg) + 4 * r < len ? sc[r] * ks : -INFINITY;
             bm = fmaxf(bm, x[r]);
           }
         }
-        bm = fmaxf(bm, __shfl_xor(bm, 16));
-        bm = fmaxf(bm, __shfl_xor(bm, 32));
+        bm = pg_max4(bm);
         float pw[4];
         {
 #pragma clang fp contract(off)
@@ -603,7 +691,18 @@ __global__ __launch_bounds__(kPgBlock) void paged_attention_kernel(PgAttArgs a) 
           }
           m = mn;
         }
-        pg_tile_values<D>(vf, cur, pw, vz, acc);
+        if (Tile::kF32V && vf == SWRT_XF_F32) {  // chunks larger than the tile's blocks
+          uint32_t w[4][MT];
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            pg_load_raw<MT * 4>(P.arena + field64(d.v_offset, l) +
+                                    int64_t(min(i + 4 * c + int32_t(qg), len - 1)) * (4 * D) +
+                                    int64_t(j) * (4 * MT),
+                                w[c]);
+          pg_values_words<D, SWRT_XF_F32>(w, pw, 0, acc);
+        } else {
+          pg_tile_values<D>(vf, cur, pw, vz, acc);
+        }
         l = ln;
         i = in_;
         if constexpr (kPgPrefetch<D>) {
@@ -618,8 +717,7 @@ __global__ __launch_bounds__(kPgBlock) void paged_attention_kernel(PgAttArgs a) 
     if (a.flags && lane == 0) atomicOr(a.flags, SWRT_FLAG_BAD_PAGES);
     return;
   }
-  l_sum += __shfl_xor(l_sum, 16);
-  l_sum += __shfl_xor(l_sum, 32);
+  l_sum = pg_sum4(l_sum);
   if (!head) return;
   const float inv = l_sum > 0.0f ? 1.0f / l_sum : 0.0f;  // no visible token: zeros
   float y[4 * MT];
@@ -664,8 +762,8 @@ __device__ __forceinline__ void pg_store8_t(char *dst, const float (&y)[8], floa
     uint32_t w[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) w[e] = y[e] != y[e] ? 0x7FC00000u : __float_as_uint(y[e]);
-    __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]}, reinterpret_cast<u32x4 *>(dst));
-    __builtin_nontemporal_store(u32x4{w[4], w[5], w[6], w[7]}, reinterpret_cast<u32x4 *>(dst) + 1);
+    __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]}, pg_gw(reinterpret_cast<u32x4 *>(dst)));
+    __builtin_nontemporal_store(u32x4{w[4], w[5], w[6], w[7]}, pg_gw(reinterpret_cast<u32x4 *>(dst) + 1));
   } else if constexpr (FMT == SWRT_XF_F16 || FMT == SWRT_XF_BF16) {
     uint32_t w[4];
 #pragma unroll
@@ -674,7 +772,7 @@ __device__ __forceinline__ void pg_store8_t(char *dst, const float (&y)[8], floa
       const uint32_t hi = FMT == SWRT_XF_BF16 ? xf_bf16(y[2 * e + 1]) : xf_f16(y[2 * e + 1]);
       w[e] = lo | (hi << 16);
     }
-    __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]}, reinterpret_cast<u32x4 *>(dst));
+    __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]}, pg_gw(reinterpret_cast<u32x4 *>(dst)));
   } else {
     constexpr int B = pg_bits(FMT);
     uint64_t packed = 0;
@@ -685,11 +783,11 @@ __device__ __forceinline__ void pg_store8_t(char *dst, const float (&y)[8], floa
     }
     if constexpr (B == 8) {
       __builtin_nontemporal_store(u32x2{uint32_t(packed), uint32_t(packed >> 32)},
-                                  reinterpret_cast<u32x2 *>(dst));
+                                  pg_gw(reinterpret_cast<u32x2 *>(dst)));
     } else if constexpr (B == 4) {
-      __builtin_nontemporal_store(uint32_t(packed), reinterpret_cast<uint32_t *>(dst));
+      __builtin_nontemporal_store(uint32_t(packed), pg_gw(reinterpret_cast<uint32_t *>(dst)));
     } else {
-      __builtin_nontemporal_store(uint16_t(packed), reinterpret_cast<uint16_t *>(dst));
+      __builtin_nontemporal_store(uint16_t(packed), pg_gw(reinterpret_cast<uint16_t *>(dst)));
     }
   }
 }
