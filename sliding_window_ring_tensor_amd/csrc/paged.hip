@@ -255,11 +255,6 @@ __device__ __forceinline__ void pg_load_decode(int fmt, const char *row, uint32_
 // ---------------------------------------------------------------------------
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// the next tile's payload is loaded before this tile's arithmetic up to
-// head_dim 128 (two sets of raw chunks fit the registers)
-template <int D>
-constexpr bool kPgPrefetch = D <= 128;
-
 struct PgAttArgs {
   PgLayer L[kMaxLayers];
   uint32_t *flags;
@@ -279,6 +274,7 @@ struct PgTile {
   static constexpr int KB = KQ * 2 / 16 > 0 ? KQ * 2 / 16 : 1;  // blocks of a 16-bit K chunk
   static constexpr int VB = MT * 2 / 16 > 0 ? MT * 2 / 16 : 1;  // blocks of a 16-bit V chunk
   static constexpr bool kF32K = KQ * 4 > 16 * KB, kF32V = MT * 4 > 16 * VB;
+  static constexpr int NBLK = KB + 4 * VB;  // blocks per lane
   u32x4 kb[KB];
   u32x4 vb[4][VB];
   uint32_t kbit;
@@ -335,6 +331,15 @@ __device__ __forceinline__ void pg_chunk_words(const u32x4 (&blk)[NB], uint32_t 
 #pragma unroll
     for (int e = 0; e < NW; ++e) w[e] = e == 0 ? s0 : e == 1 ? s1 : 0u;
   }
+}
+
+// One 16-byte block per lane loaded straight into LDS: lane l's block lands
+// at row + 16 l (a wave's 64 blocks side by side), without passing through
+// registers; the wave's vector-memory counter covers it.
+__device__ __forceinline__ void pg_stage_block(uintptr_t src, u32x4 *row) {
+  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void *)src,
+                                   (__attribute__((address_space(3))) void *)row, 16, 0,
+                                   2 /* non-temporal */);
 }
 
 // reductions over the four lanes of a head slot (l, l ^ 16, l ^ 32, l ^ 48)
@@ -497,10 +502,15 @@ template <int D, bool QBF>
 __global__ __launch_bounds__(kPgBlock) void paged_attention_kernel(PgAttArgs a) {
   constexpr int KQ = D / 4;   // dimensions per lane of the score product
   constexpr int MT = D / 16;  // output tiles; V elements per lane and row
-  const uint32_t lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  // per wave: one tile's blocks, block-major, lane-minor
+  __shared__ u32x4 stage_all[kPgWaves][PgTile<D>::NBLK][64];
+  // the wave index is uniform: everything derived from it (the stream, the
+  // layer's pointers) then lives in scalar registers
+  const uint32_t lane = threadIdx.x % 64, wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
   const uint32_t j = lane % 16, qg = lane / 16;
   const uint32_t item = blockIdx.x * kPgWaves + wave;
   if (item >= uint32_t(a.items)) return;
+  u32x4 (&stage)[PgTile<D>::NBLK][64] = stage_all[wave];
   const uint32_t g = item % uint32_t(a.Hkv), b = (item / uint32_t(a.Hkv)) % uint32_t(a.B);
   const uint32_t layer = item / uint32_t(a.Hkv * a.B);
   const PgLayer &P = a.L[layer];
@@ -587,10 +597,11 @@ __global__ __launch_bounds__(kPgBlock) void paged_attention_kernel(PgAttArgs a) 
       };
       using Tile = PgTile<D>;
       constexpr int KB = Tile::KB, VB = Tile::VB;
-      // a tile's blocks, loaded without branches (blocks past a chunk repeat
-      // its first; every block lies inside the arena, whose size is a
-      // multiple of 16)
-      auto load_tile = [&](Tile &t, int l, int32_t i) {
+      // A tile's blocks go straight into the wave's LDS buffer (blocks past a
+      // chunk are not loaded; every block lies inside the arena, whose size
+      // is a multiple of 16), with the lane's bit offsets of its chunks
+      // inside their first blocks.
+      auto stage_tile = [&](int l, int32_t i, uint32_t &kbit, uint32_t (&vbit)[4]) {
         const int kf = field(d.k_format, l), vf = field(d.v_format, l);
         const int32_t len = field(d.length, l);
         const int64_t krow = pg_row_bytes(kf, D), vrow = pg_row_bytes(vf, D);
@@ -599,36 +610,49 @@ __global__ __launch_bounds__(kPgBlock) void paged_attention_kernel(PgAttArgs a) 
         const uintptr_t ka = reinterpret_cast<uintptr_t>(
             P.arena + field64(d.k_offset, l) + int64_t(min(i + pk, len - 1)) * krow +
             int64_t(qg) * kchunk);
-        t.kbit = uint32_t(ka & 15) * 8;
+        kbit = uint32_t(ka & 15) * 8;
 #pragma unroll
         for (int b = 0; b < KB; ++b)
-          t.kb[b] = __builtin_nontemporal_load(
-              pg_g<u32x4>((ka & ~uintptr_t(15)) + 16 * uintptr_t(b < nkb ? b : 0)));
+          if (b < nkb) pg_stage_block((ka & ~uintptr_t(15)) + 16 * uintptr_t(b), stage[b]);
         const int vbits = MT * pg_bits(vf);  // chunk bits, at least 4
         const int nvb = vbits >= 128 ? vbits / 128 : 1;
-        const int64_t vbit = int64_t(j) * vbits;
-        const char *vp = P.arena + field64(d.v_offset, l) + vbit / 8;
+        const int64_t vbit0 = int64_t(j) * vbits;
+        const char *vp = P.arena + field64(d.v_offset, l) + vbit0 / 8;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const uintptr_t va = reinterpret_cast<uintptr_t>(
               vp + int64_t(min(i + 4 * c + int32_t(qg), len - 1)) * vrow);
-          t.vbit[c] = uint32_t(va & 15) * 8 + uint32_t(vbit % 8);
+          vbit[c] = uint32_t(va & 15) * 8 + uint32_t(vbit0 % 8);
 #pragma unroll
           for (int b = 0; b < VB; ++b)
-            t.vb[c][b] = __builtin_nontemporal_load(
-                pg_g<u32x4>((va & ~uintptr_t(15)) + 16 * uintptr_t(b < nvb ? b : 0)));
+            if (b < nvb) pg_stage_block((va & ~uintptr_t(15)) + 16 * uintptr_t(b), stage[KB + c * VB + b]);
         }
       };
       auto first_row = [&](int l) {
         const int64_t st = field64(d.start, l);
         return int32_t(r0 > st ? r0 - st : 0);
       };
-      // the group's visible pages in token order: lanes n_in - 1 .. 0
+      // The group's visible pages in token order: lanes n_in - 1 .. 0. Each
+      // tile waits for its staged blocks, copies them to registers, and only
+      // then stages the next tile into the same buffer, whose loads run
+      // while this tile is computed.
       int l = n_in - 1;
       int32_t i = first_row(l);
-      Tile cur, nxt;
-      load_tile(cur, l, i);
+      uint32_t kbit_n, vbit_n[4];
+      stage_tile(l, i, kbit_n, vbit_n);
       while (l >= 0) {
+        Tile cur;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this tile's blocks have landed
+#pragma unroll
+        for (int b = 0; b < KB; ++b) cur.kb[b] = stage[b][lane];
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int b = 0; b < VB; ++b) cur.vb[c][b] = stage[KB + c * VB + b][lane];
+        cur.kbit = kbit_n;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) cur.vbit[c] = vbit_n[c];
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read out before it is refilled
         // the tile after this one
         int ln = l;
         int32_t in_ = i + 16;
@@ -636,9 +660,7 @@ __global__ __launch_bounds__(kPgBlock) void paged_attention_kernel(PgAttArgs a) 
           ln = l - 1;
           in_ = ln >= 0 ? first_row(ln) : 0;
         }
-        if constexpr (kPgPrefetch<D>) {
-          if (ln >= 0) load_tile(nxt, ln, in_);
-        }
+        if (ln >= 0) stage_tile(ln, in_, kbit_n, vbit_n);
         // this tile: page l's formats and scales
         const int kf = field(d.k_format, l), vf = field(d.v_format, l);
         const int32_t len = field(d.length, l);
@@ -705,11 +727,6 @@ __global__ __launch_bounds__(kPgBlock) void paged_attention_kernel(PgAttArgs a) 
         }
         l = ln;
         i = in_;
-        if constexpr (kPgPrefetch<D>) {
-          cur = nxt;
-        } else {
-          if (l >= 0) load_tile(cur, l, i);
-        }
       }
     }
   }
