@@ -48,18 +48,29 @@ struct PgLayer {
 // ---------------------------------------------------------------------------
 // formats
 // ---------------------------------------------------------------------------
+// Format properties as table lookups (a chain of comparisons on a run-time
+// format would compile to a chain of branches). Nibble f of kPgLogBits is
+// log2 of format f's element bits (0: not a format): F32 5, F16 and BF16 4,
+// INT8 and UINT8 3, INT4 and UINT4 2, INT2 and UINT2 1.
+constexpr uint64_t kPgLogBits = 0x1122334450ull;
 __host__ __device__ constexpr int pg_bits(int f) {
-  return f == SWRT_XF_F32 ? 32
-         : (f == SWRT_XF_F16 || f == SWRT_XF_BF16) ? 16
-         : (f == SWRT_XF_INT8 || f == SWRT_XF_UINT8) ? 8
-         : (f == SWRT_XF_INT4 || f == SWRT_XF_UINT4) ? 4
-         : (f == SWRT_XF_INT2 || f == SWRT_XF_UINT2) ? 2
-                                                     : 0;
+  return f >= 0 && f <= SWRT_XF_UINT2 && ((kPgLogBits >> (4 * f)) & 15) != 0
+             ? 1 << ((kPgLogBits >> (4 * f)) & 15)
+             : 0;
 }
 __host__ __device__ constexpr bool pg_affine(int f) { return f >= SWRT_XF_INT8 && f <= SWRT_XF_UINT2; }
-__host__ __device__ constexpr bool pg_signed(int f) {
-  return f == SWRT_XF_INT8 || f == SWRT_XF_INT4 || f == SWRT_XF_INT2;
+__host__ __device__ constexpr bool pg_signed(int f) {  // INT8, INT4, INT2: bits 4, 6, 8
+  return f >= 0 && f <= SWRT_XF_UINT2 && ((0x150u >> f) & 1u) != 0;
 }
+static_assert(pg_bits(SWRT_XF_F32) == 32 && pg_bits(SWRT_XF_F16) == 16 && pg_bits(SWRT_XF_BF16) == 16 &&
+                  pg_bits(SWRT_XF_INT8) == 8 && pg_bits(SWRT_XF_UINT8) == 8 && pg_bits(SWRT_XF_INT4) == 4 &&
+                  pg_bits(SWRT_XF_UINT4) == 4 && pg_bits(SWRT_XF_INT2) == 2 && pg_bits(SWRT_XF_UINT2) == 2 &&
+                  pg_bits(0) == 0 && pg_bits(10) == 0,
+              "format bits");
+static_assert(pg_signed(SWRT_XF_INT8) && pg_signed(SWRT_XF_INT4) && pg_signed(SWRT_XF_INT2) &&
+                  !pg_signed(SWRT_XF_UINT8) && !pg_signed(SWRT_XF_UINT4) && !pg_signed(SWRT_XF_UINT2) &&
+                  !pg_signed(SWRT_XF_BF16),
+              "signed formats");
 __host__ __device__ constexpr int32_t pg_lo(int f) { return pg_signed(f) ? -(1 << (pg_bits(f) - 1)) : 0; }
 __host__ __device__ constexpr int32_t pg_hi(int f) {
   return pg_signed(f) ? (1 << (pg_bits(f) - 1)) - 1 : (1 << pg_bits(f)) - 1;
@@ -163,63 +174,6 @@ __device__ __forceinline__ float pg_elem(const uint32_t *w, int e, int32_t zp) {
 }
 
 
-// the first n bytes (1, 2, 4, 8 or a multiple of 16, at most 4 * NW; uniform
-// in the wave) of a payload chunk as 32-bit words
-template <int NW>
-__device__ __forceinline__ void pg_load_bytes(const char *p, int n, uint32_t (&w)[NW]) {
-  switch (n) {
-    case 1: w[0] = __builtin_nontemporal_load(pg_g(reinterpret_cast<const uint8_t *>(p))); break;
-    case 2: w[0] = __builtin_nontemporal_load(pg_g(reinterpret_cast<const uint16_t *>(p))); break;
-    case 4: w[0] = __builtin_nontemporal_load(pg_g(reinterpret_cast<const uint32_t *>(p))); break;
-    case 8: {
-      const u32x2 x = __builtin_nontemporal_load(pg_g(reinterpret_cast<const u32x2 *>(p)));
-      w[0] = x.x;
-      w[1] = x.y;
-      break;
-    }
-    default:
-#pragma unroll
-      for (int i = 0; i < (NW + 3) / 4; ++i)
-        if (16 * i < n) {
-          const u32x4 x = __builtin_nontemporal_load(pg_g(reinterpret_cast<const u32x4 *>(p) + i));
-          if (4 * i < NW) w[4 * i] = x.x;
-          if (4 * i + 1 < NW) w[4 * i + 1] = x.y;
-          if (4 * i + 2 < NW) w[4 * i + 2] = x.z;
-          if (4 * i + 3 < NW) w[4 * i + 3] = x.w;
-        }
-      break;
-  }
-}
-
-// N elements of packed words decoded (see pg_elem); a chunk of fewer than 8
-// bits sits `shift` bits up its byte
-template <int N, int NW>
-__device__ __forceinline__ void pg_decode(int fmt, const uint32_t (&w)[NW], int shift, int32_t zp,
-                                          float (&out)[N]) {
-  uint32_t v[NW];
-#pragma unroll
-  for (int i = 0; i < NW; ++i) v[i] = w[i];
-  v[0] >>= shift;
-  switch (fmt) {  // uniform in the wave
-#define SWRT_PG_CASE(F)                                              \
-  case F:                                                            \
-    _Pragma("unroll") for (int e = 0; e < N; ++e) out[e] = pg_elem<F>(v, e, zp); \
-    break;
-    SWRT_PG_CASE(SWRT_XF_F32)
-    SWRT_PG_CASE(SWRT_XF_F16)
-    SWRT_PG_CASE(SWRT_XF_BF16)
-    SWRT_PG_CASE(SWRT_XF_INT8)
-    SWRT_PG_CASE(SWRT_XF_UINT8)
-    SWRT_PG_CASE(SWRT_XF_INT4)
-    SWRT_PG_CASE(SWRT_XF_UINT4)
-    SWRT_PG_CASE(SWRT_XF_INT2)
-    default:
-      _Pragma("unroll") for (int e = 0; e < N; ++e) out[e] = pg_elem<SWRT_XF_UINT2>(v, e, zp);
-      break;
-#undef SWRT_PG_CASE
-  }
-}
-
 // N elements starting at element `first` of a row, decoded (see pg_elem)
 template <int N, int FMT>
 __device__ __forceinline__ void pg_load_decode_t(const char *row, uint32_t first, int32_t zp,
@@ -263,22 +217,19 @@ struct PgAttArgs {
   int32_t B, Hq, Hkv, items, q_type, out_type;
 };
 
-// A tile's raw payload for one lane: the 16-byte aligned blocks holding its
-// K chunk (D/4 elements of row pk) and its four V chunks (D/16 elements of
-// rows 4 c + q), with each chunk's first bit inside its first block. The
-// blocks hold a chunk of up to 16 bits per element; a larger fp32 chunk
-// (kF32K, kF32V) is loaded by its own tile code instead.
+// A tile is up to 16 consecutive rows of one page, staged in LDS as they lie
+// in the page: 16 K rows, then 16 V rows, of up to 16 bits per element (an
+// fp32 page is read from memory by its own tile code). Each lane then reads
+// exactly its chunks: the K chunk of row pk, elements [q D/4, (q + 1) D/4),
+// and the V chunks of rows 4 c + q, elements [MT j, MT (j + 1)). Up to
+// head_dim 128 a wave has two such buffers, so the next tile's rows are
+// staged while this one is computed.
 template <int D>
-struct PgTile {
-  static constexpr int KQ = D / 4, MT = D / 16;
-  static constexpr int KB = KQ * 2 / 16 > 0 ? KQ * 2 / 16 : 1;  // blocks of a 16-bit K chunk
-  static constexpr int VB = MT * 2 / 16 > 0 ? MT * 2 / 16 : 1;  // blocks of a 16-bit V chunk
-  static constexpr bool kF32K = KQ * 4 > 16 * KB, kF32V = MT * 4 > 16 * VB;
-  static constexpr int NBLK = KB + 4 * VB;  // blocks per lane
-  u32x4 kb[KB];
-  u32x4 vb[4][VB];
-  uint32_t kbit;
-  uint32_t vbit[4];
+struct PgStage {
+  static constexpr int BYTES = 16 * D * 2;       // one tile's K (or V) rows
+  static constexpr int NBUF = D <= 128 ? 2 : 1;  // buffers per wave
+  static constexpr int LG_D = D == 32 ? 5 : D == 64 ? 6 : D == 128 ? 7 : 8;
+  static_assert((1 << LG_D) == D, "head_dim");
 };
 
 // One lane's query operand: head slot j's D/4 dimensions of lane group q, as
@@ -307,39 +258,69 @@ struct PgQuery<D, false> {
   __device__ __forceinline__ float f(int e) const { return v[e]; }
 };
 
-// word k of a block, k chosen per lane: selects on k's two bits (a chain of
-// equality tests would become a branch per lane)
-__device__ __forceinline__ uint32_t pg_sel4(u32x4 v, uint32_t k) {
-  const bool odd = (k & 1u) != 0, high = (k & 2u) != 0;
-  const uint32_t lo = odd ? v.y : v.x;
-  const uint32_t hi = odd ? v.w : v.z;
-  return high ? hi : lo;
+// Payload staged straight into LDS, without passing through registers: lane
+// l's 16 (or 4) bytes land at dst + 16 l (dst + 4 l); the wave's
+// vector-memory counter covers the copy.
+__device__ __forceinline__ void pg_stage16(const char *src, char *dst) {
+  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void *)src,
+                                   (__attribute__((address_space(3))) void *)dst, 16, 0,
+                                   2 /* non-temporal */);
+}
+__device__ __forceinline__ void pg_stage4(const char *src, char *dst) {
+  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void *)src,
+                                   (__attribute__((address_space(3))) void *)dst, 4, 0,
+                                   2 /* non-temporal */);
 }
 
-// a chunk of `bits` bits as words from its first bit: 16 bytes or more start a
-// block; a shorter chunk lies inside one (aligned to its size, or a part of
-// a byte). Every word is written so the array stays in registers.
-template <int NW, int BITS, int NB>
-__device__ __forceinline__ void pg_chunk_words(const u32x4 (&blk)[NB], uint32_t bit,
-                                               uint32_t (&w)[NW]) {
-  if constexpr (BITS >= 128) {
-#pragma unroll
-    for (int e = 0; e < NW; ++e) w[e] = e < BITS / 32 ? blk[(e / 4) % NB][e % 4] : 0u;
-  } else {
-    const uint32_t s0 = pg_sel4(blk[0], bit / 32) >> (bit % 32);
-    const uint32_t s1 = BITS > 32 ? pg_sel4(blk[0], (bit / 32 + 1) & 3) : 0u;
-#pragma unroll
-    for (int e = 0; e < NW; ++e) w[e] = e == 0 ? s0 : e == 1 ? s1 : 0u;
+// Rows [i, i + 16) of a page's payload (rows of 2^lg_rb bytes, 8 to 512) to
+// LDS at dst, as they lie in the page. Byte o of the tile comes from row
+// i + o / row bytes; rows past the page's last (len - 1) repeat that row, so
+// every load stays inside the page (scores of such rows are masked).
+__device__ __forceinline__ void pg_stage_rows(const char *page, int32_t i, int32_t len, int lg_rb,
+                                              char *dst, uint32_t lane) {
+  if (lg_rb >= 4) {
+    const int n = lg_rb >= 6 ? 1 << (lg_rb - 6) : 1;  // 16 rows in 1 KiB instructions
+    for (int k = 0; k < n; ++k) {  // uniform
+      const uint32_t o = uint32_t(k) * 1024 + lane * 16;
+      const int32_t r = min(i + int32_t(o >> lg_rb), len - 1);
+      pg_stage16(page + (int64_t(r) << lg_rb) + (o & ((1u << lg_rb) - 1)), dst + k * 1024);
+    }
+  } else {  // 8-byte rows: 128 bytes, four per lane (lanes past 31 repeat the last row)
+    const uint32_t o = min(lane, 31u) * 4;
+    const int32_t r = min(i + int32_t(o >> 3), len - 1);
+    pg_stage4(page + int64_t(r) * 8 + (o & 7), dst);
   }
 }
 
-// One 16-byte block per lane loaded straight into LDS: lane l's block lands
-// at row + 16 l (a wave's 64 blocks side by side), without passing through
-// registers; the wave's vector-memory counter covers it.
-__device__ __forceinline__ void pg_stage_block(uintptr_t src, u32x4 *row) {
-  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void *)src,
-                                   (__attribute__((address_space(3))) void *)row, 16, 0,
-                                   2 /* non-temporal */);
+// NB bytes (1, 2, 4, 8 or a multiple of 16, aligned to min(NB, 16)) of LDS as
+// 32-bit words; words past them are zero
+template <int NB, int NW>
+__device__ __forceinline__ void pg_lds_read(const char *p, uint32_t (&w)[NW]) {
+  constexpr int N = (NB + 3) / 4;
+  static_assert(N <= NW, "chunk words");
+#pragma unroll
+  for (int e = N; e < NW; ++e) w[e] = 0u;
+  if constexpr (NB == 1) {
+    w[0] = *reinterpret_cast<const uint8_t *>(p);
+  } else if constexpr (NB == 2) {
+    w[0] = *reinterpret_cast<const uint16_t *>(p);
+  } else if constexpr (NB == 4) {
+    w[0] = *reinterpret_cast<const uint32_t *>(p);
+  } else if constexpr (NB == 8) {
+    const u32x2 x = *reinterpret_cast<const u32x2 *>(p);
+    w[0] = x.x;
+    w[1] = x.y;
+  } else {
+    static_assert(NB % 16 == 0, "chunk bytes");
+#pragma unroll
+    for (int b = 0; b < NB / 16; ++b) {
+      const u32x4 x = reinterpret_cast<const u32x4 *>(p)[b];
+      w[4 * b] = x.x;
+      w[4 * b + 1] = x.y;
+      w[4 * b + 2] = x.z;
+      w[4 * b + 3] = x.w;
+    }
+  }
 }
 
 // reductions over the four lanes of a head slot (l, l ^ 16, l ^ 32, l ^ 48)
@@ -394,11 +375,13 @@ __device__ __forceinline__ f32x4 pg_scores_words(const uint32_t (&w)[D / 4], con
   return sc;
 }
 
+// the lane's K chunk read from the staged tile kt
 template <int D, int KF, bool QBF>
-__device__ __forceinline__ f32x4 pg_tile_scores_t(const PgTile<D> &t, const PgQuery<D, QBF> &q, int32_t kz) {
-  constexpr int KQ = D / 4;
+__device__ __forceinline__ f32x4 pg_tile_scores_t(const char *kt, uint32_t pk, uint32_t qg,
+                                                  const PgQuery<D, QBF> &q, int32_t kz) {
+  constexpr int KQ = D / 4, NB = KQ * pg_bits(KF) / 8;  // at least 2 bytes
   uint32_t w[KQ];
-  pg_chunk_words<KQ, KQ * pg_bits(KF)>(t.kb, t.kbit, w);
+  pg_lds_read<NB>(kt + pk * (D * pg_bits(KF) / 8) + qg * NB, w);
   return pg_scores_words<D, KF, QBF>(w, q, kz);
 }
 
@@ -443,49 +426,53 @@ __device__ __forceinline__ void pg_values_words(const uint32_t (&w)[4][D / 16], 
   }
 }
 
+// the lane's four V chunks read from the staged tile vt (a chunk of fewer
+// than 8 bits is shifted down from its place in its byte)
 template <int D, int VF>
-__device__ __forceinline__ void pg_tile_values_t(const PgTile<D> &t, const float (&pw)[4], int32_t vz,
-                                                 f32x4 (&acc)[D / 16]) {
-  constexpr int MT = D / 16;
+__device__ __forceinline__ void pg_tile_values_t(const char *vt, uint32_t j, uint32_t qg, const float (&pw)[4],
+                                                 int32_t vz, f32x4 (&acc)[D / 16]) {
+  constexpr int MT = D / 16, BITS = MT * pg_bits(VF), RB = D * pg_bits(VF) / 8;
   uint32_t w[4][MT];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) pg_chunk_words<MT, MT * pg_bits(VF)>(t.vb[c], t.vbit[c], w[c]);
+  for (int c = 0; c < 4; ++c) {
+    const char *row = vt + (4 * c + qg) * RB;
+    if constexpr (BITS >= 8) {
+      pg_lds_read<BITS / 8>(row + j * (BITS / 8), w[c]);
+    } else {
+      pg_lds_read<1>(row + j * BITS / 8, w[c]);
+      w[c][0] >>= (j * BITS) % 8;
+    }
+  }
   pg_values_words<D, VF>(w, pw, vz, acc);
 }
 
-// every format but fp32 and the last one (the switch's default)
+// every staged format but the last one (the switch's default); an fp32 page
+// never reaches these
 #define SWRT_PG_FORMATS(X) \
   X(SWRT_XF_F16) X(SWRT_XF_BF16) X(SWRT_XF_INT8) X(SWRT_XF_UINT8) X(SWRT_XF_INT4) \
   X(SWRT_XF_UINT4) X(SWRT_XF_INT2)
 
-// an fp32 page reaches these only when its chunk fits the tile's blocks
 template <int D, bool QBF>
-__device__ __forceinline__ f32x4 pg_tile_scores(int kf, const PgTile<D> &t, const PgQuery<D, QBF> &q,
-                                                int32_t kz) {
+__device__ __forceinline__ f32x4 pg_tile_scores(int kf, const char *kt, uint32_t pk, uint32_t qg,
+                                                const PgQuery<D, QBF> &q, int32_t kz) {
   switch (kf) {  // uniform in the wave
-    case SWRT_XF_F32:
-      if constexpr (!PgTile<D>::kF32K) return pg_tile_scores_t<D, SWRT_XF_F32, QBF>(t, q, kz);
-      return f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #define SWRT_PG_K(F) \
-  case F: return pg_tile_scores_t<D, F, QBF>(t, q, kz);
+  case F: return pg_tile_scores_t<D, F, QBF>(kt, pk, qg, q, kz);
     SWRT_PG_FORMATS(SWRT_PG_K)
 #undef SWRT_PG_K
-    default: return pg_tile_scores_t<D, SWRT_XF_UINT2, QBF>(t, q, kz);
+    default: return pg_tile_scores_t<D, SWRT_XF_UINT2, QBF>(kt, pk, qg, q, kz);
   }
 }
 
 template <int D>
-__device__ __forceinline__ void pg_tile_values(int vf, const PgTile<D> &t, const float (&pw)[4],
-                                               int32_t vz, f32x4 (&acc)[D / 16]) {
+__device__ __forceinline__ void pg_tile_values(int vf, const char *vt, uint32_t j, uint32_t qg,
+                                               const float (&pw)[4], int32_t vz, f32x4 (&acc)[D / 16]) {
   switch (vf) {  // uniform in the wave
-    case SWRT_XF_F32:
-      if constexpr (!PgTile<D>::kF32V) pg_tile_values_t<D, SWRT_XF_F32>(t, pw, vz, acc);
-      break;
 #define SWRT_PG_V(F) \
-  case F: pg_tile_values_t<D, F>(t, pw, vz, acc); break;
+  case F: pg_tile_values_t<D, F>(vt, j, qg, pw, vz, acc); break;
     SWRT_PG_FORMATS(SWRT_PG_V)
 #undef SWRT_PG_V
-    default: pg_tile_values_t<D, SWRT_XF_UINT2>(t, pw, vz, acc); break;
+    default: pg_tile_values_t<D, SWRT_XF_UINT2>(vt, j, qg, pw, vz, acc); break;
   }
 }
 
@@ -502,15 +489,15 @@ template <int D, bool QBF>
 __global__ __launch_bounds__(kPgBlock) void paged_attention_kernel(PgAttArgs a) {
   constexpr int KQ = D / 4;   // dimensions per lane of the score product
   constexpr int MT = D / 16;  // output tiles; V elements per lane and row
-  // per wave: one tile's blocks, block-major, lane-minor
-  __shared__ u32x4 stage_all[kPgWaves][PgTile<D>::NBLK][64];
+  using Stage = PgStage<D>;
+  __shared__ __attribute__((aligned(16))) char stage_all[kPgWaves][Stage::NBUF][2 * Stage::BYTES];
   // the wave index is uniform: everything derived from it (the stream, the
   // layer's pointers) then lives in scalar registers
   const uint32_t lane = threadIdx.x % 64, wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
   const uint32_t j = lane % 16, qg = lane / 16;
   const uint32_t item = blockIdx.x * kPgWaves + wave;
   if (item >= uint32_t(a.items)) return;
-  u32x4 (&stage)[PgTile<D>::NBLK][64] = stage_all[wave];
+  char *stage = stage_all[wave][0];
   const uint32_t g = item % uint32_t(a.Hkv), b = (item / uint32_t(a.Hkv)) % uint32_t(a.B);
   const uint32_t layer = item / uint32_t(a.Hkv * a.B);
   const PgLayer &P = a.L[layer];
@@ -595,64 +582,31 @@ __global__ __launch_bounds__(kPgBlock) void paged_attention_kernel(PgAttArgs a) 
         return int64_t((uint64_t(uint32_t(field(int32_t(uint64_t(x) >> 32), l))) << 32) |
                        uint32_t(field(int32_t(x), l)));
       };
-      using Tile = PgTile<D>;
-      constexpr int KB = Tile::KB, VB = Tile::VB;
-      // A tile's blocks go straight into the wave's LDS buffer (blocks past a
-      // chunk are not loaded; every block lies inside the arena, whose size
-      // is a multiple of 16), with the lane's bit offsets of its chunks
-      // inside their first blocks.
-      auto stage_tile = [&](int l, int32_t i, uint32_t &kbit, uint32_t (&vbit)[4]) {
+      // Stage rows [i, i + 16) of page l's K and V payloads (an fp32 payload
+      // is read by its tile code instead) into buffer buf.
+      auto stage_tile = [&](int l, int32_t i, int buf) {
         const int kf = field(d.k_format, l), vf = field(d.v_format, l);
         const int32_t len = field(d.length, l);
-        const int64_t krow = pg_row_bytes(kf, D), vrow = pg_row_bytes(vf, D);
-        const int kchunk = KQ * pg_bits(kf) / 8;  // bytes, at least 2
-        const int nkb = kchunk >= 16 ? kchunk / 16 : 1;
-        const uintptr_t ka = reinterpret_cast<uintptr_t>(
-            P.arena + field64(d.k_offset, l) + int64_t(min(i + pk, len - 1)) * krow +
-            int64_t(qg) * kchunk);
-        kbit = uint32_t(ka & 15) * 8;
-#pragma unroll
-        for (int b = 0; b < KB; ++b)
-          if (b < nkb) pg_stage_block((ka & ~uintptr_t(15)) + 16 * uintptr_t(b), stage[b]);
-        const int vbits = MT * pg_bits(vf);  // chunk bits, at least 4
-        const int nvb = vbits >= 128 ? vbits / 128 : 1;
-        const int64_t vbit0 = int64_t(j) * vbits;
-        const char *vp = P.arena + field64(d.v_offset, l) + vbit0 / 8;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const uintptr_t va = reinterpret_cast<uintptr_t>(
-              vp + int64_t(min(i + 4 * c + int32_t(qg), len - 1)) * vrow);
-          vbit[c] = uint32_t(va & 15) * 8 + uint32_t(vbit0 % 8);
-#pragma unroll
-          for (int b = 0; b < VB; ++b)
-            if (b < nvb) pg_stage_block((va & ~uintptr_t(15)) + 16 * uintptr_t(b), stage[KB + c * VB + b]);
-        }
+        char *dst = stage + buf * (2 * Stage::BYTES);
+        if (kf != SWRT_XF_F32)
+          pg_stage_rows(P.arena + field64(d.k_offset, l), i, len,
+                        Stage::LG_D + int((kPgLogBits >> (4 * kf)) & 15) - 3, dst, lane);
+        if (vf != SWRT_XF_F32)
+          pg_stage_rows(P.arena + field64(d.v_offset, l), i, len,
+                        Stage::LG_D + int((kPgLogBits >> (4 * vf)) & 15) - 3, dst + Stage::BYTES, lane);
       };
       auto first_row = [&](int l) {
         const int64_t st = field64(d.start, l);
         return int32_t(r0 > st ? r0 - st : 0);
       };
-      // The group's visible pages in token order: lanes n_in - 1 .. 0. Each
-      // tile waits for its staged blocks, copies them to registers, and only
-      // then stages the next tile into the same buffer, whose loads run
-      // while this tile is computed.
+      // The group's visible pages in token order: lanes n_in - 1 .. 0. With
+      // two buffers the next tile is staged before this one is computed.
       int l = n_in - 1;
       int32_t i = first_row(l);
-      uint32_t kbit_n, vbit_n[4];
-      stage_tile(l, i, kbit_n, vbit_n);
+      int buf = 0;
+      stage_tile(l, i, 0);
       while (l >= 0) {
-        Tile cur;
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this tile's blocks have landed
-#pragma unroll
-        for (int b = 0; b < KB; ++b) cur.kb[b] = stage[b][lane];
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-#pragma unroll
-          for (int b = 0; b < VB; ++b) cur.vb[c][b] = stage[KB + c * VB + b][lane];
-        cur.kbit = kbit_n;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) cur.vbit[c] = vbit_n[c];
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read out before it is refilled
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this tile's rows have landed
         // the tile after this one
         int ln = l;
         int32_t in_ = i + 16;
@@ -660,7 +614,10 @@ __global__ __launch_bounds__(kPgBlock) void paged_attention_kernel(PgAttArgs a) 
           ln = l - 1;
           in_ = ln >= 0 ? first_row(ln) : 0;
         }
-        if (ln >= 0) stage_tile(ln, in_, kbit_n, vbit_n);
+        if constexpr (Stage::NBUF == 2) {
+          if (ln >= 0) stage_tile(ln, in_, buf ^ 1);
+        }
+        const char *kt = stage + buf * (2 * Stage::BYTES), *vt = kt + Stage::BYTES;
         // this tile: page l's formats and scales
         const int kf = field(d.k_format, l), vf = field(d.v_format, l);
         const int32_t len = field(d.length, l);
@@ -675,14 +632,14 @@ __global__ __launch_bounds__(kPgBlock) void paged_attention_kernel(PgAttArgs a) 
         {
 #pragma clang fp contract(off)
           f32x4 sc;
-          if (Tile::kF32K && kf == SWRT_XF_F32) {  // a chunk larger than the tile's blocks
+          if (kf == SWRT_XF_F32) {  // not staged
             uint32_t w[KQ];
             pg_load_raw<KQ * 4>(P.arena + field64(d.k_offset, l) +
                                     int64_t(min(i + pk, len - 1)) * (4 * D) + int64_t(qg) * (4 * KQ),
                                 w);
             sc = pg_scores_words<D, SWRT_XF_F32, QBF>(w, q, 0);
           } else {
-            sc = pg_tile_scores<D, QBF>(kf, cur, q, kz);
+            sc = pg_tile_scores<D, QBF>(kf, kt, pk, qg, q, kz);
           }
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
@@ -713,7 +670,7 @@ __global__ __launch_bounds__(kPgBlock) void paged_attention_kernel(PgAttArgs a) 
           }
           m = mn;
         }
-        if (Tile::kF32V && vf == SWRT_XF_F32) {  // chunks larger than the tile's blocks
+        if (vf == SWRT_XF_F32) {  // not staged
           uint32_t w[4][MT];
 #pragma unroll
           for (int c = 0; c < 4; ++c)
@@ -723,7 +680,13 @@ __global__ __launch_bounds__(kPgBlock) void paged_attention_kernel(PgAttArgs a) 
                                 w[c]);
           pg_values_words<D, SWRT_XF_F32>(w, pw, 0, acc);
         } else {
-          pg_tile_values<D>(vf, cur, pw, vz, acc);
+          pg_tile_values<D>(vf, vt, j, qg, pw, vz, acc);
+        }
+        if constexpr (Stage::NBUF == 2) {
+          buf ^= 1;
+        } else if (ln >= 0) {
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this tile read out before the refill
+          stage_tile(ln, in_, 0);
         }
         l = ln;
         i = in_;
