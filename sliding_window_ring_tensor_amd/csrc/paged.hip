@@ -162,8 +162,7 @@ __device__ __forceinline__ float pg_elem(const uint32_t *w, int e, int32_t zp) {
   } else if constexpr (FMT == SWRT_XF_UINT8) {
     return float((w[e / 4] >> (8 * (e % 4))) & 0xFFu) - float(zp);  // a byte conversion, exact
   } else if constexpr (FMT == SWRT_XF_INT8) {
-    // c - zp = (c + 128) - (zp + 128), and c + 128 is the byte with its top bit flipped
-    return float(((w[e / 4] ^ 0x80808080u) >> (8 * (e % 4))) & 0xFFu) - float(zp + 128);
+    return float(int(int8_t(w[e / 4] >> (8 * (e % 4))))) - float(zp);  // a sign-extending byte conversion
   } else {
     constexpr int B = pg_bits(FMT);
     const uint32_t raw = (w[e * B / 32] >> (e * B % 32)) & ((1u << B) - 1u);
@@ -641,11 +640,15 @@ __global__ __launch_bounds__(kPgBlock) void paged_attention_kernel(PgAttArgs a) 
           } else {
             sc = pg_tile_scores<D, QBF>(kf, kt, pk, qg, q, kz);
           }
+          if (i + 16 <= len) {  // a whole tile (uniform): no row to mask
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            x[r] = i + int32_t(qg) + 4 * r < len ? sc[r] * ks : -INFINITY;
-            bm = fmaxf(bm, x[r]);
+            for (int r = 0; r < 4; ++r) x[r] = sc[r] * ks;
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) x[r] = i + int32_t(qg) + 4 * r < len ? sc[r] * ks : -INFINITY;
           }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) bm = fmaxf(bm, x[r]);
         }
         bm = pg_max4(bm);
         float pw[4];
@@ -661,10 +664,10 @@ __global__ __launch_bounds__(kPgBlock) void paged_attention_kernel(PgAttArgs a) 
 #pragma unroll
             for (int t = 0; t < MT; ++t) acc[t] *= f;
           }
-          const bool none = mn == -INFINITY;
+          const float ms = mn == -INFINITY ? 0.0f : mn;  // no finite score yet: every weight 0
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float w = none ? 0.0f : __builtin_amdgcn_exp2f(x[r] - mn);
+            const float w = __builtin_amdgcn_exp2f(x[r] - ms);
             l_sum += w;
             pw[r] = w * vs;  // an affine page's V scale rides on the weight
           }
