@@ -22,10 +22,11 @@ __device__ __forceinline__ void bf16_split3(const float (&x4)[4], uint32_t (&pb)
   for (int r = 0; r < 4; ++r) {
     float x = x4[r];
 #pragma unroll
-    for (int k = 0; k < 3; ++k) {
+    for (int k = 0; k < 2; ++k) {
       part[k][r] = __uint_as_float(__float_as_uint(x) & 0xFFFF0000u);
       x = x - part[k][r];  // exact
     }
+    part[2][r] = x;  // the packing below keeps its top 16 bits: the truncation
   }
 #pragma unroll
   for (int k = 0; k < 3; ++k) {

@@ -260,12 +260,13 @@ struct PgQuery<D, false> {
 // Payload staged straight into LDS, without passing through registers: lane
 // l's 16 (or 4) bytes land at dst + 16 l (dst + 4 l); the wave's
 // vector-memory counter covers the copy.
-__device__ __forceinline__ void pg_stage16(const char *src, char *dst) {
+typedef const __attribute__((address_space(1))) char *pg_gchar;
+__device__ __forceinline__ void pg_stage16(pg_gchar src, char *dst) {
   __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void *)src,
                                    (__attribute__((address_space(3))) void *)dst, 16, 0,
                                    2 /* non-temporal */);
 }
-__device__ __forceinline__ void pg_stage4(const char *src, char *dst) {
+__device__ __forceinline__ void pg_stage4(pg_gchar src, char *dst) {
   __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void *)src,
                                    (__attribute__((address_space(3))) void *)dst, 4, 0,
                                    2 /* non-temporal */);
@@ -273,21 +274,24 @@ __device__ __forceinline__ void pg_stage4(const char *src, char *dst) {
 
 // Rows [i, i + 16) of a page's payload (rows of 2^lg_rb bytes, 8 to 512) to
 // LDS at dst, as they lie in the page. Byte o of the tile comes from row
-// i + o / row bytes; rows past the page's last (len - 1) repeat that row, so
-// every load stays inside the page (scores of such rows are masked).
-__device__ __forceinline__ void pg_stage_rows(const char *page, int32_t i, int32_t len, int lg_rb,
+// i + o / row bytes; rows past the page's last (lim rows after row i) repeat
+// that row, so every load stays inside the page (scores of such rows are
+// masked). The page's row i is the uniform base; a lane adds a 32-bit offset.
+__device__ __forceinline__ void pg_stage_rows(const char *page, int32_t i, int32_t lim, int lg_rb,
                                               char *dst, uint32_t lane) {
+  const pg_gchar base = pg_gchar(page) + (int64_t(i) << lg_rb);
   if (lg_rb >= 4) {
     const int n = lg_rb >= 6 ? 1 << (lg_rb - 6) : 1;  // 16 rows in 1 KiB instructions
+    const uint32_t in_row = (1u << lg_rb) - 1;
     for (int k = 0; k < n; ++k) {  // uniform
       const uint32_t o = uint32_t(k) * 1024 + lane * 16;
-      const int32_t r = min(i + int32_t(o >> lg_rb), len - 1);
-      pg_stage16(page + (int64_t(r) << lg_rb) + (o & ((1u << lg_rb) - 1)), dst + k * 1024);
+      const uint32_t rr = uint32_t(min(int32_t(o >> lg_rb), lim));
+      pg_stage16(base + ((rr << lg_rb) | (o & in_row)), dst + k * 1024);
     }
   } else {  // 8-byte rows: 128 bytes, four per lane (lanes past 31 repeat the last row)
     const uint32_t o = min(lane, 31u) * 4;
-    const int32_t r = min(i + int32_t(o >> 3), len - 1);
-    pg_stage4(page + int64_t(r) * 8 + (o & 7), dst);
+    const uint32_t rr = uint32_t(min(int32_t(o >> 3), lim));
+    pg_stage4(base + ((rr << 3) | (o & 7)), dst);
   }
 }
 
@@ -500,6 +504,7 @@ __global__ __launch_bounds__(kPgBlock) void paged_attention_kernel(PgAttArgs a) 
   const uint32_t g = item % uint32_t(a.Hkv), b = (item / uint32_t(a.Hkv)) % uint32_t(a.B);
   const uint32_t layer = item / uint32_t(a.Hkv * a.B);
   const PgLayer &P = a.L[layer];
+  const char *const arena = P.arena;
   const int G = a.Hq / a.Hkv;
   const bool head = int(j) < G;
   const int64_t s = int64_t(b) * a.Hkv + g;
@@ -575,57 +580,78 @@ __global__ __launch_bounds__(kPgBlock) void paged_attention_kernel(PgAttArgs a) 
       const int n_in = hits ? h + 1 : 64;
       next_start = int64_t((uint64_t(uint32_t(__builtin_amdgcn_readlane(int(shi), n_in - 1))) << 32) |
                            uint32_t(__builtin_amdgcn_readlane(int(slo), n_in - 1)));
+      // Each lane's page packed for the tile loop: both formats, the row the
+      // window starts at in it, both zero points (each fits 16 bits).
+      const int32_t p_fmt = d.k_format | (d.v_format << 8);
+      const int32_t p_first = r0 > d.start ? int32_t(min(r0 - d.start, int64_t(d.length))) : 0;
+      const int32_t p_zp = (d.k_zero_point & 0xFFFF) | (d.v_zero_point << 16);
       // page l's fields, uniform
       auto field = [&](int32_t x, int l) { return __builtin_amdgcn_readlane(x, l); };
       auto field64 = [&](int64_t x, int l) {
         return int64_t((uint64_t(uint32_t(field(int32_t(uint64_t(x) >> 32), l))) << 32) |
                        uint32_t(field(int32_t(x), l)));
       };
+      // what the tile code needs of page l, uniform
+      struct PgCur {
+        int kf, vf;
+        int32_t len, kz, vz;
+        float ks, vs;
+      };
+      auto cur_of = [&](int l) {
+        PgCur c;
+        const int32_t fmt = field(p_fmt, l), zp = field(p_zp, l);
+        c.kf = fmt & 0xFF;
+        c.vf = fmt >> 8;
+        c.len = field(d.length, l);
+        const bool ka = pg_affine(c.kf), va = pg_affine(c.vf);
+        c.ks = ka ? __int_as_float(field(__float_as_int(d.k_scale), l)) * a.scale_log2 : a.scale_log2;
+        c.vs = va ? __int_as_float(field(__float_as_int(d.v_scale), l)) : 1.0f;
+        c.kz = ka ? int32_t(int16_t(zp)) : 0;
+        c.vz = va ? zp >> 16 : 0;
+        return c;
+      };
       // Stage rows [i, i + 16) of page l's K and V payloads (an fp32 payload
       // is read by its tile code instead) into buffer buf.
-      auto stage_tile = [&](int l, int32_t i, int buf) {
-        const int kf = field(d.k_format, l), vf = field(d.v_format, l);
-        const int32_t len = field(d.length, l);
+      auto stage_tile = [&](int l, int32_t i, int buf, const PgCur &c) {
         char *dst = stage + buf * (2 * Stage::BYTES);
-        if (kf != SWRT_XF_F32)
-          pg_stage_rows(P.arena + field64(d.k_offset, l), i, len,
-                        Stage::LG_D + int((kPgLogBits >> (4 * kf)) & 15) - 3, dst, lane);
-        if (vf != SWRT_XF_F32)
-          pg_stage_rows(P.arena + field64(d.v_offset, l), i, len,
-                        Stage::LG_D + int((kPgLogBits >> (4 * vf)) & 15) - 3, dst + Stage::BYTES, lane);
-      };
-      auto first_row = [&](int l) {
-        const int64_t st = field64(d.start, l);
-        return int32_t(r0 > st ? r0 - st : 0);
+        const int32_t lim = c.len - 1 - i;
+        if (c.kf != SWRT_XF_F32)
+          pg_stage_rows(arena + field64(d.k_offset, l), i, lim,
+                        Stage::LG_D + int((kPgLogBits >> (4 * c.kf)) & 15) - 3, dst, lane);
+        if (c.vf != SWRT_XF_F32)
+          pg_stage_rows(arena + field64(d.v_offset, l), i, lim,
+                        Stage::LG_D + int((kPgLogBits >> (4 * c.vf)) & 15) - 3, dst + Stage::BYTES, lane);
       };
       // The group's visible pages in token order: lanes n_in - 1 .. 0. With
       // two buffers the next tile is staged before this one is computed.
       int l = n_in - 1;
-      int32_t i = first_row(l);
+      int32_t i = field(p_first, l);
+      PgCur c = cur_of(l);
       int buf = 0;
-      stage_tile(l, i, 0);
-      while (l >= 0) {
+      stage_tile(l, i, 0, c);
+      while (true) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this tile's rows have landed
         // the tile after this one
         int ln = l;
         int32_t in_ = i + 16;
-        if (in_ >= field(d.length, l)) {
+        PgCur cn = c;
+        if (in_ >= c.len) {
           ln = l - 1;
-          in_ = ln >= 0 ? first_row(ln) : 0;
+          in_ = 0;
+          if (ln >= 0) {
+            cn = cur_of(ln);
+            in_ = field(p_first, ln);
+          }
         }
         if constexpr (Stage::NBUF == 2) {
-          if (ln >= 0) stage_tile(ln, in_, buf ^ 1);
+          if (ln >= 0) stage_tile(ln, in_, buf ^ 1, cn);
         }
         const char *kt = stage + buf * (2 * Stage::BYTES), *vt = kt + Stage::BYTES;
         // this tile: page l's formats and scales
-        const int kf = field(d.k_format, l), vf = field(d.v_format, l);
-        const int32_t len = field(d.length, l);
-        const bool ka = pg_affine(kf), va = pg_affine(vf);
-        const float ks = ka ? __int_as_float(field(__float_as_int(d.k_scale), l)) * a.scale_log2
-                            : a.scale_log2;
-        const float vs = va ? __int_as_float(field(__float_as_int(d.v_scale), l)) : 1.0f;
-        const int32_t kz = ka ? field(d.k_zero_point, l) : 0;
-        const int32_t vz = va ? field(d.v_zero_point, l) : 0;
+        const int kf = c.kf, vf = c.vf;
+        const int32_t len = c.len;
+        const float ks = c.ks, vs = c.vs;
+        const int32_t kz = c.kz, vz = c.vz;
         float x[4];
         float bm = -INFINITY;
         {
@@ -633,7 +659,7 @@ __global__ __launch_bounds__(kPgBlock) void paged_attention_kernel(PgAttArgs a) 
           f32x4 sc;
           if (kf == SWRT_XF_F32) {  // not staged
             uint32_t w[KQ];
-            pg_load_raw<KQ * 4>(P.arena + field64(d.k_offset, l) +
+            pg_load_raw<KQ * 4>(arena + field64(d.k_offset, l) +
                                     int64_t(min(i + pk, len - 1)) * (4 * D) + int64_t(qg) * (4 * KQ),
                                 w);
             sc = pg_scores_words<D, SWRT_XF_F32, QBF>(w, q, 0);
@@ -677,7 +703,7 @@ __global__ __launch_bounds__(kPgBlock) void paged_attention_kernel(PgAttArgs a) 
           uint32_t w[4][MT];
 #pragma unroll
           for (int c = 0; c < 4; ++c)
-            pg_load_raw<MT * 4>(P.arena + field64(d.v_offset, l) +
+            pg_load_raw<MT * 4>(arena + field64(d.v_offset, l) +
                                     int64_t(min(i + 4 * c + int32_t(qg), len - 1)) * (4 * D) +
                                     int64_t(j) * (4 * MT),
                                 w[c]);
@@ -685,14 +711,16 @@ __global__ __launch_bounds__(kPgBlock) void paged_attention_kernel(PgAttArgs a) 
         } else {
           pg_tile_values<D>(vf, vt, j, qg, pw, vz, acc);
         }
+        if (ln < 0) break;
         if constexpr (Stage::NBUF == 2) {
           buf ^= 1;
-        } else if (ln >= 0) {
+        } else {
           asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this tile read out before the refill
-          stage_tile(ln, in_, 0);
+          stage_tile(ln, in_, 0, cn);
         }
         l = ln;
         i = in_;
+        c = cn;
       }
     }
   }
