@@ -56,9 +56,9 @@ MEASURED_TRAFFIC = {
     ("bf16->int8", "decode_step_kernel", "5a17d20369dcd20b"): {"read": 101_380_857,
                                                                "written": 98_911_877},
     ("bf16", "window_in_place", "f3fee1005c69ec6b"): {"read": 195_175_201, "written": 196_001_407},
-    ("bf16", "window_attention_mfma", "af6718030985a390"): {"read": 202_110_615,
-        "written": 6_291_428},
-    ("bf16+int8", "paged_attention_kernel", "6c4c996198c25a4e"): {"read": 128_008_946,
+    ("bf16", "window_attention_mfma", "4dfda33570bfd571"): {"read": 202_168_298,
+        "written": 6_291_445},
+    ("bf16+int8", "paged_attention_kernel", "9089da8860c9c532"): {"read": 127_913_915,
         "written": 6_291_430},
 }
 _CSRC = "sliding_window_ring_tensor_amd/csrc/"

@@ -9,12 +9,14 @@
 // Three kernel families:
 //   paged_attention_kernel  one wave per (layer, batch entry, KV head) stream:
 //                           finds the pages its window reaches, checks each,
-//                           decodes each 16-row tile of a page in the page's
-//                           formats and runs both contractions on the matrix
-//                           cores in fp32 (the formats differ page to page, so
-//                           every operand is widened to binary32 first;
-//                           affine codes enter as the exact integers c - zp,
-//                           their scales applied to the score and the weight).
+//                           stages each 16-row tile of a page into LDS as it
+//                           lies in the page, decodes it in the page's formats
+//                           and runs both contractions on the matrix cores
+//                           with exact operands (bf16 values and affine codes
+//                           as the exact integers c - zp on the bf16
+//                           instructions, fp32 weights as three exact bf16
+//                           parts; fp32 and f16 pages on the fp32 ones), the
+//                           scales applied to the score and the weight.
 //   paged_validate / paged_convert / paged_publish
 //                           the conversion of selected pages: every check on
 //                           the device first, then the payloads, then the
