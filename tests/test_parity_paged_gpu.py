@@ -101,11 +101,15 @@ def bound(case, tb, q, Hkv, left_window, scale, out_dtype, ref):
             ids = case.page_ids[case.page_ptr[s]:case.page_ptr[s + 1]]
             if len(ids) == 0:
                 continue
-            k = np.concatenate([decode_rows(case.arena, tb[i], D, "k") for i in ids])
-            v = np.concatenate([decode_rows(case.arena, tb[i], D, "v") for i in ids])
-            T = len(k)
+            # the stream's pages are contiguous from token 0 (valid cases
+            # only): decode just those the window reaches
+            ends = tb[ids]["start"] + tb[ids]["length"]
+            T = int(ends[-1])
             r0 = 0 if left_window < 0 else max(0, T - 1 - left_window)
-            k, v = k[r0:], v[r0:]
+            vis = ids[ends > r0]
+            first = int(tb[vis[0]]["start"])
+            k = np.concatenate([decode_rows(case.arena, tb[i], D, "k") for i in vis])[r0 - first:]
+            v = np.concatenate([decode_rows(case.arena, tb[i], D, "v") for i in vis])[r0 - first:]
             for h in range(g * G, (g + 1) * G):
                 s1 = abs(scale) * np.abs(qd[b, h][None, :] * k).sum(axis=1).max()
                 tol[b, h] = 4 * (2 * ((D + 4) * U * s1 + 2.0 ** -21) + (5 * len(k) + 64) * U) * \
