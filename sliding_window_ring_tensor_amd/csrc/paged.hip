@@ -279,13 +279,16 @@ __device__ __forceinline__ void pg_stage4(pg_gchar src, char *dst) {
 // i + o / row bytes; rows past the page's last (lim rows after row i) repeat
 // that row, so every load stays inside the page (scores of such rows are
 // masked). The page's row i is the uniform base; a lane adds a 32-bit offset.
+template <int NMAX>
 __device__ __forceinline__ void pg_stage_rows(const char *page, int32_t i, int32_t lim, int lg_rb,
                                               char *dst, uint32_t lane) {
   const pg_gchar base = pg_gchar(page) + (int64_t(i) << lg_rb);
   if (lg_rb >= 4) {
-    const int n = lg_rb >= 6 ? 1 << (lg_rb - 6) : 1;  // 16 rows in 1 KiB instructions
+    const int n = lg_rb >= 6 ? 1 << (lg_rb - 6) : 1;  // 16 rows in 1 KiB instructions, at most NMAX
     const uint32_t in_row = (1u << lg_rb) - 1;
-    for (int k = 0; k < n; ++k) {  // uniform
+#pragma unroll
+    for (int k = 0; k < NMAX; ++k) {
+      if (k > 0 && k >= n) break;  // uniform
       const uint32_t o = uint32_t(k) * 1024 + lane * 16;
       const uint32_t rr = uint32_t(min(int32_t(o >> lg_rb), lim));
       pg_stage16(base + ((rr << lg_rb) | (o & in_row)), dst + k * 1024);
@@ -460,7 +463,10 @@ __device__ __forceinline__ void pg_tile_values_t(const char *vt, uint32_t j, uin
 template <int D, bool QBF>
 __device__ __forceinline__ f32x4 pg_tile_scores(int kf, const char *kt, uint32_t pk, uint32_t qg,
                                                 const PgQuery<D, QBF> &q, int32_t kz) {
-  switch (kf) {  // uniform in the wave
+  // the usual page formats first, then the rest (uniform in the wave)
+  if (kf == SWRT_XF_INT8) return pg_tile_scores_t<D, SWRT_XF_INT8, QBF>(kt, pk, qg, q, kz);
+  if (kf == SWRT_XF_BF16) return pg_tile_scores_t<D, SWRT_XF_BF16, QBF>(kt, pk, qg, q, kz);
+  switch (kf) {
 #define SWRT_PG_K(F) \
   case F: return pg_tile_scores_t<D, F, QBF>(kt, pk, qg, q, kz);
     SWRT_PG_FORMATS(SWRT_PG_K)
@@ -472,7 +478,10 @@ __device__ __forceinline__ f32x4 pg_tile_scores(int kf, const char *kt, uint32_t
 template <int D>
 __device__ __forceinline__ void pg_tile_values(int vf, const char *vt, uint32_t j, uint32_t qg,
                                                const float (&pw)[4], int32_t vz, f32x4 (&acc)[D / 16]) {
-  switch (vf) {  // uniform in the wave
+  // the usual page formats first, then the rest (uniform in the wave)
+  if (vf == SWRT_XF_INT8) return pg_tile_values_t<D, SWRT_XF_INT8>(vt, j, qg, pw, vz, acc);
+  if (vf == SWRT_XF_BF16) return pg_tile_values_t<D, SWRT_XF_BF16>(vt, j, qg, pw, vz, acc);
+  switch (vf) {
 #define SWRT_PG_V(F) \
   case F: pg_tile_values_t<D, F>(vt, j, qg, pw, vz, acc); break;
     SWRT_PG_FORMATS(SWRT_PG_V)
@@ -618,10 +627,10 @@ __global__ __launch_bounds__(kPgBlock) void paged_attention_kernel(PgAttArgs a) 
         char *dst = stage + buf * (2 * Stage::BYTES);
         const int32_t lim = c.len - 1 - i;
         if (c.kf != SWRT_XF_F32)
-          pg_stage_rows(arena + field64(d.k_offset, l), i, lim,
+          pg_stage_rows<Stage::BYTES / 1024>(arena + field64(d.k_offset, l), i, lim,
                         Stage::LG_D + int((kPgLogBits >> (4 * c.kf)) & 15) - 3, dst, lane);
         if (c.vf != SWRT_XF_F32)
-          pg_stage_rows(arena + field64(d.v_offset, l), i, lim,
+          pg_stage_rows<Stage::BYTES / 1024>(arena + field64(d.v_offset, l), i, lim,
                         Stage::LG_D + int((kPgLogBits >> (4 * c.vf)) & 15) - 3, dst + Stage::BYTES, lane);
       };
       // The group's visible pages in token order: lanes n_in - 1 .. 0. With
