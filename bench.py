@@ -58,8 +58,8 @@ MEASURED_TRAFFIC = {
     ("bf16", "window_in_place", "f3fee1005c69ec6b"): {"read": 195_175_201, "written": 196_001_407},
     ("bf16", "window_attention_mfma", "4dfda33570bfd571"): {"read": 202_168_298,
         "written": 6_291_445},
-    ("bf16+int8", "paged_attention_kernel", "9089da8860c9c532"): {"read": 127_913_915,
-        "written": 6_291_430},
+    ("bf16+int8", "paged_attention_kernel", "9118bc785f03eba3"): {"read": 127_915_060,
+        "written": 6_291_420},
 }
 _CSRC = "sliding_window_ring_tensor_amd/csrc/"
 KERNEL_SOURCES = {
