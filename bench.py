@@ -58,8 +58,8 @@ MEASURED_TRAFFIC = {
     ("bf16", "window_in_place", "f3fee1005c69ec6b"): {"read": 195_175_201, "written": 196_001_407},
     ("bf16", "window_attention_mfma", "4dfda33570bfd571"): {"read": 202_168_298,
         "written": 6_291_445},
-    ("bf16+int8", "paged_attention_kernel", "9118bc785f03eba3"): {"read": 127_915_060,
-        "written": 6_291_420},
+    ("bf16+int8", "paged_attention_kernel", "cbb6e311eba85622"): {"read": 127_915_441,
+        "written": 6_291_437},
 }
 _CSRC = "sliding_window_ring_tensor_amd/csrc/"
 KERNEL_SOURCES = {

@@ -626,12 +626,12 @@ __global__ __launch_bounds__(kPgBlock) void paged_attention_kernel(PgAttArgs a) 
       auto stage_tile = [&](int l, int32_t i, int buf, const PgCur &c) {
         char *dst = stage + buf * (2 * Stage::BYTES);
         const int32_t lim = c.len - 1 - i;
-        if (c.kf != SWRT_XF_F32)
-          pg_stage_rows<Stage::BYTES / 1024>(arena + field64(d.k_offset, l), i, lim,
-                        Stage::LG_D + int((kPgLogBits >> (4 * c.kf)) & 15) - 3, dst, lane);
+        constexpr int NMAX = Stage::BYTES / 1024;
+        const int klg = Stage::LG_D + int((kPgLogBits >> (4 * c.kf)) & 15) - 3;  // log2 row bytes
+        const int vlg = Stage::LG_D + int((kPgLogBits >> (4 * c.vf)) & 15) - 3;
+        if (c.kf != SWRT_XF_F32) pg_stage_rows<NMAX>(arena + field64(d.k_offset, l), i, lim, klg, dst, lane);
         if (c.vf != SWRT_XF_F32)
-          pg_stage_rows<Stage::BYTES / 1024>(arena + field64(d.v_offset, l), i, lim,
-                        Stage::LG_D + int((kPgLogBits >> (4 * c.vf)) & 15) - 3, dst + Stage::BYTES, lane);
+          pg_stage_rows<NMAX>(arena + field64(d.v_offset, l), i, lim, vlg, dst + Stage::BYTES, lane);
       };
       // The group's visible pages in token order: lanes n_in - 1 .. 0. With
       // two buffers the next tile is staged before this one is computed.
