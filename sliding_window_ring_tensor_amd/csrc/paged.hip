@@ -216,6 +216,7 @@ struct PgAttArgs {
   float scale_log2;  // scale * log2(e)
   int64_t left_window;
   int32_t B, Hq, Hkv, items, q_type, out_type;
+  int32_t chunks;  // groups of up to 16 query heads per KV head
 };
 
 // A tile is up to 16 consecutive rows of one page, staged in LDS as they lie
@@ -512,19 +513,24 @@ __global__ __launch_bounds__(kPgBlock) void paged_attention_kernel(PgAttArgs a) 
   const uint32_t item = blockIdx.x * kPgWaves + wave;
   if (item >= uint32_t(a.items)) return;
   char *stage = stage_all[wave][0];
-  const uint32_t g = item % uint32_t(a.Hkv), b = (item / uint32_t(a.Hkv)) % uint32_t(a.B);
-  const uint32_t layer = item / uint32_t(a.Hkv * a.B);
+  // an item is (layer, stream, chunk): the chunk's query heads are
+  // 16 chunk .. 16 chunk + 15 of the group (a group of more than 16 heads is
+  // split over consecutive items, whose waves read the same pages)
+  const uint32_t chunk = item % uint32_t(a.chunks), str = item / uint32_t(a.chunks);
+  const uint32_t g = str % uint32_t(a.Hkv), b = (str / uint32_t(a.Hkv)) % uint32_t(a.B);
+  const uint32_t layer = str / uint32_t(a.Hkv * a.B);
   const PgLayer &P = a.L[layer];
   const char *const arena = P.arena;
   const int G = a.Hq / a.Hkv;
-  const bool head = int(j) < G;
+  const int hs = int(16 * chunk + j);  // this lane's head within the group
+  const bool head = hs < G;
   const int64_t s = int64_t(b) * a.Hkv + g;
 
   // query operand: head slot j's dimensions of lane group qg
   PgQuery<D, QBF> q;
   {
     float qf[KQ];
-    const uint64_t qrow = uint64_t(b) * a.Hq + g * G + (head ? j : 0);
+    const uint64_t qrow = uint64_t(b) * a.Hq + g * G + (head ? hs : 0);
     const int qes = a.q_type == SWRT_XF_F32 ? 4 : 2;
     const char *qp = P.q + qrow * uint64_t(D) * qes;
     pg_load_decode<KQ>(a.q_type, qp, qg * KQ, 0, qf);
@@ -747,7 +753,7 @@ __global__ __launch_bounds__(kPgBlock) void paged_attention_kernel(PgAttArgs a) 
   for (int r = 0; r < 4; ++r)
 #pragma unroll
     for (int t = 0; t < MT; ++t) y[MT * r + t] = acc[t][r] * inv;
-  const uint64_t orow = uint64_t(b) * a.Hq + g * G + j;
+  const uint64_t orow = uint64_t(b) * a.Hq + g * G + hs;
   if (a.out_type == SWRT_XF_F32) {
     u32x4 *dst = reinterpret_cast<u32x4 *>(P.out + (orow * D + 4 * MT * qg) * 4);
 #pragma unroll
@@ -1090,10 +1096,10 @@ extern "C" int swrt_paged_attention(int n_layers, const swrt_paged_layer *layers
   if (!(scale == scale) || scale > 3.4028235e38f || scale < -3.4028235e38f) return SWRT_E_INVALID_ARG;
   if (head_dim != 32 && head_dim != 64 && head_dim != 128 && head_dim != 256)
     return SWRT_E_UNSUPPORTED;
-  if (q_heads / kv_heads > 16) return SWRT_E_UNSUPPORTED;
   if (n_layers == 0 || batch == 0 || q_heads == 0) return SWRT_OK;
   if (!layers || addr_of(d_flags) % 4) return SWRT_E_INVALID_ARG;
-  if (uint64_t(n_layers) * batch * kv_heads >= (uint64_t(1) << 31)) return SWRT_E_UNSUPPORTED;
+  const int chunks = (q_heads / kv_heads + 15) / 16;  // items per stream
+  if (uint64_t(n_layers) * batch * kv_heads * chunks >= (uint64_t(1) << 31)) return SWRT_E_UNSUPPORTED;
   PgAttArgs a;
   const int st = pg_layers(n_layers, layers, a.L, true, int64_t(batch) * kv_heads);
   if (st != SWRT_OK) return st;
@@ -1119,7 +1125,8 @@ extern "C" int swrt_paged_attention(int n_layers, const swrt_paged_layer *layers
   a.B = batch;
   a.Hq = q_heads;
   a.Hkv = kv_heads;
-  a.items = n_layers * batch * kv_heads;
+  a.items = n_layers * batch * kv_heads * chunks;
+  a.chunks = chunks;
   a.q_type = q_type;
   a.out_type = out_type;
   static_assert(sizeof(PgAttArgs) <= 4096, "kernel arguments exceed 4 KiB");

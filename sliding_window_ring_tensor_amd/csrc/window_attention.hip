@@ -39,7 +39,8 @@ struct AttArgs {
   uint32_t *flags;
   float scale_log2;  // scale * log2(e)
   int32_t W, B, Hq, Hkv, C, D, out_type;
-  int32_t items;  // n_layers * B * Hkv
+  int32_t items;   // n_layers * B * Hkv (* chunks for the matrix-core kernel)
+  int32_t chunks;  // matrix-core kernel: groups of up to 16 query heads per KV head
 };
 
 template <int ELEM>
@@ -383,17 +384,23 @@ __global__ __launch_bounds__(kAttBlock) void window_attention_mfma(AttArgs a) {
   const uint32_t j = lane % 16, qg = lane / 16;
   const uint32_t item = blockIdx.x * (kAttWaves / NW) + wave / NW, ws = wave % NW;
   if (item >= uint32_t(a.items)) return;  // NW = 4: the whole workgroup
-  const uint32_t g = item % uint32_t(a.Hkv), b = (item / uint32_t(a.Hkv)) % uint32_t(a.B);
-  const uint32_t layer = item / uint32_t(a.Hkv * a.B);
+  // an item is (layer, b, kv head, chunk): the chunk's query heads are
+  // 16 chunk .. 16 chunk + 15 of the group (a group of more than 16 heads is
+  // split over consecutive items, whose waves read the same K/V rows)
+  const uint32_t chunk = item % uint32_t(a.chunks), win = item / uint32_t(a.chunks);
+  const uint32_t g = win % uint32_t(a.Hkv), b = (win / uint32_t(a.Hkv)) % uint32_t(a.B);
+  const uint32_t layer = win / uint32_t(a.Hkv * a.B);
   const int64_t L = a.L[b];
   if (L < 0 || L > a.C) {  // no partial output for this entry (uniform in the workgroup for NW = 4)
-    if (a.flags && g == 0 && layer == 0 && ws == 0 && lane == 0) atomicOr(a.flags, SWRT_FLAG_BAD_LENGTHS);
+    if (a.flags && g == 0 && chunk == 0 && layer == 0 && ws == 0 && lane == 0)
+      atomicOr(a.flags, SWRT_FLAG_BAD_LENGTHS);
     return;
   }
   // row numbers stay below capacity + 16 < 2^31 (checked on the host)
   const int32_t Li = int32_t(L), r0 = Li > a.W ? Li - a.W : 0, last = Li - 1;
   const int G = a.Hq / a.Hkv;
-  const bool head = int(j) < G;
+  const int hs = int(16 * chunk + j);  // this lane's head within the group
+  const bool head = hs < G;
   const uint64_t kv_off = (uint64_t(b) * a.Hkv + g) * uint64_t(a.C) * row_bytes;
   const char *kb = a.k[layer] + kv_off + 16 * qg;
   const char *vb = a.v[layer] + kv_off + VB * j;
@@ -402,7 +409,7 @@ __global__ __launch_bounds__(kAttBlock) void window_attention_mfma(AttArgs a) {
   // for slots past the group; they read head 0's row to stay in bounds)
   u32x4 qo[KS];
   {
-    const char *qp = a.q[layer] + (uint64_t(b) * a.Hq + g * G + (head ? j : 0)) * row_bytes +
+    const char *qp = a.q[layer] + (uint64_t(b) * a.Hq + g * G + (head ? hs : 0)) * row_bytes +
                      16 * qg;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -602,7 +609,7 @@ __global__ __launch_bounds__(kAttBlock) void window_attention_mfma(AttArgs a) {
   for (int r = 0; r < 4; ++r)
 #pragma unroll
     for (int i = 0; i < MT; ++i) y[MT * r + i] = acc[i][r] * inv;
-  const uint64_t orow = uint64_t(b) * a.Hq + g * G + j;
+  const uint64_t orow = uint64_t(b) * a.Hq + g * G + hs;
   if (a.out_type == SWRT_XF_F32) {
     u32x4 *dst = reinterpret_cast<u32x4 *>(a.out[layer] + (orow * D + 4 * MT * qg) * 4);
 #pragma unroll
@@ -700,7 +707,8 @@ extern "C" int swrt_window_attention(int n_layers, const void *const *q,
   if (!(scale == scale) || scale > 3.4028235e38f || scale < -3.4028235e38f) return SWRT_E_INVALID_ARG;
   if (n_layers == 0 || batch == 0 || q_heads == 0 || head_dim == 0) return SWRT_OK;
   const int G = q_heads / kv_heads;
-  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return SWRT_E_UNSUPPORTED;
+  // the VALU kernel is built for these group sizes; the matrix-core one takes any
+  const bool valu_group = G == 1 || G == 2 || G == 4 || G == 8 || G == 16;
   const int64_t es = elem_type == SWRT_XF_F32 ? 4 : 2, oes = out_type == SWRT_XF_F32 ? 4 : 2;
   const int64_t row = int64_t(head_dim) * es;
   const int64_t lpr = row / 8;
@@ -708,14 +716,15 @@ extern "C" int swrt_window_attention(int n_layers, const void *const *q,
   // 16-bit caches take the matrix-core kernel, 16-byte aligned operands
   // needed; fp32 caches (or 8-byte aligned operands) the VALU one
   bool mfma = elem_type != SWRT_XF_F32;
-  if (!mfma && G * lpr > 256) return SWRT_E_UNSUPPORTED;  // see att_supported
+  if (!mfma && (!valu_group || G * lpr > 256)) return SWRT_E_UNSUPPORTED;  // see att_supported
   if (!q || !k_caches || !v_caches || !out || !cache_total_lens) return SWRT_E_INVALID_ARG;
   int64_t cache_bytes, q_bytes, o_bytes;
   if (!mul_ok(int64_t(batch) * kv_heads * capacity, row, &cache_bytes) ||
       !mul_ok(int64_t(batch) * q_heads, row, &q_bytes) ||
       !mul_ok(int64_t(batch) * q_heads * head_dim, oes, &o_bytes))
     return SWRT_E_UNSUPPORTED;
-  if (uint64_t(n_layers) * batch * kv_heads >= (uint64_t(1) << 31)) return SWRT_E_UNSUPPORTED;
+  const int chunks = (G + 15) / 16;  // the matrix-core kernel's items per window
+  if (uint64_t(n_layers) * batch * kv_heads * chunks >= (uint64_t(1) << 31)) return SWRT_E_UNSUPPORTED;
   Range ranges[4 * kMaxLayers + 2];
   int nr = 0;
   AttArgs a;
@@ -753,15 +762,18 @@ extern "C" int swrt_window_attention(int n_layers, const void *const *q,
   static_assert(sizeof(AttArgs) <= 4096, "kernel arguments exceed 4 KiB");
   const uint32_t grid = uint32_t(n_layers) * uint32_t(batch) * uint32_t(kv_heads);
   a.items = int32_t(grid);
+  a.chunks = 1;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (mfma) {
-    // one wave per (layer, b, kv head) once there are enough of them to fill
-    // the chip, else four waves share each window
-    const int nw = grid >= 2048 ? 1 : kAttWaves;
+    // one wave per (layer, b, kv head, chunk of 16 query heads) once there
+    // are enough of them to fill the chip, else four waves share each
+    a.chunks = chunks;
+    a.items = int32_t(grid * uint32_t(chunks));
+    const int nw = uint32_t(a.items) >= 2048 ? 1 : kAttWaves;
     return elem_type == SWRT_XF_BF16 ? launch_mfma_d<SWRT_XF_BF16>(a, nw, s)
                                      : launch_mfma_d<SWRT_XF_F16>(a, nw, s);
   }
-  if (G * lpr > 256) return SWRT_E_UNSUPPORTED;  // misaligned 16-bit operands
+  if (!valu_group || G * lpr > 256) return SWRT_E_UNSUPPORTED;  // misaligned 16-bit operands
   switch (elem_type) {
     case SWRT_XF_F32: return launch_lpr<SWRT_XF_F32>(a, int(lpr), G, grid, s);
     case SWRT_XF_F16: return launch_lpr<SWRT_XF_F16>(a, int(lpr), G, grid, s);

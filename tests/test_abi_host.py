@@ -344,7 +344,9 @@ def test_window_attention_rejects(L):
     assert att() in launched
     assert att(W=0) == INV and att(Cap=0) == INV and att(Hkv=0) == INV and att(B=-1) == INV
     assert att(Hq=6, Hkv=4) == INV                           # not a multiple
-    assert att(Hq=6, Hkv=2) == UNS                           # group of 3
+    assert att(Hq=6, Hkv=2) in launched                      # group of 3: the matrix-core kernel
+    assert att(Hq=64, Hkv=2) in launched                     # group of 32: two waves per window
+    assert att(Hq=6, Hkv=2, et=1, ot=1) == UNS               # group of 3 on the VALU kernel
     assert att(D=24) == UNS and att(D=40) == UNS             # 48-, 80-byte rows
     assert att(Hq=32, Hkv=2, D=128) in launched              # 16-bit: the matrix-core kernel
     assert att(Hq=32, Hkv=2, D=128, q=A + 8) == UNS          # 8-byte aligned: the VALU kernel,
@@ -375,7 +377,7 @@ def test_paged_rejects(L):
                                       scale, qt, ot, None, None)
     assert att() in launched
     assert att(D=48) == UNS and att(D=512) == UNS           # head_dim
-    assert att(Hq=64, Hkv=2) == UNS                         # a group of 32 heads
+    assert att(Hq=64, Hkv=2) in launched                    # a group of 32: two waves per stream
     assert att(Hq=6, Hkv=4) == INV and att(qt=4) == INV and att(ot=9) == INV
     assert att(scale=float("nan")) == INV and att(n=33) == INV
     assert att(layers=[layer(arena_bytes=4100)]) == INV     # not a multiple of 16

@@ -109,6 +109,9 @@ SHAPES = [  # (dtype, D, Hq, Hkv): every lanes-per-row width and group size
     (torch.float16, 32, 8, 1), (torch.float16, 64, 64, 8), (torch.float16, 128, 8, 4),
     (torch.float16, 256, 32, 2),
     (torch.float32, 16, 4, 2), (torch.float32, 64, 64, 8), (torch.float32, 128, 8, 8),
+    # matrix cores, any group: 7 and 12 heads, and 20 and 32 (two waves per window)
+    (torch.bfloat16, 64, 14, 2), (torch.float16, 32, 24, 2), (torch.bfloat16, 128, 40, 2),
+    (torch.bfloat16, 64, 64, 2),
 ]
 
 
@@ -135,7 +138,8 @@ def test_window_attention_shapes(orc, dtype, D, Hq, Hkv, out_same):
 
 
 @pytest.mark.parametrize("dtype,D,Hq,Hkv", [(torch.bfloat16, 64, 32, 4), (torch.float16, 128, 8, 8),
-                                           (torch.bfloat16, 32, 16, 16)], ids=str)
+                                           (torch.bfloat16, 32, 16, 16), (torch.bfloat16, 64, 96, 4)],
+                         ids=str)
 def test_many_windows_one_wave_each(orc, dtype, D, Hq, Hkv):
     """Enough (layer, b, kv head) windows that each takes one wave (the
     matrix-core kernel's other launch shape), ragged lengths and windows."""

@@ -143,6 +143,8 @@ SHAPES = [  # (q dtype, D, Hq, Hkv)
     (torch.bfloat16, 64, 16, 2), (torch.bfloat16, 32, 8, 8), (torch.bfloat16, 128, 16, 1),
     (torch.bfloat16, 256, 4, 4), (torch.float16, 64, 32, 2), (torch.float32, 64, 8, 4),
     (torch.float32, 32, 3, 1), (torch.bfloat16, 64, 12, 4),
+    # groups of 7, and of 20 and 34 heads (two and three waves per stream)
+    (torch.bfloat16, 64, 14, 2), (torch.bfloat16, 64, 40, 2), (torch.float32, 32, 34, 1),
 ]
 
 
