@@ -56,10 +56,10 @@ MEASURED_TRAFFIC = {
     ("bf16->int8", "decode_step_kernel", "5a17d20369dcd20b"): {"read": 101_380_857,
                                                                "written": 98_911_877},
     ("bf16", "window_in_place", "f3fee1005c69ec6b"): {"read": 195_175_201, "written": 196_001_407},
-    ("bf16", "window_attention_mfma", "4dfda33570bfd571"): {"read": 202_168_298,
-        "written": 6_291_445},
-    ("bf16+int8", "paged_attention_kernel", "cbb6e311eba85622"): {"read": 127_915_441,
-        "written": 6_291_437},
+    ("bf16", "window_attention_mfma", "2db4abc801b9dc84"): {"read": 202_117_911,
+        "written": 6_291_465},
+    ("bf16+int8", "paged_attention_kernel", "e50d54a0dfd14812"): {"read": 127_913_960,
+        "written": 6_291_440},
 }
 _CSRC = "sliding_window_ring_tensor_amd/csrc/"
 KERNEL_SOURCES = {
