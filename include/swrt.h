@@ -487,14 +487,14 @@ int swrt_kv_decode_step_xf(int n_window_layers, void *const *win_k_caches,
  * elem_type         SWRT_XF_F32, _F16 or _BF16; out_type the same set.
  * d_flags           SWRT_FLAG_BAD_LENGTHS when L < 0 or L > capacity: that
  *                   entry's outputs are left as they were.
- * Supported shapes (else SWRT_E_UNSUPPORTED): head_dim * element size in
- * {64, 128, 256, 512} bytes. 16-bit caches with q, k, v and out all 16-byte
- * aligned run on the matrix cores and take any q_heads / kv_heads (a group of
- * more than 16 query heads runs as several waves per window, 16 heads each,
- * which all read the window's rows); fp32 caches, or 16-bit ones with an
- * operand only 8-byte aligned, run on the VALU and need q_heads / kv_heads in
- * {1, 2, 4, 8, 16} and (q_heads / kv_heads) * head_dim * element size <= 2048
- * bytes.
+ * Supported shapes (else SWRT_E_UNSUPPORTED): 16-bit caches with q, k, v and
+ * out all 16-byte aligned run on the matrix cores and take head_dim in
+ * {32, 64, 96, 128, 192, 256} and any q_heads / kv_heads (a group of more
+ * than 16 query heads runs as several waves per window, 16 heads each, which
+ * all read the window's rows); fp32 caches, or 16-bit ones with an operand
+ * only 8-byte aligned, run on the VALU and need head_dim * element size in
+ * {64, 128, 256, 512} bytes, q_heads / kv_heads in {1, 2, 4, 8, 16} and
+ * (q_heads / kv_heads) * head_dim * element size <= 2048 bytes.
  */
 int swrt_window_attention(int n_layers, const void *const *q,
                           const void *const *k_caches, const void *const *v_caches,

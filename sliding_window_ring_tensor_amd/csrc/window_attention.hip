@@ -331,7 +331,18 @@ __device__ __forceinline__ void att_load_words(const char *p, uint32_t (&w)[NB /
     const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
     w[0] = x.x;
     w[1] = x.y;
+  } else if constexpr (NB == 12) {  // head_dim 96: 4-byte aligned chunks
+#pragma unroll
+    for (int i = 0; i < 3; ++i) w[i] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p) + i);
+  } else if constexpr (NB == 24) {  // head_dim 192: 8-byte aligned chunks
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p) + i);
+      w[2 * i] = x.x;
+      w[2 * i + 1] = x.y;
+    }
   } else {
+    static_assert(NB % 16 == 0, "V chunk bytes");
 #pragma unroll
     for (int i = 0; i < NB / 16; ++i) {
       const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p) + i);
@@ -647,7 +658,9 @@ int launch_mfma_d(const AttArgs &a, int nw, hipStream_t s) {
   switch (a.D) {
     case 32: return launch_mfma<ELEM, 32>(a, nw, s);
     case 64: return launch_mfma<ELEM, 64>(a, nw, s);
+    case 96: return launch_mfma<ELEM, 96>(a, nw, s);
     case 128: return launch_mfma<ELEM, 128>(a, nw, s);
+    case 192: return launch_mfma<ELEM, 192>(a, nw, s);
     default: return launch_mfma<ELEM, 256>(a, nw, s);
   }
 }
@@ -712,10 +725,16 @@ extern "C" int swrt_window_attention(int n_layers, const void *const *q,
   const int64_t es = elem_type == SWRT_XF_F32 ? 4 : 2, oes = out_type == SWRT_XF_F32 ? 4 : 2;
   const int64_t row = int64_t(head_dim) * es;
   const int64_t lpr = row / 8;
-  if (row % 8 || (lpr != 8 && lpr != 16 && lpr != 32 && lpr != 64)) return SWRT_E_UNSUPPORTED;
+  // the VALU kernel's rows: 8, 16, 32 or 64 lanes of 8 bytes; the matrix-core
+  // kernel's head dims: multiples of 32 up to 256 that it is built for
+  const bool valu_shape = row % 8 == 0 && (lpr == 8 || lpr == 16 || lpr == 32 || lpr == 64);
+  const bool mfma_shape = elem_type != SWRT_XF_F32 &&
+                          (head_dim == 32 || head_dim == 64 || head_dim == 96 || head_dim == 128 ||
+                           head_dim == 192 || head_dim == 256);
+  if (!valu_shape && !mfma_shape) return SWRT_E_UNSUPPORTED;
   // 16-bit caches take the matrix-core kernel, 16-byte aligned operands
   // needed; fp32 caches (or 8-byte aligned operands) the VALU one
-  bool mfma = elem_type != SWRT_XF_F32;
+  bool mfma = mfma_shape;
   if (!mfma && (!valu_group || G * lpr > 256)) return SWRT_E_UNSUPPORTED;  // see att_supported
   if (!q || !k_caches || !v_caches || !out || !cache_total_lens) return SWRT_E_INVALID_ARG;
   int64_t cache_bytes, q_bytes, o_bytes;
@@ -773,7 +792,7 @@ extern "C" int swrt_window_attention(int n_layers, const void *const *q,
     return elem_type == SWRT_XF_BF16 ? launch_mfma_d<SWRT_XF_BF16>(a, nw, s)
                                      : launch_mfma_d<SWRT_XF_F16>(a, nw, s);
   }
-  if (!valu_group || G * lpr > 256) return SWRT_E_UNSUPPORTED;  // misaligned 16-bit operands
+  if (!valu_shape || !valu_group || G * lpr > 256) return SWRT_E_UNSUPPORTED;  // misaligned 16-bit operands
   switch (elem_type) {
     case SWRT_XF_F32: return launch_lpr<SWRT_XF_F32>(a, int(lpr), G, grid, s);
     case SWRT_XF_F16: return launch_lpr<SWRT_XF_F16>(a, int(lpr), G, grid, s);

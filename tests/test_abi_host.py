@@ -348,6 +348,8 @@ def test_window_attention_rejects(L):
     assert att(Hq=64, Hkv=2) in launched                     # group of 32: two waves per window
     assert att(Hq=6, Hkv=2, et=1, ot=1) == UNS               # group of 3 on the VALU kernel
     assert att(D=24) == UNS and att(D=40) == UNS             # 48-, 80-byte rows
+    assert att(D=96) in launched and att(D=192) in launched  # matrix cores: head_dim 96, 192
+    assert att(D=96, q=A + 8) == UNS                         # the VALU kernel: 192-byte rows
     assert att(Hq=32, Hkv=2, D=128) in launched              # 16-bit: the matrix-core kernel
     assert att(Hq=32, Hkv=2, D=128, q=A + 8) == UNS          # 8-byte aligned: the VALU kernel,
     assert att(Hq=32, Hkv=2, D=64, et=1, ot=1) == UNS        # as for fp32: group 16 x 256 B

@@ -112,6 +112,8 @@ SHAPES = [  # (dtype, D, Hq, Hkv): every lanes-per-row width and group size
     # matrix cores, any group: 7 and 12 heads, and 20 and 32 (two waves per window)
     (torch.bfloat16, 64, 14, 2), (torch.float16, 32, 24, 2), (torch.bfloat16, 128, 40, 2),
     (torch.bfloat16, 64, 64, 2),
+    # matrix cores, head_dim 96 and 192 (12- and 24-byte V chunks per lane)
+    (torch.bfloat16, 96, 16, 2), (torch.float16, 192, 8, 8),
 ]
 
 
@@ -138,7 +140,8 @@ def test_window_attention_shapes(orc, dtype, D, Hq, Hkv, out_same):
 
 
 @pytest.mark.parametrize("dtype,D,Hq,Hkv", [(torch.bfloat16, 64, 32, 4), (torch.float16, 128, 8, 8),
-                                           (torch.bfloat16, 32, 16, 16), (torch.bfloat16, 64, 96, 4)],
+                                           (torch.bfloat16, 32, 16, 16), (torch.bfloat16, 64, 96, 4),
+                                           (torch.bfloat16, 96, 32, 8)],
                          ids=str)
 def test_many_windows_one_wave_each(orc, dtype, D, Hq, Hkv):
     """Enough (layer, b, kv head) windows that each takes one wave (the
