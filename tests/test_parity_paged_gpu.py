@@ -174,6 +174,33 @@ def test_paged_attention_mixed_formats(orc, qdt, D, Hq, Hkv, left_window):
         assert (out[0, :G] == 0).all()  # the empty stream
 
 
+@pytest.mark.parametrize("left_window", [-1, 63, 64, 150])
+@pytest.mark.parametrize("qdt", [torch.bfloat16, torch.float32], ids=str)
+def test_paged_attention_windows_over_many_pages(orc, qdt, left_window):
+    """Windows that reach more than 64 pages (pages of 1 to 3 tokens): the
+    kernel walks a stream's pages 64 at a time from the last one back, so
+    these streams take two to seven groups, with the window's first page at
+    and around a group boundary."""
+    say("paged attention, many pages", qdt, left_window)
+    g = wl.rng(900 + left_window)
+    D, Hq, Hkv, B = 64, 8, 2, 3
+    T = g.integers(100, 400, size=B * Hkv)
+    T[0] = 64  # a window of 64 one-token pages: exactly one group
+    T[1] = 65
+    caps = [1, 1, 2, 3, 1, 2]
+    streams = [wl.page_split(g, int(t), c, sealed=0.2) for t, c in zip(T, caps)]
+    assert max(len(s) for s in streams) > 128
+    case = wl.paged_case(g, D, streams, random_format(g))
+    q = torch.from_numpy(g.uniform(-1, 1, (B, Hq, D)).astype(np.float32)).to(qdt)
+    out, ref, fg, fo, tb = run_attention(orc, case, q, Hkv, left_window, torch.float32)
+    assert fg == fo == 0
+    got = out.detach().cpu().to(torch.float64).numpy()
+    tol = bound(case, tb, q, Hkv, left_window, D ** -0.5, torch.float32, ref)
+    err = np.abs(got - ref)
+    assert (err <= tol).all(), f"max err/tol {np.max(err / tol):.3g}"
+    say("  worst err/tol", round(float(np.max(err / tol)), 4))
+
+
 def test_paged_attention_bad_pages_flag_and_skip(orc):
     g = wl.rng(60)
     D, B, Hq, Hkv = 64, 2, 4, 2
