@@ -161,6 +161,26 @@ def test_many_windows_one_wave_each(orc, dtype, D, Hq, Hkv):
         say("  W", W, "worst err/tol", round(worst, 4))
 
 
+@pytest.mark.parametrize("dtype,D,Hq,Hkv", [(torch.bfloat16, 64, 8, 2), (torch.float16, 128, 32, 2),
+                                           (torch.float32, 64, 4, 1)], ids=str)
+def test_long_windows(orc, dtype, D, Hq, Hkv):
+    """Windows of up to 1000 rows (63 tiles): many blocks per wave, the tiles
+    split over four waves and merged, a window shorter than the cache, a
+    partial last tile."""
+    say("window attention, long windows", dtype, D, Hq, Hkv)
+    g = wl.rng(5000 + D + Hq)
+    B, C = 6, 1000
+    qs, ks, vs = make(g, B, Hq, Hkv, C, D, dtype, n_layers=1, qscale=0.3)
+    L = np.array([0, 1, 999, 1000, 517, 16], np.int32)
+    for W in (1000, 700, 17):
+        outs = swrt.window_attention([t.to(DEV) for t in qs], [t.to(DEV) for t in ks],
+                                     [t.to(DEV) for t in vs], torch.from_numpy(L).to(DEV), W,
+                                     out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        worst = check(orc, qs, ks, vs, L, W, D ** -0.5, outs, torch.float32)
+        say("  W", W, "worst err/tol", round(worst, 4))
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
 def test_eight_byte_aligned_operands(orc, dtype):
     """16-bit operands that are 8- but not 16-byte aligned take the VALU
