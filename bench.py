@@ -283,11 +283,12 @@ def other_workload(args, dev):
             kc, vc, kn, vn, ks, vs = wl.window_payloads(c, device=dev, staging=True)
             sk = torch.from_numpy(c.seqlens_k).to(dev)
             lens = swrt.kv_seq_lengths(sk, S, C)
-            calls.append([swrt.prepare_kv_seq_lengths(sk, S, C, out=lens),
+            calls.append([swrt.prepare_kv_window_stage_step([kc], [vc], [kn], [vn], sk, [ks], [vs],
+                                                            out=lens),
                           swrt.prepare_kv_window_append_layers(
                               [kc], [vc], [kn], [vn], lens.cache_past, lens.evict,
-                              k_stagings=[ks], v_stagings=[vs], phase="all")])
-        desc = c.name + " (lengths, stage, commit: three launches)"
+                              k_stagings=[ks], v_stagings=[vs], phase="commit")])
+        desc = c.name + " (lengths and stage in one launch, then commit: two launches)"
     torch.cuda.synchronize()
 
     def step(i):

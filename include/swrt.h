@@ -22,7 +22,8 @@
  *                          it, for K and V in one launch; in place when S = 1,
  *                          through a C+S staging cache with copy-back when S > 1.
  * plus batched forms of the last two and of TensorScatter (several layers or
- * caches per launch) and swrt_kv_decode_step (all of a decode step at once),
+ * caches per launch), swrt_kv_decode_step (all of a decode step at once) and
+ * swrt_kv_window_stage_step (the lengths and the stage phase at once),
  * and *_xf forms that fuse the row transform of the append into the write:
  * RoPE on K at the absolute position and conversion or affine quantization
  * into the cache's element type (swrt_row_transform below), and
@@ -60,7 +61,7 @@
 extern "C" {
 #endif
 
-#define SWRT_ABI_VERSION 5
+#define SWRT_ABI_VERSION 6
 
 /* synchronous status codes */
 #define SWRT_OK 0
@@ -287,6 +288,56 @@ int swrt_kv_window_append_layers(int n_layers, void *const *k_caches,
                                  int kv_heads, int capacity, int seq_len,
                                  int head_dim, int elem_bits, unsigned phase,
                                  uint32_t *d_flags, void *stream);
+
+/*
+ * swrt_kv_window_stage_step -- the lengths and the STAGE phase of a windowed
+ * step with S >= 2 new rows (pull request "GQA support sliding_window_cache",
+ * section "Design": the lengths of the step and the C+S staging cache) in
+ * one launch. It writes exactly the bytes of
+ *
+ *   swrt_kv_seq_lengths_drift(seqlens_k, batch, seq_len, capacity, window,
+ *                       total_lens, past_lens, cache_past_lens,
+ *                       cache_total_lens, evict_counts)
+ *                       (window == capacity: exactly swrt_kv_seq_lengths)
+ *   swrt_kv_window_append_layers(n_layers, ..., k_stagings, v_stagings,
+ *                       cache_past_lens, evict_counts, batch, kv_heads,
+ *                       capacity, seq_len, head_dim, elem_bits,
+ *                       SWRT_PHASE_STAGE, ...)
+ *
+ * with the stage part deriving each entry's Lp from seqlens_k itself (so the
+ * pair is always one the step accepts: no SWRT_FLAG_BAD_LENGTHS). The step is
+ * finished by swrt_kv_window_append_layers with SWRT_PHASE_COMMIT and the
+ * cache_past_lens and evict_counts written here; attention may read the
+ * staging buffers in between.
+ *
+ * n_layers             0 .. SWRT_MAX_LAYERS (0: the lengths alone); the
+ *                      caches, new rows, strides and staging buffers as for
+ *                      swrt_kv_window_append_layers.
+ * seqlens_k            device int32[batch], required when batch > 0.
+ * capacity, window     C >= 1 and 1 <= W <= C, as for
+ *                      swrt_kv_seq_lengths_drift (W = C: the base layout).
+ * total_lens .. evict_counts
+ *                      device outputs as for swrt_kv_seq_lengths;
+ *                      cache_past_lens and evict_counts are required (the
+ *                      commit reads them), the others may be NULL.
+ * seq_len              S >= 2 (S = 1 has no staging phase: see
+ *                      swrt_kv_decode_step).
+ * d_flags              SWRT_FLAG_BAD_SEQLEN (lengths clamped, step
+ *                      proceeds), as for swrt_kv_seq_lengths.
+ * No written buffer may overlap any other buffer of the call. Limits as for
+ * swrt_kv_window_append.
+ */
+int swrt_kv_window_stage_step(int n_layers, void *const *k_caches,
+                              void *const *v_caches, const void *const *k_news,
+                              const void *const *v_news,
+                              const int64_t *new_strides,
+                              void *const *k_stagings, void *const *v_stagings,
+                              const int32_t *seqlens_k, int capacity, int window,
+                              int64_t *total_lens, int64_t *past_lens,
+                              int32_t *cache_past_lens, int32_t *cache_total_lens,
+                              int32_t *evict_counts, int batch, int kv_heads,
+                              int seq_len, int head_dim, int elem_bits,
+                              uint32_t *d_flags, void *stream);
 
 /*
  * swrt_kv_decode_step -- every KV-cache update of one decode step (S = 1) of a

@@ -53,9 +53,9 @@ import torch
 __all__ = [
     "SwrtError", "PreparedCall", "WindowLengths", "library_path", "lib",
     "tensor_scatter", "tensor_scatter_batched", "kv_seq_lengths", "kv_window_append",
-    "kv_window_append_layers", "kv_decode_step",
+    "kv_window_append_layers", "kv_window_stage_step", "kv_decode_step",
     "prepare_tensor_scatter", "prepare_tensor_scatter_batched", "prepare_kv_seq_lengths",
-    "prepare_kv_window_append_layers", "prepare_kv_decode_step",
+    "prepare_kv_window_append_layers", "prepare_kv_window_stage_step", "prepare_kv_decode_step",
     "Transform", "kv_window_append_xf", "tensor_scatter_xf", "kv_decode_step_xf",
     "prepare_kv_window_append_xf", "prepare_tensor_scatter_xf", "prepare_kv_decode_step_xf",
     "window_attention", "prepare_window_attention",
@@ -78,7 +78,7 @@ MODE_LINEAR, MODE_CIRCULAR = 0, 1
 PHASE_STAGE, PHASE_COMMIT, PHASE_ALL = 1, 2, 3
 MAX_LAYERS = 32
 MAX_BATCHED = 64
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 _PHASES = {"stage": PHASE_STAGE, "commit": PHASE_COMMIT, "all": PHASE_ALL}
 _MODES = {"linear": MODE_LINEAR, "circular": MODE_CIRCULAR}
@@ -175,6 +175,8 @@ def lib() -> ctypes.CDLL:
                                         i32, i32, u32, vp, vp]
     L.swrt_kv_window_append_layers.argtypes = [i32, vpp, vpp, vpp, vpp, vp, vpp, vpp, vp, vp,
                                                i32, i32, i32, i32, i32, i32, u32, vp, vp]
+    L.swrt_kv_window_stage_step.argtypes = [i32, vpp, vpp, vpp, vpp, vp, vpp, vpp, vp, i32, i32,
+                                             vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp]
     L.swrt_kv_decode_step.argtypes = [i32, vpp, vpp, vpp, vpp, vp, vp, i32, i32, vp, vp, vp, vp,
                                       vp, i32, vpp, vpp, vp, i32, i32, i32, i32, i32, vp, vp]
     xfp = ctypes.POINTER(RowTransform)
@@ -194,7 +196,8 @@ def lib() -> ctypes.CDLL:
     L.swrt_paged_append.argtypes = [i32, vp, vpp, vpp, i32, i32, i32, vp, vp]
     for name in ("swrt_tensor_scatter", "swrt_tensor_scatter_batched", "swrt_kv_seq_lengths",
                  "swrt_kv_seq_lengths_drift",
-                 "swrt_kv_window_append", "swrt_kv_window_append_layers", "swrt_kv_decode_step",
+                 "swrt_kv_window_append", "swrt_kv_window_append_layers",
+                 "swrt_kv_window_stage_step", "swrt_kv_decode_step",
                  "swrt_kv_window_append_xf", "swrt_tensor_scatter_xf", "swrt_kv_decode_step_xf",
                  "swrt_window_attention", "swrt_paged_attention", "swrt_paged_quantize",
                  "swrt_paged_append", "swrt_abi_version"):
@@ -356,10 +359,24 @@ def _new_lengths(B: int, dev) -> WindowLengths:
                            (torch.int64, torch.int64, torch.int32, torch.int32, torch.int32)))
 
 
-def _check_seqlens(seqlens_k: torch.Tensor) -> None:
+def _check_seqlens(seqlens_k: torch.Tensor, batch: int | None = None) -> None:
     _contig("seqlens_k", seqlens_k)
     if seqlens_k.dtype != torch.int32 or seqlens_k.dim() != 1:
         raise SwrtError("seqlens_k must be a 1-D int32 tensor")
+    if batch is not None and seqlens_k.shape[0] != batch:
+        raise SwrtError(f"seqlens_k must hold one entry per batch entry ({batch})")
+
+
+def _lengths_out(out: WindowLengths | None, B: int, dev) -> WindowLengths:
+    """The length arrays to write: new ones, or the caller's after a check."""
+    if out is None:
+        return _new_lengths(B, dev)
+    for t, dt in zip(out, (torch.int64, torch.int64, torch.int32, torch.int32, torch.int32)):
+        _contig("lengths", t)
+        if t.dtype != dt or t.shape != (B,):
+            raise SwrtError("out must be WindowLengths of [B] tensors (int64 total and past, "
+                            "int32 cache_past, cache_total and evict)")
+    return out
 
 
 def prepare_kv_seq_lengths(seqlens_k: torch.Tensor, seq_len: int, capacity: int, *,
@@ -368,7 +385,7 @@ def prepare_kv_seq_lengths(seqlens_k: torch.Tensor, seq_len: int, capacity: int,
     dev = _device_of(seqlens_k, flags)
     _check_seqlens(seqlens_k)
     B = seqlens_k.shape[0]
-    out = _new_lengths(B, dev) if out is None else out
+    out = _lengths_out(out, B, dev)
     tail = (_ptr(out.total), _ptr(out.past), _ptr(out.cache_past), _ptr(out.cache_total),
             _ptr(out.evict), _ptr(flags))
     if window is None:
@@ -434,12 +451,7 @@ def prepare_kv_window_append_layers(k_caches, v_caches, k_news, v_news, cache_pa
     kc = k_caches[0]
     everything = [*k_caches, *v_caches, *k_news, *v_news, cache_past_lens, evict_counts, flags]
     if S > 1:
-        if k_stagings is None or v_stagings is None:
-            raise SwrtError("S > 1 needs k_staging and v_staging [B, H, C + S, D]")
-        for t in (*k_stagings, *v_stagings):
-            _contig("staging", t)
-            if t.shape != (B, H, C + S, D) or t.dtype != kc.dtype:
-                raise SwrtError("staging must be [B, H, C + S, D] with the caches' dtype")
+        _check_stagings(k_stagings, v_stagings, B, H, C, S, D, kc.dtype)
         everything += [*k_stagings, *v_stagings]
     else:
         k_stagings = v_stagings = None
@@ -496,6 +508,53 @@ def kv_window_append_layers(k_caches: Sequence[torch.Tensor], v_caches: Sequence
                                     phase=phase, flags=flags)()
 
 
+def _check_stagings(k_stagings, v_stagings, B: int, H: int, C: int, S: int, D: int, dtype):
+    if k_stagings is None or v_stagings is None:
+        raise SwrtError("S > 1 needs k_staging and v_staging [B, H, C + S, D]")
+    for t in (*k_stagings, *v_stagings):
+        _contig("staging", t)
+        if t.shape != (B, H, C + S, D) or t.dtype != dtype:
+            raise SwrtError("staging must be [B, H, C + S, D] with the caches' dtype")
+
+
+def prepare_kv_window_stage_step(k_caches, v_caches, k_news, v_news, seqlens_k, k_stagings,
+                                 v_stagings, *, window: int | None = None,
+                                 out: WindowLengths | None = None,
+                                 flags: torch.Tensor | None = None) -> PreparedCall:
+    """See ``kv_window_stage_step``."""
+    n, B, H, C, D, S, strides = _check_layers(k_caches, v_caches, k_news, v_news)
+    if S < 2:
+        raise SwrtError("a staged step appends S >= 2 rows")
+    _check_seqlens(seqlens_k, B)
+    kc = k_caches[0]
+    _check_stagings(k_stagings, v_stagings, B, H, C, S, D, kc.dtype)
+    if len(k_stagings) != n or len(v_stagings) != n:
+        raise SwrtError("one K and one V staging buffer per layer")
+    dev = _device_of(*k_caches, *v_caches, *k_news, *v_news, seqlens_k, *k_stagings,
+                     *v_stagings, flags)
+    out = _lengths_out(out, B, dev)
+    args = (n, _ptrs(k_caches), _ptrs(v_caches), _ptrs(k_news), _ptrs(v_news), strides,
+            _ptrs(k_stagings), _ptrs(v_stagings), _ptr(seqlens_k), C,
+            C if window is None else window, _ptr(out.total), _ptr(out.past), _ptr(out.cache_past),
+            _ptr(out.cache_total), _ptr(out.evict), B, H, S, D, _bits(kc), _ptr(flags))
+    keep = (*k_caches, *v_caches, *k_news, *v_news, seqlens_k, *k_stagings, *v_stagings, *out,
+            flags)
+    return PreparedCall(lib().swrt_kv_window_stage_step, args, dev, "kv_window_stage_step", keep,
+                        out)
+
+
+def kv_window_stage_step(k_caches, v_caches, k_news, v_news, seqlens_k, k_stagings, v_stagings,
+                         *, window: int | None = None, out: WindowLengths | None = None,
+                         flags: torch.Tensor | None = None) -> WindowLengths:
+    """The lengths of a staged windowed step (S >= 2) and its stage phase for
+    every layer, in one launch. Same bytes as kv_seq_lengths followed by
+    kv_window_append_layers(phase="stage"); finish the step with
+    kv_window_append_layers(phase="commit") on the returned lengths' cache_past
+    and evict. With ``window`` the lengths are the drifting layout's."""
+    return prepare_kv_window_stage_step(k_caches, v_caches, k_news, v_news, seqlens_k, k_stagings,
+                                        v_stagings, window=window, out=out, flags=flags)()
+
+
 # ---------------------------------------------------------------------------
 # whole decode step in one launch
 # ---------------------------------------------------------------------------
@@ -510,7 +569,7 @@ def prepare_kv_decode_step(win_k: Sequence[torch.Tensor], win_v: Sequence[torch.
     n, B, H, C, D, S, strides = _check_layers(win_k, win_v, win_k_new, win_v_new)
     if S != 1:
         raise SwrtError("a decode step appends one row (S = 1)")
-    _check_seqlens(seqlens_k)
+    _check_seqlens(seqlens_k, B)
     nf = len(full_caches)
     if len(full_new) != nf or not 0 <= nf <= MAX_BATCHED:
         raise SwrtError(f"need 0..{MAX_BATCHED} full caches, each with its new rows")
@@ -528,7 +587,7 @@ def prepare_kv_decode_step(win_k: Sequence[torch.Tensor], win_v: Sequence[torch.
             raise SwrtError("write_indices must be int64 [B]")
     dev = _device_of(*win_k, *win_v, *win_k_new, *win_v_new, seqlens_k, *full_caches,
                      *full_new, write_indices, flags)
-    out = _new_lengths(B, dev) if out is None else out
+    out = _lengths_out(out, B, dev)
     args = (n, _ptrs(win_k), _ptrs(win_v), _ptrs(win_k_new), _ptrs(win_v_new), strides,
             _ptr(seqlens_k), C, C if window is None else window, _ptr(out.total), _ptr(out.past),
             _ptr(out.cache_past),
@@ -668,7 +727,7 @@ def prepare_kv_decode_step_xf(win_k, win_v, win_k_new, win_v_new, seqlens_k, ful
                                               new_dtype=win_k_new[0].dtype)
     if S != 1:
         raise SwrtError("a decode step appends one row (S = 1)")
-    _check_seqlens(seqlens_k)
+    _check_seqlens(seqlens_k, B)
     nf = len(full_k)
     if not (len(full_v) == len(full_k_new) == len(full_v_new) == nf) or \
             not 0 <= nf <= MAX_BATCHED // 2:
@@ -690,7 +749,7 @@ def prepare_kv_decode_step_xf(win_k, win_v, win_k_new, win_v_new, seqlens_k, ful
             raise SwrtError("write_indices must be int64 [B]")
     dev = _device_of(*win_k, *win_v, *win_k_new, *win_v_new, seqlens_k, *full_k, *full_v,
                      *full_k_new, *full_v_new, write_indices, flags, *xf.tables())
-    out = _new_lengths(B, dev) if out is None else out
+    out = _lengths_out(out, B, dev)
     args = (n, _ptrs(win_k), _ptrs(win_v), _ptrs(win_k_new), _ptrs(win_v_new), strides,
             _ptr(seqlens_k), C, C if window is None else window, _ptr(out.total), _ptr(out.past),
             _ptr(out.cache_past), _ptr(out.cache_total), _ptr(out.evict), nf,

@@ -7,6 +7,9 @@
 //   window_in_place  S = 1: one workgroup per slice, shift by E then append.
 //   window_stage     S > 1, phase STAGE: 16 KiB tiles of each staging slice.
 //   window_commit    S > 1, phase COMMIT: 16 KiB tiles of each cache slice.
+//   window_stage_lengths
+//                    the lengths of the step and phase STAGE in one launch
+//                    (swrt_kv_window_stage_step).
 // Batch entries whose (Lp, E) pair is not a step that fits (C, S) are flagged
 // and left untouched. The XF instances are the fused append (xf_device.hpp):
 // new rows pass through the row transform at positions past_lens[b] + s, and
@@ -97,6 +100,45 @@ __global__ __launch_bounds__(kWinBlock) void window_commit(WinArgs<NL> a) {
                    tile);
 }
 
+// The lengths of a staged step and its STAGE phase in one grid. The first
+// len_blocks workgroups (one batch entry per thread) write the length arrays
+// with the arithmetic of kv_seq_lengths; every stage workgroup derives its
+// slice's Lp from seqlens_k the same way, so its pair is always one the step
+// accepts. The COMMIT launch that follows reads the written arrays.
+struct StageLengths {
+  const int32_t *seqlens_k;
+  int64_t *total, *past;
+  int32_t *cache_past, *cache_total, *evict;
+  FastDiv gap;  // capacity - window + 1
+  int32_t batch;
+  uint32_t len_blocks, stage_blocks;
+};
+
+template <int VEC, int NL, bool DRIFT>
+__global__ __launch_bounds__(kWinBlock) void window_stage_lengths(WinArgs<NL> a, StageLengths q) {
+  const uint32_t bid = blockIdx.x;
+  if (bid < q.len_blocks) {  // no barrier in this part
+    const int32_t b = int32_t(bid * kWinBlock + threadIdx.x);
+    if (b < q.batch) {
+      const StepLengths r = step_lengths<DRIFT>(q.seqlens_k[b], a.g.S, a.g.C, q.gap);
+      if (r.bad && a.g.flags) atomicOr(a.g.flags, SWRT_FLAG_BAD_SEQLEN);
+      if (q.total) q.total[b] = r.T;
+      if (q.past) q.past[b] = r.P;
+      q.cache_past[b] = int32_t(r.Lp);
+      if (q.cache_total) q.cache_total[b] = int32_t(r.L);
+      q.evict[b] = int32_t(r.E);
+    }
+  }
+  if (bid >= q.stage_blocks) return;  // a grid sized by the length arrays alone
+  const uint32_t slice = bid / a.g.tiles, tile = bid - slice * a.g.tiles;
+  const Slice s = decode_slice(a.g, slice);
+  const StepLengths r = step_lengths<DRIFT>(q.seqlens_k[s.b], a.g.S, a.g.C, q.gap);
+  const uint64_t bh = s.b * a.g.H + s.h;
+  stage_tile<VEC, false>(a.g, a.cache[s.layer][s.t] + bh * uint64_t(a.g.C) * a.g.row_bytes,
+                         a.stage[s.layer][s.t] + bh * uint64_t(a.g.C + a.g.S) * a.g.row_bytes,
+                         a.nw[s.layer][s.t] + s.b * a.g.nb_b + s.h * a.g.nb_h, r.Lp, tile);
+}
+
 template <int VEC, int NL, bool XF>
 int launch(const WindowPlan &p, unsigned phase, hipStream_t stream) {
   WinArgs<NL> a;
@@ -143,6 +185,95 @@ int dispatch(const WindowPlan &p, int vec, unsigned phase, hipStream_t s) {
     case 2: return launch<2, NL, XF>(p, phase, s);
     default: return launch<1, NL, XF>(p, phase, s);
   }
+}
+
+template <int VEC, int NL>
+int launch_stage_lengths(const WindowPlan &p, const StageLengths &q, bool drift, uint32_t grid,
+                         hipStream_t stream) {
+  WinArgs<NL> a;
+  for (int l = 0; l < NL && l < p.n_layers && !p.empty; ++l)
+    for (int t = 0; t < 2; ++t) {
+      a.cache[l][t] = p.cache[l][t];
+      a.nw[l][t] = p.nw[l][t];
+      a.stage[l][t] = p.stage[l][t];
+    }
+  a.g = p.g;
+  a.xf = RowXf{};
+  if (drift)
+    hipLaunchKernelGGL((window_stage_lengths<VEC, NL, true>), dim3(grid), dim3(kWinBlock), 0,
+                       stream, a, q);
+  else
+    hipLaunchKernelGGL((window_stage_lengths<VEC, NL, false>), dim3(grid), dim3(kWinBlock), 0,
+                       stream, a, q);
+  return launch_status();
+}
+
+template <int NL>
+int dispatch_stage_lengths(const WindowPlan &p, const StageLengths &q, int vec, bool drift,
+                           uint32_t grid, hipStream_t s) {
+  switch (vec) {
+    case 16: return launch_stage_lengths<16, NL>(p, q, drift, grid, s);
+    case 8: return launch_stage_lengths<8, NL>(p, q, drift, grid, s);
+    case 4: return launch_stage_lengths<4, NL>(p, q, drift, grid, s);
+    case 2: return launch_stage_lengths<2, NL>(p, q, drift, grid, s);
+    default: return launch_stage_lengths<1, NL>(p, q, drift, grid, s);
+  }
+}
+
+// the lengths (kv_seq_lengths_drift with this window) and phase STAGE of
+// swrt_kv_window_append_layers in one launch
+int stage_step(int n_layers, void *const *k_caches, void *const *v_caches,
+               const void *const *k_news, const void *const *v_news, const int64_t *new_strides,
+               void *const *k_stagings, void *const *v_stagings, const int32_t *seqlens_k,
+               int capacity, int window, int64_t *total_lens, int64_t *past_lens,
+               int32_t *cache_past_lens, int32_t *cache_total_lens, int32_t *evict_counts,
+               int batch, int kv_heads, int seq_len, int head_dim, int elem_bits,
+               uint32_t *d_flags, void *stream) {
+  if (batch < 0 || capacity < 1 || seq_len < 2) return SWRT_E_INVALID_ARG;
+  if (window < 1 || window > capacity) return SWRT_E_INVALID_ARG;
+  WindowPlan p{};
+  Range ranges[6 * kMaxLayers + 8];
+  int nr = 0;
+  int st = plan_window(n_layers, k_caches, v_caches, k_news, v_news, new_strides, k_stagings,
+                       v_stagings, nullptr, nullptr, true, batch, kv_heads, capacity, seq_len,
+                       head_dim, elem_bits, SWRT_PHASE_STAGE, d_flags, nullptr, &p, ranges, &nr);
+  if (st != SWRT_OK) return st;
+  // the commit reads Lp and E: those two arrays are required
+  if (batch > 0 && (!seqlens_k || !cache_past_lens || !evict_counts)) return SWRT_E_INVALID_ARG;
+  if (addr_of(seqlens_k) % 4 || addr_of(total_lens) % 8 || addr_of(past_lens) % 8 ||
+      addr_of(cache_past_lens) % 4 || addr_of(cache_total_lens) % 4 || addr_of(evict_counts) % 4 ||
+      addr_of(d_flags) % 4)
+    return SWRT_E_INVALID_ARG;
+  const uint64_t B = uint64_t(batch);
+  ranges[nr++] = range(seqlens_k, B * 4, false);
+  ranges[nr++] = range(total_lens, B * 8, true);
+  ranges[nr++] = range(past_lens, B * 8, true);
+  ranges[nr++] = range(cache_past_lens, B * 4, true);
+  ranges[nr++] = range(cache_total_lens, B * 4, true);
+  ranges[nr++] = range(evict_counts, B * 4, true);
+  ranges[nr++] = range(d_flags, 4, true);
+  if (written_overlap(ranges, nr)) return SWRT_E_INVALID_ARG;
+  if (batch == 0) return SWRT_OK;
+  const int vec = p.empty ? 16 : word_of(p.align);
+  if (!p.empty && (st = finish_window(&p, vec)) != SWRT_OK) return st;
+  uint64_t tiles = 1, stage_blocks = 0;
+  if (!p.empty) {
+    tiles = (uint64_t(capacity + seq_len) * p.g.row_words + kWinTile - 1) / kWinTile;
+    stage_blocks = uint64_t(p.slices) * tiles;
+  }
+  p.g.tiles = uint32_t(tiles);
+  p.g.C = capacity;
+  p.g.S = seq_len;
+  p.g.flags = d_flags;
+  StageLengths q{seqlens_k, total_lens, past_lens, cache_past_lens, cache_total_lens, evict_counts,
+                 FastDiv(uint32_t(capacity - window + 1)), batch,
+                 uint32_t((B + kWinBlock - 1) / kWinBlock), uint32_t(stage_blocks)};
+  const uint64_t grid = stage_blocks > q.len_blocks ? stage_blocks : q.len_blocks;
+  if (grid >= (uint64_t(1) << 31)) return SWRT_E_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool drift = window < capacity;
+  return n_layers <= 1 ? dispatch_stage_lengths<1>(p, q, vec, drift, uint32_t(grid), s)
+                       : dispatch_stage_lengths<kMaxLayers>(p, q, vec, drift, uint32_t(grid), s);
 }
 
 // xf: the fused append's transform (null: a plain copy), with past_lens
@@ -337,4 +468,20 @@ extern "C" int swrt_kv_window_append_xf(int n_layers, void *const *k_caches,
   return swrt::window_append(n_layers, k_caches, v_caches, k_news, v_news, new_strides, k_stagings,
                              v_stagings, cache_past_lens, evict_counts, batch, kv_heads, capacity,
                              seq_len, head_dim, 8, phase, xf, past_lens, d_flags, stream);
+}
+
+extern "C" int swrt_kv_window_stage_step(int n_layers, void *const *k_caches,
+                                         void *const *v_caches, const void *const *k_news,
+                                         const void *const *v_news, const int64_t *new_strides,
+                                         void *const *k_stagings, void *const *v_stagings,
+                                         const int32_t *seqlens_k, int capacity, int window,
+                                         int64_t *total_lens, int64_t *past_lens,
+                                         int32_t *cache_past_lens, int32_t *cache_total_lens,
+                                         int32_t *evict_counts, int batch, int kv_heads,
+                                         int seq_len, int head_dim, int elem_bits,
+                                         uint32_t *d_flags, void *stream) {
+  return swrt::stage_step(n_layers, k_caches, v_caches, k_news, v_news, new_strides, k_stagings,
+                          v_stagings, seqlens_k, capacity, window, total_lens, past_lens,
+                          cache_past_lens, cache_total_lens, evict_counts, batch, kv_heads,
+                          seq_len, head_dim, elem_bits, d_flags, stream);
 }

@@ -266,6 +266,31 @@ def test_kv_decode_step_rejects(L):
     assert call(nw=0, nf=0) == swrt.OK                         # nothing to do
 
 
+@no_gpu_visible
+def test_kv_window_stage_step_rejects(L):
+    INV = swrt.E_INVALID_ARG
+    V = ctypes.c_void_p
+
+    def call(nl=1, kc=A, ks=C_, sk=D_, C=8, S=3, batch=2, cp=D_ + 0x1000, ev=D_ + 0x2000,
+             W=None, tot=None):
+        arr = lambda *p: (V * len(p))(*p)  # noqa: E731
+        return L.swrt_kv_window_stage_step(nl, arr(kc), arr(A + 0x1000_0000), arr(B_),
+                                           arr(B_ + 0x1000), (I64 * 3)(96, 48, 16), arr(ks),
+                                           arr(C_ + 0x1000_0000), sk, C, C if W is None else W,
+                                           tot, None, cp, None, ev, batch, 2, S, 16, 16, None,
+                                           None)
+    assert call(nl=33) == INV and call(nl=-1) == INV
+    assert call(S=1) == INV                                    # one row has no stage phase
+    assert call(C=0) == INV and call(batch=-1) == INV
+    assert call(sk=0) == INV                                   # seqlens_k required
+    assert call(cp=0) == INV and call(ev=0) == INV             # the commit reads Lp and E
+    assert call(W=0) == INV and call(W=9) == INV               # window outside [1, C]
+    assert call(ks=A + 64) == INV                              # staging inside a cache
+    assert call(cp=D_ + 4) == INV                              # length output inside seqlens_k
+    assert call(tot=D_ + 0x3004) == INV                        # misaligned int64 output
+    assert call(batch=0) == swrt.OK                            # nothing to do
+
+
 def _xf(in_type=1, out_type=4, cos=None, sin=None, max_pos=0, rot=0, scale=(0.5, 0.5), zp=(0, 0)):
     x = swrt.RowTransform()
     x.in_type, x.out_type = in_type, out_type

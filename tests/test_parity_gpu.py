@@ -657,6 +657,125 @@ def test_decode_step_rejects_overlap():
 
 
 # ---------------------------------------------------------------------------
+# the lengths and the stage phase in one launch against the two calls
+# ---------------------------------------------------------------------------
+
+_STAGE_CASES = ["workload4", "layers", "drift", "bad_seqlens", "s_above_c", "odd_rows"]
+
+
+@pytest.mark.parametrize("case", _STAGE_CASES)
+def test_stage_step_equals_lengths_then_stage(orc, case):
+    """kv_window_stage_step + the commit call against kv_seq_lengths + the
+    stage call + the commit call, and both against the oracle."""
+    g = wl.rng(900 + _STAGE_CASES.index(case))
+    B, H, C, S, D, nl, dtype, W = 9, 3, 48, 7, 64, 3, torch.bfloat16, None
+    if case == "workload4":
+        c4, _ = wl.workload4()
+        B, H, C, S, D, nl, dtype = c4.batch, c4.kv_heads, c4.capacity, c4.seq_len, \
+            c4.head_dim, 1, c4.dtype
+        sk = c4.seqlens_k.astype(np.int32)
+    else:
+        if case == "drift":
+            C, W = 48 + 16, 48
+        if case == "s_above_c":
+            C, S = 5, 12
+        if case == "odd_rows":
+            D, dtype = 5, torch.float32  # 20-byte rows: 4-byte words
+        sk = g.integers(S - 1, 3 * C + S, size=B).astype(np.int32)
+        # an empty cache, a cache filled exactly, one eviction (when S <= C)
+        sk[:3] = [S - 1, C + S - 1, max(C, S - 1)]
+        if case == "bad_seqlens":
+            sk[[1, 4]] = [-3, S - 3]
+    say("stage step", case, B, H, C, S, D, nl, dtype, W)
+    mk = lambda shape: wl.host_payload(g, shape, dtype, raw_bits=True)  # noqa: E731
+    host = [[mk(shape) for _ in range(nl)] for shape in
+            ((B, H, C, D), (B, H, C, D), (B, H, S, D), (B, H, S, D), (B, H, C + S, D),
+             (B, H, C + S, D))]
+    results = []
+    for fused in (True, False):
+        kc, vc, kn, vn, ks, vs = [[t.to(DEV) for t in grp] for grp in host]
+        sk_d = torch.from_numpy(sk).to(DEV)
+        flags = flag_word()
+        if fused:
+            lens = swrt.kv_window_stage_step(kc, vc, kn, vn, sk_d, ks, vs, window=W, flags=flags)
+        else:
+            lens = swrt.kv_seq_lengths(sk_d, S, C, window=W, flags=flags)
+            swrt.kv_window_append_layers(kc, vc, kn, vn, lens.cache_past, lens.evict,
+                                         k_stagings=ks, v_stagings=vs, phase="stage", flags=flags)
+        torch.cuda.synchronize()
+        staged = [hb(t) for t in (*ks, *vs)]
+        swrt.kv_window_append_layers(kc, vc, kn, vn, lens.cache_past, lens.evict, k_stagings=ks,
+                                     v_stagings=vs, phase="commit", flags=flags)
+        torch.cuda.synchronize()
+        results.append((staged + [hb(t) for t in (*kc, *vc, *ks, *vs, *lens)], flags.item()))
+    (a, fa), (b2, fb) = results
+    assert fa == fb
+    for x, y in zip(a, b2):
+        np.testing.assert_array_equal(x, y)
+    L = orc.kv_seq_lengths(sk, S, C) if W is None else orc.kv_seq_lengths_drift(sk, S, C, W)
+    want_flags = L.flags
+    bits = torch.empty((), dtype=dtype).element_size() * 8
+    kc, vc, kn, vn, ks, vs = [[hb(t).copy() for t in grp] for grp in host]
+    staged = []
+    for phase in (oracle.PHASE_STAGE, oracle.PHASE_COMMIT):
+        for i in range(nl):
+            want_flags |= orc.kv_window_append_strided(kc[i], vc[i], kn[i], vn[i],
+                                                       (H * S * D, S * D, D), S, L.cache_past,
+                                                       L.evict, ks[i], vs[i], phase, bits,
+                                                       head_dim=D)
+        if phase == oracle.PHASE_STAGE:
+            staged = [t.copy() for t in (*ks, *vs)]
+    assert fa == want_flags
+    want = staged + [*kc, *vc, *ks, *vs]
+    for x, y in zip(a, want):
+        np.testing.assert_array_equal(x, y)
+    for x, y in zip(a[len(want):], (L.total, L.past, L.cache_past, L.cache_total, L.evict)):
+        np.testing.assert_array_equal(x.view(y.dtype), y)  # raw bytes as the oracle's type
+    if case == "bad_seqlens":
+        assert fa & swrt.FLAG_BAD_SEQLEN
+    else:
+        assert fa == 0
+    if case in ("layers", "drift"):  # workload 4's drawn lengths all evict
+        assert (L.evict > 0).any() and (L.evict == 0).any()
+
+
+def test_stage_step_lengths_alone():
+    """No layers: the call writes the length arrays only (through the C-ABI)."""
+    B, S, C = 300, 5, 40
+    sk = torch.from_numpy(wl.rng(931).integers(S - 1, 4 * C, size=B).astype(np.int32)).to(DEV)
+    got = swrt._lengths_out(None, B, DEV)
+    strides = (ctypes.c_int64 * 3)(S * 8, 8, 8)
+    flags = flag_word()
+    st = swrt.lib().swrt_kv_window_stage_step(
+        0, None, None, None, None, strides, None, None, sk.data_ptr(), C, C,
+        *[t.data_ptr() for t in got], B, 2, S, 8, 16, flags.data_ptr(), None)
+    assert st == swrt.OK
+    want = swrt.kv_seq_lengths(sk, S, C)
+    torch.cuda.synchronize()
+    for x, y in zip(got, want):
+        assert torch.equal(x, y)
+    assert flags.item() == 0
+
+
+def test_stage_step_rejects():
+    B, H, C, S, D = 2, 2, 8, 3, 16
+    mk = lambda *shape: torch.zeros(*shape, dtype=torch.bfloat16, device=DEV)  # noqa: E731
+    kc, vc, kn, vn = mk(B, H, C, D), mk(B, H, C, D), mk(B, H, S, D), mk(B, H, S, D)
+    ks, vs = mk(B, H, C + S, D), mk(B, H, C + S, D)
+    sk = torch.zeros(B, dtype=torch.int32, device=DEV)
+    with pytest.raises(swrt.SwrtError):  # one new row: no stage phase
+        swrt.kv_window_stage_step([kc], [vc], [kn[:, :, :1]], [vn[:, :, :1]], sk, [ks], [vs])
+    with pytest.raises(swrt.SwrtError):  # seqlens_k shorter than the batch
+        swrt.kv_window_stage_step([kc], [vc], [kn], [vn], sk[:1], [ks], [vs])
+    with pytest.raises(swrt.SwrtError) as e:  # window above the capacity
+        swrt.kv_window_stage_step([kc], [vc], [kn], [vn], sk, [ks], [vs], window=C + 1)
+    assert e.value.status == swrt.E_INVALID_ARG
+    with pytest.raises(swrt.SwrtError) as e:  # the V staging buffer inside the K cache's
+        swrt.kv_window_stage_step([kc], [vc], [kn], [vn], sk, [ks], [ks])
+    assert e.value.status == swrt.E_INVALID_ARG
+
+
+# ---------------------------------------------------------------------------
 # drifting layout (CPU follow-up of the pull request: Key design decisions)
 # ---------------------------------------------------------------------------
 
