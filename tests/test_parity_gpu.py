@@ -660,7 +660,8 @@ def test_decode_step_rejects_overlap():
 # the lengths and the stage phase in one launch against the two calls
 # ---------------------------------------------------------------------------
 
-_STAGE_CASES = ["workload4", "layers", "drift", "bad_seqlens", "s_above_c", "odd_rows"]
+_STAGE_CASES = ["workload4", "layers", "drift", "bad_seqlens", "s_above_c", "odd_rows",
+                "bsnh_fp8", "max_layers"]
 
 
 @pytest.mark.parametrize("case", _STAGE_CASES)
@@ -669,6 +670,7 @@ def test_stage_step_equals_lengths_then_stage(orc, case):
     stage call + the commit call, and both against the oracle."""
     g = wl.rng(900 + _STAGE_CASES.index(case))
     B, H, C, S, D, nl, dtype, W = 9, 3, 48, 7, 64, 3, torch.bfloat16, None
+    bsnh = case == "bsnh_fp8"  # new rows stored [B, S, H, D], passed as a [B, H, S, D] view
     if case == "workload4":
         c4, _ = wl.workload4()
         B, H, C, S, D, nl, dtype = c4.batch, c4.kv_heads, c4.capacity, c4.seq_len, \
@@ -681,6 +683,10 @@ def test_stage_step_equals_lengths_then_stage(orc, case):
             C, S = 5, 12
         if case == "odd_rows":
             D, dtype = 5, torch.float32  # 20-byte rows: 4-byte words
+        if bsnh:
+            dtype = torch.float8_e4m3fn
+        if case == "max_layers":
+            B, H, C, S, D, nl = 3, 2, 16, 5, 8, swrt.MAX_LAYERS
         sk = g.integers(S - 1, 3 * C + S, size=B).astype(np.int32)
         # an empty cache, a cache filled exactly, one eviction (when S <= C)
         sk[:3] = [S - 1, C + S - 1, max(C, S - 1)]
@@ -688,12 +694,16 @@ def test_stage_step_equals_lengths_then_stage(orc, case):
             sk[[1, 4]] = [-3, S - 3]
     say("stage step", case, B, H, C, S, D, nl, dtype, W)
     mk = lambda shape: wl.host_payload(g, shape, dtype, raw_bits=True)  # noqa: E731
+    new_shape = (B, S, H, D) if bsnh else (B, H, S, D)
     host = [[mk(shape) for _ in range(nl)] for shape in
-            ((B, H, C, D), (B, H, C, D), (B, H, S, D), (B, H, S, D), (B, H, C + S, D),
+            ((B, H, C, D), (B, H, C, D), new_shape, new_shape, (B, H, C + S, D),
              (B, H, C + S, D))]
+    strides = (S * H * D, D, H * D) if bsnh else (H * S * D, S * D, D)
     results = []
     for fused in (True, False):
         kc, vc, kn, vn, ks, vs = [[t.to(DEV) for t in grp] for grp in host]
+        if bsnh:
+            kn, vn = [t.transpose(1, 2) for t in kn], [t.transpose(1, 2) for t in vn]
         sk_d = torch.from_numpy(sk).to(DEV)
         flags = flag_word()
         if fused:
@@ -720,7 +730,7 @@ def test_stage_step_equals_lengths_then_stage(orc, case):
     for phase in (oracle.PHASE_STAGE, oracle.PHASE_COMMIT):
         for i in range(nl):
             want_flags |= orc.kv_window_append_strided(kc[i], vc[i], kn[i], vn[i],
-                                                       (H * S * D, S * D, D), S, L.cache_past,
+                                                       strides, S, L.cache_past,
                                                        L.evict, ks[i], vs[i], phase, bits,
                                                        head_dim=D)
         if phase == oracle.PHASE_STAGE:
@@ -735,7 +745,7 @@ def test_stage_step_equals_lengths_then_stage(orc, case):
         assert fa & swrt.FLAG_BAD_SEQLEN
     else:
         assert fa == 0
-    if case in ("layers", "drift"):  # workload 4's drawn lengths all evict
+    if case in ("layers", "drift", "bsnh_fp8"):  # workload 4's drawn lengths all evict
         assert (L.evict > 0).any() and (L.evict == 0).any()
 
 
