@@ -55,7 +55,7 @@ MEASURED_TRAFFIC = {
                                                          "written": 196_844_560},
     ("bf16->int8", "decode_step_kernel", "5a17d20369dcd20b"): {"read": 101_380_857,
                                                                "written": 98_911_877},
-    ("bf16", "window_in_place", "6454690358c11ed9"): {"read": 195_175_201, "written": 196_001_407},
+    ("bf16", "window_in_place", "6bd7c1b202861988"): {"read": 195_175_201, "written": 196_001_407},
     ("bf16", "window_attention_mfma", "fa5f3e2921ea5ec8"): {"read": 202_127_956,
         "written": 6_291_472},
     ("bf16+int8", "paged_attention_kernel", "e50d54a0dfd14812"): {"read": 127_913_960,

@@ -464,6 +464,30 @@ int swrt_kv_window_append_xf(int n_layers, void *const *k_caches,
                              uint32_t *d_flags, void *stream);
 
 /*
+ * swrt_kv_window_stage_step_xf -- swrt_kv_window_stage_step whose stage
+ * phase is that of swrt_kv_window_append_xf: the new rows pass through *xf
+ * at absolute positions P + s, P derived from seqlens_k like the lengths.
+ * past_lens is then required too (the fused commit,
+ * swrt_kv_window_append_xf with SWRT_PHASE_COMMIT, reads it); an entry whose
+ * positions leave the rotary tables is flagged SWRT_FLAG_ROPE_RANGE and its
+ * staging left untouched, as in the fused stage call. The caches and staging
+ * buffers hold xf->out_type elements; other arguments as for
+ * swrt_kv_window_stage_step and swrt_kv_window_append_xf.
+ */
+int swrt_kv_window_stage_step_xf(int n_layers, void *const *k_caches,
+                                 void *const *v_caches, const void *const *k_news,
+                                 const void *const *v_news,
+                                 const int64_t *new_strides,
+                                 void *const *k_stagings, void *const *v_stagings,
+                                 const int32_t *seqlens_k, int capacity, int window,
+                                 int64_t *total_lens, int64_t *past_lens,
+                                 int32_t *cache_past_lens, int32_t *cache_total_lens,
+                                 int32_t *evict_counts, int batch, int kv_heads,
+                                 int seq_len, int head_dim,
+                                 const swrt_row_transform *xf, uint32_t *d_flags,
+                                 void *stream);
+
+/*
  * swrt_tensor_scatter_xf -- swrt_tensor_scatter_batched with axis = rank - 2
  * (a row is the last dimension, head_dim) whose update rows (in_type) pass
  * through *xf: update row s of batch entry b at absolute position

@@ -58,6 +58,7 @@ __all__ = [
     "prepare_kv_window_append_layers", "prepare_kv_window_stage_step", "prepare_kv_decode_step",
     "Transform", "kv_window_append_xf", "tensor_scatter_xf", "kv_decode_step_xf",
     "prepare_kv_window_append_xf", "prepare_tensor_scatter_xf", "prepare_kv_decode_step_xf",
+    "kv_window_stage_step_xf", "prepare_kv_window_stage_step_xf",
     "window_attention", "prepare_window_attention",
     "PagedCache", "PAGE_DTYPE", "PAGE_FORMATS", "page_table", "paged_attention",
     "prepare_paged_attention", "paged_quantize", "paged_append", "prepare_paged_append",
@@ -182,6 +183,9 @@ def lib() -> ctypes.CDLL:
     xfp = ctypes.POINTER(RowTransform)
     L.swrt_kv_window_append_xf.argtypes = [i32, vpp, vpp, vpp, vpp, vp, vpp, vpp, vp, vp, vp,
                                            i32, i32, i32, i32, i32, u32, xfp, vp, vp]
+    L.swrt_kv_window_stage_step_xf.argtypes = [i32, vpp, vpp, vpp, vpp, vp, vpp, vpp, vp, i32,
+                                                i32, vp, vp, vp, vp, vp, i32, i32, i32, i32, xfp,
+                                                vp, vp]
     L.swrt_tensor_scatter_xf.argtypes = [i32, vpp, vpp, vpp, vp, vp, vp, i32, i64, i32, xfp, vp,
                                          vp]
     L.swrt_kv_decode_step_xf.argtypes = [i32, vpp, vpp, vpp, vpp, vp, vp, i32, i32, vp, vp, vp,
@@ -198,7 +202,8 @@ def lib() -> ctypes.CDLL:
                  "swrt_kv_seq_lengths_drift",
                  "swrt_kv_window_append", "swrt_kv_window_append_layers",
                  "swrt_kv_window_stage_step", "swrt_kv_decode_step",
-                 "swrt_kv_window_append_xf", "swrt_tensor_scatter_xf", "swrt_kv_decode_step_xf",
+                 "swrt_kv_window_append_xf", "swrt_kv_window_stage_step_xf",
+                 "swrt_tensor_scatter_xf", "swrt_kv_decode_step_xf",
                  "swrt_window_attention", "swrt_paged_attention", "swrt_paged_quantize",
                  "swrt_paged_append", "swrt_abi_version"):
         getattr(L, name).restype = ctypes.c_int
@@ -451,7 +456,7 @@ def prepare_kv_window_append_layers(k_caches, v_caches, k_news, v_news, cache_pa
     kc = k_caches[0]
     everything = [*k_caches, *v_caches, *k_news, *v_news, cache_past_lens, evict_counts, flags]
     if S > 1:
-        _check_stagings(k_stagings, v_stagings, B, H, C, S, D, kc.dtype)
+        _check_stagings(k_stagings, v_stagings, n, B, H, C, S, D, kc.dtype)
         everything += [*k_stagings, *v_stagings]
     else:
         k_stagings = v_stagings = None
@@ -508,9 +513,12 @@ def kv_window_append_layers(k_caches: Sequence[torch.Tensor], v_caches: Sequence
                                     phase=phase, flags=flags)()
 
 
-def _check_stagings(k_stagings, v_stagings, B: int, H: int, C: int, S: int, D: int, dtype):
+def _check_stagings(k_stagings, v_stagings, n: int, B: int, H: int, C: int, S: int, D: int,
+                    dtype):
     if k_stagings is None or v_stagings is None:
         raise SwrtError("S > 1 needs k_staging and v_staging [B, H, C + S, D]")
+    if len(k_stagings) != n or len(v_stagings) != n:
+        raise SwrtError("one K and one V staging buffer per layer")
     for t in (*k_stagings, *v_stagings):
         _contig("staging", t)
         if t.shape != (B, H, C + S, D) or t.dtype != dtype:
@@ -527,9 +535,7 @@ def prepare_kv_window_stage_step(k_caches, v_caches, k_news, v_news, seqlens_k, 
         raise SwrtError("a staged step appends S >= 2 rows")
     _check_seqlens(seqlens_k, B)
     kc = k_caches[0]
-    _check_stagings(k_stagings, v_stagings, B, H, C, S, D, kc.dtype)
-    if len(k_stagings) != n or len(v_stagings) != n:
-        raise SwrtError("one K and one V staging buffer per layer")
+    _check_stagings(k_stagings, v_stagings, n, B, H, C, S, D, kc.dtype)
     dev = _device_of(*k_caches, *v_caches, *k_news, *v_news, seqlens_k, *k_stagings,
                      *v_stagings, flags)
     out = _lengths_out(out, B, dev)
@@ -617,15 +623,6 @@ def kv_decode_step(win_k, win_v, win_k_new, win_v_new, seqlens_k, full_caches, f
 # fused appends: RoPE on K at the absolute position + conversion / quantization
 # ---------------------------------------------------------------------------
 
-def _check_staging(k_stagings, v_stagings, B, H, C, S, D, dtype):
-    if k_stagings is None or v_stagings is None:
-        raise SwrtError("S > 1 needs k_staging and v_staging [B, H, C + S, D]")
-    for t in (*k_stagings, *v_stagings):
-        _contig("staging", t)
-        if t.shape != (B, H, C + S, D) or t.dtype != dtype:
-            raise SwrtError("staging must be [B, H, C + S, D] with the caches' dtype")
-
-
 def prepare_kv_window_append_xf(k_caches, v_caches, k_news, v_news, cache_past_lens,
                                 evict_counts, past_lens, xf: Transform, *, k_stagings=None,
                                 v_stagings=None, phase: str = "all",
@@ -638,7 +635,7 @@ def prepare_kv_window_append_xf(k_caches, v_caches, k_news, v_news, cache_past_l
     everything = [*k_caches, *v_caches, *k_news, *v_news, cache_past_lens, evict_counts,
                   past_lens, flags, *xf.tables()]
     if S > 1:
-        _check_staging(k_stagings, v_stagings, B, H, C, S, D, kc.dtype)
+        _check_stagings(k_stagings, v_stagings, n, B, H, C, S, D, kc.dtype)
         everything += [*k_stagings, *v_stagings]
     else:
         k_stagings = v_stagings = None
@@ -669,6 +666,45 @@ def kv_window_append_xf(k_caches, v_caches, k_news, v_news, cache_past_lens, evi
     prepare_kv_window_append_xf(k_caches, v_caches, k_news, v_news, cache_past_lens, evict_counts,
                                 past_lens, xf, k_stagings=k_stagings, v_stagings=v_stagings,
                                 phase=phase, flags=flags)()
+
+
+def prepare_kv_window_stage_step_xf(k_caches, v_caches, k_news, v_news, seqlens_k, k_stagings,
+                                    v_stagings, xf: Transform, *, window: int | None = None,
+                                    out: WindowLengths | None = None,
+                                    flags: torch.Tensor | None = None) -> PreparedCall:
+    """See ``kv_window_stage_step_xf``."""
+    n, B, H, C, D, S, strides = _check_layers(k_caches, v_caches, k_news, v_news,
+                                              new_dtype=k_news[0].dtype)
+    if S < 2:
+        raise SwrtError("a staged step appends S >= 2 rows")
+    _check_seqlens(seqlens_k, B)
+    kc = k_caches[0]
+    x = xf.c(k_news[0].dtype, kc.dtype)
+    _check_stagings(k_stagings, v_stagings, n, B, H, C, S, D, kc.dtype)
+    dev = _device_of(*k_caches, *v_caches, *k_news, *v_news, seqlens_k, *k_stagings,
+                     *v_stagings, flags, *xf.tables())
+    out = _lengths_out(out, B, dev)
+    args = (n, _ptrs(k_caches), _ptrs(v_caches), _ptrs(k_news), _ptrs(v_news), strides,
+            _ptrs(k_stagings), _ptrs(v_stagings), _ptr(seqlens_k), C,
+            C if window is None else window, _ptr(out.total), _ptr(out.past), _ptr(out.cache_past),
+            _ptr(out.cache_total), _ptr(out.evict), B, H, S, D, ctypes.byref(x), _ptr(flags))
+    keep = (*k_caches, *v_caches, *k_news, *v_news, seqlens_k, *k_stagings, *v_stagings, *out,
+            flags, *xf.tables(), x)
+    return PreparedCall(lib().swrt_kv_window_stage_step_xf, args, dev, "kv_window_stage_step_xf",
+                        keep, out)
+
+
+def kv_window_stage_step_xf(k_caches, v_caches, k_news, v_news, seqlens_k, k_stagings,
+                            v_stagings, xf: Transform, *, window: int | None = None,
+                            out: WindowLengths | None = None,
+                            flags: torch.Tensor | None = None) -> WindowLengths:
+    """``kv_window_stage_step`` whose new rows pass through ``xf`` at absolute
+    positions past + s: the lengths and the fused stage phase in one launch.
+    Finish with kv_window_append_xf(phase="commit") on the returned lengths'
+    cache_past, evict and past."""
+    return prepare_kv_window_stage_step_xf(k_caches, v_caches, k_news, v_news, seqlens_k,
+                                           k_stagings, v_stagings, xf, window=window, out=out,
+                                           flags=flags)()
 
 
 def prepare_tensor_scatter_xf(pasts: Sequence[torch.Tensor], updates: Sequence[torch.Tensor],

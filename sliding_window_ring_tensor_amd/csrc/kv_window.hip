@@ -104,7 +104,8 @@ __global__ __launch_bounds__(kWinBlock) void window_commit(WinArgs<NL> a) {
 // len_blocks workgroups (one batch entry per thread) write the length arrays
 // with the arithmetic of kv_seq_lengths; every stage workgroup derives its
 // slice's Lp from seqlens_k the same way, so its pair is always one the step
-// accepts. The COMMIT launch that follows reads the written arrays.
+// accepts. The COMMIT launch that follows reads the written arrays. The XF
+// instances transform the new rows at positions P + s, P derived alike.
 struct StageLengths {
   const int32_t *seqlens_k;
   int64_t *total, *past;
@@ -114,7 +115,7 @@ struct StageLengths {
   uint32_t len_blocks, stage_blocks;
 };
 
-template <int VEC, int NL, bool DRIFT>
+template <int VEC, int NL, bool DRIFT, bool XF>
 __global__ __launch_bounds__(kWinBlock) void window_stage_lengths(WinArgs<NL> a, StageLengths q) {
   const uint32_t bid = blockIdx.x;
   if (bid < q.len_blocks) {  // no barrier in this part
@@ -133,10 +134,14 @@ __global__ __launch_bounds__(kWinBlock) void window_stage_lengths(WinArgs<NL> a,
   const uint32_t slice = bid / a.g.tiles, tile = bid - slice * a.g.tiles;
   const Slice s = decode_slice(a.g, slice);
   const StepLengths r = step_lengths<DRIFT>(q.seqlens_k[s.b], a.g.S, a.g.C, q.gap);
+  if constexpr (XF) {
+    if (!positions_ok(a.g, a.xf, s, tile == 0 && threadIdx.x == 0, r.P)) return;
+  }
   const uint64_t bh = s.b * a.g.H + s.h;
-  stage_tile<VEC, false>(a.g, a.cache[s.layer][s.t] + bh * uint64_t(a.g.C) * a.g.row_bytes,
-                         a.stage[s.layer][s.t] + bh * uint64_t(a.g.C + a.g.S) * a.g.row_bytes,
-                         a.nw[s.layer][s.t] + s.b * a.g.nb_b + s.h * a.g.nb_h, r.Lp, tile);
+  stage_tile<VEC, XF>(a.g, a.cache[s.layer][s.t] + bh * uint64_t(a.g.C) * a.g.row_bytes,
+                      a.stage[s.layer][s.t] + bh * uint64_t(a.g.C + a.g.S) * a.g.row_bytes,
+                      a.nw[s.layer][s.t] + s.b * a.g.nb_b + s.h * a.g.nb_h, r.Lp, tile, &a.xf,
+                      int(s.t), r.P);
 }
 
 template <int VEC, int NL, bool XF>
@@ -187,7 +192,7 @@ int dispatch(const WindowPlan &p, int vec, unsigned phase, hipStream_t s) {
   }
 }
 
-template <int VEC, int NL>
+template <int VEC, int NL, bool XF>
 int launch_stage_lengths(const WindowPlan &p, const StageLengths &q, bool drift, uint32_t grid,
                          hipStream_t stream) {
   WinArgs<NL> a;
@@ -198,48 +203,56 @@ int launch_stage_lengths(const WindowPlan &p, const StageLengths &q, bool drift,
       a.stage[l][t] = p.stage[l][t];
     }
   a.g = p.g;
-  a.xf = RowXf{};
+  a.xf = p.xf;
   if (drift)
-    hipLaunchKernelGGL((window_stage_lengths<VEC, NL, true>), dim3(grid), dim3(kWinBlock), 0,
+    hipLaunchKernelGGL((window_stage_lengths<VEC, NL, true, XF>), dim3(grid), dim3(kWinBlock), 0,
                        stream, a, q);
   else
-    hipLaunchKernelGGL((window_stage_lengths<VEC, NL, false>), dim3(grid), dim3(kWinBlock), 0,
-                       stream, a, q);
+    hipLaunchKernelGGL((window_stage_lengths<VEC, NL, false, XF>), dim3(grid), dim3(kWinBlock),
+                       0, stream, a, q);
   return launch_status();
 }
 
-template <int NL>
+template <int NL, bool XF>
 int dispatch_stage_lengths(const WindowPlan &p, const StageLengths &q, int vec, bool drift,
                            uint32_t grid, hipStream_t s) {
   switch (vec) {
-    case 16: return launch_stage_lengths<16, NL>(p, q, drift, grid, s);
-    case 8: return launch_stage_lengths<8, NL>(p, q, drift, grid, s);
-    case 4: return launch_stage_lengths<4, NL>(p, q, drift, grid, s);
-    case 2: return launch_stage_lengths<2, NL>(p, q, drift, grid, s);
-    default: return launch_stage_lengths<1, NL>(p, q, drift, grid, s);
+    case 16: return launch_stage_lengths<16, NL, XF>(p, q, drift, grid, s);
+    case 8: return launch_stage_lengths<8, NL, XF>(p, q, drift, grid, s);
+    case 4: return launch_stage_lengths<4, NL, XF>(p, q, drift, grid, s);
+    case 2: return launch_stage_lengths<2, NL, XF>(p, q, drift, grid, s);
+    default: return launch_stage_lengths<1, NL, XF>(p, q, drift, grid, s);
   }
 }
 
 // the lengths (kv_seq_lengths_drift with this window) and phase STAGE of
-// swrt_kv_window_append_layers in one launch
+// swrt_kv_window_append_layers (xf: of swrt_kv_window_append_xf) in one launch
 int stage_step(int n_layers, void *const *k_caches, void *const *v_caches,
                const void *const *k_news, const void *const *v_news, const int64_t *new_strides,
                void *const *k_stagings, void *const *v_stagings, const int32_t *seqlens_k,
                int capacity, int window, int64_t *total_lens, int64_t *past_lens,
                int32_t *cache_past_lens, int32_t *cache_total_lens, int32_t *evict_counts,
                int batch, int kv_heads, int seq_len, int head_dim, int elem_bits,
-               uint32_t *d_flags, void *stream) {
+               const swrt_row_transform *xf, uint32_t *d_flags, void *stream) {
   if (batch < 0 || capacity < 1 || seq_len < 2) return SWRT_E_INVALID_ARG;
   if (window < 1 || window > capacity) return SWRT_E_INVALID_ARG;
   WindowPlan p{};
-  Range ranges[6 * kMaxLayers + 8];
+  Range ranges[6 * kMaxLayers + 12];
   int nr = 0;
-  int st = plan_window(n_layers, k_caches, v_caches, k_news, v_news, new_strides, k_stagings,
-                       v_stagings, nullptr, nullptr, true, batch, kv_heads, capacity, seq_len,
-                       head_dim, elem_bits, SWRT_PHASE_STAGE, d_flags, nullptr, &p, ranges, &nr);
+  RowXf x{};
+  int st;
+  if (xf) {
+    if ((st = plan_xf(xf, head_dim, &x, ranges, &nr)) != SWRT_OK) return st;
+    elem_bits = x.out_bytes * 8;
+  }
+  st = plan_window(n_layers, k_caches, v_caches, k_news, v_news, new_strides, k_stagings,
+                   v_stagings, nullptr, nullptr, true, batch, kv_heads, capacity, seq_len,
+                   head_dim, elem_bits, SWRT_PHASE_STAGE, d_flags, xf ? &x : nullptr, &p, ranges,
+                   &nr);
   if (st != SWRT_OK) return st;
-  // the commit reads Lp and E: those two arrays are required
-  if (batch > 0 && (!seqlens_k || !cache_past_lens || !evict_counts)) return SWRT_E_INVALID_ARG;
+  // the commit reads Lp and E (and, fused, P): those arrays are required
+  if (batch > 0 && (!seqlens_k || !cache_past_lens || !evict_counts || (xf && !past_lens)))
+    return SWRT_E_INVALID_ARG;
   if (addr_of(seqlens_k) % 4 || addr_of(total_lens) % 8 || addr_of(past_lens) % 8 ||
       addr_of(cache_past_lens) % 4 || addr_of(cache_total_lens) % 4 || addr_of(evict_counts) % 4 ||
       addr_of(d_flags) % 4)
@@ -272,8 +285,13 @@ int stage_step(int n_layers, void *const *k_caches, void *const *v_caches,
   if (grid >= (uint64_t(1) << 31)) return SWRT_E_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool drift = window < capacity;
-  return n_layers <= 1 ? dispatch_stage_lengths<1>(p, q, vec, drift, uint32_t(grid), s)
-                       : dispatch_stage_lengths<kMaxLayers>(p, q, vec, drift, uint32_t(grid), s);
+  if (xf)
+    return n_layers <= 1 ? dispatch_stage_lengths<1, true>(p, q, vec, drift, uint32_t(grid), s)
+                         : dispatch_stage_lengths<kMaxLayers, true>(p, q, vec, drift,
+                                                                    uint32_t(grid), s);
+  return n_layers <= 1 ? dispatch_stage_lengths<1, false>(p, q, vec, drift, uint32_t(grid), s)
+                       : dispatch_stage_lengths<kMaxLayers, false>(p, q, vec, drift,
+                                                                   uint32_t(grid), s);
 }
 
 // xf: the fused append's transform (null: a plain copy), with past_lens
@@ -483,5 +501,19 @@ extern "C" int swrt_kv_window_stage_step(int n_layers, void *const *k_caches,
   return swrt::stage_step(n_layers, k_caches, v_caches, k_news, v_news, new_strides, k_stagings,
                           v_stagings, seqlens_k, capacity, window, total_lens, past_lens,
                           cache_past_lens, cache_total_lens, evict_counts, batch, kv_heads,
-                          seq_len, head_dim, elem_bits, d_flags, stream);
+                          seq_len, head_dim, elem_bits, nullptr, d_flags, stream);
+}
+
+extern "C" int swrt_kv_window_stage_step_xf(
+    int n_layers, void *const *k_caches, void *const *v_caches, const void *const *k_news,
+    const void *const *v_news, const int64_t *new_strides, void *const *k_stagings,
+    void *const *v_stagings, const int32_t *seqlens_k, int capacity, int window,
+    int64_t *total_lens, int64_t *past_lens, int32_t *cache_past_lens, int32_t *cache_total_lens,
+    int32_t *evict_counts, int batch, int kv_heads, int seq_len, int head_dim,
+    const swrt_row_transform *xf, uint32_t *d_flags, void *stream) {
+  if (!xf) return SWRT_E_INVALID_ARG;
+  return swrt::stage_step(n_layers, k_caches, v_caches, k_news, v_news, new_strides, k_stagings,
+                          v_stagings, seqlens_k, capacity, window, total_lens, past_lens,
+                          cache_past_lens, cache_total_lens, evict_counts, batch, kv_heads,
+                          seq_len, head_dim, 8, xf, d_flags, stream);
 }

@@ -289,6 +289,12 @@ def test_kv_window_stage_step_rejects(L):
     assert call(cp=D_ + 4) == INV                              # length output inside seqlens_k
     assert call(tot=D_ + 0x3004) == INV                        # misaligned int64 output
     assert call(batch=0) == swrt.OK                            # nothing to do
+    arr = lambda *p: (V * len(p))(*p)  # noqa: E731
+    assert L.swrt_kv_window_stage_step_xf(1, arr(A), arr(A + 0x1000_0000), arr(B_),
+                                          arr(B_ + 0x1000), (I64 * 3)(96, 48, 16), arr(C_),
+                                          arr(C_ + 0x1000_0000), D_, 8, 8, None, D_ + 0x3000,
+                                          D_ + 0x1000, None, D_ + 0x2000, 2, 2, 3, 16, None, None,
+                                          None) == INV                 # no transform
 
 
 def _xf(in_type=1, out_type=4, cos=None, sin=None, max_pos=0, rot=0, scale=(0.5, 0.5), zp=(0, 0)):

@@ -146,7 +146,8 @@ def test_scatter_xf_position_range_and_linear_bounds(orc):
 # windowed append with the transform
 # ---------------------------------------------------------------------------
 def _window_case(orc, g, B, H, C, S, D, inp, out, rot_mode, T, n_layers=1, phase_split=False,
-                 strides_bsnh=False, positions=9000):
+                 strides_bsnh=False, positions=9000, stage_step=False):
+    """stage_step: the lengths and the stage phase in one launch, then the commit."""
     xd, xo = make_xf(rot_mode, D, positions, out)
     sk = (np.asarray(T) - 1).astype(np.int32)
     lens = swrt.kv_seq_lengths(torch.from_numpy(sk).to(DEV), S, C)
@@ -167,15 +168,25 @@ def _window_case(orc, g, B, H, C, S, D, inp, out, rot_mode, T, n_layers=1, phase
     flags = flag_word()
     dkn = [view(t.to(DEV)) for t in kb]
     dvn = [view(t.to(DEV)) for t in vb]
-    phases = ("stage", "commit") if (phase_split and S > 1) else ("all",)
-    for ph in phases:
+    phases = ("stage", "commit") if ((phase_split or stage_step) and S > 1) else ("all",)
+    if stage_step:
+        got = swrt.kv_window_stage_step_xf([t.t for t in dk], [t.t for t in dv], dkn, dvn,
+                                           torch.from_numpy(sk).to(DEV), [t.t for t in dks],
+                                           [t.t for t in dvs], xd, flags=flags)
+        lens = got
+        phases_run = ("commit",)
+        for x, y in zip(got, (L.total, L.past, L.cache_past, L.cache_total, L.evict)):
+            np.testing.assert_array_equal(x.cpu().numpy(), y)
+    else:
+        phases_run = phases
+    for ph in phases_run:
         swrt.kv_window_append_xf([t.t for t in dk], [t.t for t in dv], dkn, dvn, lens.cache_past,
                                  lens.evict, lens.past, xd,
                                  k_stagings=None if dks is None else [t.t for t in dks],
                                  v_stagings=None if dvs is None else [t.t for t in dvs],
                                  phase=ph, flags=flags)
     torch.cuda.synchronize()
-    fl = 0
+    fl = L.flags if stage_step else 0  # the lengths' own flag comes from the same launch
     for i in range(n_layers):
         hk, hv = host_np(kc[i]), host_np(vc[i])
         hks, hvs = (host_np(ks[i]), host_np(vs[i])) if S > 1 else (None, None)
@@ -219,6 +230,17 @@ def test_window_xf_staged(orc, out, phase_split):
     f = _window_case(orc, g, 8, 2, 24, 7, 16, torch.bfloat16, out, "half", T, n_layers=2,
                      phase_split=phase_split, strides_bsnh=True)
     assert f == swrt.FLAG_ROPE_RANGE
+
+
+@pytest.mark.parametrize("out", [torch.bfloat16, torch.int8, torch.uint8], ids=str)
+def test_window_xf_stage_step(orc, out):
+    """The lengths and the fused stage phase in one launch, then the fused commit."""
+    say("window xf stage step", out)
+    g = wl.rng(33)
+    T = [3, 10, 40, 41, 2000, 8990, 9003, 60]  # 3: T < S; 9003: P + S past the tables
+    f = _window_case(orc, g, 8, 2, 24, 7, 16, torch.bfloat16, out, "half", T, n_layers=2,
+                     strides_bsnh=True, stage_step=True)
+    assert f == swrt.FLAG_ROPE_RANGE | swrt.FLAG_BAD_SEQLEN
 
 
 @pytest.mark.parametrize("case", ["group2", "group4", "wide_rows", "odd_words"])
