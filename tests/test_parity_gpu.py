@@ -470,6 +470,40 @@ def test_window_replay_histories(orc):
                 replay.check_window(kd.cpu().numpy(), vd.cpu().numpy(), T, C)
 
 
+def test_window_replay_histories_one_launch_forms():
+    """The same tagged histories through the one-launch forms: the lengths with
+    the stage phase (then the commit) for S > 1, the one-launch decode step for
+    S = 1; every state checked against the window invariant itself."""
+    B, H, D = 3, 2, 8
+    for C in (1, 2, 8, 16):
+        for name, sched in replay.schedules(C).items():
+            say("replay one launch", C, name)
+            k, v = replay.fresh_cache(B, H, C, D)
+            kd, vd = torch.from_numpy(k).to(DEV), torch.from_numpy(v).to(DEV)
+            T = np.zeros(B, np.int64)
+            for S in [s for s in sched if s >= 1]:
+                Ta = T + S
+                sk_d = torch.from_numpy((Ta - 1).astype(np.int32)).to(DEV)
+                kn, vn = (torch.from_numpy(x).to(DEV) for x in replay.new_block(B, H, T, S, D))
+                flags = flag_word()
+                if S > 1:
+                    kw, vw = (torch.from_numpy(x).to(DEV) for x in
+                              replay.fresh_cache(B, H, C + S, D, tensors=(2, 3)))
+                    lens = swrt.kv_window_stage_step([kd], [vd], [kn], [vn], sk_d, [kw], [vw],
+                                                     flags=flags)
+                    swrt.kv_window_append_layers([kd], [vd], [kn], [vn], lens.cache_past,
+                                                 lens.evict, k_stagings=[kw], v_stagings=[vw],
+                                                 phase="commit", flags=flags)
+                else:
+                    lens = swrt.kv_decode_step([kd], [vd], [kn], [vn], sk_d, [], [], None,
+                                               flags=flags)
+                T = Ta
+                torch.cuda.synchronize()
+                assert flags.item() == 0
+                assert (lens.cache_total.cpu().numpy() == np.minimum(T, C)).all()
+                replay.check_window(kd.cpu().numpy(), vd.cpu().numpy(), T, C)
+
+
 def test_window_bad_lengths_flag_and_skip(orc):
     B, H, C, D = 4, 2, 8, 16
     g = wl.rng(3)
