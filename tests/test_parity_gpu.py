@@ -552,6 +552,45 @@ def test_window_graph_replays():
         assert torch.equal(hb_t(graphed[1]), hb_t(eager[1])), rep
 
 
+def test_stage_step_graph_replays():
+    """The lengths with the stage phase and the commit captured in a graph (a
+    chunk of S = 6 rows): every replay matches the same calls made eagerly,
+    with eager work and synchronizations between the replays."""
+    g0 = wl.rng(961)
+    B, H, C, S, D = 5, 3, 40, 6, 32
+    sk = torch.from_numpy(g0.integers(S - 1, 3 * C, size=B).astype(np.int32)).to(DEV)
+    mk = lambda *shape: wl.host_payload(g0, shape, torch.bfloat16, True).to(DEV)  # noqa: E731
+    kc, vc, kn, vn = mk(B, H, C, D), mk(B, H, C, D), mk(B, H, S, D), mk(B, H, S, D)
+    ks, vs = mk(B, H, C + S, D), mk(B, H, C + S, D)
+    eager = [t.clone() for t in (kc, vc, ks, vs)]
+    graphed = [t.clone() for t in (kc, vc, ks, vs)]
+    lens_e = swrt.kv_seq_lengths(sk, S, C)
+    lens_g = swrt.WindowLengths(*(torch.zeros_like(t) for t in lens_e))
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            swrt.kv_window_stage_step([graphed[0]], [graphed[1]], [kn], [vn], sk, [graphed[2]],
+                                      [graphed[3]], out=lens_g)
+            swrt.kv_window_append_layers([graphed[0]], [graphed[1]], [kn], [vn],
+                                         lens_g.cache_past, lens_g.evict,
+                                         k_stagings=[graphed[2]], v_stagings=[graphed[3]],
+                                         phase="commit")
+    for rep in range(5):
+        g.replay()
+        swrt.kv_window_stage_step([eager[0]], [eager[1]], [kn], [vn], sk, [eager[2]], [eager[3]],
+                                  out=lens_e)
+        swrt.kv_window_append_layers([eager[0]], [eager[1]], [kn], [vn], lens_e.cache_past,
+                                     lens_e.evict, k_stagings=[eager[2]], v_stagings=[eager[3]],
+                                     phase="commit")
+        torch.cuda.synchronize()
+        for a, b in zip(graphed, eager):
+            assert torch.equal(hb_t(a), hb_t(b)), rep
+        for a, b in zip(lens_g, lens_e):
+            assert torch.equal(a, b), rep
+
+
 def hb_t(t):
     return t.view(torch.uint8)
 
