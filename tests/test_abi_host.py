@@ -115,6 +115,26 @@ def test_binding_refuses_cpu_tensors():
         swrt.tensor_scatter(t, t[:, :1].contiguous(), None, axis=1)
 
 
+def test_binding_checks_batch_and_staging_counts():
+    """Host-side checks of the bindings, before any device work: seqlens_k must
+    hold one entry per batch entry and there is one staging buffer per layer."""
+    B, H, C, S, D = 3, 2, 8, 4, 16
+    z = lambda *shape: torch.zeros(*shape, dtype=torch.bfloat16)  # noqa: E731
+    kc, kn, ks = z(B, H, C, D), z(B, H, S, D), z(B, H, C + S, D)
+    sk = torch.zeros(B, dtype=torch.int32)
+    with pytest.raises(swrt.SwrtError, match="one entry per batch entry"):
+        swrt.prepare_kv_window_stage_step([kc], [kc], [kn], [kn], sk[:2], [ks], [ks])
+    with pytest.raises(swrt.SwrtError, match="one entry per batch entry"):
+        swrt.prepare_kv_decode_step([kc], [kc], [kn[:, :, :1]], [kn[:, :, :1]], sk[:1], [], [],
+                                    None)
+    with pytest.raises(swrt.SwrtError, match="staging buffer per layer"):
+        swrt.prepare_kv_window_stage_step([kc, kc], [kc, kc], [kn, kn], [kn, kn], sk, [ks],
+                                          [ks])
+    with pytest.raises(swrt.SwrtError, match="staging buffer per layer"):
+        swrt.prepare_kv_window_append_layers([kc, kc], [kc, kc], [kn, kn], [kn, kn],
+                                             sk, sk, k_stagings=[ks], v_stagings=[ks])
+
+
 def test_fastdiv_exact(tmp_path):
     exe = str(tmp_path / "fastdiv_check")
     subprocess.run([swrt_build.HIPCC, "-x", "hip", f"--offload-arch={swrt_build.ARCH}", "-O2",

@@ -856,6 +856,10 @@ def test_stage_step_rejects():
     with pytest.raises(swrt.SwrtError) as e:  # the V staging buffer inside the K cache's
         swrt.kv_window_stage_step([kc], [vc], [kn], [vn], sk, [ks], [ks])
     assert e.value.status == swrt.E_INVALID_ARG
+    bad = swrt.WindowLengths(*(torch.zeros(B + 1, dtype=dt, device=DEV) for dt in
+                               (torch.int64, torch.int64, torch.int32, torch.int32, torch.int32)))
+    with pytest.raises(swrt.SwrtError, match="WindowLengths"):  # length arrays of another batch
+        swrt.kv_window_stage_step([kc], [vc], [kn], [vn], sk, [ks], [vs], out=bad)
 
 
 # ---------------------------------------------------------------------------
