@@ -225,6 +225,16 @@ def _ptr(t: torch.Tensor | None):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _flags_ptr(flags: torch.Tensor | None):
+    """The flag word's address: an int32 tensor of at least one element (the
+    library ORs 32-bit flag bits into its first element)."""
+    if flags is None:
+        return None
+    if flags.dtype != torch.int32 or flags.numel() < 1:
+        raise SwrtError("flags must be an int32 tensor with at least one element")
+    return ctypes.c_void_p(flags.data_ptr())
+
+
 def _ptrs(ts: Sequence[torch.Tensor] | None):
     if ts is None:
         return None
@@ -243,6 +253,16 @@ def _device_of(*ts: torch.Tensor | None) -> torch.device:
 
 def _bits(t: torch.Tensor) -> int:
     return t.element_size() * 8
+
+
+def _check_write_indices(write_indices: torch.Tensor | None, batch: int) -> None:
+    """write_indices: None (all zeros) or a dense int64 [batch] tensor."""
+    if write_indices is None:
+        return
+    _contig("write_indices", write_indices)
+    if write_indices.dtype != torch.int64 or tuple(write_indices.shape) != (batch,):
+        raise SwrtError(f"write_indices must be int64 [{batch}] (one index per batch entry), "
+                        f"got {write_indices.dtype} {tuple(write_indices.shape)}")
 
 
 def _contig(name: str, t: torch.Tensor) -> None:
@@ -283,6 +303,17 @@ def prepare_tensor_scatter_batched(pasts: Sequence[torch.Tensor],
         raise SwrtError(f"need 1..{MAX_BATCHED} (past, update) pairs")
     p0, u0 = pasts[0], updates[0]
     presents = [torch.empty_like(p) for p in pasts] if outs is None else list(outs)
+    rank = p0.dim()
+    ax = axis + rank if axis < 0 else axis
+    if not 0 <= ax < rank or u0.dim() != rank:
+        raise SwrtError(f"axis {axis} out of range for rank {rank}")
+    # [TS] Inputs: update is past's shape with the sequence axis replaced by S,
+    # and write_indices holds one index per batch entry
+    if any(u0.shape[d] != p0.shape[d] for d in range(rank) if d != ax):
+        raise SwrtError(f"update {tuple(u0.shape)} must match past {tuple(p0.shape)} "
+                        f"except on axis {axis}")
+    _check_write_indices(write_indices, p0.shape[0])
+    _flags_ptr(flags)
     dev = _device_of(*pasts, *updates, *presents, write_indices, flags)
     for p, u, o in zip(pasts, updates, presents):
         for name, t in (("past", p), ("update", u), ("out", o)):
@@ -291,24 +322,16 @@ def prepare_tensor_scatter_batched(pasts: Sequence[torch.Tensor],
                 len({p.dtype, u.dtype, o.dtype, p0.dtype}) != 1:
             raise SwrtError("every past/out must share one shape, every update another, "
                             "and all one dtype")
-    if write_indices is not None:
-        _contig("write_indices", write_indices)
-        if write_indices.dtype != torch.int64:
-            raise SwrtError("write_indices must be int64")
-    rank = p0.dim()
-    ax = axis + rank if axis < 0 else axis
-    if not 0 <= ax < rank or u0.dim() != rank:
-        raise SwrtError(f"axis {axis} out of range for rank {rank}")
     shape = (ctypes.c_int64 * rank)(*p0.shape)
     L = lib()
     keep = (*pasts, *updates, *presents, write_indices, flags)
     if _single:
         args = (_ptr(presents[0]), _ptr(p0), _ptr(u0), _ptr(write_indices), shape, rank, axis,
-                u0.shape[ax], _MODES[mode], _bits(p0), _ptr(flags))
+                u0.shape[ax], _MODES[mode], _bits(p0), _flags_ptr(flags))
         return PreparedCall(L.swrt_tensor_scatter, args, dev, "tensor_scatter", keep,
                             presents[0])
     args = (n, _ptrs(presents), _ptrs(pasts), _ptrs(updates), _ptr(write_indices), shape, rank,
-            axis, u0.shape[ax], _MODES[mode], _bits(p0), _ptr(flags))
+            axis, u0.shape[ax], _MODES[mode], _bits(p0), _flags_ptr(flags))
     return PreparedCall(L.swrt_tensor_scatter_batched, args, dev, "tensor_scatter_batched", keep,
                         presents)
 
@@ -392,7 +415,7 @@ def prepare_kv_seq_lengths(seqlens_k: torch.Tensor, seq_len: int, capacity: int,
     B = seqlens_k.shape[0]
     out = _lengths_out(out, B, dev)
     tail = (_ptr(out.total), _ptr(out.past), _ptr(out.cache_past), _ptr(out.cache_total),
-            _ptr(out.evict), _ptr(flags))
+            _ptr(out.evict), _flags_ptr(flags))
     if window is None:
         fn, args, what = lib().swrt_kv_seq_lengths, (_ptr(seqlens_k), B, seq_len, capacity,
                                                      *tail), "kv_seq_lengths"
@@ -471,12 +494,12 @@ def prepare_kv_window_append_layers(k_caches, v_caches, k_news, v_news, cache_pa
                 None if k_stagings is None else _ptr(k_stagings[0]),
                 None if v_stagings is None else _ptr(v_stagings[0]),
                 _ptr(cache_past_lens), _ptr(evict_counts), B, H, C, S, D, _bits(kc),
-                _PHASES[phase], _ptr(flags))
+                _PHASES[phase], _flags_ptr(flags))
         return PreparedCall(L.swrt_kv_window_append, args, dev, "kv_window_append",
                             tuple(everything))
     args = (n, _ptrs(k_caches), _ptrs(v_caches), _ptrs(k_news), _ptrs(v_news), strides,
             _ptrs(k_stagings), _ptrs(v_stagings), _ptr(cache_past_lens), _ptr(evict_counts),
-            B, H, C, S, D, _bits(kc), _PHASES[phase], _ptr(flags))
+            B, H, C, S, D, _bits(kc), _PHASES[phase], _flags_ptr(flags))
     return PreparedCall(L.swrt_kv_window_append_layers, args, dev, "kv_window_append_layers",
                         tuple(everything))
 
@@ -542,7 +565,7 @@ def prepare_kv_window_stage_step(k_caches, v_caches, k_news, v_news, seqlens_k, 
     args = (n, _ptrs(k_caches), _ptrs(v_caches), _ptrs(k_news), _ptrs(v_news), strides,
             _ptrs(k_stagings), _ptrs(v_stagings), _ptr(seqlens_k), C,
             C if window is None else window, _ptr(out.total), _ptr(out.past), _ptr(out.cache_past),
-            _ptr(out.cache_total), _ptr(out.evict), B, H, S, D, _bits(kc), _ptr(flags))
+            _ptr(out.cache_total), _ptr(out.evict), B, H, S, D, _bits(kc), _flags_ptr(flags))
     keep = (*k_caches, *v_caches, *k_news, *v_news, seqlens_k, *k_stagings, *v_stagings, *out,
             flags)
     return PreparedCall(lib().swrt_kv_window_stage_step, args, dev, "kv_window_stage_step", keep,
@@ -599,7 +622,7 @@ def prepare_kv_decode_step(win_k: Sequence[torch.Tensor], win_v: Sequence[torch.
             _ptr(out.cache_past),
             _ptr(out.cache_total), _ptr(out.evict), nf, _ptrs(full_caches) if nf else None,
             _ptrs(full_new) if nf else None, _ptr(write_indices) if nf else None, M, B, H, D,
-            _bits(win_k[0]), _ptr(flags))
+            _bits(win_k[0]), _flags_ptr(flags))
     keep = (*win_k, *win_v, *win_k_new, *win_v_new, seqlens_k, *full_caches, *full_new,
             write_indices, *out, flags)
     return PreparedCall(lib().swrt_kv_decode_step, args, dev, "kv_decode_step", keep, out)
@@ -649,7 +672,7 @@ def prepare_kv_window_append_xf(k_caches, v_caches, k_news, v_news, cache_past_l
         raise SwrtError("past_lens must be int64 [B]")
     args = (n, _ptrs(k_caches), _ptrs(v_caches), _ptrs(k_news), _ptrs(v_news), strides,
             _ptrs(k_stagings), _ptrs(v_stagings), _ptr(cache_past_lens), _ptr(evict_counts),
-            _ptr(past_lens), B, H, C, S, D, _PHASES[phase], ctypes.byref(x), _ptr(flags))
+            _ptr(past_lens), B, H, C, S, D, _PHASES[phase], ctypes.byref(x), _flags_ptr(flags))
     return PreparedCall(lib().swrt_kv_window_append_xf, args, dev, "kv_window_append_xf",
                         (*everything, x))
 
@@ -687,7 +710,7 @@ def prepare_kv_window_stage_step_xf(k_caches, v_caches, k_news, v_news, seqlens_
     args = (n, _ptrs(k_caches), _ptrs(v_caches), _ptrs(k_news), _ptrs(v_news), strides,
             _ptrs(k_stagings), _ptrs(v_stagings), _ptr(seqlens_k), C,
             C if window is None else window, _ptr(out.total), _ptr(out.past), _ptr(out.cache_past),
-            _ptr(out.cache_total), _ptr(out.evict), B, H, S, D, ctypes.byref(x), _ptr(flags))
+            _ptr(out.cache_total), _ptr(out.evict), B, H, S, D, ctypes.byref(x), _flags_ptr(flags))
     keep = (*k_caches, *v_caches, *k_news, *v_news, seqlens_k, *k_stagings, *v_stagings, *out,
             flags, *xf.tables(), x)
     return PreparedCall(lib().swrt_kv_window_stage_step_xf, args, dev, "kv_window_stage_step_xf",
@@ -719,26 +742,24 @@ def prepare_tensor_scatter_xf(pasts: Sequence[torch.Tensor], updates: Sequence[t
     p0, u0 = pasts[0], updates[0]
     presents = [torch.empty_like(p) for p in pasts] if outs is None else list(outs)
     x = xf.c(u0.dtype, p0.dtype)
-    dev = _device_of(*pasts, *updates, *presents, write_indices, flags, *xf.tables())
     if p0.dim() < 3:
         raise SwrtError("a fused TensorScatter needs rank >= 3 ([..., M, head_dim])")
+    if u0.dim() != p0.dim() or u0.shape[:-2] != p0.shape[:-2] or u0.shape[-1] != p0.shape[-1]:
+        raise SwrtError("updates must be [..., S, head_dim] with the caches' other dims")
+    _check_write_indices(write_indices, p0.shape[0])
+    _flags_ptr(flags)
+    dev = _device_of(*pasts, *updates, *presents, write_indices, flags, *xf.tables())
     for p, u, o in zip(pasts, updates, presents):
         for name, t in (("past", p), ("update", u), ("out", o)):
             _contig(name, t)
         if p.shape != p0.shape or o.shape != p0.shape or u.shape != u0.shape or \
                 p.dtype != p0.dtype or o.dtype != p0.dtype or u.dtype != u0.dtype:
             raise SwrtError("every past/out must share one shape and dtype, every update too")
-    if u0.dim() != p0.dim() or u0.shape[:-2] != p0.shape[:-2] or u0.shape[-1] != p0.shape[-1]:
-        raise SwrtError("updates must be [..., S, head_dim] with the caches' other dims")
-    if write_indices is not None:
-        _contig("write_indices", write_indices)
-        if write_indices.dtype != torch.int64:
-            raise SwrtError("write_indices must be int64")
     rank = p0.dim()
     shape = (ctypes.c_int64 * rank)(*p0.shape)
     tens = (ctypes.c_int * n)(*[int(t) for t in tensors])
     args = (n, _ptrs(presents), _ptrs(pasts), _ptrs(updates), tens, _ptr(write_indices), shape,
-            rank, u0.shape[-2], _MODES[mode], ctypes.byref(x), _ptr(flags))
+            rank, u0.shape[-2], _MODES[mode], ctypes.byref(x), _flags_ptr(flags))
     keep = (*pasts, *updates, *presents, write_indices, flags, *xf.tables(), x, tens, shape)
     return PreparedCall(lib().swrt_tensor_scatter_xf, args, dev, "tensor_scatter_xf", keep,
                         presents)
@@ -791,7 +812,7 @@ def prepare_kv_decode_step_xf(win_k, win_v, win_k_new, win_v_new, seqlens_k, ful
             _ptr(out.cache_past), _ptr(out.cache_total), _ptr(out.evict), nf,
             _ptrs(full_k) if nf else None, _ptrs(full_v) if nf else None,
             _ptrs(full_k_new) if nf else None, _ptrs(full_v_new) if nf else None,
-            _ptr(write_indices) if nf else None, M, B, H, D, ctypes.byref(x), _ptr(flags))
+            _ptr(write_indices) if nf else None, M, B, H, D, ctypes.byref(x), _flags_ptr(flags))
     keep = (*win_k, *win_v, *win_k_new, *win_v_new, seqlens_k, *full_k, *full_v, *full_k_new,
             *full_v_new, write_indices, *out, flags, *xf.tables(), x)
     return PreparedCall(lib().swrt_kv_decode_step_xf, args, dev, "kv_decode_step_xf", keep, out)
@@ -854,7 +875,7 @@ def prepare_window_attention(qs: Sequence[torch.Tensor], k_caches: Sequence[torc
     dev = _device_of(*qs, *k_caches, *v_caches, *outs, cache_total_lens, flags)
     sc = D ** -0.5 if scale is None else float(scale)
     args = (n, _ptrs(qs), _ptrs(k_caches), _ptrs(v_caches), _ptrs(outs), _ptr(cache_total_lens),
-            window, B, Hq, Hkv, C, D, sc, XF_TYPES[dt], XF_TYPES[odt], _ptr(flags))
+            window, B, Hq, Hkv, C, D, sc, XF_TYPES[dt], XF_TYPES[odt], _flags_ptr(flags))
     keep = (*qs, *k_caches, *v_caches, *outs, cache_total_lens, flags)
     return PreparedCall(lib().swrt_window_attention, args, dev, "window_attention", keep, outs)
 
@@ -978,7 +999,7 @@ def prepare_paged_attention(qs: Sequence[torch.Tensor], caches: Sequence[PagedCa
     layers = (PagedLayer * n)(*[c.layer(q, o) for c, q, o in zip(caches, qs, outs)])
     sc = D ** -0.5 if scale is None else float(scale)
     args = (n, ctypes.cast(layers, ctypes.c_void_p), int(left_window), B, Hq, kv_heads, D, sc,
-            _Q_TYPES[q0.dtype], _Q_TYPES[odt], _ptr(flags))
+            _Q_TYPES[q0.dtype], _Q_TYPES[odt], _flags_ptr(flags))
     keep = (layers, *qs, *outs, *caches, flags)
     return PreparedCall(lib().swrt_paged_attention, args, dev, "paged_attention", keep, outs)
 
@@ -1020,7 +1041,7 @@ def paged_quantize(cache: PagedCache, blocks: torch.Tensor, dst_offsets: torch.T
             _ptr(cache.arena), cache.arena.numel(), _ptr(cache.pages), cache.n_pages,
             _ptr(blocks), blocks.numel(), _ptr(dst_offsets), int(free_begin), int(free_end),
             _ptr(out), int(k_format), float(k_scale), int(k_zero_point), int(v_format),
-            float(v_scale), int(v_zero_point), int(head_dim), _ptr(flags),
+            float(v_scale), int(v_zero_point), int(head_dim), _flags_ptr(flags),
             ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
     _check(st, "paged_quantize")
     return out
@@ -1049,7 +1070,7 @@ def prepare_paged_append(caches: Sequence[PagedCache], k_news: Sequence[torch.Te
                                                                      c.page_ids)), flags)
     layers = (PagedLayer * n)(*[c.layer() for c in caches])
     args = (n, ctypes.cast(layers, ctypes.c_void_p), _ptrs(k_news), _ptrs(v_news),
-            _Q_TYPES[k0.dtype], S, D, _ptr(flags))
+            _Q_TYPES[k0.dtype], S, D, _flags_ptr(flags))
     keep = (layers, *caches, *k_news, *v_news, flags)
     return PreparedCall(lib().swrt_paged_append, args, dev, "paged_append", keep)
 

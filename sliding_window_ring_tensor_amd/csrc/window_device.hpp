@@ -316,11 +316,17 @@ __device__ __forceinline__ void shift_append_group(uint32_t first_slice, uint32_
 
 // Slices per workgroup for an in-place launch: the most (1, 2 or 4) whose
 // subgroup tile still holds a whole shift and whose subgroup covers a row.
-inline int slices_per_group(int64_t capacity, uint32_t row_words) {
+//
+// A fused append spreads the appended row over its subgroup's kWinBlock / spw
+// lanes, at most lane_elems elements per lane: row_elems > 0 also keeps the
+// subgroup wide enough for that row.
+inline int slices_per_group(int64_t capacity, uint32_t row_words, int64_t row_elems = 0,
+                            int lane_elems = 0) {
   int spw = 1;
   while (spw < 4 &&
          uint64_t(capacity - 1) * row_words <= uint64_t(kWinBlock / (2 * spw)) * kGroupUnroll &&
-         row_words <= uint32_t(kWinBlock / (2 * spw)))
+         row_words <= uint32_t(kWinBlock / (2 * spw)) &&
+         (row_elems <= 0 || row_elems <= int64_t(lane_elems) * (kWinBlock / (2 * spw))))
     spw *= 2;
   return spw;
 }

@@ -7,8 +7,9 @@ test_cc_tensorscatter_circular (circular, one batch entry wraps). This script
 parses the printed inputs and outputs out of the page text, so the stored
 values are the page's own, and writes them as JSON next to this file.
 
-Usage: python tests/golden/extract_tensorscatter_examples.py [PAGE_TEXT_FILE]
-(default PAGE_TEXT_FILE: /root/reference/PAPER.md, which holds the page text).
+Usage: python tests/golden/extract_tensorscatter_examples.py PAGE_TEXT_FILE
+where PAGE_TEXT_FILE is a plain-text copy of that page (its Examples section
+must be present).
 """
 from __future__ import annotations
 
@@ -69,7 +70,9 @@ def parse(page_text: str) -> list[dict]:
 
 
 def main() -> None:
-    src = sys.argv[1] if len(sys.argv) > 1 else "/root/reference/PAPER.md"
+    if len(sys.argv) != 2:
+        sys.exit("usage: extract_tensorscatter_examples.py PAGE_TEXT_FILE")
+    src = sys.argv[1]
     with open(src, encoding="utf-8") as f:
         examples = parse(f.read())
     dst = os.path.join(os.path.dirname(os.path.abspath(__file__)), "tensorscatter_examples.json")

@@ -135,6 +135,43 @@ def test_binding_checks_batch_and_staging_counts():
                                              sk, sk, k_stagings=[ks], v_stagings=[ks])
 
 
+def test_binding_checks_tensor_scatter_shapes():
+    """Host-side checks of the TensorScatter bindings ([TS] Inputs): the update
+    matches past on every axis but the sequence axis, write_indices holds one
+    int64 index per batch entry and the flag word is int32. The library only
+    sees past's shape, so a narrower update or a short index vector would
+    otherwise be read past its end on the device."""
+    past = torch.zeros(2, 3, 16, 8, dtype=torch.float32)
+    upd = torch.zeros(2, 3, 4, 8, dtype=torch.float32)
+    wi = torch.zeros(2, dtype=torch.int64)
+    fl = torch.zeros(1, dtype=torch.int32)
+    for bad in (torch.zeros(2, 3, 4, 4), torch.zeros(2, 2, 4, 8), torch.zeros(1, 3, 4, 8)):
+        with pytest.raises(swrt.SwrtError, match="must match past"):
+            swrt.prepare_tensor_scatter(past, bad, wi, axis=2)
+        with pytest.raises(swrt.SwrtError, match="must match past"):
+            swrt.prepare_tensor_scatter_batched([past], [bad], wi, axis=-2)
+    for bad in (wi[:1], torch.zeros(3, dtype=torch.int64), torch.zeros(2, dtype=torch.int32),
+                torch.zeros(2, 1, dtype=torch.int64)):
+        with pytest.raises(swrt.SwrtError, match="one index per batch entry"):
+            swrt.prepare_tensor_scatter(past, upd, bad, axis=2)
+    for bad in (torch.zeros(1, dtype=torch.int64), torch.zeros(0, dtype=torch.int32)):
+        with pytest.raises(swrt.SwrtError, match="int32 tensor with at least one element"):
+            swrt.prepare_tensor_scatter(past, upd, wi, axis=2, flags=bad)
+    # the fused form: [..., S, head_dim] updates, the same index and flag checks
+    xf = swrt.Transform()
+    kc = torch.zeros(2, 3, 16, 8, dtype=torch.bfloat16)
+    ku = torch.zeros(2, 3, 4, 8, dtype=torch.bfloat16)
+    with pytest.raises(swrt.SwrtError, match="other dims"):
+        swrt.prepare_tensor_scatter_xf([kc], [ku[:, :2]], [0], wi, xf)
+    with pytest.raises(swrt.SwrtError, match="one index per batch entry"):
+        swrt.prepare_tensor_scatter_xf([kc], [ku], [0], wi[:1], xf)
+    with pytest.raises(swrt.SwrtError, match="int32 tensor with at least one element"):
+        swrt.prepare_tensor_scatter_xf([kc], [ku], [0], wi, xf, flags=fl.to(torch.int64))
+    # a well-formed call gets as far as the device check (CPU tensors here)
+    with pytest.raises(swrt.SwrtError, match="GPU only"):
+        swrt.prepare_tensor_scatter(past, upd, wi, axis=2, flags=fl)
+
+
 def test_fastdiv_exact(tmp_path):
     exe = str(tmp_path / "fastdiv_check")
     subprocess.run([swrt_build.HIPCC, "-x", "hip", f"--offload-arch={swrt_build.ARCH}", "-O2",

@@ -74,19 +74,28 @@ def test_tensorscatter_page_examples(orc, ex, in_place):
 # --------------------------------------------------------------------------
 
 def _pseudocode(past, update, write_indices, axis, mode):
-    """The page's pseudocode, statement by statement (whole-tuple np.mod)."""
-    present = past.copy()
-    max_sequence_length = past.shape[axis]
-    sequence_length = update.shape[axis]
-    for prefix_idx in np.ndindex(past.shape[:axis]):
-        batch_idx = prefix_idx[0]
-        for sequence_idx in range(sequence_length):
-            cache_idx = (*prefix_idx, write_indices[batch_idx] + sequence_idx)
+    """Brute force of the ONNX operator page "TensorScatter" (description and
+    pseudocode sections), in the opposite direction to the page's listing: for
+    every element of the result, search the update block for the element that
+    lands on it. Update row s of batch entry b lands on sequence row w_b + s of
+    the same prefix (circular mode: that row modulo M; the page reduces the
+    whole index tuple, which is the same thing here because every prefix index
+    of these shapes is below M). An element no update row lands on keeps
+    past's value."""
+    M, S = past.shape[axis], update.shape[axis]
+    result = np.empty_like(past)
+    for where in itertools.product(*(range(n) for n in past.shape)):
+        lead, row, tail = where[:axis], where[axis], where[axis + 1:]
+        sources = []
+        for s in range(S):
+            target = int(write_indices[lead[0]]) + s
             if mode == "circular":
-                cache_idx = tuple(np.mod(np.asarray(cache_idx), max_sequence_length))
-            update_idx = (*prefix_idx, sequence_idx)
-            present[cache_idx] = update[update_idx]
-    return present
+                target %= M  # Python's % is a floor modulo, like np.mod
+            if target == row:
+                sources.append(lead + (s,) + tail)
+        assert len(sources) <= 1  # S <= M: no two update rows share a target
+        result[where] = update[sources[0]] if sources else past[where]
+    return result
 
 
 _TINY_SHAPES = [  # prefix dims stay below M, where the whole-tuple modulo is the

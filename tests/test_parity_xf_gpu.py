@@ -282,6 +282,42 @@ def test_window_xf_bad_lengths_before_positions(orc):
     np.testing.assert_array_equal(hb(dv), hv.view(np.uint8))
 
 
+def test_xf_wide_rows_in_shared_workgroups(orc):
+    """A slice small enough to share a workgroup (C = 4) with an appended row
+    wider than a quarter workgroup can spread at eight elements per lane (int8,
+    D = 1040): the launch keeps enough lanes per slice for the whole row, in the
+    windowed append and in the one-launch step."""
+    B, H, C, D = 3, 2, 4, 1040
+    # host arithmetic: 16-byte words per row, and the subgroup split that the
+    # plain copy alone would choose (four slices of 128 lanes: 1040 > 8 * 128)
+    row_words = D // 16
+    spw = 1
+    while spw < 4 and (C - 1) * row_words <= (512 // (2 * spw)) * 2 and \
+            row_words <= 512 // (2 * spw):
+        spw *= 2
+    assert spw == 4 and D > 8 * (512 // spw)
+    g = wl.rng(45)
+    T = np.array([1, 4, 5, 9, 2, 3])[:B]
+    say("window xf wide rows in shared workgroups")
+    _window_case(orc, g, B, H, C, 1, D, torch.bfloat16, torch.int8, "half", T, positions=64)
+    xd, xo = make_xf("half", D, 64, torch.int8)
+    sk = (T - 1).astype(np.int32)
+    wc = [wl.host_payload(g, (B, H, C, D), torch.int8, raw_bits=True) for _ in range(2)]
+    wn = [new_rows(g, (B, H, 1, D), torch.bfloat16) for _ in range(2)]
+    dc, dn = [t.to(DEV) for t in wc], [t.to(DEV) for t in wn]
+    flags = flag_word()
+    swrt.kv_decode_step_xf([dc[0]], [dc[1]], [dn[0]], [dn[1]], torch.from_numpy(sk).to(DEV), [],
+                           [], [], [], None, xd, flags=flags)
+    L = orc.kv_seq_lengths(sk, 1, C)
+    hc = [host_np(t) for t in wc]
+    f = orc.kv_window_append_xf(xo(torch.bfloat16, torch.int8), hc[0], hc[1], host_np(wn[0]),
+                                host_np(wn[1]), (H * D, D, D), 1, L.cache_past, L.evict, L.past)
+    torch.cuda.synchronize()
+    assert f == flags.item() == 0
+    for x, y in zip(dc, hc):
+        np.testing.assert_array_equal(hb(x), y.view(np.uint8))
+
+
 # ---------------------------------------------------------------------------
 # the one-launch decode step with the transform
 # ---------------------------------------------------------------------------
