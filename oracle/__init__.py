@@ -148,14 +148,20 @@ class Oracle:
                                              ctypes.c_double, i32, u32p]
         lib.orc_window_attention.restype = ctypes.c_int
         f32 = ctypes.c_float
-        lib.orc_paged_attention.argtypes = [vp, i32, vp, i64, vp, i64, vp, vp, i64, vp, i64, i64,
-                                            i64, i64, i64, ctypes.c_double, u32p]
+        lib.orc_paged_attention.argtypes = [vp, i32, vp, i64, vp, i64, vp, vp, i64, vp, i64, vp,
+                                            i64, i64, i64, i64, i64, ctypes.c_double, u32p]
         lib.orc_paged_attention.restype = ctypes.c_int
         lib.orc_paged_quantize.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, i64, vp, i32, f32,
                                            ctypes.c_int32, i32, f32, ctypes.c_int32, i64]
         lib.orc_paged_quantize.restype = ctypes.c_int
-        lib.orc_paged_append.argtypes = [vp, i64, vp, i64, vp, vp, i64, vp, vp, i32, i64, i64, u32p]
+        i32v = ctypes.c_int32
+        lib.orc_paged_append.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, vp, vp, i32, i64, i64,
+                                         i64, i64, i64, i64, i64, i32, f32, i32v, i32, f32, i32v,
+                                         u32p, ctypes.POINTER(ctypes.c_int64)]
         lib.orc_paged_append.restype = ctypes.c_int
+        lib.orc_paged_append_open.argtypes = [vp, i64, vp, i64, vp, vp, i64, vp, i64, vp, vp, i32,
+                                              i64, i64, u32p]
+        lib.orc_paged_append_open.restype = ctypes.c_int
         self.lib = lib
 
     # -- TensorScatter ----------------------------------------------------
@@ -339,9 +345,12 @@ class Oracle:
 
     # -- paged caches -----------------------------------------------------------
     def paged_attention(self, q, q_type: int, arena, pages, page_ptr, page_ids, left_window: int,
-                        kv_heads: int, scale: float, out: np.ndarray | None = None):
+                        kv_heads: int, scale: float, out: np.ndarray | None = None,
+                        page_count=None, page_stride: int = 0):
         """float64 attention of q [B, Hq, D] (q_type elements) over the paged
-        caches; returns (out [B, Hq, D] float64, flags)."""
+        caches; returns (out [B, Hq, D] float64, flags). The block table is
+        compressed rows (page_ptr) or, with page_count, slotted rows of
+        page_stride slots per stream."""
         B, Hq = q.shape[:2]
         D = q.shape[2] * q.itemsize // XF_BYTES[q_type]
         if out is None:
@@ -349,12 +358,14 @@ class Oracle:
         qc = np.ascontiguousarray(q)
         ar = np.ascontiguousarray(arena, dtype=np.uint8)
         pg = np.ascontiguousarray(pages, dtype=PAGE_DTYPE)
-        ptr = np.ascontiguousarray(page_ptr, dtype=np.int32)
+        ptr = None if page_ptr is None else np.ascontiguousarray(page_ptr, dtype=np.int32)
+        cnt = None if page_count is None else np.ascontiguousarray(page_count, dtype=np.int32)
         ids = np.ascontiguousarray(page_ids, dtype=np.int32)
         flags = ctypes.c_uint32(0)
         st = self.lib.orc_paged_attention(_ptr(qc), q_type, _ptr(ar), ar.nbytes, _ptr(pg), len(pg),
-                                          _ptr(ptr), _ptr(ids), len(ids), _ptr(out), left_window,
-                                          B, Hq, kv_heads, D, scale, ctypes.byref(flags))
+                                          _ptr(ptr), _ptr(cnt), page_stride, _ptr(ids), len(ids),
+                                          _ptr(out), left_window, B, Hq, kv_heads, D, scale,
+                                          ctypes.byref(flags))
         if st != OK:
             raise OracleError(f"orc_paged_attention status {st}")
         return out, flags.value
@@ -374,20 +385,46 @@ class Oracle:
                                          head_dim)
         return st, ar, pout
 
-    def paged_append(self, arena, pages, page_ptr, page_ids, k_new, v_new, new_type: int,
-                     head_dim: int):
-        """Decode append on copies: returns (arena, pages, flags)."""
+    def paged_append(self, arena, pages, page_count, page_stride: int, page_ids, k_new, v_new,
+                     new_type: int, seq_len: int, k_head_dim: int, v_head_dim: int, first_id: int,
+                     free_begin: int, free_end: int, k_format: int, k_scale: float,
+                     k_zero_point: int, v_format: int, v_scale: float, v_zero_point: int):
+        """Sealed-block append on copies (one new block of seq_len tokens per
+        stream): returns (status, arena, pages, page_count, page_ids, flags,
+        payload bytes written)."""
         ar = np.array(arena, dtype=np.uint8, copy=True)
         pg = np.array(pages, dtype=PAGE_DTYPE, copy=True)
-        ptr = np.ascontiguousarray(page_ptr, dtype=np.int32)
-        ids = np.ascontiguousarray(page_ids, dtype=np.int32)
+        cnt = np.array(page_count, dtype=np.int32, copy=True)
+        ids = np.array(page_ids, dtype=np.int32, copy=True)
         kn, vn = np.ascontiguousarray(k_new), np.ascontiguousarray(v_new)
         flags = ctypes.c_uint32(0)
-        st = self.lib.orc_paged_append(_ptr(ar), ar.nbytes, _ptr(pg), len(pg), _ptr(ptr), _ptr(ids),
-                                       len(ids), _ptr(kn), _ptr(vn), new_type, len(ptr) - 1,
-                                       head_dim, ctypes.byref(flags))
+        written = ctypes.c_int64(0)
+        st = self.lib.orc_paged_append(_ptr(ar), ar.nbytes, _ptr(pg), len(pg), _ptr(cnt),
+                                       page_stride, _ptr(ids), len(ids), _ptr(kn), _ptr(vn),
+                                       new_type, len(cnt), seq_len, k_head_dim, v_head_dim,
+                                       first_id, free_begin, free_end, k_format, k_scale,
+                                       k_zero_point, v_format, v_scale, v_zero_point,
+                                       ctypes.byref(flags), ctypes.byref(written))
+        return st, ar, pg, cnt, ids, flags.value, written.value
+
+    def paged_append_open(self, arena, pages, page_ptr, page_ids, k_new, v_new, new_type: int,
+                          head_dim: int, page_count=None, page_stride: int = 0):
+        """Open-page append on copies (each stream's token into its last page):
+        returns (arena, pages, flags)."""
+        ar = np.array(arena, dtype=np.uint8, copy=True)
+        pg = np.array(pages, dtype=PAGE_DTYPE, copy=True)
+        ptr = None if page_ptr is None else np.ascontiguousarray(page_ptr, dtype=np.int32)
+        cnt = None if page_count is None else np.ascontiguousarray(page_count, dtype=np.int32)
+        ids = np.ascontiguousarray(page_ids, dtype=np.int32)
+        kn, vn = np.ascontiguousarray(k_new), np.ascontiguousarray(v_new)
+        n_streams = len(cnt) if cnt is not None else len(ptr) - 1
+        flags = ctypes.c_uint32(0)
+        st = self.lib.orc_paged_append_open(_ptr(ar), ar.nbytes, _ptr(pg), len(pg), _ptr(ptr),
+                                            _ptr(cnt), page_stride, _ptr(ids), len(ids), _ptr(kn),
+                                            _ptr(vn), new_type, n_streams, head_dim,
+                                            ctypes.byref(flags))
         if st != OK:
-            raise OracleError(f"orc_paged_append status {st}")
+            raise OracleError(f"orc_paged_append_open status {st}")
         return ar, pg, flags.value
 
 

@@ -861,55 +861,76 @@ static int pg_code_range(int fmt, int32_t *lo, int32_t *hi)
     }
 }
 
-/* bytes of one row, or -1 when the format is unknown or the row is not whole bytes */
-static int64_t pg_row_bytes(int fmt, int64_t head_dim)
+/* Bytes of a payload of n elements. A block's K (or V) payload is its logical
+ * tensor [1, 1, capacity, head_size]: element e of row r sits at flat index
+ * r * head_size + e, sub-byte codes follow one another with no gap at row
+ * ends and only the last byte is padded. -1 for an unknown format. */
+static int64_t pg_payload_bytes(int fmt, int64_t n)
 {
     const int bits = pg_bits(fmt);
-    if (bits == 0 || (head_dim * bits) % 8 != 0)
+    if (bits == 0 || n < 0 || n > INT64_MAX / 32)
         return -1;
-    return head_dim * bits / 8;
+    return (n * bits + 7) / 8;
 }
 
 /* a format with its parameters: an affine one needs a positive finite scale and
  * a zero point inside its code range */
-static int pg_format_ok(int fmt, float scale, int32_t zero_point, int64_t head_dim)
+static int pg_format_ok(int fmt, float scale, int32_t zero_point)
 {
     int32_t lo, hi;
-    if (pg_row_bytes(fmt, head_dim) < 0)
+    if (pg_bits(fmt) == 0)
         return 0;
     if (pg_code_range(fmt, &lo, &hi))
         return scale > 0.0f && !isinf(scale) && zero_point >= lo && zero_point <= hi;
     return 1;
 }
 
-/* [offset, offset + bytes) inside [0, arena_bytes), offset 16-byte aligned (the
- * library's layout rule for payloads) */
+/* [offset, offset + bytes) inside [0, arena_bytes) */
 static int pg_inside(int64_t offset, int64_t bytes, int64_t arena_bytes)
 {
-    return offset >= 0 && offset % 16 == 0 && bytes >= 0 && offset <= arena_bytes &&
-           bytes <= arena_bytes - offset;
+    return offset >= 0 && bytes >= 0 && offset <= arena_bytes && bytes <= arena_bytes - offset;
 }
 
-static int pg_page_ok(const orc_page *p, int64_t head_dim, int64_t arena_bytes)
+/* a page whose K rows hold k_dim and V rows v_dim elements */
+static int pg_page_ok(const orc_page *p, int64_t k_dim, int64_t v_dim, int64_t arena_bytes)
 {
     if (p->start < 0 || p->capacity < 1 || p->length < 1 || p->length > p->capacity)
         return 0;
-    if (!pg_format_ok(p->k_format, p->k_scale, p->k_zero_point, head_dim) ||
-        !pg_format_ok(p->v_format, p->v_scale, p->v_zero_point, head_dim))
+    if (!pg_format_ok(p->k_format, p->k_scale, p->k_zero_point) ||
+        !pg_format_ok(p->v_format, p->v_scale, p->v_zero_point))
         return 0;
     if (p->start > INT64_MAX - p->length)
         return 0;
-    return pg_inside(p->k_offset, p->capacity * pg_row_bytes(p->k_format, head_dim), arena_bytes) &&
-           pg_inside(p->v_offset, p->capacity * pg_row_bytes(p->v_format, head_dim), arena_bytes);
+    return pg_inside(p->k_offset, pg_payload_bytes(p->k_format, p->capacity * k_dim), arena_bytes) &&
+           pg_inside(p->v_offset, pg_payload_bytes(p->v_format, p->capacity * v_dim), arena_bytes);
 }
 
-/* code e of an affine row: bits e*b .. e*b + b - 1 counted from the least
+/* The block table: stream s's pages, in token order, are page_ids[*p0 .. *p1).
+ * Without page_count (compressed rows): *p0 = page_ptr[s], *p1 = page_ptr[s+1].
+ * With page_count (slotted rows): the stream owns the page_stride slots from
+ * *p0 = s * page_stride and uses the first page_count[s] of them. Returns 0
+ * when the range does not lie inside page_ids. */
+static int pg_stream(const int32_t *page_ptr, const int32_t *page_count, int64_t page_stride,
+                     int64_t n_ids, int64_t s, int64_t *p0, int64_t *p1)
+{
+    if (page_count) {
+        const int64_t n = page_count[s];
+        *p0 = s * page_stride;
+        *p1 = *p0 + n;
+        return n >= 0 && n <= page_stride && page_stride <= n_ids - *p0;
+    }
+    *p0 = page_ptr[s];
+    *p1 = page_ptr[s + 1];
+    return *p0 >= 0 && *p1 >= *p0 && *p1 <= n_ids;
+}
+
+/* code i of an affine payload: bits i*b .. i*b + b - 1 counted from the least
  * significant bit of byte 0; signed formats in two's complement */
-static int32_t pg_get_code(int fmt, const char *row, int64_t e)
+static int32_t pg_get_code(int fmt, const char *base, int64_t i)
 {
     const int bits = pg_bits(fmt);
-    const int64_t bit = e * bits;
-    const unsigned byte = (unsigned char)row[bit / 8];
+    const int64_t bit = i * bits;
+    const unsigned byte = (unsigned char)base[bit / 8];
     const unsigned raw = (byte >> (bit % 8)) & ((1u << bits) - 1u);
     const int is_signed = fmt == ORC_XF_INT8 || fmt == ORC_XF_INT4 || fmt == ORC_XF_INT2;
     if (is_signed && (raw >> (bits - 1)))
@@ -917,48 +938,49 @@ static int32_t pg_get_code(int fmt, const char *row, int64_t e)
     return (int32_t)raw;
 }
 
-static void pg_put_code(int fmt, char *row, int64_t e, int32_t code)
+static void pg_put_code(int fmt, char *base, int64_t i, int32_t code)
 {
     const int bits = pg_bits(fmt);
-    const int64_t bit = e * bits;
+    const int64_t bit = i * bits;
     const unsigned mask = ((1u << bits) - 1u) << (bit % 8);
-    unsigned byte = (unsigned char)row[bit / 8];
+    unsigned byte = (unsigned char)base[bit / 8];
     byte = (byte & ~mask) | (((unsigned)code << (bit % 8)) & mask);
-    row[bit / 8] = (char)byte;
+    base[bit / 8] = (char)byte;
 }
 
-/* element e as a float64 value (exact: a dense element, or (c - zp) * scale
- * with a small integer and a binary32 scale) */
-static double pg_value64(int fmt, float scale, int32_t zero_point, const char *row, int64_t e)
+/* element i of a payload as a float64 value (exact: a dense element, or
+ * (c - zp) * scale with a small integer and a binary32 scale) */
+static double pg_value64(int fmt, float scale, int32_t zero_point, const char *base, int64_t i)
 {
     int32_t lo, hi;
     if (pg_code_range(fmt, &lo, &hi))
-        return (double)(pg_get_code(fmt, row, e) - zero_point) * (double)scale;
-    return (double)xf_load(fmt, row, e);
+        return (double)(pg_get_code(fmt, base, i) - zero_point) * (double)scale;
+    return (double)xf_load(fmt, base, i);
 }
 
-/* element e decoded in binary32: a dense element as is, an affine one as
+/* element i decoded in binary32: a dense element as is, an affine one as
  * fl((c - zp) * scale), one rounding */
-static float pg_value32(int fmt, float scale, int32_t zero_point, const char *row, int64_t e)
+static float pg_value32(int fmt, float scale, int32_t zero_point, const char *base, int64_t i)
 {
     int32_t lo, hi;
     if (pg_code_range(fmt, &lo, &hi))
-        return (float)(pg_get_code(fmt, row, e) - zero_point) * scale;
-    return xf_load(fmt, row, e);
+        return (float)(pg_get_code(fmt, base, i) - zero_point) * scale;
+    return xf_load(fmt, base, i);
 }
 
-/* element e written in a target format */
-static void pg_store(int fmt, float scale, int32_t zero_point, char *row, int64_t e, float y)
+/* element i written in a target format */
+static void pg_store(int fmt, float scale, int32_t zero_point, char *base, int64_t i, float y)
 {
     int32_t lo, hi;
     if (pg_code_range(fmt, &lo, &hi))
-        pg_put_code(fmt, row, e, xf_quantize(y, scale, zero_point, lo, hi));
+        pg_put_code(fmt, base, i, xf_quantize(y, scale, zero_point, lo, hi));
     else
-        store_dense(fmt, row, e, y);
+        store_dense(fmt, base, i, y);
 }
 
 int orc_paged_attention(const void *q, int q_type, const char *arena, int64_t arena_bytes,
                         const orc_page *pages, int64_t n_pages, const int32_t *page_ptr,
+                        const int32_t *page_count, int64_t page_stride,
                         const int32_t *page_ids, int64_t n_ids, double *out,
                         int64_t left_window, int64_t batch, int64_t q_heads,
                         int64_t kv_heads, int64_t head_dim, double scale, uint32_t *flags)
@@ -970,12 +992,12 @@ int orc_paged_attention(const void *q, int q_type, const char *arena, int64_t ar
 
     if (B < 0 || Hq < 0 || Hkv < 1 || D < 0 || n_pages < 0 || n_ids < 0 || arena_bytes < 0)
         return ORC_E_INVALID_ARG;
-    if (!xf_float_type(q_type) || Hq % Hkv != 0)
+    if (!xf_float_type(q_type) || Hq % Hkv != 0 || (page_count && page_stride < 1))
         return ORC_E_INVALID_ARG;
     if (B == 0 || Hq == 0 || D == 0)
         return ORC_OK;
-    if (!q || !out || !page_ptr || (n_pages > 0 && !pages) || (n_ids > 0 && !page_ids) ||
-        (arena_bytes > 0 && !arena))
+    if (!q || !out || (!page_ptr && !page_count) || (n_pages > 0 && !pages) ||
+        (n_ids > 0 && !page_ids) || (arena_bytes > 0 && !arena))
         return ORC_E_INVALID_ARG;
     qes = xf_elem_bytes(q_type);
     group = Hq / Hkv;
@@ -989,18 +1011,18 @@ int orc_paged_attention(const void *q, int q_type, const char *arena, int64_t ar
     for (int64_t b = 0; b < B; ++b) {
         for (int64_t g = 0; g < Hkv; ++g) {
             const int64_t st = b * Hkv + g;
-            const int64_t p0 = page_ptr[st], p1 = page_ptr[st + 1];
+            int64_t p0, p1;
             int64_t T = 0, r0 = 0, nv = 0, ok = 1;
             /* the stream's pages the window reaches, walked back from the last:
              * each must be valid and end where the next one starts */
-            if (p0 < 0 || p1 < p0 || p1 > n_ids)
+            if (!pg_stream(page_ptr, page_count, page_stride, n_ids, st, &p0, &p1))
                 ok = 0;
             if (ok && p1 > p0) {
                 int64_t end = -1;
                 for (int64_t k = p1 - 1; k >= p0 && ok; --k) {
                     const int64_t id = page_ids[k];
                     const orc_page *p;
-                    if (id < 0 || id >= n_pages || !pg_page_ok(&pages[id], D, arena_bytes)) {
+                    if (id < 0 || id >= n_pages || !pg_page_ok(&pages[id], D, D, arena_bytes)) {
                         ok = 0;
                         break;
                     }
@@ -1037,18 +1059,15 @@ int orc_paged_attention(const void *q, int q_type, const char *arena, int64_t ar
                 for (int pass = 0; pass < 2; ++pass) {
                     for (int64_t v = nv - 1; v >= 0; --v) {
                         const orc_page *p = &pages[visit[v]];
-                        const int64_t kr = pg_row_bytes(p->k_format, D);
-                        const int64_t vr = pg_row_bytes(p->v_format, D);
+                        const char *kbase = arena + p->k_offset, *vbase = arena + p->v_offset;
                         for (int64_t i = 0; i < p->length; ++i) {
-                            const char *krow, *vrow;
                             double dot = 0.0, sc;
                             if (p->start + i < r0)
                                 continue;
-                            krow = arena + p->k_offset + i * kr;
-                            vrow = arena + p->v_offset + i * vr;
                             for (int64_t d = 0; d < D; ++d)
                                 dot += (double)xf_load(q_type, qrow, d) *
-                                       pg_value64(p->k_format, p->k_scale, p->k_zero_point, krow, d);
+                                       pg_value64(p->k_format, p->k_scale, p->k_zero_point, kbase,
+                                                  i * D + d);
                             sc = scale * dot;
                             if (pass == 0) {
                                 if (sc > m)
@@ -1058,7 +1077,7 @@ int orc_paged_attention(const void *q, int q_type, const char *arena, int64_t ar
                                 denom += w;
                                 for (int64_t d = 0; d < D; ++d)
                                     acc[d] += w * pg_value64(p->v_format, p->v_scale,
-                                                             p->v_zero_point, vrow, d);
+                                                             p->v_zero_point, vbase, i * D + d);
                             }
                         }
                     }
@@ -1101,7 +1120,7 @@ int orc_paged_quantize(char *arena, int64_t arena_bytes, const orc_page *pages_i
     if (free_begin < 0 || free_end < free_begin || free_end > arena_bytes)
         return ORC_E_INVALID_ARG;
     for (int t = 0; t < 2; ++t) {
-        if (!pg_format_ok(fmt[t], sc[t], zp[t], D))
+        if (!pg_format_ok(fmt[t], sc[t], zp[t]))
             return ORC_E_INVALID_ARG;
         if (!pg_code_range(fmt[t], &lo, &hi)) { /* a dense target has no parameters */
             sc[t] = 1.0f;
@@ -1110,12 +1129,12 @@ int orc_paged_quantize(char *arena, int64_t arena_bytes, const orc_page *pages_i
     }
     for (int64_t i = 0; i < n_pages; ++i) {
         const orc_page *p = &pages_in[i];
-        if (!pg_page_ok(p, D, arena_bytes))
+        if (!pg_page_ok(p, D, D, arena_bytes))
             return ORC_E_INVALID_ARG;
         if (pg_overlap(free_begin, free_end - free_begin, p->k_offset,
-                       p->capacity * pg_row_bytes(p->k_format, D)) ||
+                       pg_payload_bytes(p->k_format, p->capacity * D)) ||
             pg_overlap(free_begin, free_end - free_begin, p->v_offset,
-                       p->capacity * pg_row_bytes(p->v_format, D)))
+                       pg_payload_bytes(p->v_format, p->capacity * D)))
             return ORC_E_INVALID_ARG; /* the free region holds no live payload */
     }
     for (int64_t i = 0; i < n_blocks; ++i) {
@@ -1123,9 +1142,9 @@ int orc_paged_quantize(char *arena, int64_t arena_bytes, const orc_page *pages_i
         if (id < 0 || id >= n_pages || (i > 0 && id <= blocks[i - 1]))
             return ORC_E_INVALID_ARG;
         for (int t = 0; t < 2; ++t) {
-            const int64_t bytes = pages_in[id].capacity * pg_row_bytes(fmt[t], D);
+            const int64_t bytes = pg_payload_bytes(fmt[t], pages_in[id].capacity * D);
             const int64_t dst = dst_offsets[2 * i + t];
-            if (dst < next || dst % 16 != 0 || bytes > free_end - dst)
+            if (dst < next || bytes > free_end - dst)
                 return ORC_E_INVALID_ARG;
             next = dst + bytes;
         }
@@ -1137,14 +1156,15 @@ int orc_paged_quantize(char *arena, int64_t arena_bytes, const orc_page *pages_i
             const int sfmt = t ? p->v_format : p->k_format;
             const float ss = t ? p->v_scale : p->k_scale;
             const int32_t sz = t ? p->v_zero_point : p->k_zero_point;
-            const int64_t srb = pg_row_bytes(sfmt, D), drb = pg_row_bytes(fmt[t], D);
             const char *src = arena + (t ? p->v_offset : p->k_offset);
             char *dst = arena + dst_offsets[2 * i + t];
+            /* a packed payload's padding bits in its last byte are zero */
+            memset(dst, 0, (size_t)pg_payload_bytes(fmt[t], p->capacity * D));
             for (int64_t r = 0; r < p->capacity; ++r)
                 for (int64_t e = 0; e < D; ++e) {
                     /* rows past the valid prefix are logical zeros, never read */
-                    const float y = r < p->length ? pg_value32(sfmt, ss, sz, src + r * srb, e) : 0.0f;
-                    pg_store(fmt[t], sc[t], zp[t], dst + r * drb, e, y);
+                    const float y = r < p->length ? pg_value32(sfmt, ss, sz, src, r * D + e) : 0.0f;
+                    pg_store(fmt[t], sc[t], zp[t], dst, r * D + e, y);
                 }
         }
     }
@@ -1167,31 +1187,133 @@ int orc_paged_quantize(char *arena, int64_t arena_bytes, const orc_page *pages_i
 }
 
 int orc_paged_append(char *arena, int64_t arena_bytes, orc_page *pages, int64_t n_pages,
-                     const int32_t *page_ptr, const int32_t *page_ids, int64_t n_ids,
+                     int32_t *page_count, int64_t page_stride, int32_t *page_ids, int64_t n_ids,
                      const void *k_new, const void *v_new, int new_type, int64_t n_streams,
-                     int64_t head_dim, uint32_t *flags)
+                     int64_t seq_len, int64_t k_head_dim, int64_t v_head_dim, int64_t first_id,
+                     int64_t free_begin, int64_t free_end, int k_format, float k_scale,
+                     int32_t k_zero_point, int v_format, float v_scale, int32_t v_zero_point,
+                     uint32_t *flags, int64_t *written_bytes)
+{
+    const int64_t S = seq_len, dim[2] = {k_head_dim, v_head_dim};
+    const int fmt[2] = {k_format, v_format};
+    const char *news[2] = {(const char *)k_new, (const char *)v_new};
+    float sc[2] = {k_scale, v_scale};
+    int32_t zp[2] = {k_zero_point, v_zero_point};
+    int64_t bytes[2], stride, nes, written = 0;
+    int32_t lo, hi;
+
+    if (written_bytes)
+        *written_bytes = 0;
+    if (n_streams < 0 || S < 1 || k_head_dim < 1 || v_head_dim < 1 || n_pages < 0 || n_ids < 0 ||
+        arena_bytes < 0 || !xf_float_type(new_type) || page_stride < 1)
+        return ORC_E_INVALID_ARG;
+    for (int t = 0; t < 2; ++t) {
+        if (!pg_format_ok(fmt[t], sc[t], zp[t]) || dim[t] > INT64_MAX / 64 / S)
+            return ORC_E_INVALID_ARG;
+        if (!pg_code_range(fmt[t], &lo, &hi)) { /* a dense block has no parameters */
+            sc[t] = 1.0f;
+            zp[t] = 0;
+        }
+        bytes[t] = pg_payload_bytes(fmt[t], S * dim[t]);
+    }
+    stride = bytes[0] + bytes[1]; /* one stream's new payload: K, then V */
+    /* the new descriptors take ids first_id .. first_id + n_streams - 1, the new
+     * payloads the start of the free region, stream after stream */
+    if (first_id < 0 || first_id > n_pages - n_streams)
+        return ORC_E_INVALID_ARG;
+    if (free_begin < 0 || free_end < free_begin || free_end > arena_bytes ||
+        (n_streams > 0 && stride > (free_end - free_begin) / n_streams))
+        return ORC_E_INVALID_ARG;
+    if (n_streams > n_ids / page_stride)
+        return ORC_E_INVALID_ARG; /* every stream's slots inside page_ids */
+    if (n_streams == 0)
+        return ORC_OK;
+    if (!page_count || !page_ids || !k_new || !v_new || !pages || (arena_bytes > 0 && !arena))
+        return ORC_E_INVALID_ARG;
+    nes = xf_elem_bytes(new_type);
+    for (int64_t s = 0; s < n_streams; ++s) {
+        int64_t p0, p1, T = 0, id = first_id + s;
+        char *dst[2];
+        orc_page *np;
+        if (!pg_stream(NULL, page_count, page_stride, n_ids, s, &p0, &p1)) {
+            set_flag(flags, ORC_FLAG_BAD_PAGES);
+            continue;
+        }
+        if (p1 == p0 + page_stride) { /* no free slot for the new block */
+            set_flag(flags, ORC_FLAG_PAGE_FULL);
+            continue;
+        }
+        if (p1 > p0) {
+            /* the last block fixes where the new one starts; it is never written.
+             * Its id may not be one of the ids this call hands out. */
+            const int64_t last = page_ids[p1 - 1];
+            if (last < 0 || last >= n_pages || (last >= first_id && last < first_id + n_streams) ||
+                !pg_page_ok(&pages[last], k_head_dim, v_head_dim, arena_bytes) ||
+                pages[last].start + pages[last].length > INT64_MAX - S) {
+                set_flag(flags, ORC_FLAG_BAD_PAGES);
+                continue;
+            }
+            T = pages[last].start + pages[last].length;
+        }
+        /* the new block: S tokens, capacity S, encoded in the call's formats */
+        dst[0] = arena + free_begin + s * stride;
+        dst[1] = dst[0] + bytes[0];
+        for (int t = 0; t < 2; ++t) {
+            memset(dst[t], 0, (size_t)bytes[t]); /* padding bits of a packed last byte */
+            for (int64_t r = 0; r < S; ++r)
+                for (int64_t e = 0; e < dim[t]; ++e)
+                    pg_store(fmt[t], sc[t], zp[t], dst[t], r * dim[t] + e,
+                             xf_load(new_type, news[t] + (s * S + r) * dim[t] * nes, e));
+            written += bytes[t];
+        }
+        np = &pages[id];
+        memset(np, 0, sizeof(*np));
+        np->start = T;
+        np->length = (int32_t)S;
+        np->capacity = (int32_t)S;
+        np->k_offset = free_begin + s * stride;
+        np->v_offset = np->k_offset + bytes[0];
+        np->k_format = fmt[0];
+        np->v_format = fmt[1];
+        np->k_scale = sc[0];
+        np->v_scale = sc[1];
+        np->k_zero_point = zp[0];
+        np->v_zero_point = zp[1];
+        /* the stream's next slot names the new block */
+        page_ids[p1] = (int32_t)id;
+        page_count[s] += 1;
+    }
+    if (written_bytes)
+        *written_bytes = written;
+    return ORC_OK;
+}
+
+int orc_paged_append_open(char *arena, int64_t arena_bytes, orc_page *pages, int64_t n_pages,
+                          const int32_t *page_ptr, const int32_t *page_count, int64_t page_stride,
+                          const int32_t *page_ids, int64_t n_ids, const void *k_new,
+                          const void *v_new, int new_type, int64_t n_streams, int64_t head_dim,
+                          uint32_t *flags)
 {
     const int64_t D = head_dim;
     int64_t nes;
     if (n_streams < 0 || D < 1 || n_pages < 0 || n_ids < 0 || arena_bytes < 0 ||
-        !xf_float_type(new_type))
+        !xf_float_type(new_type) || (page_count && page_stride < 1))
         return ORC_E_INVALID_ARG;
     if (n_streams == 0)
         return ORC_OK;
-    if (!page_ptr || !k_new || !v_new || (n_pages > 0 && !pages) || (n_ids > 0 && !page_ids) ||
-        (arena_bytes > 0 && !arena))
+    if ((!page_ptr && !page_count) || !k_new || !v_new || (n_pages > 0 && !pages) ||
+        (n_ids > 0 && !page_ids) || (arena_bytes > 0 && !arena))
         return ORC_E_INVALID_ARG;
     nes = xf_elem_bytes(new_type);
     for (int64_t s = 0; s < n_streams; ++s) {
-        const int64_t p0 = page_ptr[s], p1 = page_ptr[s + 1];
-        int64_t id;
+        int64_t p0, p1, id;
         orc_page *p;
-        if (p0 < 0 || p1 <= p0 || p1 > n_ids) {
+        if (!pg_stream(page_ptr, page_count, page_stride, n_ids, s, &p0, &p1) || p1 == p0) {
             set_flag(flags, ORC_FLAG_BAD_PAGES);
             continue;
         }
         id = page_ids[p1 - 1]; /* the stream's last page takes the token */
-        if (id < 0 || id >= n_pages || !pg_page_ok(&pages[id], D, arena_bytes)) {
+        if (id < 0 || id >= n_pages || !pg_page_ok(&pages[id], D, D, arena_bytes)) {
             set_flag(flags, ORC_FLAG_BAD_PAGES);
             continue;
         }
@@ -1205,9 +1327,9 @@ int orc_paged_append(char *arena, int64_t arena_bytes, orc_page *pages, int64_t 
             const float sc = t ? p->v_scale : p->k_scale;
             const int32_t zp = t ? p->v_zero_point : p->k_zero_point;
             const char *in = (const char *)(t ? v_new : k_new) + s * D * nes;
-            char *row = arena + (t ? p->v_offset : p->k_offset) + p->length * pg_row_bytes(fmt, D);
+            char *base = arena + (t ? p->v_offset : p->k_offset);
             for (int64_t e = 0; e < D; ++e)
-                pg_store(fmt, sc, zp, row, e, xf_load(new_type, in, e));
+                pg_store(fmt, sc, zp, base, p->length * D + e, xf_load(new_type, in, e));
         }
         p->length += 1;
     }

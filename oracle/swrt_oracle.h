@@ -238,15 +238,16 @@ int orc_window_attention(const void *q, const void *k_cache, const void *v_cache
 
 /*
  * [PF-PAGED] one page (block) of a paged cache: tokens [start, start + length)
- * of one stream (batch entry, KV head), capacity physical rows of head_dim
- * elements for K and for V at byte offsets of an arena. Dense formats
- * (ORC_XF_F32 / F16 / BF16) hold values; affine formats (INT8, UINT8, INT4,
- * UINT4, INT2, UINT2) hold codes c with value (c - zero_point) * scale.
- * Payload offsets are 16-byte aligned. A row of a b-bit format is
- * head_dim * b / 8 bytes; sub-byte codes pack from the
- * least significant bits of each byte (element 0 in the low bits), signed
- * codes in two's complement. The layout is the GPU library's page descriptor
- * (64 bytes), defined here on its own.
+ * of one stream (batch entry, KV head), capacity physical rows of K and of V
+ * at byte offsets of an arena. Dense formats (ORC_XF_F32 / F16 / BF16) hold
+ * values; affine formats (INT8, UINT8, INT4, UINT4, INT2, UINT2) hold codes c
+ * with value (c - zero_point) * scale. A K (or V) payload is the block's
+ * logical tensor [1, 1, capacity, head_size] stored flat: element e of row r
+ * is element r * head_size + e; sub-byte codes pack from the least
+ * significant bits of each byte (element 0 in the low bits), one after
+ * another across row ends, the last byte padded; signed codes in two's
+ * complement. The layout is the GPU library's page descriptor (64 bytes),
+ * defined here on its own.
  */
 typedef struct {
     int64_t start;
@@ -264,25 +265,36 @@ typedef struct {
 } orc_page;
 
 /*
+ * [PF-PAGED] the block table names each stream's pages in token order, as
+ * ids into the descriptor array, in one of two forms:
+ *   compressed rows  page_count NULL: stream s owns
+ *                    page_ids[page_ptr[s] .. page_ptr[s + 1]);
+ *   slotted rows     page_count given: stream s owns the page_stride slots
+ *                    from s * page_stride and uses the first page_count[s]
+ *                    (0 <= page_count[s] <= page_stride); page_ptr unused.
+ */
+
+/*
  * [PF-PAGED] + [ATT]: one-token decode attention over paged caches. Stream
- * s = b * kv_heads + g owns pages page_ids[page_ptr[s] .. page_ptr[s+1]) in
- * token order; its length T is the last page's start + length (0 without
- * pages). Query head h of entry b reads stream b * kv_heads + h / (Hq / Hkv)
- * over tokens [max(0, T - 1 - left_window), T) (left_window < 0: all T; the
- * query is token T - 1 and left_window bounds the tokens before it), in
- * float64 from the exactly decoded values:
+ * s = b * kv_heads + g owns its pages through the block table; its length T
+ * is the last page's start + length (0 without pages). Query head h of entry
+ * b reads stream b * kv_heads + h / (Hq / Hkv) over tokens
+ * [max(0, T - 1 - left_window), T) (left_window < 0: all T; the query is
+ * token T - 1 and left_window bounds the tokens before it), in float64 from
+ * the exactly decoded values:
  *   o = sum_r exp(s_r - max s) v_r / sum_r exp(s_r - max s),  s_r = scale q.k_r
  * q [B, Hq, D] of q_type (F32 / F16 / BF16); out [B, Hq, D] float64.
  * The pages the window reaches must be contiguous (each start the previous
- * start + length), 1 <= length <= capacity, of valid formats and parameters
- * (scale > 0 and finite, zero point in the code range) and inside the arena;
- * page ids must be in [0, n_pages) and the stream's range of page_ids inside
- * [0, n_ids). A stream that fails is flagged BAD_PAGES and the outputs of its
- * query heads are left as they were; pages before the window are not read.
- * An empty window gives zeros.
+ * start + length, the first page starting at 0), 1 <= length <= capacity, of
+ * valid formats and parameters (scale > 0 and finite, zero point in the code
+ * range) and inside the arena; page ids must be in [0, n_pages) and the
+ * stream's range of the block table inside [0, n_ids). A stream that fails is
+ * flagged BAD_PAGES and the outputs of its query heads are left as they were;
+ * pages before the window are not read. An empty window gives zeros.
  */
 int orc_paged_attention(const void *q, int q_type, const char *arena, int64_t arena_bytes,
                         const orc_page *pages, int64_t n_pages, const int32_t *page_ptr,
+                        const int32_t *page_count, int64_t page_stride,
                         const int32_t *page_ids, int64_t n_ids, double *out,
                         int64_t left_window, int64_t batch, int64_t q_heads,
                         int64_t kv_heads, int64_t head_dim, double scale, uint32_t *flags);
@@ -294,16 +306,16 @@ int orc_paged_attention(const void *q, int q_type, const char *arena, int64_t ar
  * formats at dst_offsets[2 i] (K) and dst_offsets[2 i + 1] (V): F32 as is
  * (NaN canonical), F16 / BF16 rounded to nearest even (NaN canonical), affine
  * formats as saturate(round_half_even(fl(y / scale)) + zero_point) (NaN ->
- * zero point), packed. Rows [length, capacity) are written as logical zeros
- * of the target (0.0, or the zero point's code) without reading the source.
- * pages_out (may be pages_in) is pages_in with the selected descriptors'
- * formats, parameters and offsets replaced; a dense target's scale is 1 and
- * zero point 0. Everything is checked first: every page of pages_in (valid,
- * its payloads outside the free region [free_begin, free_end)); the indices
- * strictly ascending in [0, n_pages); the targets; the destinations in the
- * order K0, V0, K1, V1, ... each 16-byte aligned and at or after the end of
- * the one before, inside the free region. On any failure nothing is written and the call
- * returns ORC_E_INVALID_ARG.
+ * zero point), packed (padding bits zero). Rows [length, capacity) are
+ * written as logical zeros of the target (0.0, or the zero point's code)
+ * without reading the source. pages_out (may be pages_in) is pages_in with
+ * the selected descriptors' formats, parameters and offsets replaced; a
+ * dense target's scale is 1 and zero point 0. Everything is checked first:
+ * every page of pages_in (valid, its payloads outside the free region
+ * [free_begin, free_end)); the indices strictly ascending in [0, n_pages);
+ * the targets; the destinations in the order K0, V0, K1, V1, ... each at or
+ * after the end of the one before, inside the free region. On any failure
+ * nothing is written and the call returns ORC_E_INVALID_ARG.
  */
 int orc_paged_quantize(char *arena, int64_t arena_bytes, const orc_page *pages_in,
                        int64_t n_pages, const int32_t *blocks, int64_t n_blocks,
@@ -312,17 +324,54 @@ int orc_paged_quantize(char *arena, int64_t arena_bytes, const orc_page *pages_i
                        int v_format, float v_scale, int32_t v_zero_point, int64_t head_dim);
 
 /*
- * [PF-PAGED] decode append: stream s writes its new K and V rows (new_type
- * F32 / F16 / BF16, [n_streams, head_dim]) as row `length` of its last page,
- * encoded in that page's formats as orc_paged_quantize encodes, and the
- * page's length grows by one. A stream without pages, or whose last page is
- * invalid, is flagged BAD_PAGES; one whose last page is full, PAGE_FULL;
- * either is skipped.
+ * [PF-PAGED] append with sealed blocks ("Partial blocks are sealed": an append
+ * adds new blocks and never rewrites an earlier, partly filled one). Every
+ * stream s < n_streams appends seq_len tokens as ONE new block:
+ *   id        first_id + s (descriptor pages[id] is written whole)
+ *   start     T, the stream's length (its last block's start + length; 0 for
+ *             a stream without blocks)
+ *   length    = capacity = seq_len
+ *   payload   K at free_begin + s * (kb + vb), V right after it, where kb and
+ *             vb are the packed payload bytes of seq_len rows of k_head_dim /
+ *             v_head_dim elements in k_format / v_format
+ *   formats   the call's k_format / v_format with their scalar parameters (a
+ *             dense format: scale 1, zero point 0), rows encoded from k_new /
+ *             v_new ([n_streams, seq_len, head_dim] of new_type) as
+ *             orc_paged_quantize encodes
+ * and the block table's next slot of the stream, page_ids[s * page_stride +
+ * page_count[s]], receives id, page_count[s] growing by one (slotted rows
+ * only). No earlier block, descriptor or payload byte is read beyond the
+ * last block's descriptor, and none is written. A stream whose slot count is
+ * out of range, or whose last block fails its checks (id in [0, n_pages) and
+ * not one this call hands out, a valid page), is flagged BAD_PAGES; one with
+ * all page_stride slots in use, PAGE_FULL; either is skipped and its id and
+ * payload room stay untouched. ORC_E_INVALID_ARG (nothing written) for bad
+ * arguments: formats, ids past n_pages, a free region too small for
+ * n_streams payloads or outside the arena, slots past n_ids.
+ * *written_bytes (may be NULL) receives the payload bytes written.
  */
 int orc_paged_append(char *arena, int64_t arena_bytes, orc_page *pages, int64_t n_pages,
-                     const int32_t *page_ptr, const int32_t *page_ids, int64_t n_ids,
+                     int32_t *page_count, int64_t page_stride, int32_t *page_ids, int64_t n_ids,
                      const void *k_new, const void *v_new, int new_type, int64_t n_streams,
-                     int64_t head_dim, uint32_t *flags);
+                     int64_t seq_len, int64_t k_head_dim, int64_t v_head_dim, int64_t first_id,
+                     int64_t free_begin, int64_t free_end, int k_format, float k_scale,
+                     int32_t k_zero_point, int v_format, float v_scale, int32_t v_zero_point,
+                     uint32_t *flags, int64_t *written_bytes);
+
+/*
+ * Open-block append, an extension beside the pages' sealed rule: stream s
+ * writes its new K and V rows (new_type F32 / F16 / BF16, [n_streams,
+ * head_dim]) as row `length` of its last page, encoded in that page's
+ * formats as orc_paged_quantize encodes, and the page's length grows by one.
+ * A stream without pages, or whose last page is invalid, is flagged
+ * BAD_PAGES; one whose last page is full, PAGE_FULL; either is skipped.
+ * Either block-table form.
+ */
+int orc_paged_append_open(char *arena, int64_t arena_bytes, orc_page *pages, int64_t n_pages,
+                          const int32_t *page_ptr, const int32_t *page_count, int64_t page_stride,
+                          const int32_t *page_ids, int64_t n_ids, const void *k_new,
+                          const void *v_new, int new_type, int64_t n_streams, int64_t head_dim,
+                          uint32_t *flags);
 
 #ifdef __cplusplus
 }

@@ -133,25 +133,41 @@ MUTANTS = {
     # paged caches
     "paged_window_one_short": ("T - 1 - left_window > 0 ? T - 1 - left_window : 0",
                                "T - left_window > 0 ? T - left_window : 0"),
-    "paged_zero_point_kept": ("return (double)(pg_get_code(fmt, row, e) - zero_point) * (double)scale;",
-                              "return (double)pg_get_code(fmt, row, e) * (double)scale;"),
+    "paged_zero_point_kept": ("return (double)(pg_get_code(fmt, base, i) - zero_point) * (double)scale;",
+                              "return (double)pg_get_code(fmt, base, i) * (double)scale;"),
     "paged_codes_high_bits_first": ("const unsigned raw = (byte >> (bit % 8))",
                                     "const unsigned raw = (byte >> ((8 - bits - bit % 8) & 7))"),
     "paged_codes_unsigned": ("if (is_signed && (raw >> (bits - 1)))", "if (0 && is_signed)"),
-    "paged_unused_rows_read": ("const float y = r < p->length ? pg_value32(sfmt, ss, sz, src + r * srb, e) : 0.0f;",
-                               "const float y = pg_value32(sfmt, ss, sz, src + r * srb, e);"),
+    "paged_unused_rows_read": ("const float y = r < p->length ? pg_value32(sfmt, ss, sz, src, r * D + e) : 0.0f;",
+                               "const float y = pg_value32(sfmt, ss, sz, src, r * D + e);"),
     "paged_contiguity_unchecked": ("} else if (p->start + p->length != end) {", "} else if (0) {"),
     "paged_reads_before_window": ("if (p->start <= r0)\n                        break;",
                                   "if (p->start <= r0)\n                        (void)0;"),
-    "paged_append_overwrites": ("(t ? p->v_offset : p->k_offset) + p->length * pg_row_bytes(fmt, D);",
-                                "(t ? p->v_offset : p->k_offset) + (p->length - 1) * pg_row_bytes(fmt, D);"),
+    "paged_append_overwrites": ("pg_store(fmt, sc, zp, base, p->length * D + e,",
+                                "pg_store(fmt, sc, zp, base, (p->length - 1) * D + e,"),
     "paged_append_length_kept": ("        p->length += 1;\n", "        (void)0;\n"),
-    "paged_dense_target_keeps_parameters": ("            sc[t] = 1.0f;\n            zp[t] = 0;\n", ""),
+    "paged_dense_target_keeps_parameters": ("/* a dense target has no parameters */\n            sc[t] = 1.0f;\n            zp[t] = 0;\n",
+                                            "/* a dense target has no parameters */\n"),
     "paged_live_payload_overwritable": ("return ORC_E_INVALID_ARG; /* the free region holds no live payload */",
                                         "(void)0;"),
     "paged_duplicates_accepted": ("(i > 0 && id <= blocks[i - 1])", "(i > 0 && id < blocks[i - 1])"),
-    "paged_destinations_overlap": ("if (dst < next || dst % 16 != 0 || bytes > free_end - dst)",
-                                   "if (dst % 16 != 0 || bytes > free_end - dst)"),
+    "paged_destinations_overlap": ("if (dst < next || bytes > free_end - dst)",
+                                   "if (bytes > free_end - dst)"),
+    # the sealed-block append and the slotted block table
+    "sealed_start_off_by_one": ("T = pages[last].start + pages[last].length;",
+                                "T = pages[last].start + pages[last].length - 1;"),
+    "sealed_v_over_k": ("dst[1] = dst[0] + bytes[0];", "dst[1] = dst[0];"),
+    "sealed_count_kept": ("page_count[s] += 1;", "(void)0;"),
+    "sealed_slot_overwrites_last": ("page_ids[p1] = (int32_t)id;",
+                                    "page_ids[p1 > p0 ? p1 - 1 : p1] = (int32_t)id;"),
+    "sealed_rows_byte_aligned": ("pg_store(fmt[t], sc[t], zp[t], dst[t], r * dim[t] + e,",
+                                 "pg_store(fmt[t], sc[t], zp[t], dst[t] + r * ((dim[t] * pg_bits(fmt[t]) + 7) / 8), e,"),
+    "sealed_handed_out_id_accepted": ("(last >= first_id && last < first_id + n_streams) ||", ""),
+    "sealed_full_not_flagged": ("if (p1 == p0 + page_stride) {", "if (0) {"),
+    "sealed_payloads_overlap": ("stride = bytes[0] + bytes[1];", "stride = bytes[0];"),
+    "sealed_dense_block_keeps_parameters": ("/* a dense block has no parameters */\n            sc[t] = 1.0f;\n            zp[t] = 0;\n",
+                                            "/* a dense block has no parameters */\n"),
+    "slotted_range_short": ("*p1 = *p0 + n;", "*p1 = *p0 + n - 1;"),
     "paged_heads_interleaved": ("const int64_t h = g * group + j;", "const int64_t h = j * Hkv + g;"),
     "paged_scale_dropped": ("sc = scale * dot;", "sc = dot;"),
 }

@@ -393,7 +393,254 @@ def test_invalid_requests_write_nothing(orc):
 
 # -- append ---------------------------------------------------------------------------
 
-def test_append_writes_the_next_row_and_grows_the_page(orc):
+def slotted(case: wl.PagedCase, stride: int):
+    """The case's block table as slotted rows: (page_count, page_ids) with
+    ``stride`` slots per stream (unused slots hold -1)."""
+    n = len(case.page_ptr) - 1
+    count = np.diff(case.page_ptr).astype(np.int32)
+    ids = np.full(n * stride, -1, np.int32)
+    for s in range(n):
+        ids[s * stride:s * stride + count[s]] = case.page_ids[case.page_ptr[s]:case.page_ptr[s + 1]]
+    return count, ids
+
+
+def grow_table(tb: np.ndarray, extra: int) -> np.ndarray:
+    """The descriptor table with ``extra`` unused descriptors after it."""
+    out = np.zeros(len(tb) + extra, oracle.PAGE_DTYPE)
+    out[:len(tb)] = tb
+    return out
+
+
+def test_sealed_append_the_pages_windowed_fixture(orc):
+    """The pages' windowed fixture: six retained tokens, then two tokens
+    appended with INT8 keys of width 2 and UINT4 values of width 3. The append
+    writes 7 new payload bytes (2 x 2 one-byte codes, 2 x 3 four-bit codes
+    packed into 3 bytes) and copies no prior block: every earlier payload
+    byte, descriptor and block-table slot is unchanged."""
+    g = wl.rng(60)
+    case = wl.paged_case(g, 2, [[(4, 4), (2, 4)]], lambda s, i, n: (F32, F32, 1.0, 1.0, 0, 0),
+                         spare_bytes=64)
+    # the case's pages have K and V rows of head_dim 2; V rows here are 3 wide:
+    # re-place the V payloads after the K ones, 3 floats a row
+    tb = table(case)
+    off = case.free_offset
+    arena = np.zeros(off + 4 * 4 * 3 * 2 + 64, np.uint8)
+    arena[:case.arena.nbytes] = case.arena
+    for pid in range(2):
+        tb[pid]["v_offset"] = off
+        vals = g.uniform(-1, 1, 4 * 3).astype(np.float32)
+        arena[off:off + vals.nbytes] = vals.view(np.uint8)
+        off += vals.nbytes
+    count, ids = slotted(case, 4)
+    tb3 = grow_table(tb, 1)
+    k = np.array([[[0.173, -0.173], [0.346, -0.346]]], np.float32)
+    v = np.array([[[0.173, -0.173, 0.173], [0.346, -0.346, 0.346]]], np.float32)
+    free = off
+    st, ar, out, cnt, ids2, flags, written = orc.paged_append(
+        arena, tb3, count, 4, ids, k, v, oracle.XF_F32, 2, 2, 3, 2, free, len(arena),
+        I8, 0.01, 0, U4, 0.25, 8)
+    assert st == oracle.OK and flags == 0
+    assert written == 7
+    # codes by hand: k / 0.01 = 17.3, -17.3, 34.6, -34.6; v / 0.25 + 8 = 8.692 ...
+    assert bytes(ar[free:free + 4]) == bytes([17, 256 - 17, 35, 256 - 35])
+    # V codes 9, 7, 9, 9, 7, 9 packed low nibble first, across the row boundary
+    assert bytes(ar[free + 4:free + 7]) == bytes([0x79, 0x99, 0x97])
+    keep = np.ones(len(ar), bool)
+    keep[free:free + 7] = False
+    np.testing.assert_array_equal(ar[keep], arena[keep])  # no prior payload copied or touched
+    assert out[:2].tobytes() == tb.tobytes()
+    new = out[2]
+    assert (new["start"], new["length"], new["capacity"]) == (6, 2, 2)
+    assert (new["k_offset"], new["v_offset"]) == (free, free + 4)
+    assert (new["k_format"], new["v_format"], new["k_zero_point"], new["v_zero_point"]) == \
+        (I8, U4, 0, 8)
+    assert new["k_scale"] == np.float32(0.01) and new["v_scale"] == 0.25
+    assert list(cnt) == [3] and list(ids2) == [ids[0], ids[1], 2, -1]
+
+
+def test_sealed_append_the_pages_dense_fixture(orc):
+    """The pages' dense fixture: three FLOAT tokens with widths 3 (K) and 2
+    (V) appended on each call write 60 payload bytes, however long the cache
+    has grown; each call's block starts where the last one ended."""
+    g = wl.rng(61)
+    n_calls = 6
+    arena = np.zeros(60 * n_calls, np.uint8)
+    tb = np.zeros(n_calls, oracle.PAGE_DTYPE)
+    count, ids = np.zeros(1, np.int32), np.full(n_calls, -1, np.int32)
+    for c in range(n_calls):
+        k = g.uniform(-1, 1, (1, 3, 3)).astype(np.float32)
+        v = g.uniform(-1, 1, (1, 3, 2)).astype(np.float32)
+        st, arena2, tb2, count2, ids2, flags, written = orc.paged_append(
+            arena, tb, count, n_calls, ids, k, v, oracle.XF_F32, 3, 3, 2, c, 60 * c, len(arena),
+            F32, 1.0, 0, F32, 1.0, 0)
+        assert st == oracle.OK and flags == 0 and written == 60
+        np.testing.assert_array_equal(arena2[:60 * c], arena[:60 * c])
+        assert tb2[:c].tobytes() == tb[:c].tobytes()
+        assert tb2[c]["start"] == 3 * c and tb2[c]["length"] == 3
+        np.testing.assert_array_equal(arena2[60 * c:60 * c + 36].view(np.float32), k.ravel())
+        np.testing.assert_array_equal(arena2[60 * c + 36:60 * c + 60].view(np.float32), v.ravel())
+        arena, tb, count, ids = arena2, tb2, count2, ids2
+    assert list(count) == [n_calls] and list(ids) == list(range(n_calls))
+
+
+@pytest.mark.parametrize("left_window", [-1, 0, 6, 30])
+def test_sealed_decode_blocks_attend_like_open_pages(orc, left_window):
+    """A decode loop that adds a one-token block per step (sealed rule) and
+    the same loop filling open pages hold the same tokens in different page
+    splits: attention over the slotted table equals attention over the
+    compressed one, bit for bit, at every step."""
+    g = wl.rng(62)
+    D, steps, Hq = 16, 12, 2
+    T0 = [5, 0, 16, 9]
+    streams = [wl.page_split(g, t, 8) for t in T0]
+    cap_pages = [[(n, 8) for n, _ in st] for st in streams]
+    # open pages: every stream gets a last page with room for all the steps
+    open_streams = [st + [(0, steps)] for st in cap_pages]
+    case = wl.paged_case(wl.rng(63), D, open_streams, lambda s, i, n: (F32, F32, 1.0, 1.0, 0, 0),
+                         spare_bytes=16 * D * 4 * steps * len(T0) + 4096)
+    # a page of length 0 is not valid: drop the empty last pages for the
+    # sealed copy, keep them (length 0 -> grows on the first append) for the
+    # open copy by starting it at length 1 with the first token
+    tb = table(case)
+    n_str = len(T0)
+    stride = 64
+    sealed_count = np.zeros(n_str, np.int32)
+    sealed_ids = np.full(n_str * stride, -1, np.int32)
+    for s in range(n_str):
+        pids = case.page_ids[case.page_ptr[s]:case.page_ptr[s + 1] - 1]
+        sealed_count[s] = len(pids)
+        sealed_ids[s * stride:s * stride + len(pids)] = pids
+    open_ids = case.page_ids.copy()
+    first_tok = g.uniform(-1, 1, (2, n_str, D)).astype(np.float32)
+    for s in range(n_str):  # the open pages start holding one token
+        pid = case.page_ids[case.page_ptr[s + 1] - 1]
+        tb[pid]["start"] = T0[s]
+        tb[pid]["length"] = 1
+        tb[pid]["capacity"] = steps + 1
+    arena = np.zeros(case.arena.nbytes + 2 * (steps + 1) * n_str * D * 4, np.uint8)
+    arena[:case.arena.nbytes] = case.arena
+    o = case.arena.nbytes
+    for s in range(n_str):
+        pid = case.page_ids[case.page_ptr[s + 1] - 1]
+        for kv in range(2):
+            tb[pid]["v_offset" if kv else "k_offset"] = o
+            arena[o:o + D * 4] = first_tok[kv, s].view(np.uint8)
+            o += (steps + 1) * D * 4
+    open_tb, open_arena = tb.copy(), arena.copy()
+    sealed_tb = grow_table(tb, n_str * (steps + 1))
+    sealed_arena = np.zeros(o + (steps + 1) * n_str * 2 * D * 4, np.uint8)
+    sealed_arena[:len(arena)] = arena
+    free = o
+    nxt = len(tb)
+    # the sealed copy takes the first token as a one-token block too
+    st, sealed_arena, sealed_tb, sealed_count, sealed_ids, f, _ = orc.paged_append(
+        sealed_arena, sealed_tb, sealed_count, stride, sealed_ids, first_tok[0][:, None],
+        first_tok[1][:, None], oracle.XF_F32, 1, D, D, nxt, free, len(sealed_arena),
+        F32, 1.0, 0, F32, 1.0, 0)
+    assert st == oracle.OK and f == 0
+    nxt += n_str
+    free += n_str * 2 * D * 4
+    for step in range(steps):
+        kn = g.uniform(-1, 1, (n_str, D)).astype(np.float32)
+        vn = g.uniform(-1, 1, (n_str, D)).astype(np.float32)
+        q = g.uniform(-1, 1, (n_str, Hq, D)).astype(np.float32)
+        open_arena, open_tb, f1 = orc.paged_append_open(open_arena, open_tb, case.page_ptr,
+                                                        open_ids, kn, vn, oracle.XF_F32, D)
+        st, sealed_arena, sealed_tb, sealed_count, sealed_ids, f2, w = orc.paged_append(
+            sealed_arena, sealed_tb, sealed_count, stride, sealed_ids, kn[:, None], vn[:, None],
+            oracle.XF_F32, 1, D, D, nxt, free, len(sealed_arena), F32, 1.0, 0, F32, 1.0, 0)
+        assert st == oracle.OK and f1 == f2 == 0 and w == n_str * 2 * D * 4
+        nxt += n_str
+        free += w
+        a, fa = orc.paged_attention(q, oracle.XF_F32, open_arena, open_tb, case.page_ptr,
+                                    open_ids, left_window, 1, 0.4)
+        b, fb = orc.paged_attention(q, oracle.XF_F32, sealed_arena, sealed_tb, None, sealed_ids,
+                                    left_window, 1, 0.4, page_count=sealed_count,
+                                    page_stride=stride)
+        assert fa == fb == 0
+        np.testing.assert_array_equal(a, b)
+    assert list(sealed_count) == [len(cp) + 1 + steps for cp in cap_pages]
+
+
+def test_sealed_append_flags_and_skips(orc):
+    """Per stream: an empty stream starts its first block at 0; a stream whose
+    slots are all in use is flagged PAGE_FULL; a last block that fails its
+    checks, or whose id is one this call hands out, is flagged BAD_PAGES; a
+    skipped stream's id and payload room stay untouched."""
+    g = wl.rng(64)
+    D = 16
+    streams = [wl.page_split(g, 10, 4), [], wl.page_split(g, 8, 4), wl.page_split(g, 5, 4),
+               wl.page_split(g, 3, 4)]
+    case = wl.paged_case(g, D, streams, lambda s, i, n: (BF16, I8, 1.0, 0.05, 0, 0),
+                         spare_bytes=4096)
+    tb = grow_table(table(case), 5)
+    count, ids = slotted(case, 4)
+    # stream 2 holds 2 pages in 4 slots: fill the other two (all slots in use)
+    ids[2 * 4 + 2] = ids[2 * 4 + 3] = ids[2 * 4 + 1]
+    count[2] = 4
+    tb[ids[3 * 4 + count[3] - 1]]["length"] = 0           # stream 3: invalid last block
+    first = case.n_pages
+    ids[4 * 4 + count[4] - 1] = first + 1                 # stream 4: its last id is handed out
+    kn = g.uniform(-1, 1, (5, 1, D)).astype(np.float32)
+    vn = g.uniform(-1, 1, (5, 1, D)).astype(np.float32)
+    free = case.free_offset
+    st, ar, out, cnt, ids2, flags, written = orc.paged_append(
+        case.arena, tb, count, 4, ids, kn, vn, oracle.XF_F32, 1, D, D, first, free,
+        len(case.arena), BF16, 0.5, 3, I8, 0.05, 0)  # a dense format's parameters are ignored
+    assert st == oracle.OK
+    assert flags == oracle.FLAG_PAGE_FULL | oracle.FLAG_BAD_PAGES
+    stride = 2 * D + D
+    assert written == 2 * stride
+    assert list(cnt) == [count[0] + 1, 1, 4, count[3], count[4]]
+    assert out[first]["start"] == 10 and out[first + 1]["start"] == 0
+    assert (out[first]["k_scale"], out[first]["k_zero_point"]) == (1.0, 0)
+    assert (out[first]["v_scale"], out[first]["v_zero_point"]) == (np.float32(0.05), 0)
+    assert ids2[0 * 4 + count[0]] == first and ids2[4] == first + 1
+    for s in (2, 3, 4):  # skipped: descriptor and payload room untouched
+        assert out[first + s].tobytes() == tb[first + s].tobytes()
+        np.testing.assert_array_equal(ar[free + s * stride:free + (s + 1) * stride],
+                                      case.arena[free + s * stride:free + (s + 1) * stride])
+    np.testing.assert_array_equal(ids2[8:], ids[8:])
+    # the new block's rows: bf16 K, int8 V codes
+    np.testing.assert_array_equal(ar[free:free + 2 * D].view(np.int16), bf16_bits(kn[0, 0]))
+    np.testing.assert_array_equal(ar[free + 2 * D:free + 3 * D].view(np.int8),
+                                  np.clip(np.rint(vn[0, 0] / np.float32(0.05)), -128, 127))
+
+
+def test_sealed_append_invalid_requests_write_nothing(orc):
+    g = wl.rng(65)
+    D = 16
+    case = wl.paged_case(g, D, [wl.page_split(g, 6, 4), wl.page_split(g, 2, 4)], dense_bf16,
+                         spare_bytes=1024)
+    tb = grow_table(table(case), 2)
+    count, ids = slotted(case, 4)
+    kn = g.uniform(-1, 1, (2, 1, D)).astype(np.float32)
+    free, end = case.free_offset, len(case.arena)
+    good = dict(first=case.n_pages, fb=free, fe=end, kf=BF16, ks=1.0, kz=0, vf=I8, vs=0.1, vz=0,
+                stride=4, S=1)
+
+    def run(**kw):
+        a = {**good, **kw}
+        return orc.paged_append(case.arena, tb, count, a["stride"], ids, kn, kn, oracle.XF_F32,
+                                a["S"], D, D, a["first"], a["fb"], a["fe"], a["kf"], a["ks"],
+                                a["kz"], a["vf"], a["vs"], a["vz"])
+    assert run()[0] == oracle.OK
+    for kw in (dict(first=case.n_pages + 1), dict(first=-1),   # ids past the table
+               dict(fe=free + 2 * 48 - 1),                      # room for one stream only
+               dict(fb=end + 16, fe=end + 16),                  # region past the arena
+               dict(stride=5),                                  # slots past page_ids
+               dict(ks=0.0, kf=I8), dict(vz=200), dict(kf=10),  # formats and parameters
+               dict(S=0)):
+        st, ar, out, cnt, ids2, flags, written = run(**kw)
+        assert st == oracle.E_INVALID_ARG, kw
+        np.testing.assert_array_equal(ar, case.arena)
+        assert out.tobytes() == tb.tobytes() and (cnt == count).all() and (ids2 == ids).all()
+        assert written == 0
+
+
+
+def test_open_append_writes_the_next_row_and_grows_the_page(orc):
+    """The open-page extension: each stream's token goes into its last page."""
     g = wl.rng(49)
     D = 16
     streams = [wl.page_split(g, 13, 8), wl.page_split(g, 8, 8), [], wl.page_split(g, 3, 4)]
@@ -402,8 +649,8 @@ def test_append_writes_the_next_row_and_grows_the_page(orc):
     tb = table(case)
     kn = g.uniform(-1, 1, (4, D)).astype(np.float32)
     vn = g.uniform(-1, 1, (4, D)).astype(np.float32)
-    ar, out, flags = orc.paged_append(case.arena, tb, case.page_ptr, case.page_ids, kn, vn,
-                                      oracle.XF_F32, D)
+    ar, out, flags = orc.paged_append_open(case.arena, tb, case.page_ptr, case.page_ids, kn, vn,
+                                           oracle.XF_F32, D)
     # stream 1's page is full, stream 2 has no pages
     assert flags == oracle.FLAG_PAGE_FULL | oracle.FLAG_BAD_PAGES
     p0 = tb[case.page_ids[1]]
