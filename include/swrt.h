@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define SWRT_ABI_VERSION 6
+#define SWRT_ABI_VERSION 7
 
 /* synchronous status codes */
 #define SWRT_OK 0
@@ -595,15 +595,19 @@ int swrt_window_attention(int n_layers, const void *const *q,
  * One page (block) of one stream (batch entry b, KV head g; stream
  * b * kv_heads + g): tokens [start, start + length) of the stream, capacity
  * physical rows of head_dim elements for K and for V at byte offsets of the
- * layer's arena (16-byte aligned). A row of a b-bit format is
- * head_dim * b / 8 bytes. Dense formats (SWRT_XF_F32 / _F16 / _BF16) hold
- * values; affine formats (SWRT_XF_INT8, _UINT8, _INT4, _UINT4, _INT2,
- * _UINT2) hold codes c meaning (c - zero_point) * scale, scale > 0 and
- * finite, zero_point inside the code range; sub-byte codes are packed from
- * the least significant bits of each byte (element 0 lowest), signed codes in
- * two's complement. A stream's pages, in token order, are contiguous from
- * zero (each start is the previous start + length) with
- * 1 <= length <= capacity. 64 bytes, device memory.
+ * layer's arena. A payload is the block's logical [1, 1, capacity, head_dim]
+ * tensor stored flat (row r, element e at r * head_dim + e). Dense formats
+ * (SWRT_XF_F32 / _F16 / _BF16) hold values; affine formats (SWRT_XF_INT8,
+ * _UINT8, _INT4, _UINT4, _INT2, _UINT2) hold codes c meaning
+ * (c - zero_point) * scale, scale > 0 and finite, zero_point inside the code
+ * range; sub-byte codes are packed from the least significant bits of each
+ * byte (element 0 lowest), signed codes in two's complement. A stream's
+ * pages, in token order, are contiguous from zero (each start is the previous
+ * start + length) with 1 <= length <= capacity. 64 bytes, device memory.
+ *
+ * Library layout rule (not the pages'): the kernels read payloads in
+ * aligned 16-byte blocks, so every payload offset is a multiple of 16; a page
+ * whose offset is not is treated as invalid (SWRT_FLAG_BAD_PAGES).
  */
 typedef struct swrt_page {
   int64_t start;
@@ -627,14 +631,21 @@ typedef struct swrt_page {
  *   out        [batch, q_heads, head_dim] out_type, 16-byte aligned; must not
  *              overlap any input.
  *   arena      device bytes holding every page payload, 16-byte aligned,
- *              arena_bytes long (a multiple of 16: the kernels read payload
- *              in aligned 16-byte blocks).
+ *              arena_bytes long (a multiple of 16).
  *   pages      device swrt_page[n_pages].
- *   page_ptr   device int32[batch * kv_heads + 1]: stream s owns
- *              page_ids[page_ptr[s] .. page_ptr[s + 1]) in token order.
- *   page_ids   device int32[n_ids]: indices into pages.
- * Layers may share pages, page_ptr and page_ids (one block table for every
- * layer, each with its own arena).
+ *   page_ids   device int32[n_ids]: indices into pages, the block table.
+ *   The block table names each stream's pages in token order, in one of
+ *   two forms:
+ *   page_ptr   compressed rows (page_count NULL): device int32[batch *
+ *              kv_heads + 1]; stream s owns page_ids[page_ptr[s] ..
+ *              page_ptr[s + 1]).
+ *   page_count slotted rows (non-NULL): device int32[batch * kv_heads];
+ *              stream s owns the page_stride slots from s * page_stride and
+ *              uses the first page_count[s] (0 .. page_stride) of them;
+ *              page_ptr is then unused (may be NULL). The sealed append
+ *              (swrt_paged_append) grows this form.
+ * Layers may share pages and the block table (one table for every layer,
+ * each with its own arena).
  */
 typedef struct swrt_paged_layer {
   const void *q;
@@ -646,6 +657,8 @@ typedef struct swrt_paged_layer {
   const int32_t *page_ptr;
   const int32_t *page_ids;
   int64_t n_ids;
+  int32_t *page_count;
+  int64_t page_stride;
 } swrt_paged_layer;
 
 /*
@@ -706,21 +719,64 @@ int swrt_paged_quantize(void *arena, int64_t arena_bytes, const swrt_page *pages
                         int32_t v_zero_point, int head_dim, uint32_t *d_flags, void *stream);
 
 /*
- * swrt_paged_append -- the decode step's new token into each stream's last
- * page: stream s writes k_new[s, :] and v_new[s, :] (new_type F32 / F16 /
- * BF16, [n_streams, head_dim], 16-byte aligned) as row `length` of page
- * page_ids[page_ptr[s + 1] - 1], encoded in that page's formats as
- * swrt_paged_quantize encodes, and that page's length grows by one (on the
- * device). A stream without pages or whose last page fails its checks raises
- * SWRT_FLAG_BAD_PAGES, one whose last page is full SWRT_FLAG_PAGE_FULL;
- * either is skipped. n_layers 1 .. SWRT_MAX_LAYERS, each with its own arena,
- * pages and block table (arena, pages, page_ptr, page_ids of each
- * swrt_paged_layer; q and out unused); pages must not be shared between the
- * layers of one call (each layer's append grows its own pages).
+ * swrt_paged_append -- append with sealed blocks (section "Optional
+ * heterogeneous paged KV": partial blocks are sealed, so an append adds new
+ * blocks and never rewrites an earlier, partly filled one; the selected
+ * format is stored in every new block; affine appends use scalar
+ * parameters). Every stream s < n_streams of every layer appends seq_len
+ * tokens as ONE new block:
+ *   descriptor  pages[first_id + s], written whole: start = T (the stream's
+ *               last block's start + length; 0 for a stream without
+ *               blocks), length = capacity = seq_len, the call's formats and
+ *               parameters (a dense format: scale 1, zero point 0)
+ *   payload     K at free_begin + s * (kb + vb), V at that + kb, where kb, vb
+ *               are the bytes of seq_len rows of head_dim elements in
+ *               k_format / v_format; rows encoded from k_new / v_new
+ *               ([n_streams, seq_len, head_dim] of new_type F32 / F16 / BF16,
+ *               16-byte aligned) as swrt_paged_quantize encodes
+ *   block table page_ids[s * page_stride + page_count[s]] = first_id + s,
+ *               then page_count[s] + 1 (slotted rows: page_count required)
+ * Only the last block's descriptor is read; no earlier payload, descriptor
+ * or slot is written. A stream whose page_count is out of [0, page_stride],
+ * or whose last block fails its checks (id in [0, n_pages) and not among the
+ * ids this call hands out, a valid page), raises SWRT_FLAG_BAD_PAGES; one
+ * with all page_stride slots in use, SWRT_FLAG_PAGE_FULL; either is skipped
+ * and its id and payload room stay untouched. The caller keeps the free
+ * region clear of live payload (not checked: it would cost a pass over every
+ * page) and first_id .. first_id + n_streams - 1 clear of live descriptors.
+ *
+ * n_layers 1 .. SWRT_MAX_LAYERS: each layer's arena gets its own payloads
+ * (at the same offsets); layers either share all of pages, page_count and
+ * page_ids (the descriptors and the table then grow once, and their arenas
+ * must be equally long) or share none of them. d_flags may be NULL.
+ * SWRT_E_INVALID_ARG (nothing launched): a bad format or parameter, seq_len
+ * < 1, first_id outside [0, n_pages - n_streams], a free region outside the
+ * arena or too small for n_streams payloads, n_streams * page_stride > n_ids.
+ * SWRT_E_UNSUPPORTED (library layout rule): head_dim not a multiple of 16 in
+ * [16, 4096], free_begin, kb or vb not a multiple of 16.
  */
 int swrt_paged_append(int n_layers, const swrt_paged_layer *layers, const void *const *k_new,
-                      const void *const *v_new, int new_type, int n_streams, int head_dim,
-                      uint32_t *d_flags, void *stream);
+                      const void *const *v_new, int new_type, int n_streams, int seq_len,
+                      int head_dim, int64_t first_id, int64_t free_begin, int64_t free_end,
+                      int k_format, float k_scale, int32_t k_zero_point, int v_format,
+                      float v_scale, int32_t v_zero_point, uint32_t *d_flags, void *stream);
+
+/*
+ * swrt_paged_append_open -- open-page append, an extension beside the pages'
+ * sealed rule (it rewrites the last block, which a sealed cache never does):
+ * stream s writes k_new[s, :] and v_new[s, :] (new_type F32 / F16 / BF16,
+ * [n_streams, head_dim], 16-byte aligned) as row `length` of its last page,
+ * encoded in that page's formats as swrt_paged_quantize encodes, and that
+ * page's length grows by one (on the device). A stream without pages or
+ * whose last page fails its checks raises SWRT_FLAG_BAD_PAGES, one whose
+ * last page is full SWRT_FLAG_PAGE_FULL; either is skipped. n_layers 1 ..
+ * SWRT_MAX_LAYERS, each with its own arena and either block-table form;
+ * layers either share all of pages, page_ptr / page_count and page_ids (the
+ * lengths grow once) or none. head_dim a multiple of 16 in [16, 4096].
+ */
+int swrt_paged_append_open(int n_layers, const swrt_paged_layer *layers, const void *const *k_new,
+                           const void *const *v_new, int new_type, int n_streams, int head_dim,
+                           uint32_t *d_flags, void *stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *swrt_status_string(int status);

@@ -79,7 +79,7 @@ MODE_LINEAR, MODE_CIRCULAR = 0, 1
 PHASE_STAGE, PHASE_COMMIT, PHASE_ALL = 1, 2, 3
 MAX_LAYERS = 32
 MAX_BATCHED = 64
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 _PHASES = {"stage": PHASE_STAGE, "commit": PHASE_COMMIT, "all": PHASE_ALL}
 _MODES = {"linear": MODE_LINEAR, "circular": MODE_CIRCULAR}
@@ -197,7 +197,10 @@ def lib() -> ctypes.CDLL:
     L.swrt_paged_attention.argtypes = [i32, vp, i64, i32, i32, i32, i32, f32, i32, i32, vp, vp]
     L.swrt_paged_quantize.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, i64, vp, i32, f32,
                                       ctypes.c_int32, i32, f32, ctypes.c_int32, i32, vp, vp]
-    L.swrt_paged_append.argtypes = [i32, vp, vpp, vpp, i32, i32, i32, vp, vp]
+    i32v = ctypes.c_int32
+    L.swrt_paged_append.argtypes = [i32, vp, vpp, vpp, i32, i32, i32, i32, i64, i64, i64, i32,
+                                    f32, i32v, i32, f32, i32v, vp, vp]
+    L.swrt_paged_append_open.argtypes = [i32, vp, vpp, vpp, i32, i32, i32, vp, vp]
     for name in ("swrt_tensor_scatter", "swrt_tensor_scatter_batched", "swrt_kv_seq_lengths",
                  "swrt_kv_seq_lengths_drift",
                  "swrt_kv_window_append", "swrt_kv_window_append_layers",
@@ -205,7 +208,7 @@ def lib() -> ctypes.CDLL:
                  "swrt_kv_window_append_xf", "swrt_kv_window_stage_step_xf",
                  "swrt_tensor_scatter_xf", "swrt_kv_decode_step_xf",
                  "swrt_window_attention", "swrt_paged_attention", "swrt_paged_quantize",
-                 "swrt_paged_append", "swrt_abi_version"):
+                 "swrt_paged_append", "swrt_paged_append_open", "swrt_abi_version"):
         getattr(L, name).restype = ctypes.c_int
     L.swrt_status_string.argtypes = [ctypes.c_int]
     L.swrt_status_string.restype = ctypes.c_char_p
@@ -911,7 +914,8 @@ class PagedLayer(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p), ("out", ctypes.c_void_p), ("arena", ctypes.c_void_p),
                 ("arena_bytes", ctypes.c_int64), ("pages", ctypes.c_void_p),
                 ("n_pages", ctypes.c_int64), ("page_ptr", ctypes.c_void_p),
-                ("page_ids", ctypes.c_void_p), ("n_ids", ctypes.c_int64)]
+                ("page_ids", ctypes.c_void_p), ("n_ids", ctypes.c_int64),
+                ("page_count", ctypes.c_void_p), ("page_stride", ctypes.c_int64)]
 
 
 def page_table(fields: dict) -> np.ndarray:
@@ -927,45 +931,78 @@ def page_table(fields: dict) -> np.ndarray:
 @dataclass
 class PagedCache:
     """One layer's paged cache on the device: ``arena`` (uint8, every page
-    payload), ``pages`` (uint8 [n_pages * 64]: the swrt_page descriptors),
-    ``page_ptr`` (int32 [streams + 1]) and ``page_ids`` (int32): stream s owns
-    page_ids[page_ptr[s]:page_ptr[s + 1]] in token order. Several layers may
-    share pages, page_ptr and page_ids (one block table, one arena each)."""
+    payload), ``pages`` (uint8 [n_pages * 64]: the swrt_page descriptors) and
+    a block table naming each stream's pages in token order through
+    ``page_ids`` (int32), in one of two forms:
+
+    - compressed rows: ``page_ptr`` (int32 [streams + 1]); stream s owns
+      page_ids[page_ptr[s]:page_ptr[s + 1]];
+    - slotted rows: ``page_count`` (int32 [streams]) and ``page_stride``;
+      stream s owns the page_stride slots from s * page_stride and uses the
+      first page_count[s]. The sealed append grows this form.
+
+    Several layers may share pages and the block table (one arena each)."""
     arena: torch.Tensor
     pages: torch.Tensor
-    page_ptr: torch.Tensor
+    page_ptr: torch.Tensor | None
     page_ids: torch.Tensor
+    page_count: torch.Tensor | None = None
+    page_stride: int = 0
 
     @staticmethod
-    def upload(table: np.ndarray, page_ptr, page_ids, arena, device) -> "PagedCache":
+    def upload(table: np.ndarray, page_ptr, page_ids, arena, device, page_count=None,
+               page_stride: int = 0) -> "PagedCache":
         def dev(a, dt):
             return torch.from_numpy(np.ascontiguousarray(a, dtype=dt)).to(device)
         pages = torch.from_numpy(np.ascontiguousarray(table, PAGE_DTYPE).view(np.uint8)).to(device)
         ar = arena if isinstance(arena, torch.Tensor) else dev(arena, np.uint8)
-        return PagedCache(ar, pages, dev(page_ptr, np.int32), dev(page_ids, np.int32))
+        return PagedCache(ar, pages, None if page_ptr is None else dev(page_ptr, np.int32),
+                          dev(page_ids, np.int32),
+                          None if page_count is None else dev(page_count, np.int32), page_stride)
 
     @property
     def n_pages(self) -> int:
         return self.pages.numel() // PAGE_DTYPE.itemsize
+
+    @property
+    def slotted(self) -> bool:
+        return self.page_count is not None
+
+    def n_streams(self) -> int:
+        return self.page_count.numel() if self.slotted else self.page_ptr.numel() - 1
+
+    def tensors(self) -> tuple:
+        """The device tensors of the cache (arena and block table)."""
+        return tuple(t for t in (self.arena, self.pages, self.page_ptr, self.page_ids,
+                                 self.page_count) if t is not None)
 
     def table(self) -> np.ndarray:
         """The descriptors, copied to the host."""
         return self.pages.cpu().numpy().view(PAGE_DTYPE).copy()
 
     def _check(self):
+        if (self.page_ptr is None) == (self.page_count is None):
+            raise SwrtError("a block table is either page_ptr (compressed rows) or page_count "
+                            "(slotted rows)")
         for name, t, dt in (("arena", self.arena, torch.uint8), ("pages", self.pages, torch.uint8),
                             ("page_ptr", self.page_ptr, torch.int32),
-                            ("page_ids", self.page_ids, torch.int32)):
+                            ("page_ids", self.page_ids, torch.int32),
+                            ("page_count", self.page_count, torch.int32)):
+            if t is None:
+                continue
             _contig(name, t)
             if t.dtype != dt or t.dim() != 1:
                 raise SwrtError(f"{name} must be a 1-D {dt} tensor")
         if self.pages.numel() % PAGE_DTYPE.itemsize:
             raise SwrtError("pages must hold whole 64-byte descriptors")
+        if self.slotted and self.page_stride < 1:
+            raise SwrtError("slotted rows need page_stride >= 1")
 
     def layer(self, q=None, out=None) -> PagedLayer:
         return PagedLayer(_ptr(q), _ptr(out), _ptr(self.arena), self.arena.numel(),
                           _ptr(self.pages), self.n_pages, _ptr(self.page_ptr),
-                          _ptr(self.page_ids), self.page_ids.numel())
+                          _ptr(self.page_ids), self.page_ids.numel(), _ptr(self.page_count),
+                          self.page_stride if self.slotted else 0)
 
 
 def prepare_paged_attention(qs: Sequence[torch.Tensor], caches: Sequence[PagedCache],
@@ -992,10 +1029,10 @@ def prepare_paged_attention(qs: Sequence[torch.Tensor], caches: Sequence[PagedCa
         if q.shape != q0.shape or q.dtype != q0.dtype or o.shape != q0.shape or o.dtype != odt:
             raise SwrtError("every query [B, Hq, D] of one dtype, every output of another")
         c._check()
-        if c.page_ptr.numel() != B * kv_heads + 1:
-            raise SwrtError("page_ptr must hold batch * kv_heads + 1 entries")
-    dev = _device_of(*qs, *outs, *(t for c in caches for t in (c.arena, c.pages, c.page_ptr,
-                                                                c.page_ids)), flags)
+        if c.n_streams() != B * kv_heads:
+            raise SwrtError("the block table must hold batch * kv_heads streams")
+    _flags_ptr(flags)
+    dev = _device_of(*qs, *outs, *(t for c in caches for t in c.tensors()), flags)
     layers = (PagedLayer * n)(*[c.layer(q, o) for c, q, o in zip(caches, qs, outs)])
     sc = D ** -0.5 if scale is None else float(scale)
     args = (n, ctypes.cast(layers, ctypes.c_void_p), int(left_window), B, Hq, kv_heads, D, sc,
@@ -1048,9 +1085,57 @@ def paged_quantize(cache: PagedCache, blocks: torch.Tensor, dst_offsets: torch.T
 
 
 def prepare_paged_append(caches: Sequence[PagedCache], k_news: Sequence[torch.Tensor],
-                         v_news: Sequence[torch.Tensor], *,
+                         v_news: Sequence[torch.Tensor], *, first_id: int, free_begin: int,
+                         free_end: int, k_format: int, v_format: int, k_scale: float = 1.0,
+                         k_zero_point: int = 0, v_scale: float = 1.0, v_zero_point: int = 0,
                          flags: torch.Tensor | None = None) -> PreparedCall:
     """See ``paged_append``."""
+    n = len(caches)
+    if len(k_news) != n or len(v_news) != n or not 1 <= n <= MAX_LAYERS:
+        raise SwrtError(f"need 1..{MAX_LAYERS} layers with a cache and new K and V rows each")
+    k0 = k_news[0]
+    if k0.dim() != 3 or k0.dtype not in _Q_TYPES:
+        raise SwrtError("new rows must be [streams, S, D] float32, float16 or bfloat16")
+    NS, S, D = k0.shape
+    for c, k, v in zip(caches, k_news, v_news):
+        c._check()
+        if not c.slotted:
+            raise SwrtError("the sealed append grows slotted block tables (page_count)")
+        _contig("k_new", k)
+        _contig("v_new", v)
+        if k.shape != k0.shape or v.shape != k0.shape or k.dtype != k0.dtype or v.dtype != k0.dtype:
+            raise SwrtError("every new row tensor [streams, S, D] of one dtype")
+        if c.n_streams() != NS:
+            raise SwrtError("page_count must hold one entry per stream")
+    _flags_ptr(flags)
+    dev = _device_of(*k_news, *v_news, *(t for c in caches for t in c.tensors()), flags)
+    layers = (PagedLayer * n)(*[c.layer() for c in caches])
+    args = (n, ctypes.cast(layers, ctypes.c_void_p), _ptrs(k_news), _ptrs(v_news),
+            _Q_TYPES[k0.dtype], NS, S, D, int(first_id), int(free_begin), int(free_end),
+            int(k_format), float(k_scale), int(k_zero_point), int(v_format), float(v_scale),
+            int(v_zero_point), _flags_ptr(flags))
+    keep = (layers, *caches, *k_news, *v_news, flags)
+    return PreparedCall(lib().swrt_paged_append, args, dev, "paged_append", keep)
+
+
+def paged_append(caches, k_news, v_news, *, first_id: int, free_begin: int, free_end: int,
+                 k_format: int, v_format: int, k_scale: float = 1.0, k_zero_point: int = 0,
+                 v_scale: float = 1.0, v_zero_point: int = 0, flags=None) -> None:
+    """Sealed-block append: each stream's new K and V rows ([streams, S, D])
+    become one new block of S tokens, descriptor ``first_id + s``, payload in
+    the arena's free region from ``free_begin`` (K then V, stream after
+    stream), formats and scalar parameters as given; the stream's next slot
+    of the (slotted) block table names it. Earlier blocks are never written."""
+    prepare_paged_append(caches, k_news, v_news, first_id=first_id, free_begin=free_begin,
+                         free_end=free_end, k_format=k_format, v_format=v_format,
+                         k_scale=k_scale, k_zero_point=k_zero_point, v_scale=v_scale,
+                         v_zero_point=v_zero_point, flags=flags)()
+
+
+def prepare_paged_append_open(caches: Sequence[PagedCache], k_news: Sequence[torch.Tensor],
+                              v_news: Sequence[torch.Tensor], *,
+                              flags: torch.Tensor | None = None) -> PreparedCall:
+    """See ``paged_append_open``."""
     n = len(caches)
     if len(k_news) != n or len(v_news) != n or not 1 <= n <= MAX_LAYERS:
         raise SwrtError(f"need 1..{MAX_LAYERS} layers with a cache and new K and V rows each")
@@ -1064,19 +1149,19 @@ def prepare_paged_append(caches: Sequence[PagedCache], k_news: Sequence[torch.Te
         _contig("v_new", v)
         if k.shape != k0.shape or v.shape != k0.shape or k.dtype != k0.dtype or v.dtype != k0.dtype:
             raise SwrtError("every new row tensor [streams, D] of one dtype")
-        if c.page_ptr.numel() != S + 1:
-            raise SwrtError("page_ptr must hold streams + 1 entries")
-    dev = _device_of(*k_news, *v_news, *(t for c in caches for t in (c.arena, c.pages, c.page_ptr,
-                                                                     c.page_ids)), flags)
+        if c.n_streams() != S:
+            raise SwrtError("the block table must hold one stream per new row")
+    _flags_ptr(flags)
+    dev = _device_of(*k_news, *v_news, *(t for c in caches for t in c.tensors()), flags)
     layers = (PagedLayer * n)(*[c.layer() for c in caches])
     args = (n, ctypes.cast(layers, ctypes.c_void_p), _ptrs(k_news), _ptrs(v_news),
             _Q_TYPES[k0.dtype], S, D, _flags_ptr(flags))
     keep = (layers, *caches, *k_news, *v_news, flags)
-    return PreparedCall(lib().swrt_paged_append, args, dev, "paged_append", keep)
+    return PreparedCall(lib().swrt_paged_append_open, args, dev, "paged_append_open", keep)
 
 
-def paged_append(caches, k_news, v_news, *, flags=None) -> None:
-    """Each stream's new K and V rows ([streams, D]) into its last page,
-    encoded in the page's formats; the page grows by one row (once per
-    distinct block table)."""
-    prepare_paged_append(caches, k_news, v_news, flags=flags)()
+def paged_append_open(caches, k_news, v_news, *, flags=None) -> None:
+    """The open-page extension: each stream's new K and V rows ([streams, D])
+    into its last page, encoded in the page's formats; the page grows by one
+    row (once per distinct block table)."""
+    prepare_paged_append_open(caches, k_news, v_news, flags=flags)()

@@ -22,10 +22,14 @@
 //                           the device first, then the payloads, then the
 //                           descriptors, each later kernel stopping when the
 //                           first raised the flag.
+//   paged_append_sealed     one wave per (block table, stream): the stream's
+//                           new tokens as one new block (the pages' sealed
+//                           rule), every layer's payload encoded, then the
+//                           block's descriptor and the table slot.
 //   paged_append_rows / paged_append_commit
-//                           one wave per (layer, stream): the new token's rows
-//                           into its last page, encoded; then, once per
-//                           distinct block table, the page's length + 1.
+//                           the open-page extension: one wave per (layer,
+//                           stream) writes the new token into the last page,
+//                           then, once per distinct table, its length + 1.
 #include "swrt_host.hpp"
 #include "att_device.hpp"
 
@@ -34,6 +38,8 @@ namespace {
 
 constexpr int kPgBlock = 256;  // 4 waves, one stream each
 constexpr int kPgWaves = kPgBlock / 64;
+
+static_assert(sizeof(swrt_paged_layer) == 88, "swrt_paged_layer layout");
 
 struct PgLayer {
   const char *q;
@@ -45,6 +51,8 @@ struct PgLayer {
   const int32_t *page_ptr;
   const int32_t *page_ids;
   int64_t n_ids;
+  int32_t *page_count;  // slotted rows (null: compressed rows through page_ptr)
+  int64_t page_stride;
 };
 
 // ---------------------------------------------------------------------------
@@ -106,6 +114,24 @@ __device__ __forceinline__ bool pg_page_ok(const swrt_page &p, int D, int64_t ar
 // a descriptor read whole with uniform (scalar) loads
 __device__ __forceinline__ swrt_page pg_read(const swrt_page *pages, int32_t id) {
   return pages[__builtin_amdgcn_readfirstlane(id)];
+}
+
+// Stream s's slots of the block table, [p0, p1) of page_ids: compressed rows
+// page_ptr[s] .. page_ptr[s + 1], or slotted rows s * page_stride +
+// [0, page_count[s]). False when the range does not lie inside page_ids.
+// UNIFORM: s is the same in every lane, the loads are scalar.
+template <bool UNIFORM = true>
+__device__ __forceinline__ bool pg_stream_range(const PgLayer &P, int64_t s, int64_t &p0, int64_t &p1) {
+  auto u = [](int32_t v) { return UNIFORM ? __builtin_amdgcn_readfirstlane(v) : v; };
+  if (P.page_count) {
+    const int64_t n = u(P.page_count[s]);
+    p0 = s * P.page_stride;
+    p1 = p0 + n;
+    return n >= 0 && n <= P.page_stride && P.page_stride <= P.n_ids - p0;
+  }
+  p0 = u(P.page_ptr[s]);
+  p1 = u(P.page_ptr[s + 1]);
+  return p0 >= 0 && p0 <= p1 && p1 <= P.n_ids;
 }
 
 // Payload addresses computed as integers are turned back into pointers to
@@ -544,9 +570,8 @@ __global__ __launch_bounds__(kPgBlock) void paged_attention_kernel(PgAttArgs a) 
 #pragma unroll
   for (int i = 0; i < MT; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  const int64_t ptr0 = __builtin_amdgcn_readfirstlane(P.page_ptr[s]);
-  const int64_t ptr1 = __builtin_amdgcn_readfirstlane(P.page_ptr[s + 1]);
-  bool ok = ptr0 >= 0 && ptr0 <= ptr1 && ptr1 <= P.n_ids;
+  int64_t ptr0, ptr1;
+  bool ok = pg_stream_range(P, s, ptr0, ptr1);
   if (ok && ptr1 > ptr0) {
     // Pages are taken 64 at a time from the last one back: lane l reads the
     // whole descriptor of page top - l (ids, then descriptors, one load each
@@ -996,9 +1021,8 @@ struct PgAppArgs {
 // the page stream s's token goes to, and whether it can take it
 __device__ __forceinline__ uint32_t pg_append_target(const PgLayer &P, int64_t s, int D, int32_t &id,
                                                      swrt_page &p) {
-  const int64_t ptr0 = __builtin_amdgcn_readfirstlane(P.page_ptr[s]);
-  const int64_t ptr1 = __builtin_amdgcn_readfirstlane(P.page_ptr[s + 1]);
-  if (ptr0 < 0 || ptr1 <= ptr0 || ptr1 > P.n_ids) return SWRT_FLAG_BAD_PAGES;
+  int64_t ptr0, ptr1;
+  if (!pg_stream_range(P, s, ptr0, ptr1) || ptr1 == ptr0) return SWRT_FLAG_BAD_PAGES;
   id = __builtin_amdgcn_readfirstlane(P.page_ids[ptr1 - 1]);
   if (id < 0 || id >= P.n_pages) return SWRT_FLAG_BAD_PAGES;
   p = pg_read(P.pages, id);
@@ -1045,12 +1069,106 @@ __global__ __launch_bounds__(kPgBlock) void paged_append_commit_kernel(PgAppArgs
   if (x >= int64_t(a.n_tables) * a.n_streams) return;
   const PgLayer &P = a.L[a.table[x / a.n_streams]];
   const int64_t s = x % a.n_streams;
-  const int64_t ptr0 = P.page_ptr[s], ptr1 = P.page_ptr[s + 1];
-  if (ptr0 < 0 || ptr1 <= ptr0 || ptr1 > P.n_ids) return;
+  int64_t ptr0, ptr1;
+  if (!pg_stream_range<false>(P, s, ptr0, ptr1) || ptr1 == ptr0) return;
   const int32_t id = P.page_ids[ptr1 - 1];
   if (id < 0 || id >= P.n_pages) return;
   swrt_page *pg = const_cast<swrt_page *>(P.pages) + id;
   if (pg_page_ok(*pg, a.D, P.arena_bytes) && pg->length < pg->capacity) pg->length += 1;
+}
+
+// ---------------------------------------------------------------------------
+// sealed append: one new block per stream
+// ---------------------------------------------------------------------------
+struct PgSealArgs {
+  PgLayer L[kMaxLayers];
+  const char *k_new[kMaxLayers];
+  const char *v_new[kMaxLayers];
+  int8_t order[kMaxLayers];          // layers, each table's consecutive
+  int8_t group_begin[kMaxLayers + 1];
+  uint32_t *flags;
+  int64_t first_id, free_begin, kb, vb;
+  int32_t fmt[2];
+  float scale[2];  // 1 for a dense format
+  int32_t zp[2];   // 0 for a dense format
+  int32_t n_groups, n_streams, S, D, new_type, items;
+};
+
+// One wave per (block table, stream): check the stream's last block (the
+// only descriptor read), encode the S new rows of every layer sharing the
+// table into the stream's room of the free region, then write the new
+// block's descriptor and take the stream's next slot. Streams touch
+// disjoint slots, descriptors and payload room, and no wave writes a
+// descriptor another reads (the last block's id may not be a new one), so
+// the waves need no ordering among themselves.
+__global__ __launch_bounds__(kPgBlock) void paged_append_sealed_kernel(PgSealArgs a) {
+  const uint32_t lane = threadIdx.x % 64, wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+  const uint32_t item = blockIdx.x * kPgWaves + wave;
+  if (item >= uint32_t(a.items)) return;
+  const int64_t s = item % uint32_t(a.n_streams);
+  const int grp = int(item / uint32_t(a.n_streams));
+  const PgLayer &T0 = a.L[a.order[a.group_begin[grp]]];  // the table's fields
+  int64_t p0, p1;
+  uint32_t bad = 0;
+  int64_t T = 0;
+  if (!pg_stream_range(T0, s, p0, p1)) {
+    bad = SWRT_FLAG_BAD_PAGES;
+  } else if (p1 == p0 + T0.page_stride) {
+    bad = SWRT_FLAG_PAGE_FULL;  // no free slot for the new block
+  } else if (p1 > p0) {
+    const int32_t last = __builtin_amdgcn_readfirstlane(T0.page_ids[p1 - 1]);
+    if (last < 0 || last >= T0.n_pages || (last >= a.first_id && last < a.first_id + a.n_streams)) {
+      bad = SWRT_FLAG_BAD_PAGES;
+    } else {
+      const swrt_page d = pg_read(T0.pages, last);
+      if (!pg_page_ok(d, a.D, T0.arena_bytes) || d.start + d.length > INT64_MAX - a.S)
+        bad = SWRT_FLAG_BAD_PAGES;
+      else
+        T = d.start + d.length;
+    }
+  }
+  if (bad) {
+    if (a.flags && lane == 0) atomicOr(a.flags, bad);
+    return;
+  }
+  const int64_t koff = a.free_begin + s * (a.kb + a.vb), voff = koff + a.kb;
+  const int nes = a.new_type == SWRT_XF_F32 ? 4 : 2;
+  const int32_t per_row = a.D / 8;
+  const int64_t n8 = int64_t(a.S) * per_row;  // eight-element groups per tensor
+  for (int i = a.group_begin[grp]; i < a.group_begin[grp + 1]; ++i) {
+    const int layer = a.order[i];
+    char *arena = const_cast<char *>(a.L[layer].arena);
+    for (int t = 0; t < 2; ++t) {
+      const int fmt = a.fmt[t];
+      const char *in = (t ? a.v_new[layer] : a.k_new[layer]) + s * int64_t(a.S) * a.D * nes;
+      char *dst = arena + (t ? voff : koff);
+      for (int64_t o = lane; o < n8; o += 64) {
+        const int64_t r = o / per_row;
+        const uint32_t e0 = uint32_t(o - r * per_row) * 8;
+        float y[8];
+        pg_load_decode<8>(a.new_type, in + r * a.D * nes, e0, 0, y);
+        pg_store8(fmt, dst + (r * a.D + e0) * pg_bits(fmt) / 8, y, a.scale[t], a.zp[t]);
+      }
+    }
+  }
+  if (lane == 0) {
+    const int64_t id = a.first_id + s;
+    swrt_page np = {};
+    np.start = T;
+    np.length = a.S;
+    np.capacity = a.S;
+    np.k_offset = koff;
+    np.v_offset = voff;
+    np.k_format = a.fmt[0];
+    np.v_format = a.fmt[1];
+    np.k_scale = a.scale[0];
+    np.v_scale = a.scale[1];
+    np.k_zero_point = a.zp[0];
+    np.v_zero_point = a.zp[1];
+    const_cast<swrt_page *>(T0.pages)[id] = np;
+    const_cast<int32_t *>(T0.page_ids)[p1] = int32_t(id);
+    T0.page_count[s] = int32_t(p1 - p0 + 1);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1063,19 +1181,49 @@ int pg_layers(int n_layers, const swrt_paged_layer *layers, PgLayer *out, bool a
               int64_t n_streams) {
   for (int l = 0; l < n_layers; ++l) {
     const swrt_paged_layer &x = layers[l];
-    if (!x.arena || !x.pages || !x.page_ptr || (x.n_ids > 0 && !x.page_ids)) return SWRT_E_INVALID_ARG;
+    if (!x.arena || !x.pages || (!x.page_ptr && !x.page_count) || (x.n_ids > 0 && !x.page_ids))
+      return SWRT_E_INVALID_ARG;
     if (x.arena_bytes < 0 || x.arena_bytes % 16 || x.n_pages < 0 || x.n_ids < 0 ||
-        x.n_pages > INT32_MAX)
+        x.n_pages > INT32_MAX || (x.page_count && x.page_stride < 1))
       return SWRT_E_INVALID_ARG;
     if (addr_of(x.arena) % 16 || addr_of(x.pages) % 8 || addr_of(x.page_ptr) % 4 ||
-        addr_of(x.page_ids) % 4)
+        addr_of(x.page_ids) % 4 || addr_of(x.page_count) % 4)
       return SWRT_E_INVALID_ARG;
     if (attention && (!x.q || !x.out || addr_of(x.q) % 16 || addr_of(x.out) % 16))
       return SWRT_E_INVALID_ARG;
     out[l] = PgLayer{static_cast<const char *>(x.q), static_cast<char *>(x.out),
                      static_cast<const char *>(x.arena), x.arena_bytes, x.pages, x.n_pages,
-                     x.page_ptr, x.page_ids, x.n_ids};
+                     x.page_count ? nullptr : x.page_ptr, x.page_ids, x.n_ids, x.page_count,
+                     x.page_count ? x.page_stride : 0};
     (void)n_streams;
+  }
+  return SWRT_OK;
+}
+
+// the block table's read range of a layer: page_ptr (compressed rows) or
+// page_count (slotted rows)
+Range pg_table_range(const swrt_paged_layer &x, int64_t n_streams, bool written) {
+  return x.page_count ? range(x.page_count, uint64_t(n_streams) * 4, written)
+                      : range(x.page_ptr, uint64_t(n_streams + 1) * 4, written);
+}
+
+// Layers that share a block table: either all of pages, the table form and
+// page_ids, or none of them. group[l] = the first layer with l's table.
+int pg_groups(int n_layers, const swrt_paged_layer *layers, int32_t *group) {
+  for (int l = 0; l < n_layers; ++l) {
+    group[l] = l;
+    const swrt_paged_layer &y = layers[l];
+    for (int e = 0; e < l; ++e) {
+      const swrt_paged_layer &x = layers[e];
+      const int same = int(x.pages == y.pages) + int(x.page_ids == y.page_ids) +
+                       int(x.page_ptr == y.page_ptr && x.page_count == y.page_count);
+      if (same == 0) continue;
+      if (same != 3 || x.n_pages != y.n_pages || x.n_ids != y.n_ids ||
+          x.page_stride != y.page_stride)
+        return SWRT_E_INVALID_ARG;  // partly shared
+      group[l] = group[e];
+      break;
+    }
   }
   return SWRT_OK;
 }
@@ -1114,7 +1262,7 @@ extern "C" int swrt_paged_attention(int n_layers, const swrt_paged_layer *layers
     ranges[nr++] = range(x.out, uint64_t(rows * oes), true);
     ranges[nr++] = range(x.arena, uint64_t(x.arena_bytes), false);
     ranges[nr++] = range(x.pages, uint64_t(x.n_pages) * sizeof(swrt_page), false);
-    ranges[nr++] = range(x.page_ptr, uint64_t(int64_t(batch) * kv_heads + 1) * 4, false);
+    ranges[nr++] = pg_table_range(x, int64_t(batch) * kv_heads, false);
     ranges[nr++] = range(x.page_ids, uint64_t(x.n_ids) * 4, false);
   }
   ranges[nr++] = range(d_flags, 4, true);
@@ -1222,9 +1370,10 @@ extern "C" int swrt_paged_quantize(void *arena, int64_t arena_bytes, const swrt_
   return launch_status();
 }
 
-extern "C" int swrt_paged_append(int n_layers, const swrt_paged_layer *layers,
-                                 const void *const *k_new, const void *const *v_new, int new_type,
-                                 int n_streams, int head_dim, uint32_t *d_flags, void *stream) {
+extern "C" int swrt_paged_append_open(int n_layers, const swrt_paged_layer *layers,
+                                      const void *const *k_new, const void *const *v_new,
+                                      int new_type, int n_streams, int head_dim, uint32_t *d_flags,
+                                      void *stream) {
   if (n_layers < 0 || n_layers > kMaxLayers || n_streams < 0 || !pg_q_type_ok(new_type))
     return SWRT_E_INVALID_ARG;
   if (head_dim < 16 || head_dim % 16 || head_dim > 4096) return SWRT_E_INVALID_ARG;
@@ -1232,24 +1381,14 @@ extern "C" int swrt_paged_append(int n_layers, const swrt_paged_layer *layers,
   if (!layers || !k_new || !v_new || addr_of(d_flags) % 4) return SWRT_E_INVALID_ARG;
   if (uint64_t(n_layers) * n_streams >= (uint64_t(1) << 31)) return SWRT_E_UNSUPPORTED;
   PgAppArgs a;
-  const int st = pg_layers(n_layers, layers, a.L, false, n_streams);
+  int st = pg_layers(n_layers, layers, a.L, false, n_streams);
   if (st != SWRT_OK) return st;
-  // block tables: a layer either has its own (descriptors, page_ptr and
-  // page_ids apart from every other layer's) or shares all three with an
-  // earlier layer; the lengths of each distinct table grow once
+  // the lengths of each distinct block table grow once
+  int32_t group[kMaxLayers];
+  if ((st = pg_groups(n_layers, layers, group)) != SWRT_OK) return st;
   a.n_tables = 0;
-  for (int l = 0; l < n_layers; ++l) {
-    int same = -1;
-    for (int e = 0; e < l; ++e) {
-      const swrt_paged_layer &x = layers[e], &y = layers[l];
-      if (x.pages == y.pages && x.page_ptr == y.page_ptr && x.page_ids == y.page_ids &&
-          x.n_pages == y.n_pages && x.n_ids == y.n_ids) {
-        same = e;
-        break;
-      }
-    }
-    if (same < 0) a.table[a.n_tables++] = l;
-  }
+  for (int l = 0; l < n_layers; ++l)
+    if (group[l] == l) a.table[a.n_tables++] = l;
   const int64_t nes = new_type == SWRT_XF_F32 ? 4 : 2;
   Range ranges[7 * kMaxLayers + 1];
   int nr = 0;
@@ -1266,7 +1405,7 @@ extern "C" int swrt_paged_append(int n_layers, const swrt_paged_layer *layers,
   for (int t = 0; t < a.n_tables; ++t) {  // each distinct table once
     const swrt_paged_layer &x = layers[a.table[t]];
     ranges[nr++] = range(x.pages, uint64_t(x.n_pages) * sizeof(swrt_page), true);
-    ranges[nr++] = range(x.page_ptr, uint64_t(n_streams + 1) * 4, false);
+    ranges[nr++] = pg_table_range(x, n_streams, false);
     ranges[nr++] = range(x.page_ids, uint64_t(x.n_ids) * 4, false);
   }
   ranges[nr++] = range(d_flags, 4, true);
@@ -1285,5 +1424,100 @@ extern "C" int swrt_paged_append(int n_layers, const swrt_paged_layer *layers,
   const int64_t nc = int64_t(a.n_tables) * n_streams;
   hipLaunchKernelGGL(paged_append_commit_kernel, dim3(uint32_t((nc + kPgBlock - 1) / kPgBlock)),
                      dim3(kPgBlock), 0, s, a);
+  return launch_status();
+}
+
+extern "C" int swrt_paged_append(int n_layers, const swrt_paged_layer *layers,
+                                 const void *const *k_new, const void *const *v_new, int new_type,
+                                 int n_streams, int seq_len, int head_dim, int64_t first_id,
+                                 int64_t free_begin, int64_t free_end, int k_format, float k_scale,
+                                 int32_t k_zero_point, int v_format, float v_scale,
+                                 int32_t v_zero_point, uint32_t *d_flags, void *stream) {
+  // what the definition itself rejects
+  if (n_layers < 0 || n_layers > kMaxLayers || n_streams < 0 || seq_len < 1 ||
+      !pg_q_type_ok(new_type) || head_dim < 1)
+    return SWRT_E_INVALID_ARG;
+  if (!pg_format_ok(k_format, k_scale, k_zero_point) || !pg_format_ok(v_format, v_scale, v_zero_point))
+    return SWRT_E_INVALID_ARG;
+  // the library's layout rule: 16-byte blocks of payload
+  if (head_dim < 16 || head_dim % 16 || head_dim > 4096) return SWRT_E_UNSUPPORTED;
+  const int64_t kb = int64_t(seq_len) * head_dim * pg_bits(k_format) / 8;
+  const int64_t vb = int64_t(seq_len) * head_dim * pg_bits(v_format) / 8;
+  if (n_layers == 0) return SWRT_OK;
+  if (!layers || addr_of(d_flags) % 4) return SWRT_E_INVALID_ARG;
+  for (int l = 0; l < n_layers; ++l) {
+    const swrt_paged_layer &x = layers[l];
+    if (!x.page_count || x.page_stride < 1) return SWRT_E_INVALID_ARG;  // slotted rows only
+    if (first_id < 0 || first_id > x.n_pages - n_streams) return SWRT_E_INVALID_ARG;
+    if (free_begin < 0 || free_end < free_begin || free_end > x.arena_bytes ||
+        (n_streams > 0 && kb + vb > (free_end - free_begin) / n_streams))
+      return SWRT_E_INVALID_ARG;
+    if (n_streams > x.n_ids / x.page_stride) return SWRT_E_INVALID_ARG;
+  }
+  if (free_begin % 16 || kb % 16 || vb % 16) return SWRT_E_UNSUPPORTED;
+  if (n_streams == 0) return SWRT_OK;
+  if (!k_new || !v_new) return SWRT_E_INVALID_ARG;
+  if (uint64_t(n_layers) * n_streams >= (uint64_t(1) << 31) ||
+      uint64_t(seq_len) * head_dim >= (uint64_t(1) << 31))
+    return SWRT_E_UNSUPPORTED;
+  PgSealArgs a;
+  int st = pg_layers(n_layers, layers, a.L, false, n_streams);
+  if (st != SWRT_OK) return st;
+  int32_t group[kMaxLayers];
+  if ((st = pg_groups(n_layers, layers, group)) != SWRT_OK) return st;
+  // layers ordered so that each table's layers are consecutive
+  a.n_groups = 0;
+  int n = 0;
+  for (int l = 0; l < n_layers; ++l) {
+    if (group[l] != l) continue;
+    a.group_begin[a.n_groups++] = n;
+    for (int e = l; e < n_layers; ++e)
+      if (group[e] == l) {
+        if (layers[e].arena_bytes != layers[l].arena_bytes) return SWRT_E_INVALID_ARG;
+        a.order[n++] = e;
+      }
+  }
+  a.group_begin[a.n_groups] = n;
+  const int64_t nes = new_type == SWRT_XF_F32 ? 4 : 2;
+  const uint64_t new_bytes = uint64_t(n_streams) * seq_len * head_dim * nes;
+  Range ranges[7 * kMaxLayers + 1];
+  int nr = 0;
+  for (int l = 0; l < n_layers; ++l) {
+    const swrt_paged_layer &x = layers[l];
+    if (!k_new[l] || !v_new[l] || addr_of(k_new[l]) % 16 || addr_of(v_new[l]) % 16)
+      return SWRT_E_INVALID_ARG;
+    a.k_new[l] = static_cast<const char *>(k_new[l]);
+    a.v_new[l] = static_cast<const char *>(v_new[l]);
+    ranges[nr++] = range(x.arena, uint64_t(x.arena_bytes), true);
+    ranges[nr++] = range(k_new[l], new_bytes, false);
+    ranges[nr++] = range(v_new[l], new_bytes, false);
+  }
+  for (int g = 0; g < a.n_groups; ++g) {  // each distinct table once
+    const swrt_paged_layer &x = layers[a.order[a.group_begin[g]]];
+    ranges[nr++] = range(x.pages, uint64_t(x.n_pages) * sizeof(swrt_page), true);
+    ranges[nr++] = range(x.page_count, uint64_t(n_streams) * 4, true);
+    ranges[nr++] = range(x.page_ids, uint64_t(x.n_ids) * 4, true);
+  }
+  ranges[nr++] = range(d_flags, 4, true);
+  if (written_overlap(ranges, nr)) return SWRT_E_INVALID_ARG;
+  a.flags = d_flags;
+  a.n_streams = n_streams;
+  a.S = seq_len;
+  a.D = head_dim;
+  a.new_type = new_type;
+  a.first_id = first_id;
+  a.free_begin = free_begin;
+  a.kb = kb;
+  a.vb = vb;
+  a.fmt[0] = k_format;
+  a.fmt[1] = v_format;
+  a.scale[0] = pg_affine(k_format) ? k_scale : 1.0f;
+  a.scale[1] = pg_affine(v_format) ? v_scale : 1.0f;
+  a.zp[0] = pg_affine(k_format) ? k_zero_point : 0;
+  a.zp[1] = pg_affine(v_format) ? v_zero_point : 0;
+  a.items = a.n_groups * n_streams;
+  static_assert(sizeof(PgSealArgs) <= 4096, "kernel arguments exceed 4 KiB");
+  hipLaunchKernelGGL(paged_append_sealed_kernel, dim3((uint32_t(a.items) + kPgWaves - 1) / kPgWaves),
+                     dim3(kPgBlock), 0, static_cast<hipStream_t>(stream), a);
   return launch_status();
 }

@@ -4,9 +4,9 @@ input/output feedback", section "Optional heterogeneous paged KV").
 Every layer keeps its K/V pages in its own arena; one block table (page
 descriptors, page_ptr, page_ids) serves all layers. A step is
 
-  1. paged_append      each stream's new K and V rows into its last page
-                       (optional: the benchmark times attention over a fixed
-                       cache, since appends fill pages);
+  1. paged_append      each stream's new K and V rows as a new sealed block
+                       (on a slotted copy of the table; the benchmark times
+                       attention over a fixed cache, since appends grow it);
   2. paged_attention   every layer's 64 query heads over the visible tokens
                        of their KV head's stream, pages decoded in their own
                        formats (cold pages int8, the last two bf16), one

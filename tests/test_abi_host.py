@@ -50,7 +50,7 @@ def test_exports_every_declared_function(L):
             "swrt_kv_window_append_layers", "swrt_kv_decode_step", "swrt_kv_seq_lengths_drift",
             "swrt_kv_window_append_xf", "swrt_tensor_scatter_xf", "swrt_kv_decode_step_xf",
             "swrt_window_attention", "swrt_paged_attention", "swrt_paged_quantize",
-            "swrt_paged_append", "swrt_status_string",
+            "swrt_paged_append", "swrt_paged_append_open", "swrt_status_string",
             "swrt_abi_version"} <= declared
     out = subprocess.run(["nm", "-D", "--defined-only", swrt.LIBRARY], check=True,
                          capture_output=True, text=True).stdout
@@ -96,7 +96,7 @@ def test_constants_agree():
         == {k: swrt.PAGE_FORMATS[k] for k in ("int4", "uint4", "int2", "uint2")}
     assert (oracle.FLAG_BAD_PAGES, oracle.FLAG_PAGE_FULL) == (swrt.FLAG_BAD_PAGES, swrt.FLAG_PAGE_FULL)
     assert oracle.PAGE_DTYPE == swrt.PAGE_DTYPE and swrt.PAGE_DTYPE.itemsize == 64
-    assert ctypes.sizeof(swrt.PagedLayer) == 72
+    assert ctypes.sizeof(swrt.PagedLayer) == 88
     assert (oracle.MODE_LINEAR, oracle.MODE_CIRCULAR) == (swrt.MODE_LINEAR, swrt.MODE_CIRCULAR)
     assert (oracle.PHASE_STAGE, oracle.PHASE_COMMIT, oracle.PHASE_ALL) == \
         (swrt.PHASE_STAGE, swrt.PHASE_COMMIT, swrt.PHASE_ALL)
@@ -457,7 +457,8 @@ def test_paged_rejects(L):
 
     def layer(**kw):
         f = dict(q=A, out=D_, arena=B_, arena_bytes=4096, pages=C_, n_pages=4,
-                 page_ptr=C_ + 0x1000, page_ids=C_ + 0x2000, n_ids=4)
+                 page_ptr=C_ + 0x1000, page_ids=C_ + 0x2000, n_ids=4, page_count=None,
+                 page_stride=0)
         f.update(kw)
         return swrt.PagedLayer(*[f[n] for n, _ in swrt.PagedLayer._fields_])
 
@@ -493,8 +494,8 @@ def test_paged_rejects(L):
         arr = (swrt.PagedLayer * n)(*([layer()] * n if layers is None else layers))
         kn = (ctypes.c_void_p * n)(*[D_ + 0x200000 * (i + 1) for i in range(n)])
         vn = (ctypes.c_void_p * n)(*[D_ + 0x200000 * (i + 1) + 0x100000 for i in range(n)])
-        return L.swrt_paged_append(n, ctypes.cast(arr, ctypes.c_void_p), kn, vn, nt, S, D,
-                                   None, None)
+        return L.swrt_paged_append_open(n, ctypes.cast(arr, ctypes.c_void_p), kn, vn, nt, S, D,
+                                        None, None)
     assert app() in launched
     three = [layer(arena=B_ + 0x10000 * i) for i in range(3)]
     assert app(layers=three, n=3) in launched               # three arenas, one block table
@@ -502,3 +503,37 @@ def test_paged_rejects(L):
     assert app(layers=[three[0], layer(arena=B_ + 0x20000, page_ids=C_ + 0x5000)], n=2) == INV
     assert app(D=40) == INV and app(nt=4) == INV and app(n=33) == INV
     assert app(layers=[layer(arena_bytes=4104)]) == INV
+    # slotted rows: page_count with a stride (page_ptr unused)
+    slot = dict(page_ptr=None, page_count=C_ + 0x1000, page_stride=2, n_ids=16)
+    assert att(layers=[layer(**slot)]) in launched
+    assert att(layers=[layer(**{**slot, "page_stride": 0})]) == INV
+    assert att(layers=[layer(page_ptr=None)]) == INV           # no table at all
+
+    def seal(layers=None, n=1, NS=8, S=1, D=64, nt=3, first=8, fb=1024, fe=4096, kf=3, ks=1.0,
+             kz=0, vf=4, vs=0.1, vz=0):
+        arr = (swrt.PagedLayer * n)(*([layer(**sl)] * n if layers is None else layers))
+        kn = (ctypes.c_void_p * n)(*[D_ + 0x200000 * (i + 1) for i in range(n)])
+        vn = (ctypes.c_void_p * n)(*[D_ + 0x200000 * (i + 1) + 0x100000 for i in range(n)])
+        return L.swrt_paged_append(n, ctypes.cast(arr, ctypes.c_void_p), kn, vn, nt, NS, S, D,
+                                   first, fb, fe, kf, ks, kz, vf, vs, vz, None, None)
+    sl = dict(page_ptr=None, page_count=C_ + 0x1000, page_stride=2, n_ids=16, n_pages=16)
+    assert seal() in launched
+    assert seal(first=9) == INV and seal(first=-1) == INV    # new ids past the descriptors
+    assert seal(fe=1024 + 8 * 192 - 16) == INV                # room for seven streams only
+    assert seal(fb=5000, fe=5000) == INV                      # free region past the arena
+    assert seal(NS=9, first=0) == INV                         # slots past page_ids
+    assert seal(S=0) == INV and seal(nt=4) == INV and seal(kf=10) == INV and seal(vs=0.0) == INV
+    assert seal(vz=128) == INV                                # int8 zero point
+    assert seal(layers=[layer(**{**sl, "page_count": None, "page_ptr": C_ + 0x1000})]) == INV
+    assert seal(D=40) == UNS and seal(D=8) == UNS             # head_dim: 16-byte blocks
+    assert seal(fb=1032) == UNS                               # free region not 16-byte aligned
+    assert seal(D=32, vf=8) == UNS                            # int2 rows of 8 bytes
+    assert seal(D=32, vf=8, S=2) in launched                  # two of them: 16 bytes
+    three = [layer(**{**sl, "arena": B_ + 0x10000 * i}) for i in range(3)]
+    assert seal(layers=three, n=3) in launched                # three arenas, one block table
+    assert seal(n=3) == INV                                   # one arena written by three layers
+    part = layer(**{**sl, "arena": B_ + 0x20000, "page_ids": C_ + 0x5000})
+    assert seal(layers=[three[0], part], n=2) == INV          # partly shared table
+    other = layer(**{**sl, "arena": B_ + 0x30000, "arena_bytes": 8192})
+    assert seal(layers=[three[0], other], n=2) == INV         # shared table, arenas of two sizes
+    assert seal(NS=0) == swrt.OK and seal(n=0) == swrt.OK

@@ -1,7 +1,8 @@
 """GPU parity of the paged caches against the oracle.
 
-Conversion (swrt_paged_quantize) and append (swrt_paged_append) decide every
-byte in binary32 on both sides: whole arenas and descriptor tables are
+Conversion (swrt_paged_quantize) and append (swrt_paged_append, sealed
+blocks; swrt_paged_append_open, the open-page extension) decide every byte in
+binary32 on both sides: whole arenas, descriptor tables and block tables are
 compared byte for byte. Attention (swrt_paged_attention) reduces in fp32
 against the oracle's float64 and is held, per batch entry and head, to the
 bound of the windowed attention's tests with the paged kernel's extra
@@ -227,9 +228,6 @@ def test_paged_attention_bad_pages_flag_and_skip(orc):
     t4 = tb.copy()
     t4[case.page_ids[case.page_ptr[4] - 1]]["v_scale"] = 0.0
     cases.append((t4, oracle.FLAG_BAD_PAGES))
-    t5 = tb.copy()
-    t5[case.page_ids[case.page_ptr[4] - 1]]["k_offset"] += 8
-    cases.append((t5, oracle.FLAG_BAD_PAGES))
     for t, want in cases:
         cache = swrt.PagedCache.upload(t, case.page_ptr, case.page_ids, case.arena, DEV)
         out = torch.full((B, Hq, D), 7.0, device=DEV)
@@ -244,6 +242,23 @@ def test_paged_attention_bad_pages_flag_and_skip(orc):
         same = refo == 7.0
         assert (got[same] == 7.0).all()
         np.testing.assert_allclose(got[~same], refo[~same], atol=1e-4)
+    # the library's layout rule (not the pages'): a payload offset that is not
+    # a multiple of 16 makes the page invalid for the kernels; the oracle,
+    # which follows the pages, reads it
+    t5 = tb.copy()
+    pid = case.page_ids[case.page_ptr[4] - 1]
+    t5[pid]["k_offset"] += 8
+    cache = swrt.PagedCache.upload(t5, case.page_ptr, case.page_ids, case.arena, DEV)
+    out = torch.full((B, Hq, D), 7.0, device=DEV)
+    flags = flag_word()
+    swrt.paged_attention([q.to(DEV)], [cache], 9, Hkv, outs=[out], flags=flags)
+    torch.cuda.synchronize()
+    _, fo = orc.paged_attention(q_host(q), oracle.XF_BF16, case.arena, t5, case.page_ptr,
+                                case.page_ids, 9, Hkv, D ** -0.5)
+    assert fo == 0 and int(flags.item()) == swrt.FLAG_BAD_PAGES
+    got = out.cpu().numpy()
+    assert (got[1, 2:] == 7.0).all()  # stream 3 = (b 1, kv head 1): its heads untouched
+    np.testing.assert_allclose(got[0], good.cpu().numpy()[0], atol=1e-4)
     # an id out of range among the visible pages, and page_ptr past page_ids
     for mut in ("id", "ptr"):
         ids, ptr = case.page_ids.copy(), case.page_ptr.copy()
@@ -346,7 +361,6 @@ def test_paged_quantize_rejects_and_writes_nothing(orc):
     good = dict(blocks=[0, 1], dst=[base, base + 128, base + 256, base + 384], fb=base, fe=end)
     bads = [dict(blocks=[1, 1]), dict(blocks=[1, 0]), dict(blocks=[0, case.n_pages]),
             dict(dst=[base, base + 100, base + 256, base + 384]),
-            dict(dst=[base, base + 136, base + 256, base + 384]),   # misaligned
             dict(dst=[base + 16, base, base + 256, base + 384]),    # out of order
             dict(fb=base - 16, dst=[base - 16, base + 128, base + 256, base + 384]),
             dict(fe=base + 400)]
@@ -365,6 +379,20 @@ def test_paged_quantize_rejects_and_writes_nothing(orc):
         assert int(flags.item()) == swrt.FLAG_BAD_PAGES, kw
         np.testing.assert_array_equal(c.arena.cpu().numpy(), case.arena)
         assert out.cpu().numpy().tobytes() == tb.tobytes()
+    # the library's layout rule: destinations at multiples of 16 (the oracle,
+    # which follows the pages, accepts this request)
+    dst = [base, base + 136, base + 256, base + 384]
+    st, _, _ = orc.paged_quantize(case.arena, tb, [0, 1], dst, base, end, I8, 0.1, 0, I8, 0.1, 0, D)
+    assert st == oracle.OK
+    c = upload(case)
+    flags = flag_word()
+    out = swrt.paged_quantize(c, torch.tensor([0, 1], dtype=torch.int32, device=DEV),
+                              torch.tensor(dst, dtype=torch.int64, device=DEV), base, end, I8, 0.1,
+                              0, I8, 0.1, 0, D, pages_out=c.pages, flags=flags)
+    torch.cuda.synchronize()
+    assert int(flags.item()) == swrt.FLAG_BAD_PAGES
+    np.testing.assert_array_equal(c.arena.cpu().numpy(), case.arena)
+    assert out.cpu().numpy().tobytes() == tb.tobytes()
     # a bad page anywhere in the table stops everything, selected or not
     t = tb.copy()
     t[case.n_pages - 1]["capacity"] = 0
@@ -381,7 +409,8 @@ def test_paged_quantize_rejects_and_writes_nothing(orc):
 # -- append ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("new_dtype", [torch.bfloat16, torch.float32, torch.float16])
-def test_paged_append_equals_the_oracle(orc, new_dtype):
+def test_paged_append_open_equals_the_oracle(orc, new_dtype):
+    """The open-page extension."""
     g = wl.rng(64)
     D, S = 64, 24
     T = g.integers(0, 50, S)
@@ -393,11 +422,11 @@ def test_paged_append_equals_the_oracle(orc, new_dtype):
     tb = otable(case)
     kn = torch.from_numpy(g.uniform(-2, 2, (S, D)).astype(np.float32)).to(new_dtype)
     vn = torch.from_numpy(g.uniform(-2, 2, (S, D)).astype(np.float32)).to(new_dtype)
-    ar, pout, fo = orc.paged_append(case.arena, tb, case.page_ptr, case.page_ids, q_host(kn),
-                                    q_host(vn), QT[new_dtype], D)
+    ar, pout, fo = orc.paged_append_open(case.arena, tb, case.page_ptr, case.page_ids,
+                                         q_host(kn), q_host(vn), QT[new_dtype], D)
     c = upload(case)
     flags = flag_word()
-    swrt.paged_append([c], [kn.to(DEV)], [vn.to(DEV)], flags=flags)
+    swrt.paged_append_open([c], [kn.to(DEV)], [vn.to(DEV)], flags=flags)
     torch.cuda.synchronize()
     assert int(flags.item()) == fo
     assert fo == swrt.FLAG_BAD_PAGES | swrt.FLAG_PAGE_FULL
@@ -405,7 +434,7 @@ def test_paged_append_equals_the_oracle(orc, new_dtype):
     assert c.table().tobytes() == pout.tobytes()
 
 
-def test_paged_append_shared_table_grows_once_then_attention_sees_it(orc):
+def test_paged_append_open_shared_table_grows_once_then_attention_sees_it(orc):
     g = wl.rng(65)
     D, B, Hkv, n = 64, 2, 4, 3
     S = B * Hkv
@@ -423,13 +452,14 @@ def test_paged_append_shared_table_grows_once_then_attention_sees_it(orc):
     full = int((cases[0].fields["length"] == cases[0].fields["capacity"])[
         cases[0].page_ids[cases[0].page_ptr[1:] - 1]].sum())
     flags = flag_word()
-    swrt.paged_append(caches, [k.to(DEV) for k in kn], [v.to(DEV) for v in vn], flags=flags)
+    swrt.paged_append_open(caches, [k.to(DEV) for k in kn], [v.to(DEV) for v in vn], flags=flags)
     torch.cuda.synchronize()
     assert int(flags.item()) == (swrt.FLAG_PAGE_FULL if full else 0)
     tb0 = otable(cases[0])
     for i in range(n):
-        ar, pout, _ = orc.paged_append(cases[i].arena, tb0, cases[0].page_ptr, cases[0].page_ids,
-                                       q_host(kn[i]), q_host(vn[i]), oracle.XF_BF16, D)
+        ar, pout, _ = orc.paged_append_open(cases[i].arena, tb0, cases[0].page_ptr,
+                                            cases[0].page_ids, q_host(kn[i]), q_host(vn[i]),
+                                            oracle.XF_BF16, D)
         np.testing.assert_array_equal(caches[i].arena.cpu().numpy(), ar)
         assert table.table().tobytes() == pout.tobytes()  # grew once, not n times
     # attention with a zero left window returns each appended V exactly
@@ -448,15 +478,192 @@ def test_paged_append_shared_table_grows_once_then_attention_sees_it(orc):
             np.testing.assert_array_equal(got, np.stack([want, want]))
 
 
+def slotted_upload(case, stride: int, extra_pages: int, table=None, arena=None):
+    """The case as a slotted block table on the device with ``extra_pages``
+    free descriptors after its pages; returns (cache, host descriptors,
+    page_count, page_ids)."""
+    n = len(case.page_ptr) - 1
+    count = np.diff(case.page_ptr).astype(np.int32)
+    ids = np.full(n * stride, -1, np.int32)
+    for s in range(n):
+        ids[s * stride:s * stride + count[s]] = case.page_ids[case.page_ptr[s]:case.page_ptr[s + 1]]
+    base = otable(case) if table is None else table
+    tb = np.zeros(len(base) + extra_pages, oracle.PAGE_DTYPE)
+    tb[:len(base)] = base
+    ar = case.arena if arena is None else arena
+    cache = swrt.PagedCache.upload(tb.view(swrt.PAGE_DTYPE), None, ids, ar, DEV,
+                                   page_count=count, page_stride=stride)
+    return cache, tb, count, ids
+
+
+def sealed_both(orc, cache, tb, count, ids, arena, kn, vn, first, free, fmt):
+    """The sealed append on the device and in the oracle; returns the flags of
+    both and the oracle's (arena, descriptors, count, ids)."""
+    kf, ks, kz, vf, vs, vz = fmt
+    NS, S, D = kn.shape
+    flags = flag_word()
+    swrt.paged_append([cache], [kn.to(DEV)], [vn.to(DEV)], first_id=first, free_begin=free,
+                      free_end=cache.arena.numel(), k_format=kf, k_scale=ks, k_zero_point=kz,
+                      v_format=vf, v_scale=vs, v_zero_point=vz, flags=flags)
+    st, ar, pout, cnt, ids2, fo, written = orc.paged_append(
+        arena, tb, count, cache.page_stride, ids, q_host(kn), q_host(vn), QT[kn.dtype], S, D, D,
+        first, free, len(arena), kf, ks, kz, vf, vs, vz)
+    assert st == oracle.OK
+    torch.cuda.synchronize()
+    return int(flags.item()), fo, (ar, pout, cnt, ids2), written
+
+
+@pytest.mark.parametrize("S", [1, 4])
+@pytest.mark.parametrize("new_dtype", [torch.bfloat16, torch.float32, torch.float16])
+def test_paged_sealed_append_equals_the_oracle(orc, new_dtype, S):
+    """One new block per stream in every target format pair: arena,
+    descriptors and the slotted block table byte for byte; streams that are
+    empty, have no free slot, or whose last block is bad are handled as the
+    oracle handles them; no byte outside the new blocks changes."""
+    g = wl.rng(70 + S)
+    D, NS, stride = 64, 24, 6
+    T = g.integers(0, 60, NS)
+    T[0] = 0
+    streams = [wl.page_split(g, int(t), int(g.choice([4, 8, 16])), 0.3) for t in T]
+    streams[1] = [(4, 4)] * stride  # every slot in use
+    streams[2] = [(3, 4), (2, 4)]
+    case = wl.paged_case(g, D, streams, random_format(g), spare_bytes=NS * S * D * 4 * 2 + 4096)
+    tbase = otable(case)
+    tbase[case.page_ids[case.page_ptr[3] - 1]]["capacity"] = 0  # stream 2: a bad last block
+    for fmt in [(I8, 0.05, 3, U4, 0.25, 8), (BF16, 1.0, 0, F32, 1.0, 0), (I2, 0.5, -1, U2, 0.3, 2),
+                (F16, 1.0, 0, I4, 0.125, -2), (U8, 0.02, 128, BF16, 1.0, 0)]:
+        say("paged sealed append", new_dtype, S, fmt)
+        cache, tb, count, ids = slotted_upload(case, stride, NS, table=tbase)
+        kn = torch.from_numpy(g.uniform(-2, 2, (NS, S, D)).astype(np.float32)).to(new_dtype)
+        vn = torch.from_numpy(g.uniform(-2, 2, (NS, S, D)).astype(np.float32)).to(new_dtype)
+        free = case.free_offset + 16
+        fg, fo, (ar, pout, cnt, ids2), written = sealed_both(orc, cache, tb, count, ids,
+                                                             case.arena, kn, vn, case.n_pages,
+                                                             free, fmt)
+        assert fg == fo == swrt.FLAG_BAD_PAGES | swrt.FLAG_PAGE_FULL
+        np.testing.assert_array_equal(cache.arena.cpu().numpy(), ar)
+        assert cache.table().tobytes() == pout.tobytes()
+        np.testing.assert_array_equal(cache.page_count.cpu().numpy(), cnt)
+        np.testing.assert_array_equal(cache.page_ids.cpu().numpy(), ids2)
+        bits = oracle.PAGE_BITS[fmt[0]] + oracle.PAGE_BITS[fmt[3]]
+        assert written == (NS - 2) * S * D * bits // 8
+        # nothing outside the new payloads changed
+        keep = np.ones(len(ar), bool)
+        keep[free:free + NS * S * D * bits // 8] = False
+        np.testing.assert_array_equal(ar[keep], case.arena[keep])
+
+
+def test_paged_sealed_decode_loop_shared_table_then_attention(orc):
+    """Layers sharing one slotted block table take a one-token block per
+    stream and step (the descriptors and the table grow once per step, every
+    arena gets its rows); attention then reads the old pages and every new
+    block: a zero left window returns each stream's last V exactly, a wide one
+    stays within the attention bound of the oracle."""
+    g = wl.rng(75)
+    D, B, Hkv, Hq, n, steps = 64, 2, 4, 8, 3, 5
+    NS = B * Hkv
+    streams = [wl.page_split(g, int(t), 16) for t in g.integers(1, 60, NS)]
+    stride = max(len(st) for st in streams) + steps
+    spare = steps * NS * 2 * D * 2
+    cases = [wl.paged_case(wl.rng(80), D, streams, lambda s, i, m: (BF16, BF16, 1.0, 1.0, 0, 0),
+                           payload_rng=wl.rng(90 + i), spare_bytes=spare) for i in range(n)]
+    base, tb, count, ids = slotted_upload(cases[0], stride, steps * NS)
+    caches = [swrt.PagedCache(torch.from_numpy(c.arena).to(DEV), base.pages, None, base.page_ids,
+                              base.page_count, stride) for c in cases]
+    arenas = [c.arena.copy() for c in cases]
+    first, free = cases[0].n_pages, cases[0].free_offset
+    for step in range(steps):
+        kn = [torch.from_numpy(g.uniform(-1, 1, (NS, 1, D)).astype(np.float32)).to(torch.bfloat16)
+              for _ in range(n)]
+        vn = [torch.from_numpy(g.uniform(-1, 1, (NS, 1, D)).astype(np.float32)).to(torch.bfloat16)
+              for _ in range(n)]
+        flags = flag_word()
+        swrt.paged_append(caches, [k.to(DEV) for k in kn], [v.to(DEV) for v in vn],
+                          first_id=first, free_begin=free, free_end=len(arenas[0]),
+                          k_format=BF16, v_format=BF16, flags=flags)
+        torch.cuda.synchronize()
+        assert int(flags.item()) == 0
+        for i in range(n):
+            st, arenas[i], tb_i, cnt, ids_i, fo, w = orc.paged_append(
+                arenas[i], tb, count, stride, ids, q_host(kn[i]), q_host(vn[i]), oracle.XF_BF16,
+                1, D, D, first, free, len(arenas[i]), BF16, 1.0, 0, BF16, 1.0, 0)
+            assert st == oracle.OK and fo == 0
+            np.testing.assert_array_equal(caches[i].arena.cpu().numpy(), arenas[i])
+        tb, count, ids = tb_i, cnt, ids_i
+        assert base.table().tobytes() == tb.tobytes()  # grew once, not n times
+        np.testing.assert_array_equal(base.page_count.cpu().numpy(), count)
+        np.testing.assert_array_equal(base.page_ids.cpu().numpy(), ids)
+        first += NS
+        free += w
+    q = torch.from_numpy(g.uniform(-1, 1, (B, Hq, D)).astype(np.float32)).to(torch.bfloat16)
+    outs = swrt.paged_attention([q.to(DEV)] * n, caches, 0, Hkv, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    G = Hq // Hkv
+    for i in range(n):
+        for s in range(NS):
+            got = outs[i][s // Hkv, (s % Hkv) * G:(s % Hkv + 1) * G].cpu().numpy()
+            want = vn[i][s, 0].float().cpu().numpy()
+            np.testing.assert_array_equal(got, np.stack([want] * G))
+    flags = flag_word()
+    outs = swrt.paged_attention([q.to(DEV)] * n, caches, 40, Hkv, out_dtype=torch.float32,
+                                flags=flags)
+    torch.cuda.synchronize()
+    assert int(flags.item()) == 0
+    ptr = np.concatenate([[0], np.cumsum(count)]).astype(np.int32)
+    flat = np.concatenate([ids[s * stride:s * stride + count[s]] for s in range(NS)])
+    for i in range(n):
+        ref, f = orc.paged_attention(q_host(q), oracle.XF_BF16, arenas[i], tb, None, ids, 40, Hkv,
+                                     D ** -0.5, page_count=count, page_stride=stride)
+        ref2, _ = orc.paged_attention(q_host(q), oracle.XF_BF16, arenas[i], tb, ptr, flat, 40,
+                                      Hkv, D ** -0.5)
+        assert f == 0
+        np.testing.assert_array_equal(ref, ref2)  # the two table forms agree
+        case = wl.PagedCase(D, {}, ptr, flat, arenas[i], 0)
+        tol = bound(case, tb, q, Hkv, 40, D ** -0.5, torch.float32, ref)
+        assert (np.abs(outs[i].cpu().numpy() - ref) <= tol).all()
+
+
+def test_paged_sealed_append_layout_rule(orc):
+    """The library's layout rule: payload rows of 16-byte blocks. Rows of 8
+    bytes (int2, head_dim 32) and a free region off a 16-byte boundary are
+    refused at the boundary (the oracle, which follows the pages, takes them);
+    two tokens per block make the int2 payload 16 bytes again."""
+    g = wl.rng(76)
+    D, NS = 32, 4
+    case = wl.paged_case(g, D, [wl.page_split(g, 5, 4) for _ in range(NS)],
+                         lambda s, i, n: (BF16, BF16, 1.0, 1.0, 0, 0), spare_bytes=4096)
+    cache, tb, count, ids = slotted_upload(case, 4, NS)
+    kn = torch.zeros((NS, 1, D), dtype=torch.bfloat16, device=DEV)
+    free = case.free_offset
+    for kw in (dict(v_format=I2, v_scale=0.5), dict(free_begin=free + 8)):
+        a = dict(first_id=case.n_pages, free_begin=free, free_end=len(case.arena),
+                 k_format=BF16, v_format=BF16)
+        a.update(kw)
+        with pytest.raises(swrt.SwrtError) as e:
+            swrt.paged_append([cache], [kn], [kn], **a)
+        assert e.value.args[1] == swrt.E_UNSUPPORTED
+        st = orc.paged_append(case.arena, tb, count, 4, ids, q_host(kn), q_host(kn),
+                              oracle.XF_BF16, 1, D, D, a["first_id"], a["free_begin"],
+                              a["free_end"], a["k_format"], 1.0, 0, a["v_format"],
+                              a.get("v_scale", 1.0), 0)[0]
+        assert st == oracle.OK
+    kn2 = torch.zeros((NS, 2, D), dtype=torch.bfloat16, device=DEV)
+    swrt.paged_append([cache], [kn2], [kn2], first_id=case.n_pages, free_begin=free,
+                      free_end=len(case.arena), k_format=BF16, v_format=I2, v_scale=0.5)
+    torch.cuda.synchronize()
+    assert list(cache.page_count.cpu().numpy()) == list(count + 1)
+
+
 def test_workload9_full_size(orc):
     """The paged decode step at full size in the launch configuration the
     benchmark times: attention over all 12 layers (every output compared),
-    then the cooling conversion of every stream's oldest hot page in one layer
-    and one append into every stream of every layer (bytes compared)."""
+    then the cooling conversion of every stream's oldest hot page in one layer,
+    one sealed append into every stream of every layer (bytes compared) and
+    attention again over the grown table."""
     from sliding_window_ring_tensor_amd.paged_step import PagedDecodeStep
     spec = wl.workload9()
     say("workload 9 full size")
-    st = PagedDecodeStep(spec, DEV, set_id=0, spare_bytes=1 << 20)
+    st = PagedDecodeStep(spec, DEV, set_id=0, spare_bytes=2 << 20)
     st.attention()
     torch.cuda.synchronize()
     assert int(st.flags.item()) == 0
@@ -477,7 +684,7 @@ def test_workload9_full_size(orc):
         worst = max(worst, float(np.max(err / tol)))
     say("  attention worst err/tol", round(worst, 4))
     # cooling: the oldest hot page of every stream, bf16 -> int8, in layer 3
-    blocks, dst, _ = st.cooling_selection()
+    blocks, dst, cool_bytes = st.cooling_selection()
     arena = st.arenas[3].cpu().numpy()
     code, ar, pout = orc.paged_quantize(arena, tb, blocks, dst, st.layout_bytes, len(arena),
                                         spec.cold_format, spec.k_scale, 0, spec.cold_format,
@@ -492,20 +699,57 @@ def test_workload9_full_size(orc):
     assert int(flags.item()) == 0
     np.testing.assert_array_equal(st.arenas[3].cpu().numpy(), ar)
     assert out.cpu().numpy().tobytes() == pout.tobytes()
-    # append: one token into every stream's last page, every layer, one table
-    S = spec.batch * spec.kv_heads
-    kn = [wl.device_payload((S, spec.head_dim), torch.bfloat16, 9, 300 + i, DEV)
+    # sealed append: one new one-token block per stream, every layer, one
+    # slotted block table; attention then reads the new blocks too
+    NS = spec.batch * spec.kv_heads
+    count = np.diff(st.page_ptr_host).astype(np.int32)
+    stride = int(count.max()) + 1
+    ids = np.full(NS * stride, -1, np.int32)
+    for s_ in range(NS):
+        ids[s_ * stride:s_ * stride + count[s_]] = \
+            st.page_ids_host[st.page_ptr_host[s_]:st.page_ptr_host[s_ + 1]]
+    tb2 = np.zeros(len(tb) + NS, oracle.PAGE_DTYPE)
+    tb2[:len(tb)] = tb
+    base = swrt.PagedCache.upload(tb2.view(swrt.PAGE_DTYPE), None, ids, st.arenas[0], DEV,
+                                  page_count=count, page_stride=stride)
+    caches = [swrt.PagedCache(a, base.pages, None, base.page_ids, base.page_count, stride)
+              for a in st.arenas]
+    free = st.layout_bytes + (-(-cool_bytes // 16)) * 16
+    kn = [wl.device_payload((NS, 1, spec.head_dim), torch.bfloat16, 9, 300 + i, DEV)
           for i in range(spec.layers)]
-    vn = [wl.device_payload((S, spec.head_dim), torch.bfloat16, 9, 400 + i, DEV)
+    vn = [wl.device_payload((NS, 1, spec.head_dim), torch.bfloat16, 9, 400 + i, DEV)
           for i in range(spec.layers)]
     before = [a.cpu().numpy() for a in st.arenas]
     flags = flag_word()
-    swrt.paged_append(st.caches, kn, vn, flags=flags)
+    swrt.paged_append(caches, kn, vn, first_id=len(tb), free_begin=free,
+                      free_end=len(before[0]), k_format=spec.hot_format,
+                      v_format=spec.hot_format, flags=flags)
     torch.cuda.synchronize()
-    full = int((st.fields["length"] == st.fields["capacity"])[st.page_ptr_host[1:] - 1].any())
-    assert int(flags.item()) == (swrt.FLAG_PAGE_FULL if full else 0)
+    assert int(flags.item()) == 0
     for i in (0, 7, 11):
-        ar, pout, f = orc.paged_append(before[i], tb, st.page_ptr_host, st.page_ids_host,
-                                       q_host(kn[i]), q_host(vn[i]), oracle.XF_BF16, spec.head_dim)
+        code, ar, pout, cnt, ids2, f, _ = orc.paged_append(
+            before[i], tb2, count, stride, ids, q_host(kn[i]), q_host(vn[i]), oracle.XF_BF16, 1,
+            spec.head_dim, spec.head_dim, len(tb), free, len(before[i]), spec.hot_format, 1.0, 0,
+            spec.hot_format, 1.0, 0)
+        assert code == oracle.OK and f == 0
         np.testing.assert_array_equal(st.arenas[i].cpu().numpy(), ar)
-        assert st.caches[i].table().tobytes() == pout.tobytes()
+        assert base.table().tobytes() == pout.tobytes()
+        np.testing.assert_array_equal(base.page_count.cpu().numpy(), cnt)
+        np.testing.assert_array_equal(base.page_ids.cpu().numpy(), ids2)
+    flags = flag_word()
+    outs = swrt.paged_attention(st.qs, caches, spec.left_window, spec.kv_heads, flags=flags)
+    torch.cuda.synchronize()
+    assert int(flags.item()) == 0
+    ptr = np.concatenate([[0], np.cumsum(cnt)]).astype(np.int32)
+    flat = np.concatenate([ids2[s_ * stride:s_ * stride + cnt[s_]] for s_ in range(NS)])
+    for i in (0, 11):
+        arena = st.arenas[i].cpu().numpy()
+        ref, f = orc.paged_attention(q_host(st.qs[i]), oracle.XF_BF16, arena, pout, None, ids2,
+                                     spec.left_window, spec.kv_heads, spec.head_dim ** -0.5,
+                                     page_count=cnt, page_stride=stride)
+        assert f == 0
+        case = wl.PagedCase(spec.head_dim, {}, ptr, flat, arena, 0)
+        tol = bound(case, pout, st.qs[i], spec.kv_heads, spec.left_window,
+                    spec.head_dim ** -0.5, torch.bfloat16, ref)
+        err = np.abs(outs[i].float().cpu().numpy() - ref)
+        assert (err <= tol).all(), f"after the append, layer {i}: max err/tol {np.max(err / tol):.3g}"
