@@ -381,8 +381,9 @@ def test_paged_quantize_rejects_and_writes_nothing(orc):
         assert out.cpu().numpy().tobytes() == tb.tobytes()
     # the library's layout rule: destinations at multiples of 16 (the oracle,
     # which follows the pages, accepts this request)
-    dst = [base, base + 136, base + 256, base + 384]
-    st, _, _ = orc.paged_quantize(case.arena, tb, [0, 1], dst, base, end, I8, 0.1, 0, I8, 0.1, 0, D)
+    dst = [base, base + 264, base + 520, base + 776]  # 256-byte payloads, three off by 8
+    st, _, _ = orc.paged_quantize(case.arena, tb, [0, 1], dst, base, end, I8, 0.1, 0, I8, 0.1, 0,
+                                  D)
     assert st == oracle.OK
     c = upload(case)
     flags = flag_word()
