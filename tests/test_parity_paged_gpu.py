@@ -522,10 +522,11 @@ def test_paged_sealed_append_equals_the_oracle(orc, new_dtype, S):
     empty, have no free slot, or whose last block is bad are handled as the
     oracle handles them; no byte outside the new blocks changes."""
     g = wl.rng(70 + S)
-    D, NS, stride = 64, 24, 6
+    D, NS = 64, 24
     T = g.integers(0, 60, NS)
     T[0] = 0
     streams = [wl.page_split(g, int(t), int(g.choice([4, 8, 16])), 0.3) for t in T]
+    stride = max(len(st) for st in streams) + 1
     streams[1] = [(4, 4)] * stride  # every slot in use
     streams[2] = [(3, 4), (2, 4)]
     case = wl.paged_case(g, D, streams, random_format(g), spare_bytes=NS * S * D * 4 * 2 + 4096)
@@ -547,6 +548,7 @@ def test_paged_sealed_append_equals_the_oracle(orc, new_dtype, S):
         np.testing.assert_array_equal(cache.page_count.cpu().numpy(), cnt)
         np.testing.assert_array_equal(cache.page_ids.cpu().numpy(), ids2)
         bits = oracle.PAGE_BITS[fmt[0]] + oracle.PAGE_BITS[fmt[3]]
+        assert list(cnt - count) == [1] + [0, 0] + [1] * (NS - 3)  # streams 1 and 2 skipped
         assert written == (NS - 2) * S * D * bits // 8
         # nothing outside the new payloads changed
         keep = np.ones(len(ar), bool)
