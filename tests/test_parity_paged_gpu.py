@@ -644,7 +644,7 @@ def test_paged_sealed_append_layout_rule(orc):
         a.update(kw)
         with pytest.raises(swrt.SwrtError) as e:
             swrt.paged_append([cache], [kn], [kn], **a)
-        assert e.value.args[1] == swrt.E_UNSUPPORTED
+        assert e.value.status == swrt.E_UNSUPPORTED
         st = orc.paged_append(case.arena, tb, count, 4, ids, q_host(kn), q_host(kn),
                               oracle.XF_BF16, 1, D, D, a["first_id"], a["free_begin"],
                               a["free_end"], a["k_format"], 1.0, 0, a["v_format"],
