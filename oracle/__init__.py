@@ -36,7 +36,8 @@ PHASE_ALL = 3
 FLAG_ROPE_RANGE = 8
 # element types of the row transform
 XF_F32, XF_F16, XF_BF16, XF_INT8, XF_UINT8 = 1, 2, 3, 4, 5
-XF_BYTES = {XF_F32: 4, XF_F16: 2, XF_BF16: 2, XF_INT8: 1, XF_UINT8: 1}
+XF_FP8_E4M3 = 10
+XF_BYTES = {XF_F32: 4, XF_F16: 2, XF_BF16: 2, XF_INT8: 1, XF_UINT8: 1, XF_FP8_E4M3: 1}
 # page formats beyond those: sub-byte affine codes; bits per element of every format
 XF_INT4, XF_UINT4, XF_INT2, XF_UINT2 = 6, 7, 8, 9
 PAGE_BITS = {XF_F32: 32, XF_F16: 16, XF_BF16: 16, XF_INT8: 8, XF_UINT8: 8, XF_INT4: 4,
@@ -71,7 +72,8 @@ class RowXf(ctypes.Structure):
                 ("cos_table", ctypes.c_void_p), ("sin_table", ctypes.c_void_p),
                 ("max_position", ctypes.c_int64), ("rotary_dim", ctypes.c_int64),
                 ("interleaved", ctypes.c_int), ("scale", ctypes.c_float * 2),
-                ("zero_point", ctypes.c_int32 * 2)]
+                ("zero_point", ctypes.c_int32 * 2), ("channel_scale", ctypes.c_void_p * 2),
+                ("channel_zero_point", ctypes.c_void_p * 2)]
 
 
 @dataclass
@@ -86,6 +88,9 @@ class Transform:
     interleaved: bool = False
     scale: tuple = (1.0, 1.0)
     zero_point: tuple = (0, 0)
+    # per-channel parameters [kv_heads, head_dim] for K and V (None: the scalar)
+    channel_scale: tuple = (None, None)
+    channel_zero_point: tuple = (None, None)
 
     def c(self) -> RowXf:
         x = RowXf()
@@ -99,6 +104,14 @@ class Transform:
         x.interleaved = int(self.interleaved)
         x.scale[0], x.scale[1] = self.scale
         x.zero_point[0], x.zero_point[1] = self.zero_point
+        self.channel_scale = tuple(None if a is None else np.ascontiguousarray(a, np.float32)
+                                   for a in self.channel_scale)
+        self.channel_zero_point = tuple(None if a is None else np.ascontiguousarray(a, np.int32)
+                                        for a in self.channel_zero_point)
+        for k in range(2):
+            a, z = self.channel_scale[k], self.channel_zero_point[k]
+            x.channel_scale[k] = None if a is None else a.ctypes.data
+            x.channel_zero_point[k] = None if z is None else z.ctypes.data
         return x
 
 
@@ -137,7 +150,7 @@ class Oracle:
                                              i64, i64, i64, i64, i64, i32, ctypes.c_uint, u32p]
         lib.orc_kv_window_append.restype = ctypes.c_int
         xfp = ctypes.POINTER(RowXf)
-        lib.orc_xf_row.argtypes = [xfp, i32, i64, vp, vp, i64]
+        lib.orc_xf_row.argtypes = [xfp, i32, i64, i64, vp, vp, i64]
         lib.orc_xf_row.restype = ctypes.c_int
         lib.orc_kv_window_append_xf.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64,
                                                 i64, i64, i64, ctypes.c_uint, xfp, u32p]
@@ -272,13 +285,15 @@ class Oracle:
 
 
     # -- fused append: RoPE + conversion / quantization -------------------
-    def xf_row(self, x: Transform, t: int, pos: int, row: np.ndarray, out: np.ndarray) -> int:
-        """One row through the transform (row: head_dim elements of in_type,
-        out: head_dim elements of out_type, both contiguous). Returns the status."""
+    def xf_row(self, x: Transform, t: int, pos: int, row: np.ndarray, out: np.ndarray,
+               head: int = 0) -> int:
+        """One row of KV head ``head`` through the transform (row: head_dim
+        elements of in_type, out: head_dim elements of out_type, both
+        contiguous). Returns the status."""
         D = out.size
         if x.in_type in (XF_F32, XF_F16, XF_BF16) and x.out_type in XF_BYTES:
             assert row.nbytes == D * XF_BYTES[x.in_type] and out.nbytes == D * XF_BYTES[x.out_type]
-        return self.lib.orc_xf_row(ctypes.byref(x.c()), t, pos, _ptr(row), _ptr(out), D)
+        return self.lib.orc_xf_row(ctypes.byref(x.c()), t, head, pos, _ptr(row), _ptr(out), D)
 
     def kv_window_append_xf(self, x: Transform, k_cache, v_cache, k_new, v_new, new_strides,
                             seq_len, cache_past_lens, evict_counts, past_lens, k_staging=None,

@@ -386,7 +386,8 @@ static int64_t xf_elem_bytes(int type)
     case ORC_XF_F16:
     case ORC_XF_BF16: return 2;
     case ORC_XF_INT8:
-    case ORC_XF_UINT8: return 1;
+    case ORC_XF_UINT8:
+    case ORC_XF_FP8_E4M3: return 1;
     default: return 0;
     }
 }
@@ -409,7 +410,9 @@ static int xf_code_range(int type, int32_t *lo, int32_t *hi)
 /* a transform the functions below accept, for rows of head_dim elements */
 static int xf_valid(const orc_row_xf *x, int64_t head_dim)
 {
-    int32_t lo, hi;
+    int32_t lo = 0, hi = 0;
+    const int affine = xf_code_range(x ? x->out_type : 0, &lo, &hi);
+    const int fp8 = x && x->out_type == ORC_XF_FP8_E4M3;
     if (!x || !xf_float_type(x->in_type) || xf_elem_bytes(x->out_type) == 0)
         return 0;
     if ((x->cos_table == NULL) != (x->sin_table == NULL))
@@ -419,11 +422,15 @@ static int xf_valid(const orc_row_xf *x, int64_t head_dim)
             x->rotary_dim > head_dim)
             return 0;
     }
-    if (xf_code_range(x->out_type, &lo, &hi)) {
-        for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < 2; ++t) {
+        /* per-channel scales belong to the scaled targets, zero points to the
+         * affine integer codes */
+        if ((x->channel_scale[t] && !affine && !fp8) || (x->channel_zero_point[t] && !affine))
+            return 0;
+        if (affine || fp8) {
             if (!(x->scale[t] > 0.0f) || isinf(x->scale[t]))
                 return 0;
-            if (x->zero_point[t] < lo || x->zero_point[t] > hi)
+            if (affine ? (x->zero_point[t] < lo || x->zero_point[t] > hi) : x->zero_point[t] != 0)
                 return 0;
         }
     }
@@ -516,18 +523,52 @@ static float xf_load(int type, const char *row, int64_t i)
     }
 }
 
-/* [PF]: saturate(round_half_even(y / scale) + zero_point); NaN -> zero_point */
+/* [PF]: saturate(round_half_even(y / scale) + zero_point); NaN -> zero_point
+ * (the zero point itself saturated: a per-channel table is data, not checked) */
 static int32_t xf_quantize(float y, float scale, int32_t zero_point, int32_t lo, int32_t hi)
 {
     float q;
     if (isnan(y))
-        return zero_point;
+        return zero_point < lo ? lo : (zero_point > hi ? hi : zero_point);
     q = nearbyintf(y / scale) + (float)zero_point; /* default rounding: ties to even */
     if (q < (float)lo)
         return lo;
     if (q > (float)hi)
         return hi;
     return (int32_t)q;
+}
+
+/* The OCP 8-bit float E4M3 ("float8e4m3fn"): 1 sign bit, 4 exponent bits of
+ * bias 7, 3 fraction bits, no infinities, S.1111.111 the only NaN, largest
+ * finite 448 = 1.75 * 2^8, smallest normal 2^-6, subnormals m * 2^-9. A
+ * binary32 value is rounded to nearest, ties to even; a finite value beyond
+ * 448, or an infinity, saturates to +-448 (the saturating conversion); NaN
+ * becomes the positive NaN 0x7F. */
+static uint8_t float_to_e4m3_bits(float f)
+{
+    const uint8_t sign = signbit(f) ? 0x80 : 0;
+    double a, q;
+    int e;
+    if (isnan(f))
+        return 0x7F;
+    a = fabs((double)f);
+    if (a >= 448.0)
+        return sign | 0x7E; /* +-448; beyond it saturates */
+    if (a < ldexp(1.0, -6)) {
+        /* zero or subnormal: count units of 2^-9; 8 units is the smallest normal,
+         * whose encoding (exponent 1, fraction 0) is the same integer */
+        q = nearbyint(ldexp(a, 9));
+        return sign | (uint8_t)q;
+    }
+    frexp(a, &e); /* a = m * 2^e, 0.5 <= m < 1: the leading bit is 2^(e-1) */
+    /* 4 significant bits: q in [8, 16] */
+    q = nearbyint(ldexp(a, 3 - (e - 1)));
+    if (q == 16.0) {
+        q = 8.0;
+        e += 1;
+    }
+    /* a < 448 rounds to at most 448 = exponent field 15, fraction 6 */
+    return sign | (uint8_t)(((e - 1 + 7) << 3) | (int)(q - 8.0));
 }
 
 /* element i of a dense f32 / f16 / bf16 row */
@@ -554,18 +595,39 @@ static void store_dense(int type, char *row, int64_t i, float y)
     }
 }
 
-static void xf_store(const orc_row_xf *x, int t, char *row, int64_t i, float y)
+/* element i of a row of KV head `head`: its scale and zero point, from the
+ * per-channel tables [kv_heads, head_dim] when given, else the scalars */
+static void xf_params(const orc_row_xf *x, int t, int64_t head, int64_t head_dim, int64_t i,
+                      float *scale, int32_t *zero_point)
 {
-    int32_t lo, hi, q;
+    *scale = x->channel_scale[t] ? x->channel_scale[t][head * head_dim + i] : x->scale[t];
+    *zero_point = x->channel_zero_point[t] ? x->channel_zero_point[t][head * head_dim + i]
+                                           : x->zero_point[t];
+}
+
+static void xf_store(const orc_row_xf *x, int t, int64_t head, int64_t head_dim, char *row,
+                     int64_t i, float y)
+{
+    int32_t lo = 0, hi = 0, q, zp;
+    float sc;
     switch (x->out_type) {
     case ORC_XF_F32:
     case ORC_XF_F16:
     case ORC_XF_BF16:
         store_dense(x->out_type, row, i, y);
         break;
+    case ORC_XF_FP8_E4M3: {
+        /* scaled like an affine code, y / scale rounded once to binary32 */
+        uint8_t c;
+        xf_params(x, t, head, head_dim, i, &sc, &zp);
+        c = float_to_e4m3_bits(y / sc);
+        memcpy(row + i, &c, 1);
+        break;
+    }
     default: /* ORC_XF_INT8, ORC_XF_UINT8 */
         xf_code_range(x->out_type, &lo, &hi);
-        q = xf_quantize(y, x->scale[t], x->zero_point[t], lo, hi);
+        xf_params(x, t, head, head_dim, i, &sc, &zp);
+        q = xf_quantize(y, sc, zp, lo, hi);
         if (x->out_type == ORC_XF_INT8) {
             const int8_t c = (int8_t)q;
             memcpy(row + i, &c, 1);
@@ -577,11 +639,11 @@ static void xf_store(const orc_row_xf *x, int t, char *row, int64_t i, float y)
     }
 }
 
-int orc_xf_row(const orc_row_xf *x, int t, int64_t pos, const void *in, void *out,
+int orc_xf_row(const orc_row_xf *x, int t, int64_t head, int64_t pos, const void *in, void *out,
                int64_t head_dim)
 {
     float *v;
-    if (head_dim < 0 || (t != 0 && t != 1) || !xf_valid(x, head_dim))
+    if (head_dim < 0 || head < 0 || (t != 0 && t != 1) || !xf_valid(x, head_dim))
         return ORC_E_INVALID_ARG;
     if (head_dim == 0)
         return ORC_OK;
@@ -611,7 +673,7 @@ int orc_xf_row(const orc_row_xf *x, int t, int64_t pos, const void *in, void *ou
         }
     }
     for (int64_t i = 0; i < head_dim; ++i)
-        xf_store(x, t, (char *)out, i, v[i]);
+        xf_store(x, t, head, head_dim, (char *)out, i, v[i]);
     free(v);
     return ORC_OK;
 }
@@ -670,7 +732,7 @@ int orc_kv_window_append_xf(void *k_cache, void *v_cache, const void *k_new,
         for (int t = 0; t < 2 && status == ORC_OK; ++t)
             for (int64_t h = 0; h < H && status == ORC_OK; ++h)
                 for (int64_t s = 0; s < S && status == ORC_OK; ++s)
-                    status = orc_xf_row(x, t, past_lens[b] + s,
+                    status = orc_xf_row(x, t, h, past_lens[b] + s,
                                         news[t] + (b * new_strides[0] + h * new_strides[1] +
                                                    s * new_strides[2]) * in_es,
                                         tmp[t] + (h * S + s) * out_row, D);
@@ -707,6 +769,10 @@ int orc_tensor_scatter_xf(void *present, const void *past, const void *update,
     B = shape[0];
     if (!xf_valid(x, D) || seq_len < 0 || seq_len > M)
         return ORC_E_INVALID_ARG;
+    /* per-channel tables: [shape[1], D] for rank 4 ([B, H, M, D]), [1, D] for rank 3 */
+    if (rank > 4 && (x->channel_scale[0] || x->channel_scale[1] || x->channel_zero_point[0] ||
+                     x->channel_zero_point[1]))
+        return ORC_E_INVALID_ARG;
     for (int i = 0; i < rank; ++i)
         if (shape[i] < 0)
             return ORC_E_INVALID_ARG;
@@ -739,7 +805,7 @@ int orc_tensor_scatter_xf(void *present, const void *past, const void *update,
         /* the entry's update rows, transformed at positions w + s */
         for (int64_t o = 0; o < O1 && linear_ok && status == ORC_OK; ++o)
             for (int64_t s = 0; s < seq_len && status == ORC_OK; ++s)
-                status = orc_xf_row(x, t, w + s,
+                status = orc_xf_row(x, t, rank == 4 ? o : 0, w + s,
                                     (const char *)update + ((b * O1 + o) * seq_len + s) * D * in_es,
                                     tmp + (o * seq_len + s) * D * out_es, D);
         if (status != ORC_OK)

@@ -138,6 +138,7 @@ int orc_kv_window_append(void *k_cache, void *v_cache, const void *k_new,
 #define ORC_XF_BF16 3
 #define ORC_XF_INT8 4
 #define ORC_XF_UINT8 5
+#define ORC_XF_FP8_E4M3 10 /* OCP float8 E4M3 (float8e4m3fn), scaled, saturating */
 
 typedef struct {
     int in_type;            /* new rows: ORC_XF_F32, ORC_XF_F16 or ORC_XF_BF16 */
@@ -147,23 +148,34 @@ typedef struct {
     int64_t max_position;   /* rows of the tables */
     int64_t rotary_dim;     /* even, 2 .. head_dim; later elements pass unrotated */
     int interleaved;        /* 0: pairs (j, j + rotary_dim/2); 1: pairs (2j, 2j+1) */
-    float scale[2];         /* K, V scales: positive and finite (integer out_type) */
-    int32_t zero_point[2];  /* K, V zero points: inside the code range */
+    float scale[2];         /* K, V scales: positive and finite (INT8 / UINT8 / FP8) */
+    int32_t zero_point[2];  /* K, V zero points: inside the code range (0 for FP8) */
+    /* per-channel parameters, shape [kv_heads, 1, head_dim] with the singleton
+     * dimension dropped: element i of a row of KV head h takes entry
+     * h * head_dim + i instead of the scalar. NULL: the scalar. Scales for
+     * INT8 / UINT8 / FP8 targets, zero points for INT8 / UINT8 only. Table
+     * entries are data (not checked): the formulas apply as written, a NaN
+     * taking the zero point saturated into the code range. */
+    const float *channel_scale[2];
+    const int32_t *channel_zero_point[2];
 } orc_row_xf;
 
 /*
- * One row of head_dim elements: read as float, rotate when t == 0 (K) and
- * tables are given, using table row `pos`; then write in out_type. Every
- * float operation is one IEEE binary32 operation, rounded to nearest even:
+ * One row of head_dim elements of KV head `head`: read as float, rotate when
+ * t == 0 (K) and tables are given, using table row `pos`; then write in
+ * out_type. Every float operation is one IEEE binary32 operation, rounded to
+ * nearest even:
  *   x0' = fl(fl(x0 * c) - fl(x1 * s)),  x1' = fl(fl(x1 * c) + fl(x0 * s)).
  * bf16 / f16 outputs round to nearest even (overflow -> infinity); every
  * float output stores NaN as the positive canonical quiet NaN of its type;
  * integer outputs are
- * saturate(round_half_even(fl(y / scale)) + zero_point), NaN -> zero_point.
+ * saturate(round_half_even(fl(y / scale)) + zero_point), NaN -> zero_point;
+ * FP8 outputs are E4M3(fl(y / scale)), nearest even, saturating at +-448.
+ * scale and zero_point are element i's (per-channel tables) or the scalars.
  * Returns ORC_E_INVALID_ARG on a bad transform or a position outside the
  * tables.
  */
-int orc_xf_row(const orc_row_xf *x, int t, int64_t pos, const void *in, void *out,
+int orc_xf_row(const orc_row_xf *x, int t, int64_t head, int64_t pos, const void *in, void *out,
                int64_t head_dim);
 
 /*
@@ -188,7 +200,9 @@ int orc_kv_window_append_xf(void *k_cache, void *v_cache, const void *k_new,
  * last dimension, head_dim) whose update rows (in_type) pass through the
  * transform first, update row s of batch entry b at absolute position
  * write_indices[b] + s (before any circular wrap). present / past hold
- * out_type rows. `t` selects K (0: rotated) or V (1). A linear entry out of
+ * out_type rows. Per-channel tables, if any, are [shape[1], head_dim] for
+ * rank 4 ([B, H, M, D]: prefix index 1 is the KV head) and [1, head_dim] for
+ * rank 3; rank > 4 takes none. `t` selects K (0: rotated) or V (1). A linear entry out of
  * range is flagged LINEAR_OOB and skipped; then an entry whose positions leave
  * [0, max_position) (rotation on) is flagged ROPE_RANGE and skipped (keeping
  * past's rows).

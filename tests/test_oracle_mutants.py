@@ -85,12 +85,12 @@ MUTANTS = {
                        "if (x->cos_table) {\n        /* [GQA-ROPE]"),
     "rope_tail_rotated": ("const int64_t half = x->rotary_dim / 2;",
                           "const int64_t half = head_dim / 2;"),
-    "rope_position_cache_relative": ("status = orc_xf_row(x, t, past_lens[b] + s,",
-                                     "status = orc_xf_row(x, t, cache_past_lens[b] + s,"),
-    "rope_position_ignores_s": ("status = orc_xf_row(x, t, past_lens[b] + s,",
-                                "status = orc_xf_row(x, t, past_lens[b],"),
-    "scatter_position_wrapped": ("status = orc_xf_row(x, t, w + s,",
-                                 "status = orc_xf_row(x, t, floor_mod(w + s, M),"),
+    "rope_position_cache_relative": ("status = orc_xf_row(x, t, h, past_lens[b] + s,",
+                                     "status = orc_xf_row(x, t, h, cache_past_lens[b] + s,"),
+    "rope_position_ignores_s": ("status = orc_xf_row(x, t, h, past_lens[b] + s,",
+                                "status = orc_xf_row(x, t, h, past_lens[b],"),
+    "scatter_position_wrapped": ("status = orc_xf_row(x, t, rank == 4 ? o : 0, w + s,",
+                                 "status = orc_xf_row(x, t, rank == 4 ? o : 0, floor_mod(w + s, M),"),
     "rope_range_off_by_one": ("(p0 >= 0 && p0 <= x->max_position - n)",
                               "(p0 >= 0 && p0 <= x->max_position - n + 1)"),
     "rope_range_not_flagged": ("set_flag(flags, ORC_FLAG_ROPE_RANGE);\n            continue;",
@@ -102,10 +102,9 @@ MUTANTS = {
     "quant_truncates": ("q = nearbyintf(y / scale) + (float)zero_point;",
                         "q = truncf(y / scale) + (float)zero_point;"),
     "quant_high_code_wraps": ("        *hi = 127;", "        *hi = 128;"),
-    "quant_nan_to_low_code": ("if (isnan(y))\n        return zero_point;",
-                              "if (isnan(y))\n        return lo;"),
-    "quant_v_uses_k_parameters": ("q = xf_quantize(y, x->scale[t], x->zero_point[t], lo, hi);",
-                                  "q = xf_quantize(y, x->scale[0], x->zero_point[0], lo, hi);"),
+    "quant_nan_to_low_code": ("if (isnan(y))\n        return zero_point < lo",
+                              "if (isnan(y))\n        return lo + 0 * zero_point;\n    if (0)\n        return zero_point < lo"),
+    "quant_v_uses_k_parameters": (": x->scale[t];", ": x->scale[0];"),
     "f32_nan_payload_kept": ("if (isnan(y)) {\n            const uint32_t canonical",
                              "if (0) {\n            const uint32_t canonical"),
     "bf16_ties_away": ("if (dropped > 0x8000 || (dropped == 0x8000 && (kept & 1)))",
@@ -153,6 +152,19 @@ MUTANTS = {
     "paged_duplicates_accepted": ("(i > 0 && id <= blocks[i - 1])", "(i > 0 && id < blocks[i - 1])"),
     "paged_destinations_overlap": ("if (dst < next || bytes > free_end - dst)",
                                    "if (bytes > free_end - dst)"),
+    # per-channel parameters and the fp8 target of the fused append
+    "xf_channel_head_ignored": ("x->channel_scale[t][head * head_dim + i]", "x->channel_scale[t][i]"),
+    "xf_channel_zero_ignored": ("x->channel_zero_point[t] ? x->channel_zero_point[t][head * head_dim + i]",
+                                "0 ? x->channel_zero_point[t][head * head_dim + i]"),
+    "fp8_not_scaled": ("c = float_to_e4m3_bits(y / sc);", "c = float_to_e4m3_bits(y);"),
+    "fp8_nan_beyond_range": ("return sign | 0x7E; /* +-448; beyond it saturates */",
+                             "return a > 448.0 ? 0x7F : (sign | 0x7E);"),
+    "fp8_subnormal_truncates": ("q = nearbyint(ldexp(a, 9));", "q = floor(ldexp(a, 9));"),
+    "fp8_ties_away": ("q = nearbyint(ldexp(a, 3 - (e - 1)));", "q = round(ldexp(a, 3 - (e - 1)));"),
+    "fp8_exponent_bias": ("((e - 1 + 7) << 3)", "((e - 1 + 8) << 3)"),
+    "scatter_channel_head_zero": ("status = orc_xf_row(x, t, rank == 4 ? o : 0,",
+                                  "status = orc_xf_row(x, t, 0,"),
+    "window_channel_head_zero": ("status = orc_xf_row(x, t, h,", "status = orc_xf_row(x, t, 0,"),
     # the sealed-block append and the slotted block table
     "sealed_start_off_by_one": ("T = pages[last].start + pages[last].length;",
                                 "T = pages[last].start + pages[last].length - 1;"),

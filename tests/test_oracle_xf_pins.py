@@ -449,3 +449,202 @@ def test_scatter_position_out_of_tables_keeps_past(orc):
     assert st == 0 and f == oracle.FLAG_ROPE_RANGE | oracle.FLAG_LINEAR_OOB
     np.testing.assert_array_equal(present[1:], past[1:])
     assert not np.array_equal(present[0], past[0])
+
+
+# -- per-channel parameters and the fp8 target ----------------------------------
+# The pull request "GQA support sliding_window_cache" (comment-only follow-up)
+# gives the quantized cache's per-channel scales the shape (kv_num_heads, 1,
+# head_size), the singleton dimension flattened: element i of a row of KV
+# head h takes entry h * head_size + i.
+
+def _codes(orc, x, t, head, rows):
+    """Rows [n, D] of in_type through the transform as KV head ``head``."""
+    D = rows.shape[1]
+    out = np.zeros((len(rows), D), NP.get(x.out_type, np.uint8))
+    for i, r in enumerate(rows):
+        assert orc.xf_row(x, t, 0, np.ascontiguousarray(r), out[i], head=head) == oracle.OK
+    return out
+
+
+@pytest.mark.parametrize("out_type", [XF_INT8, XF_UINT8, oracle.XF_FP8_E4M3])
+def test_per_channel_tables_of_one_value_are_the_scalar(orc, out_type):
+    """Tables holding one value everywhere give exactly the scalar
+    transform's bytes, through the windowed append and TensorScatter."""
+    g = np.random.default_rng(60)
+    B, H, C, S, D = 3, 2, 8, 2, 6
+    zp = (0, 0) if out_type != XF_UINT8 else (120, 131)
+    sc = (0.05, 0.02)
+    xs = Transform(XF_F32, out_type, scale=sc, zero_point=zp)
+    tabs = tuple(np.full((H, D), v, np.float32) for v in sc)
+    ztabs = tuple(np.full((H, D), v, np.int32) for v in zp) if out_type != oracle.XF_FP8_E4M3 \
+        else (None, None)
+    xc = Transform(XF_F32, out_type, scale=(1.0, 1.0), zero_point=(0, 0) if ztabs[0] is not None
+                   else zp, channel_scale=tabs, channel_zero_point=ztabs)
+    kn, vn = (g.standard_normal((B, H, S, D)).astype(np.float32) * 3 for _ in range(2))
+    T = np.array([2, 9, 30]) + S - 1
+    L = orc.kv_seq_lengths(T - 1, S, C)
+    base = g.integers(0, 255, (B, H, C, D), dtype=np.uint8)
+    outs = []
+    for x in (xs, xc):
+        k, v = base.copy(), base.copy()
+        st = [np.zeros((B, H, C + S, D), np.uint8) for _ in range(2)]
+        assert orc.kv_window_append_xf(x, k, v, kn, vn, (H * S * D, S * D, D), S, L.cache_past,
+                                       L.evict, L.past, st[0], st[1]) == 0
+        pres = base.copy()
+        code, f = orc.tensor_scatter_xf(x, 1, pres, pres, vn, np.array([1, 0, 5]), "linear")
+        assert code == 0 and f == 0
+        outs.append((k, v, st[0], pres))
+    for a, b in zip(*outs):
+        np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("out_type,lo,hi", [(XF_INT8, -128, 127), (XF_UINT8, 0, 255)])
+def test_per_channel_reconstruction_within_half_of_each_channels_scale(orc, out_type, lo, hi):
+    g = np.random.default_rng(61)
+    H, D, n = 3, 16, 40
+    tab = (2.0 ** g.uniform(-8, -2, (H, D))).astype(np.float32)
+    ztab = g.integers(lo + 20, hi - 20, (H, D)).astype(np.int32)
+    x = Transform(XF_F32, out_type, channel_scale=(tab, tab), channel_zero_point=(ztab, ztab))
+    for h in range(H):
+        rows = (g.uniform(-1, 1, (n, D)) * tab[h] * 60).astype(np.float32)
+        codes = _codes(orc, x, 1, h, rows).astype(np.int64)
+        rec = (codes - ztab[h]) * tab[h].astype(np.float64)
+        inside = (codes > lo) & (codes < hi)
+        assert inside.mean() > 0.8
+        assert (np.abs(rec - rows)[inside] <= tab[h][None, :].repeat(n, 0)[inside] / 2 + 1e-12).all()
+
+
+def test_per_channel_channels_and_heads_are_independent(orc):
+    """Changing one channel's scale of one head changes only that element of
+    that head's rows (K and V alike); a head reads its own table row."""
+    g = np.random.default_rng(62)
+    H, D = 3, 8
+    tab = np.full((H, D), 0.05, np.float32)
+    rows = (g.standard_normal((20, D)) * 2).astype(np.float32)
+    x0 = Transform(XF_F32, XF_INT8, channel_scale=(tab, tab))
+    ref = [[_codes(orc, x0, t, h, rows) for h in range(H)] for t in range(2)]
+    tab2 = tab.copy()
+    tab2[1, 5] = 0.2
+    x1 = Transform(XF_F32, XF_INT8, channel_scale=(tab2, tab))
+    for t in range(2):
+        for h in range(H):
+            got = _codes(orc, x1, t, h, rows)
+            changed = np.argwhere((got != ref[t][h]).any(axis=0)).ravel().tolist()
+            assert changed == ([5] if (t, h) == (0, 1) else [])
+    # per-head constant tables equal the scalar transform of that head's value
+    tab3 = np.repeat(np.array([[0.01], [0.1], [0.03]], np.float32), D, axis=1)
+    x3 = Transform(XF_F32, XF_INT8, channel_scale=(tab3, tab3))
+    for h in range(H):
+        xs = Transform(XF_F32, XF_INT8, scale=(float(tab3[h, 0]),) * 2)
+        np.testing.assert_array_equal(_codes(orc, x3, 0, h, rows), _codes(orc, xs, 0, 0, rows))
+
+
+def test_per_channel_scatter_reads_the_head_of_prefix_index_one(orc):
+    """TensorScatter of [B, H, M, D] caches: rows of prefix (b, h) use table
+    row h; a rank-5 cache takes no tables."""
+    g = np.random.default_rng(63)
+    B, H, M, S, D = 2, 3, 6, 2, 4
+    tab = (2.0 ** g.uniform(-6, -2, (H, D))).astype(np.float32)
+    x = Transform(XF_F32, XF_INT8, channel_scale=(tab, tab))
+    upd = g.standard_normal((B, H, S, D)).astype(np.float32)
+    past = np.zeros((B, H, M, D), np.int8)
+    pres = past.copy()
+    w = np.array([1, 3])
+    code, f = orc.tensor_scatter_xf(x, 0, pres, pres, upd, w, "linear")
+    assert code == 0 and f == 0
+    for b in range(B):
+        for h in range(H):
+            want = _codes(orc, x, 0, h, upd[b, h])
+            np.testing.assert_array_equal(pres[b, h, w[b]:w[b] + S], want)
+    p5 = np.zeros((B, 1, H, M, D), np.int8)
+    code, _ = orc.tensor_scatter_xf(x, 0, p5, p5, upd[:, None], w, "linear")
+    assert code == oracle.E_INVALID_ARG
+
+
+def _e4m3_decode_torch(codes: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(codes.astype(np.uint8)).view(torch.float8_e4m3fn).float().numpy()
+
+
+def test_fp8_every_code_round_trips(orc):
+    """All 256 E4M3 codes, decoded by torch's float8_e4m3fn: each finite one
+    encodes back to itself (scale 1), the two NaNs to the positive NaN."""
+    codes = np.arange(256, dtype=np.uint8)
+    vals = _e4m3_decode_torch(codes)
+    x = Transform(XF_F32, oracle.XF_FP8_E4M3)
+    got = _codes(orc, x, 0, 0, vals.reshape(32, 8)).view(np.uint8).ravel()
+    finite = ~np.isnan(vals)
+    np.testing.assert_array_equal(got[finite], codes[finite])
+    assert (got[~finite] == 0x7F).all() and finite.sum() == 254
+
+
+def test_fp8_rounds_like_torch_and_saturates(orc):
+    """Inside the range torch's float32 -> float8_e4m3fn conversion (nearest
+    even) gives the same codes, exact midpoints included; beyond +-448 and
+    at the infinities the code saturates to +-448; NaN is 0x7F."""
+    g = np.random.default_rng(64)
+    codes = np.arange(0, 0x7E, dtype=np.uint8)
+    v = _e4m3_decode_torch(codes).astype(np.float64)
+    mids = ((v[:-1] + v[1:]) / 2).astype(np.float32)  # exact in binary32
+    rnd = (g.uniform(-463.9, 463.9, 4000) * 2.0 ** g.integers(-14, 1, 4000)).astype(np.float32)
+    vals = np.concatenate([mids, -mids, rnd, [2.0 ** -10, 3 * 2.0 ** -10, -0.0, 0.0]]).astype(np.float32)
+    vals = vals[: len(vals) // 8 * 8]
+    x = Transform(XF_F32, oracle.XF_FP8_E4M3)
+    got = _codes(orc, x, 0, 0, vals.reshape(-1, 8)).view(np.uint8).ravel()
+    want = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(got, want)
+    big = np.array([448.0, 449.0, 463.9, 464.0, 1e30, np.inf, -500.0, -np.inf], np.float32)
+    got = _codes(orc, x, 0, 0, big[None]).view(np.uint8).ravel()
+    assert list(got) == [0x7E] * 6 + [0xFE] * 2
+    nan = np.full((1, 8), np.nan, np.float32)
+    assert (_codes(orc, x, 0, 0, nan).view(np.uint8) == 0x7F).all()
+
+
+def test_fp8_applies_the_scale_first(orc):
+    """The fp8 code of y is that of fl(y / scale), per channel too; a zero
+    point is refused."""
+    g = np.random.default_rng(65)
+    rows = g.standard_normal((10, 8)).astype(np.float32) * 5
+    tab = (2.0 ** g.uniform(-3, 3, (2, 8))).astype(np.float32)
+    x = Transform(XF_F32, oracle.XF_FP8_E4M3, channel_scale=(tab, tab))
+    for h in range(2):
+        got = _codes(orc, x, 1, h, rows).view(np.uint8)
+        want = torch.from_numpy((rows / tab[h]).astype(np.float32)).to(torch.float8_e4m3fn)
+        np.testing.assert_array_equal(got, want.view(torch.uint8).numpy())
+    bad = Transform(XF_F32, oracle.XF_FP8_E4M3, zero_point=(1, 0))
+    out = np.zeros(8, np.uint8)
+    assert orc.xf_row(bad, 0, 0, rows[0], out) == oracle.E_INVALID_ARG
+    bad2 = Transform(XF_F32, XF_F32, channel_scale=(tab, None))  # no scale for a float target
+    assert orc.xf_row(bad2, 0, 0, rows[0], np.zeros(8, np.float32)) == oracle.E_INVALID_ARG
+
+
+@pytest.mark.parametrize("out_type", [XF_INT8, oracle.XF_FP8_E4M3])
+def test_per_channel_window_rows_use_their_heads_tables(orc, out_type):
+    """The windowed append with per-channel tables: the appended rows of KV
+    head h are the rows transformed with table row h, the rest is the plain
+    step."""
+    g = np.random.default_rng(66)
+    B, H, C, S, D = 3, 3, 8, 2, 8
+    tab = [(2.0 ** g.uniform(-6, -1, (H, D))).astype(np.float32) for _ in range(2)]
+    z = None if out_type == oracle.XF_FP8_E4M3 else \
+        tuple(g.integers(-20, 20, (H, D)).astype(np.int32) for _ in range(2))
+    x = Transform(XF_F32, out_type, channel_scale=tuple(tab),
+                  channel_zero_point=z if z is not None else (None, None))
+    kn, vn = (g.standard_normal((B, H, S, D)).astype(np.float32) for _ in range(2))
+    T = np.array([2, 9, 30]) + S - 1
+    L = orc.kv_seq_lengths(T - 1, S, C)
+    base = g.integers(0, 255, (B, H, C, D), dtype=np.uint8)
+    k1, v1 = base.copy(), base.copy()
+    st = [np.zeros((B, H, C + S, D), np.uint8) for _ in range(2)]
+    assert orc.kv_window_append_xf(x, k1, v1, kn, vn, (H * S * D, S * D, D), S, L.cache_past,
+                                   L.evict, L.past, st[0], st[1]) == 0
+    rows = [np.zeros((B, H, S, D), np.uint8) for _ in range(2)]
+    for t, new in enumerate((kn, vn)):
+        for b in range(B):
+            for h in range(H):
+                rows[t][b, h] = _codes(orc, x, t, h, new[b, h]).view(np.uint8)
+    k2, v2 = base.copy(), base.copy()
+    st2 = [np.zeros_like(st[0]) for _ in range(2)]
+    assert orc.kv_window_append(k2, v2, rows[0], rows[1], L.cache_past, L.evict, st2[0], st2[1],
+                                elem_bits=8) == 0
+    np.testing.assert_array_equal(k1, k2)
+    np.testing.assert_array_equal(v1, v2)
