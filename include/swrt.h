@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define SWRT_ABI_VERSION 7
+#define SWRT_ABI_VERSION 8
 
 /* synchronous status codes */
 #define SWRT_OK 0
@@ -400,6 +400,13 @@ int swrt_kv_decode_step(int n_window_layers, void *const *win_k_caches,
  * KV": affine INT8 / UINT8 codes with FLOAT scales and scalar parameters on
  * append, ties rounded to even, codes saturated).
  *
+ * Per-channel parameters (same pull request, comment-only follow-up: the
+ * quantized cache's per-channel scale has shape (kv_num_heads, 1, head_size),
+ * its singleton dimension flattened): element e of a row of KV head h takes
+ * scale channel_scale[t][h * head_dim + e] and zero point
+ * channel_zero_point[t][h * head_dim + e] (t = 0 for K, 1 for V) instead of
+ * the scalar when that table is given.
+ *
  * Every new row (head_dim elements of in_type) is read as binary32. A K row
  * (never a V row) is rotated when tables are given: each pair (x0, x1) --
  * elements (j, j + rotary_dim/2), or (2j, 2j+1) when interleaved -- becomes
@@ -410,7 +417,10 @@ int swrt_kv_decode_step(int n_window_layers, void *const *win_k_caches,
  * nearest even (overflow to infinity); any NaN of a float type as its
  * positive canonical quiet NaN (0x7FC00000 / 0x7E00 / 0x7FC0); INT8 / UINT8 as
  *   clamp(round_half_even(y / scale) + zero_point, code range),
- * NaN -> zero_point, with y / scale the correctly rounded binary32 quotient.
+ * NaN -> zero_point (saturated into the code range), with y / scale the
+ * correctly rounded binary32 quotient; FP8_E4M3 (the OCP float8 E4M3 format,
+ * "float8e4m3fn") as the code of y / scale rounded to nearest even, finite
+ * values past 448 and infinities saturating to +-448, NaN as 0x7F.
  * The positions are absolute: past length + s on the windowed path,
  * write_indices[b] + s (before any circular wrap) on TensorScatter.
  * ---------------------------------------------------------------------------
@@ -420,6 +430,7 @@ int swrt_kv_decode_step(int n_window_layers, void *const *win_k_caches,
 #define SWRT_XF_BF16 3
 #define SWRT_XF_INT8 4
 #define SWRT_XF_UINT8 5
+#define SWRT_XF_FP8_E4M3 10  /* cache element type of the row transform only */
 
 typedef struct swrt_row_transform {
   int in_type;             /* new rows: SWRT_XF_F32, _F16 or _BF16 */
@@ -430,8 +441,17 @@ typedef struct swrt_row_transform {
   int64_t max_position;    /* rows of the tables, >= 1 when rotating */
   int64_t rotary_dim;      /* even, 2 .. head_dim when rotating */
   int interleaved;         /* 0: pairs (j, j + rotary_dim/2); 1: (2j, 2j+1) */
-  float scale[2];          /* K, V: positive, finite (integer out_type) */
-  int32_t zero_point[2];   /* K, V: inside the code range (integer out_type) */
+  float scale[2];          /* K, V: positive, finite (INT8 / UINT8 / FP8 out_type) */
+  int32_t zero_point[2];   /* K, V: inside the code range (INT8 / UINT8), 0 (FP8) */
+  /* per-channel parameters, device [kv_heads, head_dim] (K, V), or NULL for
+     the scalar: scales for INT8 / UINT8 / FP8 out_type, zero points for INT8 /
+     UINT8; 4-byte aligned. Their values are data, not checked: the formulas
+     apply as written (meaningful codes need positive finite scales and zero
+     points inside the code range). kv_heads is the call's; for TensorScatter
+     the cache's dimension 1 of rank 4 ([B, H, M, D]), 1 for rank 3, and no
+     tables for a higher rank. */
+  const float *channel_scale[2];
+  const int32_t *channel_zero_point[2];
 } swrt_row_transform;
 
 /*

@@ -79,7 +79,7 @@ MODE_LINEAR, MODE_CIRCULAR = 0, 1
 PHASE_STAGE, PHASE_COMMIT, PHASE_ALL = 1, 2, 3
 MAX_LAYERS = 32
 MAX_BATCHED = 64
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 _PHASES = {"stage": PHASE_STAGE, "commit": PHASE_COMMIT, "all": PHASE_ALL}
 _MODES = {"linear": MODE_LINEAR, "circular": MODE_CIRCULAR}
@@ -97,7 +97,7 @@ _lib: ctypes.CDLL | None = None
 
 # element types of a row transform (include/swrt.h SWRT_XF_*)
 XF_TYPES = {torch.float32: 1, torch.float16: 2, torch.bfloat16: 3, torch.int8: 4,
-            torch.uint8: 5}
+            torch.uint8: 5, torch.float8_e4m3fn: 10}
 
 
 class RowTransform(ctypes.Structure):
@@ -106,7 +106,8 @@ class RowTransform(ctypes.Structure):
                 ("cos_table", ctypes.c_void_p), ("sin_table", ctypes.c_void_p),
                 ("max_position", ctypes.c_int64), ("rotary_dim", ctypes.c_int64),
                 ("interleaved", ctypes.c_int), ("scale", ctypes.c_float * 2),
-                ("zero_point", ctypes.c_int32 * 2)]
+                ("zero_point", ctypes.c_int32 * 2), ("channel_scale", ctypes.c_void_p * 2),
+                ("channel_zero_point", ctypes.c_void_p * 2)]
 
 
 @dataclass
@@ -114,9 +115,13 @@ class Transform:
     """Row transform of a fused append: K rows turn by RoPE at their absolute
     position (when ``cos``/``sin`` are given: float32 [max_position,
     rotary_dim / 2] device tables), then every element is written in the
-    cache's dtype: float32 / float16 / bfloat16 rounded to nearest even, or an
+    cache's dtype: float32 / float16 / bfloat16 rounded to nearest even, an
     int8 / uint8 affine code round(y / scale) + zero_point (ties to even,
-    saturated) with the K or V scale and zero point."""
+    saturated), or a float8_e4m3fn code of y / scale (nearest even,
+    saturating at +-448), with the K or V scale and zero point -- the scalars,
+    or per channel the [kv_heads, head_dim] device tables
+    ``k_channel_scale`` / ``v_channel_scale`` (float32) and
+    ``k_channel_zero_point`` / ``v_channel_zero_point`` (int32)."""
     cos: torch.Tensor | None = None
     sin: torch.Tensor | None = None
     interleaved: bool = False
@@ -124,13 +129,22 @@ class Transform:
     v_scale: float = 1.0
     k_zero_point: int = 0
     v_zero_point: int = 0
+    k_channel_scale: torch.Tensor | None = None
+    v_channel_scale: torch.Tensor | None = None
+    k_channel_zero_point: torch.Tensor | None = None
+    v_channel_zero_point: torch.Tensor | None = None
 
-    def c(self, in_dtype: torch.dtype, out_dtype: torch.dtype) -> RowTransform:
+    def channel_tables(self) -> tuple:
+        return (self.k_channel_scale, self.v_channel_scale, self.k_channel_zero_point,
+                self.v_channel_zero_point)
+
+    def c(self, in_dtype: torch.dtype, out_dtype: torch.dtype, heads: int | None = None,
+          head_dim: int | None = None) -> RowTransform:
         if in_dtype not in (torch.float32, torch.float16, torch.bfloat16):
             raise SwrtError("new rows must be float32, float16 or bfloat16")
         if out_dtype not in XF_TYPES:
-            raise SwrtError("caches of a fused append must be float32, float16, bfloat16, int8 "
-                            "or uint8")
+            raise SwrtError("caches of a fused append must be float32, float16, bfloat16, int8, "
+                            "uint8 or float8_e4m3fn")
         x = RowTransform()
         x.in_type, x.out_type = XF_TYPES[in_dtype], XF_TYPES[out_dtype]
         if (self.cos is None) != (self.sin is None):
@@ -146,10 +160,23 @@ class Transform:
         x.interleaved = int(self.interleaved)
         x.scale[0], x.scale[1] = self.k_scale, self.v_scale
         x.zero_point[0], x.zero_point[1] = self.k_zero_point, self.v_zero_point
+        for k, (sc, zp) in enumerate(((self.k_channel_scale, self.k_channel_zero_point),
+                                      (self.v_channel_scale, self.v_channel_zero_point))):
+            for name, t, dt in (("channel scale", sc, torch.float32),
+                                ("channel zero point", zp, torch.int32)):
+                if t is None:
+                    continue
+                _contig(name, t)
+                if t.dtype != dt or (heads is not None and tuple(t.shape) != (heads, head_dim)):
+                    raise SwrtError(f"{name} tables must be {dt} [kv_heads, head_dim]"
+                                    + (f" = [{heads}, {head_dim}]" if heads is not None else ""))
+            x.channel_scale[k] = None if sc is None else sc.data_ptr()
+            x.channel_zero_point[k] = None if zp is None else zp.data_ptr()
         return x
 
     def tables(self) -> tuple:
-        return (self.cos, self.sin)
+        """Every device tensor the transform reads."""
+        return (self.cos, self.sin, *self.channel_tables())
 
 
 def library_path() -> str:
@@ -657,7 +684,7 @@ def prepare_kv_window_append_xf(k_caches, v_caches, k_news, v_news, cache_past_l
     n, B, H, C, D, S, strides = _check_layers(k_caches, v_caches, k_news, v_news,
                                               new_dtype=k_news[0].dtype)
     kc = k_caches[0]
-    x = xf.c(k_news[0].dtype, kc.dtype)
+    x = xf.c(k_news[0].dtype, kc.dtype, H, D)
     everything = [*k_caches, *v_caches, *k_news, *v_news, cache_past_lens, evict_counts,
                   past_lens, flags, *xf.tables()]
     if S > 1:
@@ -705,7 +732,7 @@ def prepare_kv_window_stage_step_xf(k_caches, v_caches, k_news, v_news, seqlens_
         raise SwrtError("a staged step appends S >= 2 rows")
     _check_seqlens(seqlens_k, B)
     kc = k_caches[0]
-    x = xf.c(k_news[0].dtype, kc.dtype)
+    x = xf.c(k_news[0].dtype, kc.dtype, H, D)
     _check_stagings(k_stagings, v_stagings, n, B, H, C, S, D, kc.dtype)
     dev = _device_of(*k_caches, *v_caches, *k_news, *v_news, seqlens_k, *k_stagings,
                      *v_stagings, flags, *xf.tables())
@@ -744,7 +771,7 @@ def prepare_tensor_scatter_xf(pasts: Sequence[torch.Tensor], updates: Sequence[t
         raise SwrtError(f"need 1..{MAX_BATCHED} (past, update, tensor) triples")
     p0, u0 = pasts[0], updates[0]
     presents = [torch.empty_like(p) for p in pasts] if outs is None else list(outs)
-    x = xf.c(u0.dtype, p0.dtype)
+    x = xf.c(u0.dtype, p0.dtype, p0.shape[1] if p0.dim() == 4 else 1, p0.shape[-1])
     if p0.dim() < 3:
         raise SwrtError("a fused TensorScatter needs rank >= 3 ([..., M, head_dim])")
     if u0.dim() != p0.dim() or u0.shape[:-2] != p0.shape[:-2] or u0.shape[-1] != p0.shape[-1]:
@@ -793,7 +820,7 @@ def prepare_kv_decode_step_xf(win_k, win_v, win_k_new, win_v_new, seqlens_k, ful
             not 0 <= nf <= MAX_BATCHED // 2:
         raise SwrtError(f"need 0..{MAX_BATCHED // 2} full layers, each with K, V and new rows")
     cdt, ndt = win_k[0].dtype, win_k_new[0].dtype
-    x = xf.c(ndt, cdt)
+    x = xf.c(ndt, cdt, H, D)
     M = full_k[0].shape[2] if nf else 1
     for c in (*full_k, *full_v):
         _contig("full cache", c)

@@ -82,6 +82,7 @@ __global__ __launch_bounds__(BLOCK) void decode_step_kernel(DecodeArgs a) {
     w.Lp = r.Lp;
     w.E = r.E;
     w.t = int(s.t);
+    w.h = s.h;
     w.pos = r.P;
     w.ok = true;
     if constexpr (XF) w.ok = positions_ok(a.wg, a.xf, s, threadIdx.x == g * (BLOCK / SPW), r.P);
@@ -93,7 +94,7 @@ __global__ __launch_bounds__(BLOCK) void decode_step_kernel(DecodeArgs a) {
     const SliceWork w = work(wb, 0);
     if (!w.ok) return;
     shift_append_slice<VEC, BLOCK, UNROLL, XF>(w.base, w.new_row, w.Lp, w.E, a.wg.row_bytes,
-                                               a.wg.row_words, &a.xf, w.t, w.pos);
+                                               a.wg.row_words, &a.xf, w.t, w.pos, w.h);
   } else {
     shift_append_group<VEC, SPW, XF>(wb * SPW, a.wg.slices, a.wg.row_bytes, a.wg.row_words, work,
                                      &a.xf);
@@ -147,12 +148,12 @@ int decode_step(int n_window_layers, void *const *win_k_caches, void *const *win
   if (window < 1 || window > capacity) return SWRT_E_INVALID_ARG;
   WindowPlan wp{};
   ScatterPlan sp{};
-  Range ranges[6 * kMaxLayers + 3 * kMaxTensors + 14];
+  Range ranges[6 * kMaxLayers + 3 * kMaxTensors + 24];
   int nr = 0;
   RowXf x{};
   int st;
   if (xf) {
-    if ((st = plan_xf(xf, head_dim, &x, ranges, &nr)) != SWRT_OK) return st;
+    if ((st = plan_xf(xf, head_dim, kv_heads, &x, ranges, &nr)) != SWRT_OK) return st;
     elem_bits = x.out_bytes * 8;
   }
   st = plan_window(n_window_layers, win_k_caches, win_v_caches, win_k_new, win_v_new,

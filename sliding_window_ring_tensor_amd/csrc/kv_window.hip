@@ -42,7 +42,7 @@ __global__ __launch_bounds__(kWinBlock) void window_in_place(WinArgs<NL> a) {
     char *base = a.cache[s.layer][s.t] + uint64_t(s.b * a.g.H + s.h) * uint64_t(a.g.C) * a.g.row_bytes;
     shift_append_slice<VEC, kWinBlock, kWinUnroll, XF>(
         base, a.nw[s.layer][s.t] + s.b * a.g.nb_b + s.h * a.g.nb_h, Lp, E, a.g.row_bytes,
-        a.g.row_words, &a.xf, int(s.t), P);
+        a.g.row_words, &a.xf, int(s.t), P, s.h);
   } else {
     constexpr uint32_t GB = kWinBlock / SPW;
     shift_append_group<VEC, SPW, XF>(
@@ -54,6 +54,7 @@ __global__ __launch_bounds__(kWinBlock) void window_in_place(WinArgs<NL> a) {
           w.E = a.g.ev[s.b];
           w.ok = lengths_ok(a.g, s, threadIdx.x == g * GB, w.Lp, w.E);
           w.t = int(s.t);
+          w.h = s.h;
           w.pos = 0;
           if constexpr (XF) {
             w.pos = a.g.past[s.b];
@@ -82,7 +83,7 @@ __global__ __launch_bounds__(kWinBlock) void window_stage(WinArgs<NL> a) {
   stage_tile<VEC, XF>(a.g, a.cache[s.layer][s.t] + bh * uint64_t(a.g.C) * a.g.row_bytes,
                       a.stage[s.layer][s.t] + bh * uint64_t(a.g.C + a.g.S) * a.g.row_bytes,
                       a.nw[s.layer][s.t] + s.b * a.g.nb_b + s.h * a.g.nb_h, Lp, tile, &a.xf,
-                      int(s.t), P);
+                      int(s.t), P, s.h);
 }
 
 template <int VEC, int NL, bool XF>
@@ -141,7 +142,7 @@ __global__ __launch_bounds__(kWinBlock) void window_stage_lengths(WinArgs<NL> a,
   stage_tile<VEC, XF>(a.g, a.cache[s.layer][s.t] + bh * uint64_t(a.g.C) * a.g.row_bytes,
                       a.stage[s.layer][s.t] + bh * uint64_t(a.g.C + a.g.S) * a.g.row_bytes,
                       a.nw[s.layer][s.t] + s.b * a.g.nb_b + s.h * a.g.nb_h, r.Lp, tile, &a.xf,
-                      int(s.t), r.P);
+                      int(s.t), r.P, s.h);
 }
 
 template <int VEC, int NL, bool XF>
@@ -239,12 +240,12 @@ int stage_step(int n_layers, void *const *k_caches, void *const *v_caches,
   if (batch < 0 || capacity < 1 || seq_len < 2) return SWRT_E_INVALID_ARG;
   if (window < 1 || window > capacity) return SWRT_E_INVALID_ARG;
   WindowPlan p{};
-  Range ranges[6 * kMaxLayers + 12];
+  Range ranges[6 * kMaxLayers + 20];
   int nr = 0;
   RowXf x{};
   int st;
   if (xf) {
-    if ((st = plan_xf(xf, head_dim, &x, ranges, &nr)) != SWRT_OK) return st;
+    if ((st = plan_xf(xf, head_dim, kv_heads, &x, ranges, &nr)) != SWRT_OK) return st;
     elem_bits = x.out_bytes * 8;
   }
   st = plan_window(n_layers, k_caches, v_caches, k_news, v_news, new_strides, k_stagings,
@@ -305,12 +306,12 @@ int window_append(int n_layers, void *const *k_caches, void *const *v_caches,
                   unsigned phase, const swrt_row_transform *xf, const int64_t *past_lens,
                   uint32_t *d_flags, void *stream) {
   WindowPlan p;
-  Range ranges[6 * kMaxLayers + 8];
+  Range ranges[6 * kMaxLayers + 16];
   int nr = 0;
   RowXf x{};
   int st;
   if (xf) {
-    if ((st = plan_xf(xf, head_dim, &x, ranges, &nr)) != SWRT_OK) return st;
+    if ((st = plan_xf(xf, head_dim, kv_heads, &x, ranges, &nr)) != SWRT_OK) return st;
     elem_bits = x.out_bytes * 8;
     // in place, the appended row is spread over one workgroup's lanes
     if (seq_len == 1 && head_dim > kXfLaneElems * kWinBlock) return SWRT_E_UNSUPPORTED;

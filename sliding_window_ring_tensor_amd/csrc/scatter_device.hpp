@@ -155,8 +155,11 @@ __device__ __forceinline__ void scatter_in_place_tile(const ScatterGeom &g, char
     int64_t j = w + s;
     if (g.circular && j >= g.M) j -= g.M;
     if (w >= 0) {
-      if constexpr (XF)
-        v[u] = xf_word<VEC>(*xf, t, update_ + uint64_t(row) * g.in_row_bytes, tb.raw[k] + s, col);
+      if constexpr (XF) {
+        const uint32_t h = xf_channels(*xf) ? o % uint32_t(xf->heads) : 0;  // KV head of the row
+        v[u] = xf_word<VEC>(*xf, t, h, update_ + uint64_t(row) * g.in_row_bytes, tb.raw[k] + s,
+                            col);
+      }
       st(present + (int64_t(o) * g.M + j) * g.words_per_row + col, v[u]);
     }
   }
@@ -191,7 +194,8 @@ __device__ __forceinline__ void scatter_out_of_place_tile(const ScatterGeom &g, 
       if (s >= g.S) s = -1;
     }
     if constexpr (XF) {
-      v[u] = s >= 0 ? xf_word<VEC>(*xf, t, update_ + (uint64_t(o) * g.S + s) * g.in_row_bytes,
+      const uint32_t h = xf_channels(*xf) ? o % uint32_t(xf->heads) : 0;  // KV head of the row
+      v[u] = s >= 0 ? xf_word<VEC>(*xf, t, h, update_ + (uint64_t(o) * g.S + s) * g.in_row_bytes,
                                    tb.raw[k] + s, col)
                     : ld(past + i);
     } else {

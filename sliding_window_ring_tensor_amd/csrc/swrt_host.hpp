@@ -80,15 +80,19 @@ int plan_scatter(int n_tensors, void *const *presents, const void *const *pasts,
 // tile_words: words per workgroup tile of the kernel that will run the plan
 int finish_scatter(ScatterPlan *p, int vec, uint32_t tile_words);
 
-// Check a row transform for rows of head_dim elements and fill the device
-// form; the tables join the read-only ranges of the call.
-inline int plan_xf(const swrt_row_transform *t, int64_t head_dim, RowXf *x, Range *ranges,
-                   int *nr) {
+// Check a row transform for rows of head_dim elements of `heads` KV heads
+// and fill the device form; the rotary and per-channel tables join the
+// read-only ranges of the call.
+inline int plan_xf(const swrt_row_transform *t, int64_t head_dim, int64_t heads, RowXf *x,
+                   Range *ranges, int *nr) {
   const auto bytes = [](int type) {
     return type == SWRT_XF_F32 ? 4 : type == SWRT_XF_F16 || type == SWRT_XF_BF16 ? 2
-                                 : type == SWRT_XF_INT8 || type == SWRT_XF_UINT8 ? 1 : 0;
+                                 : type == SWRT_XF_INT8 || type == SWRT_XF_UINT8 ||
+                                           type == SWRT_XF_FP8_E4M3
+                                     ? 1
+                                     : 0;
   };
-  if (!t || head_dim < 0) return SWRT_E_INVALID_ARG;
+  if (!t || head_dim < 0 || heads < 0) return SWRT_E_INVALID_ARG;
   if (t->in_type != SWRT_XF_F32 && t->in_type != SWRT_XF_F16 && t->in_type != SWRT_XF_BF16)
     return SWRT_E_INVALID_ARG;
   if (bytes(t->out_type) == 0) return SWRT_E_INVALID_ARG;
@@ -113,17 +117,39 @@ inline int plan_xf(const swrt_row_transform *t, int64_t head_dim, RowXf *x, Rang
     x->half = int32_t(t->rotary_dim / 2);
     x->interleaved = t->interleaved ? 1 : 0;
   }
+  const bool fp8 = t->out_type == SWRT_XF_FP8_E4M3, affine = x->out_bytes == 1 && !fp8;
   if (x->out_bytes == 1) {
     x->lo = t->out_type == SWRT_XF_INT8 ? -128 : 0;
     x->hi = t->out_type == SWRT_XF_INT8 ? 127 : 255;
     for (int k = 0; k < 2; ++k) {
       const float sc = t->scale[k];
       if (!(sc > 0.0f) || sc > 3.4028235e38f) return SWRT_E_INVALID_ARG;  // positive, finite
-      if (t->zero_point[k] < x->lo || t->zero_point[k] > x->hi) return SWRT_E_INVALID_ARG;
+      if (affine ? (t->zero_point[k] < x->lo || t->zero_point[k] > x->hi) : t->zero_point[k] != 0)
+        return SWRT_E_INVALID_ARG;
       x->scale[k] = sc;
       x->zero[k] = t->zero_point[k];
     }
   }
+  // per-channel tables [heads, head_dim]: scales of the byte targets, zero
+  // points of the affine ones; their values are data (not checked here)
+  int64_t tb = 0;
+  const bool any = t->channel_scale[0] || t->channel_scale[1] || t->channel_zero_point[0] ||
+                   t->channel_zero_point[1];
+  if (any && (!mul_ok(heads, head_dim * 4, &tb) || heads > INT32_MAX || head_dim > INT32_MAX))
+    return SWRT_E_UNSUPPORTED;
+  for (int k = 0; k < 2; ++k) {
+    if ((t->channel_scale[k] && x->out_bytes != 1) || (t->channel_zero_point[k] && !affine))
+      return SWRT_E_INVALID_ARG;
+    if (addr_of(t->channel_scale[k]) % 4 || addr_of(t->channel_zero_point[k]) % 4)
+      return SWRT_E_INVALID_ARG;
+    if (t->channel_scale[k]) ranges[(*nr)++] = range(t->channel_scale[k], uint64_t(tb), false);
+    if (t->channel_zero_point[k])
+      ranges[(*nr)++] = range(t->channel_zero_point[k], uint64_t(tb), false);
+    x->cs[k] = t->channel_scale[k];
+    x->cz[k] = t->channel_zero_point[k];
+  }
+  x->d = int32_t(head_dim);
+  x->heads = int32_t(heads > 0 ? heads : 1);
   return SWRT_OK;
 }
 

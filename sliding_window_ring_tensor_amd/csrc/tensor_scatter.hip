@@ -82,14 +82,19 @@ int scatter(int n_tensors, void *const *presents, const void *const *pasts,
             int rank, int axis, int64_t seq_len, int mode, int elem_bits,
             const swrt_row_transform *xf, const int *tensors, uint32_t *d_flags, void *stream) {
   ScatterPlan p;
-  Range ranges[3 * kMaxTensors + 5];
+  Range ranges[3 * kMaxTensors + 13];
   int nr = 0;
   RowXf x{};
   uint64_t vmask = 0;
   int st;
   if (xf) {
     if (!shape || rank < 3 || rank > SWRT_MAX_RANK) return SWRT_E_INVALID_ARG;
-    if ((st = plan_xf(xf, shape[rank - 1], &x, ranges, &nr)) != SWRT_OK) return st;
+    // per-channel tables: [shape[1], head_dim] of a [B, H, M, D] cache, one row for rank 3
+    if (rank > 4 && (xf->channel_scale[0] || xf->channel_scale[1] || xf->channel_zero_point[0] ||
+                     xf->channel_zero_point[1]))
+      return SWRT_E_INVALID_ARG;
+    if ((st = plan_xf(xf, shape[rank - 1], rank == 4 ? shape[1] : 1, &x, ranges, &nr)) != SWRT_OK)
+      return st;
     if (n_tensors > 0 && !tensors) return SWRT_E_INVALID_ARG;
     for (int t = 0; t < n_tensors && t < kMaxTensors; ++t) {
       if (tensors[t] != 0 && tensors[t] != 1) return SWRT_E_INVALID_ARG;

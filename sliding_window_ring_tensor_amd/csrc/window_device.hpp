@@ -153,7 +153,7 @@ template <int VEC, int BLOCK = kWinBlock, int UNROLL = kWinUnroll, bool XF = fal
 __device__ __forceinline__ void shift_append_slice(char *base, const char *new_row, int64_t Lp,
                                                    int64_t E, uint64_t row_bytes,
                                                    uint32_t row_words, const RowXf *xf = nullptr,
-                                                   int t = 0, int64_t pos = 0) {
+                                                   int t = 0, int64_t pos = 0, uint32_t h = 0) {
   using W = typename Word<VEC>::T;
   W *dst = reinterpret_cast<W *>(base);
   // The new row lives in its own buffer: fetch it first so its latency
@@ -187,7 +187,7 @@ __device__ __forceinline__ void shift_append_slice(char *base, const char *new_r
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u) v[u] = ld(src + min(c0 + u * BLOCK + threadIdx.x, n - 1));
       if constexpr (XF) {
-        if (c0 == 0) xf_lanes_load(xl, *xf, t, new_row, pos, threadIdx.x, BLOCK, D);
+        if (c0 == 0) xf_lanes_load(xl, *xf, t, h, new_row, pos, threadIdx.x, BLOCK, D);
         xf_lanes_hold(xl);
       }
       __syncthreads();  // every old value of this tile is in registers
@@ -210,7 +210,7 @@ __device__ __forceinline__ void shift_append_slice(char *base, const char *new_r
   }
   if (!appended) {  // no shift, or a row wider than one pass: after every load
     if (row_in_one_pass) {
-      if constexpr (XF) xf_lanes_load(xl, *xf, t, new_row, pos, threadIdx.x, BLOCK, D);
+      if constexpr (XF) xf_lanes_load(xl, *xf, t, h, new_row, pos, threadIdx.x, BLOCK, D);
       append();
     } else {
       for (uint32_t i = threadIdx.x; i < row_words; i += BLOCK) st(adst + i, ld(nsrc + i));
@@ -242,6 +242,7 @@ struct SliceWork {
   int64_t Lp, E;
   int64_t pos;          // its absolute position (fused append)
   int t;                // 0 = K, 1 = V
+  uint32_t h;           // its KV head (per-channel parameters)
   bool ok;
 };
 
@@ -290,7 +291,7 @@ __device__ __forceinline__ void shift_append_group(uint32_t first_slice, uint32_
 #pragma unroll
         for (int u = 0; u < kGroupUnroll; ++u) v[u] = ld(src + min(u * GB + lid, n - 1));
       }
-      xf_lanes_load(xl, *xf, w.t, w.new_row, w.pos, lid, GB, D);
+      xf_lanes_load(xl, *xf, w.t, w.h, w.new_row, w.pos, lid, GB, D);
       xf_lanes_hold(xl);
     } else {
       nv = ld(nsrc);
@@ -340,7 +341,7 @@ template <int VEC, bool XF = false>
 __device__ __forceinline__ void stage_tile(const WindowGeom &g, const char *cache_slice,
                                            char *stage_slice, const char *new_rows, int64_t Lp,
                                            uint32_t tile, const RowXf *xf = nullptr, int t = 0,
-                                           int64_t P = 0) {
+                                           int64_t P = 0, uint32_t h = 0) {
   using W = typename Word<VEC>::T;
   const uint32_t n_seed = uint32_t(Lp) * g.row_words;
   const uint32_t n = uint32_t(Lp + g.S) * g.row_words;
@@ -354,7 +355,8 @@ __device__ __forceinline__ void stage_tile(const WindowGeom &g, const char *cach
     const uint32_t i = min(i0 + u * kWinBlock + threadIdx.x, n - 1);  // tail lanes repeat the last word
     const uint32_t j = i < n_seed ? 0 : i - n_seed, r = g.by_row.div(j), c = j - r * g.row_words;
     if constexpr (XF) {
-      v[u] = i < n_seed ? ld(cache + i) : xf_word<VEC>(*xf, t, new_rows + int64_t(r) * g.nb_s, P + r, c);
+      v[u] = i < n_seed ? ld(cache + i)
+                        : xf_word<VEC>(*xf, t, h, new_rows + int64_t(r) * g.nb_s, P + r, c);
     } else {
       const W *p = i < n_seed ? cache + i : reinterpret_cast<const W *>(new_rows + int64_t(r) * g.nb_s) + c;
       v[u] = ld(p);

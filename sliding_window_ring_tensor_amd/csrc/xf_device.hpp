@@ -5,10 +5,13 @@
 // request "GQA support sliding_window_cache", "Summary of Changes": the append
 // uses the cache-relative offset, RoPE the absolute position, bounded by the
 // tables' own length and not by the capacity); then every element is written
-// in the cache's type: f32, f16 or bf16 rounded to nearest even, or an affine
-// INT8 / UINT8 code with the tensor's scalar scale and zero point, rounded
-// half to even and saturated (onnx-light how-to "Persistent input/output
-// feedback", section "Optional heterogeneous paged KV").
+// in the cache's type: f32, f16 or bf16 rounded to nearest even, an affine
+// INT8 / UINT8 code rounded half to even and saturated (onnx-light how-to
+// "Persistent input/output feedback", section "Optional heterogeneous paged
+// KV"), or an OCP FP8 E4M3 code of y / scale (nearest even, saturating at
+// +-448). Scales and zero points are the tensor's scalars or, per channel,
+// entry h * head_dim + e of [kv_heads, head_dim] tables (the pull request's
+// per-channel shape (kv_num_heads, 1, head_size) with the singleton dropped).
 //
 // Each pair (x0, x1) -- elements (j, j + rotary_dim/2), or (2j, 2j+1) when
 // interleaved -- turns by the angle of table row pos, column j:
@@ -36,10 +39,29 @@ struct RowXf {
   int32_t interleaved;
   int32_t in_type, out_type;    // SWRT_XF_*
   int32_t in_bytes, out_bytes;  // element sizes
-  float scale[2];               // K, V (integer codes)
+  float scale[2];               // K, V (integer and fp8 codes)
   int32_t zero[2];
   int32_t lo, hi;               // code range
+  const float *cs[2];           // per-channel scales [heads, d] (K, V), or null
+  const int32_t *cz[2];         // per-channel zero points [heads, d], or null
+  int32_t d;                    // elements per row: the tables' row length
+  int32_t heads;                // rows of the tables (TensorScatter: prefix index mod heads)
 };
+
+// any per-channel table (a uniform test on the kernel arguments)
+__device__ __forceinline__ bool xf_channels(const RowXf &x) {
+  return x.cs[0] || x.cs[1] || x.cz[0] || x.cz[1];
+}
+
+// the scale and zero point of element e of a row of KV head h, tensor t
+__device__ __forceinline__ void xf_params(const RowXf &x, int t, uint32_t h, uint32_t e, float &sc,
+                                          int32_t &zp) {
+  const float *cs = t ? x.cs[1] : x.cs[0];
+  const int32_t *cz = t ? x.cz[1] : x.cz[0];
+  const uint32_t k = h * uint32_t(x.d) + e;
+  sc = cs ? cs[k] : (t ? x.scale[1] : x.scale[0]);
+  zp = cz ? cz[k] : (t ? x.zero[1] : x.zero[0]);
+}
 
 // positions [p0, p0 + n) all have table rows (always, without rotation)
 __device__ __forceinline__ bool xf_positions_ok(const RowXf &x, int64_t p0, int64_t n) {
@@ -59,15 +81,37 @@ __device__ __forceinline__ uint16_t xf_f16(float f) {
   return __builtin_bit_cast(uint16_t, _Float16(f));  // hardware conversion, nearest even
 }
 
+// NaN takes the zero point, itself saturated into the code range (a
+// per-channel zero point is data the host never sees)
 __device__ __forceinline__ int32_t xf_code_of(const RowXf &x, float scale, int32_t zero, float y) {
-  if (y != y) return zero;
+  if (y != y) return min(max(zero, x.lo), x.hi);
   float q = __builtin_rintf(y / scale) + float(zero);
   q = fminf(fmaxf(q, float(x.lo)), float(x.hi));
   return int32_t(q);
 }
 
-__device__ __forceinline__ int32_t xf_code(const RowXf &x, int t, float y) {
-  return xf_code_of(x, t ? x.scale[1] : x.scale[0], t ? x.zero[1] : x.zero[0], y);
+// OCP FP8 E4M3 (float8e4m3fn) bits of a binary32 value: nearest even; finite
+// values past 448 and infinities saturate to +-448 (0x7E / 0xFE), NaN is 0x7F.
+// Exponent bias 7, three fraction bits; below 2^-6 the value counts units of
+// 2^-9 (subnormals; eight units is the smallest normal, the same bits).
+__device__ __forceinline__ uint8_t xf_fp8(float f) {
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t sign = (u >> 24) & 0x80u, a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return 0x7F;                        // NaN
+  if (a >= 0x43E00000u) return uint8_t(sign | 0x7Eu);      // >= 448 (and inf)
+  if (a < 0x3C800000u) {                                   // < 2^-6: units of 2^-9
+    const float q = __builtin_rintf(__uint_as_float(a) * 512.0f);  // exact scaling
+    return uint8_t(sign | uint32_t(q));
+  }
+  // normal: keep 3 fraction bits, ties to even (a carry moves the exponent)
+  const uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;
+  return uint8_t(sign | (r - (120u << 3)));  // rebias 127 -> 7
+}
+
+// one output byte of an integer or fp8 target
+__device__ __forceinline__ uint8_t xf_byte(const RowXf &x, float sc, int32_t zp, float y) {
+  if (x.out_type == SWRT_XF_FP8_E4M3) return xf_fp8(y / sc);
+  return uint8_t(xf_code_of(x, sc, zp, y));  // two's complement bits for INT8
 }
 
 // the input element e of a row as float, the input type fixed at compile time
@@ -116,9 +160,9 @@ __device__ __forceinline__ float xf_rotate(const RowXf &x, bool rot, uint32_t e,
 }
 
 template <int VEC, int IN, int OB, bool ROT>
-__device__ __forceinline__ typename Word<VEC>::T xf_word_of(const RowXf &x, int t, const char *row,
-                                                            const float *cr, const float *sr,
-                                                            uint32_t i) {
+__device__ __forceinline__ typename Word<VEC>::T xf_word_of(const RowXf &x, int t, uint32_t h,
+                                                            const char *row, const float *cr,
+                                                            const float *sr, uint32_t i) {
   using W = typename Word<VEC>::T;
   constexpr int N = VEC / OB;  // elements in the word
   uint8_t b[VEC] = {};
@@ -151,7 +195,10 @@ __device__ __forceinline__ typename Word<VEC>::T xf_word_of(const RowXf &x, int 
         const uint16_t h = x.out_type == SWRT_XF_BF16 ? xf_bf16(v) : xf_f16(v);
         __builtin_memcpy(b + 2 * k, &h, 2);
       } else {
-        b[k] = uint8_t(xf_code(x, t, v));  // two's complement bits for INT8
+        float sc;
+        int32_t zp;
+        xf_params(x, t, h, i * N + k, sc, zp);
+        b[k] = xf_byte(x, sc, zp, v);
       }
     }
   }
@@ -161,28 +208,30 @@ __device__ __forceinline__ typename Word<VEC>::T xf_word_of(const RowXf &x, int 
 }
 
 template <int VEC, int IN>
-__device__ __forceinline__ typename Word<VEC>::T xf_word_in(const RowXf &x, int t, const char *row,
-                                                            int64_t pos, uint32_t i) {
+__device__ __forceinline__ typename Word<VEC>::T xf_word_in(const RowXf &x, int t, uint32_t h,
+                                                            const char *row, int64_t pos,
+                                                            uint32_t i) {
   if (t == 0 && x.cos) {
     const float *cr = x.cos + pos * x.half, *sr = x.sin + pos * x.half;
-    if (x.out_bytes == 1) return xf_word_of<VEC, IN, 1, true>(x, t, row, cr, sr, i);
-    if (x.out_bytes == 2) return xf_word_of<VEC, IN, 2, true>(x, t, row, cr, sr, i);
-    return xf_word_of<VEC, IN, 4, true>(x, t, row, cr, sr, i);
+    if (x.out_bytes == 1) return xf_word_of<VEC, IN, 1, true>(x, t, h, row, cr, sr, i);
+    if (x.out_bytes == 2) return xf_word_of<VEC, IN, 2, true>(x, t, h, row, cr, sr, i);
+    return xf_word_of<VEC, IN, 4, true>(x, t, h, row, cr, sr, i);
   }
-  if (x.out_bytes == 1) return xf_word_of<VEC, IN, 1, false>(x, t, row, nullptr, nullptr, i);
-  if (x.out_bytes == 2) return xf_word_of<VEC, IN, 2, false>(x, t, row, nullptr, nullptr, i);
-  return xf_word_of<VEC, IN, 4, false>(x, t, row, nullptr, nullptr, i);
+  if (x.out_bytes == 1) return xf_word_of<VEC, IN, 1, false>(x, t, h, row, nullptr, nullptr, i);
+  if (x.out_bytes == 2) return xf_word_of<VEC, IN, 2, false>(x, t, h, row, nullptr, nullptr, i);
+  return xf_word_of<VEC, IN, 4, false>(x, t, h, row, nullptr, nullptr, i);
 }
 
-// Word i (VEC bytes of out_type elements) of the transform of `row`, tensor t
-// (0 = K, rotated when tables are given; 1 = V) at absolute position pos.
-// The cache's element alignment makes VEC a multiple of out_bytes.
+// Word i (VEC bytes of out_type elements) of the transform of `row` of KV head
+// h, tensor t (0 = K, rotated when tables are given; 1 = V) at absolute
+// position pos. The cache's element alignment makes VEC a multiple of
+// out_bytes.
 template <int VEC>
-__device__ __forceinline__ typename Word<VEC>::T xf_word(const RowXf &x, int t, const char *row,
-                                                         int64_t pos, uint32_t i) {
-  if (x.in_type == SWRT_XF_F32) return xf_word_in<VEC, SWRT_XF_F32>(x, t, row, pos, i);
-  if (x.in_type == SWRT_XF_BF16) return xf_word_in<VEC, SWRT_XF_BF16>(x, t, row, pos, i);
-  return xf_word_in<VEC, SWRT_XF_F16>(x, t, row, pos, i);
+__device__ __forceinline__ typename Word<VEC>::T xf_word(const RowXf &x, int t, uint32_t h,
+                                                         const char *row, int64_t pos, uint32_t i) {
+  if (x.in_type == SWRT_XF_F32) return xf_word_in<VEC, SWRT_XF_F32>(x, t, h, row, pos, i);
+  if (x.in_type == SWRT_XF_BF16) return xf_word_in<VEC, SWRT_XF_BF16>(x, t, h, row, pos, i);
+  return xf_word_in<VEC, SWRT_XF_F16>(x, t, h, row, pos, i);
 }
 
 // ---------------------------------------------------------------------------
@@ -199,15 +248,16 @@ constexpr int kXfLaneElems = 8;
 struct XfLanes {
   uint32_t x[kXfLaneElems], p[kXfLaneElems];  // raw bits of the element and its partner
   float c[kXfLaneElems], s[kXfLaneElems];     // its table entries (rotated K only)
-  float scale;                                // the tensor's affine parameters
-  int32_t zero;
+  float scale[kXfLaneElems];                  // its scale and zero point (byte targets)
+  int32_t zero[kXfLaneElems];
 };
 
 template <int IN>
-__device__ __forceinline__ void xf_lane_load_one(XfLanes &l, int k, const RowXf &x, bool rot,
-                                                 const char *row, const float *cr,
-                                                 const float *sr, uint32_t e) {
+__device__ __forceinline__ void xf_lane_load_one(XfLanes &l, int k, const RowXf &x, int t,
+                                                 uint32_t h, bool rot, const char *row,
+                                                 const float *cr, const float *sr, uint32_t e) {
   l.x[k] = xf_raw_t<IN>(row, e);
+  if (x.out_bytes == 1) xf_params(x, t, h, e, l.scale[k], l.zero[k]);
   l.p[k] = 0;
   l.c[k] = l.s[k] = 0.0f;
   if (rot) {  // an unrotated element loads a pair it will not use
@@ -221,39 +271,41 @@ __device__ __forceinline__ void xf_lane_load_one(XfLanes &l, int k, const RowXf 
 }
 
 template <int IN>
-__device__ __forceinline__ void xf_lanes_load_t(XfLanes &l, const RowXf &x, bool rot,
-                                                const char *row, const float *cr,
+__device__ __forceinline__ void xf_lanes_load_t(XfLanes &l, const RowXf &x, int t, uint32_t h,
+                                                bool rot, const char *row, const float *cr,
                                                 const float *sr, uint32_t lane, uint32_t n,
                                                 uint32_t D, uint32_t m) {
 #pragma unroll
-  for (int k = 0; k < kXfLaneElems; ++k) l.x[k] = l.p[k] = 0, l.c[k] = l.s[k] = 0.0f;
+  for (int k = 0; k < kXfLaneElems; ++k) {
+    l.x[k] = l.p[k] = 0, l.c[k] = l.s[k] = 0.0f;
+    l.scale[k] = 1.0f, l.zero[k] = 0;
+  }
   if (m == 1) {  // the usual row: one element per lane, straight-line
-    xf_lane_load_one<IN>(l, 0, x, rot, row, cr, sr, min(lane, D - 1));
+    xf_lane_load_one<IN>(l, 0, x, t, h, rot, row, cr, sr, min(lane, D - 1));
     return;
   }
 #pragma unroll
   for (int k = 0; k < kXfLaneElems; ++k)
     if (uint32_t(k) < m)  // uniform
-      xf_lane_load_one<IN>(l, k, x, rot, row, cr, sr, min(lane + k * n, D - 1));
+      xf_lane_load_one<IN>(l, k, x, t, h, rot, row, cr, sr, min(lane + k * n, D - 1));
 }
 
-__device__ __forceinline__ void xf_lanes_load(XfLanes &l, const RowXf &x, int t, const char *row,
-                                              int64_t pos, uint32_t lane, uint32_t n,
-                                              uint32_t D) {
+// (t may differ between the waves of a workgroup; picking a scalar parameter
+// may then become a load, issued here with the others; per-channel
+// parameters are loads of their own)
+__device__ __forceinline__ void xf_lanes_load(XfLanes &l, const RowXf &x, int t, uint32_t h,
+                                              const char *row, int64_t pos, uint32_t lane,
+                                              uint32_t n, uint32_t D) {
   const uint32_t m = (D + n - 1) / n;  // elements per lane (uniform)
   const bool rot = t == 0 && x.cos;
   const float *cr = rot ? x.cos + pos * x.half : nullptr;
   const float *sr = rot ? x.sin + pos * x.half : nullptr;
-  // (t may differ between the waves of a workgroup; picking the parameter
-  // may then become a load, issued here with the others)
-  l.scale = t ? x.scale[1] : x.scale[0];
-  l.zero = t ? x.zero[1] : x.zero[0];
   if (x.in_type == SWRT_XF_F32)
-    xf_lanes_load_t<SWRT_XF_F32>(l, x, rot, row, cr, sr, lane, n, D, m);
+    xf_lanes_load_t<SWRT_XF_F32>(l, x, t, h, rot, row, cr, sr, lane, n, D, m);
   else if (x.in_type == SWRT_XF_BF16)
-    xf_lanes_load_t<SWRT_XF_BF16>(l, x, rot, row, cr, sr, lane, n, D, m);
+    xf_lanes_load_t<SWRT_XF_BF16>(l, x, t, h, rot, row, cr, sr, lane, n, D, m);
   else
-    xf_lanes_load_t<SWRT_XF_F16>(l, x, rot, row, cr, sr, lane, n, D, m);
+    xf_lanes_load_t<SWRT_XF_F16>(l, x, t, h, rot, row, cr, sr, lane, n, D, m);
 }
 
 // Make the loaded values live here: called after the shift's loads are
@@ -263,8 +315,8 @@ __device__ __forceinline__ void xf_lanes_load(XfLanes &l, const RowXf &x, int t,
 __device__ __forceinline__ void xf_lanes_hold(XfLanes &l) {
 #pragma unroll
   for (int k = 0; k < kXfLaneElems; ++k)
-    asm volatile("" : "+v"(l.x[k]), "+v"(l.p[k]), "+v"(l.c[k]), "+v"(l.s[k]));
-  asm volatile("" : "+v"(l.scale), "+v"(l.zero));
+    asm volatile("" : "+v"(l.x[k]), "+v"(l.p[k]), "+v"(l.c[k]), "+v"(l.s[k]), "+v"(l.scale[k]),
+                 "+v"(l.zero[k]));
 }
 
 template <int IN>
@@ -278,7 +330,7 @@ __device__ __forceinline__ void xf_lane_store_one(const XfLanes &l, int k, const
     __builtin_nontemporal_store(x.out_type == SWRT_XF_BF16 ? xf_bf16(v) : xf_f16(v),
                                 reinterpret_cast<uint16_t *>(dst) + e);
   } else {
-    __builtin_nontemporal_store(uint8_t(xf_code_of(x, l.scale, l.zero, v)),
+    __builtin_nontemporal_store(xf_byte(x, l.scale[k], l.zero[k], v),
                                 reinterpret_cast<uint8_t *>(dst) + e);
   }
 }

@@ -397,9 +397,25 @@ def test_fused_append_rejects(L):
     assert win(ok, kn=B_ + 2) == INV                                     # f32 rows misaligned
     assert win(ok) in launched and win(ok, kn=B_ + 4) in launched       # element alignment
     assert win(_xf(in_type=3, out_type=3)) in launched
+    # the fp8 target and per-channel tables [kv_heads, head_dim]
+    assert win(_xf(out_type=10, scale=(0.5, 0.25))) in launched
+    assert win(_xf(out_type=10, zp=(1, 0))) == INV                     # fp8 has no zero point
+
+    def chan(out_type=4, cs=(None, None), cz=(None, None), **kw):
+        x = _xf(out_type=out_type, **kw)
+        x.channel_scale[0], x.channel_scale[1] = cs
+        x.channel_zero_point[0], x.channel_zero_point[1] = cz
+        return x
+    tabs = (D_ + 0x4000, D_ + 0x5000)
+    assert win(chan(cs=tabs, cz=tabs)) in launched                       # int8, both tables
+    assert win(chan(out_type=10, cs=tabs)) in launched                  # fp8 scales
+    assert win(chan(out_type=10, cz=tabs)) == INV                       # fp8: no zero points
+    assert win(chan(out_type=3, cs=tabs)) == INV                        # bf16: no scales
+    assert win(chan(cs=(D_ + 0x4002, None))) == INV                     # misaligned table
+    assert win(chan(cs=(A + 64, None))) == INV                          # table inside a cache
 
     def ts(x, rank=4, tensors=(0, 1), n=2, mode=0):
-        shape = _shape(*((2, 3, 16, 8) if rank == 4 else (2, 16)))
+        shape = _shape(*{4: (2, 3, 16, 8), 3: (2, 16, 8), 2: (2, 16)}[rank])
         t = (ctypes.c_int * 2)(*tensors)
         return L.swrt_tensor_scatter_xf(n, arr(A, A + 0x1000_0000), arr(A, A + 0x1000_0000),
                                         arr(B_, B_ + 0x1000_0000), t, None, shape, rank, 2, mode,
@@ -407,6 +423,15 @@ def test_fused_append_rejects(L):
     assert ts(None) == INV and ts(ok, rank=2) == INV and ts(ok, tensors=(0, 2)) == INV
     assert ts(_xf(cos=tab, sin=tab + 0x1000, max_pos=64, rot=10)) == INV  # > head_dim 8
     assert ts(_xf()) in launched and ts(_xf(), mode=1) in launched
+    assert ts(chan(cs=tabs)) in launched and ts(chan(cs=tabs), rank=3) in launched
+
+    def ts5(x):
+        shape = _shape(2, 2, 3, 16, 8)
+        t = (ctypes.c_int * 2)(0, 1)
+        return L.swrt_tensor_scatter_xf(2, arr(A, A + 0x1000_0000), arr(A, A + 0x1000_0000),
+                                        arr(B_, B_ + 0x1000_0000), t, None, shape, 5, 2, 0,
+                                        ctypes.byref(x), None, None)
+    assert ts5(_xf()) in launched and ts5(chan(cs=tabs)) == INV         # rank 5: no tables
 
     def dec(x, nfl=1):
         return L.swrt_kv_decode_step_xf(1, arr(A), arr(A + 0x1000_0000), arr(B_),

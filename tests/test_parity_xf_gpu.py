@@ -24,10 +24,12 @@ from tests.test_parity_gpu import DEV, Guarded, flag_word, hb, say
 pytestmark = pytest.mark.gpu
 
 FLOAT_IN = [torch.float32, torch.float16, torch.bfloat16]
-OUT = [torch.float32, torch.float16, torch.bfloat16, torch.int8, torch.uint8]
+OUT = [torch.float32, torch.float16, torch.bfloat16, torch.int8, torch.uint8,
+       torch.float8_e4m3fn]
 ORC_TYPE = {torch.float32: oracle.XF_F32, torch.float16: oracle.XF_F16,
             torch.bfloat16: oracle.XF_BF16, torch.int8: oracle.XF_INT8,
-            torch.uint8: oracle.XF_UINT8}
+            torch.uint8: oracle.XF_UINT8, torch.float8_e4m3fn: oracle.XF_FP8_E4M3}
+BYTE_OUT = (torch.int8, torch.uint8, torch.float8_e4m3fn)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -64,26 +66,54 @@ def tables(positions, rot):
     return wl.rope_tables(positions, rot)
 
 
-def make_xf(rot_mode, D, positions, out, zp=(0, 0)):
-    """(device Transform, oracle Transform) for rot_mode None / 'half' / 'inter'."""
+def channel_tables(g, H, D, out, special=False):
+    """Per-channel (scales, zero points) for K and V, [H, D] each: scales of
+    2^U[-8, -3), zero points inside the code range (None for fp8 and float
+    targets). special: some entries zero, negative, NaN or huge, some zero
+    points out of range (the tables are data; both sides apply the formula)."""
+    if out not in BYTE_OUT:
+        return (None, None), (None, None)
+    sc = [(2.0 ** g.uniform(-8, -3, (H, D))).astype(np.float32) for _ in range(2)]
+    zp = [None, None]
+    if out != torch.float8_e4m3fn:
+        lo, hi = (-128, 127) if out == torch.int8 else (0, 255)
+        zp = [g.integers(lo, hi, (H, D), endpoint=True).astype(np.int32) for _ in range(2)]
+    if special:
+        for a in sc:
+            a.flat[::7] = np.float32([0.0, -0.03, np.nan, 3e38, np.inf, 1e-30, -0.0])[
+                np.arange(len(a.flat[::7])) % 7]
+        for z in zp:
+            if z is not None:
+                z.flat[::5] = np.int32([-1000, 1000, 300, -300])[np.arange(len(z.flat[::5])) % 4]
+    return tuple(sc), tuple(zp)
+
+
+def make_xf(rot_mode, D, positions, out, zp=(0, 0), channels=None):
+    """(device Transform, oracle Transform) for rot_mode None / 'half' / 'inter'.
+    channels: per-channel tables as channel_tables returns them."""
     rot = 0 if rot_mode is None else (D if rot_mode == "half" else D - 4)
     cos = sin = None
     if rot:
         cos, sin = tables(positions, rot)
     if out == torch.uint8 and zp == (0, 0):
         zp = (128, 120)
+    (ks, vs), (kz, vz) = channels if channels is not None else ((None, None), (None, None))
+    dv = lambda a: None if a is None else torch.from_numpy(a).to(DEV)  # noqa: E731
     dev = swrt.Transform(None if cos is None else cos.to(DEV), None if sin is None else sin.to(DEV),
-                         rot_mode == "inter", 0.02, 0.01, *zp)
+                         rot_mode == "inter", 0.02, 0.01, *zp, dv(ks), dv(vs), dv(kz), dv(vz))
     return dev, lambda in_dt, out_dt: oracle.Transform(
         ORC_TYPE[in_dt], ORC_TYPE[out_dt], None if cos is None else cos.numpy(),
-        None if sin is None else sin.numpy(), rot, rot_mode == "inter", (0.02, 0.01), zp)
+        None if sin is None else sin.numpy(), rot, rot_mode == "inter", (0.02, 0.01), zp,
+        (ks, vs), (kz, vz))
 
 
 def host_np(t: torch.Tensor) -> np.ndarray:
-    """A numpy array the oracle can take (bf16 as raw uint16)."""
+    """A numpy array the oracle can take (bf16 as raw uint16, fp8 as uint8)."""
     t = t.contiguous().cpu()
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view(np.uint16).copy()
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).numpy().copy()
     return t.numpy().copy()
 
 
@@ -124,6 +154,37 @@ def test_scatter_xf_every_conversion(orc, inp, out, rot_mode):
                     outs[t].check("present")
 
 
+@pytest.mark.parametrize("special", [False, True])
+@pytest.mark.parametrize("out", BYTE_OUT, ids=str)
+def test_scatter_xf_per_channel(orc, out, special):
+    """Per-channel scales (and zero points) [H, D]: rows of cache head h read
+    table row h; rank 3 caches read one row. special: zero, negative, NaN and
+    huge scales, zero points out of range -- data both sides put through the
+    same formula."""
+    say("scatter xf per channel", out, special)
+    g = wl.rng(150 + BYTE_OUT.index(out) + 10 * special)
+    for shape in ((3, 4, 40, 24), (5, 33, 16)):
+        H = shape[1] if len(shape) == 4 else 1
+        D, S = shape[-1], 3
+        ch = channel_tables(g, H, D, out, special)
+        xd, xo = make_xf("half", D, 300, out, channels=ch)
+        w = np.array([0, 17, 30, 1, 9][:shape[0]], np.int64)
+        ushape = shape[:-2] + (S, D)
+        pasts = [wl.host_payload(g, shape, out, raw_bits=True) for _ in range(2)]
+        upds = [new_rows(g, ushape, torch.float32) for _ in range(2)]
+        dp = [p.to(DEV) for p in pasts]
+        flags = flag_word()
+        swrt.tensor_scatter_xf(dp, [u.to(DEV) for u in upds], [0, 1], torch.from_numpy(w).to(DEV),
+                               xd, outs=dp, flags=flags)
+        torch.cuda.synchronize()
+        for t in range(2):
+            want = host_np(pasts[t])
+            st, f = orc.tensor_scatter_xf(xo(torch.float32, out), t, want, want, host_np(upds[t]),
+                                          w, "linear")
+            assert st == 0 and f == flags.item() == 0
+            np.testing.assert_array_equal(hb(dp[t]), want.view(np.uint8).reshape(hb(dp[t]).shape))
+
+
 def test_scatter_xf_position_range_and_linear_bounds(orc):
     g = wl.rng(11)
     B, H, M, S, D = 4, 2, 30, 2, 8
@@ -146,9 +207,10 @@ def test_scatter_xf_position_range_and_linear_bounds(orc):
 # windowed append with the transform
 # ---------------------------------------------------------------------------
 def _window_case(orc, g, B, H, C, S, D, inp, out, rot_mode, T, n_layers=1, phase_split=False,
-                 strides_bsnh=False, positions=9000, stage_step=False):
-    """stage_step: the lengths and the stage phase in one launch, then the commit."""
-    xd, xo = make_xf(rot_mode, D, positions, out)
+                 strides_bsnh=False, positions=9000, stage_step=False, channels=None):
+    """stage_step: the lengths and the stage phase in one launch, then the
+    commit. channels: per-channel tables (channel_tables)."""
+    xd, xo = make_xf(rot_mode, D, positions, out, channels=channels)
     sk = (np.asarray(T) - 1).astype(np.int32)
     lens = swrt.kv_seq_lengths(torch.from_numpy(sk).to(DEV), S, C)
     L = orc.kv_seq_lengths(sk, S, C)
@@ -243,6 +305,22 @@ def test_window_xf_stage_step(orc, out):
     assert f == swrt.FLAG_ROPE_RANGE | swrt.FLAG_BAD_SEQLEN
 
 
+@pytest.mark.parametrize("S,C", [(1, 128), (1, 16), (5, 24)], ids=str)
+@pytest.mark.parametrize("out", BYTE_OUT, ids=str)
+def test_window_xf_per_channel(orc, out, S, C):
+    """The windowed append with per-channel tables: in place (one slice per
+    workgroup, and slices sharing a workgroup at C = 16) and staged, with
+    rotation, special table entries included."""
+    say("window xf per channel", out, S, C)
+    g = wl.rng(160 + BYTE_OUT.index(out) + S + C)
+    B, H, D = 6, 4, 64
+    T = g.integers(1, 3 * C, size=B)
+    T[:2] = [C, C + 1]
+    ch = channel_tables(g, H, D, out, special=True)
+    _window_case(orc, g, B, H, C, S, D, torch.bfloat16, out, "half", T, positions=8 * C,
+                 channels=ch, n_layers=2)
+
+
 @pytest.mark.parametrize("case", ["group2", "group4", "wide_rows", "odd_words"])
 def test_window_xf_shapes(orc, case):
     """Slices shared by 2 or 4 subgroups (int8 rows of 64 and 32 bytes), rows
@@ -322,16 +400,22 @@ def test_xf_wide_rows_in_shared_workgroups(orc):
 # the one-launch decode step with the transform
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("layout", ["base", "drift"])
-@pytest.mark.parametrize("out,D", [(torch.int8, 64), (torch.bfloat16, 64), (torch.uint8, 32),
-                                   (torch.float32, 512), (torch.float16, 6)], ids=str)
-def test_decode_step_xf(orc, out, D, layout):
-    """One launch against the three fused calls and against the oracle."""
-    say("decode step xf", out, D, layout)
+@pytest.mark.parametrize("out,D,chan", [(torch.int8, 64, False), (torch.bfloat16, 64, False),
+                                        (torch.uint8, 32, False), (torch.float32, 512, False),
+                                        (torch.float16, 6, False),
+                                        (torch.float8_e4m3fn, 64, False),
+                                        (torch.int8, 64, True), (torch.uint8, 32, True),
+                                        (torch.float8_e4m3fn, 64, True)], ids=str)
+def test_decode_step_xf(orc, out, D, chan, layout):
+    """One launch against the three fused calls and against the oracle
+    (chan: per-channel scales and zero points)."""
+    say("decode step xf", out, D, chan, layout)
     g = wl.rng(61 + D)
     B, H, M, nw, nf = 12, 2, 300, 2, 2
     W = 64
     C = W if layout == "base" else W + 16
-    xd, xo = make_xf("half" if D % 4 == 0 else "inter", D, 2000, out)
+    xd, xo = make_xf("half" if D % 4 == 0 else "inter", D, 2000, out,
+                     channels=channel_tables(g, H, D, out) if chan else None)
     T = g.integers(1, 1900, size=B)
     T[:4] = [C, C + 1, 2001, 1]  # 2001: past the tables
     sk = (T - 1).astype(np.int32)
