@@ -523,14 +523,16 @@ static float xf_load(int type, const char *row, int64_t i)
     }
 }
 
-/* [PF]: saturate(round_half_even(y / scale) + zero_point); NaN -> zero_point
- * (the zero point itself saturated: a per-channel table is data, not checked) */
+/* [PF]: saturate(round_half_even(y / scale) + zero_point). A NaN quotient (a
+ * NaN y, or a per-channel scale that makes y / scale NaN) takes the zero
+ * point, itself saturated: a per-channel table is data, not checked. */
 static int32_t xf_quantize(float y, float scale, int32_t zero_point, int32_t lo, int32_t hi)
 {
+    const float r = y / scale;
     float q;
-    if (isnan(y))
+    if (isnan(r))
         return zero_point < lo ? lo : (zero_point > hi ? hi : zero_point);
-    q = nearbyintf(y / scale) + (float)zero_point; /* default rounding: ties to even */
+    q = nearbyintf(r) + (float)zero_point; /* default rounding: ties to even */
     if (q < (float)lo)
         return lo;
     if (q > (float)hi)

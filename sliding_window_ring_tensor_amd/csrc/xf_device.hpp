@@ -81,11 +81,13 @@ __device__ __forceinline__ uint16_t xf_f16(float f) {
   return __builtin_bit_cast(uint16_t, _Float16(f));  // hardware conversion, nearest even
 }
 
-// NaN takes the zero point, itself saturated into the code range (a
-// per-channel zero point is data the host never sees)
+// A NaN quotient (a NaN y, or a per-channel scale that makes y / scale NaN)
+// takes the zero point, itself saturated into the code range (a per-channel
+// zero point is data the host never sees)
 __device__ __forceinline__ int32_t xf_code_of(const RowXf &x, float scale, int32_t zero, float y) {
-  if (y != y) return min(max(zero, x.lo), x.hi);
-  float q = __builtin_rintf(y / scale) + float(zero);
+  const float r = y / scale;
+  if (r != r) return min(max(zero, x.lo), x.hi);
+  float q = __builtin_rintf(r) + float(zero);
   q = fminf(fmaxf(q, float(x.lo)), float(x.hi));
   return int32_t(q);
 }

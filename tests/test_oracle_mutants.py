@@ -95,15 +95,15 @@ MUTANTS = {
                               "(p0 >= 0 && p0 <= x->max_position - n + 1)"),
     "rope_range_not_flagged": ("set_flag(flags, ORC_FLAG_ROPE_RANGE);\n            continue;",
                                "continue;"),
-    "quant_round_half_up": ("q = nearbyintf(y / scale) + (float)zero_point;",
-                            "q = floorf(y / scale + 0.5f) + (float)zero_point;"),
-    "quant_zero_point_subtracted": ("q = nearbyintf(y / scale) + (float)zero_point;",
-                                    "q = nearbyintf(y / scale) - (float)zero_point;"),
-    "quant_truncates": ("q = nearbyintf(y / scale) + (float)zero_point;",
-                        "q = truncf(y / scale) + (float)zero_point;"),
+    "quant_round_half_up": ("q = nearbyintf(r) + (float)zero_point;",
+                            "q = floorf(r + 0.5f) + (float)zero_point;"),
+    "quant_zero_point_subtracted": ("q = nearbyintf(r) + (float)zero_point;",
+                                    "q = nearbyintf(r) - (float)zero_point;"),
+    "quant_truncates": ("q = nearbyintf(r) + (float)zero_point;",
+                        "q = truncf(r) + (float)zero_point;"),
     "quant_high_code_wraps": ("        *hi = 127;", "        *hi = 128;"),
-    "quant_nan_to_low_code": ("if (isnan(y))\n        return zero_point < lo",
-                              "if (isnan(y))\n        return lo + 0 * zero_point;\n    if (0)\n        return zero_point < lo"),
+    "quant_nan_to_low_code": ("if (isnan(r))\n        return zero_point < lo",
+                              "if (isnan(r))\n        return lo + 0 * zero_point;\n    if (0)\n        return zero_point < lo"),
     "quant_v_uses_k_parameters": (": x->scale[t];", ": x->scale[0];"),
     "f32_nan_payload_kept": ("if (isnan(y)) {\n            const uint32_t canonical",
                              "if (0) {\n            const uint32_t canonical"),

@@ -648,3 +648,17 @@ def test_per_channel_window_rows_use_their_heads_tables(orc, out_type):
                                 elem_bits=8) == 0
     np.testing.assert_array_equal(k1, k2)
     np.testing.assert_array_equal(v1, v2)
+
+
+def test_nan_quotient_takes_the_saturated_zero_point(orc):
+    """Per-channel tables are data: a scale that makes y / scale NaN (a NaN
+    scale, or 0 / 0) gives the zero point like a NaN input does, and a zero
+    point outside the code range saturates; a zero scale on a nonzero y gives
+    an infinite quotient and so a saturated code."""
+    D = 8
+    tab = np.float32([np.nan, 0.0, 0.0, 0.5, 0.5, 0.5, -0.5, np.inf])[None]
+    z = np.int32([3, 4, 5, 300, -300, 7, 0, 9])[None]
+    x = Transform(XF_F32, XF_INT8, channel_scale=(tab, tab), channel_zero_point=(z, z))
+    row = np.float32([1.0, 0.0, 2.0, np.nan, np.nan, 1.0, 1.0, 5.0])[None]
+    got = _codes(orc, x, 0, 0, row).astype(np.int64).ravel()
+    assert list(got) == [3, 4, 127, 127, -128, 9, -2, 9]
