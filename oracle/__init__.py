@@ -129,6 +129,7 @@ class Lengths:
     cache_total: np.ndarray  # L, int32
     evict: np.ndarray        # E, int32
     flags: int
+    work: np.ndarray | None = None  # exclusive prefix of each entry's rows, int64 [B + 1]
 
 
 class Oracle:
@@ -142,9 +143,10 @@ class Oracle:
         vp, i64, i32, u32p = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.POINTER(ctypes.c_uint32)
         lib.orc_tensor_scatter.argtypes = [vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, u32p]
         lib.orc_tensor_scatter.restype = ctypes.c_int
-        lib.orc_kv_seq_lengths.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp, u32p]
+        lib.orc_kv_seq_lengths.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp, vp, u32p]
         lib.orc_kv_seq_lengths.restype = ctypes.c_int
-        lib.orc_kv_seq_lengths_drift.argtypes = [vp, i64, i64, i64, i64, vp, vp, vp, vp, vp, u32p]
+        lib.orc_kv_seq_lengths_drift.argtypes = [vp, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp,
+                                                 u32p]
         lib.orc_kv_seq_lengths_drift.restype = ctypes.c_int
         lib.orc_kv_window_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                              i64, i64, i64, i64, i64, i32, ctypes.c_uint, u32p]
@@ -219,12 +221,13 @@ class Oracle:
         Lp = np.zeros(B, np.int32)
         L = np.zeros(B, np.int32)
         E = np.zeros(B, np.int32)
+        W = np.zeros(B + 1, np.int64)
         flags = ctypes.c_uint32(0)
         st = self.lib.orc_kv_seq_lengths(_ptr(sk), B, seq_len, capacity, _ptr(T), _ptr(P),
-                                         _ptr(Lp), _ptr(L), _ptr(E), ctypes.byref(flags))
+                                         _ptr(Lp), _ptr(L), _ptr(E), _ptr(W), ctypes.byref(flags))
         if st != OK:
             raise OracleError(f"orc_kv_seq_lengths status {st}")
-        return Lengths(T, P, Lp, L, E, flags.value)
+        return Lengths(T, P, Lp, L, E, flags.value, W)
 
     def kv_seq_lengths_drift(self, seqlens_k, seq_len: int, capacity: int,
                              window: int) -> Lengths:
@@ -235,18 +238,20 @@ class Oracle:
         Lp = np.zeros(B, np.int32)
         L = np.zeros(B, np.int32)
         E = np.zeros(B, np.int32)
+        W = np.zeros(B + 1, np.int64)
         flags = ctypes.c_uint32(0)
         st = self.lib.orc_kv_seq_lengths_drift(_ptr(sk), B, seq_len, capacity, window, _ptr(T),
-                                               _ptr(P), _ptr(Lp), _ptr(L), _ptr(E),
+                                               _ptr(P), _ptr(Lp), _ptr(L), _ptr(E), _ptr(W),
                                                ctypes.byref(flags))
         if st != OK:
             raise OracleError(f"orc_kv_seq_lengths_drift status {st}")
-        return Lengths(T, P, Lp, L, E, flags.value)
+        return Lengths(T, P, Lp, L, E, flags.value, W)
 
     def kv_seq_lengths_status(self, seqlens_k, seq_len, capacity) -> int:
         sk = np.ascontiguousarray(seqlens_k, dtype=np.int32)
         B = sk.shape[0]
         out = [np.zeros(B, t) for t in (np.int64, np.int64, np.int32, np.int32, np.int32)]
+        out.append(np.zeros(B + 1, np.int64))
         flags = ctypes.c_uint32(0)
         return self.lib.orc_kv_seq_lengths(_ptr(sk), B, seq_len, capacity,
                                            *[_ptr(o) for o in out], ctypes.byref(flags))

@@ -160,10 +160,31 @@ int orc_tensor_scatter(void *present, const void *past, const void *update,
 /* [GQA] lengths of a windowed step                                         */
 /* ------------------------------------------------------------------------ */
 
+/* Rows one batch entry's step writes: S = 1 shifts Lp - E rows when it
+ * evicts (E > 0) and appends one; S > 1 fills Lp + S rows of staging. */
+static int64_t work_rows(int64_t Lp, int64_t E, int64_t S)
+{
+    if (S == 1)
+        return (E > 0 ? Lp - E : 0) + 1;
+    return Lp + S;
+}
+
+/* work_offsets[0] = 0 and work_offsets[b + 1] = work_offsets[b] + the rows of
+ * entry b: the exclusive prefix over the batch, its total last */
+static void work_prefix(const int32_t *cache_past_lens, const int32_t *evict_counts,
+                        int64_t batch, int64_t S, int64_t *work_offsets)
+{
+    if (!work_offsets)
+        return;
+    work_offsets[0] = 0;
+    for (int64_t b = 0; b < batch; ++b)
+        work_offsets[b + 1] = work_offsets[b] + work_rows(cache_past_lens[b], evict_counts[b], S);
+}
+
 int orc_kv_seq_lengths(const int32_t *seqlens_k, int64_t batch, int64_t seq_len,
                        int64_t capacity, int64_t *total_lens, int64_t *past_lens,
                        int32_t *cache_past_lens, int32_t *cache_total_lens,
-                       int32_t *evict_counts, uint32_t *flags)
+                       int32_t *evict_counts, int64_t *work_offsets, uint32_t *flags)
 {
     const int64_t S = seq_len, C = capacity;
 
@@ -196,6 +217,7 @@ int orc_kv_seq_lengths(const int32_t *seqlens_k, int64_t batch, int64_t seq_len,
         if (cache_total_lens)
             cache_total_lens[b] = (int32_t)L;
     }
+    work_prefix(cache_past_lens, evict_counts, batch, S, work_offsets);
     return ORC_OK;
 }
 
@@ -219,7 +241,7 @@ int orc_kv_seq_lengths_drift(const int32_t *seqlens_k, int64_t batch,
                              int64_t seq_len, int64_t capacity, int64_t window,
                              int64_t *total_lens, int64_t *past_lens,
                              int32_t *cache_past_lens, int32_t *cache_total_lens,
-                             int32_t *evict_counts, uint32_t *flags)
+                             int32_t *evict_counts, int64_t *work_offsets, uint32_t *flags)
 {
     const int64_t S = seq_len, C = capacity, W = window;
 
@@ -253,6 +275,7 @@ int orc_kv_seq_lengths_drift(const int32_t *seqlens_k, int64_t batch,
         if (cache_total_lens)
             cache_total_lens[b] = (int32_t)L;
     }
+    work_prefix(cache_past_lens, evict_counts, batch, S, work_offsets);
     return ORC_OK;
 }
 

@@ -92,11 +92,15 @@ int orc_tensor_scatter(void *present, const void *past, const void *update,
  * T = seqlens_k + 1, P = max(0, T - S), Lp = min(P, C),
  * E = max(0, Lp + S - C), L = Lp + S - E  (all in 64-bit arithmetic).
  * total_lens, past_lens, cache_total_lens may be NULL.
+ * work_offsets (int64[batch + 1], may be NULL): the exclusive prefix over the
+ * batch of the rows each entry's step writes, r_b = (E_b > 0 ? Lp_b - E_b : 0)
+ * + 1 for S = 1 (the shifted rows and the appended one) and Lp_b + S for
+ * S > 1 (the staged rows); work_offsets[batch] is the total.
  */
 int orc_kv_seq_lengths(const int32_t *seqlens_k, int64_t batch, int64_t seq_len,
                        int64_t capacity, int64_t *total_lens, int64_t *past_lens,
                        int32_t *cache_past_lens, int32_t *cache_total_lens,
-                       int32_t *evict_counts, uint32_t *flags);
+                       int32_t *evict_counts, int64_t *work_offsets, uint32_t *flags);
 
 /*
  * [GQA-CPU] lengths of one windowed step under the drifting layout of the
@@ -104,13 +108,13 @@ int orc_kv_seq_lengths(const int32_t *seqlens_k, int64_t batch, int64_t seq_len,
  * C - W + 1 the append point is end(x) = x while x <= C, else
  * x - gap * ceil((x - C) / gap). T = seqlens_k + 1, P = max(0, T - S),
  * Lp = end(P), L = end(T), E = Lp + S - L. W = C (gap 1) is the base method.
- * 1 <= window <= capacity.
+ * 1 <= window <= capacity. work_offsets as for orc_kv_seq_lengths.
  */
 int orc_kv_seq_lengths_drift(const int32_t *seqlens_k, int64_t batch,
                              int64_t seq_len, int64_t capacity, int64_t window,
                              int64_t *total_lens, int64_t *past_lens,
                              int32_t *cache_past_lens, int32_t *cache_total_lens,
-                             int32_t *evict_counts, uint32_t *flags);
+                             int32_t *evict_counts, int64_t *work_offsets, uint32_t *flags);
 
 /*
  * [GQA] one windowed cache step for K and V.

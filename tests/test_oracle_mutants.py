@@ -152,6 +152,13 @@ MUTANTS = {
     "paged_duplicates_accepted": ("(i > 0 && id <= blocks[i - 1])", "(i > 0 && id < blocks[i - 1])"),
     "paged_destinations_overlap": ("if (dst < next || bytes > free_end - dst)",
                                    "if (bytes > free_end - dst)"),
+    # the work prefix of the lengths call
+    "work_rows_product_form": ("return (E > 0 ? Lp - E : 0) + 1;", "return E * (Lp - E) + 1;"),
+    "work_rows_staged_without_S": ("    return Lp + S;\n}", "    return Lp;\n}"),
+    "work_not_a_prefix": ("work_offsets[b + 1] = work_offsets[b] + work_rows(",
+                          "work_offsets[b + 1] = work_rows("),
+    "work_drift_not_written": ("    work_prefix(cache_past_lens, evict_counts, batch, S, work_offsets);\n    return ORC_OK;\n}\n\n/* ------------------------------------------------------------------------ */\n/* [GQA] windowed step",
+                               "    return ORC_OK;\n}\n\n/* ------------------------------------------------------------------------ */\n/* [GQA] windowed step"),
     # per-channel parameters and the fp8 target of the fused append
     "xf_channel_head_ignored": ("x->channel_scale[t][head * head_dim + i]", "x->channel_scale[t][i]"),
     "xf_channel_zero_ignored": ("x->channel_zero_point[t] ? x->channel_zero_point[t][head * head_dim + i]",

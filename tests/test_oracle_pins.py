@@ -569,3 +569,49 @@ def test_drift_rejects_bad_window(orc):
     for W in (0, -1, 9):
         with pytest.raises(oracle.OracleError):
             orc.kv_seq_lengths_drift(sk, 1, 8, W)
+
+
+# --------------------------------------------------------------------------
+# the work prefix of the lengths call
+# --------------------------------------------------------------------------
+
+def test_work_offsets_hand_worked(orc):
+    """The exclusive prefix of the rows each entry's step writes, worked by
+    hand: S = 1 writes the shifted rows (Lp - E when it evicts) and the new
+    one; S > 1 stages Lp + S rows."""
+    # C = 4, S = 1: (Lp, E) = (0, 0), (3, 0), (4, 1), (4, 1), (0, 0) (seqlens_k < 0 clamps)
+    L = orc.kv_seq_lengths(np.array([0, 3, 4, 9, -2], np.int32), 1, 4)
+    assert list(L.work) == [0, 1, 2, 6, 10, 11]
+    # C = 4, S = 3: Lp = 0, 3, 4
+    L = orc.kv_seq_lengths(np.array([2, 5, 20], np.int32), 3, 4)
+    assert list(L.work) == [0, 3, 9, 16]
+    # drifting layout C = 6, W = 4 (gap 3), S = 1: only T = 7 compacts (E = 3, Lp = 6)
+    L = orc.kv_seq_lengths_drift(np.array([5, 6, 7, 8], np.int32), 1, 6, 4)
+    assert list(L.cache_past) == [5, 6, 4, 5] and list(L.evict) == [0, 3, 0, 0]
+    assert list(L.work) == [0, 1, 5, 6, 7]
+    assert list(orc.kv_seq_lengths(np.zeros(0, np.int32), 1, 4).work) == [0]
+
+
+@pytest.mark.parametrize("S,drift", [(1, False), (1, True), (5, False), (5, True)])
+def test_work_offsets_count_the_rows_the_step_writes(orc, S, drift):
+    """Each entry's share of the prefix is the number of rows the oracle's
+    own step changes: tagged rows are unique, so every shifted row and every
+    appended or staged row differs from what it replaced."""
+    g = np.random.default_rng(70 + S + drift)
+    B, H, C, D, W = 40, 1, 12, 4, 7
+    sk = g.integers(0, 40, size=B).astype(np.int32)
+    sk[:4] = [S - 1, C - 1, C, C + S]
+    L = orc.kv_seq_lengths_drift(sk, S, C, W) if drift else orc.kv_seq_lengths(sk, S, C)
+    k = (np.arange(B * H * C * D, dtype=np.int32) + 1).reshape(B, H, C, D)
+    kn = -(np.arange(B * H * S * D, dtype=np.int32) + 1).reshape(B, H, S, D)
+    st = np.zeros((B, H, C + S, D), np.int32) if S > 1 else None
+    k2 = k.copy()
+    assert orc.kv_window_append(k2, k2.copy(), kn, kn.copy(), L.cache_past, L.evict, st,
+                                None if st is None else st.copy(),
+                                phase=oracle.PHASE_STAGE if S > 1 else oracle.PHASE_ALL) == 0
+    if S == 1:
+        written = (k2 != k).any(axis=3)[:, 0].sum(axis=1)
+    else:
+        written = (st != 0).any(axis=3)[:, 0].sum(axis=1)
+    np.testing.assert_array_equal(np.diff(L.work), written)
+    assert L.work[0] == 0
