@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define SWRT_ABI_VERSION 8
+#define SWRT_ABI_VERSION 9
 
 /* synchronous status codes */
 #define SWRT_OK 0
@@ -173,6 +173,16 @@ int swrt_tensor_scatter_batched(int n_tensors, void *const *presents,
  * cache_past_lens  device int32[batch], required: Lp.
  * cache_total_lens device int32[batch] or NULL: L.
  * evict_counts     device int32[batch], required: E.
+ * work_offsets     device int64[batch + 1] or NULL: the exclusive prefix over
+ *                  the batch of the rows each entry's step writes,
+ *                  r_b = (E_b > 0 ? Lp_b - E_b : 0) + 1 for S = 1 (shifted rows
+ *                  and the appended one) and Lp_b + S for S > 1 (staged rows):
+ *                  work_offsets[0] = 0, work_offsets[b + 1] = work_offsets[b] +
+ *                  r_b, the total last. A flat grid sized for the worst case
+ *                  can map its tiles to (entry, row) from it without a host
+ *                  round trip. 64-bit (the total reaches batch * (C + S)).
+ *                  Computed by one workgroup scanning the batch (wave prefix by
+ *                  lane shuffles, waves joined through LDS).
  * d_flags          device uint32 or NULL. SWRT_FLAG_BAD_SEQLEN when
  *                  seqlens_k[b] < 0 or T < S; P is then clamped to 0 and the
  *                  other values follow from it.
@@ -181,7 +191,8 @@ int swrt_tensor_scatter_batched(int n_tensors, void *const *presents,
 int swrt_kv_seq_lengths(const int32_t *seqlens_k, int batch, int seq_len,
                         int capacity, int64_t *total_lens, int64_t *past_lens,
                         int32_t *cache_past_lens, int32_t *cache_total_lens,
-                        int32_t *evict_counts, uint32_t *d_flags, void *stream);
+                        int32_t *evict_counts, int64_t *work_offsets, uint32_t *d_flags,
+                        void *stream);
 
 /*
  * swrt_kv_seq_lengths_drift -- lengths of one windowed step under the
@@ -194,14 +205,15 @@ int swrt_kv_seq_lengths(const int32_t *seqlens_k, int batch, int seq_len,
  *   Lp = end(P), L = end(T), E = Lp + S - L.
  * The window W (1 <= W <= C, else SWRT_E_INVALID_ARG) is the attention
  * window the last W tokens of which stay resident; W = C gives exactly the
- * values of swrt_kv_seq_lengths. Every other argument as there. The (Lp, E)
- * pairs feed swrt_kv_window_append unchanged.
+ * values of swrt_kv_seq_lengths. Every other argument as there (work_offsets
+ * counts a whole gap's shift when the step compacts). The (Lp, E) pairs feed
+ * swrt_kv_window_append unchanged.
  */
 int swrt_kv_seq_lengths_drift(const int32_t *seqlens_k, int batch, int seq_len,
                               int capacity, int window, int64_t *total_lens,
                               int64_t *past_lens, int32_t *cache_past_lens,
                               int32_t *cache_total_lens, int32_t *evict_counts,
-                              uint32_t *d_flags, void *stream);
+                              int64_t *work_offsets, uint32_t *d_flags, void *stream);
 
 /*
  * swrt_kv_window_append -- one windowed cache step for K and V (pull request

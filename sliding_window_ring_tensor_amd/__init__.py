@@ -79,7 +79,7 @@ MODE_LINEAR, MODE_CIRCULAR = 0, 1
 PHASE_STAGE, PHASE_COMMIT, PHASE_ALL = 1, 2, 3
 MAX_LAYERS = 32
 MAX_BATCHED = 64
-ABI_VERSION = 8
+ABI_VERSION = 9
 
 _PHASES = {"stage": PHASE_STAGE, "commit": PHASE_COMMIT, "all": PHASE_ALL}
 _MODES = {"linear": MODE_LINEAR, "circular": MODE_CIRCULAR}
@@ -197,8 +197,9 @@ def lib() -> ctypes.CDLL:
     L.swrt_tensor_scatter.argtypes = [vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, vp, vp]
     L.swrt_tensor_scatter_batched.argtypes = [i32, vpp, vpp, vpp, vp, vp, i32, i32, i64, i32,
                                               i32, vp, vp]
-    L.swrt_kv_seq_lengths.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
-    L.swrt_kv_seq_lengths_drift.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
+    L.swrt_kv_seq_lengths.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.swrt_kv_seq_lengths_drift.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp,
+                                            vp]
     L.swrt_kv_window_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                         i32, i32, u32, vp, vp]
     L.swrt_kv_window_append_layers.argtypes = [i32, vpp, vpp, vpp, vpp, vp, vpp, vpp, vp, vp,
@@ -439,30 +440,39 @@ def _lengths_out(out: WindowLengths | None, B: int, dev) -> WindowLengths:
 
 def prepare_kv_seq_lengths(seqlens_k: torch.Tensor, seq_len: int, capacity: int, *,
                            window: int | None = None, out: WindowLengths | None = None,
+                           work_offsets: torch.Tensor | None = None,
                            flags: torch.Tensor | None = None) -> PreparedCall:
-    dev = _device_of(seqlens_k, flags)
     _check_seqlens(seqlens_k)
     B = seqlens_k.shape[0]
+    if work_offsets is not None:
+        _contig("work_offsets", work_offsets)
+        if work_offsets.dtype != torch.int64 or tuple(work_offsets.shape) != (B + 1,):
+            raise SwrtError(f"work_offsets must be int64 [{B + 1}]")
+    _flags_ptr(flags)
+    dev = _device_of(seqlens_k, work_offsets, flags)
     out = _lengths_out(out, B, dev)
     tail = (_ptr(out.total), _ptr(out.past), _ptr(out.cache_past), _ptr(out.cache_total),
-            _ptr(out.evict), _flags_ptr(flags))
+            _ptr(out.evict), _ptr(work_offsets), _flags_ptr(flags))
     if window is None:
         fn, args, what = lib().swrt_kv_seq_lengths, (_ptr(seqlens_k), B, seq_len, capacity,
                                                      *tail), "kv_seq_lengths"
     else:
         fn, args, what = lib().swrt_kv_seq_lengths_drift, (_ptr(seqlens_k), B, seq_len, capacity,
                                                            window, *tail), "kv_seq_lengths_drift"
-    return PreparedCall(fn, args, dev, what, (seqlens_k, *out, flags), out)
+    return PreparedCall(fn, args, dev, what, (seqlens_k, *out, work_offsets, flags), out)
 
 
 def kv_seq_lengths(seqlens_k: torch.Tensor, seq_len: int, capacity: int, *,
                    window: int | None = None, out: WindowLengths | None = None,
+                   work_offsets: torch.Tensor | None = None,
                    flags: torch.Tensor | None = None) -> WindowLengths:
     """Lengths of one windowed step for every batch entry, computed on the device.
     With ``window`` (W <= capacity) the drifting layout's lengths: the append
-    point drifts and a whole gap of C - W + 1 rows is reclaimed at once."""
+    point drifts and a whole gap of C - W + 1 rows is reclaimed at once.
+    ``work_offsets`` (int64 [B + 1], optional) receives the exclusive prefix
+    of the rows each entry's step writes."""
     return prepare_kv_seq_lengths(seqlens_k, seq_len, capacity, window=window, out=out,
-                                  flags=flags)()
+                                  work_offsets=work_offsets, flags=flags)()
 
 
 # ---------------------------------------------------------------------------

@@ -240,8 +240,8 @@ def test_tensor_scatter_rejects(L):
     assert st == INV
 
 
-def _lens(L, sk=A, batch=4, S=1, C=8, T=B_, P=B_ + 0x1000, Lp=C_, Lt=C_ + 0x1000, E=D_):
-    return L.swrt_kv_seq_lengths(sk, batch, S, C, T, P, Lp, Lt, E, None, None)
+def _lens(L, sk=A, batch=4, S=1, C=8, T=B_, P=B_ + 0x1000, Lp=C_, Lt=C_ + 0x1000, E=D_, W=None):
+    return L.swrt_kv_seq_lengths(sk, batch, S, C, T, P, Lp, Lt, E, W, None, None)
 
 
 @no_gpu_visible
@@ -254,10 +254,14 @@ def test_kv_seq_lengths_rejects(L):
     assert _lens(L, Lt=C_ + 8) == INV                                   # overlaps Lp
     assert _lens(L, E=A) == INV                                         # overlaps seqlens_k
     assert _lens(L, batch=0) == swrt.OK
+    assert _lens(L, W=D_ + 0x1004) == INV                               # work prefix: 8-byte
+    assert _lens(L, W=D_ + 8) == INV                                    # overlaps E
+    assert _lens(L, W=D_ + 0x1000) in (swrt.OK, swrt.E_LAUNCH)          # [batch + 1] int64
     drift = L.swrt_kv_seq_lengths_drift
-    assert drift(A, 4, 1, 8, 0, B_, B_ + 0x1000, C_, C_ + 0x1000, D_, None, None) == INV
-    assert drift(A, 4, 1, 8, 9, B_, B_ + 0x1000, C_, C_ + 0x1000, D_, None, None) == INV
-    assert drift(A, 0, 1, 8, 5, B_, B_ + 0x1000, C_, C_ + 0x1000, D_, None, None) == swrt.OK
+    assert drift(A, 4, 1, 8, 0, B_, B_ + 0x1000, C_, C_ + 0x1000, D_, None, None, None) == INV
+    assert drift(A, 4, 1, 8, 9, B_, B_ + 0x1000, C_, C_ + 0x1000, D_, None, None, None) == INV
+    assert drift(A, 0, 1, 8, 5, B_, B_ + 0x1000, C_, C_ + 0x1000, D_, None, None,
+                 None) == swrt.OK
 
 
 def _win(L, kc=A, vc=A + 0x1000_0000, kn=B_, vn=B_ + 0x1000_0000, strides=None, ks=None, vs=None,

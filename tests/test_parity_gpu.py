@@ -312,6 +312,60 @@ def test_lengths_workloads_and_edges(orc):
         run_lengths(orc, g.integers(-10, 20000, size=B).astype(np.int32), 3, 64)
 
 
+@pytest.mark.parametrize("drift", [False, True])
+@pytest.mark.parametrize("S", [1, 7])
+def test_lengths_work_offsets(orc, S, drift):
+    """The work prefix, bit for bit with the oracle's, with every length
+    array: one wave (B = 1, 63, 64), one past it (65), whole and ragged
+    1024-entry chunks of the one-workgroup scan, B = 4096, and B = 0 (the
+    single 0); bad and extreme seqlens_k mixed in."""
+    g = np.random.default_rng(1700 + S + 10 * drift)
+    C, W = 128, 100
+    for B in (0, 1, 63, 64, 65, 1000, 1023, 1024, 1025, 4096):
+        sk = g.integers(-3, 20000, size=B).astype(np.int32)
+        if B >= 4:
+            sk[:4] = [2**31 - 1, -2**31, C - 1, C]
+        say("work offsets", S, drift, B)
+        flags = flag_word()
+        wo = torch.full((B + 1,), -7, dtype=torch.int64, device=DEV)
+        got = swrt.kv_seq_lengths(torch.from_numpy(sk).to(DEV), S, C, window=W if drift else None,
+                                  work_offsets=wo, flags=flags)
+        want = orc.kv_seq_lengths_drift(sk, S, C, W) if drift else orc.kv_seq_lengths(sk, S, C)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(wo.cpu().numpy(), want.work)
+        for x, y in zip(got, (want.total, want.past, want.cache_past, want.cache_total,
+                              want.evict)):
+            np.testing.assert_array_equal(x.cpu().numpy(), y)
+        assert flags.item() == want.flags
+
+
+def test_lengths_work_offsets_graph_replays(orc):
+    """The lengths call with its work prefix captured in a graph: each replay,
+    on new seqlens_k copied in between (eager work and synchronizations
+    between the replays), matches the oracle."""
+    g = np.random.default_rng(1750)
+    B, S, C = 1500, 1, 64
+    sk = torch.zeros(B, dtype=torch.int32, device=DEV)
+    wo = torch.zeros(B + 1, dtype=torch.int64, device=DEV)
+    out = swrt.WindowLengths(*(torch.zeros(B, dtype=dt, device=DEV) for dt in
+                               (torch.int64, torch.int64, torch.int32, torch.int32, torch.int32)))
+    torch.cuda.synchronize()
+    st = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(graph, stream=st):
+            swrt.kv_seq_lengths(sk, S, C, out=out, work_offsets=wo)
+    for rep in range(4):
+        host = g.integers(0, 300, size=B).astype(np.int32)
+        sk.copy_(torch.from_numpy(host))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        want = orc.kv_seq_lengths(host, S, C)
+        np.testing.assert_array_equal(wo.cpu().numpy(), want.work, err_msg=str(rep))
+        np.testing.assert_array_equal(out.evict.cpu().numpy(), want.evict)
+
+
 # ---------------------------------------------------------------------------
 # windowed step: shift + append, stage + commit
 # ---------------------------------------------------------------------------
