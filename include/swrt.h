@@ -270,6 +270,30 @@ int swrt_kv_window_append(void *k_cache, void *v_cache, const void *k_new,
                           void *stream);
 
 /*
+ * swrt_kv_window_append_noalloc -- for callers that cannot allocate (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * swrt_kv_window_append with phase SWRT_PHASE_ALL and no staging arguments.
+ * S = 1 runs in place as there. For S > 1 the two [batch, kv_heads,
+ * capacity + seq_len, head_dim] staging buffers are carved from the
+ * library's own device array of SWRT_NOALLOC_STAGING_BYTES bytes, which every
+ * GPU the library runs on holds until the process ends (K's at its start, V's
+ * at the next 256-byte boundary). The call allocates and frees nothing;
+ * its first call on a device looks the array's address up with that device
+ * current (the caller makes the stream's device current, as for any HIP
+ * call). Every call on one GPU shares that GPU's array, so calls that overlap
+ * in time on one GPU (other streams, other host threads) race; calls on
+ * different GPUs do not. SWRT_E_UNSUPPORTED when one staging buffer exceeds
+ * SWRT_NOALLOC_STAGING_BYTES / 2 (it is then refused before anything is
+ * launched). Every other argument, check and result as swrt_kv_window_append.
+ */
+#define SWRT_NOALLOC_STAGING_BYTES (128ll << 20)
+int swrt_kv_window_append_noalloc(void *k_cache, void *v_cache, const void *k_new,
+                                  const void *v_new, const int64_t *new_strides,
+                                  const int32_t *cache_past_lens, const int32_t *evict_counts,
+                                  int batch, int kv_heads, int capacity, int seq_len,
+                                  int head_dim, int elem_bits, uint32_t *d_flags, void *stream);
+
+/*
  * swrt_kv_window_append_layers -- swrt_kv_window_append for several layers at
  * once (the pull request's Design section applied to every windowed layer of
  * a model in one launch per phase, as for a whole-model decode step whose

@@ -202,6 +202,8 @@ def lib() -> ctypes.CDLL:
                                             vp]
     L.swrt_kv_window_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                         i32, i32, u32, vp, vp]
+    L.swrt_kv_window_append_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                                i32, i32, vp, vp]
     L.swrt_kv_window_append_layers.argtypes = [i32, vpp, vpp, vpp, vpp, vp, vpp, vpp, vp, vp,
                                                i32, i32, i32, i32, i32, i32, u32, vp, vp]
     L.swrt_kv_window_stage_step.argtypes = [i32, vpp, vpp, vpp, vpp, vp, vpp, vpp, vp, i32, i32,
@@ -236,7 +238,8 @@ def lib() -> ctypes.CDLL:
                  "swrt_kv_window_append_xf", "swrt_kv_window_stage_step_xf",
                  "swrt_tensor_scatter_xf", "swrt_kv_decode_step_xf",
                  "swrt_window_attention", "swrt_paged_attention", "swrt_paged_quantize",
-                 "swrt_paged_append", "swrt_paged_append_open", "swrt_abi_version"):
+                 "swrt_paged_append", "swrt_paged_append_open",
+                 "swrt_kv_window_append_noalloc", "swrt_abi_version"):
         getattr(L, name).restype = ctypes.c_int
     L.swrt_status_string.argtypes = [ctypes.c_int]
     L.swrt_status_string.restype = ctypes.c_char_p
@@ -561,6 +564,39 @@ def kv_window_append(k_cache: torch.Tensor, v_cache: torch.Tensor, k_new: torch.
         k_stagings=None if k_staging is None else [k_staging],
         v_stagings=None if v_staging is None else [v_staging], phase=phase, flags=flags,
         _single=True)()
+
+
+NOALLOC_STAGING_BYTES = 128 << 20  # SWRT_NOALLOC_STAGING_BYTES
+
+
+def prepare_kv_window_append_noalloc(k_cache, v_cache, k_new, v_new, cache_past_lens,
+                                     evict_counts, *,
+                                     flags: torch.Tensor | None = None) -> PreparedCall:
+    """See ``kv_window_append_noalloc``."""
+    n, B, H, C, D, S, strides = _check_layers([k_cache], [v_cache], [k_new], [v_new])
+    for t in (cache_past_lens, evict_counts):
+        _contig("lengths", t)
+        if t.dtype != torch.int32 or t.shape != (B,):
+            raise SwrtError("cache_past_lens and evict_counts must be int32 [B]")
+    _flags_ptr(flags)
+    everything = (k_cache, v_cache, k_new, v_new, cache_past_lens, evict_counts, flags)
+    dev = _device_of(*everything)
+    args = (_ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), strides,
+            _ptr(cache_past_lens), _ptr(evict_counts), B, H, C, S, D, _bits(k_cache),
+            _flags_ptr(flags))
+    return PreparedCall(lib().swrt_kv_window_append_noalloc, args, dev,
+                        "kv_window_append_noalloc", everything)
+
+
+def kv_window_append_noalloc(k_cache: torch.Tensor, v_cache: torch.Tensor, k_new: torch.Tensor,
+                             v_new: torch.Tensor, cache_past_lens: torch.Tensor,
+                             evict_counts: torch.Tensor, *,
+                             flags: torch.Tensor | None = None) -> None:
+    """``kv_window_append`` (phase "all") that allocates nothing: an S > 1
+    step stages through the library's own per-GPU device array of
+    NOALLOC_STAGING_BYTES (calls that overlap on one GPU race on it)."""
+    prepare_kv_window_append_noalloc(k_cache, v_cache, k_new, v_new, cache_past_lens,
+                                     evict_counts, flags=flags)()
 
 
 def kv_window_append_layers(k_caches: Sequence[torch.Tensor], v_caches: Sequence[torch.Tensor],

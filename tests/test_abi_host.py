@@ -50,7 +50,8 @@ def test_exports_every_declared_function(L):
             "swrt_kv_window_append_layers", "swrt_kv_decode_step", "swrt_kv_seq_lengths_drift",
             "swrt_kv_window_append_xf", "swrt_tensor_scatter_xf", "swrt_kv_decode_step_xf",
             "swrt_window_attention", "swrt_paged_attention", "swrt_paged_quantize",
-            "swrt_paged_append", "swrt_paged_append_open", "swrt_status_string",
+            "swrt_paged_append", "swrt_paged_append_open", "swrt_kv_window_append_noalloc",
+            "swrt_status_string",
             "swrt_abi_version"} <= declared
     out = subprocess.run(["nm", "-D", "--defined-only", swrt.LIBRARY], check=True,
                          capture_output=True, text=True).stdout
@@ -269,6 +270,25 @@ def _win(L, kc=A, vc=A + 0x1000_0000, kn=B_, vn=B_ + 0x1000_0000, strides=None, 
     strides = (I64 * 3)(*(strides or (H * S * D, S * D, D)))
     return L.swrt_kv_window_append(kc, vc, kn, vn, strides, ks, vs, lp, ev, batch, H, C, S, D,
                                    bits, phase, None, None)
+
+
+@no_gpu_visible
+def test_kv_window_append_noalloc_rejects(L):
+    """The no-alloc variant refuses a staging buffer beyond half its array, and
+    bad arguments, before touching the device."""
+    INV, UNS = swrt.E_INVALID_ARG, swrt.E_UNSUPPORTED
+    assert swrt.NOALLOC_STAGING_BYTES == 128 << 20
+
+    def na(B=2, H=2, C=8, S=4, D=16, bits=16):
+        st = (I64 * 3)(H * S * D, S * D, D)
+        return L.swrt_kv_window_append_noalloc(A, A + 0x1000_0000, B_, B_ + 0x1000_0000, st, D_,
+                                               D_ + 0x1000, B, H, C, S, D, bits, None, None)
+    assert na(C=0) == INV and na(S=0) == INV and na(B=-1) == INV and na(bits=24) == INV
+    # (C + S) * D * 2 bytes per slice: 64 MiB + 1 slice row past half the array
+    assert na(B=1, H=1, C=4096, S=2, D=8192 + 64) == UNS
+    assert na(B=64, H=64, C=4096, S=64, D=128) == UNS
+    assert na(B=2**20, H=2**20, C=2**20, S=2, D=128) == UNS  # overflows 64-bit bytes
+    assert na(B=0) == swrt.OK or na(B=0) == swrt.E_LAUNCH
 
 
 @no_gpu_visible
