@@ -1,23 +1,11 @@
 """GPU parity of the windowed decode attention against the float64 oracle.
 
-The kernels compute in binary32 (dot products of exact 16-bit or fp32
-products, exp2 with log2(e) folded into the scale, online-softmax merges) and
-the oracle in float64, so outputs agree within a bound derived from that
-arithmetic, per batch entry and head (u = 2^-24, D = head_dim, S1 = |scale| *
-max over visible rows of sum_d |q_d k_rd|, Vmax = max |v| over visible rows,
-n = visible rows):
-
-  |gpu - oracle| <= 4 * (2 * ((D + 4) u S1 + 2^-21) + (4 n + 64) u) * Vmax
-                    (+ one output ulp, 2^-8 |oracle| for bf16, 2^-10 for f16)
-
-the first term bounding the relative error of every softmax weight (a score
-is a sum of D products rounded in fp32 in an order the matrix cores fix, at
-most D - 1 roundings of terms bounded by S1, then the scale and the shift by
-the maximum; exp2 is within 2^-22), the second the accumulation of n weighted
-rows (with bf16 V each weight enters the value product as three exact bf16
-parts: three additions per row) and one rescale per block of rows. Dropping or adding a row, a wrong
-window edge, a wrong KV head or a missing scale moves the output by about
-Vmax / n, orders of magnitude above the bound.
+The kernels compute in binary32 and the oracle in float64, so outputs agree
+within the tolerance of tests/att_bound.py, per batch entry and query head:
+the forward error of any binary32 streaming evaluation of the definition
+(the precision the onnx-light-cpu roadmap's "Phase 1" prescribes), fixed from
+the definition and not from the kernels' order of operations, plus the
+output's own rounding for 16-bit outputs.
 """
 from __future__ import annotations
 
@@ -29,13 +17,12 @@ import oracle
 import sliding_window_ring_tensor_amd as swrt
 from sliding_window_ring_tensor_amd import workloads as wl
 from sliding_window_ring_tensor_amd.decode_step import ModelDecodeStep
+from tests.att_bound import window_tolerance, with_output_rounding
 from tests.test_parity_gpu import DEV, flag_word, say
 
 pytestmark = pytest.mark.gpu
-U = 2.0 ** -24
 ORC = {torch.float32: oracle.XF_F32, torch.float16: oracle.XF_F16,
        torch.bfloat16: oracle.XF_BF16}
-ULP = {torch.float32: 0.0, torch.float16: 2.0 ** -10, torch.bfloat16: 2.0 ** -8}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -62,7 +49,7 @@ def decoded(t: torch.Tensor) -> np.ndarray:
 
 
 def bound(q, k, v, L, W, scale, out_dtype, ref):
-    """The per-(b, h) tolerance of the module docstring, broadcast over D."""
+    """The per-(b, h) tolerance of tests/att_bound.py, broadcast over D."""
     qd, kd, vd = decoded(q), decoded(k), decoded(v)
     B, Hq, D = qd.shape
     G = Hq // kd.shape[1]
@@ -72,11 +59,9 @@ def bound(q, k, v, L, W, scale, out_dtype, ref):
         if r1 <= r0:
             continue
         for h in range(Hq):
-            kr, vr = kd[b, h // G, r0:r1], vd[b, h // G, r0:r1]
-            s1 = abs(scale) * np.abs(qd[b, h][None, :] * kr).sum(axis=1).max()
-            vmax = np.abs(vr).max()
-            tol[b, h] = 4 * (2 * ((D + 4) * U * s1 + 2.0 ** -21) + (4 * (r1 - r0) + 64) * U) * vmax
-    return tol * (1 + ULP[out_dtype]) + ULP[out_dtype] * 1.01 * np.abs(ref) + 1e-30
+            tol[b, h] = window_tolerance(qd[b, h], kd[b, h // G, r0:r1], vd[b, h // G, r0:r1],
+                                         scale)
+    return with_output_rounding(tol, ref, out_dtype)
 
 
 def check(orc, qs, ks, vs, L, W, scale, outs, out_dtype):

@@ -661,8 +661,10 @@ def test_workload5_model_step_full_size(orc, dtype, fused):
     step = ModelDecodeStep(spec, DEV, set_id=0, raw_bits=True)
     b = step.buffers
     win_before = [(hb(k).copy(), hb(v).copy()) for k, v in zip(b.win_k, b.win_v)]
-    sample = [0, len(b.full_k) - 1]  # full layers compared whole; the rest by their new rows
+    sample = [0, len(b.full_k) - 1]  # full layers the host oracle also runs whole
     full_before = {i: (hb(b.full_k[i]).copy(), hb(b.full_v[i]).copy()) for i in sample}
+    # every full cache, whole, on the device: a copy taken before the step
+    full_copies = [c.view(torch.uint8).clone() for c in b.full_k + b.full_v]
     step.run(fused=fused)
     torch.cuda.synchronize()
     assert b.flags.item() == 0
@@ -684,12 +686,17 @@ def test_workload5_model_step_full_size(orc, dtype, fused):
                                            tuple(cache.shape), 2, 1, 0, bits)
             assert st == 0 and f == 0
             np.testing.assert_array_equal(hb(cache), host, err_msg=f"full layer {i}")
-    # every other full layer: the row at T - 1 holds the new row
+    # every full cache whole: the copy with the rows TensorScatter writes (row
+    # w_b = T_b - 1 of every (b, h), from the new rows; linear, S = 1, all in
+    # range) must equal the cache byte for byte, so nothing else was written
     wi = torch.from_numpy(spec.write_indices).to(DEV)
     bi = torch.arange(spec.batch, device=DEV)
-    for cache, new in zip(b.full_k + b.full_v, b.full_kn + b.full_vn):
-        got = cache.view(torch.uint8)[bi, :, wi, :]  # [B, H, row bytes]
-        assert torch.equal(got, new.view(torch.uint8)[:, :, 0, :])
+    assert ((wi >= 0) & (wi < b.full_k[0].shape[2])).all()
+    for i, (cache, new) in enumerate(zip(b.full_k + b.full_v, b.full_kn + b.full_vn)):
+        want = full_copies[i]
+        want[bi, :, wi, :] = new.view(torch.uint8)[:, :, 0, :]
+        assert torch.equal(cache.view(torch.uint8), want), f"full cache {i}"
+        full_copies[i] = None  # 512 MiB each: free as we go
 
 
 # ---------------------------------------------------------------------------
