@@ -53,14 +53,51 @@ __device__ __forceinline__ bool xf_channels(const RowXf &x) {
   return x.cs[0] || x.cs[1] || x.cz[0] || x.cz[1];
 }
 
-// the scale and zero point of element e of a row of KV head h, tensor t
+// the scale and zero point of element e of a row of KV head h, tensor t.
+// The per-tensor scalars are taken as register values (readfirstlane of a
+// kernel-uniform value) before the table select: a select between a table
+// element and a kernel-argument field would be folded into one load through a
+// pointer that may address the arguments, and the compiler then copies the
+// whole argument block to scratch memory.
 __device__ __forceinline__ void xf_params(const RowXf &x, int t, uint32_t h, uint32_t e, float &sc,
                                           int32_t &zp) {
   const float *cs = t ? x.cs[1] : x.cs[0];
   const int32_t *cz = t ? x.cz[1] : x.cz[0];
+  const float s0 = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x.scale[0])));
+  const float s1 = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x.scale[1])));
+  const int32_t z0 = __builtin_amdgcn_readfirstlane(x.zero[0]);
+  const int32_t z1 = __builtin_amdgcn_readfirstlane(x.zero[1]);
   const uint32_t k = h * uint32_t(x.d) + e;
-  sc = cs ? cs[k] : (t ? x.scale[1] : x.scale[0]);
-  zp = cz ? cz[k] : (t ? x.zero[1] : x.zero[0]);
+  sc = cs ? cs[k] : (t ? s1 : s0);
+  zp = cz ? cz[k] : (t ? z1 : z0);
+}
+
+// the same for the N consecutive elements [e0, e0 + N) of one row: one test
+// of the table pointers for all of them, the entries loaded side by side
+template <int N>
+__device__ __forceinline__ void xf_params_n(const RowXf &x, int t, uint32_t h, uint32_t e0,
+                                            float (&sc)[N], int32_t (&zp)[N]) {
+  const float *cs = t ? x.cs[1] : x.cs[0];
+  const int32_t *cz = t ? x.cz[1] : x.cz[0];
+  const float s0 = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x.scale[0])));
+  const float s1 = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x.scale[1])));
+  const int32_t z0 = __builtin_amdgcn_readfirstlane(x.zero[0]);
+  const int32_t z1 = __builtin_amdgcn_readfirstlane(x.zero[1]);
+  const uint32_t k0 = h * uint32_t(x.d) + e0;
+  if (cs) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) sc[k] = cs[k0 + k];
+  } else {
+#pragma unroll
+    for (int k = 0; k < N; ++k) sc[k] = t ? s1 : s0;
+  }
+  if (cz) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) zp[k] = cz[k0 + k];
+  } else {
+#pragma unroll
+    for (int k = 0; k < N; ++k) zp[k] = t ? z1 : z0;
+  }
 }
 
 // positions [p0, p0 + n) all have table rows (always, without rotation)
@@ -172,6 +209,9 @@ __device__ __forceinline__ typename Word<VEC>::T xf_word_of(const RowXf &x, int 
     // every load first (straight-line), then the arithmetic
     uint32_t xr[N], pr[N];
     float c[N], s[N];
+    float sc[N];
+    int32_t zp[N];
+    if constexpr (OB == 1) xf_params_n<N>(x, t, h, i * N, sc, zp);
 #pragma unroll
     for (int k = 0; k < N; ++k) {
       const uint32_t e = i * N + k;
@@ -197,10 +237,7 @@ __device__ __forceinline__ typename Word<VEC>::T xf_word_of(const RowXf &x, int 
         const uint16_t h = x.out_type == SWRT_XF_BF16 ? xf_bf16(v) : xf_f16(v);
         __builtin_memcpy(b + 2 * k, &h, 2);
       } else {
-        float sc;
-        int32_t zp;
-        xf_params(x, t, h, i * N + k, sc, zp);
-        b[k] = xf_byte(x, sc, zp, v);
+        b[k] = xf_byte(x, sc[k], zp[k], v);
       }
     }
   }
