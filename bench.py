@@ -22,11 +22,15 @@ Measurement
     3, over 512 MB of windowed caches touched between two uses of one set)
     are visited round robin, so no step finds its data in the 256 MB cache.
   - roofline: the dominant kernel (the one-launch step; with --form three the
-    window shift + append of the 12 layers) launched K times back to back
-    (buffer sets round robin) between one pair of HIP events on the launch
-    stream; achieved = its algorithmic bytes / its mean launch duration.
-  - cpu_baseline: the CPU oracle (single thread) on the same step, host copies
-    of the same inputs, for a bounded number of steps.
+    window shift + append of the 12 layers) launched back to back (buffer sets
+    round robin) in blocks, each between one pair of HIP events on the launch
+    stream; achieved = its algorithmic bytes / its median launch duration.
+  - every time is the median over blocks of steps (up to 10 blocks of at
+    least 20 steps; one block when K < 40).
+  - cpu_baseline: the CPU oracle on the same step, host copies of the same
+    inputs, for a bounded time: on every host core this process may use
+    (independent (layer, batch chunk) slices on a thread pool; `value`), and
+    on one thread; with the CPU model.
 
 One JSON line on stdout; progress on stderr.
 """
@@ -88,16 +92,40 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(step, seconds: float):
-    """The oracle as it stands, one host thread, on host copies of set 0."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def host_threads() -> int:
+    """The host cores this process may run on."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(step, seconds: float, threads: int = 1):
+    """The oracle as it stands on host copies of buffer set 0: one step is the
+    oracle's lengths call, then its windowed step on every windowed layer and
+    its TensorScatter on every full cache. With threads > 1 the independent
+    (windowed layer, batch chunk) slices, and per batch chunk the full caches'
+    scatters, are spread over a pool of host threads (the oracle's ctypes calls
+    release the interpreter lock): the batch partition of the CPU follow-up's
+    thread-pool MoveKvCacheRows."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import oracle
 
     orc = oracle.get()
     spec, b = step.spec, step.buffers
-    if b.xf is not None:
-        return cpu_baseline_xf(orc, step, seconds)
     D, H = spec.head_dim, spec.kv_heads
-    bits = torch.empty((), dtype=spec.dtype).element_size() * 8
 
     def host(t):
         return t.detach().cpu().contiguous().view(torch.uint8).numpy()
@@ -105,24 +133,69 @@ def cpu_baseline(step, seconds: float):
     wk = [host(t).copy() for t in b.win_k]
     wv = [host(t).copy() for t in b.win_v]
     wkn, wvn = [host(t) for t in b.win_kn], [host(t) for t in b.win_vn]
-    row = D * bits // 8
-    full_shape = (spec.batch, H, spec.max_seq, D)
+    row = D * torch.empty((), dtype=spec.dtype).element_size()
     # full caches: only the written rows are ever touched; their prior content
     # does not change the oracle's work, so they are left uninitialised
-    full = [np.empty((spec.batch, H, spec.max_seq, row), np.uint8)
-            for _ in range(2 * len(spec.full_layers))]
+    nf = len(spec.full_layers)
+    full = [np.empty((spec.batch, H, spec.max_seq, row), np.uint8) for _ in range(2 * nf)]
     fnew = [host(t) for t in b.full_kn + b.full_vn]
-    sk = spec.seqlens_k
+    sk, wi = spec.seqlens_k, spec.write_indices
+    xo = None
+    if b.xf is not None:  # the fused append's transform, as the oracle takes it
+        types = {torch.bfloat16: oracle.XF_BF16, torch.float16: oracle.XF_F16,
+                 torch.float32: oracle.XF_F32, torch.int8: oracle.XF_INT8,
+                 torch.uint8: oracle.XF_UINT8}
+        x = b.xf
+        xo = oracle.Transform(types[spec.new_dtype], types[spec.dtype],
+                              None if x.cos is None else x.cos.cpu().numpy(),
+                              None if x.sin is None else x.sin.cpu().numpy(),
+                              0 if x.cos is None else 2 * x.cos.shape[1], x.interleaved,
+                              (x.k_scale, x.v_scale), (x.k_zero_point, x.v_zero_point))
+    bits = row * 8 // D
+    # about two parts per thread: each windowed layer split into a few batch
+    # chunks, and every full cache's (cheap) scatter of one chunk in one part;
+    # finer parts cost more in pool hand-offs than they gain
+    chunks = max(1, min(spec.batch, -(-2 * threads // max(1, len(wk))))) if threads > 1 else 1
+    edges = [spec.batch * c // chunks for c in range(chunks + 1)]
+
+    def window_part(i, b0, b1, L):
+        if xo is None:
+            orc.kv_window_append_strided(wk[i][b0:b1], wv[i][b0:b1], wkn[i][b0:b1],
+                                         wvn[i][b0:b1], (H * D, D, D), 1, L.cache_past[b0:b1],
+                                         L.evict[b0:b1], elem_bits=bits, head_dim=D)
+        else:
+            orc.kv_window_append_xf(xo, wk[i][b0:b1], wv[i][b0:b1], wkn[i][b0:b1],
+                                    wvn[i][b0:b1], (H * D, D, D), 1, L.cache_past[b0:b1],
+                                    L.evict[b0:b1], L.past[b0:b1])
+
+    def full_part(b0, b1):
+        for i in range(len(full)):
+            c, u = full[i][b0:b1], fnew[i][b0:b1]
+            if xo is None:
+                orc.tensor_scatter_raw(c, c, u, wi[b0:b1], (b1 - b0, H, spec.max_seq, D), 2, 1,
+                                       0, bits)
+            else:
+                orc.tensor_scatter_xf(xo, i // nf, c, c, u, wi[b0:b1])
+
+    pool = ThreadPoolExecutor(max_workers=threads) if threads > 1 else None
 
     def one_step():
         L = orc.kv_seq_lengths(sk, 1, spec.window)
-        for i in range(len(wk)):
-            orc.kv_window_append_strided(wk[i], wv[i], wkn[i], wvn[i], (H * D, D, D), 1,
-                                         L.cache_past, L.evict, elem_bits=bits, head_dim=D)
-        for c, u in zip(full, fnew):
-            orc.tensor_scatter_raw(c, c, u, spec.write_indices, full_shape, 2, 1, 0, bits)
+        parts = [(window_part, (i, edges[c], edges[c + 1], L)) for i in range(len(wk))
+                 for c in range(chunks)]
+        parts += [(full_part, (edges[c], edges[c + 1])) for c in range(chunks)]
+        if pool is None:
+            for fn, a in parts:
+                fn(*a)
+        else:
+            for f in [pool.submit(fn, *a) for fn, a in parts]:
+                f.result()
 
-    return _time_steps(one_step, seconds)
+    try:
+        return _time_steps(one_step, seconds)
+    finally:
+        if pool is not None:
+            pool.shutdown()
 
 
 def _time_steps(one_step, seconds: float):
@@ -139,71 +212,54 @@ def _time_steps(one_step, seconds: float):
     return n, el
 
 
-def cpu_baseline_xf(orc, step, seconds: float):
-    """cpu_baseline for the fused-append step (workload 7)."""
-    import oracle
+def _reps(K: int) -> int:
+    """Timed blocks per measurement: blocks of at least 20 steps (a block's
+    first launch and its closing synchronization stay a small share), up to
+    10 of them, whose median is reported."""
+    return max(1, min(10, K // 20))
 
-    spec, b = step.spec, step.buffers
-    D, H = spec.head_dim, spec.kv_heads
 
-    def host(t):
-        return t.detach().cpu().contiguous().view(torch.uint8).numpy()
-
-    types = {torch.bfloat16: oracle.XF_BF16, torch.float16: oracle.XF_F16,
-             torch.float32: oracle.XF_F32, torch.int8: oracle.XF_INT8, torch.uint8: oracle.XF_UINT8}
-    x = b.xf
-    xo = oracle.Transform(types[spec.new_dtype], types[spec.dtype],
-                          None if x.cos is None else x.cos.cpu().numpy(),
-                          None if x.sin is None else x.sin.cpu().numpy(),
-                          0 if x.cos is None else 2 * x.cos.shape[1], x.interleaved,
-                          (x.k_scale, x.v_scale), (x.k_zero_point, x.v_zero_point))
-    wk = [host(t).copy() for t in b.win_k]
-    wv = [host(t).copy() for t in b.win_v]
-    wkn, wvn = [host(t) for t in b.win_kn], [host(t) for t in b.win_vn]
-    row = D * torch.empty((), dtype=spec.dtype).element_size()
-    # full caches: only the written rows are touched (see cpu_baseline)
-    nf = len(spec.full_layers)
-    full = [np.empty((spec.batch, H, spec.max_seq, row), np.uint8) for _ in range(2 * nf)]
-    fnew = [host(t) for t in b.full_kn + b.full_vn]
-    def one_step():
-        L = orc.kv_seq_lengths(spec.seqlens_k, 1, spec.window)
-        for i in range(len(wk)):
-            orc.kv_window_append_xf(xo, wk[i], wv[i], wkn[i], wvn[i], (H * D, D, D), 1,
-                                    L.cache_past, L.evict, L.past)
-        for i, (c, u) in enumerate(zip(full, fnew)):
-            orc.tensor_scatter_xf(xo, i // nf, c, c, u, spec.write_indices)
-
-    return _time_steps(one_step, seconds)
+def _median(xs):
+    return float(np.median(np.asarray(xs)))
 
 
 def _timers(stream, K, W):
-    """eager wall clock, event-timed device time and graph replay of fn(set)."""
+    """eager wall clock, event-timed device time and graph replay of fn(set),
+    each a list of per-step times, one per block of K // _reps(K) steps."""
     s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s0.record(stream)
     torch.cuda._sleep(1_000_000)
     s1.record(stream)
     torch.cuda.synchronize()
     cycles_per_s = 1_000_000 / (s0.elapsed_time(s1) * 1e-3)
+    R = _reps(K)
+    n = K // R
 
     def eager(fn, n_sets):
         for i in range(W):
             fn(i % n_sets)
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(K):
-            fn(i % n_sets)
-        torch.cuda.synchronize()
-        return (time.perf_counter() - t0) / K
+        out = []
+        for r in range(R):
+            t0 = time.perf_counter()
+            for i in range(n):
+                fn((r * n + i) % n_sets)
+            torch.cuda.synchronize()
+            out.append((time.perf_counter() - t0) / n)
+        return out
 
     def device(fn, n_sets, host_s):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda._sleep(int(cycles_per_s * min(2.0, 2.0 * K * host_s + 0.05)))
-        a.record(stream)
-        for i in range(K):
-            fn(i % n_sets)
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) * 1e-3 / K
+        out = []
+        for r in range(R):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda._sleep(int(cycles_per_s * min(2.0, 2.0 * n * host_s + 0.05)))
+            a.record(stream)
+            for i in range(n):
+                fn((r * n + i) % n_sets)
+            b.record(stream)
+            torch.cuda.synchronize()
+            out.append(a.elapsed_time(b) * 1e-3 / n)
+        return out
 
     def graph(fn, n_sets):
         graphs = []
@@ -215,11 +271,14 @@ def _timers(stream, K, W):
         for i in range(W):
             graphs[i % n_sets].replay()
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(K):
-            graphs[i % n_sets].replay()
-        torch.cuda.synchronize()
-        return (time.perf_counter() - t0) / K
+        out = []
+        for r in range(R):
+            t0 = time.perf_counter()
+            for i in range(n):
+                graphs[(r * n + i) % n_sets].replay()
+            torch.cuda.synchronize()
+            out.append((time.perf_counter() - t0) / n)
+        return out
 
     return eager, device, graph
 
@@ -303,9 +362,20 @@ def other_workload(args, dev):
             step(i % len(calls))
         torch.cuda.synchronize()
         host_s = (time.perf_counter() - t0) / max(W, 1)
-        eager_s = eager(step, len(calls))
-        device_s = device(step, len(calls), host_s)
-        graph_s = graph(step, len(calls))
+        eager_v = eager(step, len(calls))
+        device_v = device(step, len(calls), host_s)
+        graph_v = graph(step, len(calls))
+        parts = {}
+        if n == 2:  # each TensorScatter step of the workload on its own
+            for j, c in enumerate(cases):
+                pb = 2 * O * c.seq_len * row
+                dv = device(lambda i, j=j: calls[i][j](), len(calls), host_s)
+                ds = _median(dv)
+                parts[c.name] = {"bytes": pb, "device_us": round(ds * 1e6, 3),
+                                 "device_gbs": round(pb / ds / 1e9, 1),
+                                 "device_pct_of_hbm_peak": round(100 * pb / ds / 1e9 / HBM_PEAK_GBS,
+                                                                 2)}
+    eager_s, device_s, graph_s = _median(eager_v), _median(device_v), _median(graph_v)
     out = {
         "metric": "KV-cache update effective HBM GB/s (% of peak) and us per decode step",
         "value": round(step_bytes / eager_s / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
@@ -319,7 +389,10 @@ def other_workload(args, dev):
         "device_gbs": round(step_bytes / device_s / 1e9, 1),
         "device_pct_of_hbm_peak": round(100 * step_bytes / device_s / 1e9 / HBM_PEAK_GBS, 2),
         "graph_us_per_step": round(graph_s * 1e6, 2),
+        "timing": f"medians of {len(eager_v)} blocks of {args.steps // len(eager_v)} steps",
     }
+    if parts:
+        out["steps_alone"] = parts
     print(json.dumps(out))
 
 
@@ -453,10 +526,11 @@ def attention_bench(args, dev):
     eager, device, _ = _timers(stream, K, W)
     with torch.cuda.stream(stream):
         log(f"timing {K} attention launches ...")
-        att_s = eager(lambda i: steps[i].attention(), len(steps))
-        att_dev = device(lambda i: steps[i].attention(), len(steps), att_s)
+        att_s = _median(eager(lambda i: steps[i].attention(), len(steps)))
+        att_dev = _median(device(lambda i: steps[i].attention(), len(steps), att_s))
         log(f"timing {K} steps of append + attention ...")
-        both_s = eager(lambda i: (steps[i].run_fused(), steps[i].attention()), len(steps))
+        both_s = _median(eager(lambda i: (steps[i].run_fused(), steps[i].attention()),
+                               len(steps)))
         torch_copy, swrt_copy = copy_reference(dev, stream)
     flags = [int(st.buffers.flags.item()) for st in steps]
     if any(flags):
@@ -506,7 +580,7 @@ def attention_bench(args, dev):
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if meas is None else meas["read"] + meas["written"],
-                     "bytes_per_launch": byts, "mean_launch_us": round(att_dev * 1e6, 3)},
+                     "bytes_per_launch": byts, "median_launch_us": round(att_dev * 1e6, 3)},
         "cpu_baseline": cpu,
         "append_plus_attention_us_per_step": round(both_s * 1e6, 2),
         "copy_reference_gbs": {"torch_copy": round(torch_copy, 1),
@@ -535,8 +609,8 @@ def paged_bench(args, dev):
     eager, device, _ = _timers(stream, K, W)
     with torch.cuda.stream(stream):
         log(f"timing {K} paged attention launches ...")
-        att_s = eager(lambda i: steps[i].attention(), len(steps))
-        att_dev = device(lambda i: steps[i].attention(), len(steps), att_s)
+        att_s = _median(eager(lambda i: steps[i].attention(), len(steps)))
+        att_dev = _median(device(lambda i: steps[i].attention(), len(steps), att_s))
         torch_copy, swrt_copy = copy_reference(dev, stream)
         # the cooling conversion, in place on copies of each set's table
         blocks, dst, conv_written = steps[0].cooling_selection()
@@ -554,7 +628,7 @@ def paged_bench(args, dev):
                                 spec.cold_format, spec.v_scale, 0, spec.head_dim,
                                 pages_out=tables[i], flags=cflags[i])
         log(f"timing {K} conversions ...")
-        conv_s = eager(convert, len(steps))
+        conv_s = _median(eager(convert, len(steps)))
     flags = [int(st.flags.item()) for st in steps] + [int(f.item()) for f in cflags]
     if any(flags):
         raise SystemExit(f"device flags raised during the benchmark: {flags}")
@@ -606,7 +680,7 @@ def paged_bench(args, dev):
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if meas is None else meas["read"] + meas["written"],
-                     "bytes_per_launch": byts, "mean_launch_us": round(att_dev * 1e6, 3)},
+                     "bytes_per_launch": byts, "median_launch_us": round(att_dev * 1e6, 3)},
         "cpu_baseline": cpu,
         "cooling_conversion": {"pages": int(len(blocks)), "us_per_call": round(conv_s * 1e6, 2),
                                "bytes_read": int(conv_read), "bytes_written": int(conv_written),
@@ -626,7 +700,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp8_e4m3fn"])
     ap.add_argument("--sets", type=int, default=3, help="independent buffer sets, round robin")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="seconds of CPU oracle work per leg (all host cores, then one thread)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--form", default="fused", choices=["fused", "three"],
                     help="one launch per step (default) or the three-call composition")
@@ -674,6 +749,8 @@ def main():
 
     stream = torch.cuda.Stream()
     K, W = args.steps, args.warmup
+    R = _reps(K)  # timed blocks, medians reported
+    NB = K // R
     fused = args.form == "fused"
     with torch.cuda.stream(stream):
         def graph_time(fn):
@@ -691,32 +768,40 @@ def main():
             for i in range(W):
                 graphs[i % len(graphs)].replay()
             torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            for i in range(K):
-                graphs[i % len(graphs)].replay()
-            torch.cuda.synchronize()
-            return (time.perf_counter() - t0) / K
+            out = []
+            for r in range(R):
+                t0 = time.perf_counter()
+                for i in range(NB):
+                    graphs[(r * NB + i) % len(graphs)].replay()
+                torch.cuda.synchronize()
+                out.append((time.perf_counter() - t0) / NB)
+            return out
 
         def eager_time(fn):
             """K steps issued from the host (arguments marshalled once), wall
-            clock between two synchronizations."""
+            clock between two synchronizations, per block of NB steps."""
             for i in range(W):
                 fn(steps[i % len(steps)])
             torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            for i in range(K):
-                fn(steps[i % len(steps)])
-            torch.cuda.synchronize()
-            return (time.perf_counter() - t0) / K
+            out = []
+            for r in range(R):
+                t0 = time.perf_counter()
+                for i in range(NB):
+                    fn(steps[(r * NB + i) % len(steps)])
+                torch.cuda.synchronize()
+                out.append((time.perf_counter() - t0) / NB)
+            return out
 
         log(f"timing {K} eager steps, one launch per step ...")
-        eager_fused_s = eager_time(lambda st: st.run_fused())
+        eager_fused_v = eager_time(lambda st: st.run_fused())
         log(f"timing {K} eager steps, three launches per step ...")
-        eager_three_s = eager_time(lambda st: st.run_three())
+        eager_three_v = eager_time(lambda st: st.run_three())
         log(f"timing {K} graph-replayed steps, one launch per step ...")
-        graph_fused_s = graph_time(lambda st: st.run_fused())
+        graph_fused_v = graph_time(lambda st: st.run_fused())
         log(f"timing {K} graph-replayed steps, three launches per step ...")
-        graph_three_s = graph_time(lambda st: st.run_three())
+        graph_three_v = graph_time(lambda st: st.run_three())
+        eager_fused_s, eager_three_s = _median(eager_fused_v), _median(eager_three_v)
+        graph_fused_s, graph_three_s = _median(graph_fused_v), _median(graph_three_v)
 
         # ---- kernels alone: HIP events ----
         # The host needs longer to issue a launch than the GPU to run it. A
@@ -736,21 +821,24 @@ def main():
         cycles_per_s = 1_000_000 / (s0.elapsed_time(s1) * 1e-3)
 
         def events_block(fn):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda._sleep(int(cycles_per_s * min(2.0, 2.0 * K * host_step_s + 0.05)))
-            a.record(stream)
-            for i in range(K):
-                fn(steps[i % len(steps)])
-            b.record(stream)
-            torch.cuda.synchronize()
-            return a.elapsed_time(b) * 1e-3 / K
+            out = []
+            for r in range(R):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda._sleep(int(cycles_per_s * min(2.0, 2.0 * NB * host_step_s + 0.05)))
+                a.record(stream)
+                for i in range(NB):
+                    fn(steps[(r * NB + i) % len(steps)])
+                b.record(stream)
+                torch.cuda.synchronize()
+                out.append(a.elapsed_time(b) * 1e-3 / NB)
+            return out
 
         log(f"timing {K} launches of the one-launch step ...")
-        fused_mean_s = events_block(lambda st: st.run_fused())
+        fused_mean_s = _median(events_block(lambda st: st.run_fused()))
         log(f"timing {K} launches of the window kernel alone ...")
-        win_mean_s = events_block(lambda st: st.windowed())
+        win_mean_s = _median(events_block(lambda st: st.windowed()))
         log(f"timing {K} three-launch steps ...")
-        three_eager_s = events_block(lambda st: st.run_three())
+        three_eager_s = _median(events_block(lambda st: st.run_three()))
 
         torch_copy, swrt_copy = copy_reference(dev, stream)
 
@@ -776,13 +864,22 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        log(f"timing the CPU oracle for about {args.cpu_seconds:.0f} s ...")
-        n, el = cpu_baseline(steps[0], args.cpu_seconds)
-        cpu = {"value": round(acct["total"] * n / el / 1e9, 4), "unit": "GB/s", "cores": 1,
+        nt = host_threads()
+        log(f"timing the CPU oracle for about {args.cpu_seconds:.0f} s on {nt} threads ...")
+        n, el = cpu_baseline(steps[0], args.cpu_seconds, threads=nt)
+        log(f"timing the CPU oracle for about {args.cpu_seconds:.0f} s on one thread ...")
+        n1, el1 = cpu_baseline(steps[0], args.cpu_seconds, threads=1)
+        cpu = {"value": round(acct["total"] * n / el / 1e9, 4), "unit": "GB/s", "cores": nt,
                "kind": "oracle",
                "sample": f"{n} whole-model decode steps of the same workload (host copies of "
-                         f"buffer set 0), one thread, {el:.1f} s",
-               "us_per_step": round(el / n * 1e6, 1)}
+                         f"buffer set 0), (layer, batch chunk) slices over {nt} threads, "
+                         f"{el:.1f} s",
+               "us_per_step": round(el / n * 1e6, 1),
+               "cpu_model": cpu_model(),
+               "single_thread": {"value": round(acct["total"] * n1 / el1 / 1e9, 4),
+                                 "unit": "GB/s", "cores": 1,
+                                 "us_per_step": round(el1 / n1 * 1e6, 1),
+                                 "sample": f"{n1} steps, one thread, {el1:.1f} s"}}
 
     out = {
         "metric": "KV-cache update effective HBM GB/s (% of peak) and us per decode step",
@@ -815,9 +912,10 @@ def main():
                      "tensor_scatter_xf)" if xf else
                      "three launches per step (kv_seq_lengths, kv_window_append_layers, "
                      "tensor_scatter_batched)"),
-            "timing": "eager: library calls with arguments marshalled once, K steps between "
-                      "two synchronizations" if args.timing == "eager" else
-                      "HIP graph replay, one graph per buffer set",
+            "timing": ("eager: library calls with arguments marshalled once, steps between "
+                       "two synchronizations" if args.timing == "eager" else
+                       "HIP graph replay, one graph per buffer set") +
+                      f"; medians of {R} blocks of {NB} steps",
             "cache_defeat": f"{args.sets} independent buffer sets round robin",
         },
         "roofline": {
@@ -829,7 +927,7 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
             "bytes_per_launch": kbytes,
-            "mean_launch_us": round(kmean * 1e6, 3),
+            "median_launch_us": round(kmean * 1e6, 3),
         },
         "cpu_baseline": cpu,
         "one_launch": {"graph_us_per_step": round(graph_fused_s * 1e6, 2),
