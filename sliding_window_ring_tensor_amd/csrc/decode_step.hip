@@ -227,8 +227,8 @@ int decode_step(int n_window_layers, void *const *win_k_caches, void *const *win
   a.full_blocks = sp.empty ? 0 : sp.tiles * uint32_t(sp.n);
   a.len_blocks = do_len ? uint32_t((B + block - 1) / block) : 0;
   const int spw = wp.empty || drift ? 1
-                                    : slices_per_group(capacity, wp.g.row_words,
-                                                       xf ? int64_t(head_dim) : 0, kXfLaneElems);
+                                    : slices_per_group(capacity, wp.g.row_words, xf != nullptr,
+                                                       xf ? int64_t(head_dim) : 0);
   a.win_blocks = wp.empty ? 0 : (wp.slices + spw - 1) / spw;
   uint64_t grid = uint64_t(a.full_blocks) + a.win_blocks;
   if (grid < a.len_blocks) grid = a.len_blocks;  // length arrays alone

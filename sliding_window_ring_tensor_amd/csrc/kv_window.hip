@@ -157,9 +157,8 @@ int launch(const WindowPlan &p, unsigned phase, hipStream_t stream) {
   a.g = p.g;
   a.xf = p.xf;
   if (p.g.S == 1) {
-    const int spw = slices_per_group(p.g.C, p.g.row_words,
-                                     XF ? int64_t(p.g.row_bytes / uint64_t(p.xf.out_bytes)) : 0,
-                                     kXfLaneElems);
+    const int spw = slices_per_group(p.g.C, p.g.row_words, XF,
+                                     XF ? int64_t(p.g.row_bytes / uint64_t(p.xf.out_bytes)) : 0);
     const dim3 grid((p.slices + spw - 1) / spw);
     if (spw == 4)
       hipLaunchKernelGGL((window_in_place<VEC, NL, 4, XF>), grid, dim3(kWinBlock), 0, stream, a);

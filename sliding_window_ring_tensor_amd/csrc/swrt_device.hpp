@@ -62,6 +62,14 @@ __device__ __forceinline__ void st(T *p, T v) {
 #endif
 }
 
+// a 64-bit value that is equal on every lane of the wave, from its first lane
+// (it then lives in scalar registers)
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
+  const uint32_t lo = uint32_t(__builtin_amdgcn_readfirstlane(int32_t(uint32_t(v))));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_readfirstlane(int32_t(uint32_t(v >> 32))));
+  return (uint64_t(hi) << 32) | lo;
+}
+
 // ---------------------------------------------------------------------------
 // n / d for 0 <= n < 2^31 with a precomputed multiplier (round-up method:
 // l = ceil(log2 d), m = floor(2^32 (2^l - d) / d) + 1, q = (mulhi(n, m) + n) >> l).

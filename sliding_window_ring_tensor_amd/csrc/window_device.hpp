@@ -158,13 +158,13 @@ __device__ __forceinline__ void shift_append_slice(char *base, const char *new_r
   W *dst = reinterpret_cast<W *>(base);
   // The new row lives in its own buffer: fetch it first so its latency
   // overlaps the shift; it is stored at row Lp - E. (XF: its elements, one
-  // or a few per lane, as XfLanes.)
+  // or a few per lane, as XfLanes, in the waves that hold some.)
   const W *nsrc = reinterpret_cast<const W *>(new_row);
   W *adst = reinterpret_cast<W *>(base + uint64_t(Lp - E) * row_bytes);
   const bool row_in_one_pass = XF || row_words <= uint32_t(BLOCK);
   const uint32_t ai = min(threadIdx.x, row_words - 1);
   W nv;
-  XfLanes xl;
+  XfLanes<> xl;
   uint32_t D = 0;
   // XF: the row's loads go out right after the first tile's (or alone when
   // nothing shifts), never ahead of a wait the shift's addresses need
@@ -172,11 +172,16 @@ __device__ __forceinline__ void shift_append_slice(char *base, const char *new_r
     D = uint32_t(row_bytes) / uint32_t(xf->out_bytes);
   else if (row_in_one_pass)
     nv = ld(nsrc + ai);
+  const bool row_wave = (threadIdx.x & ~63u) < D;  // uniform in a wave
   const auto append = [&]() {
-    if constexpr (XF)
-      xf_lanes_store(xl, *xf, t, reinterpret_cast<char *>(adst), threadIdx.x, BLOCK, D);
-    else
+    if constexpr (XF) {
+      if (row_wave) {
+        xf_lanes_encode(xl, *xf, t, threadIdx.x, BLOCK, D);
+        xf_lanes_put(xl, *xf, reinterpret_cast<char *>(adst), threadIdx.x, BLOCK, D);
+      }
+    } else {
       st(adst + ai, nv);
+    }
   };
   bool appended = false;
   if (E) {
@@ -187,30 +192,31 @@ __device__ __forceinline__ void shift_append_slice(char *base, const char *new_r
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u) v[u] = ld(src + min(c0 + u * BLOCK + threadIdx.x, n - 1));
       if constexpr (XF) {
-        if (c0 == 0) xf_lanes_load(xl, *xf, t, h, new_row, pos, threadIdx.x, BLOCK, D);
-        xf_lanes_hold(xl);
+        if (c0 == 0 && row_wave) {
+          xf_lanes_load(xl, *xf, t, h, new_row, pos, threadIdx.x, BLOCK, D);
+          xf_lanes_hold(xl);
+        }
       }
       __syncthreads();  // every old value of this tile is in registers
       // Row Lp - E is no shift destination, and from here on every load of
       // every tile (this last one's included) has returned: the new row can
-      // go out now (a copy before the tile's stores; a transformed row after
-      // them, so its arithmetic overlaps their draining).
+      // go out now, before the tile's stores, so that no work follows them
+      // (work after a store that reuses its registers waits for the store to
+      // complete).
       const bool last = row_in_one_pass && c0 + uint32_t(BLOCK * UNROLL) >= n;
-      if (!XF && last) {
+      if (last) {
         append();
         appended = true;
       }
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u) st(dst + min(c0 + u * BLOCK + threadIdx.x, n - 1), v[u]);
-      if (XF && last) {
-        append();
-        appended = true;
-      }
     }
   }
   if (!appended) {  // no shift, or a row wider than one pass: after every load
     if (row_in_one_pass) {
-      if constexpr (XF) xf_lanes_load(xl, *xf, t, h, new_row, pos, threadIdx.x, BLOCK, D);
+      if constexpr (XF) {
+        if (row_wave) xf_lanes_load(xl, *xf, t, h, new_row, pos, threadIdx.x, BLOCK, D);
+      }
       append();
     } else {
       for (uint32_t i = threadIdx.x; i < row_words; i += BLOCK) st(adst + i, ld(nsrc + i));
@@ -246,10 +252,31 @@ struct SliceWork {
   bool ok;
 };
 
+// the work of one wave's slice, its integers taken from the first lane (they
+// are equal on every lane of the wave; the pointers stay as they are, so the
+// compiler keeps their global address space)
+__device__ __forceinline__ SliceWork wave_uniform(const SliceWork &w) {
+  SliceWork u = w;
+  u.Lp = int64_t(uniform_u64(uint64_t(w.Lp)));
+  u.E = int64_t(uniform_u64(uint64_t(w.E)));
+  u.pos = int64_t(uniform_u64(uint64_t(w.pos)));
+  u.t = __builtin_amdgcn_readfirstlane(w.t);
+  u.h = uint32_t(__builtin_amdgcn_readfirstlane(int32_t(w.h)));
+  u.ok = __builtin_amdgcn_readfirstlane(int32_t(w.ok)) != 0;
+  return u;
+}
+
 #ifndef SWRT_GROUP_UNROLL
 #define SWRT_GROUP_UNROLL 2
 #endif
 constexpr int kGroupUnroll = SWRT_GROUP_UNROLL;  // words per lane per slice in group mode
+// A fused append's subgroup takes more words a lane, so that more slices share
+// a workgroup: its row costs a few dependent steps (loads, arithmetic, store)
+// that more slices in flight per workgroup hide; a plain copy gains nothing
+// from it.
+constexpr int kGroupUnrollXf = 4;
+template <bool XF>
+constexpr int group_unroll() { return XF ? kGroupUnrollXf : kGroupUnroll; }
 
 template <int VEC, int SPW, bool XF = false, typename Info>
 __device__ __forceinline__ void shift_append_group(uint32_t first_slice, uint32_t n_slices,
@@ -268,6 +295,11 @@ __device__ __forceinline__ void shift_append_group(uint32_t first_slice, uint32_
     if (first_slice + g < n_slices) x = info(first_slice + g, g);
     if (grp == uint32_t(g)) w = x;
   }
+  // A subgroup is whole waves: each wave holds one slice's work. Saying so
+  // keeps it in scalar registers, so that what it selects (a tensor's table
+  // pointers among the kernel arguments) is a scalar load, not a vector load
+  // whose wait would also drain the shift's loads issued before it.
+  w = wave_uniform(w);
   // n, the words to shift, and w.ok are uniform inside a subgroup, so the two
   // predicated blocks below never split a wave. A slice with nothing to shift
   // (E = 0) points its shift words at the appended row: the same value to the
@@ -279,9 +311,13 @@ __device__ __forceinline__ void shift_append_group(uint32_t first_slice, uint32_
   W *adst = reinterpret_cast<W *>(w.base + uint64_t(w.Lp - w.E) * row_bytes) + ai;
   const W *src = reinterpret_cast<const W *>(w.base + uint64_t(w.E) * row_bytes);
   W *dst = reinterpret_cast<W *>(w.base);
-  W v[kGroupUnroll], nv;
-  XfLanes xl;
+  constexpr int GU = group_unroll<XF>();
+  W v[GU], nv;
+  XfLanes<1> xl;  // a row of a fused group fits its subgroup's lanes
   const uint32_t D = XF ? uint32_t(row_bytes) / uint32_t(xf->out_bytes) : 0;
+  // the waves that hold elements of the appended row (uniform in a wave): the
+  // others of the subgroup only shift
+  const bool row_wave = (lid & ~63u) < D;
   if (w.ok) {
     if constexpr (XF) {
       // the appended row is transformed, not copied: a slice with nothing to
@@ -289,27 +325,34 @@ __device__ __forceinline__ void shift_append_group(uint32_t first_slice, uint32_
       // row's loads follow the shift's (no wait for them precedes a shift load)
       if (n) {
 #pragma unroll
-        for (int u = 0; u < kGroupUnroll; ++u) v[u] = ld(src + min(u * GB + lid, n - 1));
+        for (int u = 0; u < GU; ++u) v[u] = ld(src + min(u * GB + lid, n - 1));
       }
-      xf_lanes_load(xl, *xf, w.t, w.h, w.new_row, w.pos, lid, GB, D);
-      xf_lanes_hold(xl);
+      if (row_wave) {
+        xf_lanes_load(xl, *xf, w.t, w.h, w.new_row, w.pos, lid, GB, D);
+        xf_lanes_hold(xl);
+      }
     } else {
       nv = ld(nsrc);
 #pragma unroll
-      for (int u = 0; u < kGroupUnroll; ++u) v[u] = ld(n ? src + min(u * GB + lid, n - 1) : nsrc);
+      for (int u = 0; u < GU; ++u) v[u] = ld(n ? src + min(u * GB + lid, n - 1) : nsrc);
     }
   }
   __syncthreads();  // every old value of every slice of the workgroup is in registers
   if (w.ok) {
-    if constexpr (XF) {  // the shift's stores first: the transform overlaps them
+    if constexpr (XF) {
+      // the row first, so that nothing follows the shift's stores (work after
+      // a store that reuses its registers waits for the store to complete)
+      if (row_wave) {
+        xf_lanes_encode(xl, *xf, w.t, lid, GB, D);
+        xf_lanes_put(xl, *xf, w.base + uint64_t(w.Lp - w.E) * row_bytes, lid, GB, D);
+      }
       if (n) {
 #pragma unroll
-        for (int u = 0; u < kGroupUnroll; ++u) st(dst + min(u * GB + lid, n - 1), v[u]);
+        for (int u = 0; u < GU; ++u) st(dst + min(u * GB + lid, n - 1), v[u]);
       }
-      xf_lanes_store(xl, *xf, w.t, w.base + uint64_t(w.Lp - w.E) * row_bytes, lid, GB, D);
     } else {
 #pragma unroll
-      for (int u = 0; u < kGroupUnroll; ++u) st(n ? dst + min(u * GB + lid, n - 1) : adst, v[u]);
+      for (int u = 0; u < GU; ++u) st(n ? dst + min(u * GB + lid, n - 1) : adst, v[u]);
       st(adst, nv);
     }
   }
@@ -318,16 +361,18 @@ __device__ __forceinline__ void shift_append_group(uint32_t first_slice, uint32_
 // Slices per workgroup for an in-place launch: the most (1, 2 or 4) whose
 // subgroup tile still holds a whole shift and whose subgroup covers a row.
 //
-// A fused append spreads the appended row over its subgroup's kWinBlock / spw
-// lanes, at most lane_elems elements per lane: row_elems > 0 also keeps the
-// subgroup wide enough for that row.
-inline int slices_per_group(int64_t capacity, uint32_t row_words, int64_t row_elems = 0,
-                            int lane_elems = 0) {
+// A fused append (xf) gives each lane of the subgroup (kWinBlock / spw lanes)
+// one element of the appended row, row_elems of them: the subgroup is also at
+// least as wide as that row (wider rows take the one-slice shape, a few
+// elements a lane). Its subgroups take group_unroll<true>() words a lane.
+inline int slices_per_group(int64_t capacity, uint32_t row_words, bool xf = false,
+                            int64_t row_elems = 0) {
+  const uint64_t gu = xf ? group_unroll<true>() : group_unroll<false>();
   int spw = 1;
   while (spw < 4 &&
-         uint64_t(capacity - 1) * row_words <= uint64_t(kWinBlock / (2 * spw)) * kGroupUnroll &&
+         uint64_t(capacity - 1) * row_words <= uint64_t(kWinBlock / (2 * spw)) * gu &&
          row_words <= uint32_t(kWinBlock / (2 * spw)) &&
-         (row_elems <= 0 || row_elems <= int64_t(lane_elems) * (kWinBlock / (2 * spw))))
+         row_elems <= int64_t(kWinBlock / (2 * spw)))
     spw *= 2;
   return spw;
 }

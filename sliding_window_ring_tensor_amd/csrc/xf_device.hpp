@@ -68,8 +68,13 @@ __device__ __forceinline__ void xf_params(const RowXf &x, int t, uint32_t h, uin
   const int32_t z0 = __builtin_amdgcn_readfirstlane(x.zero[0]);
   const int32_t z1 = __builtin_amdgcn_readfirstlane(x.zero[1]);
   const uint32_t k = h * uint32_t(x.d) + e;
-  sc = cs ? cs[k] : (t ? s1 : s0);
-  zp = cz ? cz[k] : (t ? z1 : z0);
+  // the default first, a table entry loaded over it: the path without a table
+  // writes no register that a load of the other path may still be filling
+  // (such a write would wait for every load in flight)
+  sc = t ? s1 : s0;
+  zp = t ? z1 : z0;
+  if (cs) sc = cs[k];
+  if (cz) zp = cz[k];
 }
 
 // the same for the N consecutive elements [e0, e0 + N) of one row: one test
@@ -84,19 +89,15 @@ __device__ __forceinline__ void xf_params_n(const RowXf &x, int t, uint32_t h, u
   const int32_t z0 = __builtin_amdgcn_readfirstlane(x.zero[0]);
   const int32_t z1 = __builtin_amdgcn_readfirstlane(x.zero[1]);
   const uint32_t k0 = h * uint32_t(x.d) + e0;
+#pragma unroll
+  for (int k = 0; k < N; ++k) sc[k] = t ? s1 : s0, zp[k] = t ? z1 : z0;
   if (cs) {
 #pragma unroll
     for (int k = 0; k < N; ++k) sc[k] = cs[k0 + k];
-  } else {
-#pragma unroll
-    for (int k = 0; k < N; ++k) sc[k] = t ? s1 : s0;
   }
   if (cz) {
 #pragma unroll
     for (int k = 0; k < N; ++k) zp[k] = cz[k0 + k];
-  } else {
-#pragma unroll
-    for (int k = 0; k < N; ++k) zp[k] = t ? z1 : z0;
   }
 }
 
@@ -284,15 +285,31 @@ __device__ __forceinline__ typename Word<VEC>::T xf_word(const RowXf &x, int t, 
 // ---------------------------------------------------------------------------
 constexpr int kXfLaneElems = 8;
 
+// M: the most elements a lane holds. The registers of all M stay allocated
+// for the whole kernel, so kernels whose rows always fit their lanes (one
+// element each) take M = 1 and keep their occupancy.
+template <int M = kXfLaneElems>
 struct XfLanes {
-  uint32_t x[kXfLaneElems], p[kXfLaneElems];  // raw bits of the element and its partner
-  float c[kXfLaneElems], s[kXfLaneElems];     // its table entries (rotated K only)
-  float scale[kXfLaneElems];                  // its scale and zero point (byte targets)
-  int32_t zero[kXfLaneElems];
+  uint32_t x[M], p[M];  // raw bits of the element and its partner
+  float c[M], s[M];     // its table entries (rotated K only)
+  float scale[M];       // its scale and zero point (byte targets)
+  int32_t zero[M];
 };
 
-template <int IN>
-__device__ __forceinline__ void xf_lane_load_one(XfLanes &l, int k, const RowXf &x, int t,
+// Make the loaded values live here: called after the shift's loads are
+// issued and before its barrier, it keeps the compiler from sinking the
+// loads past the barrier to their uses (which would wait for each of them in
+// turn); the wait it implies covers the older loads only.
+template <int M>
+__device__ __forceinline__ void xf_lanes_hold(XfLanes<M> &l) {
+#pragma unroll
+  for (int k = 0; k < M; ++k)
+    asm volatile("" : "+v"(l.x[k]), "+v"(l.p[k]), "+v"(l.c[k]), "+v"(l.s[k]), "+v"(l.scale[k]),
+                 "+v"(l.zero[k]));
+}
+
+template <int IN, int M>
+__device__ __forceinline__ void xf_lane_load_one(XfLanes<M> &l, int k, const RowXf &x, int t,
                                                  uint32_t h, bool rot, const char *row,
                                                  const float *cr, const float *sr, uint32_t e) {
   l.x[k] = xf_raw_t<IN>(row, e);
@@ -309,32 +326,74 @@ __device__ __forceinline__ void xf_lane_load_one(XfLanes &l, int k, const RowXf 
   }
 }
 
-template <int IN>
-__device__ __forceinline__ void xf_lanes_load_t(XfLanes &l, const RowXf &x, int t, uint32_t h,
+template <int IN, int M>
+__device__ __forceinline__ void xf_lanes_load_t(XfLanes<M> &l, const RowXf &x, int t, uint32_t h,
                                                 bool rot, const char *row, const float *cr,
                                                 const float *sr, uint32_t lane, uint32_t n,
                                                 uint32_t D, uint32_t m) {
 #pragma unroll
-  for (int k = 0; k < kXfLaneElems; ++k) {
+  for (int k = 0; k < M; ++k) {
     l.x[k] = l.p[k] = 0, l.c[k] = l.s[k] = 0.0f;
     l.scale[k] = 1.0f, l.zero[k] = 0;
   }
-  if (m == 1) {  // the usual row: one element per lane, straight-line
+  if (M == 1 || m == 1) {  // the usual row: one element per lane, straight-line
     xf_lane_load_one<IN>(l, 0, x, t, h, rot, row, cr, sr, min(lane, D - 1));
     return;
   }
 #pragma unroll
-  for (int k = 0; k < kXfLaneElems; ++k)
+  for (int k = 0; k < M; ++k)
     if (uint32_t(k) < m)  // uniform
       xf_lane_load_one<IN>(l, k, x, t, h, rot, row, cr, sr, min(lane + k * n, D - 1));
+}
+
+// One element a lane (M = 1), for one input type: every load is issued
+// whatever the lane's role, and the values are held in the same branch, so
+// the load phase is straight-line and its only wait is the hold's, after
+// every load in flight (the shift's among them) has been issued. A branch
+// join between the loads and the hold would cost a wait of its own (a value
+// narrower than its register is widened after the join), and such a wait
+// drains the shift's loads too. A lane that does not rotate (a V row, an
+// element past rotary_dim) loads its own element as partner and the first
+// entries of its table row, and ignores them.
+template <int IN>
+__device__ __forceinline__ void xf_lane_load1_t(XfLanes<1> &l, const RowXf &x, int t, uint32_t h,
+                                                const char *row, int64_t pos, uint32_t lane,
+                                                uint32_t D) {
+  const uint32_t e = min(lane, D - 1);
+  l.x[0] = xf_raw_t<IN>(row, e);
+  l.p[0] = 0;
+  l.c[0] = l.s[0] = 0.0f;
+  l.scale[0] = 1.0f, l.zero[0] = 0;
+  if (x.out_bytes == 1) xf_params(x, t, h, e, l.scale[0], l.zero[0]);
+  if (x.cos) {  // uniform: tables given (the position has a row, K and V alike)
+    const bool r = t == 0 && e < uint32_t(2 * x.half);
+    bool first;
+    uint32_t j, pe;
+    xf_pair(x, min(e, uint32_t(2 * x.half) - 1), first, j, pe);
+    const int64_t at = pos * x.half + (r ? j : 0);
+    l.p[0] = xf_raw_t<IN>(row, r ? pe : e);
+    l.c[0] = x.cos[at];
+    l.s[0] = x.sin[at];
+  }
+  xf_lanes_hold(l);
 }
 
 // (t may differ between the waves of a workgroup; picking a scalar parameter
 // may then become a load, issued here with the others; per-channel
 // parameters are loads of their own)
-__device__ __forceinline__ void xf_lanes_load(XfLanes &l, const RowXf &x, int t, uint32_t h,
+template <int M>
+__device__ __forceinline__ void xf_lanes_load(XfLanes<M> &l, const RowXf &x, int t, uint32_t h,
                                               const char *row, int64_t pos, uint32_t lane,
                                               uint32_t n, uint32_t D) {
+  if constexpr (M == 1) {
+    if (x.in_type == SWRT_XF_F32)
+      xf_lane_load1_t<SWRT_XF_F32>(l, x, t, h, row, pos, lane, D);
+    else if (x.in_type == SWRT_XF_BF16)
+      xf_lane_load1_t<SWRT_XF_BF16>(l, x, t, h, row, pos, lane, D);
+    else
+      xf_lane_load1_t<SWRT_XF_F16>(l, x, t, h, row, pos, lane, D);
+    return;
+  }
   const uint32_t m = (D + n - 1) / n;  // elements per lane (uniform)
   const bool rot = t == 0 && x.cos;
   const float *cr = rot ? x.cos + pos * x.half : nullptr;
@@ -347,58 +406,66 @@ __device__ __forceinline__ void xf_lanes_load(XfLanes &l, const RowXf &x, int t,
     xf_lanes_load_t<SWRT_XF_F16>(l, x, t, h, rot, row, cr, sr, lane, n, D, m);
 }
 
-// Make the loaded values live here: called after the shift's loads are
-// issued and before its barrier, it keeps the compiler from sinking the
-// loads past the barrier to their uses (which would wait for each of them in
-// turn); the wait it implies covers the older loads only.
-__device__ __forceinline__ void xf_lanes_hold(XfLanes &l) {
-#pragma unroll
-  for (int k = 0; k < kXfLaneElems; ++k)
-    asm volatile("" : "+v"(l.x[k]), "+v"(l.p[k]), "+v"(l.c[k]), "+v"(l.s[k]), "+v"(l.scale[k]),
-                 "+v"(l.zero[k]));
-}
-
-template <int IN>
-__device__ __forceinline__ void xf_lane_store_one(const XfLanes &l, int k, const RowXf &x,
-                                                  bool rot, char *dst, uint32_t e) {
+// The cache bits of lane element k (element e of the row; out_bytes wide, in
+// the low bits)
+template <int IN, int M>
+__device__ __forceinline__ uint32_t xf_lane_encode_one(const XfLanes<M> &l, int k, const RowXf &x,
+                                                       bool rot, uint32_t e) {
   const float v = xf_rotate<IN>(x, rot, e, l.x[k], l.p[k], l.c[k], l.s[k]);
-  if (x.out_bytes == 4) {
-    __builtin_nontemporal_store(v != v ? 0x7FC00000u : __float_as_uint(v),
-                                reinterpret_cast<uint32_t *>(dst) + e);
-  } else if (x.out_bytes == 2) {
-    __builtin_nontemporal_store(x.out_type == SWRT_XF_BF16 ? xf_bf16(v) : xf_f16(v),
-                                reinterpret_cast<uint16_t *>(dst) + e);
-  } else {
-    __builtin_nontemporal_store(xf_byte(x, l.scale[k], l.zero[k], v),
-                                reinterpret_cast<uint8_t *>(dst) + e);
-  }
+  if (x.out_bytes == 4) return v != v ? 0x7FC00000u : __float_as_uint(v);
+  if (x.out_bytes == 2) return x.out_type == SWRT_XF_BF16 ? xf_bf16(v) : xf_f16(v);
+  return xf_byte(x, l.scale[k], l.zero[k], v);
 }
 
-template <int IN>
-__device__ __forceinline__ void xf_lanes_store_t(const XfLanes &l, const RowXf &x, int t,
-                                                 char *dst, uint32_t lane, uint32_t n,
-                                                 uint32_t D) {
+template <int IN, int M>
+__device__ __forceinline__ void xf_lanes_encode_t(XfLanes<M> &l, const RowXf &x, int t,
+                                                  uint32_t lane, uint32_t n, uint32_t D) {
   const uint32_t m = (D + n - 1) / n;
   const bool rot = t == 0 && x.cos;
-  if (m == 1) {
-    if (lane < D) xf_lane_store_one<IN>(l, 0, x, rot, dst, lane);
+  if (M == 1 || m == 1) {
+    if (lane < D) l.x[0] = xf_lane_encode_one<IN>(l, 0, x, rot, lane);
     return;
   }
 #pragma unroll
-  for (int k = 0; k < kXfLaneElems; ++k) {
+  for (int k = 0; k < M; ++k) {
     const uint32_t e = lane + k * n;
-    if (uint32_t(k) < m && e < D) xf_lane_store_one<IN>(l, k, x, rot, dst, e);
+    if (uint32_t(k) < m && e < D) l.x[k] = xf_lane_encode_one<IN>(l, k, x, rot, e);
   }
 }
 
-__device__ __forceinline__ void xf_lanes_store(const XfLanes &l, const RowXf &x, int t, char *dst,
-                                               uint32_t lane, uint32_t n, uint32_t D) {
+// Turn the held elements into their cache bits, in place (l.x), once their
+// loads have returned and before the stores of the step: nothing computed
+// after a store then reuses its data registers (on this target the store
+// counter is the load counter, and such a reuse would wait for the store to
+// complete before the wave could go on and end).
+template <int M>
+__device__ __forceinline__ void xf_lanes_encode(XfLanes<M> &l, const RowXf &x, int t,
+                                                uint32_t lane, uint32_t n, uint32_t D) {
   if (x.in_type == SWRT_XF_F32)
-    xf_lanes_store_t<SWRT_XF_F32>(l, x, t, dst, lane, n, D);
+    xf_lanes_encode_t<SWRT_XF_F32>(l, x, t, lane, n, D);
   else if (x.in_type == SWRT_XF_BF16)
-    xf_lanes_store_t<SWRT_XF_BF16>(l, x, t, dst, lane, n, D);
+    xf_lanes_encode_t<SWRT_XF_BF16>(l, x, t, lane, n, D);
   else
-    xf_lanes_store_t<SWRT_XF_F16>(l, x, t, dst, lane, n, D);
+    xf_lanes_encode_t<SWRT_XF_F16>(l, x, t, lane, n, D);
+}
+
+// Store the encoded elements of the row at dst.
+template <int M>
+__device__ __forceinline__ void xf_lanes_put(const XfLanes<M> &l, const RowXf &x, char *dst,
+                                             uint32_t lane, uint32_t n, uint32_t D) {
+  const uint32_t m = M == 1 ? 1 : (D + n - 1) / n;
+#pragma unroll
+  for (int k = 0; k < M; ++k) {
+    const uint32_t e = lane + k * n;
+    if (uint32_t(k) < m && e < D) {
+      if (x.out_bytes == 4)
+        __builtin_nontemporal_store(l.x[k], reinterpret_cast<uint32_t *>(dst) + e);
+      else if (x.out_bytes == 2)
+        __builtin_nontemporal_store(uint16_t(l.x[k]), reinterpret_cast<uint16_t *>(dst) + e);
+      else
+        __builtin_nontemporal_store(uint8_t(l.x[k]), reinterpret_cast<uint8_t *>(dst) + e);
+    }
+  }
 }
 
 }  // namespace swrt

@@ -321,15 +321,29 @@ def test_window_xf_per_channel(orc, out, S, C):
                  channels=ch, n_layers=2)
 
 
+def fused_slices_per_group(C, row_bytes, D):
+    """The launch's split of a 512-thread workgroup into subgroups for a fused
+    append (host arithmetic): a subgroup of 512 / spw lanes holds a whole
+    shift at four 16-byte words a lane and one element of the row a lane."""
+    row_words = -(-row_bytes // 16)
+    spw = 1
+    while spw < 4 and (C - 1) * row_words <= (512 // (2 * spw)) * 4 and \
+            row_words <= 512 // (2 * spw) and D <= 512 // (2 * spw):
+        spw *= 2
+    return spw
+
+
 @pytest.mark.parametrize("case", ["group2", "group4", "wide_rows", "odd_words"])
 def test_window_xf_shapes(orc, case):
     """Slices shared by 2 or 4 subgroups (int8 rows of 64 and 32 bytes), rows
     wider than one pass of the workgroup, and 2-byte copy words."""
     g = wl.rng(41)
-    B, H, C, D, out, rot = {"group2": (6, 3, 128, 64, torch.int8, "half"),
+    B, H, C, D, out, rot = {"group2": (6, 3, 200, 64, torch.int8, "half"),
                             "group4": (6, 3, 64, 32, torch.uint8, "inter"),
                             "wide_rows": (2, 2, 3, 2304, torch.float32, "half"),
                             "odd_words": (5, 2, 9, 6, torch.bfloat16, "inter")}[case]
+    if case.startswith("group"):
+        assert fused_slices_per_group(C, D, D) == int(case[-1])
     say("window xf", case)
     T = g.integers(1, 4 * C, size=B)
     T[:2] = [C, C + 1]
@@ -360,23 +374,25 @@ def test_window_xf_bad_lengths_before_positions(orc):
     np.testing.assert_array_equal(hb(dv), hv.view(np.uint8))
 
 
-def test_xf_wide_rows_in_shared_workgroups(orc):
+@pytest.mark.parametrize("D", [192, 1040])
+def test_xf_wide_rows_in_shared_workgroups(orc, D):
     """A slice small enough to share a workgroup (C = 4) with an appended row
-    wider than a quarter workgroup can spread at eight elements per lane (int8,
-    D = 1040): the launch keeps enough lanes per slice for the whole row, in the
-    windowed append and in the one-launch step."""
-    B, H, C, D = 3, 2, 4, 1040
+    wider than a quarter workgroup's lanes (int8, D = 192: two slices a
+    workgroup then; D = 1040: one, a few elements a lane): the launch keeps a
+    lane per element of the row for every slice, in the windowed append and
+    in the one-launch step."""
+    B, H, C = 3, 2, 4
     # host arithmetic: 16-byte words per row, and the subgroup split that the
-    # plain copy alone would choose (four slices of 128 lanes: 1040 > 8 * 128)
+    # plain copy alone would choose (four slices of 128 lanes, fewer than D)
     row_words = D // 16
     spw = 1
     while spw < 4 and (C - 1) * row_words <= (512 // (2 * spw)) * 2 and \
             row_words <= 512 // (2 * spw):
         spw *= 2
-    assert spw == 4 and D > 8 * (512 // spw)
+    assert spw == 4 and D > 512 // spw
     g = wl.rng(45)
     T = np.array([1, 4, 5, 9, 2, 3])[:B]
-    say("window xf wide rows in shared workgroups")
+    say("window xf wide rows in shared workgroups", D)
     _window_case(orc, g, B, H, C, 1, D, torch.bfloat16, torch.int8, "half", T, positions=64)
     xd, xo = make_xf("half", D, 64, torch.int8)
     sk = (T - 1).astype(np.int32)
