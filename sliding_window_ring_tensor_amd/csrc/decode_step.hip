@@ -269,7 +269,7 @@ extern "C" int swrt_kv_decode_step_xf(
     const void *const *full_k_new, const void *const *full_v_new, const int64_t *write_indices,
     int max_seq, int batch, int kv_heads, int head_dim, const swrt_row_transform *xf,
     uint32_t *d_flags, void *stream) {
-  if (!xf || n_full_layers < 0 || 2 * n_full_layers > kMaxTensors) return SWRT_E_INVALID_ARG;
+  if (!xf || n_full_layers < 0 || n_full_layers > kMaxTensors / 2) return SWRT_E_INVALID_ARG;
   if (n_full_layers > 0 && (!full_k_caches || !full_v_caches || !full_k_new || !full_v_new))
     return SWRT_E_INVALID_ARG;
   void *caches[kMaxTensors];

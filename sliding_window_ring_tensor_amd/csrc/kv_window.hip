@@ -377,12 +377,20 @@ int plan_window(int n_layers, void *const *k_caches, void *const *v_caches,
   if (!lengths_in_kernel && (!cache_past_lens || !evict_counts)) return SWRT_E_INVALID_ARG;
   if (S > 1 && (!k_stagings || !v_stagings)) return SWRT_E_INVALID_ARG;
 
-  int64_t slices, cache_bytes, stage_bytes;
+  // B, H, C, S < 2^31: B * H and C + S fit; every later product is checked
+  int64_t slices, bhc, bhcs, cache_bytes, stage_bytes;
   if (!mul_ok(B * H, 2 * int64_t(n_layers), &slices) || slices >= (int64_t(1) << 31))
     return SWRT_E_UNSUPPORTED;
-  if (!mul_ok(B * H * C, row, &cache_bytes) || !mul_ok(B * H * (C + S), row, &stage_bytes))
+  if (!mul_ok(B * H, C, &bhc) || !mul_ok(B * H, C + S, &bhcs) ||
+      !mul_ok(bhc, row, &cache_bytes) || !mul_ok(bhcs, row, &stage_bytes))
     return SWRT_E_UNSUPPORTED;
-  const int64_t new_span = (B - 1) * nb[0] + (H - 1) * nb[1] + (S - 1) * nb[2] + new_row;
+  int64_t new_span = new_row;  // the last new row's end: (B-1, H-1, S-1) strides on
+  const int64_t last[3] = {B - 1, H - 1, S - 1};
+  for (int i = 0; i < 3; ++i) {
+    int64_t t;
+    if (!mul_ok(last[i], nb[i], &t) || __builtin_add_overflow(new_span, t, &new_span))
+      return SWRT_E_UNSUPPORTED;
+  }
   const uint64_t align = elem_align(elem_bits), new_align = elem_align(new_bits);
   if (addr_of(cache_past_lens) % 4 || addr_of(evict_counts) % 4 || addr_of(d_flags) % 4)
     return SWRT_E_INVALID_ARG;

@@ -1246,8 +1246,11 @@ extern "C" int swrt_paged_attention(int n_layers, const swrt_paged_layer *layers
     return SWRT_E_UNSUPPORTED;
   if (n_layers == 0 || batch == 0 || q_heads == 0) return SWRT_OK;
   if (!layers || addr_of(d_flags) % 4) return SWRT_E_INVALID_ARG;
-  const int chunks = (q_heads / kv_heads + 15) / 16;  // items per stream
-  if (uint64_t(n_layers) * batch * kv_heads * chunks >= (uint64_t(1) << 31)) return SWRT_E_UNSUPPORTED;
+  const int chunks = int((int64_t(q_heads / kv_heads) + 15) / 16);  // items per stream
+  int64_t items;
+  if (!mul_ok(int64_t(n_layers) * batch, int64_t(kv_heads) * chunks, &items) ||
+      items >= (int64_t(1) << 31))
+    return SWRT_E_UNSUPPORTED;
   PgAttArgs a;
   const int st = pg_layers(n_layers, layers, a.L, true, int64_t(batch) * kv_heads);
   if (st != SWRT_OK) return st;
@@ -1255,11 +1258,14 @@ extern "C" int swrt_paged_attention(int n_layers, const swrt_paged_layer *layers
   Range ranges[6 * kMaxLayers + 1];
   int nr = 0;
   const int64_t qes = q_type == SWRT_XF_F32 ? 4 : 2, oes = out_type == SWRT_XF_F32 ? 4 : 2;
-  const int64_t rows = int64_t(batch) * q_heads * head_dim;
+  int64_t rows, q_bytes, o_bytes;  // elements of q and out; head_dim <= 256
+  if (!mul_ok(int64_t(batch) * q_heads, head_dim, &rows) || !mul_ok(rows, qes, &q_bytes) ||
+      !mul_ok(rows, oes, &o_bytes))
+    return SWRT_E_UNSUPPORTED;
   for (int l = 0; l < n_layers; ++l) {
     const swrt_paged_layer &x = layers[l];
-    ranges[nr++] = range(x.q, uint64_t(rows * qes), false);
-    ranges[nr++] = range(x.out, uint64_t(rows * oes), true);
+    ranges[nr++] = range(x.q, uint64_t(q_bytes), false);
+    ranges[nr++] = range(x.out, uint64_t(o_bytes), true);
     ranges[nr++] = range(x.arena, uint64_t(x.arena_bytes), false);
     ranges[nr++] = range(x.pages, uint64_t(x.n_pages) * sizeof(swrt_page), false);
     ranges[nr++] = pg_table_range(x, int64_t(batch) * kv_heads, false);
@@ -1448,7 +1454,8 @@ extern "C" int swrt_paged_append(int n_layers, const swrt_paged_layer *layers,
   for (int l = 0; l < n_layers; ++l) {
     const swrt_paged_layer &x = layers[l];
     if (!x.page_count || x.page_stride < 1) return SWRT_E_INVALID_ARG;  // slotted rows only
-    if (first_id < 0 || first_id > x.n_pages - n_streams) return SWRT_E_INVALID_ARG;
+    if (x.n_pages < 0 || first_id < 0 || first_id > x.n_pages - n_streams)
+      return SWRT_E_INVALID_ARG;
     if (free_begin < 0 || free_end < free_begin || free_end > x.arena_bytes ||
         (n_streams > 0 && kb + vb > (free_end - free_begin) / n_streams))
       return SWRT_E_INVALID_ARG;

@@ -93,6 +93,7 @@ inline int plan_xf(const swrt_row_transform *t, int64_t head_dim, int64_t heads,
                                      : 0;
   };
   if (!t || head_dim < 0 || heads < 0) return SWRT_E_INVALID_ARG;
+  if (head_dim > INT32_MAX || heads > INT32_MAX) return SWRT_E_UNSUPPORTED;  // products below fit
   if (t->in_type != SWRT_XF_F32 && t->in_type != SWRT_XF_F16 && t->in_type != SWRT_XF_BF16)
     return SWRT_E_INVALID_ARG;
   if (bytes(t->out_type) == 0) return SWRT_E_INVALID_ARG;
@@ -135,8 +136,7 @@ inline int plan_xf(const swrt_row_transform *t, int64_t head_dim, int64_t heads,
   int64_t tb = 0;
   const bool any = t->channel_scale[0] || t->channel_scale[1] || t->channel_zero_point[0] ||
                    t->channel_zero_point[1];
-  if (any && (!mul_ok(heads, head_dim * 4, &tb) || heads > INT32_MAX || head_dim > INT32_MAX))
-    return SWRT_E_UNSUPPORTED;
+  if (any && !mul_ok(heads, head_dim * 4, &tb)) return SWRT_E_UNSUPPORTED;
   for (int k = 0; k < 2; ++k) {
     if ((t->channel_scale[k] && x->out_bytes != 1) || (t->channel_zero_point[k] && !affine))
       return SWRT_E_INVALID_ARG;

@@ -87,6 +87,7 @@ int scatter(int n_tensors, void *const *presents, const void *const *pasts,
   RowXf x{};
   uint64_t vmask = 0;
   int st;
+  if (n_tensors < 0 || n_tensors > kMaxTensors) return SWRT_E_INVALID_ARG;  // before any array
   if (xf) {
     if (!shape || rank < 3 || rank > SWRT_MAX_RANK) return SWRT_E_INVALID_ARG;
     // per-channel tables: [shape[1], head_dim] of a [B, H, M, D] cache, one row for rank 3
@@ -96,7 +97,7 @@ int scatter(int n_tensors, void *const *presents, const void *const *pasts,
     if ((st = plan_xf(xf, shape[rank - 1], rank == 4 ? shape[1] : 1, &x, ranges, &nr)) != SWRT_OK)
       return st;
     if (n_tensors > 0 && !tensors) return SWRT_E_INVALID_ARG;
-    for (int t = 0; t < n_tensors && t < kMaxTensors; ++t) {
+    for (int t = 0; t < n_tensors; ++t) {
       if (tensors[t] != 0 && tensors[t] != 1) return SWRT_E_INVALID_ARG;
       vmask |= uint64_t(tensors[t]) << t;
     }

@@ -737,13 +737,16 @@ extern "C" int swrt_window_attention(int n_layers, const void *const *q,
   bool mfma = mfma_shape;
   if (!mfma && (!valu_group || G * lpr > 256)) return SWRT_E_UNSUPPORTED;  // see att_supported
   if (!q || !k_caches || !v_caches || !out || !cache_total_lens) return SWRT_E_INVALID_ARG;
-  int64_t cache_bytes, q_bytes, o_bytes;
-  if (!mul_ok(int64_t(batch) * kv_heads * capacity, row, &cache_bytes) ||
+  // batch, heads, capacity, head_dim < 2^31: their pairwise products fit
+  int64_t bkc, bqd, cache_bytes, q_bytes, o_bytes, items;
+  if (!mul_ok(int64_t(batch) * kv_heads, capacity, &bkc) || !mul_ok(bkc, row, &cache_bytes) ||
       !mul_ok(int64_t(batch) * q_heads, row, &q_bytes) ||
-      !mul_ok(int64_t(batch) * q_heads * head_dim, oes, &o_bytes))
+      !mul_ok(int64_t(batch) * q_heads, head_dim, &bqd) || !mul_ok(bqd, oes, &o_bytes))
     return SWRT_E_UNSUPPORTED;
-  const int chunks = (G + 15) / 16;  // the matrix-core kernel's items per window
-  if (uint64_t(n_layers) * batch * kv_heads * chunks >= (uint64_t(1) << 31)) return SWRT_E_UNSUPPORTED;
+  const int chunks = int((int64_t(G) + 15) / 16);  // the matrix-core kernel's items per window
+  if (!mul_ok(int64_t(n_layers) * batch, int64_t(kv_heads) * chunks, &items) ||
+      items >= (int64_t(1) << 31))
+    return SWRT_E_UNSUPPORTED;
   Range ranges[4 * kMaxLayers + 2];
   int nr = 0;
   AttArgs a;
