@@ -55,15 +55,17 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD's published peak
 # (FETCH_SIZE, WRITE_SIZE), each scaled by what the counter reads for a 1 GiB
 # copy; valid only for the kernel source they were taken on (its hash).
 MEASURED_TRAFFIC = {
-    ("bf16", "decode_step_kernel", "5a17d20369dcd20b"): {"read": 196_784_295,
-                                                         "written": 196_844_560},
-    ("bf16->int8", "decode_step_kernel", "5a17d20369dcd20b"): {"read": 101_380_857,
-                                                               "written": 98_911_877},
-    ("bf16", "window_in_place", "6bd7c1b202861988"): {"read": 195_175_201, "written": 196_001_407},
-    ("bf16", "window_attention_mfma", "fa5f3e2921ea5ec8"): {"read": 202_127_956,
-        "written": 6_291_472},
-    ("bf16+int8", "paged_attention_kernel", "e50d54a0dfd14812"): {"read": 127_913_960,
-        "written": 6_291_440},
+    ("bf16", "decode_step_kernel", "b1c20a54b6eec8e0"): {"read": 196_791_352,
+                                                         "written": 196_845_239},
+    ("fp8_e4m3fn", "decode_step_kernel", "b1c20a54b6eec8e0"): {"read": 99_465_435,
+                                                               "written": 98_488_524},
+    ("bf16->int8", "decode_step_kernel", "b1c20a54b6eec8e0"): {"read": 102_628_632,
+                                                               "written": 98_868_029},
+    ("bf16", "window_in_place", "d18341f16a9a26e6"): {"read": 195_187_964, "written": 196_009_804},
+    ("bf16", "window_attention_mfma", "3277255b340464c2"): {"read": 202_197_650,
+        "written": 6_291_431},
+    ("bf16+int8", "paged_attention_kernel", "c1bd35301eab1f1c"): {"read": 127_931_687,
+        "written": 6_291_424},
 }
 _CSRC = "sliding_window_ring_tensor_amd/csrc/"
 KERNEL_SOURCES = {
