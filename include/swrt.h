@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define SWRT_ABI_VERSION 9
+#define SWRT_ABI_VERSION 10
 
 /* synchronous status codes */
 #define SWRT_OK 0
@@ -738,10 +738,17 @@ typedef struct swrt_paged_layer {
  * heads each, which all read the stream's pages); head_dim in
  * {32, 64, 128, 256}; q_type, out_type SWRT_XF_F32 / _F16 / _BF16; scale
  * finite. Status codes for bad arguments; d_flags device uint32 or NULL.
+ * page_formats: the page formats the caller's visible pages may have, bit
+ * (1 << f) for each SWRT_XF_* format f (F32 .. UINT2), or 0 for any. A page
+ * of a format outside a non-zero set fails its checks (SWRT_FLAG_BAD_PAGES
+ * for its stream). A set without SWRT_XF_F32 and SWRT_XF_F16 runs a build of
+ * the kernel without their tile paths: fewer registers, more waves per SIMD.
+ * Other bits: SWRT_E_INVALID_ARG.
  */
 int swrt_paged_attention(int n_layers, const swrt_paged_layer *layers, int64_t left_window,
                          int batch, int q_heads, int kv_heads, int head_dim, float scale,
-                         int q_type, int out_type, uint32_t *d_flags, void *stream);
+                         int q_type, int out_type, uint32_t page_formats, uint32_t *d_flags,
+                         void *stream);
 
 /*
  * swrt_paged_quantize -- selected-block conversion ("Selected-block

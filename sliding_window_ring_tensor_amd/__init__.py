@@ -79,7 +79,7 @@ MODE_LINEAR, MODE_CIRCULAR = 0, 1
 PHASE_STAGE, PHASE_COMMIT, PHASE_ALL = 1, 2, 3
 MAX_LAYERS = 32
 MAX_BATCHED = 64
-ABI_VERSION = 9
+ABI_VERSION = 10
 
 _PHASES = {"stage": PHASE_STAGE, "commit": PHASE_COMMIT, "all": PHASE_ALL}
 _MODES = {"linear": MODE_LINEAR, "circular": MODE_CIRCULAR}
@@ -224,7 +224,8 @@ def lib() -> ctypes.CDLL:
     L.swrt_window_attention.argtypes = [i32, vpp, vpp, vpp, vpp, vp, i32, i32, i32, i32, i32,
                                         i32, ctypes.c_float, i32, i32, vp, vp]
     f32 = ctypes.c_float
-    L.swrt_paged_attention.argtypes = [i32, vp, i64, i32, i32, i32, i32, f32, i32, i32, vp, vp]
+    L.swrt_paged_attention.argtypes = [i32, vp, i64, i32, i32, i32, i32, f32, i32, i32, u32, vp,
+                                       vp]
     L.swrt_paged_quantize.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, i64, vp, i32, f32,
                                       ctypes.c_int32, i32, f32, ctypes.c_int32, i32, vp, vp]
     i32v = ctypes.c_int32
@@ -1078,11 +1079,25 @@ class PagedCache:
                           self.page_stride if self.slotted else 0)
 
 
+def _formats_mask(formats) -> int:
+    """The page-format set as the library's bit mask (None: any format)."""
+    if formats is None:
+        return 0
+    mask = 0
+    for f in formats:
+        code = PAGE_FORMATS.get(f, f) if isinstance(f, str) else int(f)
+        if code not in PAGE_FORMATS.values():
+            raise SwrtError(f"unknown page format {f!r}")
+        mask |= 1 << code
+    return mask
+
+
 def prepare_paged_attention(qs: Sequence[torch.Tensor], caches: Sequence[PagedCache],
                             left_window: int, kv_heads: int, *, scale: float | None = None,
                             out_dtype: torch.dtype | None = None,
                             outs: Sequence[torch.Tensor] | None = None,
-                            flags: torch.Tensor | None = None) -> PreparedCall:
+                            flags: torch.Tensor | None = None,
+                            formats=None) -> PreparedCall:
     """See ``paged_attention``."""
     n = len(qs)
     if len(caches) != n or not 1 <= n <= MAX_LAYERS:
@@ -1109,19 +1124,25 @@ def prepare_paged_attention(qs: Sequence[torch.Tensor], caches: Sequence[PagedCa
     layers = (PagedLayer * n)(*[c.layer(q, o) for c, q, o in zip(caches, qs, outs)])
     sc = D ** -0.5 if scale is None else float(scale)
     args = (n, ctypes.cast(layers, ctypes.c_void_p), int(left_window), B, Hq, kv_heads, D, sc,
-            _Q_TYPES[q0.dtype], _Q_TYPES[odt], _flags_ptr(flags))
+            _Q_TYPES[q0.dtype], _Q_TYPES[odt], _formats_mask(formats), _flags_ptr(flags))
     keep = (layers, *qs, *outs, *caches, flags)
     return PreparedCall(lib().swrt_paged_attention, args, dev, "paged_attention", keep, outs)
 
 
 def paged_attention(qs, caches, left_window: int, kv_heads: int, *, scale: float | None = None,
-                    out_dtype: torch.dtype | None = None, outs=None, flags=None) -> list:
+                    out_dtype: torch.dtype | None = None, outs=None, flags=None,
+                    formats=None) -> list:
     """One-token decode attention of every layer's queries [B, Hq, D] over its
     paged cache: query head h of entry b reads stream b * kv_heads + h //
     (Hq // kv_heads) over its last ``left_window`` + 1 tokens (all for a
-    negative value), decoding each page's format. Returns the outputs."""
+    negative value), decoding each page's format. ``formats`` (names of
+    PAGE_FORMATS or their codes; None: any) declares the formats the visible
+    pages may have: a page of another format fails its checks (BAD_PAGES for
+    its stream), and a set without f32 and f16 runs the leaner kernel.
+    Returns the outputs."""
     return prepare_paged_attention(qs, caches, left_window, kv_heads, scale=scale,
-                                   out_dtype=out_dtype, outs=outs, flags=flags)()
+                                   out_dtype=out_dtype, outs=outs, flags=flags,
+                                   formats=formats)()
 
 
 def paged_quantize(cache: PagedCache, blocks: torch.Tensor, dst_offsets: torch.Tensor,

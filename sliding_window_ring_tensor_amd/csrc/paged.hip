@@ -178,8 +178,9 @@ __device__ __forceinline__ void pg_load_raw(const char *p, uint32_t (&w)[(NB + 3
 }
 
 // element e of packed words as binary32: a dense value, or the exact integer
-// c - zp of an affine code (its scale applied by the caller)
-template <int FMT>
+// c - zp of an affine code (its scale applied by the caller). ZP false: the
+// page's zero point is 0 (a uniform test per page), and the code is the value.
+template <int FMT, bool ZP = true>
 __device__ __forceinline__ float pg_elem(const uint32_t *w, int e, int32_t zp) {
   if constexpr (FMT == SWRT_XF_F32) {
     return __uint_as_float(w[e]);
@@ -188,9 +189,11 @@ __device__ __forceinline__ float pg_elem(const uint32_t *w, int e, int32_t zp) {
   } else if constexpr (FMT == SWRT_XF_F16) {
     return float(__builtin_bit_cast(_Float16, uint16_t(w[e / 2] >> (16 * (e & 1)))));
   } else if constexpr (FMT == SWRT_XF_UINT8) {
-    return float((w[e / 4] >> (8 * (e % 4))) & 0xFFu) - float(zp);  // a byte conversion, exact
+    const float c = float((w[e / 4] >> (8 * (e % 4))) & 0xFFu);  // a byte conversion, exact
+    return ZP ? c - float(zp) : c;
   } else if constexpr (FMT == SWRT_XF_INT8) {
-    return float(int(int8_t(w[e / 4] >> (8 * (e % 4))))) - float(zp);  // a sign-extending byte conversion
+    const float c = float(int(int8_t(w[e / 4] >> (8 * (e % 4)))));  // a sign-extending byte conversion
+    return ZP ? c - float(zp) : c;
   } else {
     constexpr int B = pg_bits(FMT);
     const uint32_t raw = (w[e * B / 32] >> (e * B % 32)) & ((1u << B) - 1u);
@@ -243,6 +246,7 @@ struct PgAttArgs {
   int64_t left_window;
   int32_t B, Hq, Hkv, items, q_type, out_type;
   int32_t chunks;  // groups of up to 16 query heads per KV head
+  uint32_t formats;  // bit f set: pages of format f are allowed
 };
 
 // A tile is up to 16 consecutive rows of one page, staged in LDS as they lie
@@ -381,7 +385,7 @@ typedef __bf16 pg_bf16x8 __attribute__((ext_vector_type(8)));
 // instruction when the query is bf16 and K is bf16 or affine (codes enter
 // as the exact bf16 integers c - zp; every product is exact), else on the
 // fp32 one with K widened to binary32
-template <int D, int KF, bool QBF>
+template <int D, int KF, bool QBF, bool ZP = true>
 __device__ __forceinline__ f32x4 pg_scores_words(const uint32_t (&w)[D / 4], const PgQuery<D, QBF> &q,
                                                  int32_t kz) {
   constexpr int KQ = D / 4;
@@ -393,7 +397,7 @@ __device__ __forceinline__ f32x4 pg_scores_words(const uint32_t (&w)[D / 4], con
       if constexpr (KF == SWRT_XF_BF16) {
         kw[i] = w[i];
       } else {  // |c - zp| <= 255: exact in bf16
-        kw[i] = bf16_pack_hi(pg_elem<KF>(w, 2 * i, kz), pg_elem<KF>(w, 2 * i + 1, kz));
+        kw[i] = bf16_pack_hi(pg_elem<KF, ZP>(w, 2 * i, kz), pg_elem<KF, ZP>(w, 2 * i + 1, kz));
       }
     }
 #pragma unroll
@@ -411,13 +415,13 @@ __device__ __forceinline__ f32x4 pg_scores_words(const uint32_t (&w)[D / 4], con
 }
 
 // the lane's K chunk read from the staged tile kt
-template <int D, int KF, bool QBF>
+template <int D, int KF, bool QBF, bool ZP = true>
 __device__ __forceinline__ f32x4 pg_tile_scores_t(const char *kt, uint32_t pk, uint32_t qg,
                                                   const PgQuery<D, QBF> &q, int32_t kz) {
   constexpr int KQ = D / 4, NB = KQ * pg_bits(KF) / 8;  // at least 2 bytes
   uint32_t w[KQ];
   pg_lds_read<NB>(kt + pk * (D * pg_bits(KF) / 8) + qg * NB, w);
-  return pg_scores_words<D, KF, QBF>(w, q, kz);
+  return pg_scores_words<D, KF, QBF, ZP>(w, q, kz);
 }
 
 typedef short pg_s16x4 __attribute__((ext_vector_type(4)));
@@ -428,7 +432,7 @@ typedef short pg_s16x4 __attribute__((ext_vector_type(4)));
 // v_mfma_f32_16x16x16_bf16 (its four k-slots per lane are those four rows;
 // V exact in bf16, the weights as three exact bf16 parts), fp32 and f16 V
 // through v_mfma_f32_16x16x4_f32 (one row per instruction).
-template <int D, int VF>
+template <int D, int VF, bool ZP = true>
 __device__ __forceinline__ void pg_values_words(const uint32_t (&w)[4][D / 16], const float (&pw)[4],
                                                 int32_t vz, f32x4 (&acc)[D / 16]) {
   constexpr int MT = D / 16;
@@ -443,8 +447,8 @@ __device__ __forceinline__ void pg_values_words(const uint32_t (&w)[4][D / 16], 
         lo = __builtin_amdgcn_perm(w[1][m / 2], w[0][m / 2], sel);
         hi = __builtin_amdgcn_perm(w[3][m / 2], w[2][m / 2], sel);
       } else {  // |c - zp| <= 255: exact in bf16
-        lo = bf16_pack_hi(pg_elem<VF>(w[0], m, vz), pg_elem<VF>(w[1], m, vz));
-        hi = bf16_pack_hi(pg_elem<VF>(w[2], m, vz), pg_elem<VF>(w[3], m, vz));
+        lo = bf16_pack_hi(pg_elem<VF, ZP>(w[0], m, vz), pg_elem<VF, ZP>(w[1], m, vz));
+        hi = bf16_pack_hi(pg_elem<VF, ZP>(w[2], m, vz), pg_elem<VF, ZP>(w[3], m, vz));
       }
       const pg_s16x4 a = __builtin_bit_cast(pg_s16x4, u32x2{lo, hi});
 #pragma unroll
@@ -463,7 +467,7 @@ __device__ __forceinline__ void pg_values_words(const uint32_t (&w)[4][D / 16], 
 
 // the lane's four V chunks read from the staged tile vt (a chunk of fewer
 // than 8 bits is shifted down from its place in its byte)
-template <int D, int VF>
+template <int D, int VF, bool ZP = true>
 __device__ __forceinline__ void pg_tile_values_t(const char *vt, uint32_t j, uint32_t qg, const float (&pw)[4],
                                                  int32_t vz, f32x4 (&acc)[D / 16]) {
   constexpr int MT = D / 16, BITS = MT * pg_bits(VF), RB = D * pg_bits(VF) / 8;
@@ -478,41 +482,58 @@ __device__ __forceinline__ void pg_tile_values_t(const char *vt, uint32_t j, uin
       w[c][0] >>= (j * BITS) % 8;
     }
   }
-  pg_values_words<D, VF>(w, pw, vz, acc);
+  pg_values_words<D, VF, ZP>(w, pw, vz, acc);
 }
 
-// every staged format but the last one (the switch's default); an fp32 page
-// never reaches these
-#define SWRT_PG_FORMATS(X) \
-  X(SWRT_XF_F16) X(SWRT_XF_BF16) X(SWRT_XF_INT8) X(SWRT_XF_UINT8) X(SWRT_XF_INT4) \
-  X(SWRT_XF_UINT4) X(SWRT_XF_INT2)
+// the staged formats of 16 bits and fewer but f16 and the last one (the
+// switch's default); an fp32 page never reaches these
+#define SWRT_PG_NARROW_FORMATS(X) \
+  X(SWRT_XF_BF16) X(SWRT_XF_INT8) X(SWRT_XF_UINT8) X(SWRT_XF_INT4) X(SWRT_XF_UINT4) \
+  X(SWRT_XF_INT2)
 
-template <int D, bool QBF>
+// WIDE: f16 pages may occur (fp32 pages take their own tile code); without
+// them the kernel is built without that path, and fewer registers
+template <int D, bool QBF, bool WIDE>
 __device__ __forceinline__ f32x4 pg_tile_scores(int kf, const char *kt, uint32_t pk, uint32_t qg,
                                                 const PgQuery<D, QBF> &q, int32_t kz) {
-  // the usual page formats first, then the rest (uniform in the wave)
-  if (kf == SWRT_XF_INT8) return pg_tile_scores_t<D, SWRT_XF_INT8, QBF>(kt, pk, qg, q, kz);
+  // the usual page formats first (int8 codes of a zero point 0 without the
+  // subtraction), then the rest (uniform in the wave)
+  if (kf == SWRT_XF_INT8)
+    return kz ? pg_tile_scores_t<D, SWRT_XF_INT8, QBF>(kt, pk, qg, q, kz)
+              : pg_tile_scores_t<D, SWRT_XF_INT8, QBF, false>(kt, pk, qg, q, 0);
   if (kf == SWRT_XF_BF16) return pg_tile_scores_t<D, SWRT_XF_BF16, QBF>(kt, pk, qg, q, kz);
   switch (kf) {
 #define SWRT_PG_K(F) \
   case F: return pg_tile_scores_t<D, F, QBF>(kt, pk, qg, q, kz);
-    SWRT_PG_FORMATS(SWRT_PG_K)
+    SWRT_PG_NARROW_FORMATS(SWRT_PG_K)
 #undef SWRT_PG_K
+    case SWRT_XF_F16:
+      if constexpr (WIDE) return pg_tile_scores_t<D, SWRT_XF_F16, QBF>(kt, pk, qg, q, kz);
+      [[fallthrough]];
     default: return pg_tile_scores_t<D, SWRT_XF_UINT2, QBF>(kt, pk, qg, q, kz);
   }
 }
 
-template <int D>
+template <int D, bool WIDE>
 __device__ __forceinline__ void pg_tile_values(int vf, const char *vt, uint32_t j, uint32_t qg,
                                                const float (&pw)[4], int32_t vz, f32x4 (&acc)[D / 16]) {
-  // the usual page formats first, then the rest (uniform in the wave)
-  if (vf == SWRT_XF_INT8) return pg_tile_values_t<D, SWRT_XF_INT8>(vt, j, qg, pw, vz, acc);
+  // the usual page formats first (int8 codes of a zero point 0 without the
+  // subtraction), then the rest (uniform in the wave)
+  if (vf == SWRT_XF_INT8)
+    return vz ? pg_tile_values_t<D, SWRT_XF_INT8>(vt, j, qg, pw, vz, acc)
+              : pg_tile_values_t<D, SWRT_XF_INT8, false>(vt, j, qg, pw, 0, acc);
   if (vf == SWRT_XF_BF16) return pg_tile_values_t<D, SWRT_XF_BF16>(vt, j, qg, pw, vz, acc);
   switch (vf) {
 #define SWRT_PG_V(F) \
   case F: pg_tile_values_t<D, F>(vt, j, qg, pw, vz, acc); break;
-    SWRT_PG_FORMATS(SWRT_PG_V)
+    SWRT_PG_NARROW_FORMATS(SWRT_PG_V)
 #undef SWRT_PG_V
+    case SWRT_XF_F16:
+      if constexpr (WIDE) {
+        pg_tile_values_t<D, SWRT_XF_F16>(vt, j, qg, pw, vz, acc);
+        break;
+      }
+      [[fallthrough]];
     default: pg_tile_values_t<D, SWRT_XF_UINT2>(vt, j, qg, pw, vz, acc); break;
   }
 }
@@ -526,7 +547,7 @@ __device__ __forceinline__ void pg_tile_values(int vf, const char *vt, uint32_t 
 // and output dimension MT i + m at matrix row i of output tile m
 // (MT = D / 16): a lane reads MT consecutive elements of a V row and ends
 // holding 4 MT consecutive output dimensions of its head.
-template <int D, bool QBF>
+template <int D, bool QBF, bool WIDE>
 __global__ __launch_bounds__(kPgBlock) void paged_attention_kernel(PgAttArgs a) {
   constexpr int KQ = D / 4;   // dimensions per lane of the score product
   constexpr int MT = D / 16;  // output tiles; V elements per lane and row
@@ -592,7 +613,8 @@ __global__ __launch_bounds__(kPgBlock) void paged_attention_kernel(PgAttArgs a) 
       swrt_page d = {};
       if (in && good) {
         d = P.pages[id];
-        good = pg_page_ok(d, D, P.arena_bytes) && (k != ptr0 || d.start == 0);
+        good = pg_page_ok(d, D, P.arena_bytes) && (k != ptr0 || d.start == 0) &&
+               ((a.formats >> d.k_format) & (a.formats >> d.v_format) & 1u);
       }
       const int64_t end = d.start + d.length;
       const uint32_t elo = uint32_t(end), ehi = uint32_t(uint64_t(end) >> 32);
@@ -699,14 +721,14 @@ __global__ __launch_bounds__(kPgBlock) void paged_attention_kernel(PgAttArgs a) 
         {
 #pragma clang fp contract(off)
           f32x4 sc;
-          if (kf == SWRT_XF_F32) {  // not staged
+          if (WIDE && kf == SWRT_XF_F32) {  // not staged
             uint32_t w[KQ];
             pg_load_raw<KQ * 4>(arena + field64(d.k_offset, l) +
                                     int64_t(min(i + pk, len - 1)) * (4 * D) + int64_t(qg) * (4 * KQ),
                                 w);
             sc = pg_scores_words<D, SWRT_XF_F32, QBF>(w, q, 0);
           } else {
-            sc = pg_tile_scores<D, QBF>(kf, kt, pk, qg, q, kz);
+            sc = pg_tile_scores<D, QBF, WIDE>(kf, kt, pk, qg, q, kz);
           }
           if (i + 16 <= len) {  // a whole tile (uniform): no row to mask
 #pragma unroll
@@ -741,7 +763,7 @@ __global__ __launch_bounds__(kPgBlock) void paged_attention_kernel(PgAttArgs a) 
           }
           m = mn;
         }
-        if (vf == SWRT_XF_F32) {  // not staged
+        if (WIDE && vf == SWRT_XF_F32) {  // not staged
           uint32_t w[4][MT];
 #pragma unroll
           for (int c = 0; c < 4; ++c)
@@ -751,7 +773,7 @@ __global__ __launch_bounds__(kPgBlock) void paged_attention_kernel(PgAttArgs a) 
                                 w[c]);
           pg_values_words<D, SWRT_XF_F32>(w, pw, 0, acc);
         } else {
-          pg_tile_values<D>(vf, vt, j, qg, pw, vz, acc);
+          pg_tile_values<D, WIDE>(vf, vt, j, qg, pw, vz, acc);
         }
         if (ln < 0) break;
         if constexpr (Stage::NBUF == 2) {
@@ -1236,12 +1258,14 @@ using namespace swrt;
 extern "C" int swrt_paged_attention(int n_layers, const swrt_paged_layer *layers,
                                     int64_t left_window, int batch, int q_heads, int kv_heads,
                                     int head_dim, float scale, int q_type, int out_type,
-                                    uint32_t *d_flags, void *stream) {
+                                    uint32_t page_formats, uint32_t *d_flags, void *stream) {
   if (n_layers < 0 || n_layers > kMaxLayers || batch < 0 || q_heads < 0 || kv_heads < 1)
     return SWRT_E_INVALID_ARG;
   if (!pg_q_type_ok(q_type) || !pg_q_type_ok(out_type) || q_heads % kv_heads)
     return SWRT_E_INVALID_ARG;
   if (!(scale == scale) || scale > 3.4028235e38f || scale < -3.4028235e38f) return SWRT_E_INVALID_ARG;
+  constexpr uint32_t kAllFormats = 0x3FEu;  // bits 1 .. 9: F32 .. UINT2
+  if (page_formats & ~kAllFormats) return SWRT_E_INVALID_ARG;
   if (head_dim != 32 && head_dim != 64 && head_dim != 128 && head_dim != 256)
     return SWRT_E_UNSUPPORTED;
   if (n_layers == 0 || batch == 0 || q_heads == 0) return SWRT_OK;
@@ -1283,15 +1307,24 @@ extern "C" int swrt_paged_attention(int n_layers, const swrt_paged_layer *layers
   a.chunks = chunks;
   a.q_type = q_type;
   a.out_type = out_type;
+  a.formats = page_formats ? page_formats : kAllFormats;
+  // without fp32 and f16 pages, the build without their paths (fewer registers)
+  const bool wide = (a.formats & ((1u << SWRT_XF_F32) | (1u << SWRT_XF_F16))) != 0;
   static_assert(sizeof(PgAttArgs) <= 4096, "kernel arguments exceed 4 KiB");
   const dim3 grid((uint32_t(a.items) + kPgWaves - 1) / kPgWaves);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool qbf = q_type == SWRT_XF_BF16;
 #define SWRT_PG_LAUNCH(DD)                                                                      \
-  if (qbf)                                                                                      \
-    hipLaunchKernelGGL((paged_attention_kernel<DD, true>), grid, dim3(kPgBlock), 0, s, a);      \
+  if (qbf && wide)                                                                              \
+    hipLaunchKernelGGL((paged_attention_kernel<DD, true, true>), grid, dim3(kPgBlock), 0, s, a); \
+  else if (qbf)                                                                                 \
+    hipLaunchKernelGGL((paged_attention_kernel<DD, true, false>), grid, dim3(kPgBlock), 0, s,    \
+                       a);                                                                      \
+  else if (wide)                                                                                \
+    hipLaunchKernelGGL((paged_attention_kernel<DD, false, true>), grid, dim3(kPgBlock), 0, s,    \
+                       a);                                                                      \
   else                                                                                          \
-    hipLaunchKernelGGL((paged_attention_kernel<DD, false>), grid, dim3(kPgBlock), 0, s, a);
+    hipLaunchKernelGGL((paged_attention_kernel<DD, false, false>), grid, dim3(kPgBlock), 0, s, a);
   switch (head_dim) {
     case 32: SWRT_PG_LAUNCH(32) break;
     case 64: SWRT_PG_LAUNCH(64) break;

@@ -55,7 +55,8 @@ class PagedDecodeStep:
         if self._att is None:
             s = self.spec
             self._att = swrt.prepare_paged_attention(self.qs, self.caches, s.left_window,
-                                                     s.kv_heads, outs=self.outs, flags=self.flags)
+                                                     s.kv_heads, outs=self.outs, flags=self.flags,
+                                                     formats=(s.hot_format, s.cold_format))
         return self._att()
 
     def visible(self):

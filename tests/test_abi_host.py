@@ -511,11 +511,14 @@ def test_paged_rejects(L):
         f.update(kw)
         return swrt.PagedLayer(*[f[n] for n, _ in swrt.PagedLayer._fields_])
 
-    def att(layers=None, lw=-1, B=2, Hq=8, Hkv=2, D=64, scale=0.125, qt=3, ot=3, n=1):
+    def att(layers=None, lw=-1, B=2, Hq=8, Hkv=2, D=64, scale=0.125, qt=3, ot=3, n=1, fm=0):
         arr = (swrt.PagedLayer * n)(*([layer()] * n if layers is None else layers))
         return L.swrt_paged_attention(n, ctypes.cast(arr, ctypes.c_void_p), lw, B, Hq, Hkv, D,
-                                      scale, qt, ot, None, None)
+                                      scale, qt, ot, fm, None, None)
     assert att() in launched
+    # the declared page formats: bits 1 .. 9 (either kernel build), nothing else
+    assert att(fm=(1 << 3) | (1 << 4)) in launched and att(fm=0x3FE) in launched
+    assert att(fm=1) == INV and att(fm=1 << 10) == INV
     assert att(D=48) == UNS and att(D=512) == UNS           # head_dim
     assert att(Hq=64, Hkv=2) in launched                    # a group of 32: two waves per stream
     assert att(Hq=6, Hkv=4) == INV and att(qt=4) == INV and att(ot=9) == INV

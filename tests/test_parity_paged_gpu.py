@@ -191,6 +191,77 @@ def test_paged_attention_windows_over_many_pages(orc, qdt, left_window):
     say("  worst err/tol", round(float(np.max(err / tol)), 4))
 
 
+@pytest.mark.parametrize("zero_points", ["zero", "any"])
+@pytest.mark.parametrize("formats", [(BF16, I8), (BF16, I8, U8, I4, U4, I2, U2)], ids=str)
+def test_paged_attention_declared_formats(orc, formats, zero_points):
+    """A declared page-format set without f32 and f16 runs the kernel built
+    without their paths: on pages of the declared formats it gives the same
+    bytes as the build for any format (the same tile code runs) and meets the
+    oracle's bound; int8 pages of zero point 0 take the decode without the
+    subtraction, others the general one. A page of an undeclared format makes
+    its stream fail its checks (BAD_PAGES, outputs untouched), and the other
+    streams' outputs stay those of the unrestricted call."""
+    say("paged attention, declared formats", formats, zero_points)
+    g = wl.rng(77 + len(formats) + (zero_points == "zero"))
+    D, B, Hq, Hkv, lw = 64, 3, 16, 2, 40
+    T = g.integers(20, 90, size=B * Hkv)
+    streams = [wl.page_split(g, int(t), int(g.choice([4, 16])), sealed=0.2) for t in T]
+    pick = random_format(g, list(formats))
+
+    def fmt(s, i, n):
+        kf, vf, ks, vs, kz, vz = pick(s, i, n)
+        if zero_points == "zero" or g.integers(0, 2):
+            kz = vz = 0
+        return kf, vf, ks, vs, kz, vz
+    case = wl.paged_case(g, D, streams, fmt)
+    q = torch.from_numpy(g.uniform(-1, 1, (B, Hq, D)).astype(np.float32)).to(torch.bfloat16)
+    cache = upload(case)
+    outs = {}
+    for decl in (None, formats):
+        flags = flag_word()
+        outs[decl] = swrt.paged_attention([q.to(DEV)], [cache], lw, Hkv, out_dtype=torch.float32,
+                                          flags=flags, formats=decl)[0]
+        torch.cuda.synchronize()
+        assert int(flags.item()) == 0
+    assert torch.equal(outs[None], outs[formats])
+    tb = otable(case)
+    ref, fo = orc.paged_attention(q_host(q), oracle.XF_BF16, case.arena, tb, case.page_ptr,
+                                  case.page_ids, lw, Hkv, D ** -0.5)
+    assert fo == 0
+    got = outs[formats].cpu().to(torch.float64).numpy()
+    tol = bound(case, tb, q, Hkv, lw, D ** -0.5, torch.float32, ref)
+    assert (np.abs(got - ref) <= tol).all()
+    # the same streams with stream 1's last page in f16 (K and V) and stream
+    # 4's in f32 (V): valid pages, outside the declared set
+    def fmt2(s, i, n):
+        kf, vf, ks, vs, kz, vz = fmt(s, i, n)
+        if i == n - 1 and s == 1:
+            return F16, F16, 1.0, 1.0, 0, 0
+        if i == n - 1 and s == 4:
+            return kf, F32, ks, 1.0, kz, 0
+        return kf, vf, ks, vs, kz, vz
+    case2 = wl.paged_case(g, D, streams, fmt2)
+    cache = upload(case2)
+    flags = flag_word()
+    full = swrt.paged_attention([q.to(DEV)], [cache], lw, Hkv, out_dtype=torch.float32,
+                                flags=flags)[0]
+    torch.cuda.synchronize()
+    assert int(flags.item()) == 0
+    out = torch.full((B, Hq, D), 7.0, device=DEV)
+    flags = flag_word()
+    swrt.paged_attention([q.to(DEV)], [cache], lw, Hkv, outs=[out], flags=flags, formats=formats)
+    torch.cuda.synchronize()
+    assert int(flags.item()) == swrt.FLAG_BAD_PAGES
+    G = Hq // Hkv
+    bad = np.zeros((B, Hq), bool)
+    for s_ in (1, 4):
+        b, kv = divmod(s_, Hkv)
+        bad[b, kv * G:(kv + 1) * G] = True
+    got, badt = out.cpu(), torch.from_numpy(bad)
+    assert (got[badt] == 7.0).all()
+    assert torch.equal(got[~badt], full.cpu()[~badt])
+
+
 def test_paged_attention_bad_pages_flag_and_skip(orc):
     g = wl.rng(60)
     D, B, Hq, Hkv = 64, 2, 4, 2
