@@ -234,8 +234,9 @@ void call_paged() {
       L[l].page_count = L[0].page_count, L[l].n_pages = L[0].n_pages, L[l].n_ids = L[0].n_ids;
     }
   }
+  static const uint32_t formats[] = {0u, (1u << 3) | (1u << 4), 0x3FEu, 1u, 1u << 12};
   tally(swrt_paged_attention(n, rnd() % 10 ? L : nullptr, big(), dim(), dim(), dim(), head_dim(),
-                             0.125f, int(pick(0, 11)), int(pick(0, 11)),
+                             0.125f, int(pick(0, 11)), int(pick(0, 11)), formats[pick(0, 4)],
                              static_cast<uint32_t *>(dev()), nullptr));
   tally(swrt_paged_quantize(dev(), big(), static_cast<const swrt_page *>(dev()), big(),
                             static_cast<const int32_t *>(dev()), big(),
