@@ -239,8 +239,8 @@ constexpr int kWaveUnroll = 16;
 // shared barrier: loads of every subgroup, barrier, stores. The same ordering
 // argument as shift_append_slice holds inside each slice; slices never share
 // rows. `info(slice, g)` returns the work of subgroup g's slice (ok = false:
-// leave it alone); it is evaluated for every subgroup in uniform code, so its
-// table lookups stay scalar, and each lane then takes its own subgroup's.
+// leave it alone); each wave evaluates it for its own subgroup only, in
+// uniform code, so its table lookups stay scalar.
 // ---------------------------------------------------------------------------
 struct SliceWork {
   char *base;           // row 0 of the slice
@@ -285,20 +285,17 @@ __device__ __forceinline__ void shift_append_group(uint32_t first_slice, uint32_
   using W = typename Word<VEC>::T;
   constexpr uint32_t GB = kWinBlock / SPW;  // threads per subgroup (a multiple of 64)
   static_assert(GB % 64 == 0, "subgroups must be whole waves");
-  const uint32_t lid = threadIdx.x % GB, grp = threadIdx.x / GB;
+  // A subgroup is whole waves: the subgroup index is uniform in a wave, so each
+  // wave works out its own slice alone, in scalar code (its table lookups are
+  // scalar loads); the slice's work then stays in scalar registers, so that
+  // what it selects (a tensor's table pointers among the kernel arguments) is
+  // a scalar load, not a vector load whose wait would also drain the shift's
+  // loads issued before it.
+  const uint32_t lid = threadIdx.x % GB;
+  const uint32_t grp = uint32_t(__builtin_amdgcn_readfirstlane(int32_t(threadIdx.x / GB)));
   SliceWork w;
   w.ok = false;
-#pragma unroll
-  for (int g = 0; g < SPW; ++g) {
-    SliceWork x;
-    x.ok = false;
-    if (first_slice + g < n_slices) x = info(first_slice + g, g);
-    if (grp == uint32_t(g)) w = x;
-  }
-  // A subgroup is whole waves: each wave holds one slice's work. Saying so
-  // keeps it in scalar registers, so that what it selects (a tensor's table
-  // pointers among the kernel arguments) is a scalar load, not a vector load
-  // whose wait would also drain the shift's loads issued before it.
+  if (first_slice + grp < n_slices) w = info(first_slice + grp, int(grp));
   w = wave_uniform(w);
   // n, the words to shift, and w.ok are uniform inside a subgroup, so the two
   // predicated blocks below never split a wave. A slice with nothing to shift
