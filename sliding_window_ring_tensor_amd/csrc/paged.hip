@@ -331,6 +331,33 @@ __device__ __forceinline__ void pg_stage_rows(const char *page, int32_t i, int32
   }
 }
 
+// A tile of a bf16 (rows of 2D bytes) or int8 (D bytes) payload to LDS at
+// dst: 16 rows from src, or the `rows` left (fewer than 16: the last one
+// repeats). A whole tile of 1 KiB pieces is copied as it lies, with no
+// per-lane clamp.
+template <int D>
+__device__ __forceinline__ void pg_stage_lean(int64_t src, int32_t rows, bool is8, char *dst,
+                                              uint32_t lane) {
+  constexpr int NMAX = PgStage<D>::BYTES / 1024;
+  const int lg = PgStage<D>::LG_D + (is8 ? 0 : 1);  // log2 row bytes
+  if (rows >= 16 && lg >= 6) {
+    const int n = 1 << (lg - 6);
+    const pg_gchar base = pg_gchar(reinterpret_cast<const char *>(src)) + lane * 16;
+#pragma unroll
+    for (int k = 0; k < NMAX; ++k) {
+      if (k > 0 && k >= n) break;  // uniform
+      pg_stage16(base + k * 1024, dst + k * 1024);
+    }
+  } else {
+    pg_stage_rows<NMAX>(reinterpret_cast<const char *>(src), 0, rows - 1, lg, dst, lane);
+  }
+}
+
+template <int V>
+struct PgBuf {
+  static constexpr int value = V;
+};
+
 // NB bytes (1, 2, 4, 8 or a multiple of 16, aligned to min(NB, 16)) of LDS as
 // 32-bit words; words past them are zero
 template <int NB, int NW>
@@ -491,9 +518,16 @@ __device__ __forceinline__ void pg_tile_values_t(const char *vt, uint32_t j, uin
   X(SWRT_XF_BF16) X(SWRT_XF_INT8) X(SWRT_XF_UINT8) X(SWRT_XF_INT4) X(SWRT_XF_UINT4) \
   X(SWRT_XF_INT2)
 
-// WIDE: f16 pages may occur (fp32 pages take their own tile code); without
-// them the kernel is built without that path, and fewer registers
-template <int D, bool QBF, bool WIDE>
+// The page formats a kernel is built for (the set the caller declares): every
+// path costs registers and scalar work in the tile loop, so a kernel carries
+// only the ones that may occur.
+//   kPgLean:   bf16 and int8 pages only (the usual hot and cold formats)
+//   kPgNarrow: every staged format but f16
+//   kPgWide:   all of them (f16 staged; fp32 read by its own tile code)
+constexpr int kPgLean = 0, kPgNarrow = 1, kPgWide = 2;
+constexpr uint32_t kPgLeanFormats = (1u << SWRT_XF_BF16) | (1u << SWRT_XF_INT8);
+
+template <int D, bool QBF, int FS>
 __device__ __forceinline__ f32x4 pg_tile_scores(int kf, const char *kt, uint32_t pk, uint32_t qg,
                                                 const PgQuery<D, QBF> &q, int32_t kz) {
   // the usual page formats first (int8 codes of a zero point 0 without the
@@ -501,20 +535,20 @@ __device__ __forceinline__ f32x4 pg_tile_scores(int kf, const char *kt, uint32_t
   if (kf == SWRT_XF_INT8)
     return kz ? pg_tile_scores_t<D, SWRT_XF_INT8, QBF>(kt, pk, qg, q, kz)
               : pg_tile_scores_t<D, SWRT_XF_INT8, QBF, false>(kt, pk, qg, q, 0);
-  if (kf == SWRT_XF_BF16) return pg_tile_scores_t<D, SWRT_XF_BF16, QBF>(kt, pk, qg, q, kz);
+  if (FS == kPgLean || kf == SWRT_XF_BF16) return pg_tile_scores_t<D, SWRT_XF_BF16, QBF>(kt, pk, qg, q, kz);
   switch (kf) {
 #define SWRT_PG_K(F) \
   case F: return pg_tile_scores_t<D, F, QBF>(kt, pk, qg, q, kz);
     SWRT_PG_NARROW_FORMATS(SWRT_PG_K)
 #undef SWRT_PG_K
     case SWRT_XF_F16:
-      if constexpr (WIDE) return pg_tile_scores_t<D, SWRT_XF_F16, QBF>(kt, pk, qg, q, kz);
+      if constexpr (FS == kPgWide) return pg_tile_scores_t<D, SWRT_XF_F16, QBF>(kt, pk, qg, q, kz);
       [[fallthrough]];
     default: return pg_tile_scores_t<D, SWRT_XF_UINT2, QBF>(kt, pk, qg, q, kz);
   }
 }
 
-template <int D, bool WIDE>
+template <int D, int FS>
 __device__ __forceinline__ void pg_tile_values(int vf, const char *vt, uint32_t j, uint32_t qg,
                                                const float (&pw)[4], int32_t vz, f32x4 (&acc)[D / 16]) {
   // the usual page formats first (int8 codes of a zero point 0 without the
@@ -522,14 +556,14 @@ __device__ __forceinline__ void pg_tile_values(int vf, const char *vt, uint32_t 
   if (vf == SWRT_XF_INT8)
     return vz ? pg_tile_values_t<D, SWRT_XF_INT8>(vt, j, qg, pw, vz, acc)
               : pg_tile_values_t<D, SWRT_XF_INT8, false>(vt, j, qg, pw, 0, acc);
-  if (vf == SWRT_XF_BF16) return pg_tile_values_t<D, SWRT_XF_BF16>(vt, j, qg, pw, vz, acc);
+  if (FS == kPgLean || vf == SWRT_XF_BF16) return pg_tile_values_t<D, SWRT_XF_BF16>(vt, j, qg, pw, vz, acc);
   switch (vf) {
 #define SWRT_PG_V(F) \
   case F: pg_tile_values_t<D, F>(vt, j, qg, pw, vz, acc); break;
     SWRT_PG_NARROW_FORMATS(SWRT_PG_V)
 #undef SWRT_PG_V
     case SWRT_XF_F16:
-      if constexpr (WIDE) {
+      if constexpr (FS == kPgWide) {
         pg_tile_values_t<D, SWRT_XF_F16>(vt, j, qg, pw, vz, acc);
         break;
       }
@@ -546,9 +580,16 @@ __device__ __forceinline__ void pg_tile_values(int vf, const char *vt, uint32_t 
 // 4 k .. 4 k + 3 of the tile, weights straight from each lane's r = k score,
 // and output dimension MT i + m at matrix row i of output tile m
 // (MT = D / 16): a lane reads MT consecutive elements of a V row and ends
-// holding 4 MT consecutive output dimensions of its head.
-template <int D, bool QBF, bool WIDE>
-__global__ __launch_bounds__(kPgBlock) void paged_attention_kernel(PgAttArgs a) {
+// holding 4 MT consecutive output dimensions of its head. FS: the page
+// formats the kernel is built for (the declared ones; others are refused).
+// The bf16 + int8 build for head_dim 64 and a bf16 query fits five waves per
+// SIMD (96 registers, no spills; its staging buffers fill a compute unit's
+// LDS at five workgroups), one more than its register count would otherwise
+// allow.
+template <int D, bool QBF, int FS>
+__global__ __launch_bounds__(kPgBlock)
+__attribute__((amdgpu_waves_per_eu(FS == kPgLean && QBF && D == 64 ? 5 : 1))) void paged_attention_kernel(
+    PgAttArgs a) {
   constexpr int KQ = D / 4;   // dimensions per lane of the score product
   constexpr int MT = D / 16;  // output tiles; V elements per lane and row
   using Stage = PgStage<D>;
@@ -655,136 +696,213 @@ __global__ __launch_bounds__(kPgBlock) void paged_attention_kernel(PgAttArgs a) 
         return int64_t((uint64_t(uint32_t(field(int32_t(uint64_t(x) >> 32), l))) << 32) |
                        uint32_t(field(int32_t(x), l)));
       };
-      // what the tile code needs of page l, uniform
-      struct PgCur {
-        int kf, vf;
-        int32_t len, kz, vz;
-        float ks, vs;
-      };
-      auto cur_of = [&](int l) {
-        PgCur c;
-        const int32_t fmt = field(p_fmt, l), zp = field(p_zp, l);
-        c.kf = fmt & 0xFF;
-        c.vf = fmt >> 8;
-        c.len = field(d.length, l);
-        const bool ka = pg_affine(c.kf), va = pg_affine(c.vf);
-        c.ks = ka ? __int_as_float(field(__float_as_int(d.k_scale), l)) * a.scale_log2 : a.scale_log2;
-        c.vs = va ? __int_as_float(field(__float_as_int(d.v_scale), l)) : 1.0f;
-        c.kz = ka ? int32_t(int16_t(zp)) : 0;
-        c.vz = va ? zp >> 16 : 0;
-        return c;
-      };
-      // Stage rows [i, i + 16) of page l's K and V payloads (an fp32 payload
-      // is read by its tile code instead) into buffer buf.
-      auto stage_tile = [&](int l, int32_t i, int buf, const PgCur &c) {
-        char *dst = stage + buf * (2 * Stage::BYTES);
-        const int32_t lim = c.len - 1 - i;
-        constexpr int NMAX = Stage::BYTES / 1024;
-        const int klg = Stage::LG_D + int((kPgLogBits >> (4 * c.kf)) & 15) - 3;  // log2 row bytes
-        const int vlg = Stage::LG_D + int((kPgLogBits >> (4 * c.vf)) & 15) - 3;
-        if (c.kf != SWRT_XF_F32) pg_stage_rows<NMAX>(arena + field64(d.k_offset, l), i, lim, klg, dst, lane);
-        if (c.vf != SWRT_XF_F32)
-          pg_stage_rows<NMAX>(arena + field64(d.v_offset, l), i, lim, vlg, dst + Stage::BYTES, lane);
-      };
-      // The group's visible pages in token order: lanes n_in - 1 .. 0. With
-      // two buffers the next tile is staged before this one is computed.
-      int l = n_in - 1;
-      int32_t i = field(p_first, l);
-      PgCur c = cur_of(l);
-      int buf = 0;
-      stage_tile(l, i, 0, c);
-      while (true) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this tile's rows have landed
-        // the tile after this one
-        int ln = l;
-        int32_t in_ = i + 16;
-        PgCur cn = c;
-        if (in_ >= c.len) {
-          ln = l - 1;
-          in_ = 0;
-          if (ln >= 0) {
-            cn = cur_of(ln);
-            in_ = field(p_first, ln);
-          }
-        }
-        if constexpr (Stage::NBUF == 2) {
-          if (ln >= 0) stage_tile(ln, in_, buf ^ 1, cn);
-        }
-        const char *kt = stage + buf * (2 * Stage::BYTES), *vt = kt + Stage::BYTES;
-        // this tile: page l's formats and scales
-        const int kf = c.kf, vf = c.vf;
-        const int32_t len = c.len;
-        const float ks = c.ks, vs = c.vs;
-        const int32_t kz = c.kz, vz = c.vz;
-        float x[4];
-        float bm = -INFINITY;
-        {
+      // The tile's weights from its scores (rows from `rows` on masked): the
+      // online maximum and sum move on, and the accumulators with them.
+      auto weigh = [&](const f32x4 &sc, float ks, float vs, int32_t rows, float (&pw)[4]) {
 #pragma clang fp contract(off)
+        float x[4];
+        if (rows >= 16) {  // a whole tile (uniform): no row to mask
+#pragma unroll
+          for (int r = 0; r < 4; ++r) x[r] = sc[r] * ks;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) x[r] = int32_t(qg) + 4 * r < rows ? sc[r] * ks : -INFINITY;
+        }
+        float bm = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) bm = fmaxf(bm, x[r]);
+        bm = pg_max4(bm);
+        // the reference maximum moves only when a tile's exceeds it by more
+        // than 2^8 (log2 units); a single visible token still weighs 1
+        const bool move = bm > m + 8.0f;
+        const float mn = move ? bm : m;
+        if (__builtin_amdgcn_ballot_w64(move && m != -INFINITY)) {
+          const float f = move ? __builtin_amdgcn_exp2f(m - mn) : 1.0f;
+          l_sum *= f;
+#pragma unroll
+          for (int t = 0; t < MT; ++t) acc[t] *= f;
+        }
+        const float ms = mn == -INFINITY ? 0.0f : mn;  // no finite score yet: every weight 0
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float w = __builtin_amdgcn_exp2f(x[r] - ms);
+          l_sum += w;
+          pw[r] = w * vs;  // an affine page's V scale rides on the weight
+        }
+        m = mn;
+      };
+      if constexpr (FS == kPgLean && Stage::NBUF == 2) {
+        // Every page bf16 or int8 (K and V apart). Per page, once for the
+        // group: the payload addresses at the window's first row, the rows
+        // from there, the formats, the scales (K's with the softmax scale).
+        const bool k8 = d.k_format == SWRT_XF_INT8, v8 = d.v_format == SWRT_XF_INT8;
+        const int64_t abase = int64_t(reinterpret_cast<uintptr_t>(arena));
+        const int64_t p_k = abase + d.k_offset + (int64_t(p_first) << (Stage::LG_D + (k8 ? 0 : 1)));
+        const int64_t p_v = abase + d.v_offset + (int64_t(p_first) << (Stage::LG_D + (v8 ? 0 : 1)));
+        const int32_t p_rows = d.length - p_first;
+        const int32_t p_kind = (k8 ? 1 : 0) | (v8 ? 2 : 0);
+        const float p_ks = k8 ? d.k_scale * a.scale_log2 : a.scale_log2;
+        const float p_vs = v8 ? d.v_scale : 1.0f;
+        struct PgLean {
+          int64_t k, v;  // this tile's first K and V rows
+          int32_t rows, kind, zp;
+          float ks, vs;
+        };
+        auto lean_of = [&](int l) {
+          PgLean c;
+          c.k = field64(p_k, l);
+          c.v = field64(p_v, l);
+          c.rows = field(p_rows, l);
+          c.kind = field(p_kind, l);
+          c.zp = field(p_zp, l);
+          c.ks = __int_as_float(field(__float_as_int(p_ks), l));
+          c.vs = __int_as_float(field(__float_as_int(p_vs), l));
+          return c;
+        };
+        auto stage_lean = [&](const PgLean &c, int buf) {
+          char *dst = stage + buf * (2 * Stage::BYTES);
+          pg_stage_lean<D>(c.k, c.rows, c.kind & 1, dst, lane);
+          pg_stage_lean<D>(c.v, c.rows, c.kind & 2, dst + Stage::BYTES, lane);
+        };
+        // The group's visible pages in token order: lanes n_in - 1 .. 0. The
+        // next tile is staged before this one is computed.
+        int l = n_in - 1;
+        PgLean c = lean_of(l);
+        int buf = 0;
+        stage_lean(c, 0);
+        while (true) {
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this tile's rows have landed
+          PgLean n = c;
+          bool more = true;
+          if (c.rows > 16) {  // the page's next 16 rows
+            n.k = c.k + ((c.kind & 1) ? 16 * D : 32 * D);
+            n.v = c.v + ((c.kind & 2) ? 16 * D : 32 * D);
+            n.rows = c.rows - 16;
+          } else {
+            more = --l >= 0;
+            if (more) n = lean_of(l);
+          }
+          if (more) stage_lean(n, buf ^ 1);
+          const char *kt = stage + buf * (2 * Stage::BYTES), *vt = kt + Stage::BYTES;
+          const int32_t kz = int16_t(c.zp), vz = c.zp >> 16;
           f32x4 sc;
-          if (WIDE && kf == SWRT_XF_F32) {  // not staged
+          if (!(c.kind & 1))
+            sc = pg_tile_scores_t<D, SWRT_XF_BF16, QBF>(kt, pk, qg, q, 0);
+          else if (kz)
+            sc = pg_tile_scores_t<D, SWRT_XF_INT8, QBF>(kt, pk, qg, q, kz);
+          else
+            sc = pg_tile_scores_t<D, SWRT_XF_INT8, QBF, false>(kt, pk, qg, q, 0);
+          float pw[4];
+          weigh(sc, c.ks, c.vs, c.rows, pw);
+          if (!(c.kind & 2))
+            pg_tile_values_t<D, SWRT_XF_BF16>(vt, j, qg, pw, 0, acc);
+          else if (vz)
+            pg_tile_values_t<D, SWRT_XF_INT8>(vt, j, qg, pw, vz, acc);
+          else
+            pg_tile_values_t<D, SWRT_XF_INT8, false>(vt, j, qg, pw, 0, acc);
+          if (!more) break;
+          c = n;
+          buf ^= 1;
+        }
+      } else {
+        // what the tile code needs of page l, uniform
+        struct PgCur {
+          int kf, vf;
+          int32_t len, kz, vz;
+          float ks, vs;
+        };
+        auto cur_of = [&](int l) {
+          PgCur c;
+          const int32_t fmt = field(p_fmt, l), zp = field(p_zp, l);
+          c.kf = fmt & 0xFF;
+          c.vf = fmt >> 8;
+          c.len = field(d.length, l);
+          const bool ka = pg_affine(c.kf), va = pg_affine(c.vf);
+          c.ks = ka ? __int_as_float(field(__float_as_int(d.k_scale), l)) * a.scale_log2 : a.scale_log2;
+          c.vs = va ? __int_as_float(field(__float_as_int(d.v_scale), l)) : 1.0f;
+          c.kz = ka ? int32_t(int16_t(zp)) : 0;
+          c.vz = va ? zp >> 16 : 0;
+          return c;
+        };
+        // Stage rows [i, i + 16) of page l's K and V payloads (an fp32 payload
+        // is read by its tile code instead) into buffer buf.
+        auto stage_tile = [&](int l, int32_t i, int buf, const PgCur &c) {
+          char *dst = stage + buf * (2 * Stage::BYTES);
+          const int32_t lim = c.len - 1 - i;
+          constexpr int NMAX = Stage::BYTES / 1024;
+          // log2 row bytes
+          const int klg = FS == kPgLean ? Stage::LG_D + (c.kf == SWRT_XF_INT8 ? 0 : 1)
+                                        : Stage::LG_D + int((kPgLogBits >> (4 * c.kf)) & 15) - 3;
+          const int vlg = FS == kPgLean ? Stage::LG_D + (c.vf == SWRT_XF_INT8 ? 0 : 1)
+                                        : Stage::LG_D + int((kPgLogBits >> (4 * c.vf)) & 15) - 3;
+          if (c.kf != SWRT_XF_F32) pg_stage_rows<NMAX>(arena + field64(d.k_offset, l), i, lim, klg, dst, lane);
+          if (c.vf != SWRT_XF_F32)
+            pg_stage_rows<NMAX>(arena + field64(d.v_offset, l), i, lim, vlg, dst + Stage::BYTES, lane);
+        };
+        // The group's visible pages in token order: lanes n_in - 1 .. 0. With
+        // two buffers the next tile is staged before this one is computed.
+        int l = n_in - 1;
+        int32_t i = field(p_first, l);
+        PgCur c = cur_of(l);
+        int buf = 0;
+        stage_tile(l, i, 0, c);
+        while (true) {
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this tile's rows have landed
+          // the tile after this one
+          int ln = l;
+          int32_t in_ = i + 16;
+          PgCur cn = c;
+          if (in_ >= c.len) {
+            ln = l - 1;
+            in_ = 0;
+            if (ln >= 0) {
+              cn = cur_of(ln);
+              in_ = field(p_first, ln);
+            }
+          }
+          if constexpr (Stage::NBUF == 2) {
+            if (ln >= 0) stage_tile(ln, in_, buf ^ 1, cn);
+          }
+          const char *kt = stage + buf * (2 * Stage::BYTES), *vt = kt + Stage::BYTES;
+          // this tile: page l's formats and scales
+          const int kf = c.kf, vf = c.vf;
+          const int32_t len = c.len;
+          const int32_t kz = c.kz, vz = c.vz;
+          f32x4 sc;
+          if (FS == kPgWide && kf == SWRT_XF_F32) {  // not staged
             uint32_t w[KQ];
             pg_load_raw<KQ * 4>(arena + field64(d.k_offset, l) +
                                     int64_t(min(i + pk, len - 1)) * (4 * D) + int64_t(qg) * (4 * KQ),
                                 w);
             sc = pg_scores_words<D, SWRT_XF_F32, QBF>(w, q, 0);
           } else {
-            sc = pg_tile_scores<D, QBF, WIDE>(kf, kt, pk, qg, q, kz);
+            sc = pg_tile_scores<D, QBF, FS>(kf, kt, pk, qg, q, kz);
           }
-          if (i + 16 <= len) {  // a whole tile (uniform): no row to mask
+          float pw[4];
+          weigh(sc, c.ks, c.vs, len - i, pw);
+          if (FS == kPgWide && vf == SWRT_XF_F32) {  // not staged
+            uint32_t w[4][MT];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) x[r] = sc[r] * ks;
+            for (int c = 0; c < 4; ++c)
+              pg_load_raw<MT * 4>(arena + field64(d.v_offset, l) +
+                                      int64_t(min(i + 4 * c + int32_t(qg), len - 1)) * (4 * D) +
+                                      int64_t(j) * (4 * MT),
+                                  w[c]);
+            pg_values_words<D, SWRT_XF_F32>(w, pw, 0, acc);
           } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) x[r] = i + int32_t(qg) + 4 * r < len ? sc[r] * ks : -INFINITY;
+            pg_tile_values<D, FS>(vf, vt, j, qg, pw, vz, acc);
           }
-#pragma unroll
-          for (int r = 0; r < 4; ++r) bm = fmaxf(bm, x[r]);
-        }
-        bm = pg_max4(bm);
-        float pw[4];
-        {
-#pragma clang fp contract(off)
-          // the reference maximum moves only when a tile's exceeds it by more
-          // than 2^8 (log2 units); a single visible token still weighs 1
-          const bool move = bm > m + 8.0f;
-          const float mn = move ? bm : m;
-          if (__builtin_amdgcn_ballot_w64(move && m != -INFINITY)) {
-            const float f = move ? __builtin_amdgcn_exp2f(m - mn) : 1.0f;
-            l_sum *= f;
-#pragma unroll
-            for (int t = 0; t < MT; ++t) acc[t] *= f;
+          if (ln < 0) break;
+          if constexpr (Stage::NBUF == 2) {
+            buf ^= 1;
+          } else {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this tile read out before the refill
+            stage_tile(ln, in_, 0, cn);
           }
-          const float ms = mn == -INFINITY ? 0.0f : mn;  // no finite score yet: every weight 0
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float w = __builtin_amdgcn_exp2f(x[r] - ms);
-            l_sum += w;
-            pw[r] = w * vs;  // an affine page's V scale rides on the weight
-          }
-          m = mn;
+          l = ln;
+          i = in_;
+          c = cn;
         }
-        if (WIDE && vf == SWRT_XF_F32) {  // not staged
-          uint32_t w[4][MT];
-#pragma unroll
-          for (int c = 0; c < 4; ++c)
-            pg_load_raw<MT * 4>(arena + field64(d.v_offset, l) +
-                                    int64_t(min(i + 4 * c + int32_t(qg), len - 1)) * (4 * D) +
-                                    int64_t(j) * (4 * MT),
-                                w[c]);
-          pg_values_words<D, SWRT_XF_F32>(w, pw, 0, acc);
-        } else {
-          pg_tile_values<D, WIDE>(vf, vt, j, qg, pw, vz, acc);
-        }
-        if (ln < 0) break;
-        if constexpr (Stage::NBUF == 2) {
-          buf ^= 1;
-        } else {
-          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this tile read out before the refill
-          stage_tile(ln, in_, 0, cn);
-        }
-        l = ln;
-        i = in_;
-        c = cn;
       }
     }
   }
@@ -1308,23 +1426,24 @@ extern "C" int swrt_paged_attention(int n_layers, const swrt_paged_layer *layers
   a.q_type = q_type;
   a.out_type = out_type;
   a.formats = page_formats ? page_formats : kAllFormats;
-  // without fp32 and f16 pages, the build without their paths (fewer registers)
-  const bool wide = (a.formats & ((1u << SWRT_XF_F32) | (1u << SWRT_XF_F16))) != 0;
+  // the build for the declared formats: bf16 and int8 only, or without fp32
+  // and f16, or all (fewer paths, fewer registers and less scalar work)
+  const int fs = (a.formats & ~kPgLeanFormats) == 0 ? kPgLean
+                 : (a.formats & ((1u << SWRT_XF_F32) | (1u << SWRT_XF_F16))) == 0 ? kPgNarrow
+                                                                                   : kPgWide;
   static_assert(sizeof(PgAttArgs) <= 4096, "kernel arguments exceed 4 KiB");
   const dim3 grid((uint32_t(a.items) + kPgWaves - 1) / kPgWaves);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool qbf = q_type == SWRT_XF_BF16;
-#define SWRT_PG_LAUNCH(DD)                                                                      \
-  if (qbf && wide)                                                                              \
-    hipLaunchKernelGGL((paged_attention_kernel<DD, true, true>), grid, dim3(kPgBlock), 0, s, a); \
-  else if (qbf)                                                                                 \
-    hipLaunchKernelGGL((paged_attention_kernel<DD, true, false>), grid, dim3(kPgBlock), 0, s,    \
-                       a);                                                                      \
-  else if (wide)                                                                                \
-    hipLaunchKernelGGL((paged_attention_kernel<DD, false, true>), grid, dim3(kPgBlock), 0, s,    \
-                       a);                                                                      \
-  else                                                                                          \
-    hipLaunchKernelGGL((paged_attention_kernel<DD, false, false>), grid, dim3(kPgBlock), 0, s, a);
+#define SWRT_PG_LAUNCH_FS(DD, QB, FS) \
+  hipLaunchKernelGGL((paged_attention_kernel<DD, QB, FS>), grid, dim3(kPgBlock), 0, s, a);
+#define SWRT_PG_LAUNCH_Q(DD, QB)                                 \
+  if (fs == kPgLean) SWRT_PG_LAUNCH_FS(DD, QB, kPgLean)          \
+  else if (fs == kPgNarrow) SWRT_PG_LAUNCH_FS(DD, QB, kPgNarrow) \
+  else SWRT_PG_LAUNCH_FS(DD, QB, kPgWide)
+#define SWRT_PG_LAUNCH(DD)          \
+  if (qbf) SWRT_PG_LAUNCH_Q(DD, true) \
+  else SWRT_PG_LAUNCH_Q(DD, false)
   switch (head_dim) {
     case 32: SWRT_PG_LAUNCH(32) break;
     case 64: SWRT_PG_LAUNCH(64) break;
@@ -1332,6 +1451,8 @@ extern "C" int swrt_paged_attention(int n_layers, const swrt_paged_layer *layers
     default: SWRT_PG_LAUNCH(256) break;
   }
 #undef SWRT_PG_LAUNCH
+#undef SWRT_PG_LAUNCH_Q
+#undef SWRT_PG_LAUNCH_FS
   return launch_status();
 }
 

@@ -191,19 +191,24 @@ def test_paged_attention_windows_over_many_pages(orc, qdt, left_window):
     say("  worst err/tol", round(float(np.max(err / tol)), 4))
 
 
+@pytest.mark.parametrize("head", [(64, torch.bfloat16), (32, torch.float32), (128, torch.bfloat16)],
+                         ids=["d64-bf16q", "d32-f32q", "d128-bf16q"])
 @pytest.mark.parametrize("zero_points", ["zero", "any"])
 @pytest.mark.parametrize("formats", [(BF16, I8), (BF16, I8, U8, I4, U4, I2, U2)], ids=str)
-def test_paged_attention_declared_formats(orc, formats, zero_points):
-    """A declared page-format set without f32 and f16 runs the kernel built
-    without their paths: on pages of the declared formats it gives the same
-    bytes as the build for any format (the same tile code runs) and meets the
-    oracle's bound; int8 pages of zero point 0 take the decode without the
+def test_paged_attention_declared_formats(orc, formats, zero_points, head):
+    """A declared page-format set runs the kernel built for it: bf16 and int8
+    only (the lean build; at head_dim 64 with a bf16 query it runs five waves
+    per SIMD), or every staged format but f16 (without the f32 and f16
+    paths). On pages of the declared formats it gives the same bytes as the
+    build for any format (the same tile code runs) and meets the oracle's
+    bound; int8 pages of zero point 0 take the decode without the
     subtraction, others the general one. A page of an undeclared format makes
     its stream fail its checks (BAD_PAGES, outputs untouched), and the other
     streams' outputs stay those of the unrestricted call."""
-    say("paged attention, declared formats", formats, zero_points)
-    g = wl.rng(77 + len(formats) + (zero_points == "zero"))
-    D, B, Hq, Hkv, lw = 64, 3, 16, 2, 40
+    say("paged attention, declared formats", formats, zero_points, head)
+    D, qdt = head
+    g = wl.rng(77 + len(formats) + (zero_points == "zero") + D)
+    B, Hq, Hkv, lw = 3, 16, 2, 40
     T = g.integers(20, 90, size=B * Hkv)
     streams = [wl.page_split(g, int(t), int(g.choice([4, 16])), sealed=0.2) for t in T]
     pick = random_format(g, list(formats))
@@ -214,7 +219,7 @@ def test_paged_attention_declared_formats(orc, formats, zero_points):
             kz = vz = 0
         return kf, vf, ks, vs, kz, vz
     case = wl.paged_case(g, D, streams, fmt)
-    q = torch.from_numpy(g.uniform(-1, 1, (B, Hq, D)).astype(np.float32)).to(torch.bfloat16)
+    q = torch.from_numpy(g.uniform(-1, 1, (B, Hq, D)).astype(np.float32)).to(qdt)
     cache = upload(case)
     outs = {}
     for decl in (None, formats):
@@ -225,7 +230,7 @@ def test_paged_attention_declared_formats(orc, formats, zero_points):
         assert int(flags.item()) == 0
     assert torch.equal(outs[None], outs[formats])
     tb = otable(case)
-    ref, fo = orc.paged_attention(q_host(q), oracle.XF_BF16, case.arena, tb, case.page_ptr,
+    ref, fo = orc.paged_attention(q_host(q), QT[q.dtype], case.arena, tb, case.page_ptr,
                                   case.page_ids, lw, Hkv, D ** -0.5)
     assert fo == 0
     got = outs[formats].cpu().to(torch.float64).numpy()
