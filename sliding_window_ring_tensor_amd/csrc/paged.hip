@@ -338,18 +338,19 @@ __device__ __forceinline__ void pg_stage_rows(const char *page, int32_t i, int32
 template <int D>
 __device__ __forceinline__ void pg_stage_lean(int64_t src, int32_t rows, bool is8, char *dst,
                                               uint32_t lane) {
-  constexpr int NMAX = PgStage<D>::BYTES / 1024;
-  const int lg = PgStage<D>::LG_D + (is8 ? 0 : 1);  // log2 row bytes
-  if (rows >= 16 && lg >= 6) {
-    const int n = 1 << (lg - 6);
+  constexpr int N8 = 16 * D / 1024, N16 = 32 * D / 1024;  // 1 KiB pieces of a whole tile
+  if (rows >= 16 && (N8 > 0 || !is8)) {
     const pg_gchar base = pg_gchar(reinterpret_cast<const char *>(src)) + lane * 16;
+    if (is8) {
 #pragma unroll
-    for (int k = 0; k < NMAX; ++k) {
-      if (k > 0 && k >= n) break;  // uniform
-      pg_stage16(base + k * 1024, dst + k * 1024);
+      for (int k = 0; k < N8; ++k) pg_stage16(base + k * 1024, dst + k * 1024);
+    } else {
+#pragma unroll
+      for (int k = 0; k < N16; ++k) pg_stage16(base + k * 1024, dst + k * 1024);
     }
   } else {
-    pg_stage_rows<NMAX>(reinterpret_cast<const char *>(src), 0, rows - 1, lg, dst, lane);
+    pg_stage_rows<PgStage<D>::BYTES / 1024>(reinterpret_cast<const char *>(src), 0, rows - 1,
+                                            PgStage<D>::LG_D + (is8 ? 0 : 1), dst, lane);
   }
 }
 
@@ -393,11 +394,18 @@ __device__ __forceinline__ void pg_lds_read(const char *p, uint32_t (&w)[NW]) {
 // with the row and half-wave swaps: plain VALU work, no LDS round trip.
 // Each step combines a lane's value with its partner's in either order,
 // and max and + are commutative, so all four lanes end with the same value.
+// (the maximum as one instruction: the values are results of arithmetic,
+// never signalling NaNs, so they need no quieting first)
+__device__ __forceinline__ float pg_vmax(uint32_t a, uint32_t b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 __device__ __forceinline__ float pg_max4(float v) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  v = pg_vmax(a[0], a[1]);
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return pg_vmax(b[0], b[1]);
 }
 __device__ __forceinline__ float pg_sum4(float v) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -412,6 +420,33 @@ typedef __bf16 pg_bf16x8 __attribute__((ext_vector_type(8)));
 // instruction when the query is bf16 and K is bf16 or affine (codes enter
 // as the exact bf16 integers c - zp; every product is exact), else on the
 // fp32 one with K widened to binary32
+// the key operand of the bf16 score product: the lane's K chunk as bf16
+// pairs (bf16 K as it is; affine codes c - zp, exact in bf16 as |c - zp| <= 255)
+template <int D, int KF, bool ZP = true>
+__device__ __forceinline__ void pg_key_bf16(const uint32_t (&w)[D / 4], int32_t kz, uint32_t (&kw)[D / 8]) {
+#pragma unroll
+  for (int i = 0; i < D / 8; ++i) {
+    if constexpr (KF == SWRT_XF_BF16) {
+      kw[i] = w[i];
+    } else {
+      kw[i] = bf16_pack_hi(pg_elem<KF, ZP>(w, 2 * i, kz), pg_elem<KF, ZP>(w, 2 * i + 1, kz));
+    }
+  }
+}
+
+// the score product on the bf16 matrix instruction (every product exact)
+template <int D, typename Q>
+__device__ __forceinline__ f32x4 pg_scores_bf16(const uint32_t (&kw)[D / 8], const Q &q) {
+  f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int st = 0; st < D / 32; ++st)
+    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+        __builtin_bit_cast(pg_bf16x8, u32x4{kw[4 * st], kw[4 * st + 1], kw[4 * st + 2], kw[4 * st + 3]}),
+        __builtin_bit_cast(pg_bf16x8, u32x4{q.b[4 * st], q.b[4 * st + 1], q.b[4 * st + 2], q.b[4 * st + 3]}),
+        sc, 0, 0, 0);
+  return sc;
+}
+
 template <int D, int KF, bool QBF, bool ZP = true>
 __device__ __forceinline__ f32x4 pg_scores_words(const uint32_t (&w)[D / 4], const PgQuery<D, QBF> &q,
                                                  int32_t kz) {
@@ -419,20 +454,8 @@ __device__ __forceinline__ f32x4 pg_scores_words(const uint32_t (&w)[D / 4], con
   f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
   if constexpr (QBF && KF != SWRT_XF_F32 && KF != SWRT_XF_F16) {
     uint32_t kw[KQ / 2];
-#pragma unroll
-    for (int i = 0; i < KQ / 2; ++i) {
-      if constexpr (KF == SWRT_XF_BF16) {
-        kw[i] = w[i];
-      } else {  // |c - zp| <= 255: exact in bf16
-        kw[i] = bf16_pack_hi(pg_elem<KF, ZP>(w, 2 * i, kz), pg_elem<KF, ZP>(w, 2 * i + 1, kz));
-      }
-    }
-#pragma unroll
-    for (int st = 0; st < KQ / 8; ++st)
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-          __builtin_bit_cast(pg_bf16x8, u32x4{kw[4 * st], kw[4 * st + 1], kw[4 * st + 2], kw[4 * st + 3]}),
-          __builtin_bit_cast(pg_bf16x8, u32x4{q.b[4 * st], q.b[4 * st + 1], q.b[4 * st + 2], q.b[4 * st + 3]}),
-          sc, 0, 0, 0);
+    pg_key_bf16<D, KF, ZP>(w, kz, kw);
+    sc = pg_scores_bf16<D>(kw, q);
   } else {
 #pragma unroll
     for (int e = 0; e < KQ; ++e)
@@ -442,12 +465,17 @@ __device__ __forceinline__ f32x4 pg_scores_words(const uint32_t (&w)[D / 4], con
 }
 
 // the lane's K chunk read from the staged tile kt
+template <int D, int KF>
+__device__ __forceinline__ void pg_key_chunk(const char *kt, uint32_t pk, uint32_t qg, uint32_t (&w)[D / 4]) {
+  constexpr int NB = D / 4 * pg_bits(KF) / 8;  // at least 2 bytes
+  pg_lds_read<NB>(kt + pk * (D * pg_bits(KF) / 8) + qg * NB, w);
+}
+
 template <int D, int KF, bool QBF, bool ZP = true>
 __device__ __forceinline__ f32x4 pg_tile_scores_t(const char *kt, uint32_t pk, uint32_t qg,
                                                   const PgQuery<D, QBF> &q, int32_t kz) {
-  constexpr int KQ = D / 4, NB = KQ * pg_bits(KF) / 8;  // at least 2 bytes
-  uint32_t w[KQ];
-  pg_lds_read<NB>(kt + pk * (D * pg_bits(KF) / 8) + qg * NB, w);
+  uint32_t w[D / 4];
+  pg_key_chunk<D, KF>(kt, pk, qg, w);
   return pg_scores_words<D, KF, QBF, ZP>(w, q, kz);
 }
 
@@ -459,30 +487,50 @@ typedef short pg_s16x4 __attribute__((ext_vector_type(4)));
 // v_mfma_f32_16x16x16_bf16 (its four k-slots per lane are those four rows;
 // V exact in bf16, the weights as three exact bf16 parts), fp32 and f16 V
 // through v_mfma_f32_16x16x4_f32 (one row per instruction).
+// the value operand of the bf16 product for output tile m: element m of
+// rows 0, 1 and of rows 2, 3 as bf16 pairs (affine codes c - zp, exact in
+// bf16 as |c - zp| <= 255)
+template <int D, int VF, bool ZP = true>
+__device__ __forceinline__ void pg_value_bf16(const uint32_t (&w)[4][D / 16], int32_t vz,
+                                              uint32_t (&va)[D / 16][2]) {
+#pragma unroll
+  for (int m = 0; m < D / 16; ++m) {
+    if constexpr (VF == SWRT_XF_BF16) {
+      const uint32_t sel = m % 2 ? 0x07060302u : 0x05040100u;
+      va[m][0] = __builtin_amdgcn_perm(w[1][m / 2], w[0][m / 2], sel);
+      va[m][1] = __builtin_amdgcn_perm(w[3][m / 2], w[2][m / 2], sel);
+    } else {
+      va[m][0] = bf16_pack_hi(pg_elem<VF, ZP>(w[0], m, vz), pg_elem<VF, ZP>(w[1], m, vz));
+      va[m][1] = bf16_pack_hi(pg_elem<VF, ZP>(w[2], m, vz), pg_elem<VF, ZP>(w[3], m, vz));
+    }
+  }
+}
+
+// the value product on the bf16 matrix instruction, the weights in three
+// exact bf16 parts, the small parts first
+template <int D>
+__device__ __forceinline__ void pg_values_bf16(const uint32_t (&va)[D / 16][2], const float (&pw)[4],
+                                               f32x4 (&acc)[D / 16]) {
+  uint32_t pb[3][2];
+  bf16_split3(pw, pb);
+#pragma unroll
+  for (int m = 0; m < D / 16; ++m) {
+    const pg_s16x4 a = __builtin_bit_cast(pg_s16x4, u32x2{va[m][0], va[m][1]});
+#pragma unroll
+    for (int k = 2; k >= 0; --k)
+      acc[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+          a, __builtin_bit_cast(pg_s16x4, u32x2{pb[k][0], pb[k][1]}), acc[m], 0, 0, 0);
+  }
+}
+
 template <int D, int VF, bool ZP = true>
 __device__ __forceinline__ void pg_values_words(const uint32_t (&w)[4][D / 16], const float (&pw)[4],
                                                 int32_t vz, f32x4 (&acc)[D / 16]) {
   constexpr int MT = D / 16;
   if constexpr (VF == SWRT_XF_BF16 || pg_affine(VF)) {
-    uint32_t pb[3][2];
-    bf16_split3(pw, pb);
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      uint32_t lo, hi;  // element m of rows 0, 1 and of rows 2, 3, as bf16 pairs
-      if constexpr (VF == SWRT_XF_BF16) {
-        const uint32_t sel = m % 2 ? 0x07060302u : 0x05040100u;
-        lo = __builtin_amdgcn_perm(w[1][m / 2], w[0][m / 2], sel);
-        hi = __builtin_amdgcn_perm(w[3][m / 2], w[2][m / 2], sel);
-      } else {  // |c - zp| <= 255: exact in bf16
-        lo = bf16_pack_hi(pg_elem<VF, ZP>(w[0], m, vz), pg_elem<VF, ZP>(w[1], m, vz));
-        hi = bf16_pack_hi(pg_elem<VF, ZP>(w[2], m, vz), pg_elem<VF, ZP>(w[3], m, vz));
-      }
-      const pg_s16x4 a = __builtin_bit_cast(pg_s16x4, u32x2{lo, hi});
-#pragma unroll
-      for (int k = 2; k >= 0; --k)  // the small parts first
-        acc[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-            a, __builtin_bit_cast(pg_s16x4, u32x2{pb[k][0], pb[k][1]}), acc[m], 0, 0, 0);
-    }
+    uint32_t va[MT][2];
+    pg_value_bf16<D, VF, ZP>(w, vz, va);
+    pg_values_bf16<D>(va, pw, acc);
   } else {
 #pragma unroll
     for (int c = 0; c < 4; ++c)
@@ -494,11 +542,10 @@ __device__ __forceinline__ void pg_values_words(const uint32_t (&w)[4][D / 16], 
 
 // the lane's four V chunks read from the staged tile vt (a chunk of fewer
 // than 8 bits is shifted down from its place in its byte)
-template <int D, int VF, bool ZP = true>
-__device__ __forceinline__ void pg_tile_values_t(const char *vt, uint32_t j, uint32_t qg, const float (&pw)[4],
-                                                 int32_t vz, f32x4 (&acc)[D / 16]) {
+template <int D, int VF>
+__device__ __forceinline__ void pg_value_chunks(const char *vt, uint32_t j, uint32_t qg,
+                                                uint32_t (&w)[4][D / 16]) {
   constexpr int MT = D / 16, BITS = MT * pg_bits(VF), RB = D * pg_bits(VF) / 8;
-  uint32_t w[4][MT];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const char *row = vt + (4 * c + qg) * RB;
@@ -509,6 +556,13 @@ __device__ __forceinline__ void pg_tile_values_t(const char *vt, uint32_t j, uin
       w[c][0] >>= (j * BITS) % 8;
     }
   }
+}
+
+template <int D, int VF, bool ZP = true>
+__device__ __forceinline__ void pg_tile_values_t(const char *vt, uint32_t j, uint32_t qg, const float (&pw)[4],
+                                                 int32_t vz, f32x4 (&acc)[D / 16]) {
+  uint32_t w[4][D / 16];
+  pg_value_chunks<D, VF>(vt, j, qg, w);
   pg_values_words<D, VF, ZP>(w, pw, vz, acc);
 }
 
@@ -588,19 +642,23 @@ __device__ __forceinline__ void pg_tile_values(int vf, const char *vt, uint32_t 
 // allow.
 template <int D, bool QBF, int FS>
 __global__ __launch_bounds__(kPgBlock)
-__attribute__((amdgpu_waves_per_eu(FS == kPgLean && QBF && D == 64 ? 5 : 1))) void paged_attention_kernel(
+__attribute__((amdgpu_waves_per_eu(FS == kPgLean && QBF && D == 64 ? 6 : 1))) void paged_attention_kernel(
     PgAttArgs a) {
   constexpr int KQ = D / 4;   // dimensions per lane of the score product
   constexpr int MT = D / 16;  // output tiles; V elements per lane and row
   using Stage = PgStage<D>;
-  __shared__ __attribute__((aligned(16))) char stage_all[kPgWaves][Stage::NBUF][2 * Stage::BYTES];
+  // a wave's staging space: the bf16 + int8 tile loop keeps one K buffer and
+  // two V buffers, the general one NBUF buffers of K and V
+  constexpr bool kLeanLoop = FS == kPgLean && Stage::NBUF == 2;
+  constexpr int kWaveStage = kLeanLoop ? 3 * Stage::BYTES : Stage::NBUF * 2 * Stage::BYTES;
+  __shared__ __attribute__((aligned(16))) char stage_all[kPgWaves][kWaveStage];
   // the wave index is uniform: everything derived from it (the stream, the
   // layer's pointers) then lives in scalar registers
   const uint32_t lane = threadIdx.x % 64, wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
   const uint32_t j = lane % 16, qg = lane / 16;
   const uint32_t item = blockIdx.x * kPgWaves + wave;
   if (item >= uint32_t(a.items)) return;
-  char *stage = stage_all[wave][0];
+  char *stage = stage_all[wave];
   // an item is (layer, stream, chunk): the chunk's query heads are
   // 16 chunk .. 16 chunk + 15 of the group (a group of more than 16 heads is
   // split over consecutive items, whose waves read the same pages)
@@ -701,12 +759,11 @@ __attribute__((amdgpu_waves_per_eu(FS == kPgLean && QBF && D == 64 ? 5 : 1))) vo
       auto weigh = [&](const f32x4 &sc, float ks, float vs, int32_t rows, float (&pw)[4]) {
 #pragma clang fp contract(off)
         float x[4];
-        if (rows >= 16) {  // a whole tile (uniform): no row to mask
 #pragma unroll
-          for (int r = 0; r < 4; ++r) x[r] = sc[r] * ks;
-        } else {
+        for (int r = 0; r < 4; ++r) x[r] = sc[r] * ks;
+        if (rows < 16) {  // a partial tile (uniform): rows past the page's last masked
 #pragma unroll
-          for (int r = 0; r < 4; ++r) x[r] = int32_t(qg) + 4 * r < rows ? sc[r] * ks : -INFINITY;
+          for (int r = 0; r < 4; ++r) x[r] = int32_t(qg) + 4 * r < rows ? x[r] : -INFINITY;
         }
         float bm = -INFINITY;
 #pragma unroll
@@ -731,7 +788,7 @@ __attribute__((amdgpu_waves_per_eu(FS == kPgLean && QBF && D == 64 ? 5 : 1))) vo
         }
         m = mn;
       };
-      if constexpr (FS == kPgLean && Stage::NBUF == 2) {
+      if constexpr (kLeanLoop) {
         // Every page bf16 or int8 (K and V apart). Per page, once for the
         // group: the payload addresses at the window's first row, the rows
         // from there, the formats, the scales (K's with the softmax scale).
@@ -759,47 +816,86 @@ __attribute__((amdgpu_waves_per_eu(FS == kPgLean && QBF && D == 64 ? 5 : 1))) vo
           c.vs = __int_as_float(field(__float_as_int(p_vs), l));
           return c;
         };
-        auto stage_lean = [&](const PgLean &c, int buf) {
-          char *dst = stage + buf * (2 * Stage::BYTES);
-          pg_stage_lean<D>(c.k, c.rows, c.kind & 1, dst, lane);
-          pg_stage_lean<D>(c.v, c.rows, c.kind & 2, dst + Stage::BYTES, lane);
+        // K has one buffer: a tile's K chunks are read out at its start and
+        // the next tile's K rows staged right after. V has two: the next
+        // tile's V rows are staged as a tile starts.
+        auto stage_k = [&](const PgLean &c) { pg_stage_lean<D>(c.k, c.rows, c.kind & 1, stage, lane); };
+        auto stage_v = [&](const PgLean &c, int buf) {
+          pg_stage_lean<D>(c.v, c.rows, c.kind & 2, stage + (1 + buf) * Stage::BYTES, lane);
         };
-        // The group's visible pages in token order: lanes n_in - 1 .. 0. The
-        // next tile is staged before this one is computed.
+        // The group's visible pages in token order: lanes n_in - 1 .. 0.
         int l = n_in - 1;
         PgLean c = lean_of(l);
         int buf = 0;
-        stage_lean(c, 0);
+        stage_v(c, 0);
+        stage_k(c);
         while (true) {
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this tile's rows have landed
-          PgLean n = c;
-          bool more = true;
-          if (c.rows > 16) {  // the page's next 16 rows
+          // the next tile: the page's next 16 rows, or the next page's first
+          // (read from any lane when there is none)
+          PgLean n;
+          if (c.rows > 16) {
+            n = c;
             n.k = c.k + ((c.kind & 1) ? 16 * D : 32 * D);
             n.v = c.v + ((c.kind & 2) ? 16 * D : 32 * D);
             n.rows = c.rows - 16;
           } else {
-            more = --l >= 0;
-            if (more) n = lean_of(l);
+            --l;
+            n = lean_of(l & 63);
           }
-          if (more) stage_lean(n, buf ^ 1);
-          const char *kt = stage + buf * (2 * Stage::BYTES), *vt = kt + Stage::BYTES;
+          const bool more = l >= 0;
+          if (more) stage_v(n, buf ^ 1);
+          const char *vt = stage + (1 + buf) * Stage::BYTES;
           const int32_t kz = int16_t(c.zp), vz = c.zp >> 16;
-          f32x4 sc;
+          // this tile's K chunk, then the next tile's K rows into the buffer
+          uint32_t w[D / 4];
           if (!(c.kind & 1))
-            sc = pg_tile_scores_t<D, SWRT_XF_BF16, QBF>(kt, pk, qg, q, 0);
-          else if (kz)
-            sc = pg_tile_scores_t<D, SWRT_XF_INT8, QBF>(kt, pk, qg, q, kz);
+            pg_key_chunk<D, SWRT_XF_BF16>(stage, pk, qg, w);
           else
-            sc = pg_tile_scores_t<D, SWRT_XF_INT8, QBF, false>(kt, pk, qg, q, 0);
+            pg_key_chunk<D, SWRT_XF_INT8>(stage, pk, qg, w);
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read out before the refill
+          if (more) stage_k(n);
           float pw[4];
-          weigh(sc, c.ks, c.vs, c.rows, pw);
-          if (!(c.kind & 2))
-            pg_tile_values_t<D, SWRT_XF_BF16>(vt, j, qg, pw, 0, acc);
-          else if (vz)
-            pg_tile_values_t<D, SWRT_XF_INT8>(vt, j, qg, pw, vz, acc);
-          else
-            pg_tile_values_t<D, SWRT_XF_INT8, false>(vt, j, qg, pw, 0, acc);
+          if constexpr (QBF) {
+            // the operands decoded per format, one chain of products for all
+            uint32_t kw[D / 8];
+            if (!(c.kind & 1))
+              pg_key_bf16<D, SWRT_XF_BF16>(w, 0, kw);
+            else if (kz)
+              pg_key_bf16<D, SWRT_XF_INT8>(w, kz, kw);
+            else
+              pg_key_bf16<D, SWRT_XF_INT8, false>(w, 0, kw);
+            weigh(pg_scores_bf16<D>(kw, q), c.ks, c.vs, c.rows, pw);
+            uint32_t va[D / 16][2];
+            if (!(c.kind & 2)) {
+              uint32_t vw[4][D / 16];
+              pg_value_chunks<D, SWRT_XF_BF16>(vt, j, qg, vw);
+              pg_value_bf16<D, SWRT_XF_BF16>(vw, 0, va);
+            } else {
+              uint32_t vw[4][D / 16];
+              pg_value_chunks<D, SWRT_XF_INT8>(vt, j, qg, vw);
+              if (vz)
+                pg_value_bf16<D, SWRT_XF_INT8>(vw, vz, va);
+              else
+                pg_value_bf16<D, SWRT_XF_INT8, false>(vw, 0, va);
+            }
+            pg_values_bf16<D>(va, pw, acc);
+          } else {
+            f32x4 sc;
+            if (!(c.kind & 1))
+              sc = pg_scores_words<D, SWRT_XF_BF16, QBF>(w, q, 0);
+            else if (kz)
+              sc = pg_scores_words<D, SWRT_XF_INT8, QBF>(w, q, kz);
+            else
+              sc = pg_scores_words<D, SWRT_XF_INT8, QBF, false>(w, q, 0);
+            weigh(sc, c.ks, c.vs, c.rows, pw);
+            if (!(c.kind & 2))
+              pg_tile_values_t<D, SWRT_XF_BF16>(vt, j, qg, pw, 0, acc);
+            else if (vz)
+              pg_tile_values_t<D, SWRT_XF_INT8>(vt, j, qg, pw, vz, acc);
+            else
+              pg_tile_values_t<D, SWRT_XF_INT8, false>(vt, j, qg, pw, 0, acc);
+          }
           if (!more) break;
           c = n;
           buf ^= 1;
