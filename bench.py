@@ -55,17 +55,17 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD's published peak
 # (FETCH_SIZE, WRITE_SIZE), each scaled by what the counter reads for a 1 GiB
 # copy; valid only for the kernel source they were taken on (its hash).
 MEASURED_TRAFFIC = {
-    ("bf16", "decode_step_kernel", "b1c20a54b6eec8e0"): {"read": 196_791_352,
-                                                         "written": 196_845_239},
-    ("fp8_e4m3fn", "decode_step_kernel", "b1c20a54b6eec8e0"): {"read": 99_465_435,
-                                                               "written": 98_488_524},
-    ("bf16->int8", "decode_step_kernel", "b1c20a54b6eec8e0"): {"read": 102_628_632,
-                                                               "written": 98_868_029},
-    ("bf16", "window_in_place", "d18341f16a9a26e6"): {"read": 195_187_964, "written": 196_009_804},
+    ("bf16", "decode_step_kernel", "0d9b2b0e7922cc28"): {"read": 196_789_459,
+                                                         "written": 196_843_539},
+    ("fp8_e4m3fn", "decode_step_kernel", "0d9b2b0e7922cc28"): {"read": 99_577_491,
+                                                               "written": 98_533_349},
+    ("bf16->int8", "decode_step_kernel", "0d9b2b0e7922cc28"): {"read": 103_588_560,
+                                                               "written": 98_800_756},
+    ("bf16", "window_in_place", "f1e8f2524c95ef7d"): {"read": 195_188_321, "written": 196_006_053},
     ("bf16", "window_attention_mfma", "3277255b340464c2"): {"read": 202_197_650,
         "written": 6_291_431},
-    ("bf16+int8", "paged_attention_kernel", "6325c5ab4be09ec9"): {"read": 127_924_240,
-        "written": 6_291_431},
+    ("bf16+int8", "paged_attention_kernel", "bf6d15dbad8736d0"): {"read": 127_860_018,
+        "written": 6_291_386},
 }
 _CSRC = "sliding_window_ring_tensor_amd/csrc/"
 KERNEL_SOURCES = {
