@@ -742,8 +742,9 @@ typedef struct swrt_paged_layer {
  * (1 << f) for each SWRT_XF_* format f (F32 .. UINT2), or 0 for any. A page
  * of a format outside a non-zero set fails its checks (SWRT_FLAG_BAD_PAGES
  * for its stream). A set without SWRT_XF_F32 and SWRT_XF_F16 runs a build of
- * the kernel without their tile paths: fewer registers, more waves per SIMD.
- * Other bits: SWRT_E_INVALID_ARG.
+ * the kernel without their tile paths: fewer registers, more waves per SIMD;
+ * a set of SWRT_XF_BF16 and SWRT_XF_INT8 alone (either or both) a build for
+ * those two formats only, the fastest. Other bits: SWRT_E_INVALID_ARG.
  */
 int swrt_paged_attention(int n_layers, const swrt_paged_layer *layers, int64_t left_window,
                          int batch, int q_heads, int kv_heads, int head_dim, float scale,
