@@ -267,6 +267,44 @@ def test_paged_attention_declared_formats(orc, formats, zero_points, head):
     assert torch.equal(got[~badt], full.cpu()[~badt])
 
 
+@pytest.mark.parametrize("left_window", [-1, 0, 5, 40])
+@pytest.mark.parametrize("D,Hq,Hkv,qdt", [(64, 16, 2, torch.bfloat16), (64, 16, 4, torch.float32),
+                                          (32, 8, 8, torch.bfloat16), (128, 16, 2, torch.bfloat16)],
+                         ids=str)
+def test_paged_attention_bf16_int8_build_tiles(orc, D, Hq, Hkv, qdt, left_window):
+    """The build for bf16 and int8 pages (declared) on pages of 4 to 48 rows:
+    several tiles in one page (the loop's advance within a page), partial
+    tiles, K and V formats apart, any zero points, ragged and empty streams;
+    within the oracle's bound, for fp32 and 16-bit outputs."""
+    say("paged attention, bf16 + int8 build", D, Hq, Hkv, qdt, left_window)
+    g = wl.rng(500 + D + Hq * 3 + Hkv * 7 + left_window)
+    B = 3
+    T = g.integers(1, 130, size=B * Hkv)
+    T[0] = 0
+    T[-1] = 17
+    streams = [wl.page_split(g, int(t), int(g.choice([4, 16, 32, 48])), sealed=0.3) for t in T]
+    case = wl.paged_case(g, D, streams, random_format(g, [BF16, I8]))
+    q = torch.from_numpy(g.uniform(-1, 1, (B, Hq, D)).astype(np.float32)).to(qdt)
+    cache = upload(case)
+    tb = otable(case)
+    ref, fo = orc.paged_attention(q_host(q), QT[qdt], case.arena, tb, case.page_ptr,
+                                  case.page_ids, left_window, Hkv, D ** -0.5)
+    assert fo == 0
+    for odt in (torch.float32, torch.bfloat16):
+        flags = flag_word()
+        out = swrt.paged_attention([q.to(DEV)], [cache], left_window, Hkv, out_dtype=odt,
+                                   flags=flags, formats=(BF16, I8))[0]
+        torch.cuda.synchronize()
+        assert int(flags.item()) == 0
+        got = out.cpu().to(torch.float64).numpy()
+        tol = bound(case, tb, q, Hkv, left_window, D ** -0.5, odt, ref)
+        err = np.abs(got - ref)
+        assert (err <= tol).all(), f"max err/tol {np.max(err / tol):.3g}"
+        say("  out", odt, "worst err/tol", round(float(np.max(err / tol)), 4))
+        G = Hq // Hkv
+        assert (out[0, :G] == 0).all()  # the empty stream
+
+
 def test_paged_attention_bad_pages_flag_and_skip(orc):
     g = wl.rng(60)
     D, B, Hq, Hkv = 64, 2, 4, 2
