@@ -823,17 +823,15 @@ __attribute__((amdgpu_waves_per_eu(FS == kPgLean && QBF && D == 64 ? 6 : 1))) vo
         auto stage_v = [&](const PgLean &c, int buf) {
           pg_stage_lean<D>(c.v, c.rows, c.kind & 2, stage + (1 + buf) * Stage::BYTES, lane);
         };
-        // The group's visible pages in token order: lanes n_in - 1 .. 0.
+        // One tile from buffer BUF (the next one staged first, into the other
+        // buffer); false after the group's last tile. Two calls an
+        // iteration, so that the buffers alternate at compile time.
         int l = n_in - 1;
-        PgLean c = lean_of(l);
-        int buf = 0;
-        stage_v(c, 0);
-        stage_k(c);
-        while (true) {
+        auto tile = [&](auto bufc, const PgLean &c, PgLean &n) {
+          constexpr int BUF = decltype(bufc)::value;
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this tile's rows have landed
           // the next tile: the page's next 16 rows, or the next page's first
           // (read from any lane when there is none)
-          PgLean n;
           if (c.rows > 16) {
             n = c;
             n.k = c.k + ((c.kind & 1) ? 16 * D : 32 * D);
@@ -844,8 +842,8 @@ __attribute__((amdgpu_waves_per_eu(FS == kPgLean && QBF && D == 64 ? 6 : 1))) vo
             n = lean_of(l & 63);
           }
           const bool more = l >= 0;
-          if (more) stage_v(n, buf ^ 1);
-          const char *vt = stage + (1 + buf) * Stage::BYTES;
+          if (more) stage_v(n, BUF ^ 1);
+          const char *vt = stage + (1 + BUF) * Stage::BYTES;
           const int32_t kz = int16_t(c.zp), vz = c.zp >> 16;
           // this tile's K chunk, then the next tile's K rows into the buffer
           uint32_t w[D / 4];
@@ -896,9 +894,14 @@ __attribute__((amdgpu_waves_per_eu(FS == kPgLean && QBF && D == 64 ? 6 : 1))) vo
             else
               pg_tile_values_t<D, SWRT_XF_INT8, false>(vt, j, qg, pw, 0, acc);
           }
-          if (!more) break;
-          c = n;
-          buf ^= 1;
+          return more;
+        };
+        PgLean c0 = lean_of(l), c1 = c0;
+        stage_v(c0, 0);
+        stage_k(c0);
+        while (true) {
+          if (!tile(PgBuf<0>(), c0, c1)) break;
+          if (!tile(PgBuf<1>(), c1, c0)) break;
         }
       } else {
         // what the tile code needs of page l, uniform
