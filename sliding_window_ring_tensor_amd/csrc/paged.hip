@@ -254,8 +254,10 @@ struct PgAttArgs {
 // fp32 page is read from memory by its own tile code). Each lane then reads
 // exactly its chunks: the K chunk of row pk, elements [q D/4, (q + 1) D/4),
 // and the V chunks of rows 4 c + q, elements [MT j, MT (j + 1)). Up to
-// head_dim 128 a wave has two such buffers, so the next tile's rows are
-// staged while this one is computed.
+// head_dim 128 the next tile's rows are staged while this one is computed:
+// the general tile loop keeps two buffers of K and V, the bf16 + int8 one a
+// K buffer (refilled as soon as the tile's K chunks are read out) and two of
+// V.
 template <int D>
 struct PgStage {
   static constexpr int BYTES = 16 * D * 2;       // one tile's K (or V) rows
