@@ -114,14 +114,14 @@ def q_host(q: torch.Tensor) -> np.ndarray:
     return t.numpy().copy()
 
 
-def run_attention(orc, case, q, Hkv, left_window, out_dtype, scale=None, tb=None):
+def run_attention(orc, case, q, Hkv, left_window, out_dtype, scale=None, tb=None, formats=None):
     D = q.shape[2]
     sc = D ** -0.5 if scale is None else scale
     cache = upload(case) if tb is None else swrt.PagedCache.upload(tb, case.page_ptr,
                                                                    case.page_ids, case.arena, DEV)
     flags = flag_word()
     out = swrt.paged_attention([q.to(DEV)], [cache], left_window, Hkv, scale=sc,
-                               out_dtype=out_dtype, flags=flags)[0]
+                               out_dtype=out_dtype, flags=flags, formats=formats)[0]
     torch.cuda.synchronize()
     tbo = otable(case) if tb is None else tb
     ref, f = orc.paged_attention(q_host(q), QT[q.dtype], case.arena, tbo, case.page_ptr,
@@ -164,14 +164,16 @@ def test_paged_attention_mixed_formats(orc, qdt, D, Hq, Hkv, left_window):
         assert (out[0, :G] == 0).all()  # the empty stream
 
 
+@pytest.mark.parametrize("formats", [None, (BF16, I8)], ids=["any", "bf16-int8"])
 @pytest.mark.parametrize("left_window", [-1, 63, 64, 150])
 @pytest.mark.parametrize("qdt", [torch.bfloat16, torch.float32], ids=str)
-def test_paged_attention_windows_over_many_pages(orc, qdt, left_window):
+def test_paged_attention_windows_over_many_pages(orc, qdt, left_window, formats):
     """Windows that reach more than 64 pages (pages of 1 to 3 tokens): the
     kernel walks a stream's pages 64 at a time from the last one back, so
     these streams take two to seven groups, with the window's first page at
-    and around a group boundary."""
-    say("paged attention, many pages", qdt, left_window)
+    and around a group boundary; for any format and in the build for bf16
+    and int8 pages (whose staging buffers carry over from group to group)."""
+    say("paged attention, many pages", qdt, left_window, formats)
     g = wl.rng(900 + left_window)
     D, Hq, Hkv, B = 64, 8, 2, 3
     T = g.integers(100, 400, size=B * Hkv)
@@ -180,9 +182,11 @@ def test_paged_attention_windows_over_many_pages(orc, qdt, left_window):
     caps = [1, 1, 2, 3, 1, 2]
     streams = [wl.page_split(g, int(t), c, sealed=0.2) for t, c in zip(T, caps)]
     assert max(len(s) for s in streams) > 128
-    case = wl.paged_case(g, D, streams, random_format(g))
+    case = wl.paged_case(g, D, streams, random_format(g) if formats is None
+                         else random_format(g, list(formats)))
     q = torch.from_numpy(g.uniform(-1, 1, (B, Hq, D)).astype(np.float32)).to(qdt)
-    out, ref, fg, fo, tb = run_attention(orc, case, q, Hkv, left_window, torch.float32)
+    out, ref, fg, fo, tb = run_attention(orc, case, q, Hkv, left_window, torch.float32,
+                                         formats=formats)
     assert fg == fo == 0
     got = out.detach().cpu().to(torch.float64).numpy()
     tol = bound(case, tb, q, Hkv, left_window, D ** -0.5, torch.float32, ref)
