@@ -944,15 +944,17 @@ __attribute__((amdgpu_waves_per_eu(FS == kPgLean && QBF && D == 64 ? 6 : 1))) vo
         // two buffers the next tile is staged before this one is computed.
         int l = n_in - 1;
         int32_t i = field(p_first, l);
-        PgCur c = cur_of(l);
-        int buf = 0;
-        stage_tile(l, i, 0, c);
-        while (true) {
+        // One tile of page l from buffer BUF, rows [i, i + 16): the next
+        // tile's page fields into cn and its rows into the other buffer
+        // first (two buffers), or into the same buffer after (one); false
+        // after the group's last tile.
+        auto step = [&](auto bufc, const PgCur &c, PgCur &cn) {
+          constexpr int BUF = decltype(bufc)::value;
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this tile's rows have landed
           // the tile after this one
           int ln = l;
           int32_t in_ = i + 16;
-          PgCur cn = c;
+          cn = c;
           if (in_ >= c.len) {
             ln = l - 1;
             in_ = 0;
@@ -962,9 +964,9 @@ __attribute__((amdgpu_waves_per_eu(FS == kPgLean && QBF && D == 64 ? 6 : 1))) vo
             }
           }
           if constexpr (Stage::NBUF == 2) {
-            if (ln >= 0) stage_tile(ln, in_, buf ^ 1, cn);
+            if (ln >= 0) stage_tile(ln, in_, BUF ^ 1, cn);
           }
-          const char *kt = stage + buf * (2 * Stage::BYTES), *vt = kt + Stage::BYTES;
+          const char *kt = stage + BUF * (2 * Stage::BYTES), *vt = kt + Stage::BYTES;
           // this tile: page l's formats and scales
           const int kf = c.kf, vf = c.vf;
           const int32_t len = c.len;
@@ -984,25 +986,36 @@ __attribute__((amdgpu_waves_per_eu(FS == kPgLean && QBF && D == 64 ? 6 : 1))) vo
           if (FS == kPgWide && vf == SWRT_XF_F32) {  // not staged
             uint32_t w[4][MT];
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
+            for (int r = 0; r < 4; ++r)
               pg_load_raw<MT * 4>(arena + field64(d.v_offset, l) +
-                                      int64_t(min(i + 4 * c + int32_t(qg), len - 1)) * (4 * D) +
+                                      int64_t(min(i + 4 * r + int32_t(qg), len - 1)) * (4 * D) +
                                       int64_t(j) * (4 * MT),
-                                  w[c]);
+                                  w[r]);
             pg_values_words<D, SWRT_XF_F32>(w, pw, 0, acc);
           } else {
             pg_tile_values<D, FS>(vf, vt, j, qg, pw, vz, acc);
           }
-          if (ln < 0) break;
-          if constexpr (Stage::NBUF == 2) {
-            buf ^= 1;
-          } else {
+          if (ln < 0) return false;
+          if constexpr (Stage::NBUF == 1) {
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this tile read out before the refill
             stage_tile(ln, in_, 0, cn);
           }
           l = ln;
           i = in_;
-          c = cn;
+          return true;
+        };
+        PgCur c0 = cur_of(l), c1 = c0;
+        stage_tile(l, i, 0, c0);
+        if constexpr (Stage::NBUF == 2) {  // two tiles an iteration: the buffers alternate
+          while (true) {
+            if (!step(PgBuf<0>(), c0, c1)) break;
+            if (!step(PgBuf<1>(), c1, c0)) break;
+          }
+        } else {
+          while (true) {
+            if (!step(PgBuf<0>(), c0, c1)) break;
+            c0 = c1;
+          }
         }
       }
     }
