@@ -16,7 +16,11 @@
 //                           as the exact integers c - zp on the bf16
 //                           instructions, fp32 weights as three exact bf16
 //                           parts; fp32 and f16 pages on the fp32 ones), the
-//                           scales applied to the score and the weight.
+//                           scales applied to the score and the weight. Built
+//                           per declared format set: bf16 and int8 pages
+//                           only (a tile loop of its own, six waves per SIMD
+//                           at head_dim 64), every staged format but f16, or
+//                           all formats.
 //   paged_validate / paged_convert / paged_publish
 //                           the conversion of selected pages: every check on
 //                           the device first, then the payloads, then the
