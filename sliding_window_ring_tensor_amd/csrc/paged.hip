@@ -248,8 +248,10 @@ struct PgAttArgs {
   uint32_t *flags;
   float scale_log2;  // scale * log2(e)
   int64_t left_window;
-  int32_t B, Hq, Hkv, items, q_type, out_type;
-  int32_t chunks;  // groups of up to 16 query heads per KV head
+  int32_t B, Hq, Hkv, q_type, out_type;
+  int32_t items;     // per layer: (stream, chunk) pairs
+  int32_t wg_layer;  // workgroups per layer, a multiple of the 8 XCDs
+  int32_t chunks;    // groups of up to 16 query heads per KV head
   uint32_t formats;  // bit f set: pages of format f are allowed
 };
 
@@ -662,15 +664,19 @@ __attribute__((amdgpu_waves_per_eu(FS == kPgLean && QBF && D == 64 ? 6 : 1))) vo
   // layer's pointers) then lives in scalar registers
   const uint32_t lane = threadIdx.x % 64, wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
   const uint32_t j = lane % 16, qg = lane / 16;
-  const uint32_t item = blockIdx.x * kPgWaves + wave;
+  // Workgroups go to the eight XCDs in turn. Each layer's workgroups start at
+  // a multiple of 8, so the waves of one stream in every layer run on the
+  // same XCD, where layers that share a block table find its ids and
+  // descriptors in that XCD's L2.
+  const uint32_t layer = blockIdx.x / uint32_t(a.wg_layer);
+  const uint32_t item = (blockIdx.x - layer * uint32_t(a.wg_layer)) * kPgWaves + wave;
   if (item >= uint32_t(a.items)) return;
   char *stage = stage_all[wave];
-  // an item is (layer, stream, chunk): the chunk's query heads are
+  // an item is (stream, chunk) of the layer: the chunk's query heads are
   // 16 chunk .. 16 chunk + 15 of the group (a group of more than 16 heads is
   // split over consecutive items, whose waves read the same pages)
   const uint32_t chunk = item % uint32_t(a.chunks), str = item / uint32_t(a.chunks);
-  const uint32_t g = str % uint32_t(a.Hkv), b = (str / uint32_t(a.Hkv)) % uint32_t(a.B);
-  const uint32_t layer = str / uint32_t(a.Hkv * a.B);
+  const uint32_t g = str % uint32_t(a.Hkv), b = str / uint32_t(a.Hkv);
   const PgLayer &P = a.L[layer];
   const char *const arena = P.arena;
   const int G = a.Hq / a.Hkv;
@@ -1539,7 +1545,8 @@ extern "C" int swrt_paged_attention(int n_layers, const swrt_paged_layer *layers
   a.B = batch;
   a.Hq = q_heads;
   a.Hkv = kv_heads;
-  a.items = n_layers * batch * kv_heads * chunks;
+  a.items = batch * kv_heads * chunks;
+  a.wg_layer = int32_t((int64_t(a.items) + 8 * kPgWaves - 1) / (8 * kPgWaves) * 8);
   a.chunks = chunks;
   a.q_type = q_type;
   a.out_type = out_type;
@@ -1550,7 +1557,7 @@ extern "C" int swrt_paged_attention(int n_layers, const swrt_paged_layer *layers
                  : (a.formats & ((1u << SWRT_XF_F32) | (1u << SWRT_XF_F16))) == 0 ? kPgNarrow
                                                                                    : kPgWide;
   static_assert(sizeof(PgAttArgs) <= 4096, "kernel arguments exceed 4 KiB");
-  const dim3 grid((uint32_t(a.items) + kPgWaves - 1) / kPgWaves);
+  const dim3 grid(uint32_t(n_layers) * uint32_t(a.wg_layer));
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool qbf = q_type == SWRT_XF_BF16;
 #define SWRT_PG_LAUNCH_FS(DD, QB, FS) \
