@@ -380,9 +380,15 @@ def test_paged_attention_bad_pages_flag_and_skip(orc):
         assert int(flags.item()) == swrt.FLAG_BAD_PAGES
 
 
-def test_paged_attention_several_layers_sharing_a_block_table(orc):
+@pytest.mark.parametrize("Hq,Hkv", [(16, 2), (68, 2)])
+def test_paged_attention_several_layers_sharing_a_block_table(orc, Hq, Hkv):
+    """Three layers on one block table. Each layer's workgroups start at a
+    multiple of 8: with 8 (stream, chunk) items a layer, or 24 at three
+    chunks a stream (34 heads a group), the later layers begin after idle
+    padding workgroups, and a stream's chunks straddle workgroups."""
+    say("paged layers on one table", Hq, Hkv)
     g = wl.rng(61)
-    D, B, Hq, Hkv, n = 64, 4, 16, 2, 3
+    D, B, n = 64, 4, 3
     streams = [wl.page_split(g, int(t), 16, 0.2) for t in g.integers(1, 200, B * Hkv)]
     # one block table (the same layout and formats), each layer its own payload bytes
     cases = [wl.paged_case(wl.rng(70), D, streams, random_format(wl.rng(71)),
