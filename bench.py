@@ -64,8 +64,8 @@ MEASURED_TRAFFIC = {
     ("bf16", "window_in_place", "f1e8f2524c95ef7d"): {"read": 195_188_321, "written": 196_006_053},
     ("bf16", "window_attention_mfma", "3277255b340464c2"): {"read": 202_197_650,
         "written": 6_291_431},
-    ("bf16+int8", "paged_attention_kernel", "3418ad9677d8b552"): {"read": 127_894_140,
-        "written": 6_291_418},
+    ("bf16+int8", "paged_attention_kernel", "b87b76986fed5b7a"): {"read": 127_894_338,
+        "written": 6_291_441},
 }
 _CSRC = "sliding_window_ring_tensor_amd/csrc/"
 KERNEL_SOURCES = {

@@ -6,8 +6,10 @@
 // selected blocks; attention over the visible tokens only, with online
 // softmax and a left window bounding the preceding tokens).
 //
-// Three kernel families:
-//   paged_attention_kernel  one wave per (layer, batch entry, KV head) stream:
+// Four kernel families:
+//   paged_attention_kernel  one wave per (layer, batch entry, KV head) stream
+//                           and chunk of 16 query heads, each layer's
+//                           workgroups aligned to the eight XCDs:
 //                           finds the pages its window reaches, checks each,
 //                           stages each 16-row tile of a page into LDS as it
 //                           lies in the page, decodes it in the page's formats
