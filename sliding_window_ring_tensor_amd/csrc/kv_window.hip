@@ -32,7 +32,7 @@ template <int VEC, int NL, int SPW, bool XF>
 __global__ __launch_bounds__(kWinBlock) void window_in_place(WinArgs<NL> a) {
   if constexpr (SPW == 1) {
     const Slice s = decode_slice(a.g, blockIdx.x);
-    const int64_t Lp = a.g.lp[s.b], E = a.g.ev[s.b];
+    const int64_t Lp = ld_invariant(a.g.lp, s.b), E = ld_invariant(a.g.ev, s.b);
     if (!lengths_ok(a.g, s, threadIdx.x == 0, Lp, E)) return;
     int64_t P = 0;
     if constexpr (XF) {
@@ -50,8 +50,8 @@ __global__ __launch_bounds__(kWinBlock) void window_in_place(WinArgs<NL> a) {
         [&](uint32_t slice, int g) {
           const Slice s = decode_slice(a.g, slice);
           SliceWork w;
-          w.Lp = a.g.lp[s.b];
-          w.E = a.g.ev[s.b];
+          w.Lp = ld_invariant(a.g.lp, s.b);
+          w.E = ld_invariant(a.g.ev, s.b);
           w.ok = lengths_ok(a.g, s, threadIdx.x == g * GB, w.Lp, w.E);
           w.t = int(s.t);
           w.h = s.h;
@@ -72,7 +72,7 @@ template <int VEC, int NL, bool XF>
 __global__ __launch_bounds__(kWinBlock) void window_stage(WinArgs<NL> a) {
   const uint32_t slice = blockIdx.x / a.g.tiles, tile = blockIdx.x - slice * a.g.tiles;
   const Slice s = decode_slice(a.g, slice);
-  const int64_t Lp = a.g.lp[s.b], E = a.g.ev[s.b];
+  const int64_t Lp = ld_invariant(a.g.lp, s.b), E = ld_invariant(a.g.ev, s.b);
   if (!lengths_ok(a.g, s, tile == 0 && threadIdx.x == 0, Lp, E)) return;
   int64_t P = 0;
   if constexpr (XF) {
@@ -90,7 +90,7 @@ template <int VEC, int NL, bool XF>
 __global__ __launch_bounds__(kWinBlock) void window_commit(WinArgs<NL> a) {
   const uint32_t slice = blockIdx.x / a.g.tiles, tile = blockIdx.x - slice * a.g.tiles;
   const Slice s = decode_slice(a.g, slice);
-  const int64_t Lp = a.g.lp[s.b], E = a.g.ev[s.b];
+  const int64_t Lp = ld_invariant(a.g.lp, s.b), E = ld_invariant(a.g.ev, s.b);
   if (!lengths_ok(a.g, s, tile == 0 && threadIdx.x == 0, Lp, E)) return;
   if constexpr (XF) {  // an entry the stage phase skipped stays untouched
     if (!positions_ok(a.g, a.xf, s, tile == 0 && threadIdx.x == 0, a.g.past[s.b])) return;
@@ -134,7 +134,7 @@ __global__ __launch_bounds__(kWinBlock) void window_stage_lengths(WinArgs<NL> a,
   if (bid >= q.stage_blocks) return;  // a grid sized by the length arrays alone
   const uint32_t slice = bid / a.g.tiles, tile = bid - slice * a.g.tiles;
   const Slice s = decode_slice(a.g, slice);
-  const StepLengths r = step_lengths<DRIFT>(q.seqlens_k[s.b], a.g.S, a.g.C, q.gap);
+  const StepLengths r = step_lengths<DRIFT>(ld_invariant(q.seqlens_k, s.b), a.g.S, a.g.C, q.gap);
   if constexpr (XF) {
     if (!positions_ok(a.g, a.xf, s, tile == 0 && threadIdx.x == 0, r.P)) return;
   }

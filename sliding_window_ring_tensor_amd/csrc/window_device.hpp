@@ -29,6 +29,16 @@ constexpr int kWinBlock = SWRT_WIN_BLOCK;
 constexpr int kWinUnroll = SWRT_WINDOW_UNROLL;  // words per thread per tile
 constexpr uint32_t kWinTile = kWinBlock * kWinUnroll;
 
+// Element i of a per-batch length array that no kernel of the launch writes
+// (seqlens_k, or Lp and E from an earlier launch), at an index equal on every
+// lane of the wave. Read through the constant address space, so the compiler
+// issues a scalar load: it waits in the scalar cache's queue, not behind the
+// CU's vector memory traffic.
+__device__ __forceinline__ int32_t ld_invariant(const int32_t *p, uint32_t i) {
+  typedef const __attribute__((address_space(4))) int32_t *ConstPtr;
+  return ((ConstPtr)p)[i];  // an address space cast (the C form is the one allowed)
+}
+
 // ---------------------------------------------------------------------------
 // lengths of one step (same page, section "Design"; the follow-up commit does
 // the arithmetic in 64 bits because seqlens_k + 1 overflows 32 bits at
