@@ -55,13 +55,13 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD's published peak
 # (FETCH_SIZE, WRITE_SIZE), each scaled by what the counter reads for a 1 GiB
 # copy; valid only for the kernel source they were taken on (its hash).
 MEASURED_TRAFFIC = {
-    ("bf16", "decode_step_kernel", "b912eb360b0a480b"): {"read": 196_792_068,
-                                                         "written": 196_842_370},
-    ("fp8_e4m3fn", "decode_step_kernel", "b912eb360b0a480b"): {"read": 99_427_929,
-                                                               "written": 98_587_015},
-    ("bf16->int8", "decode_step_kernel", "b912eb360b0a480b"): {"read": 103_034_888,
-                                                               "written": 98_767_770},
-    ("bf16", "window_in_place", "44aa31a747a92997"): {"read": 195_191_335, "written": 196_003_247},
+    ("bf16", "decode_step_kernel", "7c60268bc4021eab"): {"read": 196_791_383,
+                                                         "written": 196_860_370},
+    ("fp8_e4m3fn", "decode_step_kernel", "7c60268bc4021eab"): {"read": 99_418_076,
+                                                               "written": 98_589_539},
+    ("bf16->int8", "decode_step_kernel", "7c60268bc4021eab"): {"read": 101_391_803,
+                                                               "written": 98_796_627},
+    ("bf16", "window_in_place", "7baab05ee8cf426a"): {"read": 195_192_247, "written": 196_015_224},
     ("bf16", "window_attention_mfma", "3277255b340464c2"): {"read": 202_197_650,
         "written": 6_291_431},
     ("bf16+int8", "paged_attention_kernel", "b87b76986fed5b7a"): {"read": 127_894_338,

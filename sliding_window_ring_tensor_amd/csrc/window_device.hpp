@@ -280,11 +280,11 @@ __device__ __forceinline__ SliceWork wave_uniform(const SliceWork &w) {
 #define SWRT_GROUP_UNROLL 2
 #endif
 constexpr int kGroupUnroll = SWRT_GROUP_UNROLL;  // words per lane per slice in group mode
-// A fused append's subgroup takes more words a lane, so that more slices share
-// a workgroup: its row costs a few dependent steps (loads, arithmetic, store)
-// that more slices in flight per workgroup hide; a plain copy gains nothing
-// from it.
-constexpr int kGroupUnrollXf = 4;
+// A fused append's subgroup takes as many words a lane as a plain copy's. Four
+// (twice the slices per workgroup, to hide the row's few dependent steps:
+// loads, arithmetic, store) measured slower once each wave works out only its
+// own slice: 35.6 against 34.8 us on a 24-layer int8 fused decode step.
+constexpr int kGroupUnrollXf = 2;
 template <bool XF>
 constexpr int group_unroll() { return XF ? kGroupUnrollXf : kGroupUnroll; }
 
