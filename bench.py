@@ -64,8 +64,8 @@ MEASURED_TRAFFIC = {
     ("bf16", "window_in_place", "7baab05ee8cf426a"): {"read": 195_192_247, "written": 196_015_224},
     ("bf16", "window_attention_mfma", "3277255b340464c2"): {"read": 202_197_650,
         "written": 6_291_431},
-    ("bf16+int8", "paged_attention_kernel", "b87b76986fed5b7a"): {"read": 127_894_338,
-        "written": 6_291_441},
+    ("bf16+int8", "paged_attention_kernel", "2558684f894e20c2"): {"read": 127_909_170,
+        "written": 6_291_448},
 }
 _CSRC = "sliding_window_ring_tensor_amd/csrc/"
 KERNEL_SOURCES = {
